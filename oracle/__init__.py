@@ -1,0 +1,135 @@
+"""fp64 CPU oracle for the Mamba-1 (S6) selective scan -- test infrastructure only.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The GPU library never links, loads or calls it,
+and it imports nothing from the GPU library.
+
+The arithmetic lives in ``jscan_oracle.c`` (plain C, fp64, compiled with
+``-O2 -fno-fast-math -ffp-contract=off``); this module only widens inputs exactly to
+float64, allocates outputs and calls it through ctypes.  The recurrence it computes is the
+S6 equation of the Jamba notes page ("Jamba: A Hybrid Transformer-Mamba Language Model",
+section "Mamba layer"):
+
+    h_t = exp(Delta_t A) h_{t-1} + Delta_t B_t x_t,     y_t = C_t h_t
+
+for every (batch, channel, state) with diagonal A (lesson page "Jamba - Hybrid
+SSM-Transformer", section "Mamba-3", item 2).  Shapes: x, delta, y ``[batch, L, D]``;
+A ``[D, N]``; B, C ``[batch, L, N]``; states ``[batch, D, N]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "jscan_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle_jscan.so")
+_lib = None
+
+GCC_FLAGS = ["-O2", "-std=c99", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared", "-pthread"]
+
+
+def build() -> str:
+    """Compile the C oracle in place (always recompiles)."""
+    tmp = _LIB + ".tmp"
+    subprocess.check_call(["gcc", *GCC_FLAGS, "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    dp = ctypes.POINTER(ctypes.c_double)
+    i64 = ctypes.c_int64
+    lib.oracle_prefill_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, ctypes.c_int]
+    lib.oracle_prefill_chunked_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, i64, ctypes.c_int]
+    lib.oracle_step_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64]
+    for f in (lib.oracle_prefill_f64, lib.oracle_prefill_chunked_f64, lib.oracle_step_f64):
+        f.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _f64(a) -> np.ndarray:
+    """Exact widening to a contiguous float64 numpy array (bf16 and fp32 are exact in fp64)."""
+    if hasattr(a, "detach"):  # torch tensor
+        import torch
+
+        a = a.detach().to("cpu", torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _check_shapes(x, delta, A, B, C, h0):
+    if x.ndim != 3 or delta.shape != x.shape:
+        raise ValueError("x and delta must both be [batch, L, D]")
+    batch, L, D = x.shape
+    if A.ndim != 2 or A.shape[0] != D:
+        raise ValueError("A must be [D, N]")
+    N = A.shape[1]
+    if B.shape != (batch, L, N) or C.shape != (batch, L, N):
+        raise ValueError("B and C must be [batch, L, N]")
+    if h0 is not None and h0.shape != (batch, D, N):
+        raise ValueError("h0 must be [batch, D, N]")
+    return batch, L, D, N
+
+
+def prefill(x, delta, A, B, C, h0=None, nthreads: int = 0):
+    """Sequential fp64 scan.  Returns ``(y [batch,L,D], h_final [batch,D,N])`` as float64."""
+    lib = _load()
+    x, delta, A, B, C = (_f64(v) for v in (x, delta, A, B, C))
+    h0 = None if h0 is None else _f64(h0)
+    batch, L, D, N = _check_shapes(x, delta, A, B, C, h0)
+    y = np.empty((batch, L, D), np.float64)
+    h = np.empty((batch, D, N), np.float64)
+    rc = lib.oracle_prefill_f64(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(h0), _ptr(y), _ptr(h),
+                                batch, L, D, N, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_prefill_f64 failed ({rc})")
+    return y, h
+
+
+def prefill_chunked(x, delta, A, B, C, chunk: int, h0=None, nthreads: int = 0):
+    """The same scan evaluated chunk by chunk through the associative combine."""
+    lib = _load()
+    x, delta, A, B, C = (_f64(v) for v in (x, delta, A, B, C))
+    h0 = None if h0 is None else _f64(h0)
+    batch, L, D, N = _check_shapes(x, delta, A, B, C, h0)
+    y = np.empty((batch, L, D), np.float64)
+    h = np.empty((batch, D, N), np.float64)
+    rc = lib.oracle_prefill_chunked_f64(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(h0), _ptr(y),
+                                        _ptr(h), batch, L, D, N, int(chunk), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_prefill_chunked_f64 failed ({rc})")
+    return y, h
+
+
+def step(h, x_t, delta_t, A, B_t, C_t):
+    """One decode step.  Returns ``(y_t [batch,D], h_new [batch,D,N])``; the input h is not modified."""
+    lib = _load()
+    h = _f64(h).copy()
+    x_t, delta_t, A, B_t, C_t = (_f64(v) for v in (x_t, delta_t, A, B_t, C_t))
+    batch, D, N = h.shape
+    if x_t.shape != (batch, D) or delta_t.shape != (batch, D) or A.shape != (D, N):
+        raise ValueError("step: x_t, delta_t must be [batch, D] and A [D, N]")
+    if B_t.shape != (batch, N) or C_t.shape != (batch, N):
+        raise ValueError("step: B_t and C_t must be [batch, N]")
+    y = np.empty((batch, D), np.float64)
+    rc = lib.oracle_step_f64(_ptr(h), _ptr(x_t), _ptr(delta_t), _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(y),
+                             batch, D, N)
+    if rc != 0:
+        raise RuntimeError(f"oracle_step_f64 failed ({rc})")
+    return y, h

@@ -1,0 +1,218 @@
+/*
+ * jscan_oracle.c - plain, slow, fp64 CPU oracle for the Mamba-1 (S6) selective scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call this
+ * file: only the test suite, the smoke check and the CPU-baseline leg of the bench use it.
+ * It shares no code, header, table or helper with the GPU library.
+ *
+ * What it computes.  The S6 recurrence of the Jamba notes page ("Jamba: A Hybrid
+ * Transformer-Mamba Language Model", section "Mamba layer", the S6 equation) and of the
+ * lesson page ("Jamba - Hybrid SSM-Transformer", section "SSM on one page"):
+ *
+ *     h_t = Abar_t * h_{t-1} + Bbar_t x_t,          y_t = C_t h_t
+ *
+ * with input-dependent Delta_t, B_t, C_t (notes page, same section) and a real diagonal A
+ * (lesson page, section "Mamba-3", item 2).  The discretisation is
+ *
+ *     Abar_t = exp(Delta_t * A),                    Bbar_t x_t = Delta_t * B_t * x_t
+ *
+ * Because A is diagonal every (batch b, channel d, state n) is an independent scalar
+ * recurrence, and y_t[d] is the dot product of C_t with the state vector h_t[d, :]
+ * taken AFTER the update of step t.
+ *
+ * Layouts (row-major, last index fastest):
+ *     x, delta, y : [batch][L][D]          A      : [D][N]
+ *     B, C        : [batch][L][N]          h0, h  : [batch][D][N]
+ *
+ * Every value is a double.  The caller widens bf16 / fp32 inputs exactly to double first.
+ * The time loop is strictly sequential; only independent (b, d) chains are spread over
+ * threads, which does not change a single rounding.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+typedef struct {
+    const double *x, *delta, *A, *B, *C, *h0;
+    double *y, *h_final;
+    int64_t batch, L, D, N, chunk;
+    int64_t item_begin, item_end; /* items are (b, d) pairs, item = b * D + d */
+} scan_job;
+
+/* One (b, d) chain over all L tokens: the recurrence written out term by term. */
+static void scan_chain_sequential(const scan_job *j, int64_t b, int64_t d)
+{
+    const int64_t L = j->L, D = j->D, N = j->N;
+    double *h = (double *)malloc((size_t)N * sizeof(double));
+    for (int64_t n = 0; n < N; ++n)
+        h[n] = j->h0 ? j->h0[(b * D + d) * N + n] : 0.0;
+
+    for (int64_t t = 0; t < L; ++t) {
+        const double delta_t = j->delta[(b * L + t) * D + d];
+        const double x_t = j->x[(b * L + t) * D + d];
+        const double *B_t = j->B + (b * L + t) * N;
+        const double *C_t = j->C + (b * L + t) * N;
+        double y_t = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const double Abar = exp(delta_t * j->A[d * N + n]);     /* Abar_t = exp(Delta_t A)   */
+            const double Bbar_x = delta_t * B_t[n] * x_t;           /* Bbar_t x_t = Delta_t B_t x_t */
+            h[n] = Abar * h[n] + Bbar_x;                            /* h_t = Abar_t h_{t-1} + Bbar_t x_t */
+            y_t += C_t[n] * h[n];                                   /* y_t = C_t h_t             */
+        }
+        j->y[(b * L + t) * D + d] = y_t;
+    }
+    if (j->h_final)
+        for (int64_t n = 0; n < N; ++n)
+            j->h_final[(b * D + d) * N + n] = h[n];
+    free(h);
+}
+
+/*
+ * The same chain evaluated chunk by chunk with the associative combine of the linear
+ * recurrence: a chunk of tokens acts on an incoming state as h -> P * h + q, where
+ * P = prod(Abar) over the chunk and q is the chunk's own scan started from zero;
+ * composing two such maps gives (P1, q1) then (P2, q2) = (P1 P2, P2 q1 + q2).
+ * Inside a chunk, h_t = P_{<=t} h_in + q_t.  Used only to pin that chunked evaluation
+ * equals the sequential one (the basis of time-parallel and sequence-split scans).
+ */
+static void scan_chain_chunked(const scan_job *j, int64_t b, int64_t d)
+{
+    const int64_t L = j->L, D = j->D, N = j->N, K = j->chunk;
+    double *h_in = (double *)malloc((size_t)N * sizeof(double));
+    double *P = (double *)malloc((size_t)N * sizeof(double));
+    double *q = (double *)malloc((size_t)N * sizeof(double));
+    for (int64_t n = 0; n < N; ++n)
+        h_in[n] = j->h0 ? j->h0[(b * D + d) * N + n] : 0.0;
+
+    for (int64_t t0 = 0; t0 < L; t0 += K) {
+        const int64_t t1 = (t0 + K < L) ? t0 + K : L;
+        for (int64_t n = 0; n < N; ++n) {
+            P[n] = 1.0;
+            q[n] = 0.0;
+        }
+        for (int64_t t = t0; t < t1; ++t) {
+            const double delta_t = j->delta[(b * L + t) * D + d];
+            const double x_t = j->x[(b * L + t) * D + d];
+            const double *B_t = j->B + (b * L + t) * N;
+            const double *C_t = j->C + (b * L + t) * N;
+            double y_t = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                const double Abar = exp(delta_t * j->A[d * N + n]);
+                P[n] = P[n] * Abar;                              /* product of Abar inside the chunk */
+                q[n] = Abar * q[n] + delta_t * B_t[n] * x_t;     /* chunk-local scan from zero        */
+                y_t += C_t[n] * (P[n] * h_in[n] + q[n]);         /* state = P h_in + q                */
+            }
+            j->y[(b * L + t) * D + d] = y_t;
+        }
+        for (int64_t n = 0; n < N; ++n)
+            h_in[n] = P[n] * h_in[n] + q[n];                     /* carry the state into the next chunk */
+    }
+    if (j->h_final)
+        for (int64_t n = 0; n < N; ++n)
+            j->h_final[(b * D + d) * N + n] = h_in[n];
+    free(h_in);
+    free(P);
+    free(q);
+}
+
+static void *scan_worker(void *arg)
+{
+    const scan_job *j = (const scan_job *)arg;
+    for (int64_t item = j->item_begin; item < j->item_end; ++item) {
+        const int64_t b = item / j->D, d = item % j->D;
+        if (j->chunk > 0)
+            scan_chain_chunked(j, b, d);
+        else
+            scan_chain_sequential(j, b, d);
+    }
+    return NULL;
+}
+
+static int run_scan(scan_job base, int nthreads)
+{
+    const int64_t items = base.batch * base.D;
+    if (items <= 0 || base.L <= 0)
+        return 0;
+    if (nthreads <= 0) {
+        long c = sysconf(_SC_NPROCESSORS_ONLN);
+        nthreads = c > 0 ? (int)c : 1;
+    }
+    if (nthreads > items)
+        nthreads = (int)items;
+    pthread_t *tid = (pthread_t *)malloc((size_t)nthreads * sizeof(pthread_t));
+    scan_job *jobs = (scan_job *)malloc((size_t)nthreads * sizeof(scan_job));
+    int started = 0, rc = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i] = base;
+        jobs[i].item_begin = items * i / nthreads;
+        jobs[i].item_end = items * (i + 1) / nthreads;
+        if (pthread_create(&tid[i], NULL, scan_worker, &jobs[i]) != 0) {
+            scan_worker(&jobs[i]); /* fall back to running this share inline */
+            continue;
+        }
+        tid[started] = tid[i];
+        ++started;
+    }
+    for (int i = 0; i < started; ++i)
+        pthread_join(tid[i], NULL);
+    free(tid);
+    free(jobs);
+    return rc;
+}
+
+/* Prefill: y for every token and the state after the last token.  h0 may be NULL (zero state). */
+int oracle_prefill_f64(const double *x, const double *delta, const double *A, const double *B,
+                       const double *C, const double *h0, double *y, double *h_final,
+                       int64_t batch, int64_t L, int64_t D, int64_t N, int nthreads)
+{
+    scan_job j;
+    memset(&j, 0, sizeof j);
+    j.x = x; j.delta = delta; j.A = A; j.B = B; j.C = C; j.h0 = h0;
+    j.y = y; j.h_final = h_final;
+    j.batch = batch; j.L = L; j.D = D; j.N = N; j.chunk = 0;
+    return run_scan(j, nthreads);
+}
+
+/* Prefill evaluated chunk by chunk (chunk >= 1 tokens) through the associative combine. */
+int oracle_prefill_chunked_f64(const double *x, const double *delta, const double *A,
+                               const double *B, const double *C, const double *h0, double *y,
+                               double *h_final, int64_t batch, int64_t L, int64_t D, int64_t N,
+                               int64_t chunk, int nthreads)
+{
+    if (chunk < 1)
+        return -1;
+    scan_job j;
+    memset(&j, 0, sizeof j);
+    j.x = x; j.delta = delta; j.A = A; j.B = B; j.C = C; j.h0 = h0;
+    j.y = y; j.h_final = h_final;
+    j.batch = batch; j.L = L; j.D = D; j.N = N; j.chunk = chunk;
+    return run_scan(j, nthreads);
+}
+
+/*
+ * One decode step (constant memory: only h_{t-1} and the current token are needed, lesson
+ * page, "SSM on one page").  h is [batch][D][N] and is updated in place; x_t, delta_t and
+ * y_t are [batch][D]; B_t and C_t are [batch][N].
+ */
+int oracle_step_f64(double *h, const double *x_t, const double *delta_t, const double *A,
+                    const double *B_t, const double *C_t, double *y_t,
+                    int64_t batch, int64_t D, int64_t N)
+{
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < D; ++d) {
+            const double dl = delta_t[b * D + d], xv = x_t[b * D + d];
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                double *hn = &h[(b * D + d) * N + n];
+                const double Abar = exp(dl * A[d * N + n]);
+                *hn = Abar * *hn + dl * B_t[b * N + n] * xv;
+                acc += C_t[b * N + n] * *hn;
+            }
+            y_t[b * D + d] = acc;
+        }
+    }
+    return 0;
+}
