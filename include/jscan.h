@@ -1,0 +1,132 @@
+/*
+ * jscan.h - C ABI of libjscan, the Mamba-1 (S6) selective state-space scan on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation.  For every batch row b, channel d < D and state n < N = 16, the scan
+ * runs the selective recurrence of the Jamba notes page ("Jamba: A Hybrid
+ * Transformer-Mamba Language Model", section "Mamba layer", the S6 equation):
+ *
+ *     h_t[d,n] = exp(delta_t[d] * A[d,n]) * h_{t-1}[d,n] + (delta_t[d] * x_t[d]) * B_t[n]
+ *     y_t[d]   = sum_n C_t[n] * h_t[d,n]
+ *
+ * The decay exp(delta A) and the input term delta B x are the discretised A-bar and
+ * B-bar x of that equation.  delta, B and C are inputs that depend on the token (same
+ * section).  A is real and diagonal, one value per (channel, state) (lesson page
+ * "Jamba - Hybrid SSM-Transformer", section "Mamba-3", item 2).  d_state is 16 (notes
+ * page, "Mamba layer").  Only h_{t-1} and the current token are needed to advance one
+ * token, so decoding runs in constant memory (lesson page, section "SSM on one page").
+ *
+ * Arithmetic.  The state is fp32 and is never rounded to the input dtype.  Every state
+ * element is advanced by the same fp32 expression in every entry point:
+ *     h = fmaf(exp2(delta * A2), h, (delta * x) * B),   with A2 = A * log2(e) in fp32,
+ * and exp2 is the hardware v_exp_f32.  Tokens are visited in increasing t, one after the
+ * other.  So the state that jscan_prefill returns is bit-identical to the state after L
+ * calls of jscan_step on the same tokens, starting from +0.0.  y accumulates in fp32 and is
+ * rounded to nearest even to the output dtype.
+ *
+ * Layouts.  All arrays are row-major with the last index contiguous:
+ *     x, delta, y : [batch][L][D]      B, C : [batch][L][N]
+ *     A           : [D][N] fp32        h0, h, h_final : [batch][D][N] fp32
+ * x, delta, B, C and y share one dtype (jscan_dtype).
+ *
+ * Ownership and execution.  Every array pointer is a DEVICE pointer that the caller
+ * allocates, owns and frees.  The library allocates no memory, keeps no state between
+ * calls and never synchronises.  Work is enqueued on `stream` (a hipStream_t; NULL means
+ * the default stream), and results are valid once that stream has been synchronised.
+ * Calls on different streams may run from different host threads.
+ *
+ * Errors.  Arguments are checked before anything is launched.  On any error nothing is
+ * launched and no output is touched.
+ *     JSCAN_ERR_NULL   a required pointer is NULL
+ *     JSCAN_ERR_SHAPE  negative sizes, N != 16, D not a multiple of 8, a row stride
+ *                      shorter than its row or not a multiple of 8
+ *     JSCAN_ERR_DTYPE  unknown dtype
+ *     JSCAN_ERR_ALIGN  an array pointer not 16-byte aligned
+ *     JSCAN_ERR_ALIAS  an output overlaps an input or another output (the exceptions are
+ *                      the in-place state of jscan_step, and h0 == h_final exactly for
+ *                      jscan_prefill_resume)
+ *     JSCAN_ERR_HIP    the launch failed; jscan_last_hip_error() gives the hipError_t
+ * Faults inside a kernel surface at the caller's next synchronisation.  A is not
+ * range-checked.  With delta >= 0 and A <= 0 the decay lies in (0, 1] and the recurrence
+ * is stable; other values may overflow.  Zero-sized work (batch == 0 or D == 0) returns
+ * JSCAN_OK without touching anything.
+ */
+#ifndef JSCAN_H
+#define JSCAN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    JSCAN_OK = 0,
+    JSCAN_ERR_NULL = 1,
+    JSCAN_ERR_SHAPE = 2,
+    JSCAN_ERR_DTYPE = 3,
+    JSCAN_ERR_ALIGN = 4,
+    JSCAN_ERR_ALIAS = 5,
+    JSCAN_ERR_HIP = 6
+} jscan_status;
+
+/* dtype of x, delta, B, C and y.  A and every state are always fp32. */
+typedef enum { JSCAN_F32 = 0, JSCAN_BF16 = 1 } jscan_dtype;
+
+#define JSCAN_D_STATE 16
+
+/*
+ * Prefill: scan L tokens from the zero state.  Writes y for every token and the state after
+ * the last token.
+ *   x, delta [batch][L][D]   inputs (delta is used as given: no softplus or bias is applied)
+ *   A        [D][N]          fp32 diagonal of A
+ *   B, C     [batch][L][N]   inputs
+ *   y        [batch][L][D]   output, same dtype as x
+ *   h_final  [batch][D][N]   output fp32 state after token L-1 (zeros when L == 0)
+ * With L == 0, x, delta, B, C and y may be NULL.
+ */
+jscan_status jscan_prefill(const void *x, const void *delta, const float *A, const void *B,
+                           const void *C, void *y, float *h_final, int64_t batch, int64_t L,
+                           int64_t D, int64_t N, jscan_dtype dtype, void *stream);
+
+/*
+ * Prefill from a caller-supplied state h0 [batch][D][N] fp32 instead of zeros.  This resumes
+ * a scan: scanning tokens [0, L1) and then resuming over [L1, L) gives bit-identical y and
+ * h_final to one prefill over [0, L).  h0 may equal h_final (an in-place update of the
+ * state) but must not partly overlap it.  The other arguments are as for jscan_prefill.
+ */
+jscan_status jscan_prefill_resume(const void *x, const void *delta, const float *A,
+                                  const void *B, const void *C, const float *h0, void *y,
+                                  float *h_final, int64_t batch, int64_t L, int64_t D,
+                                  int64_t N, jscan_dtype dtype, void *stream);
+
+/*
+ * Decode step: advance the state by one token, in place, and write that token's output.
+ *   h        [batch][D][N] fp32, read and overwritten with the new state
+ *   x_t, delta_t: batch rows of D values; row b starts at element b * ld_xd
+ *   A        [D][N] fp32
+ *   B_t, C_t: batch rows of N values; row b starts at element b * ld_bc
+ *   y_t      batch rows of D values, row stride ld_xd, same dtype as x_t
+ * The strides let a caller pass token t of prefill-layout tensors without a copy
+ * (x + t*D with ld_xd = L*D, B + t*N with ld_bc = L*N).  ld_xd >= D, ld_bc >= N, and
+ * both must be multiples of 8.
+ */
+jscan_status jscan_step(float *h, const void *x_t, const void *delta_t, const float *A,
+                        const void *B_t, const void *C_t, void *y_t, int64_t batch, int64_t D,
+                        int64_t N, int64_t ld_xd, int64_t ld_bc, jscan_dtype dtype,
+                        void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *jscan_status_string(jscan_status s);
+
+/* hipError_t behind the last JSCAN_ERR_HIP returned on the calling thread (0 if none). */
+int jscan_last_hip_error(void);
+
+/* Library ABI version: 100 * major + minor. */
+int jscan_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JSCAN_H */

@@ -1,0 +1,149 @@
+"""ctypes binding of libjscan (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libjscan.so")
+
+D_STATE = 16
+JSCAN_F32, JSCAN_BF16 = 0, 1
+_DTYPES = {torch.float32: JSCAN_F32, torch.bfloat16: JSCAN_BF16}
+_lib = None
+
+
+class JScanError(RuntimeError):
+    """A libjscan call returned an error status."""
+
+    def __init__(self, status: int, msg: str, hip_error: int = 0):
+        super().__init__(f"libjscan: {msg} (status {status}" + (f", hipError {hip_error})" if hip_error else ")"))
+        self.status = status
+        self.hip_error = hip_error
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def library():
+    """Load libjscan.so (building it first if it is missing) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build
+
+        build.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, fp, i64, i32 = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.jscan_prefill.argtypes = [vp, vp, fp, vp, vp, vp, fp, i64, i64, i64, i64, i32, vp]
+    lib.jscan_prefill_resume.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, i32, vp]
+    lib.jscan_step.argtypes = [fp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+    for f in (lib.jscan_prefill, lib.jscan_prefill_resume, lib.jscan_step):
+        f.restype = i32
+    lib.jscan_status_string.argtypes = [i32]
+    lib.jscan_status_string.restype = ctypes.c_char_p
+    lib.jscan_last_hip_error.restype = i32
+    lib.jscan_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = library()
+        raise JScanError(status, lib.jscan_status_string(status).decode(), lib.jscan_last_hip_error())
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _require(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def prefill(x, delta, A, B, C, h0=None, y=None, h_final=None):
+    """Scan ``L`` tokens.  x, delta ``[batch, L, D]``, B, C ``[batch, L, 16]`` (bf16 or fp32, one
+    dtype), A ``[D, 16]`` fp32, optional h0 ``[batch, D, 16]`` fp32 to resume from.
+    Returns ``(y [batch, L, D] in the input dtype, h_final [batch, D, 16] fp32)``.
+    ``h_final`` may be passed as ``h0`` itself to update a state in place."""
+    _require(x.is_cuda, "inputs must be CUDA (HIP) tensors")
+    _require(x.dtype in _DTYPES, "x must be bfloat16 or float32")
+    _require(x.dim() == 3, "x must be [batch, L, D]")
+    batch, L, D = x.shape
+    for name, t, shape, dt in (("delta", delta, (batch, L, D), x.dtype), ("A", A, (D, D_STATE), torch.float32),
+                               ("B", B, (batch, L, D_STATE), x.dtype), ("C", C, (batch, L, D_STATE), x.dtype)):
+        _require(tuple(t.shape) == shape, f"{name} must have shape {shape}, got {tuple(t.shape)}")
+        _require(t.dtype == dt, f"{name} must be {dt}")
+        _require(t.device == x.device, f"{name} is on another device")
+        _require(t.is_contiguous(), f"{name} must be contiguous")
+    _require(x.is_contiguous(), "x must be contiguous")
+    if h0 is not None:
+        _require(tuple(h0.shape) == (batch, D, D_STATE) and h0.dtype == torch.float32 and h0.is_contiguous()
+                 and h0.device == x.device, "h0 must be a contiguous fp32 [batch, D, 16] tensor on x's device")
+    if y is None:
+        y = torch.empty_like(x)
+    if h_final is None:
+        h_final = torch.empty((batch, D, D_STATE), dtype=torch.float32, device=x.device)
+    lib = library()
+    args_tail = (ctypes.c_void_p(y.data_ptr()), ctypes.c_void_p(h_final.data_ptr()), batch, L, D, D_STATE,
+                 _DTYPES[x.dtype], _stream(x.device))
+    with torch.cuda.device(x.device):
+        if h0 is None:
+            st = lib.jscan_prefill(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), *args_tail)
+        else:
+            st = lib.jscan_prefill_resume(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(h0), *args_tail)
+    _check(st)
+    return y, h_final
+
+
+def step_raw(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, dtype):
+    """Direct call of ``jscan_step`` on raw tensors/pointers with explicit row strides (no checks
+    beyond the library's own).  ``x_t`` etc. may be tensors or integer device addresses."""
+    lib = library()
+
+    def p(v):
+        return ctypes.c_void_p(v if isinstance(v, int) else v.data_ptr())
+
+    dev = h.device if hasattr(h, "device") else torch.device("cuda")
+    st = lib.jscan_step(p(h), p(x_t), p(delta_t), p(A), p(B_t), p(C_t), p(y_t), batch, D, D_STATE, ld_xd, ld_bc,
+                        _DTYPES[dtype], _stream(dev))
+    _check(st)
+
+
+def step(h, x_t, delta_t, A, B_t, C_t, y_t=None):
+    """One decode token for a batch: h ``[batch, D, 16]`` fp32 is updated in place; x_t, delta_t
+    ``[batch, D]`` and B_t, C_t ``[batch, 16]`` (rows may be strided views of prefill tensors,
+    e.g. ``x[:, t]``).  Returns y_t ``[batch, D]``."""
+    _require(h.is_cuda and h.dtype == torch.float32 and h.dim() == 3 and h.shape[2] == D_STATE and h.is_contiguous(),
+             "h must be a contiguous fp32 [batch, D, 16] CUDA tensor")
+    batch, D, _ = h.shape
+    _require(x_t.dtype in _DTYPES, "x_t must be bfloat16 or float32")
+    for name, t, shape in (("x_t", x_t, (batch, D)), ("delta_t", delta_t, (batch, D)),
+                           ("B_t", B_t, (batch, D_STATE)), ("C_t", C_t, (batch, D_STATE))):
+        _require(tuple(t.shape) == shape, f"{name} must have shape {shape}")
+        _require(t.dtype == x_t.dtype, f"{name} must be {x_t.dtype}")
+        _require(t.stride(1) == 1, f"{name} rows must be contiguous")
+        _require(t.device == h.device, f"{name} is on another device")
+    _require(A.dtype == torch.float32 and tuple(A.shape) == (D, D_STATE) and A.is_contiguous(), "A must be fp32 [D,16]")
+    ld_xd = x_t.stride(0) if batch > 1 else D
+    _require(batch <= 1 or delta_t.stride(0) == ld_xd, "x_t and delta_t must share a row stride")
+    ld_bc = B_t.stride(0) if batch > 1 else D_STATE
+    _require(batch <= 1 or C_t.stride(0) == ld_bc, "B_t and C_t must share a row stride")
+    if y_t is None:
+        # y_t rows share x_t's row stride in the ABI
+        y_t = torch.empty((batch, ld_xd), dtype=x_t.dtype, device=h.device)[:, :D]
+    _require(tuple(y_t.shape) == (batch, D) and y_t.dtype == x_t.dtype and y_t.stride(1) == 1
+             and (batch <= 1 or y_t.stride(0) == ld_xd), "y_t must be [batch, D] with x_t's row stride")
+    with torch.cuda.device(h.device):
+        step_raw(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, x_t.dtype)
+    return y_t

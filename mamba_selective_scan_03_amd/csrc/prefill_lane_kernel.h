@@ -1,0 +1,62 @@
+// prefill_lane_kernel.h - the general prefill: one lane per (batch row, channel), all 16
+// states of the channel in registers, tokens walked one after the other.
+//
+// It handles every shape the ABI accepts.  A workgroup is one wave of 64 consecutive
+// channels of one batch row, so the token's B_t and C_t rows are the same for the whole
+// wave and are fetched once per wave through the scalar cache; x and delta are read as one
+// coalesced row segment per token.  Its parallelism is batch * D lanes, so it fills the chip
+// only when batch * D is large (for example batched prefill); long single sequences use
+// the row-mapped kernel instead.
+#pragma once
+
+#include "scan_update.h"
+
+namespace jscan {
+
+template <typename E>
+__global__ __launch_bounds__(64) void prefill_lane_kernel(
+    const typename E::store_t *__restrict__ x, const typename E::store_t *__restrict__ dl,
+    const float *__restrict__ A, const typename E::store_t *__restrict__ B,
+    const typename E::store_t *__restrict__ C, const float *__restrict__ h0,
+    typename E::store_t *__restrict__ y, float *__restrict__ h_final, int64_t L, int D,
+    int blocks_per_row) {
+    const int b = blockIdx.x / blocks_per_row;
+    const int d = (blockIdx.x - b * blocks_per_row) * 64 + threadIdx.x;
+    if (d >= D) return;  // no cross-lane work below, so idle lanes may leave
+
+    float a2[kDState], h[kDState];
+#pragma unroll
+    for (int n = 0; n < kDState; ++n) {
+        a2[n] = scaled_A(A[(int64_t)d * kDState + n]);
+        h[n] = h0 ? h0[((int64_t)b * D + d) * kDState + n] : 0.0f;
+    }
+    const int64_t row = (int64_t)b * L;
+    const typename E::store_t *xr = x + row * D + d;
+    const typename E::store_t *dr = dl + row * D + d;
+    typename E::store_t *yr = y + row * D + d;
+    const typename E::store_t *Br = B + row * kDState;
+    const typename E::store_t *Cr = C + row * kDState;
+
+    for (int64_t t = 0; t < L; ++t) {
+        const float xv = E::load(xr + t * D), dv = E::load(dr + t * D);
+        const float dx = delta_x(dv, xv);
+        float acc = 0.0f;
+#pragma unroll
+        for (int n = 0; n < kDState; ++n) {
+            h[n] = advance(h[n], dv, a2[n], dx, E::load(Br + t * kDState + n));
+            acc = __builtin_fmaf(E::load(Cr + t * kDState + n), h[n], acc);
+        }
+        E::store(yr + t * D, acc);
+    }
+#pragma unroll
+    for (int n = 0; n < kDState; ++n) h_final[((int64_t)b * D + d) * kDState + n] = h[n];
+}
+
+// Fills the final state when there are no tokens: copies h0, or writes zeros.
+__global__ __launch_bounds__(256) void copy_state_kernel(const float *__restrict__ h0,
+                                                         float *__restrict__ h_final, int64_t count) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < count) h_final[i] = h0 ? h0[i] : 0.0f;
+}
+
+}  // namespace jscan

@@ -1,0 +1,66 @@
+// scan_update.h - the one definition of how a state element advances by one token.
+//
+// Every kernel of the library (prefill, resume, decode step) advances state elements only
+// through `advance()` below, so they all compute bit-identical fp32 states for the same
+// tokens.  That is what lets a prefill's final state equal, bit for bit, the state after
+// the same tokens fed one at a time through the decode step.
+//
+// The recurrence is the S6 equation of the Jamba notes page ("Jamba: A Hybrid
+// Transformer-Mamba Language Model", section "Mamba layer"):
+//     h_t = Abar_t h_{t-1} + Bbar_t x_t,   Abar_t = exp(delta_t A),   Bbar_t x_t = delta_t B_t x_t
+// with A real and diagonal (lesson page "Jamba - Hybrid SSM-Transformer", section "Mamba-3").
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jscan {
+
+constexpr int kDState = 16;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// A2 = A * log2(e), rounded once to fp32, so that exp(delta * A) = 2^(delta * A2).
+__device__ __forceinline__ float scaled_A(float a) { return a * kLog2e; }
+
+// The decay Abar = exp(delta * A), evaluated by the hardware base-2 exponential (v_exp_f32).
+__device__ __forceinline__ float decay(float delta, float a2) {
+    return __builtin_amdgcn_exp2f(delta * a2);
+}
+
+// The fp32 product delta * x, shared by the 16 states of one channel.
+__device__ __forceinline__ float delta_x(float delta, float x) { return delta * x; }
+
+// One state element advanced by one token:  h <- Abar * h + (delta * x) * B.
+__device__ __forceinline__ float advance(float h, float delta, float a2, float dx, float b) {
+    return __builtin_fmaf(decay(delta, a2), h, dx * b);
+}
+
+// ---- element formats -------------------------------------------------------------------
+
+// bf16 -> fp32 is exact: the 16 stored bits are the high half of the fp32 pattern.
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even (the hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    __bf16 b = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// Storage traits: F32 stores float, BF16 stores the 16-bit pattern.
+struct F32 {
+    using store_t = float;
+    static __device__ __forceinline__ float load(const store_t *p) { return *p; }
+    static __device__ __forceinline__ void store(store_t *p, float v) { *p = v; }
+};
+struct BF16 {
+    using store_t = uint16_t;
+    static __device__ __forceinline__ float load(const store_t *p) { return bf16_bits_to_f32(*p); }
+    static __device__ __forceinline__ void store(store_t *p, float v) { *p = f32_to_bf16_bits(v); }
+};
+
+}  // namespace jscan

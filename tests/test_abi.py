@@ -1,0 +1,115 @@
+"""The C ABI loads, exports every symbol declared in include/jscan.h and rejects bad
+arguments before touching the GPU (pointers below are never dereferenced: every call
+fails validation first).  CPU only."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import mamba_selective_scan_03_amd as jscan
+from mamba_selective_scan_03_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, ENULL, ESHAPE, EDTYPE, EALIGN, EALIAS, EHIP = range(7)
+F32, BF16 = 0, 1
+P = 0x10000000  # a 16-byte aligned address that is never dereferenced
+
+
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "jscan.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(jscan_\w+)\s*\(", text, re.M)))
+
+
+def test_header_symbols_are_exported():
+    lib = jscan.library()
+    names = header_symbols()
+    assert {"jscan_prefill", "jscan_prefill_resume", "jscan_step", "jscan_status_string",
+            "jscan_last_hip_error", "jscan_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    lib = jscan.library()
+    for s in range(7):
+        assert lib.jscan_status_string(s)
+    assert lib.jscan_status_string(99) == b"unknown status"
+    assert lib.jscan_version() == 100
+    assert lib.jscan_last_hip_error() == 0
+
+
+def prefill(x=P, d=P + 0x100000, A=P + 0x200000, B=P + 0x300000, C=P + 0x400000, y=P + 0x500000,
+            h=P + 0x600000, batch=1, L=64, D=64, N=16, dtype=BF16):
+    return jscan.library().jscan_prefill(x, d, A, B, C, y, h, batch, L, D, N, dtype, None)
+
+
+def resume(h0, h=P + 0x600000, **kw):
+    lib = jscan.library()
+    return lib.jscan_prefill_resume(P, P + 0x100000, P + 0x200000, P + 0x300000, P + 0x400000, h0,
+                                    P + 0x500000, h, kw.get("batch", 1), kw.get("L", 64), kw.get("D", 64), 16,
+                                    BF16, None)
+
+
+def step(h=P, x=P + 0x100000, d=P + 0x200000, A=P + 0x300000, B=P + 0x400000, C=P + 0x500000,
+         y=P + 0x600000, batch=2, D=64, N=16, ld_xd=64, ld_bc=16, dtype=BF16):
+    return jscan.library().jscan_step(h, x, d, A, B, C, y, batch, D, N, ld_xd, ld_bc, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), EDTYPE), (dict(N=8), ESHAPE), (dict(D=60), ESHAPE), (dict(L=-1), ESHAPE),
+    (dict(batch=-2), ESHAPE), (dict(x=None), ENULL), (dict(h=None), ENULL), (dict(A=None), ENULL),
+    (dict(C=None), ENULL), (dict(y=P + 0x500008), EALIGN), (dict(B=P + 0x300002), EALIGN),
+    (dict(y=P + 0x100000), EALIAS), (dict(h=P + 0x200000), EALIAS), (dict(h=P + 0x500000 + 64 * 64 * 2 - 16), EALIAS),
+])
+def test_prefill_validation(kw, code):
+    assert prefill(**kw) == code
+
+
+def test_prefill_zero_sized_is_a_no_op():
+    assert prefill(batch=0, x=None, y=None, h=None, A=None) == OK
+    assert prefill(D=0, x=None, y=None, h=None, A=None) == OK
+
+
+def test_prefill_empty_sequence_needs_no_token_arrays():
+    # L == 0 writes only h_final; the validation accepts NULL token arrays (the launch itself
+    # would need a GPU, so only a failing variant is called here)
+    assert prefill(L=0, x=None, d=None, B=None, C=None, y=None, A=None) == ENULL
+
+
+def test_resume_aliasing_rules():
+    assert resume(None) == ENULL
+    assert resume(P + 0x600000 + 16) == EALIAS          # partial overlap with h_final
+    assert resume(P + 0x500000) == EALIAS               # overlaps y
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), EDTYPE), (dict(N=17), ESHAPE), (dict(D=12), ESHAPE), (dict(ld_xd=32), ESHAPE),
+    (dict(ld_bc=8), ESHAPE), (dict(ld_xd=68), ESHAPE), (dict(h=None), ENULL), (dict(B=None), ENULL),
+    (dict(x=P + 0x100004), EALIGN), (dict(y=P + 0x100000), EALIAS), (dict(y=P + 64 * 16 * 4), EALIAS),
+    (dict(h=P + 0x300000 - 64), EALIAS),
+])
+def test_step_validation(kw, code):
+    assert step(**kw) == code
+
+
+def test_binding_refuses_cpu_tensors():
+    x = torch.zeros(1, 8, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        jscan.prefill(x, x, torch.zeros(32, 16), torch.zeros(1, 8, 16, dtype=torch.bfloat16),
+                      torch.zeros(1, 8, 16, dtype=torch.bfloat16))
+
+
+def test_binding_error_type():
+    e = _binding.JScanError(2, "bad shape")
+    assert e.status == 2 and "bad shape" in str(e)
+
+
+def test_library_does_not_reference_the_oracle():
+    lib_src = open(os.path.join(ROOT, "mamba_selective_scan_03_amd", "_binding.py")).read()
+    assert "oracle" not in lib_src
+    for f in os.listdir(os.path.join(ROOT, "mamba_selective_scan_03_amd", "csrc")):
+        assert "oracle" not in open(os.path.join(ROOT, "mamba_selective_scan_03_amd", "csrc", f)).read().lower()
+    syms = open(jscan.library_path(), "rb").read()
+    assert b"oracle_prefill" not in syms
