@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective-scan hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_64k]
+
+One step is one full pass of the hot path over one batch: a jscan_prefill of the whole
+sequence (prefill workloads) or one decode token through all layers (decode workload).
+Inputs are generated once, moved to HBM, and stay resident; the timed region holds only
+the library's kernels, bracketed by stream synchronisation and timed with HIP events on
+the stream the kernels run on.  Prints exactly one JSON line.
+
+The roofline of the prefill kernel is its VALU issue rate, not HBM: each state element
+needs 5 fp32 instructions (the exponent product, the base-2 exponential, the input
+product and two fused multiply-adds), and the exponential issues at half rate, so
+6 issue slots per element is the floor.  The chip issues 256 CUs x 4 SIMDs x 16 lanes x
+2.4 GHz = 3.93e13 lane-slots/s, hence at most 6.55e12 state elements/s.  In flops the
+five instructions are 7 operations (each FMA counts 2), so the same bound reads
+45.9 TFLOP/s.  HBM traffic (about 6 bytes per B*L*D element in bf16) is reported beside
+it as GB/s and as a fraction of 8 TB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "selective-scan elems/s (B·L·D) + HBM GB/s % of peak, L=64K D=8192 N=16"
+HBM_PEAK_GBPS = 8000.0
+VALU_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9      # fp32 lane-instructions per second (no packed math)
+SLOTS_PER_STATE_ELEM = 6                      # mul, exp (2 slots), mul, fma, fma
+FLOPS_PER_STATE_ELEM = 7                      # mul 1 + exp 1 + mul 1 + fma 2 + fma 2
+PEAK_STATE_ELEMS = VALU_SLOTS_PER_S / SLOTS_PER_STATE_ELEM
+KERNEL_SOURCES = ["scan_update.h", "prefill_rows_kernel.h", "prefill_lane_kernel.h", "step_kernel.h", "jscan.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mamba_selective_scan_03_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(wl) -> int:
+    es = 4 if wl.dtype == "f32" else 2
+    if wl.layers > 1:  # decode: state read + write, token rows in and out, A, per layer
+        per_layer = 2 * wl.batch * wl.D * wl.N * 4 + 3 * wl.batch * wl.D * es + 2 * wl.batch * wl.N * es + wl.D * wl.N * 4
+        return per_layer * wl.layers
+    return (3 * wl.batch * wl.L * wl.D * es + 2 * wl.batch * wl.L * wl.N * es
+            + wl.D * wl.N * 4 + wl.batch * wl.D * wl.N * 4)
+
+
+def read_traffic(workload: str, launches_per_step: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        m = re.match(r"\s*(\w+)\s*=\s*([0-9.eE+-]+|[0-9a-f]+)\s*$", line)
+        if m:
+            vals[m.group(1)] = m.group(2)
+    if vals.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, inp, channels: int):
+    """The fp64 oracle, as it stands, on a bounded sample: all tokens of `channels` channels."""
+    import numpy as np
+
+    import oracle
+
+    threads = min(16, os.cpu_count() or 1)
+    x = inp["x"][:, :, :channels]
+    dl = inp["delta"][:, :, :channels]
+    A = inp["A"][:channels]
+    args = [np.ascontiguousarray(t.float().numpy(), dtype=np.float64) for t in (x, dl, A, inp["B"], inp["C"])]
+    t0 = time.perf_counter()
+    oracle.prefill(*args, nthreads=threads)
+    dt = time.perf_counter() - t0
+    elems = wl.batch * wl.L * channels
+    return {"value": elems / dt, "unit": "elems/s", "cores": threads, "kind": "oracle",
+            "sample": f"{wl.name}: batch {wl.batch}, all {wl.L} tokens, first {channels} of {wl.D} channels, "
+                      f"N {wl.N}, fp64 ({dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_64k",
+                    choices=["prefill_64k", "prefill_4k", "prefill_256k", "decode_256x28", "tiny_fp32"])
+    ap.add_argument("--cpu-channels", type=int, default=2048, help="oracle sample width (0 = skip)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the scan, time a plain device-to-device copy of MIB mebibytes (the reference "
+                         "kernel for scaling the profiler's FETCH_SIZE / WRITE_SIZE counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; the scan's multi-GPU sharding is a design note, "
+              "not an implemented path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mamba_selective_scan_03_amd as jscan
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        c1.record()
+        torch.cuda.synchronize()
+        ms = c0.elapsed_time(c1) / args.steps
+        print(json.dumps({"calibration": "copy", "bytes_read_per_launch": n * 4, "bytes_written_per_launch": n * 4,
+                          "ms_per_launch": ms, "GBps": 2 * n * 4 / ms / 1e6}), flush=True)
+        return
+    wl = workloads.get(args.workload)
+    torch.cuda.set_device(dev)
+    log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)  # noqa: E731
+
+    t0 = time.perf_counter()
+    if wl.layers > 1:
+        layers = []
+        for layer in range(wl.layers):
+            inp = workloads.decode_layer_inputs(wl, layer)
+            layers.append({k: v.to(dev) for k, v in inp.items()})
+            layers[-1]["h"] = layers[-1].pop("h0")
+
+        def one_step():
+            for L_ in layers:
+                jscan.step(L_["h"], L_["x"], L_["delta"], L_["A"], L_["B"], L_["C"], y_t=L_.setdefault(
+                    "y", torch.empty_like(L_["x"])))
+        launches = wl.layers
+        host_inp = None
+    else:
+        host_inp = workloads.prefill_inputs(wl)
+        d = {k: v.to(dev) for k, v in host_inp.items()}
+        y = torch.empty_like(d["x"])
+        h = torch.empty((wl.batch, wl.D, wl.N), dtype=torch.float32, device=dev)
+
+        def one_step():
+            jscan.prefill(d["x"], d["delta"], d["A"], d["B"], d["C"], y=y, h_final=h)
+        launches = 1
+    torch.cuda.synchronize()
+    log(f"inputs for {wl.name} resident in HBM ({time.perf_counter() - t0:.1f} s)")
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+    log(f"{args.steps} steps: {ms_total:.3f} ms by HIP events, {wall * 1e3:.3f} ms wall")
+
+    elems = wl.elems
+    value = elems / (ms_step * 1e-3)
+    alg_bytes = algorithmic_bytes(wl)
+    gbps = alg_bytes / (ms_step * 1e-3) / 1e9
+    per_launch_ms = ms_step / launches
+    if wl.layers > 1:
+        roofline = {"bound": "hbm", "achieved": round(alg_bytes / launches / (per_launch_ms * 1e-3) / 1e9, 1),
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
+        roofline["frac"] = round(roofline["achieved"] / HBM_PEAK_GBPS, 4)
+    else:
+        state_elems = elems * wl.N
+        achieved_tf = state_elems * FLOPS_PER_STATE_ELEM / (per_launch_ms * 1e-3) / 1e12
+        peak_tf = PEAK_STATE_ELEMS * FLOPS_PER_STATE_ELEM / 1e12
+        roofline = {"bound": "alu", "achieved": round(achieved_tf, 2), "peak": round(peak_tf, 2), "unit": "TFLOP/s",
+                    "frac": round(achieved_tf / peak_tf, 4)}
+    roofline["traffic"] = read_traffic(wl.name, launches)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "elems/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "L": wl.L, "D": wl.D, "N": wl.N,
+                   "layers": wl.layers, "io_dtype": wl.dtype, "state_dtype": "f32"},
+        "hbm_GBps": round(gbps, 1),
+        "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": alg_bytes,
+        "roofline": roofline,
+    }
+    if host_inp is not None and args.cpu_channels > 0 and wl.layers == 1:
+        out["cpu_baseline"] = cpu_baseline(wl, host_inp, min(args.cpu_channels, wl.D))
+        log(f"oracle sample: {out['cpu_baseline']['sample']}")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

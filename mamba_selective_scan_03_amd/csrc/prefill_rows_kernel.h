@@ -21,9 +21,11 @@
 //     stages), then 2 waves through LDS.  The last stage is fused with the bf16 conversion
 //     and a coalesced row store.
 //
-// Pipeline.  Tokens go in tiles of 64.  While tile k is computed, tile k+1 sits in LDS
-// (converted) and tile k+2 is in flight from HBM into registers.  One workgroup barrier per
-// tile orders the double-buffered LDS tiles and the double-buffered y exchange buffer.
+// Pipeline.  Tokens go in tiles of 64.  While tile k is scanned, tile k+1 is converted from
+// registers into LDS and tiles k+2 and k+3 are in flight from HBM into two register sets,
+// so every HBM load has two tiles of work to arrive.  One workgroup barrier per tile orders
+// the double-buffered LDS tiles and the double-buffered y exchange buffer; the staging, the
+// HBM requests and the previous tile's y stores are spread into the scan of the first group.
 // A ragged last tile is padded with identity tokens (delta = 0, x = -0, B = C = 0): they
 // leave every state bit-identical (decay 2^0 = 1, input term -0) and their y is not stored.
 #pragma once
@@ -36,10 +38,13 @@ namespace rows {
 constexpr int kT = 64;          // tokens per tile
 constexpr int kCh = 32;         // channels per workgroup
 constexpr int kThreads = 256;   // 4 waves
-constexpr int kBcStride = kT + 8;   // LDS row length of the [n][token] B/C tiles (bank spread)
-constexpr int kYStride = kCh + 8;   // LDS row length of the [token][channel] y exchange
-// LDS (floats): delta*x/delta pairs [kT/2][kCh][4], B and C [16][kBcStride], y [2][kT][kYStride]
-constexpr int kDxSize = kT / 2 * kCh * 4;
+// LDS row lengths, padded so that the accesses of a wave spread over all banks:
+constexpr int kDxStride = (kCh + 1) * 4;   // [token pair][channel][4]: +1 float4 per pair row
+constexpr int kBcStride = kT + 8;          // [state][token] B and C tiles
+constexpr int kYStride = kCh + 16;         // [token][channel] y exchange: the 4 rows of a wave
+                                           // (token offsets 0, 2, 1, 3) land 16 banks apart
+// LDS (floats): delta*x/delta pairs [kT/2][kDxStride], B and C [16][kBcStride], y [2][kT][kYStride]
+constexpr int kDxSize = kT / 2 * kDxStride;
 constexpr int kBcSize = kDState * kBcStride;
 constexpr int kYSize = 2 * kT * kYStride;
 }  // namespace rows
@@ -69,6 +74,10 @@ template <typename E> struct TileRegs {
     typename Vec4<E>::raw bc[2];         // B (threads 0-127) or C (128-255): one token, 8 states
 };
 
+template <int V> struct IntConst {
+    static constexpr int value = V;
+};
+
 // DPP row broadcast of lane k of each 16-lane row (row_newbcast:k).
 template <int k> __device__ __forceinline__ float row_bcast(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + k, 0xF, 0xF, true));
@@ -92,6 +101,21 @@ __device__ __forceinline__ void swap16(float &v, float &w) {
     w = __builtin_bit_cast(float, (unsigned)(q >> 32));
 }
 
+// acc + (lane k's c_tile, broadcast over the row) * h in one v_fmac_f32_dpp: the DPP
+// operand folds into the multiply-add, so the broadcast issues no instruction of its own.
+// The compiler does not fold DPP into v_fmac by itself.  `c_tile` is only ever written by
+// LDS reads, never by a VALU op in the two preceding instructions, so no DPP wait state is
+// needed; the leading s_nop on k == 0 keeps that true even if register allocation moves it.
+template <int k> __device__ __forceinline__ float fmac_bcast(float acc, float c_tile, float h) {
+    if constexpr (k == 0)
+        asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:0 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+            : "+v"(acc) : "v"(c_tile), "v"(h));
+    else
+        asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+            : "+v"(acc) : "v"(c_tile), "v"(h), "i"(k));
+    return acc;
+}
+
 // Sum of four tokens' partials over the 4 rows: returns a register whose row r holds the
 // row-sum of token kRowToken[r] = {0, 2, 1, 3}[r], added as (row0 + row2) + (row1 + row3).
 __device__ __forceinline__ float reduce_rows4(float p0, float p1, float p2, float p3) {
@@ -102,58 +126,172 @@ __device__ __forceinline__ float reduce_rows4(float p0, float p1, float p2, floa
     return u01 + u23;
 }
 
+// Requests one tile's raw inputs.  The loads are unconditional per lane: a load inside a
+// divergent branch makes the compiler wait for it where the branch merges, which would expose
+// the full HBM latency.  Whole tiles take 32-bit lane offsets from a tile base; the last,
+// partial tile re-reads token L-1 for tokens past the end, which staging then replaces by
+// identity tokens.
 template <typename E>
 __device__ __forceinline__ void load_tile(TileRegs<E> &R, const typename E::store_t *xb,
                                           const typename E::store_t *db, const typename E::store_t *bcb,
                                           int64_t t0, int64_t L, int D, int tid) {
-    const int p = tid >> 3, q = tid & 7;  // token pair p, channel quad q
+    const int p = tid >> 3, q = tid & 7;                   // token pair p, channel quad q
+    const int tb = (tid & 127) >> 1, nb = (tid & 1) * 8;  // B/C: one token, 8 states
+    if (t0 + rows::kT <= L) {
+        const typename E::store_t *xt = xb + t0 * D, *dt = db + t0 * D, *bt = bcb + t0 * kDState;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int64_t t = t0 + 2 * p + j;
-        if (t < L) {
+        for (int j = 0; j < 2; ++j) {
+            const int off = (2 * p + j) * D + 4 * q;
+            R.x[j] = Vec4<E>::load(xt + off);
+            R.dl[j] = Vec4<E>::load(dt + off);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) R.bc[j] = Vec4<E>::load(bt + tb * kDState + nb + 4 * j);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t t = min(t0 + 2 * p + j, L - 1);
             R.x[j] = Vec4<E>::load(xb + t * D + 4 * q);
             R.dl[j] = Vec4<E>::load(db + t * D + 4 * q);
-        } else {
-            R.x[j] = Vec4<E>::neg_zero();
-            R.dl[j] = Vec4<E>::zero();
         }
-    }
-    const int tb = (tid & 127) >> 1, nb = (tid & 1) * 8;  // B/C: one token, 8 states
-    const int64_t t = t0 + tb;
+        const int64_t t = min(t0 + tb, L - 1);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-        R.bc[j] = t < L ? Vec4<E>::load(bcb + t * kDState + nb + 4 * j) : Vec4<E>::zero();
+        for (int j = 0; j < 2; ++j) R.bc[j] = Vec4<E>::load(bcb + t * kDState + nb + 4 * j);
+    }
 }
 
-template <typename E>
-__device__ __forceinline__ void stage_tile(const TileRegs<E> &R, float *dx_s, float *bc_s, int tid) {
+// Converts one quarter of a tile from registers into LDS: channel 4q + part of this thread's
+// (delta*x, delta) fp32 pairs, and states nb + 2*part, nb + 2*part + 1 of its B or C token.
+// Tokens at or past L become identity tokens (delta = 0, x = -0, B = C = 0).  A tile is staged
+// a quarter per 16-token group so that the LDS writes never pile up behind each other.
+template <typename E, int part>
+__device__ __forceinline__ void stage_part(const TileRegs<E> &R, float *dx_s, float *bc_s, int64_t t0, int64_t L,
+                                           int tid) {
     const int p = tid >> 3, q = tid & 7;
-    float xv[2][4], dv[2][4];
+    float4 v;
+    {
+        float xv[4], dv[4];
+        const bool live0 = t0 + 2 * p < L, live1 = t0 + 2 * p + 1 < L;
+        Vec4<E>::widen(live0 ? R.x[0] : Vec4<E>::neg_zero(), xv);
+        Vec4<E>::widen(live0 ? R.dl[0] : Vec4<E>::zero(), dv);
+        v.x = delta_x(dv[part], xv[part]);
+        v.y = dv[part];
+        Vec4<E>::widen(live1 ? R.x[1] : Vec4<E>::neg_zero(), xv);
+        Vec4<E>::widen(live1 ? R.dl[1] : Vec4<E>::zero(), dv);
+        v.z = delta_x(dv[part], xv[part]);
+        v.w = dv[part];
+    }
+    *reinterpret_cast<float4 *>(dx_s + p * rows::kDxStride + (4 * q + part) * 4) = v;
+    const int tb = (tid & 127) >> 1, nb = (tid & 1) * 8;
+    const bool live = t0 + tb < L;
+    float *dst = bc_s + (tid >= 128 ? rows::kBcSize : 0);
+    float f[4];
+    Vec4<E>::widen(live ? R.bc[part >> 1] : Vec4<E>::zero(), f);
+    dst[(nb + 2 * part) * rows::kBcStride + tb] = f[(2 * part) & 3];
+    dst[(nb + 2 * part + 1) * rows::kBcStride + tb] = f[(2 * part + 1) & 3];
+}
+template <typename E>
+__device__ __forceinline__ void stage_tile(const TileRegs<E> &R, float *dx_s, float *bc_s, int64_t t0, int64_t L,
+                                           int tid) {
+    stage_part<E, 0>(R, dx_s, bc_s, t0, L, tid);
+    stage_part<E, 1>(R, dx_s, bc_s, t0, L, tid);
+    stage_part<E, 2>(R, dx_s, bc_s, t0, L, tid);
+    stage_part<E, 3>(R, dx_s, bc_s, t0, L, tid);
+}
+
+// One 16-token group's LDS operands for one lane: (delta*x, delta) of its channel for the 16
+// tokens, and token (tg + c)'s B and C of the lane's two states (broadcast per token later).
+// They are read in two halves (tokens 0-7 with B and C, then tokens 8-15), each issued half a
+// group ahead of its use: a wave may have at most 15 LDS operations in flight, and larger
+// bursts stall issue until the oldest complete.
+struct GroupRegs {
+    float4 v[8];
+    float b0, b1, c0, c1;
+};
+template <int H>
+__device__ __forceinline__ void load_half(GroupRegs &g, const float *dxs, const float *bcs, int tg, int ch, int n0,
+                                          int c) {
+#pragma unroll
+    for (int i = 4 * H; i < 4 * H + 4; ++i)
+        g.v[i] = *reinterpret_cast<const float4 *>(dxs + ((tg >> 1) + i) * rows::kDxStride + ch * 4);
+    if constexpr (H == 0) {
+        g.b0 = bcs[n0 * rows::kBcStride + tg + c];
+        g.b1 = bcs[(n0 + 1) * rows::kBcStride + tg + c];
+        g.c0 = bcs[rows::kBcSize + n0 * rows::kBcStride + tg + c];
+        g.c1 = bcs[rows::kBcSize + (n0 + 1) * rows::kBcStride + tg + c];
+    }
+}
+
+// One token: advance this lane's two states and return C*h summed over them.
+template <int TAU>
+__device__ __forceinline__ float token_step(const GroupRegs &g, float &h_0, float &h_1, float a2_0, float a2_1) {
+    const float4 v = g.v[TAU >> 1];
+    const float dxv = (TAU & 1) ? v.z : v.x;
+    const float dv = (TAU & 1) ? v.w : v.y;
+    h_0 = advance(h_0, dv, a2_0, dxv, row_bcast<TAU>(g.b0));
+    h_1 = advance(h_1, dv, a2_1, dxv, row_bcast<TAU>(g.b1));
+    return fmac_bcast<TAU>(row_bcast<TAU>(g.c0) * h_0, g.c1, h_1);
+}
+
+// Advance this lane's two states over tokens 8H..8H+7 of a 16-token group and leave their y
+// partials (summed over the wave's 4 rows) in the y exchange rows `ys` (row = token in group).
+template <int H>
+__device__ __forceinline__ void scan_half(const GroupRegs &g, float &h_0, float &h_1, float a2_0, float a2_1, float *ys,
+                                          int rt, int ch) {
+    float P[8];
+#define JSCAN_STEP(i) P[i] = token_step<8 * H + (i)>(g, h_0, h_1, a2_0, a2_1);
+    JSCAN_STEP(0) JSCAN_STEP(1) JSCAN_STEP(2) JSCAN_STEP(3)
+    JSCAN_STEP(4) JSCAN_STEP(5) JSCAN_STEP(6) JSCAN_STEP(7)
+#undef JSCAN_STEP
+    // rows -> one register per 4 tokens; row r holds token 4j + {0,2,1,3}[r]
+    ys[(8 * H + rt) * rows::kYStride + ch] = reduce_rows4(P[0], P[1], P[2], P[3]);
+    ys[(8 * H + 4 + rt) * rows::kYStride + ch] = reduce_rows4(P[4], P[5], P[6], P[7]);
+}
+
+// The last step of y for one tile: this thread's token row t = tid / 4 and 8 channels, as the
+// two state halves' sums read from the exchange buffer.
+struct FinalRegs {
+    float4 u[2], w[2];
+};
+__device__ __forceinline__ void read_final(FinalRegs &F, const float *y_tile, int tid) {
+    const int t = tid >> 2, c8 = (tid & 3) * 8;
+    const float *y0 = y_tile + t * rows::kYStride + c8;
+    const float *y1 = y0 + rows::kT * rows::kYStride;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        Vec4<E>::widen(R.x[j], xv[j]);
-        Vec4<E>::widen(R.dl[j], dv[j]);
+        F.u[j] = *reinterpret_cast<const float4 *>(y0 + 4 * j);
+        F.w[j] = *reinterpret_cast<const float4 *>(y1 + 4 * j);
     }
+}
+template <typename E>
+__device__ __forceinline__ void write_final(const FinalRegs &F, typename E::store_t *yb, int64_t t0, int64_t L, int D,
+                                            int tid) {
+    const int t = tid >> 2, c8 = (tid & 3) * 8;
+    float o[8];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        float4 v;
-        v.x = delta_x(dv[0][c], xv[0][c]);
-        v.y = dv[0][c];
-        v.z = delta_x(dv[1][c], xv[1][c]);
-        v.w = dv[1][c];
-        *reinterpret_cast<float4 *>(dx_s + (p * rows::kCh + 4 * q + c) * 4) = v;
+    for (int j = 0; j < 2; ++j) {
+        o[4 * j] = F.u[j].x + F.w[j].x;
+        o[4 * j + 1] = F.u[j].y + F.w[j].y;
+        o[4 * j + 2] = F.u[j].z + F.w[j].z;
+        o[4 * j + 3] = F.u[j].w + F.w[j].w;
     }
-    const int tb = (tid & 127) >> 1, nb = (tid & 1) * 8;
-    float* dst = bc_s + (tid >= 128 ? rows::kBcSize : 0);
-    float f[8];
-    Vec4<E>::widen(R.bc[0], f);
-    Vec4<E>::widen(R.bc[1], f + 4);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dst[(nb + j) * rows::kBcStride + tb] = f[j];
+    const int64_t tt = t0 + t;
+    if (tt < L) {
+        typename E::store_t *dst = yb + tt * D + c8;
+        if constexpr (sizeof(typename E::store_t) == 2) {
+            uint4 pk;
+            pk.x = pack_bf16x2(o[0], o[1]); pk.y = pack_bf16x2(o[2], o[3]);
+            pk.z = pack_bf16x2(o[4], o[5]); pk.w = pack_bf16x2(o[6], o[7]);
+            *reinterpret_cast<uint4 *>(dst) = pk;
+        } else {
+            *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<float4 *>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+        }
+    }
 }
 
 template <typename E>
-__global__ __launch_bounds__(rows::kThreads, 1) void prefill_rows_kernel(
+__global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_rows_kernel(
     const typename E::store_t *__restrict__ x, const typename E::store_t *__restrict__ dl,
     const float *__restrict__ A, const typename E::store_t *__restrict__ B,
     const typename E::store_t *__restrict__ C, const float *__restrict__ h0,
@@ -194,83 +332,99 @@ __global__ __launch_bounds__(rows::kThreads, 1) void prefill_rows_kernel(
     typename E::store_t *yb = y + row * D + d0;
 
     const int ntiles = (int)((L + rows::kT - 1) / rows::kT);
-    TileRegs<E> R;
-    load_tile<E>(R, xb, db, bcb, 0, L, D, tid);
-    stage_tile<E>(R, dx_s[0], bc_s[0], tid);
-    if (ntiles > 1) load_tile<E>(R, xb, db, bcb, rows::kT, L, D, tid);
-    __syncthreads();
+    const int rt = (r == 1) ? 2 : (r == 2) ? 1 : r;   // token slot of this row after reduce_rows4
 
-    for (int k = 0; k < ntiles; ++k) {
-        const int cur = k & 1, nxt = cur ^ 1;
-        // (a) tile k+1: registers -> LDS;  (b) tile k+2: HBM -> registers
-        if (k + 1 < ntiles) {
-            stage_tile<E>(R, dx_s[nxt], bc_s[nxt], tid);
-            if (k + 2 < ntiles) load_tile<E>(R, xb, db, bcb, (int64_t)(k + 2) * rows::kT, L, D, tid);
-        }
-        // (c) the scan over tile k
-        const float *dxs = dx_s[cur];
-        const float *Bs = bc_s[cur];
-        const float *Cs = bc_s[cur] + rows::kBcSize;
+    // Prologue: tile 0 staged in LDS, tiles 1 and 2 in flight into the two register sets (the
+    // requests are unconditional; past the end they re-read the last token and are never used).
+    TileRegs<E> R[2];
+    load_tile<E>(R[0], xb, db, bcb, 0, L, D, tid);
+    stage_tile<E>(R[0], dx_s[0], bc_s[0], 0, L, tid);
+    // (each tile's requests stay one block in issue order, so the wait before staging a tile
+    // only covers that tile's requests)
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile<E>(R[1], xb, db, bcb, rows::kT, L, D, tid);
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile<E>(R[0], xb, db, bcb, 2 * rows::kT, L, D, tid);
+    __builtin_amdgcn_sched_barrier(0);
+    // Let the prologue's requests land before the loop: the loop then enters with nothing in
+    // flight, and the compiler's wait before each staging covers only the tile being staged
+    // (two tiles old) instead of everything outstanding.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    GroupRegs G[2];
+    load_half<0>(G[0], dx_s[0], bc_s[0], 0, ch, n0, c);
+    load_half<1>(G[0], dx_s[0], bc_s[0], 0, ch, n0, c);
+    FinalRegs F;
+
+    // Per tile k, everything that is not the scan is spread over its eight 8-token halves so that
+    // no half issues more than about ten LDS operations:
+    //   LDS operands are read one group ahead, half by half
+    //   halves 1-2: the previous tile's y halves read, then finished and stored
+    //   halves 2-5: tile k+1 staged from registers into LDS a quarter at a time; after half 5,
+    //               tile k+3 is requested from HBM into the registers just freed
+    // One barrier per tile then publishes tile k+1's LDS operands and tile k's y halves.
+    // The loop runs two tiles per trip so that every buffer index is a compile-time constant
+    // (a run-time index into the register sets would force a wait on the loads in flight).
+#define JSCAN_SB __builtin_amdgcn_sched_barrier(0)
+    auto tile = [&](auto cur_c, int k) {
+        constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
         float *ys = y_s[cur] + sh * rows::kT * rows::kYStride;
-#pragma unroll 1
-        for (int grp = 0; grp < rows::kT / 16; ++grp) {
-            const int tg = grp * 16;
-            // token tg + c of this row's two states; broadcast per token below
-            const float Bt0 = Bs[n0 * rows::kBcStride + tg + c];
-            const float Bt1 = Bs[(n0 + 1) * rows::kBcStride + tg + c];
-            const float Ct0 = Cs[n0 * rows::kBcStride + tg + c];
-            const float Ct1 = Cs[(n0 + 1) * rows::kBcStride + tg + c];
-            float P[16];
-#define JSCAN_TOKEN(TAU)                                                                         \
-    {                                                                                            \
-        const float4 v = *reinterpret_cast<const float4 *>(dxs + (((tg + TAU) >> 1) * rows::kCh + ch) * 4); \
-        const float dxv = ((TAU) & 1) ? v.z : v.x;                                               \
-        const float dv = ((TAU) & 1) ? v.w : v.y;                                                \
-        h_0 = advance(h_0, dv, a2_0, dxv, row_bcast<TAU>(Bt0));                                  \
-        h_1 = advance(h_1, dv, a2_1, dxv, row_bcast<TAU>(Bt1));                                  \
-        P[TAU] = __builtin_fmaf(row_bcast<TAU>(Ct1), h_1, row_bcast<TAU>(Ct0) * h_0);           \
-    }
-            JSCAN_TOKEN(0) JSCAN_TOKEN(1) JSCAN_TOKEN(2) JSCAN_TOKEN(3)
-            JSCAN_TOKEN(4) JSCAN_TOKEN(5) JSCAN_TOKEN(6) JSCAN_TOKEN(7)
-            JSCAN_TOKEN(8) JSCAN_TOKEN(9) JSCAN_TOKEN(10) JSCAN_TOKEN(11)
-            JSCAN_TOKEN(12) JSCAN_TOKEN(13) JSCAN_TOKEN(14) JSCAN_TOKEN(15)
-#undef JSCAN_TOKEN
-            // rows -> one register per 4 tokens; row r holds token 4j + {0,2,1,3}[r]
-            const int rt = (r == 1) ? 2 : (r == 2) ? 1 : r;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float s = reduce_rows4(P[4 * j], P[4 * j + 1], P[4 * j + 2], P[4 * j + 3]);
-                ys[(tg + 4 * j + rt) * rows::kYStride + ch] = s;
-            }
-        }
+        const bool more = k + 1 < ntiles;
+        const int64_t t1 = (int64_t)(k + 1) * rows::kT;
+        const float *dxc = dx_s[cur], *bcc = bc_s[cur];
+        // group 0 (operands in G[0])
+        load_half<0>(G[1], dxc, bcc, 16, ch, n0, c);
+        JSCAN_SB;
+        scan_half<0>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch);
+        JSCAN_SB;
+        load_half<1>(G[1], dxc, bcc, 16, ch, n0, c);
+        if (k > 0) read_final(F, y_s[nxt], tid);
+        JSCAN_SB;
+        scan_half<1>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch);
+        JSCAN_SB;
+        // group 1 (operands in G[1])
+        if (k > 0) write_final<E>(F, yb, (int64_t)(k - 1) * rows::kT, L, D, tid);
+        load_half<0>(G[0], dxc, bcc, 32, ch, n0, c);
+        if (more) stage_part<E, 0>(R[nxt], dx_s[nxt], bc_s[nxt], t1, L, tid);
+        JSCAN_SB;
+        scan_half<0>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch);
+        JSCAN_SB;
+        load_half<1>(G[0], dxc, bcc, 32, ch, n0, c);
+        if (more) stage_part<E, 1>(R[nxt], dx_s[nxt], bc_s[nxt], t1, L, tid);
+        JSCAN_SB;
+        scan_half<1>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch);
+        JSCAN_SB;
+        // group 2 (operands in G[0])
+        load_half<0>(G[1], dxc, bcc, 48, ch, n0, c);
+        if (more) stage_part<E, 2>(R[nxt], dx_s[nxt], bc_s[nxt], t1, L, tid);
+        JSCAN_SB;
+        scan_half<0>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch);
+        JSCAN_SB;
+        load_half<1>(G[1], dxc, bcc, 48, ch, n0, c);
+        if (more) stage_part<E, 3>(R[nxt], dx_s[nxt], bc_s[nxt], t1, L, tid);
+        JSCAN_SB;
+        if (more && k + 3 < ntiles) load_tile<E>(R[nxt], xb, db, bcb, (int64_t)(k + 3) * rows::kT, L, D, tid);
+        JSCAN_SB;
+        scan_half<1>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch);
+        JSCAN_SB;
+        // group 3 (operands in G[1])
+        scan_half<0>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch);
+        JSCAN_SB;
+        scan_half<1>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch);
         __syncthreads();
-        // (d) add the two state halves, round to the output dtype, store coalesced rows
-        {
-            const int t = tid >> 2, c8 = (tid & 3) * 8;
-            const float *y0 = y_s[cur] + t * rows::kYStride + c8;
-            const float *y1 = y0 + rows::kT * rows::kYStride;
-            float o[8];
-#pragma unroll
-            for (int j = 0; j < 8; j += 4) {
-                const float4 u = *reinterpret_cast<const float4 *>(y0 + j);
-                const float4 w = *reinterpret_cast<const float4 *>(y1 + j);
-                o[j] = u.x + w.x; o[j + 1] = u.y + w.y; o[j + 2] = u.z + w.z; o[j + 3] = u.w + w.w;
-            }
-            const int64_t tt = (int64_t)k * rows::kT + t;
-            if (tt < L) {
-                typename E::store_t *dst = yb + tt * D + c8;
-                if constexpr (sizeof(typename E::store_t) == 2) {
-                    uint4 pk;
-                    pk.x = pack_bf16x2(o[0], o[1]); pk.y = pack_bf16x2(o[2], o[3]);
-                    pk.z = pack_bf16x2(o[4], o[5]); pk.w = pack_bf16x2(o[6], o[7]);
-                    *reinterpret_cast<uint4 *>(dst) = pk;
-                } else {
-                    *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
-                    *reinterpret_cast<float4 *>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
-                }
-            }
+        if (more) {
+            load_half<0>(G[0], dx_s[nxt], bc_s[nxt], 0, ch, n0, c);
+            load_half<1>(G[0], dx_s[nxt], bc_s[nxt], 0, ch, n0, c);
         }
+    };
+    for (int k = 0; k < ntiles; k += 2) {
+        tile(IntConst<0>{}, k);
+        if (k + 1 < ntiles) tile(IntConst<1>{}, k + 1);
     }
+#undef JSCAN_SB
+    // the last tile's y
+    read_final(F, y_s[(ntiles - 1) & 1], tid);
+    write_final<E>(F, yb, (int64_t)(ntiles - 1) * rows::kT, L, D, tid);
     *reinterpret_cast<float2 *>(h_final + ((int64_t)b * D + d) * kDState + n0) = make_float2(h_0, h_1);
 }
 
