@@ -103,7 +103,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill_64k",
                     choices=["prefill_64k", "prefill_4k", "prefill_256k", "decode_256x28", "tiny_fp32"])
-    ap.add_argument("--cpu-channels", type=int, default=2048, help="oracle sample width (0 = skip)")
+    ap.add_argument("--cpu-channels", type=int, default=8192,
+                    help="oracle sample: all tokens of the first CPU_CHANNELS channels (default: every channel "
+                         "of the 64K workload, a few seconds on 16 cores; 0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the scan, time a plain device-to-device copy of MIB mebibytes (the reference "
                          "kernel for scaling the profiler's FETCH_SIZE / WRITE_SIZE counters)")
