@@ -37,12 +37,17 @@ VALU_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9      # fp32 lane-instructions per second
 SLOTS_PER_STATE_ELEM = 6                      # mul, exp (2 slots), mul, fma, fma
 FLOPS_PER_STATE_ELEM = 7                      # mul 1 + exp 1 + mul 1 + fma 2 + fma 2
 PEAK_STATE_ELEMS = VALU_SLOTS_PER_S / SLOTS_PER_STATE_ELEM
-KERNEL_SOURCES = ["scan_update.h", "prefill_rows_kernel.h", "prefill_lane_kernel.h", "step_kernel.h", "jscan.hip"]
+KERNEL_SOURCES = {
+    "prefill": ["scan_update.h", "prefill_rows_kernel.h"],
+    "step": ["scan_update.h", "step_kernel.h"],
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kind: str) -> str:
+    """Hash of the sources of one kernel ("prefill" or "step"); a profile summary records it,
+    and its counters count only while the sources are unchanged."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, "mamba_selective_scan_03_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -68,7 +73,8 @@ def read_traffic(workload: str, launches_per_step: int):
         m = re.match(r"\s*(\w+)\s*=\s*([0-9.eE+-]+|[0-9a-f]+)\s*$", line)
         if m:
             vals[m.group(1)] = m.group(2)
-    if vals.get("kernel_source_hash") != kernel_source_hash():
+    kind = "step" if workload.startswith("decode") else "prefill"
+    if vals.get("kernel_source_hash") != kernel_source_hash(kind):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -154,10 +160,26 @@ def main():
             layers.append({k: v.to(dev) for k, v in inp.items()})
             layers[-1]["h"] = layers[-1].pop("h0")
 
-        def one_step():
+        for L_ in layers:
+            L_["y"] = torch.empty_like(L_["x"])
+
+        def token_step():
             for L_ in layers:
-                jscan.step(L_["h"], L_["x"], L_["delta"], L_["A"], L_["B"], L_["C"], y_t=L_.setdefault(
-                    "y", torch.empty_like(L_["x"])))
+                jscan.step(L_["h"], L_["x"], L_["delta"], L_["A"], L_["B"], L_["C"], y_t=L_["y"])
+
+        # One token step is 28 short launches; a captured HIP graph replays them without the
+        # host launch overhead of 28 separate calls.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            token_step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            token_step()
+
+        def one_step():
+            graph.replay()
         launches = wl.layers
         host_inp = None
     else:

@@ -113,11 +113,12 @@ jscan_status launch_step(float *h, const void *x_t, const void *delta_t, const f
                          const void *B_t, const void *C_t, void *y_t, int64_t batch, int64_t D,
                          int64_t ld_xd, int64_t ld_bc, hipStream_t stream) {
     using T = typename E::store_t;
-    const int blocks_per_row = (int)((D * 4 + 255) / 256);
-    hipLaunchKernelGGL(jscan::step_kernel<E>, dim3((unsigned)(batch * blocks_per_row)), dim3(256), 0, stream,
+    const int blocks_per_rows = (int)((D * 4 + 255) / 256);
+    const int64_t row_groups = (batch + jscan::step::kRows - 1) / jscan::step::kRows;
+    hipLaunchKernelGGL(jscan::step_kernel<E>, dim3((unsigned)(row_groups * blocks_per_rows)), dim3(256), 0, stream,
                        h, static_cast<const T *>(x_t), static_cast<const T *>(delta_t), A,
-                       static_cast<const T *>(B_t), static_cast<const T *>(C_t), static_cast<T *>(y_t), (int)D,
-                       blocks_per_row, ld_xd, ld_bc);
+                       static_cast<const T *>(B_t), static_cast<const T *>(C_t), static_cast<T *>(y_t), (int)batch,
+                       (int)D, blocks_per_rows, ld_xd, ld_bc);
     return launch_status();
 }
 

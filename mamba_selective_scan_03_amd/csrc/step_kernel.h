@@ -2,10 +2,12 @@
 // only the previous state and the current token are read; lesson page "Jamba - Hybrid
 // SSM-Transformer", section "SSM on one page").
 //
-// Mapping: one lane per (batch row b, channel d, quad q); the quad's four lanes hold
-// states 4q..4q+3 of the channel, so a wave reads and writes 1 KiB of contiguous state with
-// 16-byte accesses.  The state is read and written exactly once (in place), which makes
-// the kernel HBM-bound: 128 of the ~134 bytes moved per (b, d) are state.
+// Mapping: one lane per (channel d, quad q) and kRows batch rows; the quad's four lanes hold
+// states 4q..4q+3 of the channel, so a wave reads and writes 1 KiB of contiguous state per
+// row with 16-byte accesses.  A lane loads its A quad once for all its rows and has all its
+// rows' state in flight at once.  The state is read and written exactly once (in place), which
+// makes the kernel HBM-bound: 128 of the ~134 bytes moved per (b, d) are state.  On MI355X it
+// runs at the speed of a device-to-device copy of the state.
 // y_t[d] is the sum over the quad: each lane adds its four C*h terms in increasing n, then
 // two DPP quad exchanges add (q0+q1)+(q2+q3); every lane of the quad ends with the same sum.
 #pragma once
@@ -14,6 +16,22 @@
 
 namespace jscan {
 
+namespace step {
+constexpr int kRows = 2;   // batch rows per lane
+}
+
+// Four consecutive B or C values of one row as fp32.
+template <typename E> struct Quad;
+template <> struct Quad<BF16> {
+    static __device__ __forceinline__ float4 load(const uint16_t *p) {
+        const uint2 w = *reinterpret_cast<const uint2 *>(p);
+        return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+    }
+};
+template <> struct Quad<F32> {
+    static __device__ __forceinline__ float4 load(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+};
+
 template <typename E>
 __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ h,
                                                    const typename E::store_t *__restrict__ x,
@@ -21,37 +39,49 @@ __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ h,
                                                    const float *__restrict__ A,
                                                    const typename E::store_t *__restrict__ Bt,
                                                    const typename E::store_t *__restrict__ Ct,
-                                                   typename E::store_t *__restrict__ y, int D,
-                                                   int blocks_per_row, int64_t ld_xd, int64_t ld_bc) {
-    const int b = blockIdx.x / blocks_per_row;
-    const int lane_in_row = (blockIdx.x - b * blocks_per_row) * 256 + threadIdx.x;
+                                                   typename E::store_t *__restrict__ y, int batch, int D,
+                                                   int blocks_per_rows, int64_t ld_xd, int64_t ld_bc) {
+    constexpr int NR = step::kRows;
+    const int rg = blockIdx.x / blocks_per_rows;   // group of NR batch rows
+    const int lane_in_row = (blockIdx.x - rg * blocks_per_rows) * 256 + threadIdx.x;
     if (lane_in_row >= D * 4) return;  // whole quads leave together (D * 4 is a multiple of 4)
     const int d = lane_in_row >> 2, q = lane_in_row & 3;
 
-    float *hp = h + ((int64_t)b * D + d) * kDState + q * 4;
-    const float4 hv = *reinterpret_cast<const float4 *>(hp);
     const float4 av = *reinterpret_cast<const float4 *>(A + (int64_t)d * kDState + q * 4);
-    const float xv = E::load(x + (int64_t)b * ld_xd + d);
-    const float dv = E::load(dl + (int64_t)b * ld_xd + d);
-    const typename E::store_t *bp = Bt + (int64_t)b * ld_bc + q * 4;
-    const typename E::store_t *cp = Ct + (int64_t)b * ld_bc + q * 4;
-
-    const float dx = delta_x(dv, xv);
-    float4 hn;
-    hn.x = advance(hv.x, dv, scaled_A(av.x), dx, E::load(bp + 0));
-    hn.y = advance(hv.y, dv, scaled_A(av.y), dx, E::load(bp + 1));
-    hn.z = advance(hv.z, dv, scaled_A(av.z), dx, E::load(bp + 2));
-    hn.w = advance(hv.w, dv, scaled_A(av.w), dx, E::load(bp + 3));
-    *reinterpret_cast<float4 *>(hp) = hn;
-
-    float p = E::load(cp + 0) * hn.x;
-    p = __builtin_fmaf(E::load(cp + 1), hn.y, p);
-    p = __builtin_fmaf(E::load(cp + 2), hn.z, p);
-    p = __builtin_fmaf(E::load(cp + 3), hn.w, p);
-    // quad_perm [1,0,3,2] then [2,3,0,1]
-    p = p + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, p), 0xB1, 0xF, 0xF, true));
-    p = p + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, p), 0x4E, 0xF, 0xF, true));
-    if (q == 0) E::store(y + (int64_t)b * ld_xd + d, p);
+    const float a0 = scaled_A(av.x), a1 = scaled_A(av.y), a2 = scaled_A(av.z), a3 = scaled_A(av.w);
+    float4 hv[NR], bv[NR], cv[NR];
+    float xv[NR], dv[NR];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        // a missing last row re-reads the row before it and stores nothing
+        const int b = min(rg * NR + j, batch - 1);
+        hv[j] = *reinterpret_cast<const float4 *>(h + ((int64_t)b * D + d) * kDState + q * 4);
+        xv[j] = E::load(x + (int64_t)b * ld_xd + d);
+        dv[j] = E::load(dl + (int64_t)b * ld_xd + d);
+        bv[j] = Quad<E>::load(Bt + (int64_t)b * ld_bc + q * 4);
+        cv[j] = Quad<E>::load(Ct + (int64_t)b * ld_bc + q * 4);
+    }
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        const int b = rg * NR + j;
+        const float dx = delta_x(dv[j], xv[j]);
+        float4 hn;
+        hn.x = advance(hv[j].x, dv[j], a0, dx, bv[j].x);
+        hn.y = advance(hv[j].y, dv[j], a1, dx, bv[j].y);
+        hn.z = advance(hv[j].z, dv[j], a2, dx, bv[j].z);
+        hn.w = advance(hv[j].w, dv[j], a3, dx, bv[j].w);
+        float p = cv[j].x * hn.x;
+        p = __builtin_fmaf(cv[j].y, hn.y, p);
+        p = __builtin_fmaf(cv[j].z, hn.z, p);
+        p = __builtin_fmaf(cv[j].w, hn.w, p);
+        // quad_perm [1,0,3,2] then [2,3,0,1]
+        p = p + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, p), 0xB1, 0xF, 0xF, true));
+        p = p + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, p), 0x4E, 0xF, 0xF, true));
+        if (b < batch) {
+            *reinterpret_cast<float4 *>(h + ((int64_t)b * D + d) * kDState + q * 4) = hn;
+            if (q == 0) E::store(y + (int64_t)b * ld_xd + d, p);
+        }
+    }
 }
 
 }  // namespace jscan

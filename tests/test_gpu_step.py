@@ -101,3 +101,16 @@ def test_step_zero_delta_keeps_state_exactly():
     assert torch.equal(bits(h), bits(h0))
     ref = (B.float()[:, None, :] * h0).sum(-1)
     assert torch.allclose(y.float(), ref, rtol=1e-2, atol=1e-2)
+
+
+@pytest.mark.parametrize("batch", [1, 3, 5])
+def test_step_odd_batches(batch):
+    """Lanes carry two batch rows; an odd batch leaves the last lane one row short."""
+    wl = workloads.Workload("decode_odd", 79, batch, 1, 96, 16, "bf16", True, layers=1)
+    inp = workloads.decode_layer_inputs(wl, 0)
+    d = to_dev(inp)
+    h = d["h0"].clone()
+    y = jscan.step(h, d["x"], d["delta"], d["A"], d["B"], d["C"])
+    y_ref, h_ref = oracle.step(inp["h0"], inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"])
+    assert_parity(f64(y), y_ref, torch.bfloat16, f"odd batch {batch} y")
+    assert_parity(f64(h), h_ref, torch.bfloat16, f"odd batch {batch} h")
