@@ -37,7 +37,8 @@ namespace jscan {
 namespace rows {
 constexpr int kT = 64;          // tokens per tile
 constexpr int kCh = 32;         // channels per workgroup
-constexpr int kThreads = 256;   // 4 waves
+constexpr int kThreads = 512;   // 4 scan waves + 4 helper waves
+constexpr int kHalf = 256;      // threads per role
 // LDS row lengths, padded so that the accesses of a wave spread over all banks:
 constexpr int kDxStride = (kCh + 1) * 4;   // [token pair][channel][4]: +1 float4 per pair row
 constexpr int kBcStride = kT + 8;          // [state][token] B and C tiles
@@ -291,7 +292,7 @@ __device__ __forceinline__ void write_final(const FinalRegs &F, typename E::stor
 }
 
 template <typename E>
-__global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_rows_kernel(
+__global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_rows_kernel(
     const typename E::store_t *__restrict__ x, const typename E::store_t *__restrict__ dl,
     const float *__restrict__ A, const typename E::store_t *__restrict__ B,
     const typename E::store_t *__restrict__ C, const float *__restrict__ h0,
@@ -308,6 +309,48 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
     const int b = wg / blocks_per_row;
     const int d0 = (wg - b * blocks_per_row) * rows::kCh;
 
+    const int64_t row = (int64_t)b * L;
+    const int ntiles = (int)((L + rows::kT - 1) / rows::kT);
+
+    if (threadIdx.x >= rows::kHalf) {
+        // ---------------- helper waves: HBM <-> LDS, never touch the states ----------------
+        // Tile k+1 is converted into LDS while the scan waves work on tile k, and the y halves
+        // of tile k-1 are summed, rounded and stored.  Each tile's raw inputs are requested
+        // two tiles before they are staged.
+        const int tid = threadIdx.x - rows::kHalf;
+        const typename E::store_t *xb = x + row * D + d0;
+        const typename E::store_t *db = dl + row * D + d0;
+        const typename E::store_t *bcb = (tid < 128 ? B : C) + row * kDState;
+        typename E::store_t *yb = y + row * D + d0;
+        TileRegs<E> R[2];
+        load_tile<E>(R[0], xb, db, bcb, 0, L, D, tid);
+        stage_tile<E>(R[0], dx_s[0], bc_s[0], 0, L, tid);
+        load_tile<E>(R[1], xb, db, bcb, rows::kT, L, D, tid);
+        load_tile<E>(R[0], xb, db, bcb, 2 * rows::kT, L, D, tid);
+        __syncthreads();
+        FinalRegs F;
+        auto tile = [&](auto cur_c, int k) {
+            constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
+            if (k + 1 < ntiles) {
+                stage_tile<E>(R[nxt], dx_s[nxt], bc_s[nxt], (int64_t)(k + 1) * rows::kT, L, tid);
+                if (k + 3 < ntiles) load_tile<E>(R[nxt], xb, db, bcb, (int64_t)(k + 3) * rows::kT, L, D, tid);
+            }
+            if (k > 0) {
+                read_final(F, y_s[nxt], tid);
+                write_final<E>(F, yb, (int64_t)(k - 1) * rows::kT, L, D, tid);
+            }
+            __syncthreads();
+        };
+        for (int k = 0; k < ntiles; k += 2) {
+            tile(IntConst<0>{}, k);
+            if (k + 1 < ntiles) tile(IntConst<1>{}, k + 1);
+        }
+        read_final(F, y_s[(ntiles - 1) & 1], tid);
+        write_final<E>(F, yb, (int64_t)(ntiles - 1) * rows::kT, L, D, tid);
+        return;
+    }
+
+    // ---------------- scan waves: the states, token by token ----------------
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int r = lane >> 4, c = lane & 15;
@@ -324,107 +367,59 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
         h_0 = hv.x;
         h_1 = hv.y;
     }
-
-    const int64_t row = (int64_t)b * L;
-    const typename E::store_t *xb = x + row * D + d0;
-    const typename E::store_t *db = dl + row * D + d0;
-    const typename E::store_t *bcb = (tid < 128 ? B : C) + row * kDState;
-    typename E::store_t *yb = y + row * D + d0;
-
-    const int ntiles = (int)((L + rows::kT - 1) / rows::kT);
     const int rt = (r == 1) ? 2 : (r == 2) ? 1 : r;   // token slot of this row after reduce_rows4
-
-    // Prologue: tile 0 staged in LDS, tiles 1 and 2 in flight into the two register sets (the
-    // requests are unconditional; past the end they re-read the last token and are never used).
-    TileRegs<E> R[2];
-    load_tile<E>(R[0], xb, db, bcb, 0, L, D, tid);
-    stage_tile<E>(R[0], dx_s[0], bc_s[0], 0, L, tid);
-    // (each tile's requests stay one block in issue order, so the wait before staging a tile
-    // only covers that tile's requests)
-    __builtin_amdgcn_sched_barrier(0);
-    load_tile<E>(R[1], xb, db, bcb, rows::kT, L, D, tid);
-    __builtin_amdgcn_sched_barrier(0);
-    load_tile<E>(R[0], xb, db, bcb, 2 * rows::kT, L, D, tid);
-    __builtin_amdgcn_sched_barrier(0);
-    // Let the prologue's requests land before the loop: the loop then enters with nothing in
-    // flight, and the compiler's wait before each staging covers only the tile being staged
-    // (two tiles old) instead of everything outstanding.
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    __syncthreads();
+    __syncthreads();   // tile 0 staged by the helper waves
     GroupRegs G[2];
     load_half<0>(G[0], dx_s[0], bc_s[0], 0, ch, n0, c);
     load_half<1>(G[0], dx_s[0], bc_s[0], 0, ch, n0, c);
-    FinalRegs F;
 
-    // Per tile k, everything that is not the scan is spread over its eight 8-token halves so that
-    // no half issues more than about ten LDS operations:
-    //   LDS operands are read one group ahead, half by half
-    //   halves 1-2: the previous tile's y halves read, then finished and stored
-    //   halves 2-5: tile k+1 staged from registers into LDS a quarter at a time; after half 5,
-    //               tile k+3 is requested from HBM into the registers just freed
-    // One barrier per tile then publishes tile k+1's LDS operands and tile k's y halves.
-    // The loop runs two tiles per trip so that every buffer index is a compile-time constant
-    // (a run-time index into the register sets would force a wait on the loads in flight).
+    // Per tile: four 16-token groups, each group's LDS operands read (in two halves) while the
+    // previous group is scanned.  One barrier per tile, shared with the helper waves, orders
+    // the double-buffered LDS tiles and the double-buffered y exchange.  The loop runs two
+    // tiles per trip so that every buffer index is a compile-time constant.
 #define JSCAN_SB __builtin_amdgcn_sched_barrier(0)
     auto tile = [&](auto cur_c, int k) {
         constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
         float *ys = y_s[cur] + sh * rows::kT * rows::kYStride;
-        const bool more = k + 1 < ntiles;
-        const int64_t t1 = (int64_t)(k + 1) * rows::kT;
         const float *dxc = dx_s[cur], *bcc = bc_s[cur];
-        // group 0 (operands in G[0])
         load_half<0>(G[1], dxc, bcc, 16, ch, n0, c);
         JSCAN_SB;
         scan_half<0>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch);
         JSCAN_SB;
         load_half<1>(G[1], dxc, bcc, 16, ch, n0, c);
-        if (k > 0) read_final(F, y_s[nxt], tid);
         JSCAN_SB;
         scan_half<1>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch);
         JSCAN_SB;
-        // group 1 (operands in G[1])
-        if (k > 0) write_final<E>(F, yb, (int64_t)(k - 1) * rows::kT, L, D, tid);
         load_half<0>(G[0], dxc, bcc, 32, ch, n0, c);
-        if (more) stage_part<E, 0>(R[nxt], dx_s[nxt], bc_s[nxt], t1, L, tid);
         JSCAN_SB;
         scan_half<0>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch);
         JSCAN_SB;
         load_half<1>(G[0], dxc, bcc, 32, ch, n0, c);
-        if (more) stage_part<E, 1>(R[nxt], dx_s[nxt], bc_s[nxt], t1, L, tid);
         JSCAN_SB;
         scan_half<1>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch);
         JSCAN_SB;
-        // group 2 (operands in G[0])
         load_half<0>(G[1], dxc, bcc, 48, ch, n0, c);
-        if (more) stage_part<E, 2>(R[nxt], dx_s[nxt], bc_s[nxt], t1, L, tid);
         JSCAN_SB;
         scan_half<0>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch);
         JSCAN_SB;
         load_half<1>(G[1], dxc, bcc, 48, ch, n0, c);
-        if (more) stage_part<E, 3>(R[nxt], dx_s[nxt], bc_s[nxt], t1, L, tid);
-        JSCAN_SB;
-        if (more && k + 3 < ntiles) load_tile<E>(R[nxt], xb, db, bcb, (int64_t)(k + 3) * rows::kT, L, D, tid);
         JSCAN_SB;
         scan_half<1>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch);
         JSCAN_SB;
-        // group 3 (operands in G[1])
         scan_half<0>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch);
         JSCAN_SB;
         scan_half<1>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch);
         __syncthreads();
-        if (more) {
+        if (k + 1 < ntiles) {
             load_half<0>(G[0], dx_s[nxt], bc_s[nxt], 0, ch, n0, c);
             load_half<1>(G[0], dx_s[nxt], bc_s[nxt], 0, ch, n0, c);
         }
     };
+#undef JSCAN_SB
     for (int k = 0; k < ntiles; k += 2) {
         tile(IntConst<0>{}, k);
         if (k + 1 < ntiles) tile(IntConst<1>{}, k + 1);
     }
-#undef JSCAN_SB
-    // the last tile's y
-    read_final(F, y_s[(ntiles - 1) & 1], tid);
-    write_final<E>(F, yb, (int64_t)(ntiles - 1) * rows::kT, L, D, tid);
     *reinterpret_cast<float2 *>(h_final + ((int64_t)b * D + d) * kDState + n0) = make_float2(h_0, h_1);
 }
 
