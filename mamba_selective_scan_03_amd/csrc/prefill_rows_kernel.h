@@ -351,6 +351,9 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
     }
 
     // ---------------- scan waves: the states, token by token ----------------
+    // The scan wave outranks the helper wave sharing its SIMD, so the helper only issues in the
+    // cycles the scan wave leaves idle.
+    __builtin_amdgcn_s_setprio(3);
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int r = lane >> 4, c = lane & 15;
