@@ -108,7 +108,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill_64k",
-                    choices=["prefill_64k", "prefill_4k", "prefill_256k", "decode_256x28", "tiny_fp32"])
+                    choices=["prefill_64k", "prefill_4k", "prefill_256k", "decode_256x28", "tiny_fp32",
+                             "prefill_64k_tp8"])
+    ap.add_argument("--chunked", action="store_true",
+                    help="prefill through the time-parallel jscan_prefill_chunked (automatic segments) instead of "
+                         "the token-by-token jscan_prefill")
     ap.add_argument("--cpu-channels", type=int, default=8192,
                     help="oracle sample: all tokens of the first CPU_CHANNELS channels (default: every channel "
                          "of the 64K workload, a few seconds on 16 cores; 0 = skip)")
@@ -188,9 +192,18 @@ def main():
         y = torch.empty_like(d["x"])
         h = torch.empty((wl.batch, wl.D, wl.N), dtype=torch.float32, device=dev)
 
-        def one_step():
-            jscan.prefill(d["x"], d["delta"], d["A"], d["B"], d["C"], y=y, h_final=h)
-        launches = 1
+        if args.chunked:
+            ws_bytes = jscan.chunked_workspace_bytes(wl.batch, wl.L, wl.D)
+            ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+            log(f"time-parallel prefill: {ws_bytes} bytes of workspace")
+
+            def one_step():
+                jscan.prefill_chunked(d["x"], d["delta"], d["A"], d["B"], d["C"], y=y, h_final=h, workspace=ws)
+            launches = 3 if ws_bytes > 0 else 1
+        else:
+            def one_step():
+                jscan.prefill(d["x"], d["delta"], d["A"], d["B"], d["C"], y=y, h_final=h)
+            launches = 1
     torch.cuda.synchronize()
     log(f"inputs for {wl.name} resident in HBM ({time.perf_counter() - t0:.1f} s)")
 
@@ -215,6 +228,10 @@ def main():
     alg_bytes = algorithmic_bytes(wl)
     gbps = alg_bytes / (ms_step * 1e-3) / 1e9
     per_launch_ms = ms_step / launches
+    if args.chunked:
+        # three launches per step (segment summaries, carry, rescan): the line reports the
+        # whole pass against the one-pass ALU bound
+        per_launch_ms = ms_step
     if wl.layers > 1:
         roofline = {"bound": "hbm", "achieved": round(alg_bytes / launches / (per_launch_ms * 1e-3) / 1e9, 1),
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
@@ -225,7 +242,7 @@ def main():
         peak_tf = PEAK_STATE_ELEMS * FLOPS_PER_STATE_ELEM / 1e12
         roofline = {"bound": "alu", "achieved": round(achieved_tf, 2), "peak": round(peak_tf, 2), "unit": "TFLOP/s",
                     "frac": round(achieved_tf / peak_tf, 4)}
-    roofline["traffic"] = read_traffic(wl.name, launches)
+    roofline["traffic"] = None if args.chunked else read_traffic(wl.name, launches)
 
     out = {
         "metric": METRIC,
@@ -241,7 +258,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "L": wl.L, "D": wl.D, "N": wl.N,
-                   "layers": wl.layers, "io_dtype": wl.dtype, "state_dtype": "f32"},
+                   "layers": wl.layers, "io_dtype": wl.dtype, "state_dtype": "f32",
+                   "path": "time-parallel" if args.chunked else "sequential"},
         "hbm_GBps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": alg_bytes,

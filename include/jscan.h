@@ -46,6 +46,7 @@
  *                      the in-place state of jscan_step, and h0 == h_final exactly for
  *                      jscan_prefill_resume)
  *     JSCAN_ERR_HIP    the launch failed; jscan_last_hip_error() gives the hipError_t
+ *     JSCAN_ERR_WORKSPACE  the workspace passed to jscan_prefill_chunked is too small
  * Faults inside a kernel surface at the caller's next synchronisation.  A is not
  * range-checked.  With delta >= 0 and A <= 0 the decay lies in (0, 1] and the recurrence
  * is stable; other values may overflow.  Zero-sized work (batch == 0 or D == 0) returns
@@ -67,7 +68,8 @@ typedef enum {
     JSCAN_ERR_DTYPE = 3,
     JSCAN_ERR_ALIGN = 4,
     JSCAN_ERR_ALIAS = 5,
-    JSCAN_ERR_HIP = 6
+    JSCAN_ERR_HIP = 6,
+    JSCAN_ERR_WORKSPACE = 7
 } jscan_status;
 
 /* dtype of x, delta, B, C and y.  A and every state are always fp32. */
@@ -101,6 +103,45 @@ jscan_status jscan_prefill_resume(const void *x, const void *delta, const float 
                                   int64_t N, jscan_dtype dtype, void *stream);
 
 /*
+ * Time-parallel prefill, for shapes whose batch * D channels are too few to fill the GPU
+ * (a single sequence of a channel-sharded layer, for example).  Same inputs and outputs as
+ * jscan_prefill_resume (h0 may be NULL for the zero state, and may equal h_final), computed
+ * in three passes over segments of `chunk` tokens:
+ *   1. every segment is scanned from the zero state, giving its end state h_loc[s] and,
+ *      per channel, the sum of its delta values S[s];
+ *   2. the segments' starting states follow in order from h_in[0] = h0 by composing the
+ *      per-segment maps: h_in[s+1] = exp(A * S[s]) * h_in[s] + h_loc[s];
+ *   3. every segment is scanned again from h_in[s], writing y and (last segment) h_final.
+ * Pass 2 rests on the recurrence being affine in h: over a run of tokens the map
+ * h -> exp(delta A) h + delta B x composes to h -> exp(A * sum delta) h + h_loc, where h_loc
+ * is the run's end state from zero (S6 equation, notes page "Jamba: A Hybrid
+ * Transformer-Mamba Language Model", section "Mamba layer").
+ * Rounding: the first segment's y is bit-identical to jscan_prefill_resume's; later
+ * segments start from composed states whose rounding differs from the token-by-token walk,
+ * so their y and h_final agree with it to within fp32 rounding of the composition, not bit
+ * for bit.  Results are deterministic (no atomics; fixed summation orders).
+ *   chunk      tokens per segment; 0 picks a length that fills the GPU.  When it yields a
+ *              single segment the call is exactly jscan_prefill_resume (and needs no
+ *              workspace).
+ *   workspace  device memory of at least jscan_prefill_chunked_workspace(...) bytes,
+ *              16-byte aligned, owned by the caller, not overlapping any other array;
+ *              may be NULL when that size is 0.  Its contents on entry do not matter.
+ * Calls that share a workspace must be ordered on one stream.
+ */
+jscan_status jscan_prefill_chunked(const void *x, const void *delta, const float *A,
+                                   const void *B, const void *C, const float *h0, void *y,
+                                   float *h_final, int64_t batch, int64_t L, int64_t D,
+                                   int64_t N, int64_t chunk, void *workspace,
+                                   int64_t workspace_bytes, jscan_dtype dtype, void *stream);
+
+/*
+ * Workspace bytes jscan_prefill_chunked needs for this shape and chunk (0 when it runs as
+ * a single segment), or -1 if the shape or chunk is invalid.  Host-only; launches nothing.
+ */
+int64_t jscan_prefill_chunked_workspace(int64_t batch, int64_t L, int64_t D, int64_t N,
+                                        int64_t chunk);
+
+/*
  * Decode step: advance the state by one token, in place, and write that token's output.
  *   h        [batch][D][N] fp32, read and overwritten with the new state
  *   x_t, delta_t: batch rows of D values; row b starts at element b * ld_xd
@@ -122,7 +163,7 @@ const char *jscan_status_string(jscan_status s);
 /* hipError_t behind the last JSCAN_ERR_HIP returned on the calling thread (0 if none). */
 int jscan_last_hip_error(void);
 
-/* Library ABI version: 100 * major + minor. */
+/* Library ABI version: 100 * major + minor (101 adds the time-parallel prefill). */
 int jscan_version(void);
 
 #ifdef __cplusplus

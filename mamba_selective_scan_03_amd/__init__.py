@@ -7,13 +7,16 @@ There is no CPU fallback: without the built library every call raises.
     y, h_final = prefill(x, delta, A, B, C)                # scan from the zero state
     y, h_final = prefill(x, delta, A, B, C, h0=h)          # resume from a state
     y_t = step(h, x_t, delta_t, A, B_t, C_t)               # one decode token, h in place
+    y, h_final = prefill_chunked(x, delta, A, B, C)        # time-parallel, for few channels
 """
 from ._binding import (  # noqa: F401
     D_STATE,
     JScanError,
+    chunked_workspace_bytes,
     library,
     library_path,
     prefill,
+    prefill_chunked,
     step,
     step_raw,
 )

@@ -42,7 +42,10 @@ def library():
     lib.jscan_prefill.argtypes = [vp, vp, fp, vp, vp, vp, fp, i64, i64, i64, i64, i32, vp]
     lib.jscan_prefill_resume.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, i32, vp]
     lib.jscan_step.argtypes = [fp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
-    for f in (lib.jscan_prefill, lib.jscan_prefill_resume, lib.jscan_step):
+    lib.jscan_prefill_chunked.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, i64, vp, i64, i32, vp]
+    lib.jscan_prefill_chunked_workspace.argtypes = [i64, i64, i64, i64, i64]
+    lib.jscan_prefill_chunked_workspace.restype = i64
+    for f in (lib.jscan_prefill, lib.jscan_prefill_resume, lib.jscan_step, lib.jscan_prefill_chunked):
         f.restype = i32
     lib.jscan_status_string.argtypes = [i32]
     lib.jscan_status_string.restype = ctypes.c_char_p
@@ -71,11 +74,7 @@ def _require(cond: bool, msg: str):
         raise ValueError(msg)
 
 
-def prefill(x, delta, A, B, C, h0=None, y=None, h_final=None):
-    """Scan ``L`` tokens.  x, delta ``[batch, L, D]``, B, C ``[batch, L, 16]`` (bf16 or fp32, one
-    dtype), A ``[D, 16]`` fp32, optional h0 ``[batch, D, 16]`` fp32 to resume from.
-    Returns ``(y [batch, L, D] in the input dtype, h_final [batch, D, 16] fp32)``.
-    ``h_final`` may be passed as ``h0`` itself to update a state in place."""
+def _check_prefill_args(x, delta, A, B, C, h0):
     _require(x.is_cuda, "inputs must be CUDA (HIP) tensors")
     _require(x.dtype in _DTYPES, "x must be bfloat16 or float32")
     _require(x.dim() == 3, "x must be [batch, L, D]")
@@ -90,6 +89,15 @@ def prefill(x, delta, A, B, C, h0=None, y=None, h_final=None):
     if h0 is not None:
         _require(tuple(h0.shape) == (batch, D, D_STATE) and h0.dtype == torch.float32 and h0.is_contiguous()
                  and h0.device == x.device, "h0 must be a contiguous fp32 [batch, D, 16] tensor on x's device")
+    return batch, L, D
+
+
+def prefill(x, delta, A, B, C, h0=None, y=None, h_final=None):
+    """Scan ``L`` tokens.  x, delta ``[batch, L, D]``, B, C ``[batch, L, 16]`` (bf16 or fp32, one
+    dtype), A ``[D, 16]`` fp32, optional h0 ``[batch, D, 16]`` fp32 to resume from.
+    Returns ``(y [batch, L, D] in the input dtype, h_final [batch, D, 16] fp32)``.
+    ``h_final`` may be passed as ``h0`` itself to update a state in place."""
+    batch, L, D = _check_prefill_args(x, delta, A, B, C, h0)
     if y is None:
         y = torch.empty_like(x)
     if h_final is None:
@@ -102,6 +110,37 @@ def prefill(x, delta, A, B, C, h0=None, y=None, h_final=None):
             st = lib.jscan_prefill(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), *args_tail)
         else:
             st = lib.jscan_prefill_resume(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(h0), *args_tail)
+    _check(st)
+    return y, h_final
+
+
+def chunked_workspace_bytes(batch: int, L: int, D: int, chunk: int = 0) -> int:
+    """Bytes of workspace ``prefill_chunked`` needs (0 when it runs as one segment)."""
+    n = library().jscan_prefill_chunked_workspace(batch, L, D, D_STATE, chunk)
+    if n < 0:
+        raise ValueError(f"invalid shape or chunk: batch={batch} L={L} D={D} chunk={chunk}")
+    return n
+
+
+def prefill_chunked(x, delta, A, B, C, h0=None, y=None, h_final=None, chunk=0, workspace=None):
+    """Time-parallel prefill (``jscan_prefill_chunked``): the same result as :func:`prefill` up
+    to fp32 rounding of the segment composition, for shapes with too few channels to fill
+    the GPU.  ``chunk`` is the segment length in tokens (0 = automatic).  ``workspace`` is a
+    CUDA tensor of at least :func:`chunked_workspace_bytes` bytes; one is allocated if None."""
+    batch, L, D = _check_prefill_args(x, delta, A, B, C, h0)
+    need = chunked_workspace_bytes(batch, L, D, chunk)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if y is None:
+        y = torch.empty_like(x)
+    if h_final is None:
+        h_final = torch.empty((batch, D, D_STATE), dtype=torch.float32, device=x.device)
+    lib = library()
+    with torch.cuda.device(x.device):
+        st = lib.jscan_prefill_chunked(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(h0), _ptr(y),
+                                       _ptr(h_final), batch, L, D, D_STATE, chunk, _ptr(workspace), ws_bytes,
+                                       _DTYPES[x.dtype], _stream(x.device))
     _check(st)
     return y, h_final
 

@@ -7,6 +7,7 @@
 #include "../../include/jscan.h"
 #include "prefill_lane_kernel.h"
 #include "prefill_rows_kernel.h"
+#include "chunk_carry_kernel.h"
 #include "step_kernel.h"
 
 namespace {
@@ -41,45 +42,61 @@ jscan_status launch_status() {
     return JSCAN_OK;
 }
 
-// ---- prefill ---------------------------------------------------------------------------
+// ---- prefill ----------------------------------------------------------------------------
 
-template <typename E>
-jscan_status launch_prefill(const void *x, const void *delta, const float *A, const void *B,
-                            const void *C, const float *h0, void *y, float *h_final,
-                            int64_t batch, int64_t L, int64_t D, hipStream_t stream) {
+// Largest grid the launchers accept (work-group counts and row indices are 32-bit ints).
+constexpr int64_t kMaxBlocks = (int64_t)1 << 30;
+
+// Scans `nrows` rows (see Segments) with the row-mapped kernel when it applies, otherwise
+// with one lane per (row, channel).
+template <typename E, bool kSummary>
+void launch_rows(const void *x, const void *delta, const float *A, const void *B, const void *C, const float *h0,
+                 void *y, float *h_final, float *dsum, const jscan::Segments &sg, int64_t nrows, int64_t D,
+                 hipStream_t stream) {
     using T = typename E::store_t;
+    const T *xt = static_cast<const T *>(x), *dt = static_cast<const T *>(delta);
+    const T *bt = static_cast<const T *>(B), *ct = static_cast<const T *>(C);
+    T *yt = static_cast<T *>(y);
+    if (jscan::rows_kernel_applies(nrows, D)) {
+        jscan::launch_prefill_rows<E, kSummary>(xt, dt, A, bt, ct, h0, yt, h_final, dsum, sg, nrows, (int)D, stream);
+        return;
+    }
+    const int blocks_per_row = (int)((D + 63) / 64);
+    hipLaunchKernelGGL((jscan::prefill_lane_kernel<E, kSummary>), dim3((unsigned)(nrows * blocks_per_row)), dim3(64),
+                       0, stream, xt, dt, A, bt, ct, h0, yt, h_final, dsum, sg, (int)D, blocks_per_row);
+}
+
+// Token-by-token prefill of whole sequences (one row per sequence).
+template <typename E>
+jscan_status launch_prefill(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                            const float *h0, void *y, float *h_final, int64_t batch, int64_t L, int64_t D,
+                            hipStream_t stream) {
     if (L == 0) {
         const int64_t count = batch * D * jscan::kDState;
         const int64_t blocks = (count + 255) / 256;
-        hipLaunchKernelGGL(jscan::copy_state_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                           h0, h_final, count);
+        hipLaunchKernelGGL(jscan::copy_state_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, h0, h_final, count);
         return launch_status();
     }
-    if (jscan::rows_kernel_applies(batch, D)) {
-        return jscan::launch_prefill_rows<E>(static_cast<const T *>(x), static_cast<const T *>(delta), A,
-                                             static_cast<const T *>(B), static_cast<const T *>(C), h0,
-                                             static_cast<T *>(y), h_final, batch, L, (int)D, stream)
-                   ? launch_status()
-                   : JSCAN_ERR_HIP;
-    }
-    const int blocks_per_row = (int)((D + 63) / 64);
-    hipLaunchKernelGGL(jscan::prefill_lane_kernel<E>, dim3((unsigned)(batch * blocks_per_row)), dim3(64), 0,
-                       stream, static_cast<const T *>(x), static_cast<const T *>(delta), A,
-                       static_cast<const T *>(B), static_cast<const T *>(C), h0, static_cast<T *>(y),
-                       h_final, L, (int)D, blocks_per_row);
+    const jscan::Segments sg{L, L, 1, 0};
+    launch_rows<E, false>(x, delta, A, B, C, h0, y, h_final, nullptr, sg, batch, D, stream);
     return launch_status();
 }
 
-jscan_status prefill_impl(const void *x, const void *delta, const float *A, const void *B,
-                          const void *C, const float *h0, bool resume, void *y, float *h_final,
-                          int64_t batch, int64_t L, int64_t D, int64_t N, jscan_dtype dtype,
-                          void *stream) {
+// Argument checks shared by every prefill entry point.  Sets *nothing_to_do for zero-sized
+// work (which is then OK without a launch).
+jscan_status check_prefill(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                           const float *h0, bool h0_required, const void *y, const float *h_final, int64_t batch,
+                           int64_t L, int64_t D, int64_t N, jscan_dtype dtype, bool *nothing_to_do) {
+    *nothing_to_do = false;
     if (dtype != JSCAN_F32 && dtype != JSCAN_BF16) return JSCAN_ERR_DTYPE;
     if (batch < 0 || L < 0 || D < 0 || N != JSCAN_D_STATE || D % 8 != 0) return JSCAN_ERR_SHAPE;
     // index arithmetic inside the kernels: rows of D fit in int, grid sizes in 32 bits
-    if (D > (1 << 24) || batch > (1 << 20)) return JSCAN_ERR_SHAPE;
-    if (batch == 0 || D == 0) return JSCAN_OK;
-    if (!A || !h_final || (resume && !h0)) return JSCAN_ERR_NULL;
+    if (D > (1 << 24) || batch > (1 << 20) || batch * ((D + 63) / 64) > kMaxBlocks) return JSCAN_ERR_SHAPE;
+    if (batch == 0 || D == 0) {
+        *nothing_to_do = true;
+        return JSCAN_OK;
+    }
+    if (!A || !h_final || (h0_required && !h0)) return JSCAN_ERR_NULL;
     if (L > 0 && (!x || !delta || !B || !C || !y)) return JSCAN_ERR_NULL;
 
     const int64_t es = elem_bytes(dtype);
@@ -99,11 +116,79 @@ jscan_status prefill_impl(const void *x, const void *delta, const float *A, cons
         if (overlaps(sy, s0)) return JSCAN_ERR_ALIAS;
         if (overlaps(sh, s0) && h0 != h_final) return JSCAN_ERR_ALIAS;  // exact in-place is allowed
     }
+    return JSCAN_OK;
+}
 
+jscan_status prefill_impl(const void *x, const void *delta, const float *A, const void *B,
+                          const void *C, const float *h0, bool resume, void *y, float *h_final,
+                          int64_t batch, int64_t L, int64_t D, int64_t N, jscan_dtype dtype,
+                          void *stream) {
+    bool empty = false;
+    const jscan_status st = check_prefill(x, delta, A, B, C, h0, resume, y, h_final, batch, L, D, N, dtype, &empty);
+    if (st != JSCAN_OK || empty) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == JSCAN_BF16)
         return launch_prefill<jscan::BF16>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s);
     return launch_prefill<jscan::F32>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s);
+}
+
+// ---- time-parallel prefill ---------------------------------------------------------------
+
+struct ChunkPlan {
+    int64_t seg_len = 0;
+    int64_t n_seg = 1;
+};
+
+// Segments of `chunk` tokens, or (chunk == 0) as many segments as it takes for the rows of
+// all segments to fill the GPU once: 8192 channels for the row-mapped kernel (256
+// work-groups of 32 channels, one per CU), 65536 for the lane kernel (one wave per SIMD).
+// Automatic segments are at least 256 tokens long and a multiple of the 64-token tile.
+ChunkPlan plan_chunks(int64_t batch, int64_t L, int64_t D, int64_t chunk) {
+    ChunkPlan p;
+    p.seg_len = L;
+    if (L <= 0 || batch <= 0 || D <= 0) return p;
+    if (chunk > 0) {
+        p.seg_len = chunk < L ? chunk : L;
+    } else {
+        const int64_t channels = batch * D;
+        const int64_t target = (D % jscan::rows::kCh == 0) ? 8192 : 65536;
+        int64_t n = channels >= target ? 1 : target / channels;
+        const int64_t by_length = L / 256 > 1 ? L / 256 : 1;
+        if (n > by_length) n = by_length;
+        p.seg_len = (L + n - 1) / n;
+        p.seg_len = (p.seg_len + jscan::rows::kT - 1) / jscan::rows::kT * jscan::rows::kT;
+        if (p.seg_len > L) p.seg_len = L;
+    }
+    p.n_seg = (L + p.seg_len - 1) / p.seg_len;
+    return p;
+}
+
+// Workspace bytes of a plan: h_loc / h_in [batch * n_seg][D][N] and delta sums [batch * n_seg][D].
+int64_t chunk_workspace_bytes(const ChunkPlan &p, int64_t batch, int64_t D) {
+    if (p.n_seg <= 1) return 0;
+    return batch * p.n_seg * D * (JSCAN_D_STATE + 1) * 4;
+}
+
+template <typename E>
+jscan_status launch_chunked(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                            const float *h0, void *y, float *h_final, int64_t batch, int64_t L, int64_t D,
+                            const ChunkPlan &p, void *workspace, hipStream_t stream) {
+    float *hbuf = static_cast<float *>(workspace);
+    float *dsum = hbuf + batch * p.n_seg * D * jscan::kDState;
+    const int64_t nrows = batch * p.n_seg;
+    // 1. every segment from zero: end states into hbuf, delta sums into dsum (no y)
+    const jscan::Segments each{L, p.seg_len, (int)p.n_seg, 0};
+    launch_rows<E, true>(x, delta, A, B, C, nullptr, y, hbuf, dsum, each, nrows, D, stream);
+    if (launch_status() != JSCAN_OK) return JSCAN_ERR_HIP;
+    // 2. starting state of every segment, in place in hbuf
+    const int64_t count = batch * D * jscan::kDState;
+    hipLaunchKernelGGL(jscan::chunk_carry_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream, hbuf,
+                       dsum, A, h0, count, (int)D, (int)p.n_seg);
+    if (launch_status() != JSCAN_OK) return JSCAN_ERR_HIP;
+    // 3. every segment again from its starting state: y, and h_final from the last segments
+    const jscan::Segments again{L, p.seg_len, (int)p.n_seg, 1};
+    launch_rows<E, false>(x, delta, A, B, C, hbuf, y, h_final, nullptr, again, nrows, D, stream);
+    return launch_status();
 }
 
 // ---- decode step -----------------------------------------------------------------------
@@ -139,6 +224,43 @@ jscan_status jscan_prefill_resume(const void *x, const void *delta, const float 
     return prefill_impl(x, delta, A, B, C, h0, true, y, h_final, batch, L, D, N, dtype, stream);
 }
 
+int64_t jscan_prefill_chunked_workspace(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t chunk) {
+    if (batch < 0 || L < 0 || D < 0 || N != JSCAN_D_STATE || D % 8 != 0 || chunk < 0) return -1;
+    if (D > (1 << 24) || batch > (1 << 20)) return -1;
+    const ChunkPlan p = plan_chunks(batch, L, D, chunk);
+    if (batch * p.n_seg > (1 << 24) || batch * p.n_seg * ((D + 63) / 64) > kMaxBlocks) return -1;
+    return chunk_workspace_bytes(p, batch, D);
+}
+
+jscan_status jscan_prefill_chunked(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                                   const float *h0, void *y, float *h_final, int64_t batch, int64_t L, int64_t D,
+                                   int64_t N, int64_t chunk, void *workspace, int64_t workspace_bytes,
+                                   jscan_dtype dtype, void *stream) {
+    bool empty = false;
+    jscan_status st = check_prefill(x, delta, A, B, C, h0, false, y, h_final, batch, L, D, N, dtype, &empty);
+    if (st != JSCAN_OK) return st;
+    if (chunk < 0) return JSCAN_ERR_SHAPE;
+    if (empty) return JSCAN_OK;
+    const ChunkPlan p = plan_chunks(batch, L, D, chunk);
+    if (p.n_seg <= 1) return prefill_impl(x, delta, A, B, C, h0, false, y, h_final, batch, L, D, N, dtype, stream);
+    if (batch * p.n_seg > (1 << 24) || batch * p.n_seg * ((D + 63) / 64) > kMaxBlocks) return JSCAN_ERR_SHAPE;
+    const int64_t need = chunk_workspace_bytes(p, batch, D);
+    if (!workspace) return JSCAN_ERR_NULL;
+    if (workspace_bytes < need) return JSCAN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return JSCAN_ERR_ALIGN;
+    const int64_t es = elem_bytes(dtype);
+    const int64_t seq = batch * L * D * es, bc = batch * L * N * es, state = batch * D * N * 4;
+    const Span sw = span(workspace, need);
+    const Span others[] = {span(x, seq), span(delta, seq), span(A, D * N * 4), span(B, bc), span(C, bc),
+                           span(h0, state), span(y, seq), span(h_final, state)};
+    for (const Span &o : others)
+        if (overlaps(sw, o)) return JSCAN_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == JSCAN_BF16)
+        return launch_chunked<jscan::BF16>(x, delta, A, B, C, h0, y, h_final, batch, L, D, p, workspace, s);
+    return launch_chunked<jscan::F32>(x, delta, A, B, C, h0, y, h_final, batch, L, D, p, workspace, s);
+}
+
 jscan_status jscan_step(float *h, const void *x_t, const void *delta_t, const float *A,
                         const void *B_t, const void *C_t, void *y_t, int64_t batch, int64_t D,
                         int64_t N, int64_t ld_xd, int64_t ld_bc, jscan_dtype dtype,
@@ -146,6 +268,8 @@ jscan_status jscan_step(float *h, const void *x_t, const void *delta_t, const fl
     if (dtype != JSCAN_F32 && dtype != JSCAN_BF16) return JSCAN_ERR_DTYPE;
     if (batch < 0 || D < 0 || N != JSCAN_D_STATE || D % 8 != 0) return JSCAN_ERR_SHAPE;
     if (D > (1 << 24) || batch > (1 << 20)) return JSCAN_ERR_SHAPE;
+    if ((batch + jscan::step::kRows - 1) / jscan::step::kRows * ((D * 4 + 255) / 256) > kMaxBlocks)
+        return JSCAN_ERR_SHAPE;
     if (batch == 0 || D == 0) return JSCAN_OK;
     if (ld_xd < D || ld_bc < N || ld_xd % 8 != 0 || ld_bc % 8 != 0) return JSCAN_ERR_SHAPE;
     if (!h || !x_t || !delta_t || !A || !B_t || !C_t || !y_t) return JSCAN_ERR_NULL;
@@ -177,12 +301,13 @@ const char *jscan_status_string(jscan_status s) {
     case JSCAN_ERR_ALIGN: return "array pointer not 16-byte aligned";
     case JSCAN_ERR_ALIAS: return "an output overlaps an input or another output";
     case JSCAN_ERR_HIP: return "HIP launch failed (see jscan_last_hip_error)";
+    case JSCAN_ERR_WORKSPACE: return "workspace smaller than jscan_prefill_chunked_workspace() bytes";
     }
     return "unknown status";
 }
 
 int jscan_last_hip_error(void) { return g_last_hip_error; }
 
-int jscan_version(void) { return 100; }
+int jscan_version(void) { return 101; }
 
 }  // extern "C"

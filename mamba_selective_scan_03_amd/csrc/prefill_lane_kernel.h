@@ -13,43 +13,54 @@
 
 namespace jscan {
 
-template <typename E>
+// One lane scans one channel of one row (see Segments) from the row's initial state (zero
+// when h0 is null).  A segment-summary launch (kSummary) writes no y; it writes the row's
+// final state and the sum of the row's delta values to dsum[row][D].
+template <typename E, bool kSummary>
 __global__ __launch_bounds__(64) void prefill_lane_kernel(
     const typename E::store_t *__restrict__ x, const typename E::store_t *__restrict__ dl,
     const float *__restrict__ A, const typename E::store_t *__restrict__ B,
     const typename E::store_t *__restrict__ C, const float *__restrict__ h0,
-    typename E::store_t *__restrict__ y, float *__restrict__ h_final, int64_t L, int D,
+    typename E::store_t *__restrict__ y, float *__restrict__ h_final, float *__restrict__ dsum, Segments sg, int D,
     int blocks_per_row) {
-    const int b = blockIdx.x / blocks_per_row;
-    const int d = (blockIdx.x - b * blocks_per_row) * 64 + threadIdx.x;
+    const int vrow = blockIdx.x / blocks_per_row;
+    const int d = (blockIdx.x - vrow * blocks_per_row) * 64 + threadIdx.x;
     if (d >= D) return;  // no cross-lane work below, so idle lanes may leave
+    const RowSpan span = row_span(sg, vrow);
 
     float a2[kDState], h[kDState];
 #pragma unroll
     for (int n = 0; n < kDState; ++n) {
         a2[n] = scaled_A(A[(int64_t)d * kDState + n]);
-        h[n] = h0 ? h0[((int64_t)b * D + d) * kDState + n] : 0.0f;
+        h[n] = h0 ? h0[((int64_t)vrow * D + d) * kDState + n] : 0.0f;
     }
-    const int64_t row = (int64_t)b * L;
+    const int64_t row = span.tok0;
     const typename E::store_t *xr = x + row * D + d;
     const typename E::store_t *dr = dl + row * D + d;
     typename E::store_t *yr = y + row * D + d;
     const typename E::store_t *Br = B + row * kDState;
     const typename E::store_t *Cr = C + row * kDState;
 
-    for (int64_t t = 0; t < L; ++t) {
+    float dacc = 0.0f;
+    for (int64_t t = 0; t < span.len; ++t) {
         const float xv = E::load(xr + t * D), dv = E::load(dr + t * D);
         const float dx = delta_x(dv, xv);
         float acc = 0.0f;
 #pragma unroll
         for (int n = 0; n < kDState; ++n) {
             h[n] = advance(h[n], dv, a2[n], dx, E::load(Br + t * kDState + n));
-            acc = __builtin_fmaf(E::load(Cr + t * kDState + n), h[n], acc);
+            if constexpr (!kSummary) acc = __builtin_fmaf(E::load(Cr + t * kDState + n), h[n], acc);
         }
-        E::store(yr + t * D, acc);
+        if constexpr (kSummary)
+            dacc += dv;
+        else
+            E::store(yr + t * D, acc);
     }
+    if (span.state >= 0) {
 #pragma unroll
-    for (int n = 0; n < kDState; ++n) h_final[((int64_t)b * D + d) * kDState + n] = h[n];
+        for (int n = 0; n < kDState; ++n) h_final[((int64_t)span.state * D + d) * kDState + n] = h[n];
+    }
+    if constexpr (kSummary) dsum[(int64_t)vrow * D + d] = dacc;
 }
 
 // Fills the final state when there are no tokens: copies h0, or writes zeros.

@@ -236,17 +236,24 @@ __device__ __forceinline__ float token_step(const GroupRegs &g, float &h_0, floa
 
 // Advance this lane's two states over tokens 8H..8H+7 of a 16-token group and leave their y
 // partials (summed over the wave's 4 rows) in the y exchange rows `ys` (row = token in group).
-template <int H>
+// A segment-summary scan (kSummary) produces no y; it adds the tokens' delta to `dsum` in
+// token order instead, and the y arithmetic is left out of the code altogether.
+template <int H, bool kSummary>
 __device__ __forceinline__ void scan_half(const GroupRegs &g, float &h_0, float &h_1, float a2_0, float a2_1, float *ys,
-                                          int rt, int ch) {
+                                          int rt, int ch, float &dsum) {
     float P[8];
 #define JSCAN_STEP(i) P[i] = token_step<8 * H + (i)>(g, h_0, h_1, a2_0, a2_1);
     JSCAN_STEP(0) JSCAN_STEP(1) JSCAN_STEP(2) JSCAN_STEP(3)
     JSCAN_STEP(4) JSCAN_STEP(5) JSCAN_STEP(6) JSCAN_STEP(7)
 #undef JSCAN_STEP
-    // rows -> one register per 4 tokens; row r holds token 4j + {0,2,1,3}[r]
-    ys[(8 * H + rt) * rows::kYStride + ch] = reduce_rows4(P[0], P[1], P[2], P[3]);
-    ys[(8 * H + 4 + rt) * rows::kYStride + ch] = reduce_rows4(P[4], P[5], P[6], P[7]);
+    if constexpr (kSummary) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dsum += (i & 1) ? g.v[4 * H + (i >> 1)].w : g.v[4 * H + (i >> 1)].y;
+    } else {
+        // rows -> one register per 4 tokens; row r holds token 4j + {0,2,1,3}[r]
+        ys[(8 * H + rt) * rows::kYStride + ch] = reduce_rows4(P[0], P[1], P[2], P[3]);
+        ys[(8 * H + 4 + rt) * rows::kYStride + ch] = reduce_rows4(P[4], P[5], P[6], P[7]);
+    }
 }
 
 // The last step of y for one tile: this thread's token row t = tid / 4 and 8 channels, as the
@@ -291,13 +298,16 @@ __device__ __forceinline__ void write_final(const FinalRegs &F, typename E::stor
     }
 }
 
-template <typename E>
+// One work-group scans 32 channels of one row (see Segments) from the row's initial state
+// (zero when h0 is null).  A segment-summary launch (kSummary) writes no y; it writes the
+// row's final state and, per channel, the sum of the row's delta values to dsum[row][D].
+template <typename E, bool kSummary>
 __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_rows_kernel(
     const typename E::store_t *__restrict__ x, const typename E::store_t *__restrict__ dl,
     const float *__restrict__ A, const typename E::store_t *__restrict__ B,
     const typename E::store_t *__restrict__ C, const float *__restrict__ h0,
-    typename E::store_t *__restrict__ y, float *__restrict__ h_final, int64_t L, int D, int blocks_per_row,
-    int xcd_stride) {
+    typename E::store_t *__restrict__ y, float *__restrict__ h_final, float *__restrict__ dsum, Segments sg, int D,
+    int blocks_per_row, int xcd_stride) {
     __shared__ __attribute__((aligned(16))) float dx_s[2][rows::kDxSize];
     __shared__ __attribute__((aligned(16))) float bc_s[2][2 * rows::kBcSize];
     __shared__ __attribute__((aligned(16))) float y_s[2][rows::kYSize];
@@ -306,10 +316,11 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
     // the 8 XCDs), so the two blocks sharing a 128-byte row segment share one L2.
     int wg = blockIdx.x;
     if (xcd_stride > 0) wg = (wg & 7) * xcd_stride + (wg >> 3);
-    const int b = wg / blocks_per_row;
-    const int d0 = (wg - b * blocks_per_row) * rows::kCh;
+    const int vrow = wg / blocks_per_row;
+    const int d0 = (wg - vrow * blocks_per_row) * rows::kCh;
 
-    const int64_t row = (int64_t)b * L;
+    const RowSpan span = row_span(sg, vrow);
+    const int64_t row = span.tok0, L = span.len;
     const int ntiles = (int)((L + rows::kT - 1) / rows::kT);
 
     if (threadIdx.x >= rows::kHalf) {
@@ -335,7 +346,7 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
                 stage_tile<E>(R[nxt], dx_s[nxt], bc_s[nxt], (int64_t)(k + 1) * rows::kT, L, tid);
                 if (k + 3 < ntiles) load_tile<E>(R[nxt], xb, db, bcb, (int64_t)(k + 3) * rows::kT, L, D, tid);
             }
-            if (k > 0) {
+            if (!kSummary && k > 0) {
                 read_final(F, y_s[nxt], tid);
                 write_final<E>(F, yb, (int64_t)(k - 1) * rows::kT, L, D, tid);
             }
@@ -345,8 +356,10 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
             tile(IntConst<0>{}, k);
             if (k + 1 < ntiles) tile(IntConst<1>{}, k + 1);
         }
-        read_final(F, y_s[(ntiles - 1) & 1], tid);
-        write_final<E>(F, yb, (int64_t)(ntiles - 1) * rows::kT, L, D, tid);
+        if constexpr (!kSummary) {
+            read_final(F, y_s[(ntiles - 1) & 1], tid);
+            write_final<E>(F, yb, (int64_t)(ntiles - 1) * rows::kT, L, D, tid);
+        }
         return;
     }
 
@@ -366,13 +379,14 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
     const float a2_1 = scaled_A(A[(int64_t)d * kDState + n0 + 1]);
     float h_0 = 0.0f, h_1 = 0.0f;
     if (h0) {
-        const float2 hv = *reinterpret_cast<const float2 *>(h0 + ((int64_t)b * D + d) * kDState + n0);
+        const float2 hv = *reinterpret_cast<const float2 *>(h0 + ((int64_t)vrow * D + d) * kDState + n0);
         h_0 = hv.x;
         h_1 = hv.y;
     }
     const int rt = (r == 1) ? 2 : (r == 2) ? 1 : r;   // token slot of this row after reduce_rows4
     __syncthreads();   // tile 0 staged by the helper waves
     GroupRegs G[2];
+    float dacc = 0.0f;
     load_half<0>(G[0], dx_s[0], bc_s[0], 0, ch, n0, c);
     load_half<1>(G[0], dx_s[0], bc_s[0], 0, ch, n0, c);
 
@@ -387,31 +401,31 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
         const float *dxc = dx_s[cur], *bcc = bc_s[cur];
         load_half<0>(G[1], dxc, bcc, 16, ch, n0, c);
         JSCAN_SB;
-        scan_half<0>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch);
+        scan_half<0, kSummary>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch, dacc);
         JSCAN_SB;
         load_half<1>(G[1], dxc, bcc, 16, ch, n0, c);
         JSCAN_SB;
-        scan_half<1>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch);
+        scan_half<1, kSummary>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch, dacc);
         JSCAN_SB;
         load_half<0>(G[0], dxc, bcc, 32, ch, n0, c);
         JSCAN_SB;
-        scan_half<0>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch);
+        scan_half<0, kSummary>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch, dacc);
         JSCAN_SB;
         load_half<1>(G[0], dxc, bcc, 32, ch, n0, c);
         JSCAN_SB;
-        scan_half<1>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch);
+        scan_half<1, kSummary>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch, dacc);
         JSCAN_SB;
         load_half<0>(G[1], dxc, bcc, 48, ch, n0, c);
         JSCAN_SB;
-        scan_half<0>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch);
+        scan_half<0, kSummary>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch, dacc);
         JSCAN_SB;
         load_half<1>(G[1], dxc, bcc, 48, ch, n0, c);
         JSCAN_SB;
-        scan_half<1>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch);
+        scan_half<1, kSummary>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch, dacc);
         JSCAN_SB;
-        scan_half<0>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch);
+        scan_half<0, kSummary>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch, dacc);
         JSCAN_SB;
-        scan_half<1>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch);
+        scan_half<1, kSummary>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch, dacc);
         __syncthreads();
         if (k + 1 < ntiles) {
             load_half<0>(G[0], dx_s[nxt], bc_s[nxt], 0, ch, n0, c);
@@ -423,24 +437,28 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
         tile(IntConst<0>{}, k);
         if (k + 1 < ntiles) tile(IntConst<1>{}, k + 1);
     }
-    *reinterpret_cast<float2 *>(h_final + ((int64_t)b * D + d) * kDState + n0) = make_float2(h_0, h_1);
+    if (span.state >= 0)
+        *reinterpret_cast<float2 *>(h_final + ((int64_t)span.state * D + d) * kDState + n0) = make_float2(h_0, h_1);
+    if constexpr (kSummary) {
+        if (n0 == 0) dsum[(int64_t)vrow * D + d] = dacc;
+    }
 }
 
 // The row-mapped kernel needs whole 32-channel blocks; it is the better choice while
 // batch * D is too small for one lane per channel to fill the chip.
 inline bool rows_kernel_applies(int64_t batch, int64_t D) { return D % rows::kCh == 0 && batch * D <= 65536; }
 
-template <typename E>
-bool launch_prefill_rows(const typename E::store_t *x, const typename E::store_t *dl, const float *A,
+// Launches one work-group per 32 channels of each of the `nrows` rows described by sg.
+template <typename E, bool kSummary>
+void launch_prefill_rows(const typename E::store_t *x, const typename E::store_t *dl, const float *A,
                          const typename E::store_t *B, const typename E::store_t *C, const float *h0,
-                         typename E::store_t *y, float *h_final, int64_t batch, int64_t L, int D,
-                         hipStream_t stream) {
+                         typename E::store_t *y, float *h_final, float *dsum, const Segments &sg, int64_t nrows,
+                         int D, hipStream_t stream) {
     const int blocks_per_row = D / rows::kCh;
-    const int64_t blocks = batch * blocks_per_row;
+    const int64_t blocks = nrows * blocks_per_row;
     const int xcd_stride = (blocks % 8 == 0) ? (int)(blocks / 8) : 0;
-    hipLaunchKernelGGL(prefill_rows_kernel<E>, dim3((unsigned)blocks), dim3(rows::kThreads), 0, stream, x, dl, A, B,
-                       C, h0, y, h_final, L, D, blocks_per_row, xcd_stride);
-    return true;
+    hipLaunchKernelGGL((prefill_rows_kernel<E, kSummary>), dim3((unsigned)blocks), dim3(rows::kThreads), 0, stream, x,
+                       dl, A, B, C, h0, y, h_final, dsum, sg, D, blocks_per_row, xcd_stride);
 }
 
 }  // namespace jscan

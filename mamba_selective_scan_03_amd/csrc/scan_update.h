@@ -35,6 +35,38 @@ __device__ __forceinline__ float advance(float h, float delta, float a2, float d
     return __builtin_fmaf(decay(delta, a2), h, dx * b);
 }
 
+// ---- rows of work ----------------------------------------------------------------------
+
+// The prefill kernels walk "rows": a run of consecutive tokens of one sequence, scanned in
+// order from a given initial state.  A plain prefill has one row per sequence.  The
+// time-parallel prefill cuts each sequence into segments of seg_len tokens (the last one may
+// be shorter) and gives every segment a row of its own; row v is segment v % n_seg of
+// sequence v / n_seg.  Initial states are indexed by row.  Final states are indexed by row
+// too, unless final_by_sequence is set: then only the last segment of each sequence writes
+// its final state, at that sequence's index.
+struct Segments {
+    int64_t L;              // tokens per sequence
+    int64_t seg_len;        // tokens per segment (L for a plain prefill)
+    int n_seg;              // segments per sequence, ceil(L / seg_len)
+    int final_by_sequence;  // see above
+};
+
+struct RowSpan {
+    int64_t tok0;  // index of the row's first token in the [batch][L] token order
+    int64_t len;   // tokens in the row (>= 1)
+    int state;     // index of the row's final state, or -1 if it writes none
+};
+
+__device__ __forceinline__ RowSpan row_span(const Segments &sg, int row) {
+    const int seq = row / sg.n_seg, seg = row - seq * sg.n_seg;
+    const int64_t t_begin = (int64_t)seg * sg.seg_len;
+    RowSpan r;
+    r.tok0 = (int64_t)seq * sg.L + t_begin;
+    r.len = min(sg.seg_len, sg.L - t_begin);
+    r.state = !sg.final_by_sequence ? row : (seg == sg.n_seg - 1 ? seq : -1);
+    return r;
+}
+
 // ---- element formats -------------------------------------------------------------------
 
 // bf16 -> fp32 is exact: the 16 stored bits are the high half of the fp32 pattern.

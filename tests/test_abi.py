@@ -12,7 +12,7 @@ import mamba_selective_scan_03_amd as jscan
 from mamba_selective_scan_03_amd import _binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OK, ENULL, ESHAPE, EDTYPE, EALIGN, EALIAS, EHIP = range(7)
+OK, ENULL, ESHAPE, EDTYPE, EALIGN, EALIAS, EHIP, EWORKSPACE = range(8)
 F32, BF16 = 0, 1
 P = 0x10000000  # a 16-byte aligned address that is never dereferenced
 
@@ -26,17 +26,18 @@ def test_header_symbols_are_exported():
     lib = jscan.library()
     names = header_symbols()
     assert {"jscan_prefill", "jscan_prefill_resume", "jscan_step", "jscan_status_string",
-            "jscan_last_hip_error", "jscan_version"} <= set(names)
+            "jscan_last_hip_error", "jscan_version", "jscan_prefill_chunked",
+            "jscan_prefill_chunked_workspace"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_status_strings_and_version():
     lib = jscan.library()
-    for s in range(7):
-        assert lib.jscan_status_string(s)
+    for s in range(8):
+        assert lib.jscan_status_string(s) and lib.jscan_status_string(s) != b"unknown status"
     assert lib.jscan_status_string(99) == b"unknown status"
-    assert lib.jscan_version() == 100
+    assert lib.jscan_version() == 101
     assert lib.jscan_last_hip_error() == 0
 
 
@@ -92,6 +93,39 @@ def test_resume_aliasing_rules():
 ])
 def test_step_validation(kw, code):
     assert step(**kw) == code
+
+
+WS = P + 0x700000  # fake workspace address
+
+
+def chunked(x=P, d=P + 0x100000, A=P + 0x200000, B=P + 0x300000, C=P + 0x400000, h0=None, y=P + 0x500000,
+            h=P + 0x600000, batch=1, L=4096, D=64, N=16, chunk=256, ws=WS, ws_bytes=1 << 20, dtype=BF16):
+    return jscan.library().jscan_prefill_chunked(x, d, A, B, C, h0, y, h, batch, L, D, N, chunk, ws, ws_bytes, dtype,
+                                                 None)
+
+
+def test_chunked_workspace_sizes():
+    ws = jscan.library().jscan_prefill_chunked_workspace
+    # automatic chunking of one sequence of 1024 channels: 8 segments fill 256 work-groups
+    assert ws(1, 65536, 1024, 16, 0) == 8 * 1024 * 17 * 4
+    assert ws(1, 4096, 64, 16, 256) == 16 * 64 * 17 * 4          # explicit 256-token segments
+    assert ws(2, 4000, 64, 16, 1000) == 2 * 4 * 64 * 17 * 4       # 4 segments per sequence
+    assert ws(1, 65536, 8192, 16, 0) == 0                         # enough channels: one segment
+    assert ws(1, 100, 64, 16, 0) == 0                             # too short to split
+    assert ws(1, 4096, 64, 16, 4096) == 0 and ws(1, 4096, 64, 16, 10 ** 6) == 0
+    assert ws(1, 0, 64, 16, 0) == 0
+    assert ws(1, 4096, 64, 8, 0) == -1 and ws(1, 4096, 60, 16, 0) == -1 and ws(1, 4096, 64, 16, -1) == -1
+    assert ws(1 << 20, 1 << 20, 64, 16, 1) == -1                  # too many segment rows
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), EDTYPE), (dict(N=4), ESHAPE), (dict(D=20), ESHAPE), (dict(chunk=-1), ESHAPE),
+    (dict(ws=None), ENULL), (dict(ws_bytes=16 * 64 * 17 * 4 - 4), EWORKSPACE), (dict(ws=WS + 8), EALIGN),
+    (dict(ws=P + 0x500000 + 1024), EALIAS), (dict(ws=P + 0x600000 - 64), EALIAS), (dict(h0=WS + 4096), EALIAS),
+    (dict(x=None), ENULL), (dict(y=P + 0x100000), EALIAS), (dict(h0=P + 0x600000 + 16), EALIAS),
+])
+def test_chunked_validation(kw, code):
+    assert chunked(**kw) == code
 
 
 def test_binding_refuses_cpu_tensors():

@@ -46,6 +46,8 @@ def test_named_workload_shapes():
     assert (w["prefill_64k"].batch, w["prefill_64k"].L, w["prefill_64k"].D, w["prefill_64k"].N) == (1, 65536, 8192, 16)
     assert w["decode_256x28"].layers == 28 and w["decode_256x28"].batch == 256
     assert w["prefill_256k"].L == 262144 and w["prefill_256k"].extra_tokens == 64
+    assert (w["prefill_64k_tp8"].batch, w["prefill_64k_tp8"].L, w["prefill_64k_tp8"].D) == (1, 65536, 1024)
+    assert len({v.wid for v in w.values()}) == len(w)     # distinct seed streams
 
 
 def test_decode_layer_inputs_small():

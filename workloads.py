@@ -9,7 +9,8 @@ d_inner D = 8192, and d_state N = 16 (notes page "Jamba: A Hybrid Transformer-Ma
 Language Model", section "Mamba layer"); 28 of the 32 layers are Mamba layers (lesson page
 "Jamba - Hybrid SSM-Transformer", section "memory budget").  The prompt lengths (4K, 64K,
 256K) span the pages' long-context range (notes page, throughput table; 256K context on
-one 80 GB GPU).
+one 80 GB GPU).  prefill_64k_tp8 is the 64K prompt with d_inner split 8 ways, the share of
+one GPU under channel (tensor) parallelism.
 
 Distributions (the same for every workload):
     x, B, C ~ N(0, 1)                              per element
@@ -72,6 +73,9 @@ WORKLOADS = {
         Workload("prefill_64k", 2, 1, 65536, 8192, 16, "bf16", True),
         Workload("decode_256x28", 3, 256, 1, 8192, 16, "bf16", True, layers=28),
         Workload("prefill_256k", 4, 1, 262144, 8192, 16, "bf16", True, extra_tokens=64),
+        # one GPU's share of the 64K prefill when the 8192 channels are split over 8 GPUs
+        # (channels are independent, so each GPU scans D = 1024 of them on its own)
+        Workload("prefill_64k_tp8", 5, 1, 65536, 1024, 16, "bf16", True),
     ]
 }
 
