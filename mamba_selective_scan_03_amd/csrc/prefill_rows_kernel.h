@@ -223,15 +223,22 @@ __device__ __forceinline__ void load_half(GroupRegs &g, const float *dxs, const 
     }
 }
 
-// One token: advance this lane's two states and return C*h summed over them.
-template <int TAU>
-__device__ __forceinline__ float token_step(const GroupRegs &g, float &h_0, float &h_1, float a2_0, float a2_1) {
+// One token: advance this lane's two states and return C*h summed over them (a summary
+// scan adds the token's delta to `dsum` instead and returns nothing useful).
+template <int TAU, bool kSummary>
+__device__ __forceinline__ float token_step(const GroupRegs &g, float &h_0, float &h_1, float a2_0, float a2_1,
+                                            float &dsum) {
     const float4 v = g.v[TAU >> 1];
     const float dxv = (TAU & 1) ? v.z : v.x;
     const float dv = (TAU & 1) ? v.w : v.y;
     h_0 = advance(h_0, dv, a2_0, dxv, row_bcast<TAU>(g.b0));
     h_1 = advance(h_1, dv, a2_1, dxv, row_bcast<TAU>(g.b1));
-    return fmac_bcast<TAU>(row_bcast<TAU>(g.c0) * h_0, g.c1, h_1);
+    if constexpr (kSummary) {
+        dsum += dv;
+        return 0.0f;
+    } else {
+        return fmac_bcast<TAU>(row_bcast<TAU>(g.c0) * h_0, g.c1, h_1);
+    }
 }
 
 // Advance this lane's two states over tokens 8H..8H+7 of a 16-token group and leave their y
@@ -242,13 +249,15 @@ template <int H, bool kSummary>
 __device__ __forceinline__ void scan_half(const GroupRegs &g, float &h_0, float &h_1, float a2_0, float a2_1, float *ys,
                                           int rt, int ch, float &dsum) {
     float P[8];
-#define JSCAN_STEP(i) P[i] = token_step<8 * H + (i)>(g, h_0, h_1, a2_0, a2_1);
+#define JSCAN_STEP(i) P[i] = token_step<8 * H + (i), kSummary>(g, h_0, h_1, a2_0, a2_1, dsum);
     JSCAN_STEP(0) JSCAN_STEP(1) JSCAN_STEP(2) JSCAN_STEP(3)
     JSCAN_STEP(4) JSCAN_STEP(5) JSCAN_STEP(6) JSCAN_STEP(7)
 #undef JSCAN_STEP
     if constexpr (kSummary) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) dsum += (i & 1) ? g.v[4 * H + (i >> 1)].w : g.v[4 * H + (i >> 1)].y;
+        // Nothing stores from this half, so without an anchor the compiler may sink the whole
+        // state chain past the scheduling barriers to the end of the tile, keeping every
+        // broadcast operand alive until then.  The empty asm pins the states here.
+        asm volatile("" : "+v"(h_0), "+v"(h_1), "+v"(dsum));
     } else {
         // rows -> one register per 4 tokens; row r holds token 4j + {0,2,1,3}[r]
         ys[(8 * H + rt) * rows::kYStride + ch] = reduce_rows4(P[0], P[1], P[2], P[3]);
