@@ -15,6 +15,9 @@ section "Mamba layer"):
 for every (batch, channel, state) with diagonal A (lesson page "Jamba - Hybrid
 SSM-Transformer", section "Mamba-3", item 2).  Shapes: x, delta, y ``[batch, L, D]``;
 A ``[D, N]``; B, C ``[batch, L, N]``; states ``[batch, D, N]``.
+
+``oracle.producer`` is the fp64 (numpy) oracle of the producer side that computes delta, B
+and C from x.
 """
 from __future__ import annotations
 

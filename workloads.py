@@ -38,6 +38,7 @@ BLOCK = 4096  # tokens per seeded block
 
 # tensor ids inside the seed
 T_X, T_Z, T_B, T_C, T_A, T_H0 = 0, 1, 2, 3, 4, 5
+T_WX, T_GAIN, T_WDT, T_BDT = 6, 7, 8, 9     # producer-side weights
 
 
 @dataclasses.dataclass(frozen=True)
@@ -195,6 +196,30 @@ def decode_layer_inputs(name_or_wl, layer: int, seed: int = 0, token: int = 0):
         "A": draw_A(wl, seed, layer),
         "B": mat(T_B, wl.N),
         "C": mat(T_C, wl.N),
+    }
+
+
+def producer_weights(D: int, R: int = 256, N: int = 16, seed: int = 0, wid: int = 50):
+    """Synthetic weights of the producer side (delta, B and C computed from x):
+        w_x  [R + 2N, D] bf16, N(0, 1/D): unit-variance projections of unit-variance x
+        g_d [R], g_b [N], g_c [N] fp32 gains, U(0.75, 1.25)
+        w_dt [D, R] bf16, N(0, 1/R): unit-variance pre-activations of a unit-RMS d_low
+        b_dt [D] fp32, -2 + 0.25 N(0, 1)
+    so that delta = softplus(N(0, ~1) - 2) per channel, the distribution the scan workloads
+    draw delta from directly.  R defaults to 256 (d_model 4096 / 16, the usual rank of delta)."""
+    def rng(tensor):
+        return _rng(seed, wid, tensor, D * 1000 + R, 0)
+
+    w_x = rng(T_WX).standard_normal((R + 2 * N, D), dtype=np.float32) / np.float32(np.sqrt(D))
+    gains = rng(T_GAIN).uniform(0.75, 1.25, size=R + 2 * N).astype(np.float32)
+    w_dt = rng(T_WDT).standard_normal((D, R), dtype=np.float32) / np.float32(np.sqrt(R))
+    b_dt = (-2.0 + 0.25 * rng(T_BDT).standard_normal(D)).astype(np.float32)
+    t = torch.from_numpy
+    return {
+        "w_x": t(np.ascontiguousarray(w_x)).to(torch.bfloat16),
+        "g_d": t(gains[:R].copy()), "g_b": t(gains[R:R + N].copy()), "g_c": t(gains[R + N:].copy()),
+        "w_dt": t(np.ascontiguousarray(w_dt)).to(torch.bfloat16),
+        "b_dt": t(b_dt),
     }
 
 
