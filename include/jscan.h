@@ -142,6 +142,34 @@ int64_t jscan_prefill_chunked_workspace(int64_t batch, int64_t L, int64_t D, int
                                         int64_t chunk);
 
 /*
+ * Producer side: the scan's delta, B and C computed from x (bf16 only), for M tokens.
+ * The notes page ("Jamba: A Hybrid Transformer-Mamba Language Model", section "Mamba layer")
+ * makes these parameters functions of the input and applies RMSNorm in the Mamba layer;
+ * they are computed as the selective projection of Mamba-1:
+ *     [d_low | B | C] = W_x x_t                          (fp32 accumulation of bf16 products)
+ *     d_low = rmsnorm(d_low) * g_delta,  B = rmsnorm(B) * g_B,  C = rmsnorm(C) * g_C,
+ *             rmsnorm(v) = v / sqrt(mean(v^2) + eps) over each vector's own width
+ *     delta = softplus(W_dt d_low + b_dt)
+ * Each output is rounded once, to nearest even, from its fp32 value.  The products run on the
+ * matrix cores (MFMA 16x16x32 bf16); the normalisation, bias and softplus run on the fp32
+ * accumulators before the rounding.
+ *   x          [M][D]      bf16, M = batch * L tokens in any order (rows are independent)
+ *   w_x        [R + 2N][D] bf16: rows 0..R-1 give d_low, R..R+N-1 give B, R+N.. give C
+ *   g_delta [R], g_B [N], g_C [N]   fp32 gains
+ *   w_dt       [D][R]      bf16 (row d produces channel d)
+ *   b_dt       [D]         fp32
+ *   delta_low  [M][R]      out, bf16, the normalised d_low (also the input of the second product)
+ *   delta      [M][D]      out, bf16;   B, C [M][N] out, bf16
+ * R must be 64, 128 or 256; N = 16; D a multiple of 128; eps in [0, 1].  dtype must be
+ * JSCAN_BF16 (JSCAN_ERR_DTYPE otherwise).  Outputs must not overlap inputs or each other.
+ * Two kernels are launched on `stream`, in order.
+ */
+jscan_status jscan_ssm_inputs(const void *x, const void *w_x, const float *g_delta, const float *g_B,
+                              const float *g_C, const void *w_dt, const float *b_dt, void *delta_low,
+                              void *delta, void *B, void *C, int64_t M, int64_t D, int64_t R,
+                              int64_t N, float eps, jscan_dtype dtype, void *stream);
+
+/*
  * Decode step: advance the state by one token, in place, and write that token's output.
  *   h        [batch][D][N] fp32, read and overwritten with the new state
  *   x_t, delta_t: batch rows of D values; row b starts at element b * ld_xd
@@ -163,7 +191,8 @@ const char *jscan_status_string(jscan_status s);
 /* hipError_t behind the last JSCAN_ERR_HIP returned on the calling thread (0 if none). */
 int jscan_last_hip_error(void);
 
-/* Library ABI version: 100 * major + minor (101 adds the time-parallel prefill). */
+/* Library ABI version: 100 * major + minor (101 adds the time-parallel prefill, 102 the
+ * producer side). */
 int jscan_version(void);
 
 #ifdef __cplusplus

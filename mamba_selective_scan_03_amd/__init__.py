@@ -8,6 +8,7 @@ There is no CPU fallback: without the built library every call raises.
     y, h_final = prefill(x, delta, A, B, C, h0=h)          # resume from a state
     y_t = step(h, x_t, delta_t, A, B_t, C_t)               # one decode token, h in place
     y, h_final = prefill_chunked(x, delta, A, B, C)        # time-parallel, for few channels
+    delta, B, C, d_low = ssm_inputs(x, w_x, g_d, g_B, g_C, w_dt, b_dt)   # producer side (MFMA)
 """
 from ._binding import (  # noqa: F401
     D_STATE,
@@ -17,6 +18,7 @@ from ._binding import (  # noqa: F401
     library_path,
     prefill,
     prefill_chunked,
+    ssm_inputs,
     step,
     step_raw,
 )

@@ -44,6 +44,9 @@ def library():
     lib.jscan_step.argtypes = [fp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
     lib.jscan_prefill_chunked.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, i64, vp, i64, i32, vp]
     lib.jscan_prefill_chunked_workspace.argtypes = [i64, i64, i64, i64, i64]
+    lib.jscan_ssm_inputs.argtypes = [vp, vp, fp, fp, fp, vp, fp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, i32,
+                                     vp]
+    lib.jscan_ssm_inputs.restype = i32
     lib.jscan_prefill_chunked_workspace.restype = i64
     for f in (lib.jscan_prefill, lib.jscan_prefill_resume, lib.jscan_step, lib.jscan_prefill_chunked):
         f.restype = i32
@@ -143,6 +146,36 @@ def prefill_chunked(x, delta, A, B, C, h0=None, y=None, h_final=None, chunk=0, w
                                        _DTYPES[x.dtype], _stream(x.device))
     _check(st)
     return y, h_final
+
+
+def ssm_inputs(x, w_x, g_delta, g_B, g_C, w_dt, b_dt, eps=1e-6, delta=None, B=None, C=None, delta_low=None):
+    """Producer side (``jscan_ssm_inputs``): delta, B and C of the scan computed from x.
+    x ``[..., D]`` bf16; w_x ``[R + 32, D]`` bf16; gains fp32 ``[R]``, ``[16]``, ``[16]``;
+    w_dt ``[D, R]`` bf16; b_dt ``[D]`` fp32.  Returns ``(delta [..., D], B [..., 16], C [..., 16],
+    delta_low [..., R])``, all bf16, with x's leading shape."""
+    _require(x.is_cuda and x.dtype == torch.bfloat16 and x.is_contiguous(), "x must be a contiguous bf16 CUDA tensor")
+    D = x.shape[-1]
+    lead = tuple(x.shape[:-1])
+    M = x.numel() // D if D else 0
+    R = w_dt.shape[1] if w_dt.dim() == 2 else -1
+    for name, t, shape, dt in (("w_x", w_x, (R + 2 * D_STATE, D), torch.bfloat16),
+                               ("g_delta", g_delta, (R,), torch.float32), ("g_B", g_B, (D_STATE,), torch.float32),
+                               ("g_C", g_C, (D_STATE,), torch.float32), ("w_dt", w_dt, (D, R), torch.bfloat16),
+                               ("b_dt", b_dt, (D,), torch.float32)):
+        _require(tuple(t.shape) == shape, f"{name} must have shape {shape}, got {tuple(t.shape)}")
+        _require(t.dtype == dt and t.is_contiguous() and t.device == x.device, f"{name} must be contiguous {dt} on x's device")
+    dev = x.device
+    delta = torch.empty(lead + (D,), dtype=torch.bfloat16, device=dev) if delta is None else delta
+    B = torch.empty(lead + (D_STATE,), dtype=torch.bfloat16, device=dev) if B is None else B
+    C = torch.empty(lead + (D_STATE,), dtype=torch.bfloat16, device=dev) if C is None else C
+    delta_low = torch.empty(lead + (R,), dtype=torch.bfloat16, device=dev) if delta_low is None else delta_low
+    lib = library()
+    with torch.cuda.device(dev):
+        st = lib.jscan_ssm_inputs(_ptr(x), _ptr(w_x), _ptr(g_delta), _ptr(g_B), _ptr(g_C), _ptr(w_dt), _ptr(b_dt),
+                                  _ptr(delta_low), _ptr(delta), _ptr(B), _ptr(C), M, D, R, D_STATE, float(eps),
+                                  JSCAN_BF16, _stream(dev))
+    _check(st)
+    return delta, B, C, delta_low
 
 
 def step_raw(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, dtype):

@@ -8,6 +8,7 @@
 #include "prefill_lane_kernel.h"
 #include "prefill_rows_kernel.h"
 #include "chunk_carry_kernel.h"
+#include "project_kernels.h"
 #include "step_kernel.h"
 
 namespace {
@@ -191,6 +192,21 @@ jscan_status launch_chunked(const void *x, const void *delta, const float *A, co
     return launch_status();
 }
 
+// ---- producer side: delta, B and C from x ---------------------------------------------
+
+template <int R>
+void launch_ssm_inputs(const uint16_t *x, const uint16_t *w_x, const float *g_d, const float *g_b, const float *g_c,
+                       const uint16_t *w_dt, const float *b_dt, uint16_t *d_low, uint16_t *delta, uint16_t *B,
+                       uint16_t *C, int64_t M, int D, float eps, hipStream_t stream) {
+    const int64_t row_tiles = (M + jscan::proj::kRowsX - 1) / jscan::proj::kRowsX;
+    hipLaunchKernelGGL((jscan::xproj_kernel<R / 16>), dim3((unsigned)row_tiles), dim3(256), 0, stream, x, w_x, g_d,
+                       g_b, g_c, d_low, B, C, M, D, eps);
+    const int ch_tiles = D / jscan::proj::kTileDt;
+    const int64_t tok_tiles = (M + jscan::proj::kTileDt - 1) / jscan::proj::kTileDt;
+    hipLaunchKernelGGL((jscan::dtproj_kernel<R>), dim3((unsigned)(tok_tiles * ch_tiles)), dim3(256), 0, stream, d_low,
+                       w_dt, b_dt, delta, M, D, ch_tiles);
+}
+
 // ---- decode step -----------------------------------------------------------------------
 
 template <typename E>
@@ -292,6 +308,43 @@ jscan_status jscan_step(float *h, const void *x_t, const void *delta_t, const fl
     return launch_step<jscan::F32>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s);
 }
 
+jscan_status jscan_ssm_inputs(const void *x, const void *w_x, const float *g_delta, const float *g_B,
+                              const float *g_C, const void *w_dt, const float *b_dt, void *delta_low, void *delta,
+                              void *B, void *C, int64_t M, int64_t D, int64_t R, int64_t N, float eps,
+                              jscan_dtype dtype, void *stream) {
+    if (dtype != JSCAN_F32 && dtype != JSCAN_BF16) return JSCAN_ERR_DTYPE;
+    if (dtype != JSCAN_BF16) return JSCAN_ERR_DTYPE;   // the matrix-core path is bf16 in, fp32 accumulate
+    if (M < 0 || D <= 0 || N != JSCAN_D_STATE || (R != 64 && R != 128 && R != 256)) return JSCAN_ERR_SHAPE;
+    if (D % jscan::proj::kTileDt != 0 || D > (1 << 24)) return JSCAN_ERR_SHAPE;
+    if (!(eps >= 0.0f) || eps > 1.0f) return JSCAN_ERR_SHAPE;
+    const int64_t tok_tiles = (M + jscan::proj::kTileDt - 1) / jscan::proj::kTileDt;
+    if (tok_tiles * (D / jscan::proj::kTileDt) > kMaxBlocks) return JSCAN_ERR_SHAPE;
+    if (M == 0) return JSCAN_OK;
+    const void *arrays[] = {x, w_x, g_delta, g_B, g_C, w_dt, b_dt, delta_low, delta, B, C};
+    for (const void *p : arrays)
+        if (!p) return JSCAN_ERR_NULL;
+    for (const void *p : arrays)
+        if (!aligned16(p)) return JSCAN_ERR_ALIGN;
+    const Span outs[] = {span(delta_low, M * R * 2), span(delta, M * D * 2), span(B, M * N * 2), span(C, M * N * 2)};
+    const Span ins[] = {span(x, M * D * 2),     span(w_x, (R + 2 * N) * D * 2), span(g_delta, R * 4),
+                        span(g_B, N * 4),       span(g_C, N * 4),               span(w_dt, D * R * 2),
+                        span(b_dt, D * 4)};
+    for (int i = 0; i < 4; ++i) {
+        for (const Span &in : ins)
+            if (overlaps(outs[i], in)) return JSCAN_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], outs[j])) return JSCAN_ERR_ALIAS;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    using U = uint16_t;
+    auto xs = static_cast<const U *>(x), wx = static_cast<const U *>(w_x), wd = static_cast<const U *>(w_dt);
+    auto dl = static_cast<U *>(delta_low), de = static_cast<U *>(delta), bo = static_cast<U *>(B), co = static_cast<U *>(C);
+    if (R == 64) launch_ssm_inputs<64>(xs, wx, g_delta, g_B, g_C, wd, b_dt, dl, de, bo, co, M, (int)D, eps, s);
+    else if (R == 128) launch_ssm_inputs<128>(xs, wx, g_delta, g_B, g_C, wd, b_dt, dl, de, bo, co, M, (int)D, eps, s);
+    else launch_ssm_inputs<256>(xs, wx, g_delta, g_B, g_C, wd, b_dt, dl, de, bo, co, M, (int)D, eps, s);
+    return launch_status();
+}
+
 const char *jscan_status_string(jscan_status s) {
     switch (s) {
     case JSCAN_OK: return "ok";
@@ -308,6 +361,6 @@ const char *jscan_status_string(jscan_status s) {
 
 int jscan_last_hip_error(void) { return g_last_hip_error; }
 
-int jscan_version(void) { return 101; }
+int jscan_version(void) { return 102; }
 
 }  // extern "C"

@@ -27,7 +27,7 @@ def test_header_symbols_are_exported():
     names = header_symbols()
     assert {"jscan_prefill", "jscan_prefill_resume", "jscan_step", "jscan_status_string",
             "jscan_last_hip_error", "jscan_version", "jscan_prefill_chunked",
-            "jscan_prefill_chunked_workspace"} <= set(names)
+            "jscan_prefill_chunked_workspace", "jscan_ssm_inputs"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -37,7 +37,7 @@ def test_status_strings_and_version():
     for s in range(8):
         assert lib.jscan_status_string(s) and lib.jscan_status_string(s) != b"unknown status"
     assert lib.jscan_status_string(99) == b"unknown status"
-    assert lib.jscan_version() == 101
+    assert lib.jscan_version() == 102
     assert lib.jscan_last_hip_error() == 0
 
 
@@ -126,6 +126,27 @@ def test_chunked_workspace_sizes():
 ])
 def test_chunked_validation(kw, code):
     assert chunked(**kw) == code
+
+
+def ssm_inputs(x=P, wx=P + 0x100000, gd=P + 0x200000, gb=P + 0x210000, gc=P + 0x220000, wdt=P + 0x300000,
+               bdt=P + 0x400000, dlow=P + 0x500000, delta=P + 0x600000, B=P + 0x700000, C=P + 0x710000,
+               M=256, D=256, R=64, N=16, eps=1e-6, dtype=BF16):
+    return jscan.library().jscan_ssm_inputs(x, wx, gd, gb, gc, wdt, bdt, dlow, delta, B, C, M, D, R, N, eps, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=F32), EDTYPE), (dict(dtype=9), EDTYPE), (dict(R=96), ESHAPE), (dict(N=8), ESHAPE),
+    (dict(D=192), ESHAPE), (dict(M=-1), ESHAPE), (dict(eps=-1.0), ESHAPE), (dict(eps=float("nan")), ESHAPE),
+    (dict(x=None), ENULL), (dict(C=None), ENULL), (dict(gb=P + 0x210004), EALIGN),
+    (dict(delta=P + 0x100000), EALIAS), (dict(B=P + 0x500000 + 256 * 64 * 2 - 16), EALIAS),
+    (dict(C=P + 0x700000 + 16), EALIAS),
+])
+def test_ssm_inputs_validation(kw, code):
+    assert ssm_inputs(**kw) == code
+
+
+def test_ssm_inputs_zero_tokens_is_a_no_op():
+    assert ssm_inputs(M=0, x=None, delta=None) == OK
 
 
 def test_binding_refuses_cpu_tensors():

@@ -1,0 +1,126 @@
+"""jscan_ssm_inputs (the producer side: delta, B and C from x) on the GPU against the fp64
+oracle in oracle/producer.py.
+
+Every output is one rounding of an fp32 value to bf16.  The fp32 value differs from the
+oracle's fp64 value only by accumulation and function rounding, so the two bf16 results are
+equal or one bf16 step apart (when the values straddle a rounding boundary).  The test allows
+one step, |gpu - ref| <= 2^-7 |ref|, element by element, plus an absolute 2^-16 of the
+tensor's largest value: a dot product's fp32 error scales with its terms, not its result, so
+an output that cancels to near zero can miss by more than a step of its own tiny size.  That
+slack is still 500 times below a bf16 step at the tensor's scale.  delta is checked from the
+GPU's own d_low, so a step in d_low does not carry into delta's check.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mamba_selective_scan_03_amd as jscan
+import oracle
+import workloads
+from gpu_util import assert_parity, bits, f64, say
+from oracle import producer as P
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-6
+
+
+def one_step_close(got, ref, what):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    bound = 2.0 ** -7 * np.maximum(np.abs(ref), np.abs(got)) + 2.0 ** -16 * np.max(np.abs(ref))
+    bad = np.abs(got - ref) > bound
+    differ = np.count_nonzero(got != ref)
+    say(f"{what}: {differ} of {ref.size} elements one bf16 step apart, {np.count_nonzero(bad)} beyond")
+    assert not bad.any(), f"{what}: {np.count_nonzero(bad)} elements beyond one bf16 step"
+    assert differ <= max(8, ref.size // 200), f"{what}: too many rounding differences ({differ})"
+
+
+def run(M, D, R, seed=0, rows=None):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(M, D, generator=g).to(torch.bfloat16)
+    wts = workloads.producer_weights(D, R, seed=seed)
+    dev = {k: v.cuda() for k, v in wts.items()}
+    xd = x.cuda()
+    delta, B, C, d_low = jscan.ssm_inputs(xd, dev["w_x"], dev["g_d"], dev["g_b"], dev["g_c"], dev["w_dt"],
+                                          dev["b_dt"], eps=EPS)
+    torch.cuda.synchronize()
+    sel = slice(None) if rows is None else rows
+    xs = x[sel].double().numpy()
+    d_ref, B_ref, C_ref, _ = P.ssm_inputs(xs, wts["w_x"].double().numpy(), wts["g_d"].numpy(), wts["g_b"].numpy(),
+                                          wts["g_c"].numpy(), wts["w_dt"].double().numpy(), wts["b_dt"].numpy(), EPS, R)
+    tag = f"{M}x{D} R={R}"
+    one_step_close(f64(d_low)[sel], d_ref, f"{tag} d_low")
+    one_step_close(f64(B)[sel], B_ref, f"{tag} B")
+    one_step_close(f64(C)[sel], C_ref, f"{tag} C")
+    delta_ref = P.delta_from_low(f64(d_low)[sel], wts["w_dt"].double().numpy(), wts["b_dt"].numpy())
+    one_step_close(f64(delta)[sel], delta_ref, f"{tag} delta (from the GPU's d_low)")
+    return x, wts, (delta, B, C, d_low)
+
+
+@pytest.mark.parametrize("M,D,R", [
+    (256, 256, 64),      # whole tiles
+    (1000, 512, 128),    # ragged last row tile
+    (777, 1024, 256),    # the full rank, ragged
+    (1, 128, 256),       # a single token (decode-sized)
+])
+def test_ssm_inputs_match_oracle(M, D, R):
+    run(M, D, R, seed=M + D)
+
+
+def test_ssm_inputs_deterministic():
+    x = torch.randn(513, 512, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).cuda()
+    w = {k: v.cuda() for k, v in workloads.producer_weights(512, 128).items()}
+    a = jscan.ssm_inputs(x, w["w_x"], w["g_d"], w["g_b"], w["g_c"], w["w_dt"], w["b_dt"])
+    b = jscan.ssm_inputs(x, w["w_x"], w["g_d"], w["g_b"], w["g_c"], w["w_dt"], w["b_dt"])
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(bits(u), bits(v))
+
+
+def test_producer_then_scan_against_oracle():
+    """x -> (delta, B, C) -> scan, end to end, against the oracle doing the same two stages
+    (the oracle scan is fed the oracle's own bf16 delta, B and C)."""
+    L, D, R = 1024, 512, 256
+    inp = workloads.small_prefill(1, L, D, "bf16", seed=12)
+    wts = workloads.producer_weights(D, R, seed=12)
+    dev = {k: v.cuda() for k, v in wts.items()}
+    x = inp["x"].cuda()
+    delta, B, C, _ = jscan.ssm_inputs(x, dev["w_x"], dev["g_d"], dev["g_b"], dev["g_c"], dev["w_dt"], dev["b_dt"])
+    A = inp["A"].cuda()
+    y, h = jscan.prefill(x, delta, A, B, C)
+    torch.cuda.synchronize()
+    d_ref, B_ref, C_ref, delta_ref = P.ssm_inputs(inp["x"][0].double().numpy(), wts["w_x"].double().numpy(),
+                                                  wts["g_d"].numpy(), wts["g_b"].numpy(), wts["g_c"].numpy(),
+                                                  wts["w_dt"].double().numpy(), wts["b_dt"].numpy(), 1e-6, R)
+    y_ref, h_ref = oracle.prefill(inp["x"].double().numpy(), delta_ref[None], inp["A"].double().numpy(), B_ref[None],
+                                  C_ref[None])
+    assert_parity(f64(y), y_ref, torch.bfloat16, "producer + scan y")
+    assert_parity(f64(h), h_ref, torch.bfloat16, "producer + scan h_final")
+
+
+def test_ssm_inputs_full_size_sampled_rows():
+    """The 64K x 8192 workload's x through the producer at full size (R = 256), checked on
+    sampled rows (rows are independent): the first and last rows of row tiles and random ones."""
+    wl = workloads.get("prefill_64k")
+    say("generating prefill_64k x")
+    x = workloads.prefill_inputs(wl)["x"][0]
+    wts = workloads.producer_weights(wl.D, 256)
+    dev = {k: v.cuda() for k, v in wts.items()}
+    delta, B, C, d_low = jscan.ssm_inputs(x.cuda(), dev["w_x"], dev["g_d"], dev["g_b"], dev["g_c"], dev["w_dt"],
+                                          dev["b_dt"])
+    torch.cuda.synchronize()
+    rows = sorted(set([0, 1, 127, 128, 129, 4095, 32768, 65535] +
+                      np.random.default_rng(3).choice(wl.L, 24, replace=False).tolist()))
+    idx = torch.tensor(rows)
+    xs = x[idx].double().numpy()
+    d_ref, B_ref, C_ref, _ = P.ssm_inputs(xs, wts["w_x"].double().numpy(), wts["g_d"].numpy(), wts["g_b"].numpy(),
+                                          wts["g_c"].numpy(), wts["w_dt"].double().numpy(), wts["b_dt"].numpy(), EPS,
+                                          256)
+    dl = f64(d_low.cpu()[idx])
+    one_step_close(dl, d_ref, "64K d_low (sampled rows)")
+    one_step_close(f64(B.cpu()[idx]), B_ref, "64K B (sampled rows)")
+    one_step_close(f64(C.cpu()[idx]), C_ref, "64K C (sampled rows)")
+    one_step_close(f64(delta.cpu()[idx]), P.delta_from_low(dl, wts["w_dt"].double().numpy(), wts["b_dt"].numpy()),
+                   "64K delta (sampled rows)")
+    assert torch.isfinite(delta.float()).all() and float(delta.float().min()) > 0
