@@ -33,6 +33,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "selective-scan elems/s (B·L·D) + HBM GB/s % of peak, L=64K D=8192 N=16"
 HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0                # dense bf16 matrix-core peak of MI355X
+PRODUCER_RANK = 256                           # rank of delta's projection (d_model 4096 / 16)
 VALU_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9      # fp32 lane-instructions per second (no packed math)
 SLOTS_PER_STATE_ELEM = 6                      # mul, exp (2 slots), mul, fma, fma
 FLOPS_PER_STATE_ELEM = 7                      # mul 1 + exp 1 + mul 1 + fma 2 + fma 2
@@ -110,6 +112,9 @@ def main():
     ap.add_argument("--workload", default="prefill_64k",
                     choices=["prefill_64k", "prefill_4k", "prefill_256k", "decode_256x28", "tiny_fp32",
                              "prefill_64k_tp8"])
+    ap.add_argument("--producer", action="store_true",
+                    help="prefill workloads: compute delta, B and C from x with jscan_ssm_inputs (synthetic weights, "
+                         "rank 256) inside each step, then scan")
     ap.add_argument("--chunked", action="store_true",
                     help="prefill through the time-parallel jscan_prefill_chunked (automatic segments) instead of "
                          "the token-by-token jscan_prefill")
@@ -192,7 +197,28 @@ def main():
         y = torch.empty_like(d["x"])
         h = torch.empty((wl.batch, wl.D, wl.N), dtype=torch.float32, device=dev)
 
-        if args.chunked:
+        if args.producer:
+            if wl.dtype != "bf16":
+                print("bench.py: --producer needs a bf16 workload", file=sys.stderr)
+                sys.exit(2)
+            pw = {k: v.to(dev) for k, v in workloads.producer_weights(wl.D, PRODUCER_RANK).items()}
+            d["delta"] = torch.empty_like(d["x"])
+            d["B"] = torch.empty_like(d["B"])
+            d["C"] = torch.empty_like(d["C"])
+            d_low = torch.empty((wl.batch, wl.L, PRODUCER_RANK), dtype=torch.bfloat16, device=dev)
+
+            def produce():
+                jscan.ssm_inputs(d["x"], pw["w_x"], pw["g_d"], pw["g_b"], pw["g_c"], pw["w_dt"], pw["b_dt"],
+                                 delta=d["delta"], B=d["B"], C=d["C"], delta_low=d_low)
+
+            def scan():
+                jscan.prefill(d["x"], d["delta"], d["A"], d["B"], d["C"], y=y, h_final=h)
+
+            def one_step():
+                produce()
+                scan()
+            launches = 3
+        elif args.chunked:
             ws_bytes = jscan.chunked_workspace_bytes(wl.batch, wl.L, wl.D)
             ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
             log(f"time-parallel prefill: {ws_bytes} bytes of workspace")
@@ -228,6 +254,31 @@ def main():
     alg_bytes = algorithmic_bytes(wl)
     gbps = alg_bytes / (ms_step * 1e-3) / 1e9
     per_launch_ms = ms_step / launches
+    producer_info = None
+    if args.producer:
+        # time the two stages alone too (same stream, HIP events), for the per-stage rooflines
+        def timed(fn, n):
+            fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(n):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / n
+        p_ms, s_ms = timed(produce, args.steps), timed(scan, args.steps)
+        tokens = wl.batch * wl.L
+        flops = 2 * tokens * wl.D * (PRODUCER_RANK + 2 * wl.N) + 2 * tokens * PRODUCER_RANK * wl.D
+        hbm = tokens * wl.D * 2 * 2 + tokens * (PRODUCER_RANK + 2 * wl.N) * 2 * 2
+        producer_info = {"ms": round(p_ms, 4), "scan_ms": round(s_ms, 4), "rank": PRODUCER_RANK,
+                         "mfma_TFLOPs": round(flops / (p_ms * 1e-3) / 1e12, 1), "mfma_peak_TFLOPs": BF16_MFMA_PEAK_TFLOPS,
+                         "mfma_frac": round(flops / (p_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                         "hbm_GBps": round(hbm / (p_ms * 1e-3) / 1e9, 1),
+                         "hbm_frac": round(hbm / (p_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        log(f"producer {p_ms:.3f} ms, scan {s_ms:.3f} ms")
+        # the scan kernel stays the dominant kernel for the roofline object below
+        per_launch_ms = s_ms
     if args.chunked:
         # three launches per step (segment summaries, carry, rescan): the line reports the
         # whole pass against the one-pass ALU bound
@@ -242,7 +293,7 @@ def main():
         peak_tf = PEAK_STATE_ELEMS * FLOPS_PER_STATE_ELEM / 1e12
         roofline = {"bound": "alu", "achieved": round(achieved_tf, 2), "peak": round(peak_tf, 2), "unit": "TFLOP/s",
                     "frac": round(achieved_tf / peak_tf, 4)}
-    roofline["traffic"] = None if args.chunked else read_traffic(wl.name, launches)
+    roofline["traffic"] = None if (args.chunked or args.producer) else read_traffic(wl.name, launches)
 
     out = {
         "metric": METRIC,
@@ -259,12 +310,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "L": wl.L, "D": wl.D, "N": wl.N,
                    "layers": wl.layers, "io_dtype": wl.dtype, "state_dtype": "f32",
-                   "path": "time-parallel" if args.chunked else "sequential"},
+                   "path": "producer+scan" if args.producer else ("time-parallel" if args.chunked else "sequential")},
         "hbm_GBps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": alg_bytes,
         "roofline": roofline,
     }
+    if producer_info is not None:
+        out["producer"] = producer_info
     if host_inp is not None and args.cpu_channels > 0 and wl.layers == 1:
         out["cpu_baseline"] = cpu_baseline(wl, host_inp, min(args.cpu_channels, wl.D))
         log(f"oracle sample: {out['cpu_baseline']['sample']}")

@@ -201,10 +201,13 @@ void launch_ssm_inputs(const uint16_t *x, const uint16_t *w_x, const float *g_d,
     const int64_t row_tiles = (M + jscan::proj::kRowsX - 1) / jscan::proj::kRowsX;
     hipLaunchKernelGGL((jscan::xproj_kernel<R / 16>), dim3((unsigned)row_tiles), dim3(256), 0, stream, x, w_x, g_d,
                        g_b, g_c, d_low, B, C, M, D, eps);
+    // one work-group per CU (the LDS tiles allow one): 256 groups of (channel slice, token tiles)
     const int ch_tiles = D / jscan::proj::kTileDt;
     const int64_t tok_tiles = (M + jscan::proj::kTileDt - 1) / jscan::proj::kTileDt;
-    hipLaunchKernelGGL((jscan::dtproj_kernel<R>), dim3((unsigned)(tok_tiles * ch_tiles)), dim3(256), 0, stream, d_low,
-                       w_dt, b_dt, delta, M, D, ch_tiles);
+    int64_t groups = ch_tiles >= 256 ? 1 : 256 / ch_tiles;
+    if (groups > tok_tiles) groups = tok_tiles;
+    hipLaunchKernelGGL((jscan::dtproj_kernel<R>), dim3((unsigned)(groups * ch_tiles)), dim3(256), 0, stream, d_low,
+                       w_dt, b_dt, delta, M, D, ch_tiles, (int)groups);
 }
 
 // ---- decode step -----------------------------------------------------------------------

@@ -75,9 +75,6 @@ template <typename E> struct TileRegs {
     typename Vec4<E>::raw bc[2];         // B (threads 0-127) or C (128-255): one token, 8 states
 };
 
-template <int V> struct IntConst {
-    static constexpr int value = V;
-};
 
 // DPP row broadcast of lane k of each 16-lane row (row_newbcast:k).
 template <int k> __device__ __forceinline__ float row_bcast(float v) {

@@ -25,6 +25,7 @@ namespace jscan {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));   // 16 raw bytes in registers
 
 namespace proj {
 constexpr int kRowsX = 128;   // x-projection rows (tokens) per work-group: 4 waves x 32
@@ -33,7 +34,7 @@ constexpr int kTileDt = 128;  // delta-projection tile: 128 channels x 128 token
 
 // 8 consecutive bf16 (16 bytes) as an MFMA operand.
 __device__ __forceinline__ bf16x8_t load_frag(const uint16_t *p) {
-    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(p));
+    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(p));
 }
 
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
@@ -61,8 +62,72 @@ __device__ __forceinline__ float softplus_f32(float z) {
 
 // x projection: one work-group = 128 rows (tokens) x all R + 2N output columns; wave w owns
 // rows 32w .. 32w+31 as two 16-row tiles.  RT = R / 16 column tiles of d_low, then one tile
-// each of B and C (N = 16).  The K loop walks D in steps of 32 with the next step's operands
-// loaded while the current step's MFMAs run.
+// each of B and C (N = 16).  K (= D) goes in stages of 64: each stage's x tile [128][64] and
+// W_x tile [16 CT][64] are loaded by all 256 threads into registers two stages ahead, then
+// written to LDS (double-buffered) for the waves' MFMA operand reads.  LDS rows are padded to
+// 72 bf16 (144 bytes), so the 16 rows one operand read touches fall on distinct banks.
+namespace proj {
+constexpr int kStageK = 64;          // K per stage
+constexpr int kLdsRow = 72;          // bf16 per LDS row (64 + 8 padding)
+}
+
+// (ext_vector_type, not HIP's uint4 struct: copies of the struct type become memcpys that
+// keep the whole set in scratch memory)
+template <int CT> struct XprojRegs {
+    u32x4_t xr[4];          // x: 128 rows x 8 chunks of 16 bytes = 1024 chunks, 4 per thread
+    u32x4_t wr[CT / 2];     // W_x: 16 CT rows x 8 chunks = 128 CT chunks, CT / 2 per thread
+};
+
+template <int CT>
+__device__ __forceinline__ void xproj_load(XprojRegs<CT> &g, const uint16_t *x, const uint16_t *w, int64_t row_base,
+                                           int64_t M, int D, int k0, int tid) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int i = tid + 256 * j, r = i >> 3, part = i & 7;
+        g.xr[j] = *reinterpret_cast<const u32x4_t *>(x + min(row_base + r, M - 1) * D + k0 + 8 * part);
+    }
+#pragma unroll
+    for (int j = 0; j < CT / 2; ++j) {
+        const int i = tid + 256 * j, r = i >> 3, part = i & 7;
+        g.wr[j] = *reinterpret_cast<const u32x4_t *>(w + (int64_t)r * D + k0 + 8 * part);
+    }
+}
+
+template <int CT>
+__device__ __forceinline__ void xproj_store(const XprojRegs<CT> &g, uint16_t *xs, uint16_t *ws, int tid) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int i = tid + 256 * j, r = i >> 3, part = i & 7;
+        *reinterpret_cast<u32x4_t *>(xs + r * proj::kLdsRow + 8 * part) = g.xr[j];
+    }
+#pragma unroll
+    for (int j = 0; j < CT / 2; ++j) {
+        const int i = tid + 256 * j, r = i >> 3, part = i & 7;
+        *reinterpret_cast<u32x4_t *>(ws + r * proj::kLdsRow + 8 * part) = g.wr[j];
+    }
+}
+
+// One stage's MFMAs of one wave: its 32 rows (two 16-row tiles) against all CT column tiles,
+// two 32-wide k steps, operands read from LDS.
+template <int CT>
+__device__ __forceinline__ void xproj_mfma(f32x4_t (&acc)[2][CT], const uint16_t *xs, const uint16_t *ws, int wave,
+                                           int r16, int kq) {
+    const uint16_t *xw = xs + (wave * 32 + r16) * proj::kLdsRow + kq;
+    const uint16_t *wb = ws + r16 * proj::kLdsRow + kq;
+#pragma unroll
+    for (int kk = 0; kk < proj::kStageK; kk += 32) {
+        const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(xw + kk));
+        const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(xw + 16 * proj::kLdsRow + kk));
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+            const bf16x8_t b =
+                __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(wb + 16 * c * proj::kLdsRow + kk));
+            acc[0][c] = mfma16(a0, b, acc[0][c]);
+            acc[1][c] = mfma16(a1, b, acc[1][c]);
+        }
+    }
+}
+
 template <int RT>
 __global__ __launch_bounds__(256) void xproj_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                                                     const float *__restrict__ g_d, const float *__restrict__ g_b,
@@ -70,14 +135,14 @@ __global__ __launch_bounds__(256) void xproj_kernel(const uint16_t *__restrict__
                                                     uint16_t *__restrict__ Bo, uint16_t *__restrict__ Co, int64_t M,
                                                     int D, float eps) {
     constexpr int CT = RT + 2;   // column tiles
-    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int64_t row0 = (int64_t)blockIdx.x * proj::kRowsX + wave * 32;
+    constexpr int kXs = proj::kRowsX * proj::kLdsRow, kWs = 16 * CT * proj::kLdsRow;
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][kXs];
+    __shared__ __attribute__((aligned(16))) uint16_t ws[2][kWs];
+    const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+    const int64_t row_base = (int64_t)blockIdx.x * proj::kRowsX;
+    const int64_t row0 = row_base + wave * 32;
     const int r16 = l & 15, kq = 8 * (l >> 4);
-    // A rows of this lane (clamped: rows past M compute garbage that is never stored)
-    const uint16_t *xa[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) xa[t] = x + min(row0 + 16 * t + r16, M - 1) * D + kq;
-    const uint16_t *wb = w + (int64_t)r16 * D + kq;   // column tile c adds 16 * c * D
+    const int stages = D / proj::kStageK;
 
     f32x4_t acc[2][CT];
 #pragma unroll
@@ -85,25 +150,31 @@ __global__ __launch_bounds__(256) void xproj_kernel(const uint16_t *__restrict__
 #pragma unroll
         for (int c = 0; c < CT; ++c) acc[t][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    bf16x8_t a[2][2], b[2][CT];
-    auto load = [&](int s, int k0) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) a[s][t] = load_frag(xa[t] + k0);
-#pragma unroll
-        for (int c = 0; c < CT; ++c) b[s][c] = load_frag(wb + (int64_t)16 * c * D + k0);
-    };
-    auto step = [&](int s) {
-#pragma unroll
-        for (int c = 0; c < CT; ++c)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) acc[t][c] = mfma16(a[s][t], b[s][c], acc[t][c]);
-    };
-    load(0, 0);
-    for (int k0 = 0; k0 < D; k0 += 64) {   // D % 64 == 0
-        load(1, k0 + 32);
-        step(0);
-        if (k0 + 64 < D) load(0, k0 + 64);
-        step(1);
+    // Two named register sets (not an array) so that nothing is indexed at run time.
+    XprojRegs<CT> Ga, Gb;
+    xproj_load<CT>(Ga, x, w, row_base, M, D, 0, tid);
+    if (stages > 1) xproj_load<CT>(Gb, x, w, row_base, M, D, proj::kStageK, tid);
+    xproj_store<CT>(Ga, xs[0], ws[0], tid);
+    if (stages > 2) xproj_load<CT>(Ga, x, w, row_base, M, D, 2 * proj::kStageK, tid);
+    __syncthreads();
+
+    // Stage s: MFMAs from LDS buffer s & 1; stage s+1 (in registers since stage s-2) goes to the
+    // other buffer, and stage s+3 is requested into the registers it leaves.
+    for (int s = 0; s < stages; s += 2) {
+        xproj_mfma<CT>(acc, xs[0], ws[0], wave, r16, kq);
+        if (s + 1 < stages) {
+            xproj_store<CT>(Gb, xs[1], ws[1], tid);
+            if (s + 3 < stages) xproj_load<CT>(Gb, x, w, row_base, M, D, (s + 3) * proj::kStageK, tid);
+        }
+        __syncthreads();
+        if (s + 1 < stages) {
+            xproj_mfma<CT>(acc, xs[1], ws[1], wave, r16, kq);
+            if (s + 2 < stages) {
+                xproj_store<CT>(Ga, xs[0], ws[0], tid);
+                if (s + 4 < stages) xproj_load<CT>(Ga, x, w, row_base, M, D, (s + 4) * proj::kStageK, tid);
+            }
+            __syncthreads();
+        }
     }
 
     // Epilogue.  Lane l holds rows 4 * (l / 16) + i of each 16-row tile, column 16 c + l % 16.
@@ -134,55 +205,99 @@ __global__ __launch_bounds__(256) void xproj_kernel(const uint16_t *__restrict__
     }
 }
 
-// Delta projection: one work-group = 128 channels x 128 tokens of delta; wave w owns
-// channels 64 (w & 1) .. +63 and tokens 64 (w >> 1) .. +63 as 4 x 4 MFMA tiles.  A = W_dt
-// (rows = channels), B = d_low^T (columns = tokens), so each lane's result is 4 consecutive
-// channels of one token: the epilogue adds the bias, applies softplus and writes 8 bytes.
+// Delta projection.  A work-group owns one 128-channel slice of W_dt and walks the token
+// tiles t = g, g + G, g + 2G, ... (G groups per channel slice).  Each wave keeps its 64
+// channels of W_dt as MFMA A operands in registers for the whole kernel; each 128-token tile
+// of d_low is loaded by all 256 threads into registers one tile ahead and stored to LDS
+// (double-buffered, rows padded to R + 8 bf16), from where the waves read their B operands
+// (wave w: channels 64 (w & 1) .. +63, tokens 64 (w >> 1) .. +63 of the tile).  A = W_dt and
+// B = d_low^T, so each lane's result is 4 consecutive channels of one token: the epilogue adds
+// the bias, applies softplus and writes 8 bytes.
 template <int R>
 __global__ __launch_bounds__(256) void dtproj_kernel(const uint16_t *__restrict__ d_low, const uint16_t *__restrict__ w,
                                                      const float *__restrict__ bias, uint16_t *__restrict__ delta,
-                                                     int64_t M, int D, int ch_tiles) {
-    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int64_t tok_tile = blockIdx.x / ch_tiles;
-    const int ch0 = (blockIdx.x - (int)(tok_tile * ch_tiles)) * proj::kTileDt + 64 * (wave & 1);
-    const int64_t tok0 = tok_tile * proj::kTileDt + 64 * (wave >> 1);
+                                                     int64_t M, int D, int ch_tiles, int groups) {
+    constexpr int KS = R / 32;                 // MFMA k steps
+    constexpr int kRow = R + 8;                // LDS row (bf16), padded
+    constexpr int kChunks = proj::kTileDt * R / 8 / 256;   // 16-byte chunks of a d_low tile per thread
+    __shared__ __attribute__((aligned(16))) uint16_t ds[2][proj::kTileDt * kRow];
+    const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+    const int ct = blockIdx.x % ch_tiles, grp = blockIdx.x / ch_tiles;
+    const int ch0 = ct * proj::kTileDt + 64 * (wave & 1);
+    const int tw = 64 * (wave >> 1);           // this wave's token offset inside a tile
     const int r16 = l & 15, kq = 8 * (l >> 4);
-    const uint16_t *wa = w + (int64_t)(ch0 + r16) * R + kq;                // channel tile u adds 16 u R
-    const uint16_t *db[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) db[v] = d_low + min(tok0 + 16 * v + r16, M - 1) * R + kq;
+    const int64_t tok_tiles = (M + proj::kTileDt - 1) / proj::kTileDt;
 
-    f32x4_t acc[4][4];
+    bf16x8_t a[4][KS];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[u][v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < KS; ++ks) a[u][ks] = load_frag(w + (int64_t)(ch0 + 16 * u + r16) * R + 32 * ks + kq);
+    float4 bs[4];
 #pragma unroll
-    for (int k0 = 0; k0 < R; k0 += 32) {
-        bf16x8_t a[4], b[4];
+    for (int u = 0; u < 4; ++u) bs[u] = *reinterpret_cast<const float4 *>(bias + ch0 + 16 * u + 4 * (l >> 4));
+
+    u32x4_t pre[kChunks];
+    auto load_tile = [&](int64_t t) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) a[u] = load_frag(wa + 16 * u * R + k0);
+        for (int j = 0; j < kChunks; ++j) {
+            const int i = tid + 256 * j, r = i / (R / 8), part = i % (R / 8);
+            pre[j] = *reinterpret_cast<const u32x4_t *>(d_low + min(t * proj::kTileDt + r, M - 1) * R + 8 * part);
+        }
+    };
+    auto store_tile = [&](uint16_t *dst) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) b[v] = load_frag(db[v] + k0);
+        for (int j = 0; j < kChunks; ++j) {
+            const int i = tid + 256 * j, r = i / (R / 8), part = i % (R / 8);
+            *reinterpret_cast<u32x4_t *>(dst + r * kRow + 8 * part) = pre[j];
+        }
+    };
+
+    int buf = 0;
+    if (grp < tok_tiles) {
+        load_tile(grp);
+        store_tile(ds[0]);
+    }
+    __syncthreads();
+    for (int64_t t = grp; t < tok_tiles; t += groups) {
+        const int64_t tn = t + groups;
+        if (tn < tok_tiles) load_tile(tn);      // in flight during this tile's MFMAs
+        const uint16_t *bt = ds[buf] + (tw + r16) * kRow + kq;
+        f32x4_t acc[4][4];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[u][v] = mfma16(a[u], b[v], acc[u][v]);
-    }
+            for (int v = 0; v < 4; ++v) acc[u][v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int c = ch0 + 16 * u + 4 * (l >> 4);
-        const float4 bs = *reinterpret_cast<const float4 *>(bias + c);
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8_t b[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t tok = tok0 + 16 * v + r16;
-            if (tok < M) {
-                uint2 pk;
-                pk.x = pack_bf16x2(softplus_f32(acc[u][v][0] + bs.x), softplus_f32(acc[u][v][1] + bs.y));
-                pk.y = pack_bf16x2(softplus_f32(acc[u][v][2] + bs.z), softplus_f32(acc[u][v][3] + bs.w));
-                *reinterpret_cast<uint2 *>(delta + tok * D + c) = pk;
+            for (int v = 0; v < 4; ++v)
+                b[v] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(bt + 16 * v * kRow + 32 * ks));
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[u][v] = mfma16(a[u][ks], b[v], acc[u][v]);
+        }
+        // the next tile goes to LDS before this tile's stores are issued: waiting for its loads
+        // then does not also wait for fresh stores (one counter covers both)
+        if (tn < tok_tiles) store_tile(ds[buf ^ 1]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = ch0 + 16 * u + 4 * (l >> 4);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t tok = t * proj::kTileDt + tw + 16 * v + r16;
+                if (tok < M) {
+                    uint2 pk;
+                    pk.x = pack_bf16x2(softplus_f32(acc[u][v][0] + bs[u].x), softplus_f32(acc[u][v][1] + bs[u].y));
+                    pk.y = pack_bf16x2(softplus_f32(acc[u][v][2] + bs[u].z), softplus_f32(acc[u][v][3] + bs[u].w));
+                    *reinterpret_cast<uint2 *>(delta + tok * D + c) = pk;
+                }
             }
         }
+        buf ^= 1;
+        __syncthreads();
     }
 }
 

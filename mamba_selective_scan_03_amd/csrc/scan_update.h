@@ -35,6 +35,12 @@ __device__ __forceinline__ float advance(float h, float delta, float a2, float d
     return __builtin_fmaf(decay(delta, a2), h, dx * b);
 }
 
+// A compile-time integer as a value: lets an unrolled loop body pick register sets and LDS
+// buffers by constant index.
+template <int V> struct IntConst {
+    static constexpr int value = V;
+};
+
 // ---- rows of work ----------------------------------------------------------------------
 
 // The prefill kernels walk "rows": a run of consecutive tokens of one sequence, scanned in
