@@ -206,7 +206,7 @@ void launch_ssm_inputs(const uint16_t *x, const uint16_t *w_x, const float *g_d,
     const int64_t tok_tiles = (M + jscan::proj::kTileDt - 1) / jscan::proj::kTileDt;
     int64_t groups = ch_tiles >= 256 ? 1 : 256 / ch_tiles;
     if (groups > tok_tiles) groups = tok_tiles;
-    hipLaunchKernelGGL((jscan::dtproj_kernel<R>), dim3((unsigned)(groups * ch_tiles)), dim3(256), 0, stream, d_low,
+    hipLaunchKernelGGL((jscan::dtproj_kernel<R>), dim3((unsigned)(groups * ch_tiles)), dim3(512), 0, stream, d_low,
                        w_dt, b_dt, delta, M, D, ch_tiles, (int)groups);
 }
 

@@ -51,12 +51,13 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
-// softplus(z) = log(1 + e^z) = max(z, 0) + log1p(e^-|z|), with e^-|z| in (0, 1].
+// softplus(z) = log(1 + e^z) = max(z, 0) + log1p(e^-|z|), with t = e^-|z| in (0, 1].
+// log1p(t) is the hardware log2 of 1 + t, except below t = 2^-10, where 1 + t would lose t's
+// low bits and log1p(t) = t (1 - t/2 + ...) is t to within t/2 <= 2^-11 relative, below the
+// bf16 precision (2^-8) the result is stored with.
 __device__ __forceinline__ float softplus_f32(float z) {
     const float t = __builtin_amdgcn_exp2f(-fabsf(z) * kLog2e);
-    // log1p(t): the series where 1 + t would lose t's low bits, the hardware log2 elsewhere
-    const float l = t < 0x1.0p-10f ? t * (1.0f - t * (0.5f - t * (1.0f / 3.0f)))
-                                   : __builtin_amdgcn_logf(1.0f + t) * 0.69314718055994530942f;
+    const float l = t < 0x1.0p-10f ? t : __builtin_amdgcn_logf(1.0f + t) * 0.69314718055994530942f;
     return fmaxf(z, 0.0f) + l;
 }
 
@@ -208,23 +209,24 @@ __global__ __launch_bounds__(256) void xproj_kernel(const uint16_t *__restrict__
 // Delta projection.  A work-group owns one 128-channel slice of W_dt and walks the token
 // tiles t = g, g + G, g + 2G, ... (G groups per channel slice).  Each wave keeps its 64
 // channels of W_dt as MFMA A operands in registers for the whole kernel; each 128-token tile
-// of d_low is loaded by all 256 threads into registers one tile ahead and stored to LDS
+// of d_low is loaded by all 512 threads into registers one tile ahead and stored to LDS
 // (double-buffered, rows padded to R + 8 bf16), from where the waves read their B operands
-// (wave w: channels 64 (w & 1) .. +63, tokens 64 (w >> 1) .. +63 of the tile).  A = W_dt and
+// (wave w of 8: channels 64 (w & 1) .. +63, tokens 32 (w >> 1) .. +31 of the tile).  Two waves
+// per SIMD let one wave's softplus epilogue overlap the other's matrix work.  A = W_dt and
 // B = d_low^T, so each lane's result is 4 consecutive channels of one token: the epilogue adds
 // the bias, applies softplus and writes 8 bytes.
 template <int R>
-__global__ __launch_bounds__(256) void dtproj_kernel(const uint16_t *__restrict__ d_low, const uint16_t *__restrict__ w,
+__global__ __launch_bounds__(512) void dtproj_kernel(const uint16_t *__restrict__ d_low, const uint16_t *__restrict__ w,
                                                      const float *__restrict__ bias, uint16_t *__restrict__ delta,
                                                      int64_t M, int D, int ch_tiles, int groups) {
     constexpr int KS = R / 32;                 // MFMA k steps
     constexpr int kRow = R + 8;                // LDS row (bf16), padded
-    constexpr int kChunks = proj::kTileDt * R / 8 / 256;   // 16-byte chunks of a d_low tile per thread
+    constexpr int kChunks = proj::kTileDt * R / 8 / 512;   // 16-byte chunks of a d_low tile per thread
     __shared__ __attribute__((aligned(16))) uint16_t ds[2][proj::kTileDt * kRow];
     const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
     const int ct = blockIdx.x % ch_tiles, grp = blockIdx.x / ch_tiles;
     const int ch0 = ct * proj::kTileDt + 64 * (wave & 1);
-    const int tw = 64 * (wave >> 1);           // this wave's token offset inside a tile
+    const int tw = 32 * (wave >> 1);           // this wave's token offset inside a tile
     const int r16 = l & 15, kq = 8 * (l >> 4);
     const int64_t tok_tiles = (M + proj::kTileDt - 1) / proj::kTileDt;
 
@@ -241,14 +243,14 @@ __global__ __launch_bounds__(256) void dtproj_kernel(const uint16_t *__restrict_
     auto load_tile = [&](int64_t t) {
 #pragma unroll
         for (int j = 0; j < kChunks; ++j) {
-            const int i = tid + 256 * j, r = i / (R / 8), part = i % (R / 8);
+            const int i = tid + 512 * j, r = i / (R / 8), part = i % (R / 8);
             pre[j] = *reinterpret_cast<const u32x4_t *>(d_low + min(t * proj::kTileDt + r, M - 1) * R + 8 * part);
         }
     };
     auto store_tile = [&](uint16_t *dst) {
 #pragma unroll
         for (int j = 0; j < kChunks; ++j) {
-            const int i = tid + 256 * j, r = i / (R / 8), part = i % (R / 8);
+            const int i = tid + 512 * j, r = i / (R / 8), part = i % (R / 8);
             *reinterpret_cast<u32x4_t *>(dst + r * kRow + 8 * part) = pre[j];
         }
     };
@@ -263,21 +265,21 @@ __global__ __launch_bounds__(256) void dtproj_kernel(const uint16_t *__restrict_
         const int64_t tn = t + groups;
         if (tn < tok_tiles) load_tile(tn);      // in flight during this tile's MFMAs
         const uint16_t *bt = ds[buf] + (tw + r16) * kRow + kq;
-        f32x4_t acc[4][4];
+        f32x4_t acc[4][2];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[u][v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int v = 0; v < 2; ++v) acc[u][v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            bf16x8_t b[4];
+            bf16x8_t b[2];
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
+            for (int v = 0; v < 2; ++v)
                 b[v] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(bt + 16 * v * kRow + 32 * ks));
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[u][v] = mfma16(a[u][ks], b[v], acc[u][v]);
+                for (int v = 0; v < 2; ++v) acc[u][v] = mfma16(a[u][ks], b[v], acc[u][v]);
         }
         // the next tile goes to LDS before this tile's stores are issued: waiting for its loads
         // then does not also wait for fresh stores (one counter covers both)
@@ -286,7 +288,7 @@ __global__ __launch_bounds__(256) void dtproj_kernel(const uint16_t *__restrict_
         for (int u = 0; u < 4; ++u) {
             const int c = ch0 + 16 * u + 4 * (l >> 4);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
+            for (int v = 0; v < 2; ++v) {
                 const int64_t tok = t * proj::kTileDt + tw + 16 * v + r16;
                 if (tok < M) {
                     uint2 pk;
