@@ -93,6 +93,8 @@ jscan_status check_prefill(const void *x, const void *delta, const float *A, con
     if (batch < 0 || L < 0 || D < 0 || N != JSCAN_D_STATE || D % 8 != 0) return JSCAN_ERR_SHAPE;
     // index arithmetic inside the kernels: rows of D fit in int, grid sizes in 32 bits
     if (D > (1 << 24) || batch > (1 << 20) || batch * ((D + 63) / 64) > kMaxBlocks) return JSCAN_ERR_SHAPE;
+    // the state-wide kernels (empty-sequence copy, segment carry) run one thread per element
+    if (batch * D * JSCAN_D_STATE / 256 > kMaxBlocks) return JSCAN_ERR_SHAPE;
     if (batch == 0 || D == 0) {
         *nothing_to_do = true;
         return JSCAN_OK;
