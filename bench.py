@@ -40,7 +40,7 @@ SLOTS_PER_STATE_ELEM = 6                      # mul, exp (2 slots), mul, fma, fm
 FLOPS_PER_STATE_ELEM = 7                      # mul 1 + exp 1 + mul 1 + fma 2 + fma 2
 PEAK_STATE_ELEMS = VALU_SLOTS_PER_S / SLOTS_PER_STATE_ELEM
 KERNEL_SOURCES = {
-    "prefill": ["scan_update.h", "prefill_rows_kernel.h"],
+    "prefill": ["scan_update.h", "project_kernels.h", "prefill_rows_kernel.h"],
     "step": ["scan_update.h", "step_kernel.h"],
 }
 
@@ -115,6 +115,8 @@ def main():
     ap.add_argument("--producer", action="store_true",
                     help="prefill workloads: compute delta, B and C from x with jscan_ssm_inputs (synthetic weights, "
                          "rank 256) inside each step, then scan")
+    ap.add_argument("--fused", action="store_true",
+                    help="with --producer: compute delta inside the scan (jscan_prefill_fused) instead of storing it")
     ap.add_argument("--chunked", action="store_true",
                     help="prefill through the time-parallel jscan_prefill_chunked (automatic segments) instead of "
                          "the token-by-token jscan_prefill")
@@ -207,17 +209,25 @@ def main():
             d["C"] = torch.empty_like(d["C"])
             d_low = torch.empty((wl.batch, wl.L, PRODUCER_RANK), dtype=torch.bfloat16, device=dev)
 
-            def produce():
-                jscan.ssm_inputs(d["x"], pw["w_x"], pw["g_d"], pw["g_b"], pw["g_c"], pw["w_dt"], pw["b_dt"],
-                                 delta=d["delta"], B=d["B"], C=d["C"], delta_low=d_low)
+            if args.fused:
+                def produce():
+                    jscan.ssm_inputs(d["x"], pw["w_x"], pw["g_d"], pw["g_b"], pw["g_c"], pw["w_dt"], pw["b_dt"],
+                                     B=d["B"], C=d["C"], delta_low=d_low, skip_delta=True)
 
-            def scan():
-                jscan.prefill(d["x"], d["delta"], d["A"], d["B"], d["C"], y=y, h_final=h)
+                def scan():
+                    jscan.prefill_fused(d["x"], d_low, pw["w_dt"], pw["b_dt"], d["A"], d["B"], d["C"], y=y, h_final=h)
+            else:
+                def produce():
+                    jscan.ssm_inputs(d["x"], pw["w_x"], pw["g_d"], pw["g_b"], pw["g_c"], pw["w_dt"], pw["b_dt"],
+                                     delta=d["delta"], B=d["B"], C=d["C"], delta_low=d_low)
+
+                def scan():
+                    jscan.prefill(d["x"], d["delta"], d["A"], d["B"], d["C"], y=y, h_final=h)
 
             def one_step():
                 produce()
                 scan()
-            launches = 3
+            launches = 2 if args.fused else 3
         elif args.chunked:
             ws_bytes = jscan.chunked_workspace_bytes(wl.batch, wl.L, wl.D)
             ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
@@ -269,8 +279,11 @@ def main():
             return a.elapsed_time(b) / n
         p_ms, s_ms = timed(produce, args.steps), timed(scan, args.steps)
         tokens = wl.batch * wl.L
-        flops = 2 * tokens * wl.D * (PRODUCER_RANK + 2 * wl.N) + 2 * tokens * PRODUCER_RANK * wl.D
-        hbm = tokens * wl.D * 2 * 2 + tokens * (PRODUCER_RANK + 2 * wl.N) * 2 * 2
+        flops = 2 * tokens * wl.D * (PRODUCER_RANK + 2 * wl.N)
+        hbm = tokens * wl.D * 2 + tokens * (PRODUCER_RANK + 2 * wl.N) * 2
+        if not args.fused:   # the delta projection runs in the producer, not inside the scan
+            flops += 2 * tokens * PRODUCER_RANK * wl.D
+            hbm += tokens * wl.D * 2 + tokens * (PRODUCER_RANK + 2 * wl.N) * 2
         producer_info = {"ms": round(p_ms, 4), "scan_ms": round(s_ms, 4), "rank": PRODUCER_RANK,
                          "mfma_TFLOPs": round(flops / (p_ms * 1e-3) / 1e12, 1), "mfma_peak_TFLOPs": BF16_MFMA_PEAK_TFLOPS,
                          "mfma_frac": round(flops / (p_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
@@ -310,7 +323,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "L": wl.L, "D": wl.D, "N": wl.N,
                    "layers": wl.layers, "io_dtype": wl.dtype, "state_dtype": "f32",
-                   "path": "producer+scan" if args.producer else ("time-parallel" if args.chunked else "sequential")},
+                   "path": ("producer+fused-scan" if args.fused else "producer+scan") if args.producer
+                   else ("time-parallel" if args.chunked else "sequential")},
         "hbm_GBps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": alg_bytes,

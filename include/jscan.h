@@ -162,12 +162,33 @@ int64_t jscan_prefill_chunked_workspace(int64_t batch, int64_t L, int64_t D, int
  *   delta      [M][D]      out, bf16;   B, C [M][N] out, bf16
  * R must be 64, 128 or 256; N = 16; D a multiple of 128; eps in [0, 1].  dtype must be
  * JSCAN_BF16 (JSCAN_ERR_DTYPE otherwise).  Outputs must not overlap inputs or each other.
- * Two kernels are launched on `stream`, in order.
+ * Two kernels are launched on `stream`, in order.  With delta == NULL only the first
+ * product runs (delta_low, B and C; w_dt and b_dt may then be NULL): the input of
+ * jscan_prefill_fused, which computes delta itself.
  */
 jscan_status jscan_ssm_inputs(const void *x, const void *w_x, const float *g_delta, const float *g_B,
                               const float *g_C, const void *w_dt, const float *b_dt, void *delta_low,
                               void *delta, void *B, void *C, int64_t M, int64_t D, int64_t R,
                               int64_t N, float eps, jscan_dtype dtype, void *stream);
+
+/*
+ * Prefill with the second product of jscan_ssm_inputs folded into the scan's load path: delta
+ * is never stored.  The kernel computes, tile by tile, delta = softplus(W_dt delta_low + b_dt)
+ * with the same matrix-core sequence, bias add, softplus and bf16 rounding as
+ * jscan_ssm_inputs, so y and h_final are bit-identical to jscan_ssm_inputs followed by
+ * jscan_prefill_resume (jscan_prefill when h0 is NULL).
+ *   x          [batch][L][D] bf16      delta_low [batch][L][R] bf16 (from jscan_ssm_inputs)
+ *   w_dt       [D][R] bf16             b_dt [D] fp32
+ *   A, B, C, h0 (may be NULL), y, h_final as for jscan_prefill_resume
+ * Limits: bf16 only, R = 256, D a multiple of 32 and batch * D <= 65536 (the long-sequence
+ * shapes of the row-mapped prefill); other shapes return JSCAN_ERR_SHAPE and are served by
+ * jscan_ssm_inputs then jscan_prefill.
+ */
+jscan_status jscan_prefill_fused(const void *x, const void *delta_low, const void *w_dt,
+                                 const float *b_dt, const float *A, const void *B, const void *C,
+                                 const float *h0, void *y, float *h_final, int64_t batch,
+                                 int64_t L, int64_t D, int64_t N, int64_t R, jscan_dtype dtype,
+                                 void *stream);
 
 /*
  * Decode step: advance the state by one token, in place, and write that token's output.
@@ -192,7 +213,7 @@ const char *jscan_status_string(jscan_status s);
 int jscan_last_hip_error(void);
 
 /* Library ABI version: 100 * major + minor (101 adds the time-parallel prefill, 102 the
- * producer side). */
+ * producer side, 103 the fused prefill). */
 int jscan_version(void);
 
 #ifdef __cplusplus

@@ -9,6 +9,7 @@ There is no CPU fallback: without the built library every call raises.
     y_t = step(h, x_t, delta_t, A, B_t, C_t)               # one decode token, h in place
     y, h_final = prefill_chunked(x, delta, A, B, C)        # time-parallel, for few channels
     delta, B, C, d_low = ssm_inputs(x, w_x, g_d, g_B, g_C, w_dt, b_dt)   # producer side (MFMA)
+    y, h_final = prefill_fused(x, d_low, w_dt, b_dt, A, B, C)             # delta computed in the scan
 """
 from ._binding import (  # noqa: F401
     D_STATE,
@@ -18,6 +19,7 @@ from ._binding import (  # noqa: F401
     library_path,
     prefill,
     prefill_chunked,
+    prefill_fused,
     ssm_inputs,
     step,
     step_raw,

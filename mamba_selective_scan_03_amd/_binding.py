@@ -47,6 +47,8 @@ def library():
     lib.jscan_ssm_inputs.argtypes = [vp, vp, fp, fp, fp, vp, fp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, i32,
                                      vp]
     lib.jscan_ssm_inputs.restype = i32
+    lib.jscan_prefill_fused.argtypes = [vp, vp, vp, fp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, i64, i32, vp]
+    lib.jscan_prefill_fused.restype = i32
     lib.jscan_prefill_chunked_workspace.restype = i64
     for f in (lib.jscan_prefill, lib.jscan_prefill_resume, lib.jscan_step, lib.jscan_prefill_chunked):
         f.restype = i32
@@ -148,11 +150,13 @@ def prefill_chunked(x, delta, A, B, C, h0=None, y=None, h_final=None, chunk=0, w
     return y, h_final
 
 
-def ssm_inputs(x, w_x, g_delta, g_B, g_C, w_dt, b_dt, eps=1e-6, delta=None, B=None, C=None, delta_low=None):
+def ssm_inputs(x, w_x, g_delta, g_B, g_C, w_dt, b_dt, eps=1e-6, delta=None, B=None, C=None, delta_low=None,
+               skip_delta=False):
     """Producer side (``jscan_ssm_inputs``): delta, B and C of the scan computed from x.
     x ``[..., D]`` bf16; w_x ``[R + 32, D]`` bf16; gains fp32 ``[R]``, ``[16]``, ``[16]``;
     w_dt ``[D, R]`` bf16; b_dt ``[D]`` fp32.  Returns ``(delta [..., D], B [..., 16], C [..., 16],
-    delta_low [..., R])``, all bf16, with x's leading shape."""
+    delta_low [..., R])``, all bf16, with x's leading shape.  ``skip_delta`` runs only the first
+    product (delta is then None): the input of :func:`prefill_fused`."""
     _require(x.is_cuda and x.dtype == torch.bfloat16 and x.is_contiguous(), "x must be a contiguous bf16 CUDA tensor")
     D = x.shape[-1]
     lead = tuple(x.shape[:-1])
@@ -165,7 +169,10 @@ def ssm_inputs(x, w_x, g_delta, g_B, g_C, w_dt, b_dt, eps=1e-6, delta=None, B=No
         _require(tuple(t.shape) == shape, f"{name} must have shape {shape}, got {tuple(t.shape)}")
         _require(t.dtype == dt and t.is_contiguous() and t.device == x.device, f"{name} must be contiguous {dt} on x's device")
     dev = x.device
-    delta = torch.empty(lead + (D,), dtype=torch.bfloat16, device=dev) if delta is None else delta
+    if skip_delta:
+        delta = None
+    elif delta is None:
+        delta = torch.empty(lead + (D,), dtype=torch.bfloat16, device=dev)
     B = torch.empty(lead + (D_STATE,), dtype=torch.bfloat16, device=dev) if B is None else B
     C = torch.empty(lead + (D_STATE,), dtype=torch.bfloat16, device=dev) if C is None else C
     delta_low = torch.empty(lead + (R,), dtype=torch.bfloat16, device=dev) if delta_low is None else delta_low
@@ -176,6 +183,33 @@ def ssm_inputs(x, w_x, g_delta, g_B, g_C, w_dt, b_dt, eps=1e-6, delta=None, B=No
                                   JSCAN_BF16, _stream(dev))
     _check(st)
     return delta, B, C, delta_low
+
+
+def prefill_fused(x, delta_low, w_dt, b_dt, A, B, C, h0=None, y=None, h_final=None):
+    """Prefill with delta computed inside the scan from delta_low (``jscan_prefill_fused``):
+    bit-identical to ``ssm_inputs`` then ``prefill``.  bf16, rank 256, long-sequence shapes."""
+    _require(x.is_cuda and x.dtype == torch.bfloat16 and x.dim() == 3 and x.is_contiguous(),
+             "x must be a contiguous bf16 [batch, L, D] CUDA tensor")
+    batch, L, D = x.shape
+    R = delta_low.shape[-1]
+    for name, t, shape, dt in (("delta_low", delta_low, (batch, L, R), torch.bfloat16),
+                               ("w_dt", w_dt, (D, R), torch.bfloat16), ("b_dt", b_dt, (D,), torch.float32),
+                               ("A", A, (D, D_STATE), torch.float32), ("B", B, (batch, L, D_STATE), torch.bfloat16),
+                               ("C", C, (batch, L, D_STATE), torch.bfloat16)):
+        _require(tuple(t.shape) == shape, f"{name} must have shape {shape}, got {tuple(t.shape)}")
+        _require(t.dtype == dt and t.is_contiguous() and t.device == x.device, f"{name} must be contiguous {dt}")
+    if h0 is not None:
+        _require(tuple(h0.shape) == (batch, D, D_STATE) and h0.dtype == torch.float32 and h0.is_contiguous(),
+                 "h0 must be a contiguous fp32 [batch, D, 16] tensor")
+    y = torch.empty_like(x) if y is None else y
+    h_final = torch.empty((batch, D, D_STATE), dtype=torch.float32, device=x.device) if h_final is None else h_final
+    lib = library()
+    with torch.cuda.device(x.device):
+        st = lib.jscan_prefill_fused(_ptr(x), _ptr(delta_low), _ptr(w_dt), _ptr(b_dt), _ptr(A), _ptr(B), _ptr(C),
+                                     _ptr(h0), _ptr(y), _ptr(h_final), batch, L, D, D_STATE, R, JSCAN_BF16,
+                                     _stream(x.device))
+    _check(st)
+    return y, h_final
 
 
 def step_raw(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, dtype):

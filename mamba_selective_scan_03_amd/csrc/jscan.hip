@@ -203,6 +203,7 @@ void launch_ssm_inputs(const uint16_t *x, const uint16_t *w_x, const float *g_d,
     const int64_t row_tiles = (M + jscan::proj::kRowsX - 1) / jscan::proj::kRowsX;
     hipLaunchKernelGGL((jscan::xproj_kernel<R / 16>), dim3((unsigned)row_tiles), dim3(256), 0, stream, x, w_x, g_d,
                        g_b, g_c, d_low, B, C, M, D, eps);
+    if (!delta) return;   // x projection only: delta is computed inside jscan_prefill_fused
     // one work-group per CU (the LDS tiles allow one): 256 groups of (channel slice, token tiles)
     const int ch_tiles = D / jscan::proj::kTileDt;
     const int64_t tok_tiles = (M + jscan::proj::kTileDt - 1) / jscan::proj::kTileDt;
@@ -325,11 +326,14 @@ jscan_status jscan_ssm_inputs(const void *x, const void *w_x, const float *g_del
     const int64_t tok_tiles = (M + jscan::proj::kTileDt - 1) / jscan::proj::kTileDt;
     if (tok_tiles * (D / jscan::proj::kTileDt) > kMaxBlocks) return JSCAN_ERR_SHAPE;
     if (M == 0) return JSCAN_OK;
-    const void *arrays[] = {x, w_x, g_delta, g_B, g_C, w_dt, b_dt, delta_low, delta, B, C};
+    // delta == NULL: the x projection alone (w_dt and b_dt are then not used and may be NULL)
+    const void *arrays[] = {x, w_x, g_delta, g_B, g_C, delta_low, B, C};
     for (const void *p : arrays)
         if (!p) return JSCAN_ERR_NULL;
-    for (const void *p : arrays)
-        if (!aligned16(p)) return JSCAN_ERR_ALIGN;
+    if (delta && (!w_dt || !b_dt)) return JSCAN_ERR_NULL;
+    const void *maybe[] = {x, w_x, g_delta, g_B, g_C, delta_low, B, C, delta, w_dt, b_dt};
+    for (const void *p : maybe)
+        if (p && !aligned16(p)) return JSCAN_ERR_ALIGN;
     const Span outs[] = {span(delta_low, M * R * 2), span(delta, M * D * 2), span(B, M * N * 2), span(C, M * N * 2)};
     const Span ins[] = {span(x, M * D * 2),     span(w_x, (R + 2 * N) * D * 2), span(g_delta, R * 4),
                         span(g_B, N * 4),       span(g_C, N * 4),               span(w_dt, D * R * 2),
@@ -350,6 +354,41 @@ jscan_status jscan_ssm_inputs(const void *x, const void *w_x, const float *g_del
     return launch_status();
 }
 
+jscan_status jscan_prefill_fused(const void *x, const void *delta_low, const void *w_dt, const float *b_dt,
+                                 const float *A, const void *B, const void *C, const float *h0, void *y,
+                                 float *h_final, int64_t batch, int64_t L, int64_t D, int64_t N, int64_t R,
+                                 jscan_dtype dtype, void *stream) {
+    if (dtype != JSCAN_F32 && dtype != JSCAN_BF16) return JSCAN_ERR_DTYPE;
+    if (dtype != JSCAN_BF16) return JSCAN_ERR_DTYPE;
+    bool empty = false;
+    // the usual prefill checks, with x standing in for delta (same shape)
+    jscan_status st = check_prefill(x, x, A, B, C, h0, false, y, h_final, batch, L, D, N, dtype, &empty);
+    if (st != JSCAN_OK) return st;
+    if (R != jscan::fused::kRank) return JSCAN_ERR_SHAPE;
+    if (empty) return JSCAN_OK;
+    if (!jscan::rows_kernel_applies(batch, D)) return JSCAN_ERR_SHAPE;
+    if (!w_dt || !b_dt || (L > 0 && !delta_low)) return JSCAN_ERR_NULL;
+    const void *more[] = {delta_low, w_dt, b_dt};
+    for (const void *p : more)
+        if (p && !aligned16(p)) return JSCAN_ERR_ALIGN;
+    const int64_t seq = batch * L * D * 2, state = batch * D * N * 4;
+    const Span outs[] = {span(y, L > 0 ? seq : 0), span(h_final, state)};
+    const Span ins[] = {span(delta_low, batch * L * R * 2), span(w_dt, D * R * 2), span(b_dt, D * 4)};
+    for (const Span &o : outs)
+        for (const Span &i : ins)
+            if (overlaps(o, i)) return JSCAN_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (L == 0) return launch_prefill<jscan::BF16>(x, x, A, B, C, h0, y, h_final, batch, L, D, s);
+    using U = uint16_t;
+    const jscan::Segments sg{L, L, 1, 0};
+    const jscan::DeltaProj dp{static_cast<const U *>(delta_low), static_cast<const U *>(w_dt), b_dt};
+    jscan::launch_prefill_rows<jscan::BF16, false, true>(static_cast<const U *>(x), nullptr, A,
+                                                         static_cast<const U *>(B), static_cast<const U *>(C), h0,
+                                                         static_cast<U *>(y), h_final, nullptr, sg, batch, (int)D, s,
+                                                         dp);
+    return launch_status();
+}
+
 const char *jscan_status_string(jscan_status s) {
     switch (s) {
     case JSCAN_OK: return "ok";
@@ -366,6 +405,6 @@ const char *jscan_status_string(jscan_status s) {
 
 int jscan_last_hip_error(void) { return g_last_hip_error; }
 
-int jscan_version(void) { return 102; }
+int jscan_version(void) { return 103; }
 
 }  // extern "C"

@@ -30,6 +30,7 @@
 // leave every state bit-identical (decay 2^0 = 1, input term -0) and their y is not stored.
 #pragma once
 
+#include "project_kernels.h"
 #include "scan_update.h"
 
 namespace jscan {
@@ -129,7 +130,7 @@ __device__ __forceinline__ float reduce_rows4(float p0, float p1, float p2, floa
 // the full HBM latency.  Whole tiles take 32-bit lane offsets from a tile base; the last,
 // partial tile re-reads token L-1 for tokens past the end, which staging then replaces by
 // identity tokens.
-template <typename E>
+template <typename E, bool kLoadDelta = true>
 __device__ __forceinline__ void load_tile(TileRegs<E> &R, const typename E::store_t *xb,
                                           const typename E::store_t *db, const typename E::store_t *bcb,
                                           int64_t t0, int64_t L, int D, int tid) {
@@ -141,7 +142,7 @@ __device__ __forceinline__ void load_tile(TileRegs<E> &R, const typename E::stor
         for (int j = 0; j < 2; ++j) {
             const int off = (2 * p + j) * D + 4 * q;
             R.x[j] = Vec4<E>::load(xt + off);
-            R.dl[j] = Vec4<E>::load(dt + off);
+            if constexpr (kLoadDelta) R.dl[j] = Vec4<E>::load(dt + off);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) R.bc[j] = Vec4<E>::load(bt + tb * kDState + nb + 4 * j);
@@ -150,12 +151,64 @@ __device__ __forceinline__ void load_tile(TileRegs<E> &R, const typename E::stor
         for (int j = 0; j < 2; ++j) {
             const int64_t t = min(t0 + 2 * p + j, L - 1);
             R.x[j] = Vec4<E>::load(xb + t * D + 4 * q);
-            R.dl[j] = Vec4<E>::load(db + t * D + 4 * q);
+            if constexpr (kLoadDelta) R.dl[j] = Vec4<E>::load(db + t * D + 4 * q);
         }
         const int64_t t = min(t0 + tb, L - 1);
 #pragma unroll
         for (int j = 0; j < 2; ++j) R.bc[j] = Vec4<E>::load(bcb + t * kDState + nb + 4 * j);
     }
+}
+
+// ---- delta computed on the load path ---------------------------------------------------
+// With the producer's second projection folded in, the helper waves compute each tile's delta
+// themselves: delta = softplus(W_dt d_low + b_dt) for the tile's 64 tokens and the work-group's
+// 32 channels, on the matrix cores, with the same MFMA sequence, bias add, softplus and bf16
+// rounding as the separate delta projection (project_kernels.h), so the scan sees bit-identical
+// delta values.  Helper wave hw computes the 16 tokens 16 hw .. 16 hw + 15 that its own lanes
+// stage, so the result only has to move between lanes of one wave (through a small per-wave
+// LDS area, which needs no barrier).
+struct DeltaProj {
+    const uint16_t *d_low;   // [tokens][kRank] bf16, tokens in the order of x's rows
+    const uint16_t *w_dt;    // [D][kRank] bf16
+    const float *b_dt;       // [D] fp32
+};
+namespace fused {
+constexpr int kRank = 256;               // rank of the low-rank delta input
+constexpr int kKS = kRank / 32;          // MFMA k steps
+constexpr int kXchRow = 36;              // bf16 per row of the per-wave exchange (32 + 4)
+constexpr int kXchWave = 16 * kXchRow;   // one wave's exchange area: 16 tokens
+}
+
+// This lane's MFMA B operands (its token's d_low row, all k) for the tile starting at t0.
+__device__ __forceinline__ void load_dlow(u32x4_t (&f)[fused::kKS], const uint16_t *d_low, int64_t row, int64_t t0,
+                                          int64_t L, int hw, int l) {
+    const int64_t t = row + min(t0 + 16 * hw + (l & 15), L - 1);
+#pragma unroll
+    for (int ks = 0; ks < fused::kKS; ++ks)
+        f[ks] = *reinterpret_cast<const u32x4_t *>(d_low + t * fused::kRank + 32 * ks + 8 * (l >> 4));
+}
+
+// delta for this wave's 16 tokens x 32 channels, rounded to bf16, into the staging registers
+// R.dl of the lanes that stage those tokens.
+__device__ __forceinline__ void fused_delta(const u32x4_t (&f)[fused::kKS], const bf16x8_t (&wf)[2][fused::kKS],
+                                            const float4 (&bias)[2], uint16_t *xch, TileRegs<BF16> &R, int l) {
+    f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < fused::kKS; ++ks)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) acc[u] = mfma16(wf[u][ks], __builtin_bit_cast(bf16x8_t, f[ks]), acc[u]);
+    // lane l holds channels 16u + 4 (l / 16) + i of token l % 16
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        uint2 pk;
+        pk.x = pack_bf16x2(softplus_f32(acc[u][0] + bias[u].x), softplus_f32(acc[u][1] + bias[u].y));
+        pk.y = pack_bf16x2(softplus_f32(acc[u][2] + bias[u].z), softplus_f32(acc[u][3] + bias[u].w));
+        *reinterpret_cast<uint2 *>(xch + (l & 15) * fused::kXchRow + 16 * u + 4 * (l >> 4)) = pk;
+    }
+    // the staging lane (token pair l / 8, channel quad l % 8) reads its two tokens' 4 channels
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        R.dl[j] = *reinterpret_cast<const uint2 *>(xch + (2 * (l >> 3) + j) * fused::kXchRow + 4 * (l & 7));
 }
 
 // Converts one quarter of a tile from registers into LDS: channel 4q + part of this thread's
@@ -307,16 +360,19 @@ __device__ __forceinline__ void write_final(const FinalRegs &F, typename E::stor
 // One work-group scans 32 channels of one row (see Segments) from the row's initial state
 // (zero when h0 is null).  A segment-summary launch (kSummary) writes no y; it writes the
 // row's final state and, per channel, the sum of the row's delta values to dsum[row][D].
-template <typename E, bool kSummary>
+// With kFused, delta is not read: the helper waves compute it from dp (bf16 only).
+template <typename E, bool kSummary, bool kFused = false>
 __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_rows_kernel(
     const typename E::store_t *__restrict__ x, const typename E::store_t *__restrict__ dl,
     const float *__restrict__ A, const typename E::store_t *__restrict__ B,
     const typename E::store_t *__restrict__ C, const float *__restrict__ h0,
     typename E::store_t *__restrict__ y, float *__restrict__ h_final, float *__restrict__ dsum, Segments sg, int D,
-    int blocks_per_row, int xcd_stride) {
+    int blocks_per_row, int xcd_stride, DeltaProj dp) {
+    static_assert(!kFused || (sizeof(typename E::store_t) == 2 && !kSummary), "the fused delta path is bf16 only");
     __shared__ __attribute__((aligned(16))) float dx_s[2][rows::kDxSize];
     __shared__ __attribute__((aligned(16))) float bc_s[2][2 * rows::kBcSize];
     __shared__ __attribute__((aligned(16))) float y_s[2][rows::kYSize];
+    __shared__ __attribute__((aligned(16))) uint16_t xch_s[kFused ? 4 * fused::kXchWave : 8];
 
     // Consecutive channel blocks go to the same XCD (work-groups are dealt round-robin over
     // the 8 XCDs), so the two blocks sharing a 128-byte row segment share one L2.
@@ -340,17 +396,45 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
         const typename E::store_t *bcb = (tid < 128 ? B : C) + row * kDState;
         typename E::store_t *yb = y + row * D + d0;
         TileRegs<E> R[2];
-        load_tile<E>(R[0], xb, db, bcb, 0, L, D, tid);
+        // fused delta: W_dt operands and biases of this wave's 32 channels, d_low operand ring
+        const int hw = tid >> 6, l = tid & 63;
+        bf16x8_t wf[2][fused::kKS];
+        float4 bias[2];
+        u32x4_t dfr[2][fused::kKS];
+        uint16_t *xch = xch_s + (kFused ? hw * fused::kXchWave : 0);
+        if constexpr (kFused) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                for (int ks = 0; ks < fused::kKS; ++ks)
+                    wf[u][ks] = load_frag(dp.w_dt + (int64_t)(d0 + 16 * u + (l & 15)) * fused::kRank + 32 * ks +
+                                          8 * (l >> 4));
+                bias[u] = *reinterpret_cast<const float4 *>(dp.b_dt + d0 + 16 * u + 4 * (l >> 4));
+            }
+        }
+        load_tile<E, !kFused>(R[0], xb, db, bcb, 0, L, D, tid);
+        if constexpr (kFused) {
+            load_dlow(dfr[0], dp.d_low, row, 0, L, hw, l);
+            fused_delta(dfr[0], wf, bias, xch, R[0], l);
+        }
         stage_tile<E>(R[0], dx_s[0], bc_s[0], 0, L, tid);
-        load_tile<E>(R[1], xb, db, bcb, rows::kT, L, D, tid);
-        load_tile<E>(R[0], xb, db, bcb, 2 * rows::kT, L, D, tid);
+        load_tile<E, !kFused>(R[1], xb, db, bcb, rows::kT, L, D, tid);
+        load_tile<E, !kFused>(R[0], xb, db, bcb, 2 * rows::kT, L, D, tid);
+        if constexpr (kFused) {
+            load_dlow(dfr[1], dp.d_low, row, rows::kT, L, hw, l);
+            load_dlow(dfr[0], dp.d_low, row, 2 * rows::kT, L, hw, l);
+        }
         __syncthreads();
         FinalRegs F;
         auto tile = [&](auto cur_c, int k) {
             constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
             if (k + 1 < ntiles) {
+                if constexpr (kFused) fused_delta(dfr[nxt], wf, bias, xch, R[nxt], l);
                 stage_tile<E>(R[nxt], dx_s[nxt], bc_s[nxt], (int64_t)(k + 1) * rows::kT, L, tid);
-                if (k + 3 < ntiles) load_tile<E>(R[nxt], xb, db, bcb, (int64_t)(k + 3) * rows::kT, L, D, tid);
+                if (k + 3 < ntiles) {
+                    load_tile<E, !kFused>(R[nxt], xb, db, bcb, (int64_t)(k + 3) * rows::kT, L, D, tid);
+                    if constexpr (kFused) load_dlow(dfr[nxt], dp.d_low, row, (int64_t)(k + 3) * rows::kT, L, hw, l);
+                }
             }
             if (!kSummary && k > 0) {
                 read_final(F, y_s[nxt], tid);
@@ -455,16 +539,16 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
 inline bool rows_kernel_applies(int64_t batch, int64_t D) { return D % rows::kCh == 0 && batch * D <= 65536; }
 
 // Launches one work-group per 32 channels of each of the `nrows` rows described by sg.
-template <typename E, bool kSummary>
+template <typename E, bool kSummary, bool kFused = false>
 void launch_prefill_rows(const typename E::store_t *x, const typename E::store_t *dl, const float *A,
                          const typename E::store_t *B, const typename E::store_t *C, const float *h0,
                          typename E::store_t *y, float *h_final, float *dsum, const Segments &sg, int64_t nrows,
-                         int D, hipStream_t stream) {
+                         int D, hipStream_t stream, DeltaProj dp = DeltaProj{nullptr, nullptr, nullptr}) {
     const int blocks_per_row = D / rows::kCh;
     const int64_t blocks = nrows * blocks_per_row;
     const int xcd_stride = (blocks % 8 == 0) ? (int)(blocks / 8) : 0;
-    hipLaunchKernelGGL((prefill_rows_kernel<E, kSummary>), dim3((unsigned)blocks), dim3(rows::kThreads), 0, stream, x,
-                       dl, A, B, C, h0, y, h_final, dsum, sg, D, blocks_per_row, xcd_stride);
+    hipLaunchKernelGGL((prefill_rows_kernel<E, kSummary, kFused>), dim3((unsigned)blocks), dim3(rows::kThreads), 0,
+                       stream, x, dl, A, B, C, h0, y, h_final, dsum, sg, D, blocks_per_row, xcd_stride, dp);
 }
 
 }  // namespace jscan

@@ -27,7 +27,7 @@ def test_header_symbols_are_exported():
     names = header_symbols()
     assert {"jscan_prefill", "jscan_prefill_resume", "jscan_step", "jscan_status_string",
             "jscan_last_hip_error", "jscan_version", "jscan_prefill_chunked",
-            "jscan_prefill_chunked_workspace", "jscan_ssm_inputs"} <= set(names)
+            "jscan_prefill_chunked_workspace", "jscan_ssm_inputs", "jscan_prefill_fused"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -37,7 +37,7 @@ def test_status_strings_and_version():
     for s in range(8):
         assert lib.jscan_status_string(s) and lib.jscan_status_string(s) != b"unknown status"
     assert lib.jscan_status_string(99) == b"unknown status"
-    assert lib.jscan_version() == 102
+    assert lib.jscan_version() == 103
     assert lib.jscan_last_hip_error() == 0
 
 
@@ -143,6 +143,26 @@ def ssm_inputs(x=P, wx=P + 0x100000, gd=P + 0x200000, gb=P + 0x210000, gc=P + 0x
 ])
 def test_ssm_inputs_validation(kw, code):
     assert ssm_inputs(**kw) == code
+
+
+def fused(x=P, dlow=P + 0x100000, wdt=P + 0x200000, bdt=P + 0x300000, A=P + 0x310000, B=P + 0x320000,
+          C=P + 0x330000, h0=None, y=P + 0x400000, h=P + 0x500000, batch=1, L=64, D=64, N=16, R=256, dtype=BF16):
+    return jscan.library().jscan_prefill_fused(x, dlow, wdt, bdt, A, B, C, h0, y, h, batch, L, D, N, R, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=F32), EDTYPE), (dict(R=128), ESHAPE), (dict(D=72), ESHAPE), (dict(batch=3, L=1, D=32768, h=P + 0x10000000, A=P + 0x20000000), ESHAPE),
+    (dict(dlow=None), ENULL), (dict(wdt=None), ENULL), (dict(bdt=P + 0x300004), EALIGN),
+    (dict(y=P + 0x100000), EALIAS), (dict(h=P + 0x200000 + 64), EALIAS), (dict(x=None), ENULL),
+])
+def test_prefill_fused_validation(kw, code):
+    assert fused(**kw) == code
+
+
+def test_ssm_inputs_without_delta_needs_no_second_weights():
+    # delta == NULL: w_dt and b_dt may be NULL; a misaligned gain is still reported first
+    assert ssm_inputs(delta=None, wdt=None, bdt=None, gb=P + 0x210004) == EALIGN
+    assert ssm_inputs(wdt=None) == ENULL
 
 
 def test_ssm_inputs_zero_tokens_is_a_no_op():

@@ -124,3 +124,26 @@ def test_ssm_inputs_full_size_sampled_rows():
     one_step_close(f64(delta.cpu()[idx]), P.delta_from_low(dl, wts["w_dt"].double().numpy(), wts["b_dt"].numpy()),
                    "64K delta (sampled rows)")
     assert torch.isfinite(delta.float()).all() and float(delta.float().min()) > 0
+
+
+@pytest.mark.parametrize("batch,L,D,with_h0", [(1, 1000, 512, False), (2, 300, 1024, True), (1, 4096, 8192, False),
+                                                (1, 63, 128, True), (1, 1, 128, False)])
+def test_fused_prefill_is_bit_identical_to_producer_then_scan(batch, L, D, with_h0):
+    """Delta computed inside the scan (jscan_prefill_fused) equals the producer's delta bit for
+    bit, so y and h_final match jscan_ssm_inputs followed by jscan_prefill(_resume) exactly."""
+    inp = workloads.small_prefill(batch, L, D, "bf16", seed=L + D)
+    wts = workloads.producer_weights(D, 256, seed=D)
+    dev = {k: v.cuda() for k, v in wts.items()}
+    x = inp["x"].cuda()
+    A = inp["A"].cuda()
+    h0 = (torch.randn(batch, D, 16, generator=torch.Generator().manual_seed(1)) * 0.1).cuda() if with_h0 else None
+    delta, B, C, d_low = jscan.ssm_inputs(x, dev["w_x"], dev["g_d"], dev["g_b"], dev["g_c"], dev["w_dt"], dev["b_dt"])
+    y1, h1 = jscan.prefill(x, delta, A, B, C, h0=h0)
+    _, B2, C2, d_low2 = jscan.ssm_inputs(x, dev["w_x"], dev["g_d"], dev["g_b"], dev["g_c"], dev["w_dt"], dev["b_dt"],
+                                         skip_delta=True)
+    y2, h2 = jscan.prefill_fused(x, d_low2, dev["w_dt"], dev["b_dt"], A, B2, C2, h0=h0)
+    torch.cuda.synchronize()
+    say(f"fused {batch}x{L}x{D} h0={with_h0}")
+    assert torch.equal(bits(d_low), bits(d_low2)) and torch.equal(bits(B), bits(B2))
+    assert torch.equal(bits(y1), bits(y2)), "fused y differs"
+    assert torch.equal(bits(h1), bits(h2)), "fused h_final differs"
