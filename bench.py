@@ -129,8 +129,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only; the scan's multi-GPU sharding is a design note, "
-              "not an implemented path. Run with --gpus 1.", file=sys.stderr)
+        print("bench.py: the benchmark runs on one GPU; sharding the scan over several GPUs is described in the "
+              "design notes, not implemented. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

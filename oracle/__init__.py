@@ -1,7 +1,7 @@
 """fp64 CPU oracle for the Mamba-1 (S6) selective scan -- test infrastructure only.
 
-Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
-``bench.py`` may import this package.  The GPU library never links, loads or calls it,
+Only the test suite, the smoke check of the repository's entry module and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The GPU library never links, loads or calls it,
 and it imports nothing from the GPU library.
 
 The arithmetic lives in ``jscan_oracle.c`` (plain C, fp64, compiled with
