@@ -64,3 +64,59 @@ def test_prefill_in_a_graph_matches_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(bits(y_g), bits(y_e)) and torch.equal(bits(h_g), bits(h_e)), f"replay {replay}"
+
+
+def _capture(fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def test_time_parallel_prefill_in_a_graph_matches_eager():
+    """Three launches (segment summaries, carry, rescan) sharing a workspace, replayed."""
+    d = to_dev(workloads.small_prefill(1, 2000, 256, "bf16", seed=4))
+    h0 = torch.randn(1, 256, 16, generator=torch.Generator().manual_seed(2)).cuda() * 0.1
+    ws = torch.empty(jscan.chunked_workspace_bytes(1, 2000, 256, 256), dtype=torch.uint8, device="cuda")
+    y_e, h_e = jscan.prefill_chunked(d["x"], d["delta"], d["A"], d["B"], d["C"], h0=h0, chunk=256, workspace=ws)
+    y_g, h_g = torch.empty_like(y_e), torch.empty_like(h_e)
+    g = _capture(lambda: jscan.prefill_chunked(d["x"], d["delta"], d["A"], d["B"], d["C"], h0=h0, y=y_g,
+                                               h_final=h_g, chunk=256, workspace=ws))
+    for replay in range(3):
+        y_g.fill_(float("nan"))
+        h_g.fill_(float("nan"))
+        ws.fill_(0xAB)                    # the workspace's contents on entry do not matter
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bits(y_g), bits(y_e)) and torch.equal(bits(h_g), bits(h_e)), f"replay {replay}"
+
+
+def test_producer_and_fused_prefill_in_a_graph_match_eager():
+    x = workloads.small_prefill(1, 512, 256, "bf16", seed=6)
+    d = to_dev(x)
+    w = {k: v.cuda() for k, v in workloads.producer_weights(256, 256, seed=6).items()}
+    _, B_e, C_e, dl_e = jscan.ssm_inputs(d["x"], w["w_x"], w["g_d"], w["g_b"], w["g_c"], w["w_dt"], w["b_dt"],
+                                         skip_delta=True)
+    y_e, h_e = jscan.prefill_fused(d["x"], dl_e, w["w_dt"], w["b_dt"], d["A"], B_e, C_e)
+    B_g, C_g, dl_g = torch.empty_like(B_e), torch.empty_like(C_e), torch.empty_like(dl_e)
+    y_g, h_g = torch.empty_like(y_e), torch.empty_like(h_e)
+
+    def layer():
+        jscan.ssm_inputs(d["x"], w["w_x"], w["g_d"], w["g_b"], w["g_c"], w["w_dt"], w["b_dt"], B=B_g, C=C_g,
+                         delta_low=dl_g, skip_delta=True)
+        jscan.prefill_fused(d["x"], dl_g, w["w_dt"], w["b_dt"], d["A"], B_g, C_g, y=y_g, h_final=h_g)
+    g = _capture(layer)
+    for replay in range(3):
+        for t in (B_g, C_g, dl_g, y_g):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in ((B_g, B_e), (dl_g, dl_e), (y_g, y_e), (h_g, h_e)):
+            assert torch.equal(bits(got), bits(want)), f"replay {replay}"
