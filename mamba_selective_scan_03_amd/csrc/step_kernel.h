@@ -7,7 +7,7 @@
 // row with 16-byte accesses.  A lane loads its A quad once for all its rows and has all its
 // rows' state in flight at once.  The state is read and written exactly once (in place), which
 // makes the kernel HBM-bound: 128 of the ~134 bytes moved per (b, d) are state.  On MI355X it
-// runs at the speed of a device-to-device copy of the state.
+// moves the state faster than the runtime's device-to-device copy does.
 // y_t[d] is the sum over the quad: each lane adds its four C*h terms in increasing n, then
 // two DPP quad exchanges add (q0+q1)+(q2+q3); every lane of the quad ends with the same sum.
 #pragma once
@@ -18,6 +18,18 @@ namespace jscan {
 
 namespace step {
 constexpr int kRows = 2;   // batch rows per lane
+}
+
+// The state is streamed: every element is read once and written once per token, and a
+// 28-layer token step moves 7 GiB, far beyond the caches.  Non-temporal accesses keep it from
+// evicting anything on its way through (about 9% faster than ordinary accesses here).
+typedef float step_f4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_state(const float *p) {
+    const step_f4 v = __builtin_nontemporal_load(reinterpret_cast<const step_f4 *>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_state(float *p, float4 v) {
+    __builtin_nontemporal_store(step_f4{v.x, v.y, v.z, v.w}, reinterpret_cast<step_f4 *>(p));
 }
 
 // Four consecutive B or C values of one row as fp32.
@@ -55,7 +67,7 @@ __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ h,
     for (int j = 0; j < NR; ++j) {
         // a missing last row re-reads the row before it and stores nothing
         const int b = min(rg * NR + j, batch - 1);
-        hv[j] = *reinterpret_cast<const float4 *>(h + ((int64_t)b * D + d) * kDState + q * 4);
+        hv[j] = load_state(h + ((int64_t)b * D + d) * kDState + q * 4);
         xv[j] = E::load(x + (int64_t)b * ld_xd + d);
         dv[j] = E::load(dl + (int64_t)b * ld_xd + d);
         bv[j] = Quad<E>::load(Bt + (int64_t)b * ld_bc + q * 4);
@@ -78,7 +90,7 @@ __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ h,
         p = p + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, p), 0xB1, 0xF, 0xF, true));
         p = p + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, p), 0x4E, 0xF, 0xF, true));
         if (b < batch) {
-            *reinterpret_cast<float4 *>(h + ((int64_t)b * D + d) * kDState + q * 4) = hn;
+            store_state(h + ((int64_t)b * D + d) * kDState + q * 4, hn);
             if (q == 0) E::store(y + (int64_t)b * ld_xd + d, p);
         }
     }
