@@ -17,6 +17,11 @@ product and two fused multiply-adds), and the exponential issues at half rate, s
 five instructions are 7 operations (each FMA counts 2), so the same bound reads
 45.9 TFLOP/s.  HBM traffic (about 6 bytes per B*L*D element in bf16) is reported beside
 it as GB/s and as a fraction of 8 TB/s.
+
+With --scalar-a (A a scaled identity, one value per channel: the Mamba-2 form) the decay is
+shared by a channel's 16 states, so a state element needs only the input product and two
+fused multiply-adds (3 slots) plus a sixteenth of the decay's product and exponential
+(3/16): 3.1875 slots and 5.125 flops per element, a bound of 63.2 TFLOP/s.
 """
 from __future__ import annotations
 
@@ -39,6 +44,8 @@ VALU_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9      # fp32 lane-instructions per second
 SLOTS_PER_STATE_ELEM = 6                      # mul, exp (2 slots), mul, fma, fma
 FLOPS_PER_STATE_ELEM = 7                      # mul 1 + exp 1 + mul 1 + fma 2 + fma 2
 PEAK_STATE_ELEMS = VALU_SLOTS_PER_S / SLOTS_PER_STATE_ELEM
+SCALAR_A_SLOTS = 3 + 3 / 16                   # mul, fma, fma; decay (mul + exp) once per 16 states
+SCALAR_A_FLOPS = 5 + 2 / 16
 KERNEL_SOURCES = {
     "prefill": ["scan_update.h", "project_kernels.h", "prefill_rows_kernel.h"],
     "step": ["scan_update.h", "step_kernel.h"],
@@ -84,8 +91,9 @@ def read_traffic(workload: str, launches_per_step: int):
         return None
 
 
-def cpu_baseline(wl, inp, channels: int):
-    """The fp64 oracle, as it stands, on a bounded sample: all tokens of `channels` channels."""
+def cpu_baseline(wl, inp, channels: int, scalar_a=None):
+    """The fp64 oracle, as it stands, on a bounded sample: all tokens of `channels` channels
+    (with `scalar_a`, the scaled-identity oracle on that A)."""
     import numpy as np
 
     import oracle
@@ -93,10 +101,11 @@ def cpu_baseline(wl, inp, channels: int):
     threads = min(16, os.cpu_count() or 1)
     x = inp["x"][:, :, :channels]
     dl = inp["delta"][:, :, :channels]
-    A = inp["A"][:channels]
+    A = inp["A"][:channels] if scalar_a is None else scalar_a[:channels]
     args = [np.ascontiguousarray(t.float().numpy(), dtype=np.float64) for t in (x, dl, A, inp["B"], inp["C"])]
+    fn = oracle.prefill if scalar_a is None else oracle.prefill_scalar_a
     t0 = time.perf_counter()
-    oracle.prefill(*args, nthreads=threads)
+    fn(*args, nthreads=threads)
     dt = time.perf_counter() - t0
     elems = wl.batch * wl.L * channels
     return {"value": elems / dt, "unit": "elems/s", "cores": threads, "kind": "oracle",
@@ -120,6 +129,9 @@ def main():
     ap.add_argument("--chunked", action="store_true",
                     help="prefill through the time-parallel jscan_prefill_chunked (automatic segments) instead of "
                          "the token-by-token jscan_prefill")
+    ap.add_argument("--scalar-a", action="store_true",
+                    help="A is a scaled identity, one value per channel (the Mamba-2 form): "
+                         "jscan_prefill_scalar_a / jscan_step_scalar_a")
     ap.add_argument("--cpu-channels", type=int, default=8192,
                     help="oracle sample: all tokens of the first CPU_CHANNELS channels (default: every channel "
                          "of the 64K workload, a few seconds on 16 cores; 0 = skip)")
@@ -160,6 +172,9 @@ def main():
                           "ms_per_launch": ms, "GBps": 2 * n * 4 / ms / 1e6}), flush=True)
         return
     wl = workloads.get(args.workload)
+    if args.scalar_a and (args.producer or args.chunked):
+        print("bench.py: --scalar-a runs the plain prefill or decode step only", file=sys.stderr)
+        sys.exit(2)
     torch.cuda.set_device(dev)
     log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)  # noqa: E731
 
@@ -168,15 +183,18 @@ def main():
         layers = []
         for layer in range(wl.layers):
             inp = workloads.decode_layer_inputs(wl, layer)
+            if args.scalar_a:
+                inp["A"] = workloads.draw_scalar_a(wl, layer=layer)
             layers.append({k: v.to(dev) for k, v in inp.items()})
             layers[-1]["h"] = layers[-1].pop("h0")
 
         for L_ in layers:
             L_["y"] = torch.empty_like(L_["x"])
+        step_fn = jscan.step_scalar_a if args.scalar_a else jscan.step
 
         def token_step():
             for L_ in layers:
-                jscan.step(L_["h"], L_["x"], L_["delta"], L_["A"], L_["B"], L_["C"], y_t=L_["y"])
+                step_fn(L_["h"], L_["x"], L_["delta"], L_["A"], L_["B"], L_["C"], y_t=L_["y"])
 
         # One token step is 28 short launches; a captured HIP graph replays them without the
         # host launch overhead of 28 separate calls.
@@ -236,6 +254,13 @@ def main():
             def one_step():
                 jscan.prefill_chunked(d["x"], d["delta"], d["A"], d["B"], d["C"], y=y, h_final=h, workspace=ws)
             launches = 3 if ws_bytes > 0 else 1
+        elif args.scalar_a:
+            host_a = workloads.draw_scalar_a(wl)
+            d["a"] = host_a.to(dev)
+
+            def one_step():
+                jscan.prefill_scalar_a(d["x"], d["delta"], d["a"], d["B"], d["C"], y=y, h_final=h)
+            launches = 1
         else:
             def one_step():
                 jscan.prefill(d["x"], d["delta"], d["A"], d["B"], d["C"], y=y, h_final=h)
@@ -262,6 +287,8 @@ def main():
     elems = wl.elems
     value = elems / (ms_step * 1e-3)
     alg_bytes = algorithmic_bytes(wl)
+    if args.scalar_a:   # A is [D] instead of [D, N]
+        alg_bytes -= (wl.D * wl.N - wl.D) * 4 * max(wl.layers, 1)
     gbps = alg_bytes / (ms_step * 1e-3) / 1e9
     per_launch_ms = ms_step / launches
     producer_info = None
@@ -302,11 +329,14 @@ def main():
         roofline["frac"] = round(roofline["achieved"] / HBM_PEAK_GBPS, 4)
     else:
         state_elems = elems * wl.N
-        achieved_tf = state_elems * FLOPS_PER_STATE_ELEM / (per_launch_ms * 1e-3) / 1e12
-        peak_tf = PEAK_STATE_ELEMS * FLOPS_PER_STATE_ELEM / 1e12
+        slots, flops = (SCALAR_A_SLOTS, SCALAR_A_FLOPS) if args.scalar_a else (SLOTS_PER_STATE_ELEM,
+                                                                              FLOPS_PER_STATE_ELEM)
+        achieved_tf = state_elems * flops / (per_launch_ms * 1e-3) / 1e12
+        peak_tf = VALU_SLOTS_PER_S / slots * flops / 1e12
         roofline = {"bound": "alu", "achieved": round(achieved_tf, 2), "peak": round(peak_tf, 2), "unit": "TFLOP/s",
                     "frac": round(achieved_tf / peak_tf, 4)}
-    roofline["traffic"] = None if (args.chunked or args.producer) else read_traffic(wl.name, launches)
+    roofline["traffic"] = None if (args.chunked or args.producer) else read_traffic(
+        wl.name + ("_scalar_a" if args.scalar_a else ""), launches)
 
     out = {
         "metric": METRIC,
@@ -323,6 +353,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "L": wl.L, "D": wl.D, "N": wl.N,
                    "layers": wl.layers, "io_dtype": wl.dtype, "state_dtype": "f32",
+                   "A": "scaled_identity" if args.scalar_a else "diagonal",
                    "path": ("producer+fused-scan" if args.fused else "producer+scan") if args.producer
                    else ("time-parallel" if args.chunked else "sequential")},
         "hbm_GBps": round(gbps, 1),
@@ -333,7 +364,8 @@ def main():
     if producer_info is not None:
         out["producer"] = producer_info
     if host_inp is not None and args.cpu_channels > 0 and wl.layers == 1:
-        out["cpu_baseline"] = cpu_baseline(wl, host_inp, min(args.cpu_channels, wl.D))
+        out["cpu_baseline"] = cpu_baseline(wl, host_inp, min(args.cpu_channels, wl.D),
+                                           host_a if args.scalar_a else None)
         log(f"oracle sample: {out['cpu_baseline']['sample']}")
     print(json.dumps(out), flush=True)
 

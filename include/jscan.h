@@ -206,6 +206,32 @@ jscan_status jscan_step(float *h, const void *x_t, const void *delta_t, const fl
                         int64_t N, int64_t ld_xd, int64_t ld_bc, jscan_dtype dtype,
                         void *stream);
 
+/*
+ * Scaled-identity A (the Mamba-2 form).  The lesson page ("Jamba - Hybrid SSM-Transformer",
+ * section "Mamba-3", item 2) describes Mamba-2's state matrix as a scaled identity instead of
+ * Mamba-1's real diagonal; everything else about the layer is taken to be unchanged (same
+ * Euler-style input term, same delta, B, C and y).  So A is one value per channel:
+ *     A[d][n] = a[d] for every n,   a [D] fp32.
+ * The decay exp(delta_t[d] * a[d]) is then the same for all 16 states of a channel, and these
+ * kernels evaluate it once per (token, channel) instead of once per state element, by the
+ * same fp32 expression as the general kernels.  Their y, h_final and decode states are
+ * therefore bit-identical to jscan_prefill_resume / jscan_step run on the expanded A[d][n] =
+ * a[d], only faster.
+ *
+ * Prefill from h0 (NULL for the zero state; h0 may equal h_final).  The other arguments,
+ * layouts and errors are those of jscan_prefill_resume, with `a` [D] fp32 in place of A.
+ */
+jscan_status jscan_prefill_scalar_a(const void *x, const void *delta, const float *a,
+                                    const void *B, const void *C, const float *h0, void *y,
+                                    float *h_final, int64_t batch, int64_t L, int64_t D,
+                                    int64_t N, jscan_dtype dtype, void *stream);
+
+/* Decode step with a scaled-identity A: jscan_step with `a` [D] fp32 in place of A. */
+jscan_status jscan_step_scalar_a(float *h, const void *x_t, const void *delta_t, const float *a,
+                                 const void *B_t, const void *C_t, void *y_t, int64_t batch,
+                                 int64_t D, int64_t N, int64_t ld_xd, int64_t ld_bc,
+                                 jscan_dtype dtype, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *jscan_status_string(jscan_status s);
 
@@ -213,7 +239,7 @@ const char *jscan_status_string(jscan_status s);
 int jscan_last_hip_error(void);
 
 /* Library ABI version: 100 * major + minor (101 adds the time-parallel prefill, 102 the
- * producer side, 103 the fused prefill). */
+ * producer side, 103 the fused prefill, 104 the scaled-identity A entry points). */
 int jscan_version(void);
 
 #ifdef __cplusplus

@@ -10,6 +10,8 @@ There is no CPU fallback: without the built library every call raises.
     y, h_final = prefill_chunked(x, delta, A, B, C)        # time-parallel, for few channels
     delta, B, C, d_low = ssm_inputs(x, w_x, g_d, g_B, g_C, w_dt, b_dt)   # producer side (MFMA)
     y, h_final = prefill_fused(x, d_low, w_dt, b_dt, A, B, C)             # delta computed in the scan
+    y, h_final = prefill_scalar_a(x, delta, a, B, C)       # scaled-identity A (a: [D])
+    y_t = step_scalar_a(h, x_t, delta_t, a, B_t, C_t)
 """
 from ._binding import (  # noqa: F401
     D_STATE,
@@ -20,7 +22,9 @@ from ._binding import (  # noqa: F401
     prefill,
     prefill_chunked,
     prefill_fused,
+    prefill_scalar_a,
     ssm_inputs,
     step,
     step_raw,
+    step_scalar_a,
 )

@@ -49,8 +49,11 @@ def library():
     lib.jscan_ssm_inputs.restype = i32
     lib.jscan_prefill_fused.argtypes = [vp, vp, vp, fp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, i64, i32, vp]
     lib.jscan_prefill_fused.restype = i32
+    lib.jscan_prefill_scalar_a.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, i32, vp]
+    lib.jscan_step_scalar_a.argtypes = [fp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
     lib.jscan_prefill_chunked_workspace.restype = i64
-    for f in (lib.jscan_prefill, lib.jscan_prefill_resume, lib.jscan_step, lib.jscan_prefill_chunked):
+    for f in (lib.jscan_prefill, lib.jscan_prefill_resume, lib.jscan_step, lib.jscan_prefill_chunked,
+              lib.jscan_prefill_scalar_a, lib.jscan_step_scalar_a):
         f.restype = i32
     lib.jscan_status_string.argtypes = [i32]
     lib.jscan_status_string.restype = ctypes.c_char_p
@@ -79,12 +82,13 @@ def _require(cond: bool, msg: str):
         raise ValueError(msg)
 
 
-def _check_prefill_args(x, delta, A, B, C, h0):
+def _check_prefill_args(x, delta, A, B, C, h0, scalar_a=False):
     _require(x.is_cuda, "inputs must be CUDA (HIP) tensors")
     _require(x.dtype in _DTYPES, "x must be bfloat16 or float32")
     _require(x.dim() == 3, "x must be [batch, L, D]")
     batch, L, D = x.shape
-    for name, t, shape, dt in (("delta", delta, (batch, L, D), x.dtype), ("A", A, (D, D_STATE), torch.float32),
+    a_shape = (D,) if scalar_a else (D, D_STATE)
+    for name, t, shape, dt in (("delta", delta, (batch, L, D), x.dtype), ("A", A, a_shape, torch.float32),
                                ("B", B, (batch, L, D_STATE), x.dtype), ("C", C, (batch, L, D_STATE), x.dtype)):
         _require(tuple(t.shape) == shape, f"{name} must have shape {shape}, got {tuple(t.shape)}")
         _require(t.dtype == dt, f"{name} must be {dt}")
@@ -115,6 +119,23 @@ def prefill(x, delta, A, B, C, h0=None, y=None, h_final=None):
             st = lib.jscan_prefill(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), *args_tail)
         else:
             st = lib.jscan_prefill_resume(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(h0), *args_tail)
+    _check(st)
+    return y, h_final
+
+
+def prefill_scalar_a(x, delta, a, B, C, h0=None, y=None, h_final=None):
+    """Prefill with a scaled-identity A (``jscan_prefill_scalar_a``): ``a`` ``[D]`` fp32 stands
+    for ``A[d, n] = a[d]``.  Bit-identical to :func:`prefill` on that expanded A, and faster
+    (one decay per token and channel).  Other arguments and results as for :func:`prefill`."""
+    batch, L, D = _check_prefill_args(x, delta, a, B, C, h0, scalar_a=True)
+    if y is None:
+        y = torch.empty_like(x)
+    if h_final is None:
+        h_final = torch.empty((batch, D, D_STATE), dtype=torch.float32, device=x.device)
+    lib = library()
+    with torch.cuda.device(x.device):
+        st = lib.jscan_prefill_scalar_a(_ptr(x), _ptr(delta), _ptr(a), _ptr(B), _ptr(C), _ptr(h0), _ptr(y),
+                                        _ptr(h_final), batch, L, D, D_STATE, _DTYPES[x.dtype], _stream(x.device))
     _check(st)
     return y, h_final
 
@@ -212,21 +233,28 @@ def prefill_fused(x, delta_low, w_dt, b_dt, A, B, C, h0=None, y=None, h_final=No
     return y, h_final
 
 
-def step_raw(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, dtype):
-    """Direct call of ``jscan_step`` on raw tensors/pointers with explicit row strides (no checks
-    beyond the library's own).  ``x_t`` etc. may be tensors or integer device addresses."""
+def step_raw(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, dtype, scalar_a=False):
+    """Direct call of ``jscan_step`` (``jscan_step_scalar_a`` with ``scalar_a``) on raw
+    tensors/pointers with explicit row strides (no checks beyond the library's own).  ``x_t``
+    etc. may be tensors or integer device addresses."""
     lib = library()
 
     def p(v):
         return ctypes.c_void_p(v if isinstance(v, int) else v.data_ptr())
 
     dev = h.device if hasattr(h, "device") else torch.device("cuda")
-    st = lib.jscan_step(p(h), p(x_t), p(delta_t), p(A), p(B_t), p(C_t), p(y_t), batch, D, D_STATE, ld_xd, ld_bc,
-                        _DTYPES[dtype], _stream(dev))
+    fn = lib.jscan_step_scalar_a if scalar_a else lib.jscan_step
+    st = fn(p(h), p(x_t), p(delta_t), p(A), p(B_t), p(C_t), p(y_t), batch, D, D_STATE, ld_xd, ld_bc, _DTYPES[dtype],
+            _stream(dev))
     _check(st)
 
 
-def step(h, x_t, delta_t, A, B_t, C_t, y_t=None):
+def step_scalar_a(h, x_t, delta_t, a, B_t, C_t, y_t=None):
+    """:func:`step` with a scaled-identity A, ``a`` ``[D]`` fp32 (``jscan_step_scalar_a``)."""
+    return step(h, x_t, delta_t, a, B_t, C_t, y_t, _scalar_a=True)
+
+
+def step(h, x_t, delta_t, A, B_t, C_t, y_t=None, _scalar_a=False):
     """One decode token for a batch: h ``[batch, D, 16]`` fp32 is updated in place; x_t, delta_t
     ``[batch, D]`` and B_t, C_t ``[batch, 16]`` (rows may be strided views of prefill tensors,
     e.g. ``x[:, t]``).  Returns y_t ``[batch, D]``."""
@@ -240,7 +268,9 @@ def step(h, x_t, delta_t, A, B_t, C_t, y_t=None):
         _require(t.dtype == x_t.dtype, f"{name} must be {x_t.dtype}")
         _require(t.stride(1) == 1, f"{name} rows must be contiguous")
         _require(t.device == h.device, f"{name} is on another device")
-    _require(A.dtype == torch.float32 and tuple(A.shape) == (D, D_STATE) and A.is_contiguous(), "A must be fp32 [D,16]")
+    a_shape = (D,) if _scalar_a else (D, D_STATE)
+    _require(A.dtype == torch.float32 and tuple(A.shape) == a_shape and A.is_contiguous(),
+             f"A must be a contiguous fp32 tensor of shape {a_shape}")
     ld_xd = x_t.stride(0) if batch > 1 else D
     _require(batch <= 1 or delta_t.stride(0) == ld_xd, "x_t and delta_t must share a row stride")
     ld_bc = B_t.stride(0) if batch > 1 else D_STATE
@@ -251,5 +281,5 @@ def step(h, x_t, delta_t, A, B_t, C_t, y_t=None):
     _require(tuple(y_t.shape) == (batch, D) and y_t.dtype == x_t.dtype and y_t.stride(1) == 1
              and (batch <= 1 or y_t.stride(0) == ld_xd), "y_t must be [batch, D] with x_t's row stride")
     with torch.cuda.device(h.device):
-        step_raw(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, x_t.dtype)
+        step_raw(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, x_t.dtype, scalar_a=_scalar_a)
     return y_t

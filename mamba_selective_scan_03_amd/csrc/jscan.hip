@@ -49,8 +49,8 @@ jscan_status launch_status() {
 constexpr int64_t kMaxBlocks = (int64_t)1 << 30;
 
 // Scans `nrows` rows (see Segments) with the row-mapped kernel when it applies, otherwise
-// with one lane per (row, channel).
-template <typename E, bool kSummary>
+// with one lane per (row, channel).  kScalarA: A is the scaled identity a[D].
+template <typename E, bool kSummary, bool kScalarA = false>
 void launch_rows(const void *x, const void *delta, const float *A, const void *B, const void *C, const float *h0,
                  void *y, float *h_final, float *dsum, const jscan::Segments &sg, int64_t nrows, int64_t D,
                  hipStream_t stream) {
@@ -59,16 +59,17 @@ void launch_rows(const void *x, const void *delta, const float *A, const void *B
     const T *bt = static_cast<const T *>(B), *ct = static_cast<const T *>(C);
     T *yt = static_cast<T *>(y);
     if (jscan::rows_kernel_applies(nrows, D)) {
-        jscan::launch_prefill_rows<E, kSummary>(xt, dt, A, bt, ct, h0, yt, h_final, dsum, sg, nrows, (int)D, stream);
+        jscan::launch_prefill_rows<E, kSummary, false, kScalarA>(xt, dt, A, bt, ct, h0, yt, h_final, dsum, sg, nrows,
+                                                                  (int)D, stream);
         return;
     }
     const int blocks_per_row = (int)((D + 63) / 64);
-    hipLaunchKernelGGL((jscan::prefill_lane_kernel<E, kSummary>), dim3((unsigned)(nrows * blocks_per_row)), dim3(64),
+    hipLaunchKernelGGL((jscan::prefill_lane_kernel<E, kSummary, kScalarA>), dim3((unsigned)(nrows * blocks_per_row)), dim3(64),
                        0, stream, xt, dt, A, bt, ct, h0, yt, h_final, dsum, sg, (int)D, blocks_per_row);
 }
 
 // Token-by-token prefill of whole sequences (one row per sequence).
-template <typename E>
+template <typename E, bool kScalarA = false>
 jscan_status launch_prefill(const void *x, const void *delta, const float *A, const void *B, const void *C,
                             const float *h0, void *y, float *h_final, int64_t batch, int64_t L, int64_t D,
                             hipStream_t stream) {
@@ -79,15 +80,17 @@ jscan_status launch_prefill(const void *x, const void *delta, const float *A, co
         return launch_status();
     }
     const jscan::Segments sg{L, L, 1, 0};
-    launch_rows<E, false>(x, delta, A, B, C, h0, y, h_final, nullptr, sg, batch, D, stream);
+    launch_rows<E, false, kScalarA>(x, delta, A, B, C, h0, y, h_final, nullptr, sg, batch, D, stream);
     return launch_status();
 }
 
-// Argument checks shared by every prefill entry point.  Sets *nothing_to_do for zero-sized
+// Argument checks shared by every prefill entry point.  scalar_a: A holds D values (the
+// scaled identity) instead of D * N.  Sets *nothing_to_do for zero-sized
 // work (which is then OK without a launch).
 jscan_status check_prefill(const void *x, const void *delta, const float *A, const void *B, const void *C,
                            const float *h0, bool h0_required, const void *y, const float *h_final, int64_t batch,
-                           int64_t L, int64_t D, int64_t N, jscan_dtype dtype, bool *nothing_to_do) {
+                           int64_t L, int64_t D, int64_t N, jscan_dtype dtype, bool *nothing_to_do,
+                           bool scalar_a = false) {
     *nothing_to_do = false;
     if (dtype != JSCAN_F32 && dtype != JSCAN_BF16) return JSCAN_ERR_DTYPE;
     if (batch < 0 || L < 0 || D < 0 || N != JSCAN_D_STATE || D % 8 != 0) return JSCAN_ERR_SHAPE;
@@ -108,7 +111,7 @@ jscan_status check_prefill(const void *x, const void *delta, const float *A, con
         if (p && !aligned16(p)) return JSCAN_ERR_ALIGN;
 
     const int64_t seq = batch * L * D * es, bc = batch * L * N * es;
-    const int64_t state = batch * D * N * 4, a_bytes = D * N * 4;
+    const int64_t state = batch * D * N * 4, a_bytes = D * (scalar_a ? 1 : N) * 4;
     const Span sy = span(y, L > 0 ? seq : 0), sh = span(h_final, state);
     const Span inputs[] = {span(x, seq), span(delta, seq), span(A, a_bytes), span(B, bc), span(C, bc)};
     for (const Span &s : inputs)
@@ -125,11 +128,17 @@ jscan_status check_prefill(const void *x, const void *delta, const float *A, con
 jscan_status prefill_impl(const void *x, const void *delta, const float *A, const void *B,
                           const void *C, const float *h0, bool resume, void *y, float *h_final,
                           int64_t batch, int64_t L, int64_t D, int64_t N, jscan_dtype dtype,
-                          void *stream) {
+                          void *stream, bool scalar_a = false) {
     bool empty = false;
-    const jscan_status st = check_prefill(x, delta, A, B, C, h0, resume, y, h_final, batch, L, D, N, dtype, &empty);
+    const jscan_status st =
+        check_prefill(x, delta, A, B, C, h0, resume, y, h_final, batch, L, D, N, dtype, &empty, scalar_a);
     if (st != JSCAN_OK || empty) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (scalar_a) {
+        if (dtype == JSCAN_BF16)
+            return launch_prefill<jscan::BF16, true>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s);
+        return launch_prefill<jscan::F32, true>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s);
+    }
     if (dtype == JSCAN_BF16)
         return launch_prefill<jscan::BF16>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s);
     return launch_prefill<jscan::F32>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s);
@@ -215,18 +224,54 @@ void launch_ssm_inputs(const uint16_t *x, const uint16_t *w_x, const float *g_d,
 
 // ---- decode step -----------------------------------------------------------------------
 
-template <typename E>
+template <typename E, bool kScalarA>
 jscan_status launch_step(float *h, const void *x_t, const void *delta_t, const float *A,
                          const void *B_t, const void *C_t, void *y_t, int64_t batch, int64_t D,
                          int64_t ld_xd, int64_t ld_bc, hipStream_t stream) {
     using T = typename E::store_t;
     const int blocks_per_rows = (int)((D * 4 + 255) / 256);
     const int64_t row_groups = (batch + jscan::step::kRows - 1) / jscan::step::kRows;
-    hipLaunchKernelGGL(jscan::step_kernel<E>, dim3((unsigned)(row_groups * blocks_per_rows)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((jscan::step_kernel<E, kScalarA>), dim3((unsigned)(row_groups * blocks_per_rows)), dim3(256), 0, stream,
                        h, static_cast<const T *>(x_t), static_cast<const T *>(delta_t), A,
                        static_cast<const T *>(B_t), static_cast<const T *>(C_t), static_cast<T *>(y_t), (int)batch,
                        (int)D, blocks_per_rows, ld_xd, ld_bc);
     return launch_status();
+}
+
+// Checks and launch shared by the two decode-step entry points.  scalar_a: A holds D values.
+jscan_status step_impl(float *h, const void *x_t, const void *delta_t, const float *A, const void *B_t, const void *C_t,
+                       void *y_t, int64_t batch, int64_t D, int64_t N, int64_t ld_xd, int64_t ld_bc, jscan_dtype dtype,
+                       void *stream, bool scalar_a) {
+    if (dtype != JSCAN_F32 && dtype != JSCAN_BF16) return JSCAN_ERR_DTYPE;
+    if (batch < 0 || D < 0 || N != JSCAN_D_STATE || D % 8 != 0) return JSCAN_ERR_SHAPE;
+    if (D > (1 << 24) || batch > (1 << 20)) return JSCAN_ERR_SHAPE;
+    if ((batch + jscan::step::kRows - 1) / jscan::step::kRows * ((D * 4 + 255) / 256) > kMaxBlocks)
+        return JSCAN_ERR_SHAPE;
+    if (batch == 0 || D == 0) return JSCAN_OK;
+    if (ld_xd < D || ld_bc < N || ld_xd % 8 != 0 || ld_bc % 8 != 0) return JSCAN_ERR_SHAPE;
+    if (!h || !x_t || !delta_t || !A || !B_t || !C_t || !y_t) return JSCAN_ERR_NULL;
+    const void *arrays[] = {h, x_t, delta_t, A, B_t, C_t, y_t};
+    for (const void *p : arrays)
+        if (!aligned16(p)) return JSCAN_ERR_ALIGN;
+
+    const int64_t es = elem_bytes(dtype);
+    const int64_t rows_xd = ((batch - 1) * ld_xd + D) * es, rows_bc = ((batch - 1) * ld_bc + N) * es;
+    const Span sh = span(h, batch * D * N * 4), sy = span(y_t, rows_xd);
+    const Span inputs[] = {span(x_t, rows_xd), span(delta_t, rows_xd), span(A, D * (scalar_a ? 1 : N) * 4), span(B_t, rows_bc),
+                           span(C_t, rows_bc)};
+    for (const Span &s : inputs)
+        if (overlaps(sy, s) || overlaps(sh, s)) return JSCAN_ERR_ALIAS;
+    if (overlaps(sy, sh)) return JSCAN_ERR_ALIAS;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (scalar_a) {
+        if (dtype == JSCAN_BF16)
+            return launch_step<jscan::BF16, true>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s);
+        return launch_step<jscan::F32, true>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s);
+    }
+    if (dtype == JSCAN_BF16)
+        return launch_step<jscan::BF16, false>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s);
+    return launch_step<jscan::F32, false>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s);
 }
 
 }  // namespace
@@ -287,31 +332,19 @@ jscan_status jscan_step(float *h, const void *x_t, const void *delta_t, const fl
                         const void *B_t, const void *C_t, void *y_t, int64_t batch, int64_t D,
                         int64_t N, int64_t ld_xd, int64_t ld_bc, jscan_dtype dtype,
                         void *stream) {
-    if (dtype != JSCAN_F32 && dtype != JSCAN_BF16) return JSCAN_ERR_DTYPE;
-    if (batch < 0 || D < 0 || N != JSCAN_D_STATE || D % 8 != 0) return JSCAN_ERR_SHAPE;
-    if (D > (1 << 24) || batch > (1 << 20)) return JSCAN_ERR_SHAPE;
-    if ((batch + jscan::step::kRows - 1) / jscan::step::kRows * ((D * 4 + 255) / 256) > kMaxBlocks)
-        return JSCAN_ERR_SHAPE;
-    if (batch == 0 || D == 0) return JSCAN_OK;
-    if (ld_xd < D || ld_bc < N || ld_xd % 8 != 0 || ld_bc % 8 != 0) return JSCAN_ERR_SHAPE;
-    if (!h || !x_t || !delta_t || !A || !B_t || !C_t || !y_t) return JSCAN_ERR_NULL;
-    const void *arrays[] = {h, x_t, delta_t, A, B_t, C_t, y_t};
-    for (const void *p : arrays)
-        if (!aligned16(p)) return JSCAN_ERR_ALIGN;
+    return step_impl(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, N, ld_xd, ld_bc, dtype, stream, false);
+}
 
-    const int64_t es = elem_bytes(dtype);
-    const int64_t rows_xd = ((batch - 1) * ld_xd + D) * es, rows_bc = ((batch - 1) * ld_bc + N) * es;
-    const Span sh = span(h, batch * D * N * 4), sy = span(y_t, rows_xd);
-    const Span inputs[] = {span(x_t, rows_xd), span(delta_t, rows_xd), span(A, D * N * 4), span(B_t, rows_bc),
-                           span(C_t, rows_bc)};
-    for (const Span &s : inputs)
-        if (overlaps(sy, s) || overlaps(sh, s)) return JSCAN_ERR_ALIAS;
-    if (overlaps(sy, sh)) return JSCAN_ERR_ALIAS;
+jscan_status jscan_prefill_scalar_a(const void *x, const void *delta, const float *a, const void *B, const void *C,
+                                    const float *h0, void *y, float *h_final, int64_t batch, int64_t L, int64_t D,
+                                    int64_t N, jscan_dtype dtype, void *stream) {
+    return prefill_impl(x, delta, a, B, C, h0, false, y, h_final, batch, L, D, N, dtype, stream, true);
+}
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (dtype == JSCAN_BF16)
-        return launch_step<jscan::BF16>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s);
-    return launch_step<jscan::F32>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s);
+jscan_status jscan_step_scalar_a(float *h, const void *x_t, const void *delta_t, const float *a, const void *B_t,
+                                 const void *C_t, void *y_t, int64_t batch, int64_t D, int64_t N, int64_t ld_xd,
+                                 int64_t ld_bc, jscan_dtype dtype, void *stream) {
+    return step_impl(h, x_t, delta_t, a, B_t, C_t, y_t, batch, D, N, ld_xd, ld_bc, dtype, stream, true);
 }
 
 jscan_status jscan_ssm_inputs(const void *x, const void *w_x, const float *g_delta, const float *g_B,
@@ -405,6 +438,6 @@ const char *jscan_status_string(jscan_status s) {
 
 int jscan_last_hip_error(void) { return g_last_hip_error; }
 
-int jscan_version(void) { return 103; }
+int jscan_version(void) { return 104; }
 
 }  // extern "C"

@@ -15,8 +15,9 @@ namespace jscan {
 
 // One lane scans one channel of one row (see Segments) from the row's initial state (zero
 // when h0 is null).  A segment-summary launch (kSummary) writes no y; it writes the row's
-// final state and the sum of the row's delta values to dsum[row][D].
-template <typename E, bool kSummary>
+// final state and the sum of the row's delta values to dsum[row][D].  With kScalarA, A is the
+// scaled identity a[D] and the channel's one decay per token serves all 16 states.
+template <typename E, bool kSummary, bool kScalarA = false>
 __global__ __launch_bounds__(64) void prefill_lane_kernel(
     const typename E::store_t *__restrict__ x, const typename E::store_t *__restrict__ dl,
     const float *__restrict__ A, const typename E::store_t *__restrict__ B,
@@ -28,10 +29,11 @@ __global__ __launch_bounds__(64) void prefill_lane_kernel(
     if (d >= D) return;  // no cross-lane work below, so idle lanes may leave
     const RowSpan span = row_span(sg, vrow);
 
+    static_assert(!kScalarA || !kSummary, "the scaled-identity path is a plain prefill");
     float a2[kDState], h[kDState];
 #pragma unroll
     for (int n = 0; n < kDState; ++n) {
-        a2[n] = scaled_A(A[(int64_t)d * kDState + n]);
+        a2[n] = scaled_A(kScalarA ? A[d] : A[(int64_t)d * kDState + n]);
         h[n] = h0 ? h0[((int64_t)vrow * D + d) * kDState + n] : 0.0f;
     }
     const int64_t row = span.tok0;
@@ -45,10 +47,12 @@ __global__ __launch_bounds__(64) void prefill_lane_kernel(
     for (int64_t t = 0; t < span.len; ++t) {
         const float xv = E::load(xr + t * D), dv = E::load(dr + t * D);
         const float dx = delta_x(dv, xv);
+        const float abar = kScalarA ? decay(dv, a2[0]) : 0.0f;
         float acc = 0.0f;
 #pragma unroll
         for (int n = 0; n < kDState; ++n) {
-            h[n] = advance(h[n], dv, a2[n], dx, E::load(Br + t * kDState + n));
+            const float b = E::load(Br + t * kDState + n);
+            h[n] = kScalarA ? advance_decayed(h[n], abar, dx, b) : advance(h[n], dv, a2[n], dx, b);
             if constexpr (!kSummary) acc = __builtin_fmaf(E::load(Cr + t * kDState + n), h[n], acc);
         }
         if constexpr (kSummary)

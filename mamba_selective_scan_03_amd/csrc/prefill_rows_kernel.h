@@ -4,8 +4,8 @@
 // Why this mapping.  Each (channel, state) pair is a chain of L dependent updates.  Keeping
 // the final state bit-identical to the decode step means every chain must be walked token
 // by token in one lane, so all parallelism comes from batch * D * 16 chains: 131072 at
-// batch 1.  That is 64 chains per SIMD on a 256-CU chip, so a lane carries G = 2 states and
-// every SIMD runs exactly one wave.
+// batch 1.  That is 128 chains per SIMD on a 256-CU chip, so a lane carries G = 2 states and
+// every SIMD runs exactly one scan wave.
 //
 // Lane layout.  A wave is 4 rows of 16 lanes.  Lane c of a row owns channel c of a 16-channel
 // group; row r owns the state pair n = 8*sh + 2*r + {0,1}, where sh picks one half of the
@@ -16,7 +16,10 @@
 //     (row_newbcast:k) hands token k's value to the whole row inside the multiply.  No extra
 //     instruction is issued.
 //   * delta_t[d] and delta_t[d] * x_t[d] are per lane (per channel).  The workgroup converts
-//     each tile once into fp32 pairs in LDS, and every row reads them as a broadcast.
+//     each tile once into fp32 pairs in LDS, and every row reads them as a broadcast.  With a
+//     scaled-identity A (kScalarA: one a[d] for all states of a channel) the pair carries the
+//     channel's decay 2^(delta * a2[d]) in place of delta, computed once per (token, channel)
+//     while staging, and the scan waves run no exponential at all.
 //   * y_t[d] = sum over 16 states = 2 states in-lane, 4 rows in-wave (two permlane swap
 //     stages), then 2 waves through LDS.  The last stage is fused with the bf16 conversion
 //     and a coalesced row store.
@@ -213,11 +216,14 @@ __device__ __forceinline__ void fused_delta(const u32x4_t (&f)[fused::kKS], cons
 
 // Converts one quarter of a tile from registers into LDS: channel 4q + part of this thread's
 // (delta*x, delta) fp32 pairs, and states nb + 2*part, nb + 2*part + 1 of its B or C token.
-// Tokens at or past L become identity tokens (delta = 0, x = -0, B = C = 0).  A tile is staged
-// a quarter per 16-token group so that the LDS writes never pile up behind each other.
-template <typename E, int part>
+// With kScalarA the second member is the channel's decay 2^(delta * a2) instead, a2 taken
+// from a2q (this thread's four channels).  Tokens at or past L become identity tokens
+// (delta = 0, x = -0, B = C = 0; their decay is exactly 1).  A tile is staged a quarter per
+// 16-token group so that the LDS writes never pile up behind each other.
+template <typename E, int part, bool kScalarA>
 __device__ __forceinline__ void stage_part(const TileRegs<E> &R, float *dx_s, float *bc_s, int64_t t0, int64_t L,
-                                           int tid) {
+                                           int tid, const float4 &a2q) {
+    const float a2 = part == 0 ? a2q.x : part == 1 ? a2q.y : part == 2 ? a2q.z : a2q.w;
     const int p = tid >> 3, q = tid & 7;
     float4 v;
     {
@@ -226,11 +232,11 @@ __device__ __forceinline__ void stage_part(const TileRegs<E> &R, float *dx_s, fl
         Vec4<E>::widen(live0 ? R.x[0] : Vec4<E>::neg_zero(), xv);
         Vec4<E>::widen(live0 ? R.dl[0] : Vec4<E>::zero(), dv);
         v.x = delta_x(dv[part], xv[part]);
-        v.y = dv[part];
+        v.y = kScalarA ? decay(dv[part], a2) : dv[part];
         Vec4<E>::widen(live1 ? R.x[1] : Vec4<E>::neg_zero(), xv);
         Vec4<E>::widen(live1 ? R.dl[1] : Vec4<E>::zero(), dv);
         v.z = delta_x(dv[part], xv[part]);
-        v.w = dv[part];
+        v.w = kScalarA ? decay(dv[part], a2) : dv[part];
     }
     *reinterpret_cast<float4 *>(dx_s + p * rows::kDxStride + (4 * q + part) * 4) = v;
     const int tb = (tid & 127) >> 1, nb = (tid & 1) * 8;
@@ -241,13 +247,13 @@ __device__ __forceinline__ void stage_part(const TileRegs<E> &R, float *dx_s, fl
     dst[(nb + 2 * part) * rows::kBcStride + tb] = f[(2 * part) & 3];
     dst[(nb + 2 * part + 1) * rows::kBcStride + tb] = f[(2 * part + 1) & 3];
 }
-template <typename E>
+template <typename E, bool kScalarA>
 __device__ __forceinline__ void stage_tile(const TileRegs<E> &R, float *dx_s, float *bc_s, int64_t t0, int64_t L,
-                                           int tid) {
-    stage_part<E, 0>(R, dx_s, bc_s, t0, L, tid);
-    stage_part<E, 1>(R, dx_s, bc_s, t0, L, tid);
-    stage_part<E, 2>(R, dx_s, bc_s, t0, L, tid);
-    stage_part<E, 3>(R, dx_s, bc_s, t0, L, tid);
+                                           int tid, const float4 &a2q) {
+    stage_part<E, 0, kScalarA>(R, dx_s, bc_s, t0, L, tid, a2q);
+    stage_part<E, 1, kScalarA>(R, dx_s, bc_s, t0, L, tid, a2q);
+    stage_part<E, 2, kScalarA>(R, dx_s, bc_s, t0, L, tid, a2q);
+    stage_part<E, 3, kScalarA>(R, dx_s, bc_s, t0, L, tid, a2q);
 }
 
 // One 16-token group's LDS operands for one lane: (delta*x, delta) of its channel for the 16
@@ -274,15 +280,21 @@ __device__ __forceinline__ void load_half(GroupRegs &g, const float *dxs, const 
 }
 
 // One token: advance this lane's two states and return C*h summed over them (a summary
-// scan adds the token's delta to `dsum` instead and returns nothing useful).
-template <int TAU, bool kSummary>
+// scan adds the token's delta to `dsum` instead and returns nothing useful).  With kScalarA
+// the pair's second member is already the decay.
+template <int TAU, bool kSummary, bool kScalarA>
 __device__ __forceinline__ float token_step(const GroupRegs &g, float &h_0, float &h_1, float a2_0, float a2_1,
                                             float &dsum) {
     const float4 v = g.v[TAU >> 1];
     const float dxv = (TAU & 1) ? v.z : v.x;
     const float dv = (TAU & 1) ? v.w : v.y;
-    h_0 = advance(h_0, dv, a2_0, dxv, row_bcast<TAU>(g.b0));
-    h_1 = advance(h_1, dv, a2_1, dxv, row_bcast<TAU>(g.b1));
+    if constexpr (kScalarA) {
+        h_0 = advance_decayed(h_0, dv, dxv, row_bcast<TAU>(g.b0));
+        h_1 = advance_decayed(h_1, dv, dxv, row_bcast<TAU>(g.b1));
+    } else {
+        h_0 = advance(h_0, dv, a2_0, dxv, row_bcast<TAU>(g.b0));
+        h_1 = advance(h_1, dv, a2_1, dxv, row_bcast<TAU>(g.b1));
+    }
     if constexpr (kSummary) {
         dsum += dv;
         return 0.0f;
@@ -295,11 +307,11 @@ __device__ __forceinline__ float token_step(const GroupRegs &g, float &h_0, floa
 // partials (summed over the wave's 4 rows) in the y exchange rows `ys` (row = token in group).
 // A segment-summary scan (kSummary) produces no y; it adds the tokens' delta to `dsum` in
 // token order instead, and the y arithmetic is left out of the code altogether.
-template <int H, bool kSummary>
+template <int H, bool kSummary, bool kScalarA>
 __device__ __forceinline__ void scan_half(const GroupRegs &g, float &h_0, float &h_1, float a2_0, float a2_1, float *ys,
                                           int rt, int ch, float &dsum) {
     float P[8];
-#define JSCAN_STEP(i) P[i] = token_step<8 * H + (i), kSummary>(g, h_0, h_1, a2_0, a2_1, dsum);
+#define JSCAN_STEP(i) P[i] = token_step<8 * H + (i), kSummary, kScalarA>(g, h_0, h_1, a2_0, a2_1, dsum);
     JSCAN_STEP(0) JSCAN_STEP(1) JSCAN_STEP(2) JSCAN_STEP(3)
     JSCAN_STEP(4) JSCAN_STEP(5) JSCAN_STEP(6) JSCAN_STEP(7)
 #undef JSCAN_STEP
@@ -360,8 +372,9 @@ __device__ __forceinline__ void write_final(const FinalRegs &F, typename E::stor
 // One work-group scans 32 channels of one row (see Segments) from the row's initial state
 // (zero when h0 is null).  A segment-summary launch (kSummary) writes no y; it writes the
 // row's final state and, per channel, the sum of the row's delta values to dsum[row][D].
-// With kFused, delta is not read: the helper waves compute it from dp (bf16 only).
-template <typename E, bool kSummary, bool kFused = false>
+// With kFused, delta is not read: the helper waves compute it from dp (bf16 only).  With
+// kScalarA, A is the scaled identity a[D] (one value per channel) instead of A[D][16].
+template <typename E, bool kSummary, bool kFused = false, bool kScalarA = false>
 __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_rows_kernel(
     const typename E::store_t *__restrict__ x, const typename E::store_t *__restrict__ dl,
     const float *__restrict__ A, const typename E::store_t *__restrict__ B,
@@ -369,6 +382,7 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
     typename E::store_t *__restrict__ y, float *__restrict__ h_final, float *__restrict__ dsum, Segments sg, int D,
     int blocks_per_row, int xcd_stride, DeltaProj dp) {
     static_assert(!kFused || (sizeof(typename E::store_t) == 2 && !kSummary), "the fused delta path is bf16 only");
+    static_assert(!kScalarA || (!kSummary && !kFused), "the scaled-identity path is a plain prefill");
     __shared__ __attribute__((aligned(16))) float dx_s[2][rows::kDxSize];
     __shared__ __attribute__((aligned(16))) float bc_s[2][2 * rows::kBcSize];
     __shared__ __attribute__((aligned(16))) float y_s[2][rows::kYSize];
@@ -402,6 +416,12 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
         float4 bias[2];
         u32x4_t dfr[2][fused::kKS];
         uint16_t *xch = xch_s + (kFused ? hw * fused::kXchWave : 0);
+        // scaled-identity A: A2 of this thread's staging channels 4q .. 4q + 3
+        float4 a2q = make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (kScalarA) {
+            const float4 av = *reinterpret_cast<const float4 *>(A + d0 + 4 * (tid & 7));
+            a2q = make_float4(scaled_A(av.x), scaled_A(av.y), scaled_A(av.z), scaled_A(av.w));
+        }
         if constexpr (kFused) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -417,7 +437,7 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
             load_dlow(dfr[0], dp.d_low, row, 0, L, hw, l);
             fused_delta(dfr[0], wf, bias, xch, R[0], l);
         }
-        stage_tile<E>(R[0], dx_s[0], bc_s[0], 0, L, tid);
+        stage_tile<E, kScalarA>(R[0], dx_s[0], bc_s[0], 0, L, tid, a2q);
         load_tile<E, !kFused>(R[1], xb, db, bcb, rows::kT, L, D, tid);
         load_tile<E, !kFused>(R[0], xb, db, bcb, 2 * rows::kT, L, D, tid);
         if constexpr (kFused) {
@@ -430,7 +450,7 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
             constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
             if (k + 1 < ntiles) {
                 if constexpr (kFused) fused_delta(dfr[nxt], wf, bias, xch, R[nxt], l);
-                stage_tile<E>(R[nxt], dx_s[nxt], bc_s[nxt], (int64_t)(k + 1) * rows::kT, L, tid);
+                stage_tile<E, kScalarA>(R[nxt], dx_s[nxt], bc_s[nxt], (int64_t)(k + 1) * rows::kT, L, tid, a2q);
                 if (k + 3 < ntiles) {
                     load_tile<E, !kFused>(R[nxt], xb, db, bcb, (int64_t)(k + 3) * rows::kT, L, D, tid);
                     if constexpr (kFused) load_dlow(dfr[nxt], dp.d_low, row, (int64_t)(k + 3) * rows::kT, L, hw, l);
@@ -465,8 +485,8 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
     const int d = d0 + ch;
     const int n0 = 8 * sh + 2 * r;          // this lane's states n0, n0 + 1
 
-    const float a2_0 = scaled_A(A[(int64_t)d * kDState + n0]);
-    const float a2_1 = scaled_A(A[(int64_t)d * kDState + n0 + 1]);
+    const float a2_0 = kScalarA ? 0.0f : scaled_A(A[(int64_t)d * kDState + n0]);
+    const float a2_1 = kScalarA ? 0.0f : scaled_A(A[(int64_t)d * kDState + n0 + 1]);
     float h_0 = 0.0f, h_1 = 0.0f;
     if (h0) {
         const float2 hv = *reinterpret_cast<const float2 *>(h0 + ((int64_t)vrow * D + d) * kDState + n0);
@@ -491,31 +511,31 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
         const float *dxc = dx_s[cur], *bcc = bc_s[cur];
         load_half<0>(G[1], dxc, bcc, 16, ch, n0, c);
         JSCAN_SB;
-        scan_half<0, kSummary>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch, dacc);
+        scan_half<0, kSummary, kScalarA>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch, dacc);
         JSCAN_SB;
         load_half<1>(G[1], dxc, bcc, 16, ch, n0, c);
         JSCAN_SB;
-        scan_half<1, kSummary>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch, dacc);
+        scan_half<1, kSummary, kScalarA>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch, dacc);
         JSCAN_SB;
         load_half<0>(G[0], dxc, bcc, 32, ch, n0, c);
         JSCAN_SB;
-        scan_half<0, kSummary>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch, dacc);
+        scan_half<0, kSummary, kScalarA>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch, dacc);
         JSCAN_SB;
         load_half<1>(G[0], dxc, bcc, 32, ch, n0, c);
         JSCAN_SB;
-        scan_half<1, kSummary>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch, dacc);
+        scan_half<1, kSummary, kScalarA>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch, dacc);
         JSCAN_SB;
         load_half<0>(G[1], dxc, bcc, 48, ch, n0, c);
         JSCAN_SB;
-        scan_half<0, kSummary>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch, dacc);
+        scan_half<0, kSummary, kScalarA>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch, dacc);
         JSCAN_SB;
         load_half<1>(G[1], dxc, bcc, 48, ch, n0, c);
         JSCAN_SB;
-        scan_half<1, kSummary>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch, dacc);
+        scan_half<1, kSummary, kScalarA>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch, dacc);
         JSCAN_SB;
-        scan_half<0, kSummary>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch, dacc);
+        scan_half<0, kSummary, kScalarA>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch, dacc);
         JSCAN_SB;
-        scan_half<1, kSummary>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch, dacc);
+        scan_half<1, kSummary, kScalarA>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch, dacc);
         __syncthreads();
         if (k + 1 < ntiles) {
             load_half<0>(G[0], dx_s[nxt], bc_s[nxt], 0, ch, n0, c);
@@ -539,7 +559,7 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
 inline bool rows_kernel_applies(int64_t batch, int64_t D) { return D % rows::kCh == 0 && batch * D <= 65536; }
 
 // Launches one work-group per 32 channels of each of the `nrows` rows described by sg.
-template <typename E, bool kSummary, bool kFused = false>
+template <typename E, bool kSummary, bool kFused = false, bool kScalarA = false>
 void launch_prefill_rows(const typename E::store_t *x, const typename E::store_t *dl, const float *A,
                          const typename E::store_t *B, const typename E::store_t *C, const float *h0,
                          typename E::store_t *y, float *h_final, float *dsum, const Segments &sg, int64_t nrows,
@@ -547,7 +567,7 @@ void launch_prefill_rows(const typename E::store_t *x, const typename E::store_t
     const int blocks_per_row = D / rows::kCh;
     const int64_t blocks = nrows * blocks_per_row;
     const int xcd_stride = (blocks % 8 == 0) ? (int)(blocks / 8) : 0;
-    hipLaunchKernelGGL((prefill_rows_kernel<E, kSummary, kFused>), dim3((unsigned)blocks), dim3(rows::kThreads), 0,
+    hipLaunchKernelGGL((prefill_rows_kernel<E, kSummary, kFused, kScalarA>), dim3((unsigned)blocks), dim3(rows::kThreads), 0,
                        stream, x, dl, A, B, C, h0, y, h_final, dsum, sg, D, blocks_per_row, xcd_stride, dp);
 }
 

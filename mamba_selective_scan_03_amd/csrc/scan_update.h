@@ -5,6 +5,12 @@
 // tokens.  That is what lets a prefill's final state equal, bit for bit, the state after
 // the same tokens fed one at a time through the decode step.
 //
+// With a scaled-identity A (one value a[d] for all 16 states of a channel, the Mamba-2 form)
+// the decay 2^(delta * a2[d]) is the same for the whole channel.  The kernels for that form
+// evaluate it once per (token, channel) with the same `decay()` and hand it to
+// `advance_decayed()`, which is the second half of `advance()`: their states are therefore
+// bit-identical to the general kernels' run on A[d][n] = a[d].
+//
 // The recurrence is the S6 equation of the Jamba notes page ("Jamba: A Hybrid
 // Transformer-Mamba Language Model", section "Mamba layer"):
 //     h_t = Abar_t h_{t-1} + Bbar_t x_t,   Abar_t = exp(delta_t A),   Bbar_t x_t = delta_t B_t x_t
@@ -30,9 +36,14 @@ __device__ __forceinline__ float decay(float delta, float a2) {
 // The fp32 product delta * x, shared by the 16 states of one channel.
 __device__ __forceinline__ float delta_x(float delta, float x) { return delta * x; }
 
-// One state element advanced by one token:  h <- Abar * h + (delta * x) * B.
+// One state element advanced by one token, given its decay:  h <- Abar * h + (delta * x) * B.
+__device__ __forceinline__ float advance_decayed(float h, float abar, float dx, float b) {
+    return __builtin_fmaf(abar, h, dx * b);
+}
+
+// The same with the decay evaluated here, from delta and A2.
 __device__ __forceinline__ float advance(float h, float delta, float a2, float dx, float b) {
-    return __builtin_fmaf(decay(delta, a2), h, dx * b);
+    return advance_decayed(h, decay(delta, a2), dx, b);
 }
 
 // A compile-time integer as a value: lets an unrolled loop body pick register sets and LDS

@@ -44,7 +44,8 @@ template <> struct Quad<F32> {
     static __device__ __forceinline__ float4 load(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 };
 
-template <typename E>
+// With kScalarA, A is the scaled identity a[D]: one decay per (row, channel) serves the quad.
+template <typename E, bool kScalarA = false>
 __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ h,
                                                    const typename E::store_t *__restrict__ x,
                                                    const typename E::store_t *__restrict__ dl,
@@ -59,7 +60,8 @@ __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ h,
     if (lane_in_row >= D * 4) return;  // whole quads leave together (D * 4 is a multiple of 4)
     const int d = lane_in_row >> 2, q = lane_in_row & 3;
 
-    const float4 av = *reinterpret_cast<const float4 *>(A + (int64_t)d * kDState + q * 4);
+    const float4 av = kScalarA ? make_float4(A[d], A[d], A[d], A[d])
+                               : *reinterpret_cast<const float4 *>(A + (int64_t)d * kDState + q * 4);
     const float a0 = scaled_A(av.x), a1 = scaled_A(av.y), a2 = scaled_A(av.z), a3 = scaled_A(av.w);
     float4 hv[NR], bv[NR], cv[NR];
     float xv[NR], dv[NR];
@@ -78,10 +80,18 @@ __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ h,
         const int b = rg * NR + j;
         const float dx = delta_x(dv[j], xv[j]);
         float4 hn;
-        hn.x = advance(hv[j].x, dv[j], a0, dx, bv[j].x);
-        hn.y = advance(hv[j].y, dv[j], a1, dx, bv[j].y);
-        hn.z = advance(hv[j].z, dv[j], a2, dx, bv[j].z);
-        hn.w = advance(hv[j].w, dv[j], a3, dx, bv[j].w);
+        if constexpr (kScalarA) {
+            const float abar = decay(dv[j], a0);
+            hn.x = advance_decayed(hv[j].x, abar, dx, bv[j].x);
+            hn.y = advance_decayed(hv[j].y, abar, dx, bv[j].y);
+            hn.z = advance_decayed(hv[j].z, abar, dx, bv[j].z);
+            hn.w = advance_decayed(hv[j].w, abar, dx, bv[j].w);
+        } else {
+            hn.x = advance(hv[j].x, dv[j], a0, dx, bv[j].x);
+            hn.y = advance(hv[j].y, dv[j], a1, dx, bv[j].y);
+            hn.z = advance(hv[j].z, dv[j], a2, dx, bv[j].z);
+            hn.w = advance(hv[j].w, dv[j], a3, dx, bv[j].w);
+        }
         float p = cv[j].x * hn.x;
         p = __builtin_fmaf(cv[j].y, hn.y, p);
         p = __builtin_fmaf(cv[j].z, hn.z, p);

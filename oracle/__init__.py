@@ -16,8 +16,9 @@ for every (batch, channel, state) with diagonal A (lesson page "Jamba - Hybrid
 SSM-Transformer", section "Mamba-3", item 2).  Shapes: x, delta, y ``[batch, L, D]``;
 A ``[D, N]``; B, C ``[batch, L, N]``; states ``[batch, D, N]``.
 
-``oracle.producer`` is the fp64 (numpy) oracle of the producer side that computes delta, B
-and C from x.
+``prefill_scalar_a`` / ``step_scalar_a`` are the same recurrence with a scaled-identity A
+(one value per channel, the Mamba-2 form).  ``oracle.producer`` is the fp64 (numpy) oracle
+of the producer side that computes delta, B and C from x.
 """
 from __future__ import annotations
 
@@ -136,3 +137,28 @@ def step(h, x_t, delta_t, A, B_t, C_t):
     if rc != 0:
         raise RuntimeError(f"oracle_step_f64 failed ({rc})")
     return y, h
+
+
+# ---- scaled-identity A (the Mamba-2 form) ------------------------------------------------
+# The lesson page ("Jamba - Hybrid SSM-Transformer", section "Mamba-3", item 2) says Mamba-2
+# reduced the state matrix to a scaled identity.  Nothing else about the layer is stated to
+# change, so the scan is the same diagonal recurrence with A[d, n] = a[d] for every state n:
+# these functions write out exactly that and run the general recurrence above.
+
+
+def expand_scalar_a(a, N: int = 16) -> np.ndarray:
+    """The scaled identity a[d] * I as the diagonal [D, N]: A[d, n] = a[d]."""
+    a = _f64(a)
+    if a.ndim != 1:
+        raise ValueError("a must be [D]")
+    return np.ascontiguousarray(np.repeat(a[:, None], N, axis=1))
+
+
+def prefill_scalar_a(x, delta, a, B, C, h0=None, nthreads: int = 0):
+    """:func:`prefill` with A[d, n] = a[d]."""
+    return prefill(x, delta, expand_scalar_a(a, np.shape(B)[-1]), B, C, h0, nthreads)
+
+
+def step_scalar_a(h, x_t, delta_t, a, B_t, C_t):
+    """:func:`step` with A[d, n] = a[d]."""
+    return step(h, x_t, delta_t, expand_scalar_a(a, np.shape(B_t)[-1]), B_t, C_t)

@@ -279,6 +279,57 @@ def pin_state_shape(impl, seed=12):
         assert y.shape == (2, L, 3) and h.shape == (2, 3, 16), "state shape depends on L"
 
 
+# --------------------------------------------------------------------------------------
+# P12: scaled-identity A (A[d, n] = a[d], the Mamba-2 form of the lesson page's "Mamba-3"
+# section).  Every state of a channel then shares the decay, and the product of decays from
+# token s+1 to t is exp(a_d (S_t - S_s)) with S_t the running sum of Delta.  Summing the
+# unrolled state over n gives y as a masked matrix product over token pairs, with no state
+# at all:
+#   y_t[d] = sum_{s<=t} exp(a_d (S_t - S_s)) Delta_s x_s <C_t, B_s>  +  exp(a_d S_t) <C_t, h0[d]>
+#   h_T[d, n] = sum_s exp(a_d (S_T - S_s)) Delta_s x_s B_s[n]  +  exp(a_d S_T) h0[d, n]
+# This is a different algorithm from the recurrence (pairs of tokens, not a walk in time).
+# --------------------------------------------------------------------------------------
+def scalar_a_dual_form(x, delta, a, B, C, h0):
+    batch, L, D = x.shape
+    S = np.cumsum(delta, axis=1)                       # inclusive running sums [b, L, D]
+    G = np.einsum("btn,bsn->bts", C, B)                # <C_t, B_s>             [b, L, L]
+    u = delta * x
+    lower = np.tril(np.ones((L, L), dtype=bool))
+    y = np.empty((batch, L, D))
+    hT = np.empty((batch, D, B.shape[2]))
+    for b in range(batch):
+        for d in range(D):
+            gap = S[b, :, d][:, None] - S[b, :, d][None, :]                # S_t - S_s
+            M = np.exp(np.where(lower, a[d] * gap, -np.inf))              # 0 above the diagonal
+            y[b, :, d] = (M * G[b]) @ u[b, :, d] + np.exp(a[d] * S[b, :, d]) * (C[b] @ h0[b, d])
+            carry = np.exp(a[d] * (S[b, -1, d] - S[b, :, d]))            # [L]
+            hT[b, d] = (carry * u[b, :, d]) @ B[b] + np.exp(a[d] * S[b, -1, d]) * h0[b, d]
+    return y, hT
+
+
+def pin_scalar_a_dual_form(impl, seed=13):
+    if not hasattr(impl, "prefill_scalar_a"):
+        return
+    r = _rng(seed)
+    batch, L, D, N = 2, 48, 16, 16            # D == N, so a transposed expansion still runs
+    x = r.standard_normal((batch, L, D))
+    delta = np.logaddexp(0.0, r.standard_normal((batch, L, D)) - 2.0)
+    a = -r.integers(1, N + 1, size=D) * r.uniform(0.5, 1.5, size=D)
+    B = r.standard_normal((batch, L, N))
+    C = r.standard_normal((batch, L, N))
+    h0 = r.normal(0.0, 0.5, size=(batch, D, N))
+    y, h = impl.prefill_scalar_a(x, delta, a, B, C, h0)
+    y_ref, h_ref = scalar_a_dual_form(x, delta, a, B, C, h0)
+    assert _rel(y, y_ref) < 1e-12, f"scaled-identity y differs from the dual form {_rel(y, y_ref)}"
+    assert _rel(h, h_ref) < 1e-12, f"scaled-identity h differs from the dual form {_rel(h, h_ref)}"
+    if hasattr(impl, "step_scalar_a"):
+        hs = h0.copy()
+        for t in range(L):
+            yt, hs = impl.step_scalar_a(hs, x[:, t], delta[:, t], a, B[:, t], C[:, t])
+            assert np.array_equal(yt, y[:, t]), f"scaled-identity step y differs at token {t}"
+        assert np.array_equal(hs, h), "scaled-identity step chain differs from prefill"
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_mpmath,
@@ -292,6 +343,7 @@ ALL_PINS = [
     pin_channel_permutation,
     pin_zero_delta,
     pin_state_shape,
+    pin_scalar_a_dual_form,
 ]
 
 

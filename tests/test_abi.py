@@ -27,7 +27,8 @@ def test_header_symbols_are_exported():
     names = header_symbols()
     assert {"jscan_prefill", "jscan_prefill_resume", "jscan_step", "jscan_status_string",
             "jscan_last_hip_error", "jscan_version", "jscan_prefill_chunked",
-            "jscan_prefill_chunked_workspace", "jscan_ssm_inputs", "jscan_prefill_fused"} <= set(names)
+            "jscan_prefill_chunked_workspace", "jscan_ssm_inputs", "jscan_prefill_fused", "jscan_prefill_scalar_a",
+            "jscan_step_scalar_a"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -37,7 +38,7 @@ def test_status_strings_and_version():
     for s in range(8):
         assert lib.jscan_status_string(s) and lib.jscan_status_string(s) != b"unknown status"
     assert lib.jscan_status_string(99) == b"unknown status"
-    assert lib.jscan_version() == 103
+    assert lib.jscan_version() == 104
     assert lib.jscan_last_hip_error() == 0
 
 
@@ -93,6 +94,39 @@ def test_resume_aliasing_rules():
 ])
 def test_step_validation(kw, code):
     assert step(**kw) == code
+
+
+def prefill_sa(x=P, d=P + 0x100000, a=P + 0x200000, B=P + 0x300000, C=P + 0x400000, h0=None, y=P + 0x500000,
+               h=P + 0x600000, batch=1, L=64, D=64, N=16, dtype=BF16):
+    return jscan.library().jscan_prefill_scalar_a(x, d, a, B, C, h0, y, h, batch, L, D, N, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), EDTYPE), (dict(N=8), ESHAPE), (dict(D=60), ESHAPE), (dict(a=None), ENULL), (dict(x=None), ENULL),
+    (dict(a=P + 0x200004), EALIGN), (dict(y=P + 0x200000), EALIAS),
+    (dict(h=P + 0x200000 + 64 * 4 - 16), EALIAS),      # a is [D] fp32: its last 16 bytes
+    (dict(h0=P + 0x500000), EALIAS), (dict(h0=P + 0x600000 + 16), EALIAS),
+])
+def test_prefill_scalar_a_validation(kw, code):
+    assert prefill_sa(**kw) == code
+
+
+def test_prefill_scalar_a_zero_sized_is_a_no_op():
+    assert prefill_sa(batch=0, x=None, y=None, h=None, a=None) == OK
+
+
+def step_sa(h=P, x=P + 0x100000, d=P + 0x200000, a=P + 0x300000, B=P + 0x400000, C=P + 0x500000,
+            y=P + 0x600000, batch=2, D=64, N=16, ld_xd=64, ld_bc=16, dtype=BF16):
+    return jscan.library().jscan_step_scalar_a(h, x, d, a, B, C, y, batch, D, N, ld_xd, ld_bc, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), EDTYPE), (dict(N=17), ESHAPE), (dict(D=12), ESHAPE), (dict(ld_xd=32), ESHAPE),
+    (dict(a=None), ENULL), (dict(a=P + 0x300008), EALIGN), (dict(y=P + 0x300000), EALIAS),
+    (dict(y=P + 0x300000 + 64 * 4 - 16 - 2 * 64 * 2), EALIAS),   # the second y row reaches into a
+])
+def test_step_scalar_a_validation(kw, code):
+    assert step_sa(**kw) == code
 
 
 WS = P + 0x700000  # fake workspace address

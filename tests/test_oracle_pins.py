@@ -11,6 +11,8 @@ import pins
 class _Oracle:
     prefill = staticmethod(oracle.prefill)
     step = staticmethod(oracle.step)
+    prefill_scalar_a = staticmethod(oracle.prefill_scalar_a)
+    step_scalar_a = staticmethod(oracle.step_scalar_a)
 
     @staticmethod
     def prefill_chunked(x, delta, A, B, C, chunk, h0=None):

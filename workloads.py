@@ -17,6 +17,9 @@ Distributions (the same for every workload):
     delta   = softplus(z - 2),  z ~ N(0, 1)        evaluated in fp64, mean ~0.18
     A[d, n] = -(n + 1)                             tiny workload (exact)
     A[d, n] = -(n + 1) * U(0.5, 1.5)               other workloads, one draw per (d, n)
+    a[d]    = -(d % 16 + 1)                         scaled-identity A, tiny workload (exact)
+    a[d]    = -(k_d + 1) * U(0.5, 1.5), k_d ~ U{0..15}   scaled-identity A, other workloads:
+                                                    the channels' decays span the diagonal A's range
     h0      ~ N(0, 0.1)  (0.1 = standard deviation) decode workload's resident state
 bf16 workloads round every drawn value to bf16 by round-to-nearest-even (torch ``.to``).
 
@@ -39,6 +42,7 @@ BLOCK = 4096  # tokens per seeded block
 # tensor ids inside the seed
 T_X, T_Z, T_B, T_C, T_A, T_H0 = 0, 1, 2, 3, 4, 5
 T_WX, T_GAIN, T_WDT, T_BDT = 6, 7, 8, 9     # producer-side weights
+T_ASC = 10                                  # scaled-identity A
 
 
 @dataclasses.dataclass(frozen=True)
@@ -144,6 +148,18 @@ def draw_A(wl: Workload, seed: int = 0, layer: int = 0) -> torch.Tensor:
     else:
         u = _rng(seed, wl.wid, T_A, layer, 0).uniform(0.5, 1.5, size=(wl.D, wl.N))
         a = -n1 * u
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+
+
+def draw_scalar_a(wl: Workload, seed: int = 0, layer: int = 0) -> torch.Tensor:
+    """[D] fp32 scaled-identity A (A[d, n] = a[d] for every n; every entry < 0)."""
+    wl = get(wl)
+    if not wl.a_scaled:
+        a = -(np.arange(wl.D) % wl.N + 1).astype(np.float64)
+    else:
+        rng = _rng(seed, wl.wid, T_ASC, layer, 0)
+        k = rng.integers(0, wl.N, size=wl.D)
+        a = -(k + 1) * rng.uniform(0.5, 1.5, size=wl.D)
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
 
 
