@@ -47,7 +47,7 @@ PEAK_STATE_ELEMS = VALU_SLOTS_PER_S / SLOTS_PER_STATE_ELEM
 SCALAR_A_SLOTS = 3 + 3 / 16                   # mul, fma, fma; decay (mul + exp) once per 16 states
 SCALAR_A_FLOPS = 5 + 2 / 16
 KERNEL_SOURCES = {
-    "prefill": ["scan_update.h", "project_kernels.h", "prefill_rows_kernel.h"],
+    "prefill": ["scan_update.h", "mfma_common.h", "prefill_rows_kernel.h"],
     "step": ["scan_update.h", "step_kernel.h"],
 }
 

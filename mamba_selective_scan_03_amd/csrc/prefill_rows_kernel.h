@@ -33,7 +33,7 @@
 // leave every state bit-identical (decay 2^0 = 1, input term -0) and their y is not stored.
 #pragma once
 
-#include "project_kernels.h"
+#include "mfma_common.h"
 #include "scan_update.h"
 
 namespace jscan {

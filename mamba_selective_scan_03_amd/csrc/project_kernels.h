@@ -7,38 +7,20 @@
 //     d_low, B, C each RMS-normalised over its own width and scaled by a learned gain
 //     delta_t = softplus(W_dt d_low + b_dt)          (W_dt: D x R, b_dt: D)
 // Both products are dense contractions, so they run on the matrix cores: bf16 operands,
-// fp32 accumulation (v_mfma_f32_16x16x32_bf16), with the normalisation and the softplus
-// applied to the fp32 accumulators before the single rounding to bf16.
-//
-// MFMA 16x16x32 bf16 register layout (lane l of a wave):
-//     A operand: A[row = l % 16][k = 8 * (l / 16) + j], j = 0..7
-//     B operand: B[k = 8 * (l / 16) + j][col = l % 16]
-//     result:    D[row = 4 * (l / 16) + i][col = l % 16], i = 0..3
-// Both operands are 16-byte loads when their k index is contiguous in memory, so every matrix
-// here is stored with k fastest: x is [M][D], W_x is [R + 2N][D], d_low is [M][R] and W_dt is
-// [D][R] (the [out][in] layout of a linear layer).
+// fp32 accumulation (v_mfma_f32_16x16x32_bf16, layout in mfma_common.h), with the
+// normalisation and the softplus applied to the fp32 accumulators before the single rounding
+// to bf16.  Every matrix is stored with k fastest, so both operands are 16-byte loads: x is
+// [M][D], W_x is [R + 2N][D], d_low is [M][R] and W_dt is [D][R] (the [out][in] layout of a
+// linear layer).
 #pragma once
 
-#include "scan_update.h"
+#include "mfma_common.h"
 
 namespace jscan {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));   // 16 raw bytes in registers
 
 namespace proj {
 constexpr int kRowsX = 128;   // x-projection rows (tokens) per work-group: 4 waves x 32
 constexpr int kTileDt = 128;  // delta-projection tile: 128 channels x 128 tokens, 4 waves of 64 x 64
-}
-
-// 8 consecutive bf16 (16 bytes) as an MFMA operand.
-__device__ __forceinline__ bf16x8_t load_frag(const uint16_t *p) {
-    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(p));
-}
-
-__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // Sum over the 16 lanes of a DPP row (lanes 16q .. 16q+15); every lane gets the total.
@@ -49,16 +31,6 @@ __device__ __forceinline__ float row16_sum(float v) {
     v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x101F));   // xor 4
     v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x201F));   // xor 8
     return v;
-}
-
-// softplus(z) = log(1 + e^z) = max(z, 0) + log1p(e^-|z|), with t = e^-|z| in (0, 1].
-// log1p(t) is the hardware log2 of 1 + t, except below t = 2^-10, where 1 + t would lose t's
-// low bits and log1p(t) = t (1 - t/2 + ...) is t to within t/2 <= 2^-11 relative, below the
-// bf16 precision (2^-8) the result is stored with.
-__device__ __forceinline__ float softplus_f32(float z) {
-    const float t = __builtin_amdgcn_exp2f(-fabsf(z) * kLog2e);
-    const float l = t < 0x1.0p-10f ? t : __builtin_amdgcn_logf(1.0f + t) * 0.69314718055994530942f;
-    return fmaxf(z, 0.0f) + l;
 }
 
 // x projection: one work-group = 128 rows (tokens) x all R + 2N output columns; wave w owns
