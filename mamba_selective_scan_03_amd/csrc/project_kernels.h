@@ -33,35 +33,49 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
-// x projection: one work-group = 128 rows (tokens) x all R + 2N output columns; wave w owns
-// rows 32w .. 32w+31 as two 16-row tiles.  RT = R / 16 column tiles of d_low, then one tile
-// each of B and C (N = 16).  K (= D) goes in stages of 64: each stage's x tile [128][64] and
-// W_x tile [16 CT][64] are loaded by all 256 threads into registers two stages ahead, then
-// written to LDS (double-buffered) for the waves' MFMA operand reads.  LDS rows are padded to
-// 72 bf16 (144 bytes), so the 16 rows one operand read touches fall on distinct banks.
+// x projection: one work-group = 128 rows (tokens) x all R + 2N output columns, eight waves in
+// a 4 x 2 grid: wave (wr, wc) owns rows 32 wr .. 32 wr + 31 (two 16-row tiles) and the half
+// wc of the CT = R / 16 + 2 column tiles (d_low's R / 16 tiles, then one each of B and C).
+// K (= D) goes in stages of 64: each stage's x tile [128][64] and W_x tile [16 CT][64] are
+// loaded by all 512 threads into registers two stages ahead, then written to LDS (double-
+// buffered) for the waves' MFMA operand reads.  LDS rows are padded to 72 bf16 (144 bytes),
+// so the 16 rows one operand read touches fall on distinct banks.  Two waves per SIMD, and a
+// register budget that keeps the accumulators in place, let one wave's operand reads and
+// MFMAs overlap the other's.
 namespace proj {
 constexpr int kStageK = 64;          // K per stage
 constexpr int kLdsRow = 72;          // bf16 per LDS row (64 + 8 padding)
+constexpr int kXThreads = 512;       // threads of an x-projection work-group
 }
 
 // (ext_vector_type, not HIP's uint4 struct: copies of the struct type become memcpys that
 // keep the whole set in scratch memory)
 template <int CT> struct XprojRegs {
-    u32x4_t xr[4];          // x: 128 rows x 8 chunks of 16 bytes = 1024 chunks, 4 per thread
-    u32x4_t wr[CT / 2];     // W_x: 16 CT rows x 8 chunks = 128 CT chunks, CT / 2 per thread
+    static constexpr int kW = (16 * CT * 8 + proj::kXThreads - 1) / proj::kXThreads;
+    u32x4_t xr[2];          // x: 128 rows x 8 chunks of 16 bytes = 1024 chunks, 2 per thread
+    u32x4_t wr[kW];         // W_x: 16 CT rows x 8 chunks; the last one only in some waves
 };
+
+// Whether W_x chunk tid + 512 j exists.  16 CT * 8 chunks is a multiple of 64, so the answer is
+// the same for a whole wave; it is taken from the wave's first lane to make that visible.
+template <int CT>
+__device__ __forceinline__ bool xproj_w_chunk(int j, int tid) {
+    return __builtin_amdgcn_readfirstlane(tid) + proj::kXThreads * j < 16 * CT * 8;
+}
 
 template <int CT>
 __device__ __forceinline__ void xproj_load(XprojRegs<CT> &g, const uint16_t *x, const uint16_t *w, int64_t row_base,
                                            int64_t M, int D, int k0, int tid) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int i = tid + 256 * j, r = i >> 3, part = i & 7;
+    for (int j = 0; j < 2; ++j) {
+        const int i = tid + proj::kXThreads * j, r = i >> 3, part = i & 7;
         g.xr[j] = *reinterpret_cast<const u32x4_t *>(x + min(row_base + r, M - 1) * D + k0 + 8 * part);
     }
+    // every lane loads (a missing chunk re-reads the last one): a load under a branch would be
+    // waited for where the branch ends
 #pragma unroll
-    for (int j = 0; j < CT / 2; ++j) {
-        const int i = tid + 256 * j, r = i >> 3, part = i & 7;
+    for (int j = 0; j < XprojRegs<CT>::kW; ++j) {
+        const int i = min(tid + proj::kXThreads * j, 16 * CT * 8 - 1), r = i >> 3, part = i & 7;
         g.wr[j] = *reinterpret_cast<const u32x4_t *>(w + (int64_t)r * D + k0 + 8 * part);
     }
 }
@@ -69,59 +83,68 @@ __device__ __forceinline__ void xproj_load(XprojRegs<CT> &g, const uint16_t *x, 
 template <int CT>
 __device__ __forceinline__ void xproj_store(const XprojRegs<CT> &g, uint16_t *xs, uint16_t *ws, int tid) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int i = tid + 256 * j, r = i >> 3, part = i & 7;
+    for (int j = 0; j < 2; ++j) {
+        const int i = tid + proj::kXThreads * j, r = i >> 3, part = i & 7;
         *reinterpret_cast<u32x4_t *>(xs + r * proj::kLdsRow + 8 * part) = g.xr[j];
     }
 #pragma unroll
-    for (int j = 0; j < CT / 2; ++j) {
-        const int i = tid + 256 * j, r = i >> 3, part = i & 7;
+    for (int j = 0; j < XprojRegs<CT>::kW; ++j) {
+        if (!xproj_w_chunk<CT>(j, tid)) continue;
+        const int i = tid + proj::kXThreads * j, r = i >> 3, part = i & 7;
         *reinterpret_cast<u32x4_t *>(ws + r * proj::kLdsRow + 8 * part) = g.wr[j];
     }
 }
 
-// One stage's MFMAs of one wave: its 32 rows (two 16-row tiles) against all CT column tiles,
-// two 32-wide k steps, operands read from LDS.
-template <int CT>
-__device__ __forceinline__ void xproj_mfma(f32x4_t (&acc)[2][CT], const uint16_t *xs, const uint16_t *ws, int wave,
-                                           int r16, int kq) {
-    const uint16_t *xw = xs + (wave * 32 + r16) * proj::kLdsRow + kq;
-    const uint16_t *wb = ws + r16 * proj::kLdsRow + kq;
+// One stage's MFMAs of one wave: its 32 rows (two 16-row tiles) against its CH column tiles
+// (from tile c0), two 32-wide k steps, operands read from LDS.  All of the stage's operands
+// are requested before the first MFMA, so their LDS latency overlaps the matrix work.
+template <int CH>
+__device__ __forceinline__ void xproj_mfma(f32x4_t (&acc)[2][CH], const uint16_t *xs, const uint16_t *ws, int wr,
+                                           int c0, int r16, int kq) {
+    const uint16_t *xw = xs + (wr * 32 + r16) * proj::kLdsRow + kq;
+    const uint16_t *wb = ws + (16 * c0 + r16) * proj::kLdsRow + kq;
+    bf16x8_t a[2][2], b[2][CH];
 #pragma unroll
-    for (int kk = 0; kk < proj::kStageK; kk += 32) {
-        const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(xw + kk));
-        const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(xw + 16 * proj::kLdsRow + kk));
+    for (int k = 0; k < 2; ++k) {
+        a[k][0] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(xw + 32 * k));
+        a[k][1] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(xw + 16 * proj::kLdsRow + 32 * k));
 #pragma unroll
-        for (int c = 0; c < CT; ++c) {
-            const bf16x8_t b =
-                __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(wb + 16 * c * proj::kLdsRow + kk));
-            acc[0][c] = mfma16(a0, b, acc[0][c]);
-            acc[1][c] = mfma16(a1, b, acc[1][c]);
-        }
+        for (int c = 0; c < CH; ++c)
+            b[k][c] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(wb + 16 * c * proj::kLdsRow + 32 * k));
     }
+    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the MFMAs
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            acc[0][c] = mfma16(a[k][0], b[k][c], acc[0][c]);
+            acc[1][c] = mfma16(a[k][1], b[k][c], acc[1][c]);
+        }
 }
 
 template <int RT>
-__global__ __launch_bounds__(256) void xproj_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
-                                                    const float *__restrict__ g_d, const float *__restrict__ g_b,
-                                                    const float *__restrict__ g_c, uint16_t *__restrict__ d_low,
-                                                    uint16_t *__restrict__ Bo, uint16_t *__restrict__ Co, int64_t M,
-                                                    int D, float eps) {
+__global__ __launch_bounds__(proj::kXThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void xproj_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ g_d,
+    const float *__restrict__ g_b, const float *__restrict__ g_c, uint16_t *__restrict__ d_low,
+    uint16_t *__restrict__ Bo, uint16_t *__restrict__ Co, int64_t M, int D, float eps) {
     constexpr int CT = RT + 2;   // column tiles
+    constexpr int CH = CT / 2;   // column tiles per wave
+    static_assert(CT % 2 == 0 && CH <= RT, "each wave half must hold d_low tiles only or d_low then B and C");
     constexpr int kXs = proj::kRowsX * proj::kLdsRow, kWs = 16 * CT * proj::kLdsRow;
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][kXs];
     __shared__ __attribute__((aligned(16))) uint16_t ws[2][kWs];
-    const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+    __shared__ float ssq[2][proj::kRowsX];   // d_low sums of squares of each column half, per row
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+    const int wr = wave & 3, wc = wave >> 2, c0 = CH * wc;
     const int64_t row_base = (int64_t)blockIdx.x * proj::kRowsX;
-    const int64_t row0 = row_base + wave * 32;
     const int r16 = l & 15, kq = 8 * (l >> 4);
     const int stages = D / proj::kStageK;
 
-    f32x4_t acc[2][CT];
+    f32x4_t acc[2][CH];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int c = 0; c < CT; ++c) acc[t][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < CH; ++c) acc[t][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // Two named register sets (not an array) so that nothing is indexed at run time.
     XprojRegs<CT> Ga, Gb;
@@ -134,14 +157,14 @@ __global__ __launch_bounds__(256) void xproj_kernel(const uint16_t *__restrict__
     // Stage s: MFMAs from LDS buffer s & 1; stage s+1 (in registers since stage s-2) goes to the
     // other buffer, and stage s+3 is requested into the registers it leaves.
     for (int s = 0; s < stages; s += 2) {
-        xproj_mfma<CT>(acc, xs[0], ws[0], wave, r16, kq);
+        xproj_mfma<CH>(acc, xs[0], ws[0], wr, c0, r16, kq);
         if (s + 1 < stages) {
             xproj_store<CT>(Gb, xs[1], ws[1], tid);
             if (s + 3 < stages) xproj_load<CT>(Gb, x, w, row_base, M, D, (s + 3) * proj::kStageK, tid);
         }
         __syncthreads();
         if (s + 1 < stages) {
-            xproj_mfma<CT>(acc, xs[1], ws[1], wave, r16, kq);
+            xproj_mfma<CH>(acc, xs[1], ws[1], wr, c0, r16, kq);
             if (s + 2 < stages) {
                 xproj_store<CT>(Ga, xs[0], ws[0], tid);
                 if (s + 4 < stages) xproj_load<CT>(Ga, x, w, row_base, M, D, (s + 4) * proj::kStageK, tid);
@@ -151,28 +174,54 @@ __global__ __launch_bounds__(256) void xproj_kernel(const uint16_t *__restrict__
     }
 
     // Epilogue.  Lane l holds rows 4 * (l / 16) + i of each 16-row tile, column 16 c + l % 16.
-    // The sums of squares over a row are per-lane partial sums over the lane's columns, then
-    // a sum over the 16 lanes of the DPP row.
+    // A row's sum of squares over d_low is a per-lane sum over the lane's d_low columns, then a
+    // sum over the 16 lanes of the DPP row, then the two column halves' sums added through LDS
+    // (half 0 + half 1, the same order in both waves).  B and C lie in half 1.
+    constexpr int kDl1 = RT - CH;   // d_low tiles in half 1
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t row = row0 + 16 * t + 4 * (l >> 4) + i;
             float sd = 0.f;
+            if (wc == 0) {
 #pragma unroll
-            for (int c = 0; c < RT; ++c) sd = __builtin_fmaf(acc[t][c][i], acc[t][c][i], sd);
-            const float vb = acc[t][RT][i], vc = acc[t][RT + 1][i];
+                for (int c = 0; c < CH; ++c) sd = __builtin_fmaf(acc[t][c][i], acc[t][c][i], sd);
+            } else {
+#pragma unroll
+                for (int c = 0; c < kDl1; ++c) sd = __builtin_fmaf(acc[t][c][i], acc[t][c][i], sd);
+            }
             sd = row16_sum(sd);
-            const float sb = row16_sum(vb * vb), sc = row16_sum(vc * vc);
-            const float nd = __builtin_amdgcn_rsqf(sd * (1.0f / (16 * RT)) + eps);
-            const float nb = __builtin_amdgcn_rsqf(sb * (1.0f / 16) + eps);
-            const float nc = __builtin_amdgcn_rsqf(sc * (1.0f / 16) + eps);
-            if (row < M) {
+            if (r16 == 0) ssq[wc][wr * 32 + 16 * t + 4 * (l >> 4) + i] = sd;
+        }
+    }
+    __syncthreads();
 #pragma unroll
-                for (int c = 0; c < RT; ++c)
-                    d_low[row * (16 * RT) + 16 * c + r16] = f32_to_bf16_bits(acc[t][c][i] * nd * g_d[16 * c + r16]);
-                Bo[row * kDState + r16] = f32_to_bf16_bits(vb * nb * g_b[r16]);
-                Co[row * kDState + r16] = f32_to_bf16_bits(vc * nc * g_c[r16]);
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rr = wr * 32 + 16 * t + 4 * (l >> 4) + i;
+            const int64_t row = row_base + rr;
+            const float sd = ssq[0][rr] + ssq[1][rr];
+            const float nd = __builtin_amdgcn_rsqf(sd * (1.0f / (16 * RT)) + eps);
+            if (wc == 0) {
+                if (row < M) {
+#pragma unroll
+                    for (int c = 0; c < CH; ++c)
+                        d_low[row * (16 * RT) + 16 * c + r16] = f32_to_bf16_bits(acc[t][c][i] * nd * g_d[16 * c + r16]);
+                }
+            } else {
+                const float vb = acc[t][kDl1][i], vc = acc[t][kDl1 + 1][i];
+                const float sb = row16_sum(vb * vb), sc = row16_sum(vc * vc);
+                const float nb = __builtin_amdgcn_rsqf(sb * (1.0f / 16) + eps);
+                const float nc = __builtin_amdgcn_rsqf(sc * (1.0f / 16) + eps);
+                if (row < M) {
+#pragma unroll
+                    for (int c = 0; c < kDl1; ++c)
+                        d_low[row * (16 * RT) + 16 * (CH + c) + r16] =
+                            f32_to_bf16_bits(acc[t][c][i] * nd * g_d[16 * (CH + c) + r16]);
+                    Bo[row * kDState + r16] = f32_to_bf16_bits(vb * nb * g_b[r16]);
+                    Co[row * kDState + r16] = f32_to_bf16_bits(vc * nc * g_c[r16]);
+                }
             }
         }
     }
