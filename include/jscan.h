@@ -180,9 +180,8 @@ jscan_status jscan_ssm_inputs(const void *x, const void *w_x, const float *g_del
  *   x          [batch][L][D] bf16      delta_low [batch][L][R] bf16 (from jscan_ssm_inputs)
  *   w_dt       [D][R] bf16             b_dt [D] fp32
  *   A, B, C, h0 (may be NULL), y, h_final as for jscan_prefill_resume
- * Limits: bf16 only, R = 256, D a multiple of 32 and batch * D <= 65536 (the long-sequence
- * shapes of the row-mapped prefill); other shapes return JSCAN_ERR_SHAPE and are served by
- * jscan_ssm_inputs then jscan_prefill.
+ * Limits: bf16 only, R = 256, D a multiple of 32 (the shapes of the row-mapped prefill);
+ * other shapes return JSCAN_ERR_SHAPE and are served by jscan_ssm_inputs then jscan_prefill.
  */
 jscan_status jscan_prefill_fused(const void *x, const void *delta_low, const void *w_dt,
                                  const float *b_dt, const float *A, const void *B, const void *C,

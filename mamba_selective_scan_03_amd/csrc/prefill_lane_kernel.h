@@ -1,12 +1,11 @@
 // prefill_lane_kernel.h - the general prefill: one lane per (batch row, channel), all 16
 // states of the channel in registers, tokens walked one after the other.
 //
-// It handles every shape the ABI accepts.  A workgroup is one wave of 64 consecutive
-// channels of one batch row, so the token's B_t and C_t rows are the same for the whole
-// wave and are fetched once per wave through the scalar cache; x and delta are read as one
-// coalesced row segment per token.  Its parallelism is batch * D lanes, so it fills the chip
-// only when batch * D is large (for example batched prefill); long single sequences use
-// the row-mapped kernel instead.
+// It handles every shape the ABI accepts and serves those the row-mapped kernel does not
+// (D not a multiple of 32).  A workgroup is one wave of 64 consecutive channels of one batch
+// row, so the token's B_t and C_t rows are the same for the whole wave and are fetched once
+// per wave through the scalar cache; x and delta are read as one coalesced row segment per
+// token.
 #pragma once
 
 #include "scan_update.h"

@@ -554,9 +554,10 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
     }
 }
 
-// The row-mapped kernel needs whole 32-channel blocks; it is the better choice while
-// batch * D is too small for one lane per channel to fill the chip.
-inline bool rows_kernel_applies(int64_t batch, int64_t D) { return D % rows::kCh == 0 && batch * D <= 65536; }
+// The row-mapped kernel needs whole 32-channel blocks.  It serves every batch: even where one
+// lane per channel would fill the chip (batch * D above 65536), the lane kernel runs at a third
+// of its rate per element (its loads of x and delta are single elements, not staged tiles).
+inline bool rows_kernel_applies(int64_t /*batch*/, int64_t D) { return D % rows::kCh == 0; }
 
 // Launches one work-group per 32 channels of each of the `nrows` rows described by sg.
 template <typename E, bool kSummary, bool kFused = false, bool kScalarA = false>

@@ -38,7 +38,7 @@ def test_tiny_fp32_workload():
     (2, 300, 1024, "bf16"),      # batch > 1 through the rows kernel
     (1, 130, 72, "bf16"),        # D not a multiple of 32: lane kernel
     (3, 77, 8, "f32"),           # smallest D, lane kernel
-    (17, 40, 4096, "bf16"),      # batch * D above the rows-kernel limit: lane kernel
+    (17, 40, 4096, "bf16"),      # batch * D above 65536: still the rows kernel
 ])
 def test_prefill_shapes(batch, L, D, dtype):
     run_case(workloads.small_prefill(batch, L, D, dtype), f"{batch}x{L}x{D} {dtype}")
@@ -166,3 +166,18 @@ def test_api_errors_raise():
     with pytest.raises(jscan.JScanError) as ei:
         jscan.prefill(d["x"], d["delta"], d["A"], d["B"], d["C"], y=d["x"])   # y aliases x
     assert ei.value.status == 5
+
+
+def test_batched_prefill_sampled_parity():
+    """Sixteen 4K-token prompts at D = 8192 (a batched prefill: 131072 channels, run by the
+    row-mapped kernel) against the oracle on sampled channels of every sequence."""
+    inp = workloads.small_prefill(16, 4096, 8192, "bf16", seed=21)
+    d = to_dev(inp)
+    y, h = jscan.prefill(d["x"], d["delta"], d["A"], d["B"], d["C"])
+    torch.cuda.synchronize()
+    chans = [0, 31, 32, 4097, 8191]
+    y_ref, h_ref = oracle.prefill(inp["x"][:, :, chans], inp["delta"][:, :, chans], inp["A"][chans], inp["B"],
+                                  inp["C"])
+    idx = torch.tensor(chans, device="cuda")
+    assert_parity(f64(y.index_select(2, idx)), y_ref, torch.bfloat16, "16x4096x8192 y (sampled channels)")
+    assert_parity(f64(h.index_select(1, idx)), h_ref, torch.bfloat16, "16x4096x8192 h_final (sampled channels)")

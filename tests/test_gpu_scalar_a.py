@@ -36,7 +36,8 @@ def expanded(a):
     (1, 63, 128, "bf16", True),      # shorter than one tile
     (1, 1, 64, "bf16", False),       # one token
     (2, 777, 40, "f32", False),      # D not a multiple of 32: lane kernel
-    (9, 70, 8192, "bf16", True),     # batch * D above the row-mapped limit: lane kernel
+    (9, 70, 8192, "bf16", True),     # batch * D above 65536 (row-mapped kernel, many rows)
+    (3, 100, 200, "bf16", True),     # D not a multiple of 32 (lane kernel), bf16
 ])
 def test_bit_identical_to_general_path(batch, L, D, dtype, with_h0):
     inp = to_dev(scalar_case(batch, L, D, dtype, seed=L))
