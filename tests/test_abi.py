@@ -185,7 +185,7 @@ def fused(x=P, dlow=P + 0x100000, wdt=P + 0x200000, bdt=P + 0x300000, A=P + 0x31
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=F32), EDTYPE), (dict(R=128), ESHAPE), (dict(D=72), ESHAPE), (dict(batch=3, L=1, D=32768, h=P + 0x10000000, A=P + 0x20000000), ESHAPE),
+    (dict(dtype=F32), EDTYPE), (dict(R=128), ESHAPE), (dict(D=72), ESHAPE), (dict(D=40), ESHAPE),
     (dict(dlow=None), ENULL), (dict(wdt=None), ENULL), (dict(bdt=P + 0x300004), EALIGN),
     (dict(y=P + 0x100000), EALIAS), (dict(h=P + 0x200000 + 64), EALIAS), (dict(x=None), ENULL),
 ])
