@@ -120,7 +120,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill_64k",
                     choices=["prefill_64k", "prefill_4k", "prefill_256k", "decode_256x28", "tiny_fp32",
-                             "prefill_64k_tp8"])
+                             "prefill_64k_tp8", "prefill_16x4k"])
     ap.add_argument("--producer", action="store_true",
                     help="prefill workloads: compute delta, B and C from x with jscan_ssm_inputs (synthetic weights, "
                          "rank 256) inside each step, then scan")

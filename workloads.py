@@ -10,7 +10,8 @@ Language Model", section "Mamba layer"); 28 of the 32 layers are Mamba layers (l
 "Jamba - Hybrid SSM-Transformer", section "memory budget").  The prompt lengths (4K, 64K,
 256K) span the pages' long-context range (notes page, throughput table; 256K context on
 one 80 GB GPU).  prefill_64k_tp8 is the 64K prompt with d_inner split 8 ways, the share of
-one GPU under channel (tensor) parallelism.
+one GPU under channel (tensor) parallelism; prefill_16x4k is a batched prefill of sixteen 4K
+prompts.
 
 Distributions (the same for every workload):
     x, B, C ~ N(0, 1)                              per element
@@ -81,6 +82,8 @@ WORKLOADS = {
         # one GPU's share of the 64K prefill when the 8192 channels are split over 8 GPUs
         # (channels are independent, so each GPU scans D = 1024 of them on its own)
         Workload("prefill_64k_tp8", 5, 1, 65536, 1024, 16, "bf16", True),
+        # a batched prefill: sixteen 4K-token prompts at the same width
+        Workload("prefill_16x4k", 6, 16, 4096, 8192, 16, "bf16", True),
     ]
 }
 
