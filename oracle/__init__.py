@@ -17,7 +17,8 @@ SSM-Transformer", section "Mamba-3", item 2).  Shapes: x, delta, y ``[batch, L, 
 A ``[D, N]``; B, C ``[batch, L, N]``; states ``[batch, D, N]``.
 
 ``prefill_scalar_a`` / ``step_scalar_a`` are the same recurrence with a scaled-identity A
-(one value per channel, the Mamba-2 form).  ``oracle.producer`` is the fp64 (numpy) oracle
+(one value per channel, the Mamba-2 form); ``prefill_complex`` / ``step_complex`` run it with a
+complex-valued state (the Mamba-3 change).  ``oracle.producer`` is the fp64 (numpy) oracle
 of the producer side that computes delta, B and C from x.
 """
 from __future__ import annotations
@@ -56,7 +57,10 @@ def _load():
     lib.oracle_prefill_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, ctypes.c_int]
     lib.oracle_prefill_chunked_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, i64, ctypes.c_int]
     lib.oracle_step_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64]
-    for f in (lib.oracle_prefill_f64, lib.oracle_prefill_chunked_f64, lib.oracle_step_f64):
+    lib.oracle_prefill_complex_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, ctypes.c_int]
+    lib.oracle_step_complex_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64]
+    for f in (lib.oracle_prefill_f64, lib.oracle_prefill_chunked_f64, lib.oracle_step_f64,
+              lib.oracle_prefill_complex_f64, lib.oracle_step_complex_f64):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -162,3 +166,46 @@ def prefill_scalar_a(x, delta, a, B, C, h0=None, nthreads: int = 0):
 def step_scalar_a(h, x_t, delta_t, a, B_t, C_t):
     """:func:`step` with A[d, n] = a[d]."""
     return step(h, x_t, delta_t, expand_scalar_a(a, np.shape(B_t)[-1]), B_t, C_t)
+
+
+# ---- complex-valued state (the Mamba-3 change) ----------------------------------------------
+# The lesson page ("Jamba - Hybrid SSM-Transformer", section "Mamba-3", item 2) names a complex
+# state matrix again, equivalent to a data-dependent rotation of the state.  The N real state
+# components of a channel are read as N/2 complex states (h[2k] + i h[2k+1]); A, B and C pair
+# up the same way, A[2k] and A[2k+1] being the real and imaginary parts of the diagonal entry.
+
+
+def prefill_complex(x, delta, A, B, C, h0=None, nthreads: int = 0):
+    """Sequential fp64 scan with the complex-valued state.  Returns ``(y, h_final)`` as float64,
+    h_final in the same paired layout as h0."""
+    lib = _load()
+    x, delta, A, B, C = (_f64(v) for v in (x, delta, A, B, C))
+    h0 = None if h0 is None else _f64(h0)
+    batch, L, D, N = _check_shapes(x, delta, A, B, C, h0)
+    if N % 2:
+        raise ValueError("the complex state needs an even N")
+    y = np.empty((batch, L, D), np.float64)
+    h = np.empty((batch, D, N), np.float64)
+    rc = lib.oracle_prefill_complex_f64(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(h0), _ptr(y),
+                                        _ptr(h), batch, L, D, N, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_prefill_complex_f64 failed ({rc})")
+    return y, h
+
+
+def step_complex(h, x_t, delta_t, A, B_t, C_t):
+    """One decode step with the complex-valued state.  Returns ``(y_t, h_new)``."""
+    lib = _load()
+    h = _f64(h).copy()
+    x_t, delta_t, A, B_t, C_t = (_f64(v) for v in (x_t, delta_t, A, B_t, C_t))
+    batch, D, N = h.shape
+    if x_t.shape != (batch, D) or delta_t.shape != (batch, D) or A.shape != (D, N) or N % 2:
+        raise ValueError("step_complex: x_t, delta_t must be [batch, D] and A [D, N] with N even")
+    if B_t.shape != (batch, N) or C_t.shape != (batch, N):
+        raise ValueError("step_complex: B_t and C_t must be [batch, N]")
+    y = np.empty((batch, D), np.float64)
+    rc = lib.oracle_step_complex_f64(_ptr(h), _ptr(x_t), _ptr(delta_t), _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(y),
+                                     batch, D, N)
+    if rc != 0:
+        raise RuntimeError(f"oracle_step_complex_f64 failed ({rc})")
+    return y, h

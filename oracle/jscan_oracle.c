@@ -28,6 +28,7 @@
  * The time loop is strictly sequential; only independent (b, d) chains are spread over
  * threads, which does not change a single rounding.
  */
+#include <complex.h>
 #include <math.h>
 #include <pthread.h>
 #include <stdint.h>
@@ -39,6 +40,7 @@ typedef struct {
     const double *x, *delta, *A, *B, *C, *h0;
     double *y, *h_final;
     int64_t batch, L, D, N, chunk;
+    int cplx;                     /* complex-valued state (see scan_chain_complex) */
     int64_t item_begin, item_end; /* items are (b, d) pairs, item = b * D + d */
 } scan_job;
 
@@ -118,12 +120,58 @@ static void scan_chain_chunked(const scan_job *j, int64_t b, int64_t d)
     free(q);
 }
 
+/*
+ * Complex-valued state: the Mamba-3 change named on the lesson page ("Jamba - Hybrid
+ * SSM-Transformer", section "Mamba-3", item 2), where the state matrix becomes complex again
+ * and so multiplies the state by a data-dependent rotation.  The N real components of a
+ * channel's state are read as N/2 complex states, h[k] = h[2k] + i h[2k+1].  A holds each
+ * complex diagonal entry as (A[2k], A[2k+1]) = (real part, imaginary part), and B and C pair
+ * up the same way.  The S6 equation then reads, in complex arithmetic,
+ *     Abar_t = exp(Delta_t a_k),  a_k = A[2k] + i A[2k+1]
+ *     h_t[k] = Abar_t h_{t-1}[k] + Delta_t x_t b_k,  b_k = B_t[2k] + i B_t[2k+1]
+ *     y_t    = sum_k Re(conj(c_k) h_t[k]),  c_k = C_t[2k] + i C_t[2k+1]
+ * and the output is the same dot product of C_t with the N real components as in the real
+ * scan.  With every imaginary part of A zero it is the real scan with A[2k+1] = A[2k].
+ */
+static void scan_chain_complex(const scan_job *j, int64_t b, int64_t d)
+{
+    const int64_t L = j->L, D = j->D, N = j->N, K = N / 2;
+    double complex *h = (double complex *)malloc((size_t)K * sizeof(double complex));
+    for (int64_t k = 0; k < K; ++k)
+        h[k] = j->h0 ? j->h0[(b * D + d) * N + 2 * k] + I * j->h0[(b * D + d) * N + 2 * k + 1] : 0.0;
+
+    for (int64_t t = 0; t < L; ++t) {
+        const double delta_t = j->delta[(b * L + t) * D + d];
+        const double x_t = j->x[(b * L + t) * D + d];
+        const double *B_t = j->B + (b * L + t) * N;
+        const double *C_t = j->C + (b * L + t) * N;
+        double y_t = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double complex a = j->A[d * N + 2 * k] + I * j->A[d * N + 2 * k + 1];
+            const double complex Abar = cexp(delta_t * a);
+            const double complex bk = B_t[2 * k] + I * B_t[2 * k + 1];
+            const double complex ck = C_t[2 * k] + I * C_t[2 * k + 1];
+            h[k] = Abar * h[k] + delta_t * x_t * bk;
+            y_t += creal(conj(ck) * h[k]);
+        }
+        j->y[(b * L + t) * D + d] = y_t;
+    }
+    if (j->h_final)
+        for (int64_t k = 0; k < K; ++k) {
+            j->h_final[(b * D + d) * N + 2 * k] = creal(h[k]);
+            j->h_final[(b * D + d) * N + 2 * k + 1] = cimag(h[k]);
+        }
+    free(h);
+}
+
 static void *scan_worker(void *arg)
 {
     const scan_job *j = (const scan_job *)arg;
     for (int64_t item = j->item_begin; item < j->item_end; ++item) {
         const int64_t b = item / j->D, d = item % j->D;
-        if (j->chunk > 0)
+        if (j->cplx)
+            scan_chain_complex(j, b, d);
+        else if (j->chunk > 0)
             scan_chain_chunked(j, b, d);
         else
             scan_chain_sequential(j, b, d);
@@ -210,6 +258,48 @@ int oracle_step_f64(double *h, const double *x_t, const double *delta_t, const d
                 const double Abar = exp(dl * A[d * N + n]);
                 *hn = Abar * *hn + dl * B_t[b * N + n] * xv;
                 acc += C_t[b * N + n] * *hn;
+            }
+            y_t[b * D + d] = acc;
+        }
+    }
+    return 0;
+}
+
+/* Prefill with the complex-valued state (scan_chain_complex); N must be even. */
+int oracle_prefill_complex_f64(const double *x, const double *delta, const double *A, const double *B,
+                               const double *C, const double *h0, double *y, double *h_final,
+                               int64_t batch, int64_t L, int64_t D, int64_t N, int nthreads)
+{
+    if (N % 2 != 0)
+        return -1;
+    scan_job j;
+    memset(&j, 0, sizeof j);
+    j.x = x; j.delta = delta; j.A = A; j.B = B; j.C = C; j.h0 = h0;
+    j.y = y; j.h_final = h_final;
+    j.batch = batch; j.L = L; j.D = D; j.N = N; j.chunk = 0; j.cplx = 1;
+    return run_scan(j, nthreads);
+}
+
+/* One decode step with the complex-valued state; h [batch][D][N] is updated in place. */
+int oracle_step_complex_f64(double *h, const double *x_t, const double *delta_t, const double *A,
+                            const double *B_t, const double *C_t, double *y_t,
+                            int64_t batch, int64_t D, int64_t N)
+{
+    if (N % 2 != 0)
+        return -1;
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < D; ++d) {
+            const double dl = delta_t[b * D + d], xv = x_t[b * D + d];
+            double acc = 0.0;
+            for (int64_t k = 0; k < N / 2; ++k) {
+                double *hk = &h[(b * D + d) * N + 2 * k];
+                const double complex a = A[d * N + 2 * k] + I * A[d * N + 2 * k + 1];
+                const double complex bk = B_t[b * N + 2 * k] + I * B_t[b * N + 2 * k + 1];
+                const double complex ck = C_t[b * N + 2 * k] + I * C_t[b * N + 2 * k + 1];
+                const double complex hn = cexp(dl * a) * (hk[0] + I * hk[1]) + dl * xv * bk;
+                hk[0] = creal(hn);
+                hk[1] = cimag(hn);
+                acc += creal(conj(ck) * hn);
             }
             y_t[b * D + d] = acc;
         }

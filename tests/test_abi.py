@@ -222,3 +222,15 @@ def test_library_does_not_reference_the_oracle():
         assert "oracle" not in open(os.path.join(ROOT, "mamba_selective_scan_03_amd", "csrc", f)).read().lower()
     syms = open(jscan.library_path(), "rb").read()
     assert b"oracle_prefill" not in syms
+
+
+def test_last_hip_error_is_per_thread():
+    """jscan_last_hip_error is thread-local: a thread that made no failing launch reads 0."""
+    import threading
+
+    lib = jscan.library()
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(lib.jscan_last_hip_error()))
+    t.start()
+    t.join()
+    assert seen == [0]
