@@ -21,7 +21,10 @@ it as GB/s and as a fraction of 8 TB/s.
 With --scalar-a (A a scaled identity, one value per channel: the Mamba-2 form) the decay is
 shared by a channel's 16 states, so a state element needs only the input product and two
 fused multiply-adds (3 slots) plus a sixteenth of the decay's product and exponential
-(3/16): 3.1875 slots and 5.125 flops per element, a bound of 63.2 TFLOP/s.
+(3/16): 3.1875 slots and 5.125 flops per element, a bound of 63.2 TFLOP/s.  With --complex-a
+(the complex-valued state of the Mamba-3 form) one complex state, two elements, takes 19
+slots and 21 flops per token (decay, rotation by a hardware sine and cosine, complex update,
+output): 9.5 slots and 10.5 flops per element, a bound of 43.4 TFLOP/s.
 """
 from __future__ import annotations
 
@@ -46,6 +49,10 @@ FLOPS_PER_STATE_ELEM = 7                      # mul 1 + exp 1 + mul 1 + fma 2 + 
 PEAK_STATE_ELEMS = VALU_SLOTS_PER_S / SLOTS_PER_STATE_ELEM
 SCALAR_A_SLOTS = 3 + 3 / 16                   # mul, fma, fma; decay (mul + exp) once per 16 states
 SCALAR_A_FLOPS = 5 + 2 / 16
+# complex state, per real component (half a complex state): decay mul + exp (3), angle mul +
+# fract (2), cos and sin (4), r cos and r sin (2), two input products (2), four fma (4), y (2)
+COMPLEX_A_SLOTS = 19 / 2
+COMPLEX_A_FLOPS = 21 / 2
 KERNEL_SOURCES = {
     "prefill": ["scan_update.h", "mfma_common.h", "prefill_rows_kernel.h"],
     "step": ["scan_update.h", "step_kernel.h"],
@@ -91,9 +98,10 @@ def read_traffic(workload: str, launches_per_step: int):
         return None
 
 
-def cpu_baseline(wl, inp, channels: int, scalar_a=None):
+def cpu_baseline(wl, inp, channels: int, scalar_a=None, complex_a=False):
     """The fp64 oracle, as it stands, on a bounded sample: all tokens of `channels` channels
-    (with `scalar_a`, the scaled-identity oracle on that A)."""
+    (with `scalar_a`, the scaled-identity oracle on that A; with `complex_a`, the complex-state
+    oracle on inp["A"])."""
     import numpy as np
 
     import oracle
@@ -103,7 +111,7 @@ def cpu_baseline(wl, inp, channels: int, scalar_a=None):
     dl = inp["delta"][:, :, :channels]
     A = inp["A"][:channels] if scalar_a is None else scalar_a[:channels]
     args = [np.ascontiguousarray(t.float().numpy(), dtype=np.float64) for t in (x, dl, A, inp["B"], inp["C"])]
-    fn = oracle.prefill if scalar_a is None else oracle.prefill_scalar_a
+    fn = oracle.prefill_complex if complex_a else oracle.prefill if scalar_a is None else oracle.prefill_scalar_a
     t0 = time.perf_counter()
     fn(*args, nthreads=threads)
     dt = time.perf_counter() - t0
@@ -132,6 +140,9 @@ def main():
     ap.add_argument("--scalar-a", action="store_true",
                     help="A is a scaled identity, one value per channel (the Mamba-2 form): "
                          "jscan_prefill_scalar_a / jscan_step_scalar_a")
+    ap.add_argument("--complex-a", action="store_true",
+                    help="complex-valued state, pairs of the 16 states as 8 complex states (the Mamba-3 form): "
+                         "jscan_prefill_complex / jscan_step_complex")
     ap.add_argument("--cpu-channels", type=int, default=8192,
                     help="oracle sample: all tokens of the first CPU_CHANNELS channels (default: every channel "
                          "of the 64K workload, a few seconds on 16 cores; 0 = skip)")
@@ -172,8 +183,11 @@ def main():
                           "ms_per_launch": ms, "GBps": 2 * n * 4 / ms / 1e6}), flush=True)
         return
     wl = workloads.get(args.workload)
-    if args.scalar_a and (args.producer or args.chunked):
-        print("bench.py: --scalar-a runs the plain prefill or decode step only", file=sys.stderr)
+    if (args.scalar_a or args.complex_a) and (args.producer or args.chunked):
+        print("bench.py: --scalar-a and --complex-a run the plain prefill or decode step only", file=sys.stderr)
+        sys.exit(2)
+    if args.scalar_a and args.complex_a:
+        print("bench.py: choose one of --scalar-a and --complex-a", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(dev)
     log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)  # noqa: E731
@@ -185,12 +199,14 @@ def main():
             inp = workloads.decode_layer_inputs(wl, layer)
             if args.scalar_a:
                 inp["A"] = workloads.draw_scalar_a(wl, layer=layer)
+            if args.complex_a:
+                inp["A"] = workloads.draw_complex_a(wl, layer=layer)
             layers.append({k: v.to(dev) for k, v in inp.items()})
             layers[-1]["h"] = layers[-1].pop("h0")
 
         for L_ in layers:
             L_["y"] = torch.empty_like(L_["x"])
-        step_fn = jscan.step_scalar_a if args.scalar_a else jscan.step
+        step_fn = jscan.step_scalar_a if args.scalar_a else jscan.step_complex if args.complex_a else jscan.step
 
         def token_step():
             for L_ in layers:
@@ -254,6 +270,13 @@ def main():
             def one_step():
                 jscan.prefill_chunked(d["x"], d["delta"], d["A"], d["B"], d["C"], y=y, h_final=h, workspace=ws)
             launches = 3 if ws_bytes > 0 else 1
+        elif args.complex_a:
+            host_inp["A"] = workloads.draw_complex_a(wl)
+            d["A"] = host_inp["A"].to(dev)
+
+            def one_step():
+                jscan.prefill_complex(d["x"], d["delta"], d["A"], d["B"], d["C"], y=y, h_final=h)
+            launches = 1
         elif args.scalar_a:
             host_a = workloads.draw_scalar_a(wl)
             d["a"] = host_a.to(dev)
@@ -329,14 +352,15 @@ def main():
         roofline["frac"] = round(roofline["achieved"] / HBM_PEAK_GBPS, 4)
     else:
         state_elems = elems * wl.N
-        slots, flops = (SCALAR_A_SLOTS, SCALAR_A_FLOPS) if args.scalar_a else (SLOTS_PER_STATE_ELEM,
-                                                                              FLOPS_PER_STATE_ELEM)
+        slots, flops = ((SCALAR_A_SLOTS, SCALAR_A_FLOPS) if args.scalar_a else
+                        (COMPLEX_A_SLOTS, COMPLEX_A_FLOPS) if args.complex_a else
+                        (SLOTS_PER_STATE_ELEM, FLOPS_PER_STATE_ELEM))
         achieved_tf = state_elems * flops / (per_launch_ms * 1e-3) / 1e12
         peak_tf = VALU_SLOTS_PER_S / slots * flops / 1e12
         roofline = {"bound": "alu", "achieved": round(achieved_tf, 2), "peak": round(peak_tf, 2), "unit": "TFLOP/s",
                     "frac": round(achieved_tf / peak_tf, 4)}
     roofline["traffic"] = None if (args.chunked or args.producer) else read_traffic(
-        wl.name + ("_scalar_a" if args.scalar_a else ""), launches)
+        wl.name + ("_scalar_a" if args.scalar_a else "_complex_a" if args.complex_a else ""), launches)
 
     out = {
         "metric": METRIC,
@@ -353,7 +377,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "L": wl.L, "D": wl.D, "N": wl.N,
                    "layers": wl.layers, "io_dtype": wl.dtype, "state_dtype": "f32",
-                   "A": "scaled_identity" if args.scalar_a else "diagonal",
+                   "A": "scaled_identity" if args.scalar_a else "complex_pairs" if args.complex_a else "diagonal",
                    "path": ("producer+fused-scan" if args.fused else "producer+scan") if args.producer
                    else ("time-parallel" if args.chunked else "sequential")},
         "hbm_GBps": round(gbps, 1),
@@ -365,7 +389,7 @@ def main():
         out["producer"] = producer_info
     if host_inp is not None and args.cpu_channels > 0 and wl.layers == 1:
         out["cpu_baseline"] = cpu_baseline(wl, host_inp, min(args.cpu_channels, wl.D),
-                                           host_a if args.scalar_a else None)
+                                           host_a if args.scalar_a else None, complex_a=args.complex_a)
         log(f"oracle sample: {out['cpu_baseline']['sample']}")
     print(json.dumps(out), flush=True)
 

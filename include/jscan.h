@@ -231,6 +231,35 @@ jscan_status jscan_step_scalar_a(float *h, const void *x_t, const void *delta_t,
                                  int64_t D, int64_t N, int64_t ld_xd, int64_t ld_bc,
                                  jscan_dtype dtype, void *stream);
 
+/*
+ * Complex-valued state (the Mamba-3 form).  The lesson page ("Jamba - Hybrid SSM-Transformer",
+ * section "Mamba-3", item 2) has Mamba-3 bring back a complex state matrix, which amounts to
+ * multiplying the state by a data-dependent rotation.  Here the 16 real state components of a
+ * channel are read as 8 complex states, h[k] = h[2k] + i h[2k+1], and A[d][2k], A[d][2k+1] as
+ * the real and imaginary parts of its complex diagonal entry a; B and C pair up the same way.
+ * The S6 equation in complex arithmetic then reads
+ *     h_t[k] = exp(delta_t a) h_{t-1}[k] + (delta_t x_t) (B_t[2k] + i B_t[2k+1])
+ *     y_t    = sum_n C_t[n] h_t[n]            (= sum_k Re(conj(c_k) h_t[k]))
+ * with exp(delta a) = 2^(delta Re(a) log2 e) (cos(delta Im a) + i sin(delta Im a)): a decay by
+ * the real part and a rotation by the imaginary part.  With every Im a = 0 this is the real
+ * diagonal scan with A[d][2k+1] = A[d][2k].  Every entry point advances the pairs with the same
+ * fp32 expression (hardware sine and cosine of the angle in turns, reduced to [0, 1)), so the
+ * prefill's final state equals the step chain's bit for bit.  States, h0 and h_final keep the
+ * [batch][D][16] fp32 layout with the pairs interleaved.  Re(a) <= 0 keeps the recurrence
+ * stable; Im(a) is an angle rate in radians per unit of delta.  The other arguments, layouts
+ * and errors are those of jscan_prefill_resume (h0 may be NULL) and jscan_step.
+ */
+jscan_status jscan_prefill_complex(const void *x, const void *delta, const float *A,
+                                   const void *B, const void *C, const float *h0, void *y,
+                                   float *h_final, int64_t batch, int64_t L, int64_t D,
+                                   int64_t N, jscan_dtype dtype, void *stream);
+
+/* Decode step with the complex-valued state (see jscan_prefill_complex). */
+jscan_status jscan_step_complex(float *h, const void *x_t, const void *delta_t, const float *A,
+                                const void *B_t, const void *C_t, void *y_t, int64_t batch,
+                                int64_t D, int64_t N, int64_t ld_xd, int64_t ld_bc,
+                                jscan_dtype dtype, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *jscan_status_string(jscan_status s);
 
@@ -238,7 +267,8 @@ const char *jscan_status_string(jscan_status s);
 int jscan_last_hip_error(void);
 
 /* Library ABI version: 100 * major + minor (101 adds the time-parallel prefill, 102 the
- * producer side, 103 the fused prefill, 104 the scaled-identity A entry points). */
+ * producer side, 103 the fused prefill, 104 the scaled-identity A entry points, 105 the
+ * complex-valued state). */
 int jscan_version(void);
 
 #ifdef __cplusplus

@@ -12,6 +12,8 @@ There is no CPU fallback: without the built library every call raises.
     y, h_final = prefill_fused(x, d_low, w_dt, b_dt, A, B, C)             # delta computed in the scan
     y, h_final = prefill_scalar_a(x, delta, a, B, C)       # scaled-identity A (a: [D])
     y_t = step_scalar_a(h, x_t, delta_t, a, B_t, C_t)
+    y, h_final = prefill_complex(x, delta, A, B, C)        # complex-valued state (pairs of states)
+    y_t = step_complex(h, x_t, delta_t, A, B_t, C_t)
 """
 from ._binding import (  # noqa: F401
     D_STATE,
@@ -21,10 +23,12 @@ from ._binding import (  # noqa: F401
     library_path,
     prefill,
     prefill_chunked,
+    prefill_complex,
     prefill_fused,
     prefill_scalar_a,
     ssm_inputs,
     step,
+    step_complex,
     step_raw,
     step_scalar_a,
 )

@@ -51,9 +51,11 @@ def library():
     lib.jscan_prefill_fused.restype = i32
     lib.jscan_prefill_scalar_a.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, i32, vp]
     lib.jscan_step_scalar_a.argtypes = [fp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+    lib.jscan_prefill_complex.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, i32, vp]
+    lib.jscan_step_complex.argtypes = [fp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
     lib.jscan_prefill_chunked_workspace.restype = i64
     for f in (lib.jscan_prefill, lib.jscan_prefill_resume, lib.jscan_step, lib.jscan_prefill_chunked,
-              lib.jscan_prefill_scalar_a, lib.jscan_step_scalar_a):
+              lib.jscan_prefill_scalar_a, lib.jscan_step_scalar_a, lib.jscan_prefill_complex, lib.jscan_step_complex):
         f.restype = i32
     lib.jscan_status_string.argtypes = [i32]
     lib.jscan_status_string.restype = ctypes.c_char_p
@@ -136,6 +138,23 @@ def prefill_scalar_a(x, delta, a, B, C, h0=None, y=None, h_final=None):
     with torch.cuda.device(x.device):
         st = lib.jscan_prefill_scalar_a(_ptr(x), _ptr(delta), _ptr(a), _ptr(B), _ptr(C), _ptr(h0), _ptr(y),
                                         _ptr(h_final), batch, L, D, D_STATE, _DTYPES[x.dtype], _stream(x.device))
+    _check(st)
+    return y, h_final
+
+
+def prefill_complex(x, delta, A, B, C, h0=None, y=None, h_final=None):
+    """Prefill with the complex-valued state (``jscan_prefill_complex``): states 2k, 2k+1 of a
+    channel are one complex state and ``A[d, 2k], A[d, 2k+1]`` the real and imaginary parts of
+    its diagonal entry.  Arguments and results as for :func:`prefill`."""
+    batch, L, D = _check_prefill_args(x, delta, A, B, C, h0)
+    if y is None:
+        y = torch.empty_like(x)
+    if h_final is None:
+        h_final = torch.empty((batch, D, D_STATE), dtype=torch.float32, device=x.device)
+    lib = library()
+    with torch.cuda.device(x.device):
+        st = lib.jscan_prefill_complex(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(h0), _ptr(y),
+                                       _ptr(h_final), batch, L, D, D_STATE, _DTYPES[x.dtype], _stream(x.device))
     _check(st)
     return y, h_final
 
@@ -233,17 +252,18 @@ def prefill_fused(x, delta_low, w_dt, b_dt, A, B, C, h0=None, y=None, h_final=No
     return y, h_final
 
 
-def step_raw(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, dtype, scalar_a=False):
-    """Direct call of ``jscan_step`` (``jscan_step_scalar_a`` with ``scalar_a``) on raw
-    tensors/pointers with explicit row strides (no checks beyond the library's own).  ``x_t``
-    etc. may be tensors or integer device addresses."""
+def step_raw(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, dtype, scalar_a=False, complex_a=False):
+    """Direct call of ``jscan_step`` (``jscan_step_scalar_a`` with ``scalar_a``,
+    ``jscan_step_complex`` with ``complex_a``) on raw tensors/pointers with explicit row strides
+    (no checks beyond the library's own).  ``x_t`` etc. may be tensors or integer device
+    addresses."""
     lib = library()
 
     def p(v):
         return ctypes.c_void_p(v if isinstance(v, int) else v.data_ptr())
 
     dev = h.device if hasattr(h, "device") else torch.device("cuda")
-    fn = lib.jscan_step_scalar_a if scalar_a else lib.jscan_step
+    fn = lib.jscan_step_scalar_a if scalar_a else lib.jscan_step_complex if complex_a else lib.jscan_step
     st = fn(p(h), p(x_t), p(delta_t), p(A), p(B_t), p(C_t), p(y_t), batch, D, D_STATE, ld_xd, ld_bc, _DTYPES[dtype],
             _stream(dev))
     _check(st)
@@ -254,7 +274,12 @@ def step_scalar_a(h, x_t, delta_t, a, B_t, C_t, y_t=None):
     return step(h, x_t, delta_t, a, B_t, C_t, y_t, _scalar_a=True)
 
 
-def step(h, x_t, delta_t, A, B_t, C_t, y_t=None, _scalar_a=False):
+def step_complex(h, x_t, delta_t, A, B_t, C_t, y_t=None):
+    """:func:`step` with the complex-valued state (``jscan_step_complex``)."""
+    return step(h, x_t, delta_t, A, B_t, C_t, y_t, _complex_a=True)
+
+
+def step(h, x_t, delta_t, A, B_t, C_t, y_t=None, _scalar_a=False, _complex_a=False):
     """One decode token for a batch: h ``[batch, D, 16]`` fp32 is updated in place; x_t, delta_t
     ``[batch, D]`` and B_t, C_t ``[batch, 16]`` (rows may be strided views of prefill tensors,
     e.g. ``x[:, t]``).  Returns y_t ``[batch, D]``."""
@@ -281,5 +306,6 @@ def step(h, x_t, delta_t, A, B_t, C_t, y_t=None, _scalar_a=False):
     _require(tuple(y_t.shape) == (batch, D) and y_t.dtype == x_t.dtype and y_t.stride(1) == 1
              and (batch <= 1 or y_t.stride(0) == ld_xd), "y_t must be [batch, D] with x_t's row stride")
     with torch.cuda.device(h.device):
-        step_raw(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, x_t.dtype, scalar_a=_scalar_a)
+        step_raw(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, x_t.dtype, scalar_a=_scalar_a,
+                 complex_a=_complex_a)
     return y_t

@@ -49,8 +49,8 @@ jscan_status launch_status() {
 constexpr int64_t kMaxBlocks = (int64_t)1 << 30;
 
 // Scans `nrows` rows (see Segments) with the row-mapped kernel when it applies, otherwise
-// with one lane per (row, channel).  kScalarA: A is the scaled identity a[D].
-template <typename E, bool kSummary, bool kScalarA = false>
+// with one lane per (row, channel).  AF: the form of A.
+template <typename E, bool kSummary, jscan::AForm AF = jscan::AForm::Diagonal>
 void launch_rows(const void *x, const void *delta, const float *A, const void *B, const void *C, const float *h0,
                  void *y, float *h_final, float *dsum, const jscan::Segments &sg, int64_t nrows, int64_t D,
                  hipStream_t stream) {
@@ -59,17 +59,17 @@ void launch_rows(const void *x, const void *delta, const float *A, const void *B
     const T *bt = static_cast<const T *>(B), *ct = static_cast<const T *>(C);
     T *yt = static_cast<T *>(y);
     if (jscan::rows_kernel_applies(nrows, D)) {
-        jscan::launch_prefill_rows<E, kSummary, false, kScalarA>(xt, dt, A, bt, ct, h0, yt, h_final, dsum, sg, nrows,
+        jscan::launch_prefill_rows<E, kSummary, false, AF>(xt, dt, A, bt, ct, h0, yt, h_final, dsum, sg, nrows,
                                                                   (int)D, stream);
         return;
     }
     const int blocks_per_row = (int)((D + 63) / 64);
-    hipLaunchKernelGGL((jscan::prefill_lane_kernel<E, kSummary, kScalarA>), dim3((unsigned)(nrows * blocks_per_row)), dim3(64),
+    hipLaunchKernelGGL((jscan::prefill_lane_kernel<E, kSummary, AF>), dim3((unsigned)(nrows * blocks_per_row)), dim3(64),
                        0, stream, xt, dt, A, bt, ct, h0, yt, h_final, dsum, sg, (int)D, blocks_per_row);
 }
 
 // Token-by-token prefill of whole sequences (one row per sequence).
-template <typename E, bool kScalarA = false>
+template <typename E, jscan::AForm AF = jscan::AForm::Diagonal>
 jscan_status launch_prefill(const void *x, const void *delta, const float *A, const void *B, const void *C,
                             const float *h0, void *y, float *h_final, int64_t batch, int64_t L, int64_t D,
                             hipStream_t stream) {
@@ -80,17 +80,17 @@ jscan_status launch_prefill(const void *x, const void *delta, const float *A, co
         return launch_status();
     }
     const jscan::Segments sg{L, L, 1, 0};
-    launch_rows<E, false, kScalarA>(x, delta, A, B, C, h0, y, h_final, nullptr, sg, batch, D, stream);
+    launch_rows<E, false, AF>(x, delta, A, B, C, h0, y, h_final, nullptr, sg, batch, D, stream);
     return launch_status();
 }
 
-// Argument checks shared by every prefill entry point.  scalar_a: A holds D values (the
-// scaled identity) instead of D * N.  Sets *nothing_to_do for zero-sized
+// Argument checks shared by every prefill entry point.  af: the form of A, which fixes its
+// size (D values for the scaled identity, D * N otherwise).  Sets *nothing_to_do for zero-sized
 // work (which is then OK without a launch).
 jscan_status check_prefill(const void *x, const void *delta, const float *A, const void *B, const void *C,
                            const float *h0, bool h0_required, const void *y, const float *h_final, int64_t batch,
                            int64_t L, int64_t D, int64_t N, jscan_dtype dtype, bool *nothing_to_do,
-                           bool scalar_a = false) {
+                           jscan::AForm af = jscan::AForm::Diagonal) {
     *nothing_to_do = false;
     if (dtype != JSCAN_F32 && dtype != JSCAN_BF16) return JSCAN_ERR_DTYPE;
     if (batch < 0 || L < 0 || D < 0 || N != JSCAN_D_STATE || D % 8 != 0) return JSCAN_ERR_SHAPE;
@@ -111,7 +111,7 @@ jscan_status check_prefill(const void *x, const void *delta, const float *A, con
         if (p && !aligned16(p)) return JSCAN_ERR_ALIGN;
 
     const int64_t seq = batch * L * D * es, bc = batch * L * N * es;
-    const int64_t state = batch * D * N * 4, a_bytes = D * (scalar_a ? 1 : N) * 4;
+    const int64_t state = batch * D * N * 4, a_bytes = D * (af == jscan::AForm::ScaledIdentity ? 1 : N) * 4;
     const Span sy = span(y, L > 0 ? seq : 0), sh = span(h_final, state);
     const Span inputs[] = {span(x, seq), span(delta, seq), span(A, a_bytes), span(B, bc), span(C, bc)};
     for (const Span &s : inputs)
@@ -128,16 +128,22 @@ jscan_status check_prefill(const void *x, const void *delta, const float *A, con
 jscan_status prefill_impl(const void *x, const void *delta, const float *A, const void *B,
                           const void *C, const float *h0, bool resume, void *y, float *h_final,
                           int64_t batch, int64_t L, int64_t D, int64_t N, jscan_dtype dtype,
-                          void *stream, bool scalar_a = false) {
+                          void *stream, jscan::AForm af = jscan::AForm::Diagonal) {
+    using jscan::AForm;
     bool empty = false;
     const jscan_status st =
-        check_prefill(x, delta, A, B, C, h0, resume, y, h_final, batch, L, D, N, dtype, &empty, scalar_a);
+        check_prefill(x, delta, A, B, C, h0, resume, y, h_final, batch, L, D, N, dtype, &empty, af);
     if (st != JSCAN_OK || empty) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (scalar_a) {
+    if (af == AForm::ScaledIdentity) {
         if (dtype == JSCAN_BF16)
-            return launch_prefill<jscan::BF16, true>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s);
-        return launch_prefill<jscan::F32, true>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s);
+            return launch_prefill<jscan::BF16, AForm::ScaledIdentity>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s);
+        return launch_prefill<jscan::F32, AForm::ScaledIdentity>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s);
+    }
+    if (af == AForm::ComplexPairs) {
+        if (dtype == JSCAN_BF16)
+            return launch_prefill<jscan::BF16, AForm::ComplexPairs>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s);
+        return launch_prefill<jscan::F32, AForm::ComplexPairs>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s);
     }
     if (dtype == JSCAN_BF16)
         return launch_prefill<jscan::BF16>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s);
@@ -225,24 +231,25 @@ void launch_ssm_inputs(const uint16_t *x, const uint16_t *w_x, const float *g_d,
 
 // ---- decode step -----------------------------------------------------------------------
 
-template <typename E, bool kScalarA>
+template <typename E, jscan::AForm AF>
 jscan_status launch_step(float *h, const void *x_t, const void *delta_t, const float *A,
                          const void *B_t, const void *C_t, void *y_t, int64_t batch, int64_t D,
                          int64_t ld_xd, int64_t ld_bc, hipStream_t stream) {
     using T = typename E::store_t;
     const int blocks_per_rows = (int)((D * 4 + 255) / 256);
     const int64_t row_groups = (batch + jscan::step::kRows - 1) / jscan::step::kRows;
-    hipLaunchKernelGGL((jscan::step_kernel<E, kScalarA>), dim3((unsigned)(row_groups * blocks_per_rows)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((jscan::step_kernel<E, AF>), dim3((unsigned)(row_groups * blocks_per_rows)), dim3(256), 0, stream,
                        h, static_cast<const T *>(x_t), static_cast<const T *>(delta_t), A,
                        static_cast<const T *>(B_t), static_cast<const T *>(C_t), static_cast<T *>(y_t), (int)batch,
                        (int)D, blocks_per_rows, ld_xd, ld_bc);
     return launch_status();
 }
 
-// Checks and launch shared by the two decode-step entry points.  scalar_a: A holds D values.
+// Checks and launch shared by the decode-step entry points.  af: the form of A.
 jscan_status step_impl(float *h, const void *x_t, const void *delta_t, const float *A, const void *B_t, const void *C_t,
                        void *y_t, int64_t batch, int64_t D, int64_t N, int64_t ld_xd, int64_t ld_bc, jscan_dtype dtype,
-                       void *stream, bool scalar_a) {
+                       void *stream, jscan::AForm af) {
+    using jscan::AForm;
     if (dtype != JSCAN_F32 && dtype != JSCAN_BF16) return JSCAN_ERR_DTYPE;
     if (batch < 0 || D < 0 || N != JSCAN_D_STATE || D % 8 != 0) return JSCAN_ERR_SHAPE;
     if (D > (1 << 24) || batch > (1 << 20)) return JSCAN_ERR_SHAPE;
@@ -258,21 +265,30 @@ jscan_status step_impl(float *h, const void *x_t, const void *delta_t, const flo
     const int64_t es = elem_bytes(dtype);
     const int64_t rows_xd = ((batch - 1) * ld_xd + D) * es, rows_bc = ((batch - 1) * ld_bc + N) * es;
     const Span sh = span(h, batch * D * N * 4), sy = span(y_t, rows_xd);
-    const Span inputs[] = {span(x_t, rows_xd), span(delta_t, rows_xd), span(A, D * (scalar_a ? 1 : N) * 4), span(B_t, rows_bc),
+    const Span inputs[] = {span(x_t, rows_xd), span(delta_t, rows_xd), span(A, D * (af == AForm::ScaledIdentity ? 1 : N) * 4), span(B_t, rows_bc),
                            span(C_t, rows_bc)};
     for (const Span &s : inputs)
         if (overlaps(sy, s) || overlaps(sh, s)) return JSCAN_ERR_ALIAS;
     if (overlaps(sy, sh)) return JSCAN_ERR_ALIAS;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (scalar_a) {
+    if (af == AForm::ScaledIdentity) {
         if (dtype == JSCAN_BF16)
-            return launch_step<jscan::BF16, true>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s);
-        return launch_step<jscan::F32, true>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s);
+            return launch_step<jscan::BF16, AForm::ScaledIdentity>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd,
+                                                                    ld_bc, s);
+        return launch_step<jscan::F32, AForm::ScaledIdentity>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc,
+                                                               s);
+    }
+    if (af == AForm::ComplexPairs) {
+        if (dtype == JSCAN_BF16)
+            return launch_step<jscan::BF16, AForm::ComplexPairs>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd,
+                                                                  ld_bc, s);
+        return launch_step<jscan::F32, AForm::ComplexPairs>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc,
+                                                             s);
     }
     if (dtype == JSCAN_BF16)
-        return launch_step<jscan::BF16, false>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s);
-    return launch_step<jscan::F32, false>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s);
+        return launch_step<jscan::BF16, AForm::Diagonal>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s);
+    return launch_step<jscan::F32, AForm::Diagonal>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s);
 }
 
 }  // namespace
@@ -333,19 +349,36 @@ jscan_status jscan_step(float *h, const void *x_t, const void *delta_t, const fl
                         const void *B_t, const void *C_t, void *y_t, int64_t batch, int64_t D,
                         int64_t N, int64_t ld_xd, int64_t ld_bc, jscan_dtype dtype,
                         void *stream) {
-    return step_impl(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, N, ld_xd, ld_bc, dtype, stream, false);
+    return step_impl(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, N, ld_xd, ld_bc, dtype, stream,
+                     jscan::AForm::Diagonal);
 }
 
 jscan_status jscan_prefill_scalar_a(const void *x, const void *delta, const float *a, const void *B, const void *C,
                                     const float *h0, void *y, float *h_final, int64_t batch, int64_t L, int64_t D,
                                     int64_t N, jscan_dtype dtype, void *stream) {
-    return prefill_impl(x, delta, a, B, C, h0, false, y, h_final, batch, L, D, N, dtype, stream, true);
+    return prefill_impl(x, delta, a, B, C, h0, false, y, h_final, batch, L, D, N, dtype, stream,
+                        jscan::AForm::ScaledIdentity);
 }
 
 jscan_status jscan_step_scalar_a(float *h, const void *x_t, const void *delta_t, const float *a, const void *B_t,
                                  const void *C_t, void *y_t, int64_t batch, int64_t D, int64_t N, int64_t ld_xd,
                                  int64_t ld_bc, jscan_dtype dtype, void *stream) {
-    return step_impl(h, x_t, delta_t, a, B_t, C_t, y_t, batch, D, N, ld_xd, ld_bc, dtype, stream, true);
+    return step_impl(h, x_t, delta_t, a, B_t, C_t, y_t, batch, D, N, ld_xd, ld_bc, dtype, stream,
+                     jscan::AForm::ScaledIdentity);
+}
+
+jscan_status jscan_prefill_complex(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                                   const float *h0, void *y, float *h_final, int64_t batch, int64_t L, int64_t D,
+                                   int64_t N, jscan_dtype dtype, void *stream) {
+    return prefill_impl(x, delta, A, B, C, h0, false, y, h_final, batch, L, D, N, dtype, stream,
+                        jscan::AForm::ComplexPairs);
+}
+
+jscan_status jscan_step_complex(float *h, const void *x_t, const void *delta_t, const float *A, const void *B_t,
+                                const void *C_t, void *y_t, int64_t batch, int64_t D, int64_t N, int64_t ld_xd,
+                                int64_t ld_bc, jscan_dtype dtype, void *stream) {
+    return step_impl(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, N, ld_xd, ld_bc, dtype, stream,
+                     jscan::AForm::ComplexPairs);
 }
 
 jscan_status jscan_ssm_inputs(const void *x, const void *w_x, const float *g_delta, const float *g_B,
@@ -439,6 +472,6 @@ const char *jscan_status_string(jscan_status s) {
 
 int jscan_last_hip_error(void) { return g_last_hip_error; }
 
-int jscan_version(void) { return 104; }
+int jscan_version(void) { return 105; }
 
 }  // extern "C"

@@ -14,9 +14,10 @@ namespace jscan {
 
 // One lane scans one channel of one row (see Segments) from the row's initial state (zero
 // when h0 is null).  A segment-summary launch (kSummary) writes no y; it writes the row's
-// final state and the sum of the row's delta values to dsum[row][D].  With kScalarA, A is the
-// scaled identity a[D] and the channel's one decay per token serves all 16 states.
-template <typename E, bool kSummary, bool kScalarA = false>
+// final state and the sum of the row's delta values to dsum[row][D].  With a scaled-identity
+// A (AF), A is a[D] and the channel's one decay per token serves all 16 states; with a complex
+// state, states 2k and 2k+1 form one complex state advanced by advance_complex().
+template <typename E, bool kSummary, AForm AF = AForm::Diagonal>
 __global__ __launch_bounds__(64) void prefill_lane_kernel(
     const typename E::store_t *__restrict__ x, const typename E::store_t *__restrict__ dl,
     const float *__restrict__ A, const typename E::store_t *__restrict__ B,
@@ -28,11 +29,17 @@ __global__ __launch_bounds__(64) void prefill_lane_kernel(
     if (d >= D) return;  // no cross-lane work below, so idle lanes may leave
     const RowSpan span = row_span(sg, vrow);
 
-    static_assert(!kScalarA || !kSummary, "the scaled-identity path is a plain prefill");
+    static_assert(AF == AForm::Diagonal || !kSummary, "the other forms of A run the plain prefill");
+    constexpr bool kScalarA = AF == AForm::ScaledIdentity, kComplexA = AF == AForm::ComplexPairs;
     float a2[kDState], h[kDState];
 #pragma unroll
     for (int n = 0; n < kDState; ++n) {
-        a2[n] = scaled_A(kScalarA ? A[d] : A[(int64_t)d * kDState + n]);
+        if constexpr (kComplexA) {   // (A2, turns) of complex entry n / 2
+            const ComplexA ca = complex_A(A[(int64_t)d * kDState + (n & ~1)], A[(int64_t)d * kDState + (n | 1)]);
+            a2[n] = (n & 1) ? ca.turns : ca.a2;
+        } else {
+            a2[n] = scaled_A(kScalarA ? A[d] : A[(int64_t)d * kDState + n]);
+        }
         h[n] = h0 ? h0[((int64_t)vrow * D + d) * kDState + n] : 0.0f;
     }
     const int64_t row = span.tok0;
@@ -48,11 +55,20 @@ __global__ __launch_bounds__(64) void prefill_lane_kernel(
         const float dx = delta_x(dv, xv);
         const float abar = kScalarA ? decay(dv, a2[0]) : 0.0f;
         float acc = 0.0f;
+        if constexpr (kComplexA) {
 #pragma unroll
-        for (int n = 0; n < kDState; ++n) {
-            const float b = E::load(Br + t * kDState + n);
-            h[n] = kScalarA ? advance_decayed(h[n], abar, dx, b) : advance(h[n], dv, a2[n], dx, b);
-            if constexpr (!kSummary) acc = __builtin_fmaf(E::load(Cr + t * kDState + n), h[n], acc);
+            for (int k = 0; k < kDState / 2; ++k)
+                advance_complex(h[2 * k], h[2 * k + 1], dv, ComplexA{a2[2 * k], a2[2 * k + 1]}, dx,
+                                E::load(Br + t * kDState + 2 * k), E::load(Br + t * kDState + 2 * k + 1));
+#pragma unroll
+            for (int n = 0; n < kDState; ++n) acc = __builtin_fmaf(E::load(Cr + t * kDState + n), h[n], acc);
+        } else {
+#pragma unroll
+            for (int n = 0; n < kDState; ++n) {
+                const float b = E::load(Br + t * kDState + n);
+                h[n] = kScalarA ? advance_decayed(h[n], abar, dx, b) : advance(h[n], dv, a2[n], dx, b);
+                if constexpr (!kSummary) acc = __builtin_fmaf(E::load(Cr + t * kDState + n), h[n], acc);
+            }
         }
         if constexpr (kSummary)
             dacc += dv;

@@ -17,7 +17,7 @@
 //     instruction is issued.
 //   * delta_t[d] and delta_t[d] * x_t[d] are per lane (per channel).  The workgroup converts
 //     each tile once into fp32 pairs in LDS, and every row reads them as a broadcast.  With a
-//     scaled-identity A (kScalarA: one a[d] for all states of a channel) the pair carries the
+//     scaled-identity A (AForm::ScaledIdentity: one a[d] for all states of a channel) the pair carries the
 //     channel's decay 2^(delta * a2[d]) in place of delta, computed once per (token, channel)
 //     while staging, and the scan waves run no exponential at all.
 //   * y_t[d] = sum over 16 states = 2 states in-lane, 4 rows in-wave (two permlane swap
@@ -216,13 +216,14 @@ __device__ __forceinline__ void fused_delta(const u32x4_t (&f)[fused::kKS], cons
 
 // Converts one quarter of a tile from registers into LDS: channel 4q + part of this thread's
 // (delta*x, delta) fp32 pairs, and states nb + 2*part, nb + 2*part + 1 of its B or C token.
-// With kScalarA the second member is the channel's decay 2^(delta * a2) instead, a2 taken
+// With a scaled-identity A the second member is the channel's decay 2^(delta * a2), a2 taken
 // from a2q (this thread's four channels).  Tokens at or past L become identity tokens
 // (delta = 0, x = -0, B = C = 0; their decay is exactly 1).  A tile is staged a quarter per
 // 16-token group so that the LDS writes never pile up behind each other.
-template <typename E, int part, bool kScalarA>
+template <typename E, int part, AForm AF>
 __device__ __forceinline__ void stage_part(const TileRegs<E> &R, float *dx_s, float *bc_s, int64_t t0, int64_t L,
                                            int tid, const float4 &a2q) {
+    constexpr bool kScalarA = AF == AForm::ScaledIdentity;
     const float a2 = part == 0 ? a2q.x : part == 1 ? a2q.y : part == 2 ? a2q.z : a2q.w;
     const int p = tid >> 3, q = tid & 7;
     float4 v;
@@ -247,13 +248,13 @@ __device__ __forceinline__ void stage_part(const TileRegs<E> &R, float *dx_s, fl
     dst[(nb + 2 * part) * rows::kBcStride + tb] = f[(2 * part) & 3];
     dst[(nb + 2 * part + 1) * rows::kBcStride + tb] = f[(2 * part + 1) & 3];
 }
-template <typename E, bool kScalarA>
+template <typename E, AForm AF>
 __device__ __forceinline__ void stage_tile(const TileRegs<E> &R, float *dx_s, float *bc_s, int64_t t0, int64_t L,
                                            int tid, const float4 &a2q) {
-    stage_part<E, 0, kScalarA>(R, dx_s, bc_s, t0, L, tid, a2q);
-    stage_part<E, 1, kScalarA>(R, dx_s, bc_s, t0, L, tid, a2q);
-    stage_part<E, 2, kScalarA>(R, dx_s, bc_s, t0, L, tid, a2q);
-    stage_part<E, 3, kScalarA>(R, dx_s, bc_s, t0, L, tid, a2q);
+    stage_part<E, 0, AF>(R, dx_s, bc_s, t0, L, tid, a2q);
+    stage_part<E, 1, AF>(R, dx_s, bc_s, t0, L, tid, a2q);
+    stage_part<E, 2, AF>(R, dx_s, bc_s, t0, L, tid, a2q);
+    stage_part<E, 3, AF>(R, dx_s, bc_s, t0, L, tid, a2q);
 }
 
 // One 16-token group's LDS operands for one lane: (delta*x, delta) of its channel for the 16
@@ -280,15 +281,18 @@ __device__ __forceinline__ void load_half(GroupRegs &g, const float *dxs, const 
 }
 
 // One token: advance this lane's two states and return C*h summed over them (a summary
-// scan adds the token's delta to `dsum` instead and returns nothing useful).  With kScalarA
-// the pair's second member is already the decay.
-template <int TAU, bool kSummary, bool kScalarA>
+// scan adds the token's delta to `dsum` instead and returns nothing useful).  With a
+// scaled-identity A the pair's second member is already the decay; with a complex state the
+// lane's two states are one complex state and (a2_0, a2_1) its prepared ComplexA.
+template <int TAU, bool kSummary, AForm AF>
 __device__ __forceinline__ float token_step(const GroupRegs &g, float &h_0, float &h_1, float a2_0, float a2_1,
                                             float &dsum) {
     const float4 v = g.v[TAU >> 1];
     const float dxv = (TAU & 1) ? v.z : v.x;
     const float dv = (TAU & 1) ? v.w : v.y;
-    if constexpr (kScalarA) {
+    if constexpr (AF == AForm::ComplexPairs) {
+        advance_complex(h_0, h_1, dv, ComplexA{a2_0, a2_1}, dxv, row_bcast<TAU>(g.b0), row_bcast<TAU>(g.b1));
+    } else if constexpr (AF == AForm::ScaledIdentity) {
         h_0 = advance_decayed(h_0, dv, dxv, row_bcast<TAU>(g.b0));
         h_1 = advance_decayed(h_1, dv, dxv, row_bcast<TAU>(g.b1));
     } else {
@@ -307,11 +311,11 @@ __device__ __forceinline__ float token_step(const GroupRegs &g, float &h_0, floa
 // partials (summed over the wave's 4 rows) in the y exchange rows `ys` (row = token in group).
 // A segment-summary scan (kSummary) produces no y; it adds the tokens' delta to `dsum` in
 // token order instead, and the y arithmetic is left out of the code altogether.
-template <int H, bool kSummary, bool kScalarA>
+template <int H, bool kSummary, AForm AF>
 __device__ __forceinline__ void scan_half(const GroupRegs &g, float &h_0, float &h_1, float a2_0, float a2_1, float *ys,
                                           int rt, int ch, float &dsum) {
     float P[8];
-#define JSCAN_STEP(i) P[i] = token_step<8 * H + (i), kSummary, kScalarA>(g, h_0, h_1, a2_0, a2_1, dsum);
+#define JSCAN_STEP(i) P[i] = token_step<8 * H + (i), kSummary, AF>(g, h_0, h_1, a2_0, a2_1, dsum);
     JSCAN_STEP(0) JSCAN_STEP(1) JSCAN_STEP(2) JSCAN_STEP(3)
     JSCAN_STEP(4) JSCAN_STEP(5) JSCAN_STEP(6) JSCAN_STEP(7)
 #undef JSCAN_STEP
@@ -373,8 +377,9 @@ __device__ __forceinline__ void write_final(const FinalRegs &F, typename E::stor
 // (zero when h0 is null).  A segment-summary launch (kSummary) writes no y; it writes the
 // row's final state and, per channel, the sum of the row's delta values to dsum[row][D].
 // With kFused, delta is not read: the helper waves compute it from dp (bf16 only).  With
-// kScalarA, A is the scaled identity a[D] (one value per channel) instead of A[D][16].
-template <typename E, bool kSummary, bool kFused = false, bool kScalarA = false>
+// a scaled-identity A (AF), A is a[D] (one value per channel) instead of A[D][16]; with a
+// complex state, A[D][16] holds 8 complex entries per channel as (real, imaginary) pairs.
+template <typename E, bool kSummary, bool kFused = false, AForm AF = AForm::Diagonal>
 __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_rows_kernel(
     const typename E::store_t *__restrict__ x, const typename E::store_t *__restrict__ dl,
     const float *__restrict__ A, const typename E::store_t *__restrict__ B,
@@ -382,7 +387,8 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
     typename E::store_t *__restrict__ y, float *__restrict__ h_final, float *__restrict__ dsum, Segments sg, int D,
     int blocks_per_row, int xcd_stride, DeltaProj dp) {
     static_assert(!kFused || (sizeof(typename E::store_t) == 2 && !kSummary), "the fused delta path is bf16 only");
-    static_assert(!kScalarA || (!kSummary && !kFused), "the scaled-identity path is a plain prefill");
+    static_assert(AF == AForm::Diagonal || (!kSummary && !kFused), "the other forms of A run the plain prefill");
+    constexpr bool kScalarA = AF == AForm::ScaledIdentity;
     __shared__ __attribute__((aligned(16))) float dx_s[2][rows::kDxSize];
     __shared__ __attribute__((aligned(16))) float bc_s[2][2 * rows::kBcSize];
     __shared__ __attribute__((aligned(16))) float y_s[2][rows::kYSize];
@@ -437,7 +443,7 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
             load_dlow(dfr[0], dp.d_low, row, 0, L, hw, l);
             fused_delta(dfr[0], wf, bias, xch, R[0], l);
         }
-        stage_tile<E, kScalarA>(R[0], dx_s[0], bc_s[0], 0, L, tid, a2q);
+        stage_tile<E, AF>(R[0], dx_s[0], bc_s[0], 0, L, tid, a2q);
         load_tile<E, !kFused>(R[1], xb, db, bcb, rows::kT, L, D, tid);
         load_tile<E, !kFused>(R[0], xb, db, bcb, 2 * rows::kT, L, D, tid);
         if constexpr (kFused) {
@@ -450,7 +456,7 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
             constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
             if (k + 1 < ntiles) {
                 if constexpr (kFused) fused_delta(dfr[nxt], wf, bias, xch, R[nxt], l);
-                stage_tile<E, kScalarA>(R[nxt], dx_s[nxt], bc_s[nxt], (int64_t)(k + 1) * rows::kT, L, tid, a2q);
+                stage_tile<E, AF>(R[nxt], dx_s[nxt], bc_s[nxt], (int64_t)(k + 1) * rows::kT, L, tid, a2q);
                 if (k + 3 < ntiles) {
                     load_tile<E, !kFused>(R[nxt], xb, db, bcb, (int64_t)(k + 3) * rows::kT, L, D, tid);
                     if constexpr (kFused) load_dlow(dfr[nxt], dp.d_low, row, (int64_t)(k + 3) * rows::kT, L, hw, l);
@@ -485,8 +491,16 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
     const int d = d0 + ch;
     const int n0 = 8 * sh + 2 * r;          // this lane's states n0, n0 + 1
 
-    const float a2_0 = kScalarA ? 0.0f : scaled_A(A[(int64_t)d * kDState + n0]);
-    const float a2_1 = kScalarA ? 0.0f : scaled_A(A[(int64_t)d * kDState + n0 + 1]);
+    // diagonal: the lane's two A2 values; complex: the prepared entry of its complex state
+    float a2_0 = 0.0f, a2_1 = 0.0f;
+    if constexpr (AF == AForm::Diagonal) {
+        a2_0 = scaled_A(A[(int64_t)d * kDState + n0]);
+        a2_1 = scaled_A(A[(int64_t)d * kDState + n0 + 1]);
+    } else if constexpr (AF == AForm::ComplexPairs) {
+        const ComplexA ca = complex_A(A[(int64_t)d * kDState + n0], A[(int64_t)d * kDState + n0 + 1]);
+        a2_0 = ca.a2;
+        a2_1 = ca.turns;
+    }
     float h_0 = 0.0f, h_1 = 0.0f;
     if (h0) {
         const float2 hv = *reinterpret_cast<const float2 *>(h0 + ((int64_t)vrow * D + d) * kDState + n0);
@@ -511,31 +525,31 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
         const float *dxc = dx_s[cur], *bcc = bc_s[cur];
         load_half<0>(G[1], dxc, bcc, 16, ch, n0, c);
         JSCAN_SB;
-        scan_half<0, kSummary, kScalarA>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch, dacc);
+        scan_half<0, kSummary, AF>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch, dacc);
         JSCAN_SB;
         load_half<1>(G[1], dxc, bcc, 16, ch, n0, c);
         JSCAN_SB;
-        scan_half<1, kSummary, kScalarA>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch, dacc);
+        scan_half<1, kSummary, AF>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch, dacc);
         JSCAN_SB;
         load_half<0>(G[0], dxc, bcc, 32, ch, n0, c);
         JSCAN_SB;
-        scan_half<0, kSummary, kScalarA>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch, dacc);
+        scan_half<0, kSummary, AF>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch, dacc);
         JSCAN_SB;
         load_half<1>(G[0], dxc, bcc, 32, ch, n0, c);
         JSCAN_SB;
-        scan_half<1, kSummary, kScalarA>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch, dacc);
+        scan_half<1, kSummary, AF>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch, dacc);
         JSCAN_SB;
         load_half<0>(G[1], dxc, bcc, 48, ch, n0, c);
         JSCAN_SB;
-        scan_half<0, kSummary, kScalarA>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch, dacc);
+        scan_half<0, kSummary, AF>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch, dacc);
         JSCAN_SB;
         load_half<1>(G[1], dxc, bcc, 48, ch, n0, c);
         JSCAN_SB;
-        scan_half<1, kSummary, kScalarA>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch, dacc);
+        scan_half<1, kSummary, AF>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch, dacc);
         JSCAN_SB;
-        scan_half<0, kSummary, kScalarA>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch, dacc);
+        scan_half<0, kSummary, AF>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch, dacc);
         JSCAN_SB;
-        scan_half<1, kSummary, kScalarA>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch, dacc);
+        scan_half<1, kSummary, AF>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch, dacc);
         __syncthreads();
         if (k + 1 < ntiles) {
             load_half<0>(G[0], dx_s[nxt], bc_s[nxt], 0, ch, n0, c);
@@ -560,7 +574,7 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
 inline bool rows_kernel_applies(int64_t /*batch*/, int64_t D) { return D % rows::kCh == 0; }
 
 // Launches one work-group per 32 channels of each of the `nrows` rows described by sg.
-template <typename E, bool kSummary, bool kFused = false, bool kScalarA = false>
+template <typename E, bool kSummary, bool kFused = false, AForm AF = AForm::Diagonal>
 void launch_prefill_rows(const typename E::store_t *x, const typename E::store_t *dl, const float *A,
                          const typename E::store_t *B, const typename E::store_t *C, const float *h0,
                          typename E::store_t *y, float *h_final, float *dsum, const Segments &sg, int64_t nrows,
@@ -568,7 +582,7 @@ void launch_prefill_rows(const typename E::store_t *x, const typename E::store_t
     const int blocks_per_row = D / rows::kCh;
     const int64_t blocks = nrows * blocks_per_row;
     const int xcd_stride = (blocks % 8 == 0) ? (int)(blocks / 8) : 0;
-    hipLaunchKernelGGL((prefill_rows_kernel<E, kSummary, kFused, kScalarA>), dim3((unsigned)blocks), dim3(rows::kThreads), 0,
+    hipLaunchKernelGGL((prefill_rows_kernel<E, kSummary, kFused, AF>), dim3((unsigned)blocks), dim3(rows::kThreads), 0,
                        stream, x, dl, A, B, C, h0, y, h_final, dsum, sg, D, blocks_per_row, xcd_stride, dp);
 }
 

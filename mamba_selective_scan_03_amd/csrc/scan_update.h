@@ -9,7 +9,8 @@
 // the decay 2^(delta * a2[d]) is the same for the whole channel.  The kernels for that form
 // evaluate it once per (token, channel) with the same `decay()` and hand it to
 // `advance_decayed()`, which is the second half of `advance()`: their states are therefore
-// bit-identical to the general kernels' run on A[d][n] = a[d].
+// bit-identical to the general kernels' run on A[d][n] = a[d].  A complex-valued state (the
+// Mamba-3 form) advances through `advance_complex()`, the one definition of that update.
 //
 // The recurrence is the S6 equation of the Jamba notes page ("Jamba: A Hybrid
 // Transformer-Mamba Language Model", section "Mamba layer"):
@@ -44,6 +45,39 @@ __device__ __forceinline__ float advance_decayed(float h, float abar, float dx, 
 // The same with the decay evaluated here, from delta and A2.
 __device__ __forceinline__ float advance(float h, float delta, float a2, float dx, float b) {
     return advance_decayed(h, decay(delta, a2), dx, b);
+}
+
+// ---- forms of A -------------------------------------------------------------------------
+// Diagonal: one value per (channel, state), the Mamba-1 form.  ScaledIdentity: one value per
+// channel for all its states, the Mamba-2 form (A[d][n] = a[d]).  ComplexPairs: the state is
+// complex, the Mamba-3 form (lesson page "Jamba - Hybrid SSM-Transformer", section "Mamba-3",
+// item 2): states 2k and 2k+1 of a channel are the real and imaginary parts of one complex
+// state, and A[d][2k], A[d][2k+1] the real and imaginary parts of its diagonal entry; B and C
+// pair up the same way.
+enum class AForm : int { Diagonal, ScaledIdentity, ComplexPairs };
+
+constexpr float kInv2Pi = 0.159154943091895335769f;   // 1 / (2 pi), rounded to fp32
+
+// A complex diagonal entry a = re + i im, prepared once: A2 = re * log2(e) for the modulus of
+// the decay and im / (2 pi) for its angle in turns (what v_sin_f32 / v_cos_f32 take).
+struct ComplexA {
+    float a2, turns;
+};
+__device__ __forceinline__ ComplexA complex_A(float re, float im) { return ComplexA{re * kLog2e, im * kInv2Pi}; }
+
+// One complex state (h_re, h_im) advanced by one token:  h <- exp(delta a) h + (delta x) b, with
+// exp(delta a) = 2^(delta A2) (cos phi + i sin phi), phi = delta im in turns, reduced to [0, 1)
+// first so that the hardware sine and cosine see a small argument.  The real-part update is
+// fma(r cos, h_re, fma(-r sin, h_im, (delta x) b_re)), the imaginary one mirrors it.
+__device__ __forceinline__ void advance_complex(float &h_re, float &h_im, float delta, ComplexA a, float dx,
+                                                float b_re, float b_im) {
+    const float r = decay(delta, a.a2);
+    const float phi = __builtin_amdgcn_fractf(delta * a.turns);
+    const float rc = r * __builtin_amdgcn_cosf(phi), rs = r * __builtin_amdgcn_sinf(phi);
+    const float re = __builtin_fmaf(rc, h_re, __builtin_fmaf(-rs, h_im, dx * b_re));
+    const float im = __builtin_fmaf(rc, h_im, __builtin_fmaf(rs, h_re, dx * b_im));
+    h_re = re;
+    h_im = im;
 }
 
 // A compile-time integer as a value: lets an unrolled loop body pick register sets and LDS

@@ -44,8 +44,9 @@ template <> struct Quad<F32> {
     static __device__ __forceinline__ float4 load(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 };
 
-// With kScalarA, A is the scaled identity a[D]: one decay per (row, channel) serves the quad.
-template <typename E, bool kScalarA = false>
+// With a scaled-identity A (AF), A is a[D]: one decay per (row, channel) serves the quad.  With
+// a complex state the quad is two complex states, (4q, 4q+1) and (4q+2, 4q+3).
+template <typename E, AForm AF = AForm::Diagonal>
 __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ h,
                                                    const typename E::store_t *__restrict__ x,
                                                    const typename E::store_t *__restrict__ dl,
@@ -60,9 +61,11 @@ __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ h,
     if (lane_in_row >= D * 4) return;  // whole quads leave together (D * 4 is a multiple of 4)
     const int d = lane_in_row >> 2, q = lane_in_row & 3;
 
+    constexpr bool kScalarA = AF == AForm::ScaledIdentity, kComplexA = AF == AForm::ComplexPairs;
     const float4 av = kScalarA ? make_float4(A[d], A[d], A[d], A[d])
                                : *reinterpret_cast<const float4 *>(A + (int64_t)d * kDState + q * 4);
     const float a0 = scaled_A(av.x), a1 = scaled_A(av.y), a2 = scaled_A(av.z), a3 = scaled_A(av.w);
+    const ComplexA ca0 = complex_A(av.x, av.y), ca1 = complex_A(av.z, av.w);
     float4 hv[NR], bv[NR], cv[NR];
     float xv[NR], dv[NR];
 #pragma unroll
@@ -80,7 +83,11 @@ __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ h,
         const int b = rg * NR + j;
         const float dx = delta_x(dv[j], xv[j]);
         float4 hn;
-        if constexpr (kScalarA) {
+        if constexpr (kComplexA) {
+            hn = hv[j];
+            advance_complex(hn.x, hn.y, dv[j], ca0, dx, bv[j].x, bv[j].y);
+            advance_complex(hn.z, hn.w, dv[j], ca1, dx, bv[j].z, bv[j].w);
+        } else if constexpr (kScalarA) {
             const float abar = decay(dv[j], a0);
             hn.x = advance_decayed(hv[j].x, abar, dx, bv[j].x);
             hn.y = advance_decayed(hv[j].y, abar, dx, bv[j].y);

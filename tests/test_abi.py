@@ -28,7 +28,7 @@ def test_header_symbols_are_exported():
     assert {"jscan_prefill", "jscan_prefill_resume", "jscan_step", "jscan_status_string",
             "jscan_last_hip_error", "jscan_version", "jscan_prefill_chunked",
             "jscan_prefill_chunked_workspace", "jscan_ssm_inputs", "jscan_prefill_fused", "jscan_prefill_scalar_a",
-            "jscan_step_scalar_a"} <= set(names)
+            "jscan_step_scalar_a", "jscan_prefill_complex", "jscan_step_complex"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -38,7 +38,7 @@ def test_status_strings_and_version():
     for s in range(8):
         assert lib.jscan_status_string(s) and lib.jscan_status_string(s) != b"unknown status"
     assert lib.jscan_status_string(99) == b"unknown status"
-    assert lib.jscan_version() == 104
+    assert lib.jscan_version() == 105
     assert lib.jscan_last_hip_error() == 0
 
 
@@ -234,3 +234,18 @@ def test_last_hip_error_is_per_thread():
     t.start()
     t.join()
     assert seen == [0]
+
+
+def test_complex_entry_points_validate_like_the_general_ones():
+    lib = jscan.library()
+    # A is [D][16] here (not [D]): a pointer 256 bytes past A's start still overlaps it
+    assert lib.jscan_prefill_complex(P, P + 0x100000, P + 0x200000, P + 0x300000, P + 0x400000, None,
+                                     P + 0x500000, P + 0x200000 + 256, 1, 64, 64, 16, BF16, None) == EALIAS
+    assert lib.jscan_prefill_complex(P, P + 0x100000, None, P + 0x300000, P + 0x400000, None, P + 0x500000,
+                                     P + 0x600000, 1, 64, 64, 16, BF16, None) == ENULL
+    assert lib.jscan_prefill_complex(P, P + 0x100000, P + 0x200000, P + 0x300000, P + 0x400000, None,
+                                     P + 0x500000, P + 0x600000, 1, 64, 60, 16, BF16, None) == ESHAPE
+    assert lib.jscan_step_complex(P, P + 0x100000, P + 0x200000, P + 0x300000, P + 0x400000, P + 0x500000,
+                                  P + 0x600000, 2, 64, 16, 64, 16, 9, None) == EDTYPE
+    assert lib.jscan_step_complex(P, P + 0x100000, P + 0x200000, None, P + 0x400000, P + 0x500000,
+                                  P + 0x600000, 2, 64, 16, 64, 16, BF16, None) == ENULL

@@ -21,6 +21,8 @@ Distributions (the same for every workload):
     a[d]    = -(d % 16 + 1)                         scaled-identity A, tiny workload (exact)
     a[d]    = -(k_d + 1) * U(0.5, 1.5), k_d ~ U{0..15}   scaled-identity A, other workloads:
                                                     the channels' decays span the diagonal A's range
+    complex A (pairs 2k, 2k+1 = real, imaginary part of entry k):
+            real -(k + 1) * U(0.5, 1.5), imaginary pi * U(-1, 1), one draw per (d, k)
     h0      ~ N(0, 0.1)  (0.1 = standard deviation) decode workload's resident state
 bf16 workloads round every drawn value to bf16 by round-to-nearest-even (torch ``.to``).
 
@@ -44,6 +46,7 @@ BLOCK = 4096  # tokens per seeded block
 T_X, T_Z, T_B, T_C, T_A, T_H0 = 0, 1, 2, 3, 4, 5
 T_WX, T_GAIN, T_WDT, T_BDT = 6, 7, 8, 9     # producer-side weights
 T_ASC = 10                                  # scaled-identity A
+T_ACX = 11                                  # complex A
 
 
 @dataclasses.dataclass(frozen=True)
@@ -163,6 +166,18 @@ def draw_scalar_a(wl: Workload, seed: int = 0, layer: int = 0) -> torch.Tensor:
         rng = _rng(seed, wl.wid, T_ASC, layer, 0)
         k = rng.integers(0, wl.N, size=wl.D)
         a = -(k + 1) * rng.uniform(0.5, 1.5, size=wl.D)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+
+
+def draw_complex_a(wl: Workload, seed: int = 0, layer: int = 0) -> torch.Tensor:
+    """[D, N] fp32 complex diagonal of A as (real, imaginary) pairs: real parts < 0, imaginary
+    parts (angle rates) in (-pi, pi)."""
+    wl = get(wl)
+    K = wl.N // 2
+    rng = _rng(seed, wl.wid, T_ACX, layer, 0)
+    a = np.empty((wl.D, wl.N), np.float64)
+    a[:, 0::2] = -np.arange(1, K + 1)[None, :] * rng.uniform(0.5, 1.5, size=(wl.D, K))
+    a[:, 1::2] = np.pi * rng.uniform(-1.0, 1.0, size=(wl.D, K))
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
 
 
