@@ -330,6 +330,24 @@ __device__ __forceinline__ void scan_half(const GroupRegs &g, float &h_0, float 
         ys[(8 * H + 4 + rt) * rows::kYStride + ch] = reduce_rows4(P[4], P[5], P[6], P[7]);
     }
 }
+// The same half split in two: the tokens' partials (computed in one scheduling region) and their
+// reduction over rows and store (done in the next region, beside the next half's tokens).  The
+// scaled-identity form, whose tokens are short, runs its halves this way: 2% faster there, 2%
+// slower for the diagonal A.
+template <int H, AForm AF>
+__device__ __forceinline__ void half_partials(const GroupRegs &g, float &h_0, float &h_1, float a2_0, float a2_1,
+                                              float (&P)[8]) {
+    float dsum = 0.0f;
+#define JSCAN_STEP(i) P[i] = token_step<8 * H + (i), false, AF>(g, h_0, h_1, a2_0, a2_1, dsum);
+    JSCAN_STEP(0) JSCAN_STEP(1) JSCAN_STEP(2) JSCAN_STEP(3)
+    JSCAN_STEP(4) JSCAN_STEP(5) JSCAN_STEP(6) JSCAN_STEP(7)
+#undef JSCAN_STEP
+}
+template <int H>
+__device__ __forceinline__ void half_store(const float (&P)[8], float *ys, int rt, int ch) {
+    ys[(8 * H + rt) * rows::kYStride + ch] = reduce_rows4(P[0], P[1], P[2], P[3]);
+    ys[(8 * H + 4 + rt) * rows::kYStride + ch] = reduce_rows4(P[4], P[5], P[6], P[7]);
+}
 
 // The last step of y for one tile: this thread's token row t = tid / 4 and 8 channels, as the
 // two state halves' sums read from the exchange buffer.
@@ -523,33 +541,73 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
         constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
         float *ys = y_s[cur] + sh * rows::kT * rows::kYStride;
         const float *dxc = dx_s[cur], *bcc = bc_s[cur];
-        load_half<0>(G[1], dxc, bcc, 16, ch, n0, c);
-        JSCAN_SB;
-        scan_half<0, kSummary, AF>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch, dacc);
-        JSCAN_SB;
-        load_half<1>(G[1], dxc, bcc, 16, ch, n0, c);
-        JSCAN_SB;
-        scan_half<1, kSummary, AF>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch, dacc);
-        JSCAN_SB;
-        load_half<0>(G[0], dxc, bcc, 32, ch, n0, c);
-        JSCAN_SB;
-        scan_half<0, kSummary, AF>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch, dacc);
-        JSCAN_SB;
-        load_half<1>(G[0], dxc, bcc, 32, ch, n0, c);
-        JSCAN_SB;
-        scan_half<1, kSummary, AF>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch, dacc);
-        JSCAN_SB;
-        load_half<0>(G[1], dxc, bcc, 48, ch, n0, c);
-        JSCAN_SB;
-        scan_half<0, kSummary, AF>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch, dacc);
-        JSCAN_SB;
-        load_half<1>(G[1], dxc, bcc, 48, ch, n0, c);
-        JSCAN_SB;
-        scan_half<1, kSummary, AF>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch, dacc);
-        JSCAN_SB;
-        scan_half<0, kSummary, AF>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch, dacc);
-        JSCAN_SB;
-        scan_half<1, kSummary, AF>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch, dacc);
+        if constexpr (AF != AForm::ScaledIdentity) {
+            load_half<0>(G[1], dxc, bcc, 16, ch, n0, c);
+            JSCAN_SB;
+            scan_half<0, kSummary, AF>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch, dacc);
+            JSCAN_SB;
+            load_half<1>(G[1], dxc, bcc, 16, ch, n0, c);
+            JSCAN_SB;
+            scan_half<1, kSummary, AF>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch, dacc);
+            JSCAN_SB;
+            load_half<0>(G[0], dxc, bcc, 32, ch, n0, c);
+            JSCAN_SB;
+            scan_half<0, kSummary, AF>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch, dacc);
+            JSCAN_SB;
+            load_half<1>(G[0], dxc, bcc, 32, ch, n0, c);
+            JSCAN_SB;
+            scan_half<1, kSummary, AF>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch, dacc);
+            JSCAN_SB;
+            load_half<0>(G[1], dxc, bcc, 48, ch, n0, c);
+            JSCAN_SB;
+            scan_half<0, kSummary, AF>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch, dacc);
+            JSCAN_SB;
+            load_half<1>(G[1], dxc, bcc, 48, ch, n0, c);
+            JSCAN_SB;
+            scan_half<1, kSummary, AF>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch, dacc);
+            JSCAN_SB;
+            scan_half<0, kSummary, AF>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch, dacc);
+            JSCAN_SB;
+            scan_half<1, kSummary, AF>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch, dacc);
+        } else {
+            float Pa[8], Pb[8];
+            load_half<0>(G[1], dxc, bcc, 16, ch, n0, c);
+            JSCAN_SB;
+            half_partials<0, AF>(G[0], h_0, h_1, a2_0, a2_1, Pa);
+            JSCAN_SB;
+            load_half<1>(G[1], dxc, bcc, 16, ch, n0, c);
+            JSCAN_SB;
+            half_partials<1, AF>(G[0], h_0, h_1, a2_0, a2_1, Pb);
+            half_store<0>(Pa, ys, rt, ch);
+            JSCAN_SB;
+            load_half<0>(G[0], dxc, bcc, 32, ch, n0, c);
+            JSCAN_SB;
+            half_partials<0, AF>(G[1], h_0, h_1, a2_0, a2_1, Pa);
+            half_store<1>(Pb, ys, rt, ch);
+            JSCAN_SB;
+            load_half<1>(G[0], dxc, bcc, 32, ch, n0, c);
+            JSCAN_SB;
+            half_partials<1, AF>(G[1], h_0, h_1, a2_0, a2_1, Pb);
+            half_store<0>(Pa, ys + 16 * rows::kYStride, rt, ch);
+            JSCAN_SB;
+            load_half<0>(G[1], dxc, bcc, 48, ch, n0, c);
+            JSCAN_SB;
+            half_partials<0, AF>(G[0], h_0, h_1, a2_0, a2_1, Pa);
+            half_store<1>(Pb, ys + 16 * rows::kYStride, rt, ch);
+            JSCAN_SB;
+            load_half<1>(G[1], dxc, bcc, 48, ch, n0, c);
+            JSCAN_SB;
+            half_partials<1, AF>(G[0], h_0, h_1, a2_0, a2_1, Pb);
+            half_store<0>(Pa, ys + 32 * rows::kYStride, rt, ch);
+            JSCAN_SB;
+            half_partials<0, AF>(G[1], h_0, h_1, a2_0, a2_1, Pa);
+            half_store<1>(Pb, ys + 32 * rows::kYStride, rt, ch);
+            JSCAN_SB;
+            half_partials<1, AF>(G[1], h_0, h_1, a2_0, a2_1, Pb);
+            half_store<0>(Pa, ys + 48 * rows::kYStride, rt, ch);
+            JSCAN_SB;
+            half_store<1>(Pb, ys + 48 * rows::kYStride, rt, ch);
+        }
         __syncthreads();
         if (k + 1 < ntiles) {
             load_half<0>(G[0], dx_s[nxt], bc_s[nxt], 0, ch, n0, c);
