@@ -147,3 +147,23 @@ def test_fused_prefill_is_bit_identical_to_producer_then_scan(batch, L, D, with_
     assert torch.equal(bits(d_low), bits(d_low2)) and torch.equal(bits(B), bits(B2))
     assert torch.equal(bits(y1), bits(y2)), "fused y differs"
     assert torch.equal(bits(h1), bits(h2)), "fused h_final differs"
+
+
+def test_fused_prefill_64k_full_size():
+    """The 64K x 8192 workload through the producer in the launch configurations the
+    benchmark times: the fused scan (delta computed on the load path) equals the producer's
+    stored delta followed by jscan_prefill on every output bit."""
+    wl = workloads.get("prefill_64k")
+    say("generating prefill_64k x, A")
+    inp = workloads.prefill_inputs(wl)
+    wts = workloads.producer_weights(wl.D, 256)
+    dev = {k: v.cuda() for k, v in wts.items()}
+    x, A = inp["x"].cuda(), inp["A"].cuda()
+    del inp
+    delta, B, C, d_low = jscan.ssm_inputs(x, dev["w_x"], dev["g_d"], dev["g_b"], dev["g_c"], dev["w_dt"], dev["b_dt"])
+    y1, h1 = jscan.prefill(x, delta, A, B, C)
+    del delta
+    y2, h2 = jscan.prefill_fused(x, d_low, dev["w_dt"], dev["b_dt"], A, B, C)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "fused 64K y differs"
+    assert torch.equal(h1.view(torch.int32), h2.view(torch.int32)), "fused 64K h_final differs"
