@@ -18,7 +18,9 @@ A ``[D, N]``; B, C ``[batch, L, N]``; states ``[batch, D, N]``.
 
 ``prefill_scalar_a`` / ``step_scalar_a`` are the same recurrence with a scaled-identity A
 (one value per channel, the Mamba-2 form); ``prefill_complex`` / ``step_complex`` run it with a
-complex-valued state (the Mamba-3 change).  ``oracle.producer`` is the fp64 (numpy) oracle
+complex-valued state (the Mamba-3 change); ``prefill_trapezoid`` / ``step_trapezoid`` replace the
+Euler rule by the exponential-trapezoidal one (the other Mamba-3 change), for any of the three
+forms of A.  ``oracle.producer`` is the fp64 (numpy) oracle
 of the producer side that computes delta, B and C from x.
 """
 from __future__ import annotations
@@ -59,8 +61,12 @@ def _load():
     lib.oracle_step_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64]
     lib.oracle_prefill_complex_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, ctypes.c_int]
     lib.oracle_step_complex_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64]
+    ci = ctypes.c_int
+    lib.oracle_prefill_trapezoid_f64.argtypes = [dp] * 11 + [i64, i64, i64, i64, ci, ci]
+    lib.oracle_step_trapezoid_f64.argtypes = [dp] * 10 + [i64, i64, i64, ci]
     for f in (lib.oracle_prefill_f64, lib.oracle_prefill_chunked_f64, lib.oracle_step_f64,
-              lib.oracle_prefill_complex_f64, lib.oracle_step_complex_f64):
+              lib.oracle_prefill_complex_f64, lib.oracle_step_complex_f64, lib.oracle_prefill_trapezoid_f64,
+              lib.oracle_step_trapezoid_f64):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -208,4 +214,78 @@ def step_complex(h, x_t, delta_t, A, B_t, C_t):
                                      batch, D, N)
     if rc != 0:
         raise RuntimeError(f"oracle_step_complex_f64 failed ({rc})")
+    return y, h
+
+
+# ---- exponential-trapezoidal rule (the Mamba-3 discretisation) ----------------------------
+# The lesson page ("Jamba - Hybrid SSM-Transformer", section "Mamba-3", item 1) replaces the
+# Euler rule by a recurrence that mixes neighbouring tokens' state input inside the scan.  Read
+# as a two-point rule for the input integral over one step (jscan_oracle.c,
+# scan_chain_trapezoid):
+#     h_t = Abar_t h_{t-1} + (1 - lam_t) Delta_t Abar_t B_{t-1} x_{t-1} + lam_t Delta_t B_t x_t
+# lam is [batch, L, D] like delta; lam = 1 is the Euler rule, lam = 1/2 the trapezoid rule.
+# The token before the first is (x_prev [batch, D], B_prev [batch, N]) when given, else none.
+# ``form`` picks A: "diagonal" ([D, N]), "scalar" (a [D], A[d, n] = a[d]) or "complex"
+# ([D, N] as (real, imaginary) pairs, the complex-valued state).
+
+_FORMS = ("diagonal", "scalar", "complex")
+
+
+def _form_A(A, form: str, N: int):
+    if form not in _FORMS:
+        raise ValueError(f"form must be one of {_FORMS}")
+    return expand_scalar_a(A, N) if form == "scalar" else _f64(A)
+
+
+def prefill_trapezoid(x, delta, lam, A, B, C, h0=None, x_prev=None, B_prev=None, form: str = "diagonal",
+                      nthreads: int = 0):
+    """Sequential fp64 scan with the exponential-trapezoidal rule.  Returns ``(y, h_final)``."""
+    lib = _load()
+    x, delta, lam, B, C = (_f64(v) for v in (x, delta, lam, B, C))
+    A = _form_A(A, form, B.shape[-1])
+    h0 = None if h0 is None else _f64(h0)
+    batch, L, D, N = _check_shapes(x, delta, A, B, C, h0)
+    if lam.shape != x.shape:
+        raise ValueError("lam must be [batch, L, D]")
+    if (x_prev is None) != (B_prev is None):
+        raise ValueError("x_prev and B_prev go together")
+    if x_prev is not None:
+        x_prev, B_prev = _f64(x_prev), _f64(B_prev)
+        if x_prev.shape != (batch, D) or B_prev.shape != (batch, N):
+            raise ValueError("x_prev must be [batch, D] and B_prev [batch, N]")
+    cplx = form == "complex"
+    if cplx and N % 2:
+        raise ValueError("the complex state needs an even N")
+    y = np.empty((batch, L, D), np.float64)
+    h = np.empty((batch, D, N), np.float64)
+    rc = lib.oracle_prefill_trapezoid_f64(_ptr(x), _ptr(delta), _ptr(lam), _ptr(A), _ptr(B), _ptr(C), _ptr(h0),
+                                          _ptr(x_prev), _ptr(B_prev), _ptr(y), _ptr(h), batch, L, D, N, int(cplx),
+                                          int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_prefill_trapezoid_f64 failed ({rc})")
+    return y, h
+
+
+def step_trapezoid(h, x_prev, B_prev, x_t, delta_t, lam_t, A, B_t, C_t, form: str = "diagonal"):
+    """One decode step with the exponential-trapezoidal rule; (x_prev, B_prev) is the previous
+    token.  Returns ``(y_t, h_new)``; the input h is not modified."""
+    lib = _load()
+    h = _f64(h).copy()
+    x_prev, B_prev, x_t, delta_t, lam_t, B_t, C_t = (_f64(v) for v in (x_prev, B_prev, x_t, delta_t, lam_t, B_t,
+                                                                       C_t))
+    batch, D, N = h.shape
+    A = _form_A(A, form, N)
+    for v in (x_prev, x_t, delta_t, lam_t):
+        if v.shape != (batch, D):
+            raise ValueError("step_trapezoid: x_prev, x_t, delta_t, lam_t must be [batch, D]")
+    if B_prev.shape != (batch, N) or B_t.shape != (batch, N) or C_t.shape != (batch, N) or A.shape != (D, N):
+        raise ValueError("step_trapezoid: B_prev, B_t, C_t must be [batch, N] and A [D, N]")
+    cplx = form == "complex"
+    if cplx and N % 2:
+        raise ValueError("the complex state needs an even N")
+    y = np.empty((batch, D), np.float64)
+    rc = lib.oracle_step_trapezoid_f64(_ptr(h), _ptr(x_prev), _ptr(B_prev), _ptr(x_t), _ptr(delta_t), _ptr(lam_t),
+                                       _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(y), batch, D, N, int(cplx))
+    if rc != 0:
+        raise RuntimeError(f"oracle_step_trapezoid_f64 failed ({rc})")
     return y, h

@@ -41,6 +41,9 @@ typedef struct {
     double *y, *h_final;
     int64_t batch, L, D, N, chunk;
     int cplx;                     /* complex-valued state (see scan_chain_complex) */
+    int trap;                     /* exponential-trapezoidal rule (see scan_chain_trapezoid) */
+    const double *lam;            /* trapezoid weights [batch][L][D] */
+    const double *x_prev, *B_prev; /* token before the first: [batch][D], [batch][N]; NULL = none */
     int64_t item_begin, item_end; /* items are (b, d) pairs, item = b * D + d */
 } scan_job;
 
@@ -164,12 +167,104 @@ static void scan_chain_complex(const scan_job *j, int64_t b, int64_t d)
     free(h);
 }
 
+/*
+ * Exponential-trapezoidal discretisation: the first Mamba-3 change named on the lesson page
+ * ("Jamba - Hybrid SSM-Transformer", section "Mamba-3", item 1), which replaces the Euler
+ * rule by a recurrence that mixes the state input of neighbouring tokens inside the scan.
+ * Written out from the continuous system h' = A h + B(s) x(s): over one step of length
+ * Delta_t the state decays by Abar_t = exp(Delta_t A) and takes in the integral of
+ * exp((Delta_t - u) A) B x over the step.  The Euler rule keeps only the step's right end
+ * point (Delta_t B_t x_t).  A two-point rule weights the right end by lambda_t and the left
+ * end, which has decayed over the whole step, by 1 - lambda_t:
+ *
+ *     h_t = Abar_t h_{t-1} + (1 - lambda_t) Delta_t Abar_t B_{t-1} x_{t-1} + lambda_t Delta_t B_t x_t
+ *
+ * lambda_t = 1 is the Euler rule; lambda_t = 1/2 is the trapezoid rule, second-order accurate
+ * in Delta where the Euler rule is first-order.  The token before the first one is
+ * (x_prev, B_prev) when given (a resumed sequence), else there is none and its term is zero.
+ * y_t = C_t h_t as before.
+ */
+static void scan_chain_trapezoid(const scan_job *j, int64_t b, int64_t d)
+{
+    const int64_t L = j->L, D = j->D, N = j->N;
+    double *h = (double *)malloc((size_t)N * sizeof(double));
+    double *u_prev = (double *)malloc((size_t)N * sizeof(double));   /* B_{t-1} x_{t-1} */
+    for (int64_t n = 0; n < N; ++n) {
+        h[n] = j->h0 ? j->h0[(b * D + d) * N + n] : 0.0;
+        u_prev[n] = j->x_prev ? j->B_prev[b * N + n] * j->x_prev[b * D + d] : 0.0;
+    }
+    for (int64_t t = 0; t < L; ++t) {
+        const double delta_t = j->delta[(b * L + t) * D + d];
+        const double lam_t = j->lam[(b * L + t) * D + d];
+        const double x_t = j->x[(b * L + t) * D + d];
+        const double *B_t = j->B + (b * L + t) * N;
+        const double *C_t = j->C + (b * L + t) * N;
+        double y_t = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const double Abar = exp(delta_t * j->A[d * N + n]);
+            const double u_t = B_t[n] * x_t;
+            h[n] = Abar * h[n] + (1.0 - lam_t) * delta_t * Abar * u_prev[n] + lam_t * delta_t * u_t;
+            u_prev[n] = u_t;
+            y_t += C_t[n] * h[n];
+        }
+        j->y[(b * L + t) * D + d] = y_t;
+    }
+    if (j->h_final)
+        for (int64_t n = 0; n < N; ++n)
+            j->h_final[(b * D + d) * N + n] = h[n];
+    free(h);
+    free(u_prev);
+}
+
+/* The same rule with the complex-valued state of scan_chain_complex. */
+static void scan_chain_trapezoid_complex(const scan_job *j, int64_t b, int64_t d)
+{
+    const int64_t L = j->L, D = j->D, N = j->N, K = N / 2;
+    double complex *h = (double complex *)malloc((size_t)K * sizeof(double complex));
+    double complex *u_prev = (double complex *)malloc((size_t)K * sizeof(double complex));
+    for (int64_t k = 0; k < K; ++k) {
+        h[k] = j->h0 ? j->h0[(b * D + d) * N + 2 * k] + I * j->h0[(b * D + d) * N + 2 * k + 1] : 0.0;
+        u_prev[k] = j->x_prev
+                        ? (j->B_prev[b * N + 2 * k] + I * j->B_prev[b * N + 2 * k + 1]) * j->x_prev[b * D + d]
+                        : 0.0;
+    }
+    for (int64_t t = 0; t < L; ++t) {
+        const double delta_t = j->delta[(b * L + t) * D + d];
+        const double lam_t = j->lam[(b * L + t) * D + d];
+        const double x_t = j->x[(b * L + t) * D + d];
+        const double *B_t = j->B + (b * L + t) * N;
+        const double *C_t = j->C + (b * L + t) * N;
+        double y_t = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double complex a = j->A[d * N + 2 * k] + I * j->A[d * N + 2 * k + 1];
+            const double complex Abar = cexp(delta_t * a);
+            const double complex u_t = (B_t[2 * k] + I * B_t[2 * k + 1]) * x_t;
+            const double complex ck = C_t[2 * k] + I * C_t[2 * k + 1];
+            h[k] = Abar * h[k] + (1.0 - lam_t) * delta_t * Abar * u_prev[k] + lam_t * delta_t * u_t;
+            u_prev[k] = u_t;
+            y_t += creal(conj(ck) * h[k]);
+        }
+        j->y[(b * L + t) * D + d] = y_t;
+    }
+    if (j->h_final)
+        for (int64_t k = 0; k < K; ++k) {
+            j->h_final[(b * D + d) * N + 2 * k] = creal(h[k]);
+            j->h_final[(b * D + d) * N + 2 * k + 1] = cimag(h[k]);
+        }
+    free(h);
+    free(u_prev);
+}
+
 static void *scan_worker(void *arg)
 {
     const scan_job *j = (const scan_job *)arg;
     for (int64_t item = j->item_begin; item < j->item_end; ++item) {
         const int64_t b = item / j->D, d = item % j->D;
-        if (j->cplx)
+        if (j->trap && j->cplx)
+            scan_chain_trapezoid_complex(j, b, d);
+        else if (j->trap)
+            scan_chain_trapezoid(j, b, d);
+        else if (j->cplx)
             scan_chain_complex(j, b, d);
         else if (j->chunk > 0)
             scan_chain_chunked(j, b, d);
@@ -300,6 +395,71 @@ int oracle_step_complex_f64(double *h, const double *x_t, const double *delta_t,
                 hk[0] = creal(hn);
                 hk[1] = cimag(hn);
                 acc += creal(conj(ck) * hn);
+            }
+            y_t[b * D + d] = acc;
+        }
+    }
+    return 0;
+}
+
+/*
+ * Prefill with the exponential-trapezoidal rule (scan_chain_trapezoid, or its complex form
+ * when cplx is set; N must then be even).  lam is [batch][L][D]; x_prev [batch][D] and
+ * B_prev [batch][N] are the token before the first one, both NULL when there is none.
+ */
+int oracle_prefill_trapezoid_f64(const double *x, const double *delta, const double *lam, const double *A,
+                                 const double *B, const double *C, const double *h0, const double *x_prev,
+                                 const double *B_prev, double *y, double *h_final, int64_t batch, int64_t L,
+                                 int64_t D, int64_t N, int cplx, int nthreads)
+{
+    if ((cplx && N % 2 != 0) || ((x_prev == NULL) != (B_prev == NULL)))
+        return -1;
+    scan_job j;
+    memset(&j, 0, sizeof j);
+    j.x = x; j.delta = delta; j.A = A; j.B = B; j.C = C; j.h0 = h0;
+    j.y = y; j.h_final = h_final;
+    j.batch = batch; j.L = L; j.D = D; j.N = N; j.chunk = 0; j.cplx = cplx;
+    j.trap = 1; j.lam = lam; j.x_prev = x_prev; j.B_prev = B_prev;
+    return run_scan(j, nthreads);
+}
+
+/*
+ * One decode step with the exponential-trapezoidal rule: the previous token's x_prev [batch][D]
+ * and B_prev [batch][N] enter as the step's left end point.  h [batch][D][N] is updated in place.
+ */
+int oracle_step_trapezoid_f64(double *h, const double *x_prev, const double *B_prev, const double *x_t,
+                              const double *delta_t, const double *lam_t, const double *A, const double *B_t,
+                              const double *C_t, double *y_t, int64_t batch, int64_t D, int64_t N, int cplx)
+{
+    if (cplx && N % 2 != 0)
+        return -1;
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < D; ++d) {
+            const double dl = delta_t[b * D + d], lm = lam_t[b * D + d];
+            const double xv = x_t[b * D + d], xp = x_prev[b * D + d];
+            double acc = 0.0;
+            if (cplx) {
+                for (int64_t k = 0; k < N / 2; ++k) {
+                    double *hk = &h[(b * D + d) * N + 2 * k];
+                    const double complex a = A[d * N + 2 * k] + I * A[d * N + 2 * k + 1];
+                    const double complex Abar = cexp(dl * a);
+                    const double complex up = (B_prev[b * N + 2 * k] + I * B_prev[b * N + 2 * k + 1]) * xp;
+                    const double complex ut = (B_t[b * N + 2 * k] + I * B_t[b * N + 2 * k + 1]) * xv;
+                    const double complex ck = C_t[b * N + 2 * k] + I * C_t[b * N + 2 * k + 1];
+                    const double complex hn =
+                        Abar * (hk[0] + I * hk[1]) + (1.0 - lm) * dl * Abar * up + lm * dl * ut;
+                    hk[0] = creal(hn);
+                    hk[1] = cimag(hn);
+                    acc += creal(conj(ck) * hn);
+                }
+            } else {
+                for (int64_t n = 0; n < N; ++n) {
+                    double *hn = &h[(b * D + d) * N + n];
+                    const double Abar = exp(dl * A[d * N + n]);
+                    *hn = Abar * *hn + (1.0 - lm) * dl * Abar * (B_prev[b * N + n] * xp) +
+                          lm * dl * (B_t[b * N + n] * xv);
+                    acc += C_t[b * N + n] * *hn;
+                }
             }
             y_t[b * D + d] = acc;
         }
