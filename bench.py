@@ -24,7 +24,10 @@ fused multiply-adds (3 slots) plus a sixteenth of the decay's product and expone
 (3/16): 3.1875 slots and 5.125 flops per element, a bound of 63.2 TFLOP/s.  With --complex-a
 (the complex-valued state of the Mamba-3 form) one complex state, two elements, takes 19
 slots and 21 flops per token (decay, rotation by a hardware sine and cosine, complex update,
-output): 9.5 slots and 10.5 flops per element, a bound of 43.4 TFLOP/s.
+output): 9.5 slots and 10.5 flops per element, a bound of 43.4 TFLOP/s.  --trapezoid (the
+exponential-trapezoidal rule of Mamba-3, with any of the three forms of A) adds one fused
+multiply-add per element, the previous token's input taken in before the decay: one slot and
+two flops more than the form's own count, and lam [B, L, D] to the bytes read.
 """
 from __future__ import annotations
 
@@ -53,6 +56,7 @@ SCALAR_A_FLOPS = 5 + 2 / 16
 # fract (2), cos and sin (4), r cos and r sin (2), two input products (2), four fma (4), y (2)
 COMPLEX_A_SLOTS = 19 / 2
 COMPLEX_A_FLOPS = 21 / 2
+TRAP_SLOTS, TRAP_FLOPS = 1, 2                 # the left end point's fma, on top of the form's count
 KERNEL_SOURCES = {
     "prefill": ["scan_update.h", "mfma_common.h", "prefill_rows_kernel.h"],
     "step": ["scan_update.h", "step_kernel.h"],
@@ -69,12 +73,16 @@ def kernel_source_hash(kind: str) -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(wl) -> int:
+def algorithmic_bytes(wl, trapezoid: bool = False) -> int:
+    """Bytes a step must move at least.  The trapezoidal rule also reads lam (like delta) and,
+    in decode, the previous token's x and B rows."""
     es = 4 if wl.dtype == "f32" else 2
     if wl.layers > 1:  # decode: state read + write, token rows in and out, A, per layer
         per_layer = 2 * wl.batch * wl.D * wl.N * 4 + 3 * wl.batch * wl.D * es + 2 * wl.batch * wl.N * es + wl.D * wl.N * 4
+        if trapezoid:
+            per_layer += 2 * wl.batch * wl.D * es + wl.batch * wl.N * es
         return per_layer * wl.layers
-    return (3 * wl.batch * wl.L * wl.D * es + 2 * wl.batch * wl.L * wl.N * es
+    return ((4 if trapezoid else 3) * wl.batch * wl.L * wl.D * es + 2 * wl.batch * wl.L * wl.N * es
             + wl.D * wl.N * 4 + wl.batch * wl.D * wl.N * 4)
 
 
@@ -98,10 +106,10 @@ def read_traffic(workload: str, launches_per_step: int):
         return None
 
 
-def cpu_baseline(wl, inp, channels: int, scalar_a=None, complex_a=False):
+def cpu_baseline(wl, inp, channels: int, scalar_a=None, complex_a=False, lam=None):
     """The fp64 oracle, as it stands, on a bounded sample: all tokens of `channels` channels
     (with `scalar_a`, the scaled-identity oracle on that A; with `complex_a`, the complex-state
-    oracle on inp["A"])."""
+    oracle on inp["A"]; with `lam`, the exponential-trapezoidal oracle)."""
     import numpy as np
 
     import oracle
@@ -113,7 +121,12 @@ def cpu_baseline(wl, inp, channels: int, scalar_a=None, complex_a=False):
     args = [np.ascontiguousarray(t.float().numpy(), dtype=np.float64) for t in (x, dl, A, inp["B"], inp["C"])]
     fn = oracle.prefill_complex if complex_a else oracle.prefill if scalar_a is None else oracle.prefill_scalar_a
     t0 = time.perf_counter()
-    fn(*args, nthreads=threads)
+    if lam is not None:
+        form = "complex" if complex_a else "diagonal" if scalar_a is None else "scalar"
+        lm = np.ascontiguousarray(lam[:, :, :channels].float().numpy(), dtype=np.float64)
+        oracle.prefill_trapezoid(args[0], args[1], lm, *args[2:], form=form, nthreads=threads)
+    else:
+        fn(*args, nthreads=threads)
     dt = time.perf_counter() - t0
     elems = wl.batch * wl.L * channels
     return {"value": elems / dt, "unit": "elems/s", "cores": threads, "kind": "oracle",
@@ -143,6 +156,9 @@ def main():
     ap.add_argument("--complex-a", action="store_true",
                     help="complex-valued state, pairs of the 16 states as 8 complex states (the Mamba-3 form): "
                          "jscan_prefill_complex / jscan_step_complex")
+    ap.add_argument("--trapezoid", action="store_true",
+                    help="the exponential-trapezoidal rule (the Mamba-3 discretisation), with the diagonal A or "
+                         "with --scalar-a / --complex-a: jscan_prefill_trapezoid / jscan_step_trapezoid")
     ap.add_argument("--cpu-channels", type=int, default=8192,
                     help="oracle sample: all tokens of the first CPU_CHANNELS channels (default: every channel "
                          "of the 64K workload, a few seconds on 16 cores; 0 = skip)")
@@ -183,8 +199,9 @@ def main():
                           "ms_per_launch": ms, "GBps": 2 * n * 4 / ms / 1e6}), flush=True)
         return
     wl = workloads.get(args.workload)
-    if (args.scalar_a or args.complex_a) and (args.producer or args.chunked):
-        print("bench.py: --scalar-a and --complex-a run the plain prefill or decode step only", file=sys.stderr)
+    if (args.scalar_a or args.complex_a or args.trapezoid) and (args.producer or args.chunked):
+        print("bench.py: --scalar-a, --complex-a and --trapezoid run the plain prefill or decode step only",
+              file=sys.stderr)
         sys.exit(2)
     if args.scalar_a and args.complex_a:
         print("bench.py: choose one of --scalar-a and --complex-a", file=sys.stderr)
@@ -192,11 +209,18 @@ def main():
     torch.cuda.set_device(dev)
     log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)  # noqa: E731
 
+    form = "scalar" if args.scalar_a else "complex" if args.complex_a else "diagonal"
     t0 = time.perf_counter()
     if wl.layers > 1:
         layers = []
         for layer in range(wl.layers):
-            inp = workloads.decode_layer_inputs(wl, layer)
+            # the trapezoidal rule's step is token 1, with token 0 as its previous token
+            inp = workloads.decode_layer_inputs(wl, layer, token=1 if args.trapezoid else 0)
+            if args.trapezoid:
+                prev = workloads.decode_layer_inputs(wl, layer, token=0)
+                inp["x_prev"], inp["B_prev"] = prev["x"], prev["B"]
+            else:
+                inp.pop("lam")
             if args.scalar_a:
                 inp["A"] = workloads.draw_scalar_a(wl, layer=layer)
             if args.complex_a:
@@ -210,7 +234,11 @@ def main():
 
         def token_step():
             for L_ in layers:
-                step_fn(L_["h"], L_["x"], L_["delta"], L_["A"], L_["B"], L_["C"], y_t=L_["y"])
+                if args.trapezoid:
+                    jscan.step_trapezoid(L_["h"], L_["x_prev"], L_["B_prev"], L_["x"], L_["delta"], L_["lam"],
+                                         L_["A"], L_["B"], L_["C"], form=form, y_t=L_["y"])
+                else:
+                    step_fn(L_["h"], L_["x"], L_["delta"], L_["A"], L_["B"], L_["C"], y_t=L_["y"])
 
         # One token step is 28 short launches; a captured HIP graph replays them without the
         # host launch overhead of 28 separate calls.
@@ -270,6 +298,20 @@ def main():
             def one_step():
                 jscan.prefill_chunked(d["x"], d["delta"], d["A"], d["B"], d["C"], y=y, h_final=h, workspace=ws)
             launches = 3 if ws_bytes > 0 else 1
+        elif args.trapezoid:
+            host_inp["lam"] = workloads.lam_inputs(wl)
+            d["lam"] = host_inp["lam"].to(dev)
+            if args.scalar_a:
+                host_a = workloads.draw_scalar_a(wl)
+                d["A"] = host_a.to(dev)
+            elif args.complex_a:
+                host_inp["A"] = workloads.draw_complex_a(wl)
+                d["A"] = host_inp["A"].to(dev)
+
+            def one_step():
+                jscan.prefill_trapezoid(d["x"], d["delta"], d["lam"], d["A"], d["B"], d["C"], form=form, y=y,
+                                        h_final=h)
+            launches = 1
         elif args.complex_a:
             host_inp["A"] = workloads.draw_complex_a(wl)
             d["A"] = host_inp["A"].to(dev)
@@ -309,7 +351,7 @@ def main():
 
     elems = wl.elems
     value = elems / (ms_step * 1e-3)
-    alg_bytes = algorithmic_bytes(wl)
+    alg_bytes = algorithmic_bytes(wl, args.trapezoid)
     if args.scalar_a:   # A is [D] instead of [D, N]
         alg_bytes -= (wl.D * wl.N - wl.D) * 4 * max(wl.layers, 1)
     gbps = alg_bytes / (ms_step * 1e-3) / 1e9
@@ -355,12 +397,15 @@ def main():
         slots, flops = ((SCALAR_A_SLOTS, SCALAR_A_FLOPS) if args.scalar_a else
                         (COMPLEX_A_SLOTS, COMPLEX_A_FLOPS) if args.complex_a else
                         (SLOTS_PER_STATE_ELEM, FLOPS_PER_STATE_ELEM))
+        if args.trapezoid:
+            slots, flops = slots + TRAP_SLOTS, flops + TRAP_FLOPS
         achieved_tf = state_elems * flops / (per_launch_ms * 1e-3) / 1e12
         peak_tf = VALU_SLOTS_PER_S / slots * flops / 1e12
         roofline = {"bound": "alu", "achieved": round(achieved_tf, 2), "peak": round(peak_tf, 2), "unit": "TFLOP/s",
                     "frac": round(achieved_tf / peak_tf, 4)}
     roofline["traffic"] = None if (args.chunked or args.producer) else read_traffic(
-        wl.name + ("_scalar_a" if args.scalar_a else "_complex_a" if args.complex_a else ""), launches)
+        wl.name + ("_scalar_a" if args.scalar_a else "_complex_a" if args.complex_a else "")
+        + ("_trapezoid" if args.trapezoid else ""), launches)
 
     out = {
         "metric": METRIC,
@@ -378,6 +423,7 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "L": wl.L, "D": wl.D, "N": wl.N,
                    "layers": wl.layers, "io_dtype": wl.dtype, "state_dtype": "f32",
                    "A": "scaled_identity" if args.scalar_a else "complex_pairs" if args.complex_a else "diagonal",
+                   "discretisation": "exponential-trapezoidal" if args.trapezoid else "euler",
                    "path": ("producer+fused-scan" if args.fused else "producer+scan") if args.producer
                    else ("time-parallel" if args.chunked else "sequential")},
         "hbm_GBps": round(gbps, 1),
@@ -389,7 +435,8 @@ def main():
         out["producer"] = producer_info
     if host_inp is not None and args.cpu_channels > 0 and wl.layers == 1:
         out["cpu_baseline"] = cpu_baseline(wl, host_inp, min(args.cpu_channels, wl.D),
-                                           host_a if args.scalar_a else None, complex_a=args.complex_a)
+                                           host_a if args.scalar_a else None, complex_a=args.complex_a,
+                                           lam=host_inp.get("lam") if args.trapezoid else None)
         log(f"oracle sample: {out['cpu_baseline']['sample']}")
     print(json.dumps(out), flush=True)
 

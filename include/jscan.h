@@ -47,6 +47,7 @@
  *                      jscan_prefill_resume)
  *     JSCAN_ERR_HIP    the launch failed; jscan_last_hip_error() gives the hipError_t
  *     JSCAN_ERR_WORKSPACE  the workspace passed to jscan_prefill_chunked is too small
+ *     JSCAN_ERR_FORM   unknown form of A (jscan_a_form)
  * Faults inside a kernel surface at the caller's next synchronisation.  A is not
  * range-checked.  With delta >= 0 and A <= 0 the decay lies in (0, 1] and the recurrence
  * is stable; other values may overflow.  Zero-sized work (batch == 0 or D == 0) returns
@@ -69,7 +70,8 @@ typedef enum {
     JSCAN_ERR_ALIGN = 4,
     JSCAN_ERR_ALIAS = 5,
     JSCAN_ERR_HIP = 6,
-    JSCAN_ERR_WORKSPACE = 7
+    JSCAN_ERR_WORKSPACE = 7,
+    JSCAN_ERR_FORM = 8
 } jscan_status;
 
 /* dtype of x, delta, B, C and y.  A and every state are always fp32. */
@@ -260,6 +262,53 @@ jscan_status jscan_step_complex(float *h, const void *x_t, const void *delta_t, 
                                 int64_t D, int64_t N, int64_t ld_xd, int64_t ld_bc,
                                 jscan_dtype dtype, void *stream);
 
+/*
+ * Exponential-trapezoidal discretisation, the Mamba-3 replacement of the Euler rule (lesson
+ * page "Jamba - Hybrid SSM-Transformer", section "Mamba-3", item 1: the input term of the
+ * recurrence mixes neighbouring tokens).  The input integral over step t is weighted lam_t at
+ * the step's right end (this token) and 1 - lam_t at its left end (the previous token), which
+ * decays with the state over the step:
+ *
+ *     h_t = exp(delta_t a) (h_{t-1} + ((1 - lam_t) delta_t) x_{t-1} B_{t-1}) + ((lam_t delta_t) x_t) B_t
+ *
+ * in fp32 as k = fmaf(p, B_{t-1}, h), p = ((1 - lam) * delta) * x_{t-1}, then the form's usual
+ * update of k with q = (lam * delta) * x_t in place of delta * x_t.  y_t = C_t h_t as before.
+ * lam = 1 is the Euler rule of the other entry points, bit for bit.  lam_t in [0, 1] is
+ * expected (not checked).  The rule combines with every form of A:
+ *     JSCAN_A_DIAGONAL         A [D][N]: the Mamba-1 form of jscan_prefill
+ *     JSCAN_A_SCALED_IDENTITY  a [D]: the Mamba-2 form of jscan_prefill_scalar_a
+ *     JSCAN_A_COMPLEX          A [D][N] as (real, imaginary) pairs: jscan_prefill_complex
+ */
+typedef enum { JSCAN_A_DIAGONAL = 0, JSCAN_A_SCALED_IDENTITY = 1, JSCAN_A_COMPLEX = 2 } jscan_a_form;
+
+/*
+ * Prefill with the exponential-trapezoidal rule, from h0 (NULL: zero state).
+ *   lam     [batch][L][D], the dtype of x: the right-end weight of each (token, channel).
+ *   x_prev  [batch][D] and B_prev [batch][N], the dtype of x: the token before the first one,
+ *           whose input is the first step's left end point.  Both NULL when the sequence
+ *           starts here (that term is then zero); a resumed sequence passes its last token.
+ * Other arguments, layouts, errors and the bit-identity of h_final with the step chain are
+ * as for jscan_prefill_resume (with jscan_step_trapezoid as the step).  Added errors:
+ * JSCAN_ERR_NULL when lam is NULL or only one of x_prev and B_prev is, JSCAN_ERR_FORM for an
+ * unknown a_form, JSCAN_ERR_ALIAS when y or h_final overlaps lam, x_prev or B_prev.
+ */
+jscan_status jscan_prefill_trapezoid(const void *x, const void *delta, const void *lam, const float *A,
+                                     const void *B, const void *C, const float *h0, const void *x_prev,
+                                     const void *B_prev, void *y, float *h_final, int64_t batch, int64_t L,
+                                     int64_t D, int64_t N, jscan_a_form a_form, jscan_dtype dtype,
+                                     void *stream);
+
+/*
+ * Decode step with the exponential-trapezoidal rule.  x_prev (rows of D, stride ld_xd) and
+ * B_prev (rows of N, stride ld_bc) are the previous token's x and B, required: zeros for a
+ * sequence's first token.  lam_t has the rows of x_t.  Otherwise as jscan_step (h in place).
+ */
+jscan_status jscan_step_trapezoid(float *h, const void *x_prev, const void *B_prev, const void *x_t,
+                                  const void *delta_t, const void *lam_t, const float *A, const void *B_t,
+                                  const void *C_t, void *y_t, int64_t batch, int64_t D, int64_t N,
+                                  int64_t ld_xd, int64_t ld_bc, jscan_a_form a_form, jscan_dtype dtype,
+                                  void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *jscan_status_string(jscan_status s);
 
@@ -268,7 +317,7 @@ int jscan_last_hip_error(void);
 
 /* Library ABI version: 100 * major + minor (101 adds the time-parallel prefill, 102 the
  * producer side, 103 the fused prefill, 104 the scaled-identity A entry points, 105 the
- * complex-valued state). */
+ * complex-valued state, 106 the exponential-trapezoidal rule). */
 int jscan_version(void);
 
 #ifdef __cplusplus

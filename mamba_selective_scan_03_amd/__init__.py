@@ -14,8 +14,11 @@ There is no CPU fallback: without the built library every call raises.
     y_t = step_scalar_a(h, x_t, delta_t, a, B_t, C_t)
     y, h_final = prefill_complex(x, delta, A, B, C)        # complex-valued state (pairs of states)
     y_t = step_complex(h, x_t, delta_t, A, B_t, C_t)
+    y, h_final = prefill_trapezoid(x, delta, lam, A, B, C, form="diagonal")   # exponential-trapezoidal rule
+    y_t = step_trapezoid(h, x_prev, B_prev, x_t, delta_t, lam_t, A, B_t, C_t)
 """
 from ._binding import (  # noqa: F401
+    A_FORMS,
     D_STATE,
     JScanError,
     chunked_workspace_bytes,
@@ -26,9 +29,11 @@ from ._binding import (  # noqa: F401
     prefill_complex,
     prefill_fused,
     prefill_scalar_a,
+    prefill_trapezoid,
     ssm_inputs,
     step,
     step_complex,
     step_raw,
     step_scalar_a,
+    step_trapezoid,
 )

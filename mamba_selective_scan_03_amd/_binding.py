@@ -53,9 +53,12 @@ def library():
     lib.jscan_step_scalar_a.argtypes = [fp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
     lib.jscan_prefill_complex.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, i32, vp]
     lib.jscan_step_complex.argtypes = [fp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+    lib.jscan_prefill_trapezoid.argtypes = [vp, vp, vp, fp, vp, vp, fp, vp, vp, vp, fp, i64, i64, i64, i64, i32, i32, vp]
+    lib.jscan_step_trapezoid.argtypes = [fp, vp, vp, vp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp]
     lib.jscan_prefill_chunked_workspace.restype = i64
     for f in (lib.jscan_prefill, lib.jscan_prefill_resume, lib.jscan_step, lib.jscan_prefill_chunked,
-              lib.jscan_prefill_scalar_a, lib.jscan_step_scalar_a, lib.jscan_prefill_complex, lib.jscan_step_complex):
+              lib.jscan_prefill_scalar_a, lib.jscan_step_scalar_a, lib.jscan_prefill_complex, lib.jscan_step_complex,
+              lib.jscan_prefill_trapezoid, lib.jscan_step_trapezoid):
         f.restype = i32
     lib.jscan_status_string.argtypes = [i32]
     lib.jscan_status_string.restype = ctypes.c_char_p
@@ -308,4 +311,76 @@ def step(h, x_t, delta_t, A, B_t, C_t, y_t=None, _scalar_a=False, _complex_a=Fal
     with torch.cuda.device(h.device):
         step_raw(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, x_t.dtype, scalar_a=_scalar_a,
                  complex_a=_complex_a)
+    return y_t
+
+
+# ---- exponential-trapezoidal rule ----------------------------------------------------------
+# jscan_a_form values: the form of A that the trapezoidal entry points take.
+A_FORMS = {"diagonal": 0, "scalar": 1, "complex": 2}
+
+
+def prefill_trapezoid(x, delta, lam, A, B, C, h0=None, x_prev=None, B_prev=None, form="diagonal", y=None,
+                      h_final=None):
+    """Prefill with the exponential-trapezoidal rule (``jscan_prefill_trapezoid``).  ``lam``
+    ``[batch, L, D]`` (x's dtype) weights each step's right end; the left end, the previous
+    token's input, gets ``1 - lam`` and decays over the step.  ``x_prev [batch, D]`` and
+    ``B_prev [batch, 16]`` are the token before the first (omit both for a fresh sequence).
+    ``form``: "diagonal" (A ``[D, 16]``), "scalar" (a ``[D]``) or "complex" (A ``[D, 16]`` as
+    (real, imaginary) pairs).  Other arguments and results as for :func:`prefill`."""
+    _require(form in A_FORMS, f"form must be one of {tuple(A_FORMS)}")
+    batch, L, D = _check_prefill_args(x, delta, A, B, C, h0, scalar_a=form == "scalar")
+    _require(tuple(lam.shape) == (batch, L, D) and lam.dtype == x.dtype and lam.is_contiguous()
+             and lam.device == x.device, "lam must be a contiguous [batch, L, D] tensor like x")
+    _require((x_prev is None) == (B_prev is None), "x_prev and B_prev go together")
+    if x_prev is not None:
+        for name, t, shape in (("x_prev", x_prev, (batch, D)), ("B_prev", B_prev, (batch, D_STATE))):
+            _require(tuple(t.shape) == shape and t.dtype == x.dtype and t.is_contiguous() and t.device == x.device,
+                     f"{name} must be a contiguous {shape} tensor like x")
+    if y is None:
+        y = torch.empty_like(x)
+    if h_final is None:
+        h_final = torch.empty((batch, D, D_STATE), dtype=torch.float32, device=x.device)
+    lib = library()
+    with torch.cuda.device(x.device):
+        st = lib.jscan_prefill_trapezoid(_ptr(x), _ptr(delta), _ptr(lam), _ptr(A), _ptr(B), _ptr(C), _ptr(h0),
+                                         _ptr(x_prev), _ptr(B_prev), _ptr(y), _ptr(h_final), batch, L, D, D_STATE,
+                                         A_FORMS[form], _DTYPES[x.dtype], _stream(x.device))
+    _check(st)
+    return y, h_final
+
+
+def step_trapezoid(h, x_prev, B_prev, x_t, delta_t, lam_t, A, B_t, C_t, form="diagonal", y_t=None):
+    """One decode token with the exponential-trapezoidal rule (``jscan_step_trapezoid``): as
+    :func:`step`, plus the previous token's ``x_prev [batch, D]`` and ``B_prev [batch, 16]``
+    (zeros before a sequence's first token) and this token's ``lam_t [batch, D]``.  x_prev and
+    lam_t share x_t's row stride, B_prev shares B_t's."""
+    _require(form in A_FORMS, f"form must be one of {tuple(A_FORMS)}")
+    _require(h.is_cuda and h.dtype == torch.float32 and h.dim() == 3 and h.shape[2] == D_STATE and h.is_contiguous(),
+             "h must be a contiguous fp32 [batch, D, 16] CUDA tensor")
+    batch, D, _ = h.shape
+    _require(x_t.dtype in _DTYPES, "x_t must be bfloat16 or float32")
+    ld_xd = x_t.stride(0) if batch > 1 else D
+    ld_bc = B_t.stride(0) if batch > 1 else D_STATE
+    for name, t, shape, ld in (("x_t", x_t, (batch, D), ld_xd), ("delta_t", delta_t, (batch, D), ld_xd),
+                               ("lam_t", lam_t, (batch, D), ld_xd), ("x_prev", x_prev, (batch, D), ld_xd),
+                               ("B_t", B_t, (batch, D_STATE), ld_bc), ("C_t", C_t, (batch, D_STATE), ld_bc),
+                               ("B_prev", B_prev, (batch, D_STATE), ld_bc)):
+        _require(tuple(t.shape) == shape, f"{name} must have shape {shape}")
+        _require(t.dtype == x_t.dtype, f"{name} must be {x_t.dtype}")
+        _require(t.stride(1) == 1 and (batch <= 1 or t.stride(0) == ld), f"{name} rows must be contiguous with "
+                 f"the row stride of {'x_t' if ld is ld_xd else 'B_t'}")
+        _require(t.device == h.device, f"{name} is on another device")
+    a_shape = (D,) if form == "scalar" else (D, D_STATE)
+    _require(A.dtype == torch.float32 and tuple(A.shape) == a_shape and A.is_contiguous(),
+             f"A must be a contiguous fp32 tensor of shape {a_shape}")
+    if y_t is None:
+        y_t = torch.empty((batch, ld_xd), dtype=x_t.dtype, device=h.device)[:, :D]
+    _require(tuple(y_t.shape) == (batch, D) and y_t.dtype == x_t.dtype and y_t.stride(1) == 1
+             and (batch <= 1 or y_t.stride(0) == ld_xd), "y_t must be [batch, D] with x_t's row stride")
+    lib = library()
+    with torch.cuda.device(h.device):
+        st = lib.jscan_step_trapezoid(_ptr(h), _ptr(x_prev), _ptr(B_prev), _ptr(x_t), _ptr(delta_t), _ptr(lam_t),
+                                      _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(y_t), batch, D, D_STATE, ld_xd, ld_bc,
+                                      A_FORMS[form], _DTYPES[x_t.dtype], _stream(h.device))
+    _check(st)
     return y_t

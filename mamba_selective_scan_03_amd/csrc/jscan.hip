@@ -49,30 +49,31 @@ jscan_status launch_status() {
 constexpr int64_t kMaxBlocks = (int64_t)1 << 30;
 
 // Scans `nrows` rows (see Segments) with the row-mapped kernel when it applies, otherwise
-// with one lane per (row, channel).  AF: the form of A.
-template <typename E, bool kSummary, jscan::AForm AF = jscan::AForm::Diagonal>
+// with one lane per (row, channel).  AF: the form of A; kTrap: the trapezoidal rule (inputs tr).
+template <typename E, bool kSummary, jscan::AForm AF = jscan::AForm::Diagonal, bool kTrap = false>
 void launch_rows(const void *x, const void *delta, const float *A, const void *B, const void *C, const float *h0,
                  void *y, float *h_final, float *dsum, const jscan::Segments &sg, int64_t nrows, int64_t D,
-                 hipStream_t stream) {
+                 hipStream_t stream, jscan::Trap tr = jscan::Trap{nullptr, nullptr, nullptr}) {
     using T = typename E::store_t;
     const T *xt = static_cast<const T *>(x), *dt = static_cast<const T *>(delta);
     const T *bt = static_cast<const T *>(B), *ct = static_cast<const T *>(C);
     T *yt = static_cast<T *>(y);
     if (jscan::rows_kernel_applies(nrows, D)) {
-        jscan::launch_prefill_rows<E, kSummary, false, AF>(xt, dt, A, bt, ct, h0, yt, h_final, dsum, sg, nrows,
-                                                                  (int)D, stream);
+        jscan::launch_prefill_rows<E, kSummary, false, AF, kTrap>(xt, dt, A, bt, ct, h0, yt, h_final, dsum, sg,
+                                                                  nrows, (int)D, stream,
+                                                                  jscan::DeltaProj{nullptr, nullptr, nullptr}, tr);
         return;
     }
     const int blocks_per_row = (int)((D + 63) / 64);
-    hipLaunchKernelGGL((jscan::prefill_lane_kernel<E, kSummary, AF>), dim3((unsigned)(nrows * blocks_per_row)), dim3(64),
-                       0, stream, xt, dt, A, bt, ct, h0, yt, h_final, dsum, sg, (int)D, blocks_per_row);
+    hipLaunchKernelGGL((jscan::prefill_lane_kernel<E, kSummary, AF, kTrap>), dim3((unsigned)(nrows * blocks_per_row)),
+                       dim3(64), 0, stream, xt, dt, A, bt, ct, h0, yt, h_final, dsum, sg, (int)D, blocks_per_row, tr);
 }
 
 // Token-by-token prefill of whole sequences (one row per sequence).
-template <typename E, jscan::AForm AF = jscan::AForm::Diagonal>
+template <typename E, jscan::AForm AF = jscan::AForm::Diagonal, bool kTrap = false>
 jscan_status launch_prefill(const void *x, const void *delta, const float *A, const void *B, const void *C,
                             const float *h0, void *y, float *h_final, int64_t batch, int64_t L, int64_t D,
-                            hipStream_t stream) {
+                            hipStream_t stream, jscan::Trap tr = jscan::Trap{nullptr, nullptr, nullptr}) {
     if (L == 0) {
         const int64_t count = batch * D * jscan::kDState;
         const int64_t blocks = (count + 255) / 256;
@@ -80,7 +81,7 @@ jscan_status launch_prefill(const void *x, const void *delta, const float *A, co
         return launch_status();
     }
     const jscan::Segments sg{L, L, 1, 0};
-    launch_rows<E, false, AF>(x, delta, A, B, C, h0, y, h_final, nullptr, sg, batch, D, stream);
+    launch_rows<E, false, AF, kTrap>(x, delta, A, B, C, h0, y, h_final, nullptr, sg, batch, D, stream, tr);
     return launch_status();
 }
 
@@ -148,6 +149,29 @@ jscan_status prefill_impl(const void *x, const void *delta, const float *A, cons
     if (dtype == JSCAN_BF16)
         return launch_prefill<jscan::BF16>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s);
     return launch_prefill<jscan::F32>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s);
+}
+
+// ---- exponential-trapezoidal rule --------------------------------------------------------
+
+template <typename E>
+jscan_status launch_prefill_trap(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                                 const float *h0, void *y, float *h_final, int64_t batch, int64_t L, int64_t D,
+                                 hipStream_t s, jscan::AForm af, jscan::Trap tr) {
+    using jscan::AForm;
+    if (af == AForm::ScaledIdentity)
+        return launch_prefill<E, AForm::ScaledIdentity, true>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s, tr);
+    if (af == AForm::ComplexPairs)
+        return launch_prefill<E, AForm::ComplexPairs, true>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s, tr);
+    return launch_prefill<E, AForm::Diagonal, true>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s, tr);
+}
+
+bool form_of(jscan_a_form f, jscan::AForm *af) {
+    switch (f) {
+    case JSCAN_A_DIAGONAL: *af = jscan::AForm::Diagonal; return true;
+    case JSCAN_A_SCALED_IDENTITY: *af = jscan::AForm::ScaledIdentity; return true;
+    case JSCAN_A_COMPLEX: *af = jscan::AForm::ComplexPairs; return true;
+    }
+    return false;
 }
 
 // ---- time-parallel prefill ---------------------------------------------------------------
@@ -231,24 +255,50 @@ void launch_ssm_inputs(const uint16_t *x, const uint16_t *w_x, const float *g_d,
 
 // ---- decode step -----------------------------------------------------------------------
 
-template <typename E, jscan::AForm AF>
+// tr: the trapezoidal rule's lam_t, x_prev and B_prev (rows like x_t, x_t and B_t), when kTrap.
+template <typename E, jscan::AForm AF, bool kTrap = false>
 jscan_status launch_step(float *h, const void *x_t, const void *delta_t, const float *A,
                          const void *B_t, const void *C_t, void *y_t, int64_t batch, int64_t D,
-                         int64_t ld_xd, int64_t ld_bc, hipStream_t stream) {
+                         int64_t ld_xd, int64_t ld_bc, hipStream_t stream,
+                         jscan::Trap tr = jscan::Trap{nullptr, nullptr, nullptr}) {
     using T = typename E::store_t;
     const int blocks_per_rows = (int)((D * 4 + 255) / 256);
     const int64_t row_groups = (batch + jscan::step::kRows - 1) / jscan::step::kRows;
-    hipLaunchKernelGGL((jscan::step_kernel<E, AF>), dim3((unsigned)(row_groups * blocks_per_rows)), dim3(256), 0, stream,
-                       h, static_cast<const T *>(x_t), static_cast<const T *>(delta_t), A,
+    hipLaunchKernelGGL((jscan::step_kernel<E, AF, kTrap>), dim3((unsigned)(row_groups * blocks_per_rows)), dim3(256), 0,
+                       stream, h, static_cast<const T *>(x_t), static_cast<const T *>(delta_t), A,
                        static_cast<const T *>(B_t), static_cast<const T *>(C_t), static_cast<T *>(y_t), (int)batch,
-                       (int)D, blocks_per_rows, ld_xd, ld_bc);
+                       (int)D, blocks_per_rows, ld_xd, ld_bc, static_cast<const T *>(tr.lam),
+                       static_cast<const T *>(tr.x_prev), static_cast<const T *>(tr.B_prev));
     return launch_status();
 }
 
+template <typename E>
+jscan_status dispatch_step_trap_e(float *h, const void *x_t, const void *delta_t, const float *A, const void *B_t,
+                                  const void *C_t, void *y_t, int64_t batch, int64_t D, int64_t ld_xd, int64_t ld_bc,
+                                  hipStream_t s, jscan::AForm af, jscan::Trap tr) {
+    using jscan::AForm;
+    if (af == AForm::ScaledIdentity)
+        return launch_step<E, AForm::ScaledIdentity, true>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc,
+                                                           s, tr);
+    if (af == AForm::ComplexPairs)
+        return launch_step<E, AForm::ComplexPairs, true>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s,
+                                                         tr);
+    return launch_step<E, AForm::Diagonal, true>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s, tr);
+}
+jscan_status dispatch_step_trap(float *h, const void *x_t, const void *delta_t, const float *A, const void *B_t,
+                                const void *C_t, void *y_t, int64_t batch, int64_t D, int64_t ld_xd, int64_t ld_bc,
+                                jscan_dtype dtype, hipStream_t s, jscan::AForm af, jscan::Trap tr) {
+    if (dtype == JSCAN_BF16)
+        return dispatch_step_trap_e<jscan::BF16>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s, af, tr);
+    return dispatch_step_trap_e<jscan::F32>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s, af, tr);
+}
+
 // Checks and launch shared by the decode-step entry points.  af: the form of A.
+// With tr.lam set, the trapezoidal rule: lam_t and x_prev have the rows of x_t, B_prev those of B_t.
 jscan_status step_impl(float *h, const void *x_t, const void *delta_t, const float *A, const void *B_t, const void *C_t,
                        void *y_t, int64_t batch, int64_t D, int64_t N, int64_t ld_xd, int64_t ld_bc, jscan_dtype dtype,
-                       void *stream, jscan::AForm af) {
+                       void *stream, jscan::AForm af, jscan::Trap tr = jscan::Trap{nullptr, nullptr, nullptr},
+                       bool trap = false) {
     using jscan::AForm;
     if (dtype != JSCAN_F32 && dtype != JSCAN_BF16) return JSCAN_ERR_DTYPE;
     if (batch < 0 || D < 0 || N != JSCAN_D_STATE || D % 8 != 0) return JSCAN_ERR_SHAPE;
@@ -258,9 +308,13 @@ jscan_status step_impl(float *h, const void *x_t, const void *delta_t, const flo
     if (batch == 0 || D == 0) return JSCAN_OK;
     if (ld_xd < D || ld_bc < N || ld_xd % 8 != 0 || ld_bc % 8 != 0) return JSCAN_ERR_SHAPE;
     if (!h || !x_t || !delta_t || !A || !B_t || !C_t || !y_t) return JSCAN_ERR_NULL;
+    if (trap && (!tr.lam || !tr.x_prev || !tr.B_prev)) return JSCAN_ERR_NULL;
     const void *arrays[] = {h, x_t, delta_t, A, B_t, C_t, y_t};
     for (const void *p : arrays)
         if (!aligned16(p)) return JSCAN_ERR_ALIGN;
+    const void *extra[] = {tr.lam, tr.x_prev, tr.B_prev};
+    for (const void *p : extra)
+        if (p && !aligned16(p)) return JSCAN_ERR_ALIGN;
 
     const int64_t es = elem_bytes(dtype);
     const int64_t rows_xd = ((batch - 1) * ld_xd + D) * es, rows_bc = ((batch - 1) * ld_bc + N) * es;
@@ -270,8 +324,14 @@ jscan_status step_impl(float *h, const void *x_t, const void *delta_t, const flo
     for (const Span &s : inputs)
         if (overlaps(sy, s) || overlaps(sh, s)) return JSCAN_ERR_ALIAS;
     if (overlaps(sy, sh)) return JSCAN_ERR_ALIAS;
+    if (trap) {
+        const Span more[] = {span(tr.lam, rows_xd), span(tr.x_prev, rows_xd), span(tr.B_prev, rows_bc)};
+        for (const Span &s : more)
+            if (overlaps(sy, s) || overlaps(sh, s)) return JSCAN_ERR_ALIAS;
+    }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (trap) return dispatch_step_trap(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, dtype, s, af, tr);
     if (af == AForm::ScaledIdentity) {
         if (dtype == JSCAN_BF16)
             return launch_step<jscan::BF16, AForm::ScaledIdentity>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd,
@@ -381,6 +441,43 @@ jscan_status jscan_step_complex(float *h, const void *x_t, const void *delta_t, 
                      jscan::AForm::ComplexPairs);
 }
 
+jscan_status jscan_prefill_trapezoid(const void *x, const void *delta, const void *lam, const float *A, const void *B,
+                                     const void *C, const float *h0, const void *x_prev, const void *B_prev, void *y,
+                                     float *h_final, int64_t batch, int64_t L, int64_t D, int64_t N,
+                                     jscan_a_form a_form, jscan_dtype dtype, void *stream) {
+    jscan::AForm af;
+    if (!form_of(a_form, &af)) return JSCAN_ERR_FORM;
+    bool empty = false;
+    const jscan_status st = check_prefill(x, delta, A, B, C, h0, false, y, h_final, batch, L, D, N, dtype, &empty, af);
+    if (st != JSCAN_OK || empty) return st;
+    if ((L > 0 && !lam) || ((x_prev == nullptr) != (B_prev == nullptr))) return JSCAN_ERR_NULL;
+    const void *more[] = {lam, x_prev, B_prev};
+    for (const void *p : more)
+        if (p && !aligned16(p)) return JSCAN_ERR_ALIGN;
+    const int64_t es = elem_bytes(dtype);
+    const Span outs[] = {span(y, L > 0 ? batch * L * D * es : 0), span(h_final, batch * D * N * 4)};
+    const Span ins[] = {span(lam, L > 0 ? batch * L * D * es : 0), span(x_prev, batch * D * es),
+                        span(B_prev, batch * N * es)};
+    for (const Span &o : outs)
+        for (const Span &i : ins)
+            if (overlaps(o, i)) return JSCAN_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const jscan::Trap tr{lam, x_prev, B_prev};
+    if (dtype == JSCAN_BF16)
+        return launch_prefill_trap<jscan::BF16>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s, af, tr);
+    return launch_prefill_trap<jscan::F32>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s, af, tr);
+}
+
+jscan_status jscan_step_trapezoid(float *h, const void *x_prev, const void *B_prev, const void *x_t,
+                                  const void *delta_t, const void *lam_t, const float *A, const void *B_t,
+                                  const void *C_t, void *y_t, int64_t batch, int64_t D, int64_t N, int64_t ld_xd,
+                                  int64_t ld_bc, jscan_a_form a_form, jscan_dtype dtype, void *stream) {
+    jscan::AForm af;
+    if (!form_of(a_form, &af)) return JSCAN_ERR_FORM;
+    return step_impl(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, N, ld_xd, ld_bc, dtype, stream, af,
+                     jscan::Trap{lam_t, x_prev, B_prev}, true);
+}
+
 jscan_status jscan_ssm_inputs(const void *x, const void *w_x, const float *g_delta, const float *g_B,
                               const float *g_C, const void *w_dt, const float *b_dt, void *delta_low, void *delta,
                               void *B, void *C, int64_t M, int64_t D, int64_t R, int64_t N, float eps,
@@ -466,12 +563,13 @@ const char *jscan_status_string(jscan_status s) {
     case JSCAN_ERR_ALIAS: return "an output overlaps an input or another output";
     case JSCAN_ERR_HIP: return "HIP launch failed (see jscan_last_hip_error)";
     case JSCAN_ERR_WORKSPACE: return "workspace smaller than jscan_prefill_chunked_workspace() bytes";
+    case JSCAN_ERR_FORM: return "unknown form of A";
     }
     return "unknown status";
 }
 
 int jscan_last_hip_error(void) { return g_last_hip_error; }
 
-int jscan_version(void) { return 105; }
+int jscan_version(void) { return 106; }
 
 }  // extern "C"

@@ -16,20 +16,22 @@ namespace jscan {
 // when h0 is null).  A segment-summary launch (kSummary) writes no y; it writes the row's
 // final state and the sum of the row's delta values to dsum[row][D].  With a scaled-identity
 // A (AF), A is a[D] and the channel's one decay per token serves all 16 states; with a complex
-// state, states 2k and 2k+1 form one complex state advanced by advance_complex().
-template <typename E, bool kSummary, AForm AF = AForm::Diagonal>
+// state, states 2k and 2k+1 form one complex state advanced by advance_complex().  With the
+// exponential-trapezoidal rule (Trap, see trap_left_in) each token also takes in the previous
+// token's input; the token before the row's first is (xp[row][D], bp[row][16]), or none.
+template <typename E, bool kSummary, AForm AF = AForm::Diagonal, bool kTrap = false>
 __global__ __launch_bounds__(64) void prefill_lane_kernel(
     const typename E::store_t *__restrict__ x, const typename E::store_t *__restrict__ dl,
     const float *__restrict__ A, const typename E::store_t *__restrict__ B,
     const typename E::store_t *__restrict__ C, const float *__restrict__ h0,
     typename E::store_t *__restrict__ y, float *__restrict__ h_final, float *__restrict__ dsum, Segments sg, int D,
-    int blocks_per_row) {
+    int blocks_per_row, Trap tr) {
     const int vrow = blockIdx.x / blocks_per_row;
     const int d = (blockIdx.x - vrow * blocks_per_row) * 64 + threadIdx.x;
     if (d >= D) return;  // no cross-lane work below, so idle lanes may leave
     const RowSpan span = row_span(sg, vrow);
 
-    static_assert(AF == AForm::Diagonal || !kSummary, "the other forms of A run the plain prefill");
+    static_assert((AF == AForm::Diagonal && !kTrap) || !kSummary, "the other forms run the plain prefill");
     constexpr bool kScalarA = AF == AForm::ScaledIdentity, kComplexA = AF == AForm::ComplexPairs;
     float a2[kDState], h[kDState];
 #pragma unroll
@@ -49,10 +51,33 @@ __global__ __launch_bounds__(64) void prefill_lane_kernel(
     const typename E::store_t *Br = B + row * kDState;
     const typename E::store_t *Cr = C + row * kDState;
 
+    using S = typename E::store_t;
+    const S *lr = kTrap ? static_cast<const S *>(tr.lam) + row * D + d : nullptr;
+    float xprev = 0.0f, bprev[kDState];
+#pragma unroll
+    for (int n = 0; n < kDState; ++n) bprev[n] = 0.0f;
+    if (kTrap && tr.x_prev) {
+        xprev = E::load(static_cast<const S *>(tr.x_prev) + (int64_t)vrow * D + d);
+#pragma unroll
+        for (int n = 0; n < kDState; ++n) bprev[n] = E::load(static_cast<const S *>(tr.B_prev) + vrow * kDState + n);
+    }
+
     float dacc = 0.0f;
     for (int64_t t = 0; t < span.len; ++t) {
         const float xv = E::load(xr + t * D), dv = E::load(dr + t * D);
-        const float dx = delta_x(dv, xv);
+        float dx = delta_x(dv, xv);
+        if constexpr (kTrap) {   // left end point in; q replaces delta * x below
+            const float lv = E::load(lr + t * D);
+            const float pl = trap_left(dv, lv, xprev);
+            dx = trap_right(dv, lv, xv);
+            xprev = xv;
+#pragma unroll
+            for (int n = 0; n < kDState; ++n) {
+                const float b = E::load(Br + t * kDState + n);
+                h[n] = trap_left_in(h[n], pl, bprev[n]);
+                bprev[n] = b;
+            }
+        }
         const float abar = kScalarA ? decay(dv, a2[0]) : 0.0f;
         float acc = 0.0f;
         if constexpr (kComplexA) {

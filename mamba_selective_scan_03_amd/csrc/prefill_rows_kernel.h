@@ -52,6 +52,9 @@ constexpr int kYStride = kCh + 16;         // [token][channel] y exchange: the 4
 constexpr int kDxSize = kT / 2 * kDxStride;
 constexpr int kBcSize = kDState * kBcStride;
 constexpr int kYSize = 2 * kT * kYStride;
+// Trapezoidal rule: the left-end weights p [kT/4][kPStride] (4 tokens of a channel per float4)
+constexpr int kPStride = kCh * 4 + 4;
+constexpr int kPSize = kT / 4 * kPStride;
 }  // namespace rows
 
 // Four consecutive elements from global memory as fp32 (bf16: one 8-byte load).
@@ -77,6 +80,18 @@ template <> struct Vec4<F32> {
 template <typename E> struct TileRegs {
     typename Vec4<E>::raw x[2], dl[2];   // tokens 2p and 2p+1, channels 4q..4q+3
     typename Vec4<E>::raw bc[2];         // B (threads 0-127) or C (128-255): one token, 8 states
+    // trapezoidal rule only: lam of tokens 2p, 2p+1; x of token 2p-1; B (or C) of token tb-1
+    typename Vec4<E>::raw lam[2], xp, bcp[2];
+};
+
+// Where a trapezoidal prefill's helper thread finds the token before its row's first: the
+// caller's x_prev and B_prev rows (B_prev is also read, unused, by the C threads), or, with
+// none given, any valid address whose value staging then replaces by zero.
+template <typename E> struct PrevRow {
+    const typename E::store_t *lam;   // lam of the work-group's channels, token 0 of the row
+    const typename E::store_t *x;     // x_prev + 4q of this thread's channels, or a stand-in
+    const typename E::store_t *bc;    // B_prev + nb, or a stand-in
+    bool given;
 };
 
 
@@ -133,10 +148,11 @@ __device__ __forceinline__ float reduce_rows4(float p0, float p1, float p2, floa
 // the full HBM latency.  Whole tiles take 32-bit lane offsets from a tile base; the last,
 // partial tile re-reads token L-1 for tokens past the end, which staging then replaces by
 // identity tokens.
-template <typename E, bool kLoadDelta = true>
+template <typename E, bool kLoadDelta = true, bool kTrap = false>
 __device__ __forceinline__ void load_tile(TileRegs<E> &R, const typename E::store_t *xb,
                                           const typename E::store_t *db, const typename E::store_t *bcb,
-                                          int64_t t0, int64_t L, int D, int tid) {
+                                          int64_t t0, int64_t L, int D, int tid,
+                                          const PrevRow<E> &pr = PrevRow<E>{nullptr, nullptr, nullptr, false}) {
     const int p = tid >> 3, q = tid & 7;                   // token pair p, channel quad q
     const int tb = (tid & 127) >> 1, nb = (tid & 1) * 8;  // B/C: one token, 8 states
     if (t0 + rows::kT <= L) {
@@ -146,6 +162,7 @@ __device__ __forceinline__ void load_tile(TileRegs<E> &R, const typename E::stor
             const int off = (2 * p + j) * D + 4 * q;
             R.x[j] = Vec4<E>::load(xt + off);
             if constexpr (kLoadDelta) R.dl[j] = Vec4<E>::load(dt + off);
+            if constexpr (kTrap) R.lam[j] = Vec4<E>::load(pr.lam + t0 * D + off);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) R.bc[j] = Vec4<E>::load(bt + tb * kDState + nb + 4 * j);
@@ -155,10 +172,20 @@ __device__ __forceinline__ void load_tile(TileRegs<E> &R, const typename E::stor
             const int64_t t = min(t0 + 2 * p + j, L - 1);
             R.x[j] = Vec4<E>::load(xb + t * D + 4 * q);
             if constexpr (kLoadDelta) R.dl[j] = Vec4<E>::load(db + t * D + 4 * q);
+            if constexpr (kTrap) R.lam[j] = Vec4<E>::load(pr.lam + t * D + 4 * q);
         }
         const int64_t t = min(t0 + tb, L - 1);
 #pragma unroll
         for (int j = 0; j < 2; ++j) R.bc[j] = Vec4<E>::load(bcb + t * kDState + nb + 4 * j);
+    }
+    if constexpr (kTrap) {
+        // the previous token of pair p and of B/C token tb (clamped like the tokens themselves;
+        // token -1 is the caller's previous token)
+        const int64_t tp = min(t0 + 2 * p - 1, L - 1), tq = min(t0 + tb - 1, L - 1);
+        R.xp = Vec4<E>::load(tp >= 0 ? xb + tp * D + 4 * q : pr.x);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            R.bcp[j] = Vec4<E>::load(tq >= 0 ? bcb + tq * kDState + nb + 4 * j : pr.bc + 4 * j);
     }
 }
 
@@ -220,23 +247,46 @@ __device__ __forceinline__ void fused_delta(const u32x4_t (&f)[fused::kKS], cons
 // from a2q (this thread's four channels).  Tokens at or past L become identity tokens
 // (delta = 0, x = -0, B = C = 0; their decay is exactly 1).  A tile is staged a quarter per
 // 16-token group so that the LDS writes never pile up behind each other.
-template <typename E, int part, AForm AF>
-__device__ __forceinline__ void stage_part(const TileRegs<E> &R, float *dx_s, float *bc_s, int64_t t0, int64_t L,
-                                           int tid, const float4 &a2q) {
+//
+// With the trapezoidal rule (kTrap) the pair's first member is q = (lam delta) x, the left-end
+// weight p = ((1 - lam) delta) x_prev of each token goes to p_s, and the B threads also stage
+// B of the previous token into the third B/C tile (zero for tokens at or past L, and for token
+// 0 of a row without a previous token).  A token at or past L gets p = -0, so with its zero
+// previous B the left-end term is -0 and the state stays bit-identical.
+template <typename E, int part, AForm AF, bool kTrap>
+__device__ __forceinline__ void stage_part(const TileRegs<E> &R, float *dx_s, float *bc_s, float *p_s, int64_t t0,
+                                           int64_t L, int tid, const float4 &a2q, bool prev_given) {
     constexpr bool kScalarA = AF == AForm::ScaledIdentity;
     const float a2 = part == 0 ? a2q.x : part == 1 ? a2q.y : part == 2 ? a2q.z : a2q.w;
     const int p = tid >> 3, q = tid & 7;
     float4 v;
     {
-        float xv[4], dv[4];
+        float xv[4], dv[4], lv[4], xpv[4];
         const bool live0 = t0 + 2 * p < L, live1 = t0 + 2 * p + 1 < L;
         Vec4<E>::widen(live0 ? R.x[0] : Vec4<E>::neg_zero(), xv);
         Vec4<E>::widen(live0 ? R.dl[0] : Vec4<E>::zero(), dv);
-        v.x = delta_x(dv[part], xv[part]);
+        float p0 = 0.0f, p1 = 0.0f;
+        if constexpr (kTrap) {
+            Vec4<E>::widen(live0 ? R.lam[0] : Vec4<E>::zero(), lv);
+            Vec4<E>::widen((t0 + 2 * p > 0 || prev_given) ? R.xp : Vec4<E>::zero(), xpv);
+            v.x = trap_right(dv[part], lv[part], xv[part]);
+            p0 = live0 ? trap_left(dv[part], lv[part], xpv[part]) : -0.0f;
+            xpv[part] = xv[part];   // token 2p is token 2p+1's previous one
+        } else {
+            v.x = delta_x(dv[part], xv[part]);
+        }
         v.y = kScalarA ? decay(dv[part], a2) : dv[part];
         Vec4<E>::widen(live1 ? R.x[1] : Vec4<E>::neg_zero(), xv);
         Vec4<E>::widen(live1 ? R.dl[1] : Vec4<E>::zero(), dv);
-        v.z = delta_x(dv[part], xv[part]);
+        if constexpr (kTrap) {
+            Vec4<E>::widen(live1 ? R.lam[1] : Vec4<E>::zero(), lv);
+            v.z = trap_right(dv[part], lv[part], xv[part]);
+            p1 = live1 ? trap_left(dv[part], lv[part], xpv[part]) : -0.0f;
+            *reinterpret_cast<float2 *>(p_s + (p >> 1) * rows::kPStride + (4 * q + part) * 4 + 2 * (p & 1)) =
+                make_float2(p0, p1);
+        } else {
+            v.z = delta_x(dv[part], xv[part]);
+        }
         v.w = kScalarA ? decay(dv[part], a2) : dv[part];
     }
     *reinterpret_cast<float4 *>(dx_s + p * rows::kDxStride + (4 * q + part) * 4) = v;
@@ -247,14 +297,23 @@ __device__ __forceinline__ void stage_part(const TileRegs<E> &R, float *dx_s, fl
     Vec4<E>::widen(live ? R.bc[part >> 1] : Vec4<E>::zero(), f);
     dst[(nb + 2 * part) * rows::kBcStride + tb] = f[(2 * part) & 3];
     dst[(nb + 2 * part + 1) * rows::kBcStride + tb] = f[(2 * part + 1) & 3];
+    if constexpr (kTrap) {
+        if (tid < 128) {   // whole waves: the B threads
+            const bool prev_live = live && (t0 + tb > 0 || prev_given);
+            Vec4<E>::widen(prev_live ? R.bcp[part >> 1] : Vec4<E>::zero(), f);
+            float *bp = bc_s + 2 * rows::kBcSize;
+            bp[(nb + 2 * part) * rows::kBcStride + tb] = f[(2 * part) & 3];
+            bp[(nb + 2 * part + 1) * rows::kBcStride + tb] = f[(2 * part + 1) & 3];
+        }
+    }
 }
-template <typename E, AForm AF>
-__device__ __forceinline__ void stage_tile(const TileRegs<E> &R, float *dx_s, float *bc_s, int64_t t0, int64_t L,
-                                           int tid, const float4 &a2q) {
-    stage_part<E, 0, AF>(R, dx_s, bc_s, t0, L, tid, a2q);
-    stage_part<E, 1, AF>(R, dx_s, bc_s, t0, L, tid, a2q);
-    stage_part<E, 2, AF>(R, dx_s, bc_s, t0, L, tid, a2q);
-    stage_part<E, 3, AF>(R, dx_s, bc_s, t0, L, tid, a2q);
+template <typename E, AForm AF, bool kTrap = false>
+__device__ __forceinline__ void stage_tile(const TileRegs<E> &R, float *dx_s, float *bc_s, float *p_s, int64_t t0,
+                                           int64_t L, int tid, const float4 &a2q, bool prev_given = false) {
+    stage_part<E, 0, AF, kTrap>(R, dx_s, bc_s, p_s, t0, L, tid, a2q, prev_given);
+    stage_part<E, 1, AF, kTrap>(R, dx_s, bc_s, p_s, t0, L, tid, a2q, prev_given);
+    stage_part<E, 2, AF, kTrap>(R, dx_s, bc_s, p_s, t0, L, tid, a2q, prev_given);
+    stage_part<E, 3, AF, kTrap>(R, dx_s, bc_s, p_s, t0, L, tid, a2q, prev_given);
 }
 
 // One 16-token group's LDS operands for one lane: (delta*x, delta) of its channel for the 16
@@ -262,31 +321,53 @@ __device__ __forceinline__ void stage_tile(const TileRegs<E> &R, float *dx_s, fl
 // They are read in two halves (tokens 0-7 with B and C, then tokens 8-15), each issued half a
 // group ahead of its use: a wave may have at most 15 LDS operations in flight, and larger
 // bursts stall issue until the oldest complete.
+// A trapezoidal scan also reads the 16 tokens' left-end weights p (pv) and the previous token's
+// B of its two states (bp0, bp1; broadcast per token like B).
 struct GroupRegs {
     float4 v[8];
     float b0, b1, c0, c1;
+    float4 pv[4];
+    float bp0, bp1;
 };
-template <int H>
-__device__ __forceinline__ void load_half(GroupRegs &g, const float *dxs, const float *bcs, int tg, int ch, int n0,
-                                          int c) {
+template <int H, bool kTrap = false>
+__device__ __forceinline__ void load_half(GroupRegs &g, const float *dxs, const float *bcs, const float *ps, int tg,
+                                          int ch, int n0, int c) {
 #pragma unroll
     for (int i = 4 * H; i < 4 * H + 4; ++i)
         g.v[i] = *reinterpret_cast<const float4 *>(dxs + ((tg >> 1) + i) * rows::kDxStride + ch * 4);
+    if constexpr (kTrap) {
+#pragma unroll
+        for (int i = 2 * H; i < 2 * H + 2; ++i)
+            g.pv[i] = *reinterpret_cast<const float4 *>(ps + ((tg >> 2) + i) * rows::kPStride + ch * 4);
+    }
     if constexpr (H == 0) {
         g.b0 = bcs[n0 * rows::kBcStride + tg + c];
         g.b1 = bcs[(n0 + 1) * rows::kBcStride + tg + c];
         g.c0 = bcs[rows::kBcSize + n0 * rows::kBcStride + tg + c];
         g.c1 = bcs[rows::kBcSize + (n0 + 1) * rows::kBcStride + tg + c];
+        if constexpr (kTrap) {
+            g.bp0 = bcs[2 * rows::kBcSize + n0 * rows::kBcStride + tg + c];
+            g.bp1 = bcs[2 * rows::kBcSize + (n0 + 1) * rows::kBcStride + tg + c];
+        }
     }
+}
+
+template <int i> __device__ __forceinline__ float component(const float4 &v) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
 // One token: advance this lane's two states and return C*h summed over them (a summary
 // scan adds the token's delta to `dsum` instead and returns nothing useful).  With a
 // scaled-identity A the pair's second member is already the decay; with a complex state the
 // lane's two states are one complex state and (a2_0, a2_1) its prepared ComplexA.
-template <int TAU, bool kSummary, AForm AF>
+template <int TAU, bool kSummary, AForm AF, bool kTrap = false>
 __device__ __forceinline__ float token_step(const GroupRegs &g, float &h_0, float &h_1, float a2_0, float a2_1,
                                             float &dsum) {
+    if constexpr (kTrap) {   // the left end point: h + p * B_prev, the DPP broadcast folded in
+        const float pl = component<TAU & 3>(g.pv[TAU >> 2]);
+        h_0 = fmac_bcast<TAU>(h_0, g.bp0, pl);
+        h_1 = fmac_bcast<TAU>(h_1, g.bp1, pl);
+    }
     const float4 v = g.v[TAU >> 1];
     const float dxv = (TAU & 1) ? v.z : v.x;
     const float dv = (TAU & 1) ? v.w : v.y;
@@ -311,11 +392,11 @@ __device__ __forceinline__ float token_step(const GroupRegs &g, float &h_0, floa
 // partials (summed over the wave's 4 rows) in the y exchange rows `ys` (row = token in group).
 // A segment-summary scan (kSummary) produces no y; it adds the tokens' delta to `dsum` in
 // token order instead, and the y arithmetic is left out of the code altogether.
-template <int H, bool kSummary, AForm AF>
+template <int H, bool kSummary, AForm AF, bool kTrap = false>
 __device__ __forceinline__ void scan_half(const GroupRegs &g, float &h_0, float &h_1, float a2_0, float a2_1, float *ys,
                                           int rt, int ch, float &dsum) {
     float P[8];
-#define JSCAN_STEP(i) P[i] = token_step<8 * H + (i), kSummary, AF>(g, h_0, h_1, a2_0, a2_1, dsum);
+#define JSCAN_STEP(i) P[i] = token_step<8 * H + (i), kSummary, AF, kTrap>(g, h_0, h_1, a2_0, a2_1, dsum);
     JSCAN_STEP(0) JSCAN_STEP(1) JSCAN_STEP(2) JSCAN_STEP(3)
     JSCAN_STEP(4) JSCAN_STEP(5) JSCAN_STEP(6) JSCAN_STEP(7)
 #undef JSCAN_STEP
@@ -334,11 +415,11 @@ __device__ __forceinline__ void scan_half(const GroupRegs &g, float &h_0, float 
 // reduction over rows and store (done in the next region, beside the next half's tokens).  The
 // scaled-identity form, whose tokens are short, runs its halves this way: 2% faster there, 2%
 // slower for the diagonal A.
-template <int H, AForm AF>
+template <int H, AForm AF, bool kTrap = false>
 __device__ __forceinline__ void half_partials(const GroupRegs &g, float &h_0, float &h_1, float a2_0, float a2_1,
                                               float (&P)[8]) {
     float dsum = 0.0f;
-#define JSCAN_STEP(i) P[i] = token_step<8 * H + (i), false, AF>(g, h_0, h_1, a2_0, a2_1, dsum);
+#define JSCAN_STEP(i) P[i] = token_step<8 * H + (i), false, AF, kTrap>(g, h_0, h_1, a2_0, a2_1, dsum);
     JSCAN_STEP(0) JSCAN_STEP(1) JSCAN_STEP(2) JSCAN_STEP(3)
     JSCAN_STEP(4) JSCAN_STEP(5) JSCAN_STEP(6) JSCAN_STEP(7)
 #undef JSCAN_STEP
@@ -396,19 +477,23 @@ __device__ __forceinline__ void write_final(const FinalRegs &F, typename E::stor
 // row's final state and, per channel, the sum of the row's delta values to dsum[row][D].
 // With kFused, delta is not read: the helper waves compute it from dp (bf16 only).  With
 // a scaled-identity A (AF), A is a[D] (one value per channel) instead of A[D][16]; with a
-// complex state, A[D][16] holds 8 complex entries per channel as (real, imaginary) pairs.
-template <typename E, bool kSummary, bool kFused = false, AForm AF = AForm::Diagonal>
+// complex state, A[D][16] holds 8 complex entries per channel as (real, imaginary) pairs.  With
+// kTrap the exponential-trapezoidal rule replaces the Euler rule (extra inputs in tr).
+template <typename E, bool kSummary, bool kFused = false, AForm AF = AForm::Diagonal, bool kTrap = false>
 __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_rows_kernel(
     const typename E::store_t *__restrict__ x, const typename E::store_t *__restrict__ dl,
     const float *__restrict__ A, const typename E::store_t *__restrict__ B,
     const typename E::store_t *__restrict__ C, const float *__restrict__ h0,
     typename E::store_t *__restrict__ y, float *__restrict__ h_final, float *__restrict__ dsum, Segments sg, int D,
-    int blocks_per_row, int xcd_stride, DeltaProj dp) {
+    int blocks_per_row, int xcd_stride, DeltaProj dp, Trap tr) {
     static_assert(!kFused || (sizeof(typename E::store_t) == 2 && !kSummary), "the fused delta path is bf16 only");
-    static_assert(AF == AForm::Diagonal || (!kSummary && !kFused), "the other forms of A run the plain prefill");
+    static_assert((AF == AForm::Diagonal && !kTrap) || (!kSummary && !kFused),
+                  "the other forms of A and the trapezoidal rule run the plain prefill");
     constexpr bool kScalarA = AF == AForm::ScaledIdentity;
+    using S = typename E::store_t;
     __shared__ __attribute__((aligned(16))) float dx_s[2][rows::kDxSize];
-    __shared__ __attribute__((aligned(16))) float bc_s[2][2 * rows::kBcSize];
+    __shared__ __attribute__((aligned(16))) float bc_s[2][(kTrap ? 3 : 2) * rows::kBcSize];
+    __shared__ __attribute__((aligned(16))) float p_s[2][kTrap ? rows::kPSize : 4];
     __shared__ __attribute__((aligned(16))) float y_s[2][rows::kYSize];
     __shared__ __attribute__((aligned(16))) uint16_t xch_s[kFused ? 4 * fused::kXchWave : 8];
 
@@ -446,6 +531,16 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
             const float4 av = *reinterpret_cast<const float4 *>(A + d0 + 4 * (tid & 7));
             a2q = make_float4(scaled_A(av.x), scaled_A(av.y), scaled_A(av.z), scaled_A(av.w));
         }
+        // trapezoidal rule: lam, and the caller's previous token (or stand-ins staged as zero)
+        const bool prev_given = kTrap && tr.x_prev != nullptr;
+        PrevRow<E> pr{nullptr, nullptr, nullptr, prev_given};
+        if constexpr (kTrap) {
+            pr.lam = static_cast<const S *>(tr.lam) + row * D + d0;
+            pr.x = prev_given ? static_cast<const S *>(tr.x_prev) + (int64_t)vrow * D + d0 + 4 * (tid & 7)
+                              : xb + 4 * (tid & 7);
+            pr.bc = prev_given ? static_cast<const S *>(tr.B_prev) + (int64_t)vrow * kDState + (tid & 1) * 8
+                               : bcb + (tid & 1) * 8;
+        }
         if constexpr (kFused) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -456,14 +551,14 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
                 bias[u] = *reinterpret_cast<const float4 *>(dp.b_dt + d0 + 16 * u + 4 * (l >> 4));
             }
         }
-        load_tile<E, !kFused>(R[0], xb, db, bcb, 0, L, D, tid);
+        load_tile<E, !kFused, kTrap>(R[0], xb, db, bcb, 0, L, D, tid, pr);
         if constexpr (kFused) {
             load_dlow(dfr[0], dp.d_low, row, 0, L, hw, l);
             fused_delta(dfr[0], wf, bias, xch, R[0], l);
         }
-        stage_tile<E, AF>(R[0], dx_s[0], bc_s[0], 0, L, tid, a2q);
-        load_tile<E, !kFused>(R[1], xb, db, bcb, rows::kT, L, D, tid);
-        load_tile<E, !kFused>(R[0], xb, db, bcb, 2 * rows::kT, L, D, tid);
+        stage_tile<E, AF, kTrap>(R[0], dx_s[0], bc_s[0], p_s[0], 0, L, tid, a2q, prev_given);
+        load_tile<E, !kFused, kTrap>(R[1], xb, db, bcb, rows::kT, L, D, tid, pr);
+        load_tile<E, !kFused, kTrap>(R[0], xb, db, bcb, 2 * rows::kT, L, D, tid, pr);
         if constexpr (kFused) {
             load_dlow(dfr[1], dp.d_low, row, rows::kT, L, hw, l);
             load_dlow(dfr[0], dp.d_low, row, 2 * rows::kT, L, hw, l);
@@ -474,9 +569,10 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
             constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
             if (k + 1 < ntiles) {
                 if constexpr (kFused) fused_delta(dfr[nxt], wf, bias, xch, R[nxt], l);
-                stage_tile<E, AF>(R[nxt], dx_s[nxt], bc_s[nxt], (int64_t)(k + 1) * rows::kT, L, tid, a2q);
+                stage_tile<E, AF, kTrap>(R[nxt], dx_s[nxt], bc_s[nxt], p_s[nxt], (int64_t)(k + 1) * rows::kT, L, tid,
+                                         a2q, prev_given);
                 if (k + 3 < ntiles) {
-                    load_tile<E, !kFused>(R[nxt], xb, db, bcb, (int64_t)(k + 3) * rows::kT, L, D, tid);
+                    load_tile<E, !kFused, kTrap>(R[nxt], xb, db, bcb, (int64_t)(k + 3) * rows::kT, L, D, tid, pr);
                     if constexpr (kFused) load_dlow(dfr[nxt], dp.d_low, row, (int64_t)(k + 3) * rows::kT, L, hw, l);
                 }
             }
@@ -529,8 +625,8 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
     __syncthreads();   // tile 0 staged by the helper waves
     GroupRegs G[2];
     float dacc = 0.0f;
-    load_half<0>(G[0], dx_s[0], bc_s[0], 0, ch, n0, c);
-    load_half<1>(G[0], dx_s[0], bc_s[0], 0, ch, n0, c);
+    load_half<0, kTrap>(G[0], dx_s[0], bc_s[0], p_s[0], 0, ch, n0, c);
+    load_half<1, kTrap>(G[0], dx_s[0], bc_s[0], p_s[0], 0, ch, n0, c);
 
     // Per tile: four 16-token groups, each group's LDS operands read (in two halves) while the
     // previous group is scanned.  One barrier per tile, shared with the helper waves, orders
@@ -540,78 +636,78 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
     auto tile = [&](auto cur_c, int k) {
         constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
         float *ys = y_s[cur] + sh * rows::kT * rows::kYStride;
-        const float *dxc = dx_s[cur], *bcc = bc_s[cur];
+        const float *dxc = dx_s[cur], *bcc = bc_s[cur], *psc = p_s[cur];
         if constexpr (AF != AForm::ScaledIdentity) {
-            load_half<0>(G[1], dxc, bcc, 16, ch, n0, c);
+            load_half<0, kTrap>(G[1], dxc, bcc, psc, 16, ch, n0, c);
             JSCAN_SB;
-            scan_half<0, kSummary, AF>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch, dacc);
+            scan_half<0, kSummary, AF, kTrap>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch, dacc);
             JSCAN_SB;
-            load_half<1>(G[1], dxc, bcc, 16, ch, n0, c);
+            load_half<1, kTrap>(G[1], dxc, bcc, psc, 16, ch, n0, c);
             JSCAN_SB;
-            scan_half<1, kSummary, AF>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch, dacc);
+            scan_half<1, kSummary, AF, kTrap>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch, dacc);
             JSCAN_SB;
-            load_half<0>(G[0], dxc, bcc, 32, ch, n0, c);
+            load_half<0, kTrap>(G[0], dxc, bcc, psc, 32, ch, n0, c);
             JSCAN_SB;
-            scan_half<0, kSummary, AF>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch, dacc);
+            scan_half<0, kSummary, AF, kTrap>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch, dacc);
             JSCAN_SB;
-            load_half<1>(G[0], dxc, bcc, 32, ch, n0, c);
+            load_half<1, kTrap>(G[0], dxc, bcc, psc, 32, ch, n0, c);
             JSCAN_SB;
-            scan_half<1, kSummary, AF>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch, dacc);
+            scan_half<1, kSummary, AF, kTrap>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch, dacc);
             JSCAN_SB;
-            load_half<0>(G[1], dxc, bcc, 48, ch, n0, c);
+            load_half<0, kTrap>(G[1], dxc, bcc, psc, 48, ch, n0, c);
             JSCAN_SB;
-            scan_half<0, kSummary, AF>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch, dacc);
+            scan_half<0, kSummary, AF, kTrap>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch, dacc);
             JSCAN_SB;
-            load_half<1>(G[1], dxc, bcc, 48, ch, n0, c);
+            load_half<1, kTrap>(G[1], dxc, bcc, psc, 48, ch, n0, c);
             JSCAN_SB;
-            scan_half<1, kSummary, AF>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch, dacc);
+            scan_half<1, kSummary, AF, kTrap>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch, dacc);
             JSCAN_SB;
-            scan_half<0, kSummary, AF>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch, dacc);
+            scan_half<0, kSummary, AF, kTrap>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch, dacc);
             JSCAN_SB;
-            scan_half<1, kSummary, AF>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch, dacc);
+            scan_half<1, kSummary, AF, kTrap>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch, dacc);
         } else {
             float Pa[8], Pb[8];
-            load_half<0>(G[1], dxc, bcc, 16, ch, n0, c);
+            load_half<0, kTrap>(G[1], dxc, bcc, psc, 16, ch, n0, c);
             JSCAN_SB;
-            half_partials<0, AF>(G[0], h_0, h_1, a2_0, a2_1, Pa);
+            half_partials<0, AF, kTrap>(G[0], h_0, h_1, a2_0, a2_1, Pa);
             JSCAN_SB;
-            load_half<1>(G[1], dxc, bcc, 16, ch, n0, c);
+            load_half<1, kTrap>(G[1], dxc, bcc, psc, 16, ch, n0, c);
             JSCAN_SB;
-            half_partials<1, AF>(G[0], h_0, h_1, a2_0, a2_1, Pb);
+            half_partials<1, AF, kTrap>(G[0], h_0, h_1, a2_0, a2_1, Pb);
             half_store<0>(Pa, ys, rt, ch);
             JSCAN_SB;
-            load_half<0>(G[0], dxc, bcc, 32, ch, n0, c);
+            load_half<0, kTrap>(G[0], dxc, bcc, psc, 32, ch, n0, c);
             JSCAN_SB;
-            half_partials<0, AF>(G[1], h_0, h_1, a2_0, a2_1, Pa);
+            half_partials<0, AF, kTrap>(G[1], h_0, h_1, a2_0, a2_1, Pa);
             half_store<1>(Pb, ys, rt, ch);
             JSCAN_SB;
-            load_half<1>(G[0], dxc, bcc, 32, ch, n0, c);
+            load_half<1, kTrap>(G[0], dxc, bcc, psc, 32, ch, n0, c);
             JSCAN_SB;
-            half_partials<1, AF>(G[1], h_0, h_1, a2_0, a2_1, Pb);
+            half_partials<1, AF, kTrap>(G[1], h_0, h_1, a2_0, a2_1, Pb);
             half_store<0>(Pa, ys + 16 * rows::kYStride, rt, ch);
             JSCAN_SB;
-            load_half<0>(G[1], dxc, bcc, 48, ch, n0, c);
+            load_half<0, kTrap>(G[1], dxc, bcc, psc, 48, ch, n0, c);
             JSCAN_SB;
-            half_partials<0, AF>(G[0], h_0, h_1, a2_0, a2_1, Pa);
+            half_partials<0, AF, kTrap>(G[0], h_0, h_1, a2_0, a2_1, Pa);
             half_store<1>(Pb, ys + 16 * rows::kYStride, rt, ch);
             JSCAN_SB;
-            load_half<1>(G[1], dxc, bcc, 48, ch, n0, c);
+            load_half<1, kTrap>(G[1], dxc, bcc, psc, 48, ch, n0, c);
             JSCAN_SB;
-            half_partials<1, AF>(G[0], h_0, h_1, a2_0, a2_1, Pb);
+            half_partials<1, AF, kTrap>(G[0], h_0, h_1, a2_0, a2_1, Pb);
             half_store<0>(Pa, ys + 32 * rows::kYStride, rt, ch);
             JSCAN_SB;
-            half_partials<0, AF>(G[1], h_0, h_1, a2_0, a2_1, Pa);
+            half_partials<0, AF, kTrap>(G[1], h_0, h_1, a2_0, a2_1, Pa);
             half_store<1>(Pb, ys + 32 * rows::kYStride, rt, ch);
             JSCAN_SB;
-            half_partials<1, AF>(G[1], h_0, h_1, a2_0, a2_1, Pb);
+            half_partials<1, AF, kTrap>(G[1], h_0, h_1, a2_0, a2_1, Pb);
             half_store<0>(Pa, ys + 48 * rows::kYStride, rt, ch);
             JSCAN_SB;
             half_store<1>(Pb, ys + 48 * rows::kYStride, rt, ch);
         }
         __syncthreads();
         if (k + 1 < ntiles) {
-            load_half<0>(G[0], dx_s[nxt], bc_s[nxt], 0, ch, n0, c);
-            load_half<1>(G[0], dx_s[nxt], bc_s[nxt], 0, ch, n0, c);
+            load_half<0, kTrap>(G[0], dx_s[nxt], bc_s[nxt], p_s[nxt], 0, ch, n0, c);
+            load_half<1, kTrap>(G[0], dx_s[nxt], bc_s[nxt], p_s[nxt], 0, ch, n0, c);
         }
     };
 #undef JSCAN_SB
@@ -632,16 +728,18 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
 inline bool rows_kernel_applies(int64_t /*batch*/, int64_t D) { return D % rows::kCh == 0; }
 
 // Launches one work-group per 32 channels of each of the `nrows` rows described by sg.
-template <typename E, bool kSummary, bool kFused = false, AForm AF = AForm::Diagonal>
+template <typename E, bool kSummary, bool kFused = false, AForm AF = AForm::Diagonal, bool kTrap = false>
 void launch_prefill_rows(const typename E::store_t *x, const typename E::store_t *dl, const float *A,
                          const typename E::store_t *B, const typename E::store_t *C, const float *h0,
                          typename E::store_t *y, float *h_final, float *dsum, const Segments &sg, int64_t nrows,
-                         int D, hipStream_t stream, DeltaProj dp = DeltaProj{nullptr, nullptr, nullptr}) {
+                         int D, hipStream_t stream, DeltaProj dp = DeltaProj{nullptr, nullptr, nullptr},
+                         Trap tr = Trap{nullptr, nullptr, nullptr}) {
     const int blocks_per_row = D / rows::kCh;
     const int64_t blocks = nrows * blocks_per_row;
     const int xcd_stride = (blocks % 8 == 0) ? (int)(blocks / 8) : 0;
-    hipLaunchKernelGGL((prefill_rows_kernel<E, kSummary, kFused, AF>), dim3((unsigned)blocks), dim3(rows::kThreads), 0,
-                       stream, x, dl, A, B, C, h0, y, h_final, dsum, sg, D, blocks_per_row, xcd_stride, dp);
+    hipLaunchKernelGGL((prefill_rows_kernel<E, kSummary, kFused, AF, kTrap>), dim3((unsigned)blocks),
+                       dim3(rows::kThreads), 0, stream, x, dl, A, B, C, h0, y, h_final, dsum, sg, D, blocks_per_row,
+                       xcd_stride, dp, tr);
 }
 
 }  // namespace jscan

@@ -80,6 +80,30 @@ __device__ __forceinline__ void advance_complex(float &h_re, float &h_im, float 
     h_im = im;
 }
 
+// ---- exponential-trapezoidal rule (the Mamba-3 discretisation) ------------------------------
+// Lesson page "Jamba - Hybrid SSM-Transformer", section "Mamba-3", item 1: the input term mixes
+// neighbouring tokens.  Over step t the input integral is weighted lam_t at the right end point
+// (this token) and 1 - lam_t at the left end point (the previous token), which decays with the
+// state over the whole step:
+//     h_t = Abar_t (h_{t-1} + p_t B_{t-1}) + q_t B_t,   p_t = ((1 - lam_t) delta_t) x_{t-1},
+//                                                     q_t = (lam_t delta_t) x_t
+// Every kernel takes the left end point in first, k = fma(p_t, B_{t-1}, h), then advances k by
+// its form's update with q_t in place of delta_t * x_t.  lam = 1 gives p = 0 and q = delta * x.
+__device__ __forceinline__ float trap_right(float delta, float lam, float x) { return (lam * delta) * x; }
+__device__ __forceinline__ float trap_left(float delta, float lam, float x_prev) {
+    return ((1.0f - lam) * delta) * x_prev;
+}
+__device__ __forceinline__ float trap_left_in(float h, float p, float b_prev) { return __builtin_fmaf(p, b_prev, h); }
+
+// The extra inputs of a trapezoidal prefill, in the dtype of x: lam [tokens][D] like delta, and
+// the token before each row's first one, x_prev [rows][D] and B_prev [rows][16] (both null when
+// there is none: its term is then zero).
+struct Trap {
+    const void *lam;
+    const void *x_prev;
+    const void *B_prev;
+};
+
 // A compile-time integer as a value: lets an unrolled loop body pick register sets and LDS
 // buffers by constant index.
 template <int V> struct IntConst {

@@ -45,8 +45,10 @@ template <> struct Quad<F32> {
 };
 
 // With a scaled-identity A (AF), A is a[D]: one decay per (row, channel) serves the quad.  With
-// a complex state the quad is two complex states, (4q, 4q+1) and (4q+2, 4q+3).
-template <typename E, AForm AF = AForm::Diagonal>
+// a complex state the quad is two complex states, (4q, 4q+1) and (4q+2, 4q+3).  With the
+// exponential-trapezoidal rule (kTrap) the previous token's x (xp, rows like x) and B (bp, rows
+// like B) enter as the step's left end point, weighted by 1 - lam (lam, rows like x).
+template <typename E, AForm AF = AForm::Diagonal, bool kTrap = false>
 __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ h,
                                                    const typename E::store_t *__restrict__ x,
                                                    const typename E::store_t *__restrict__ dl,
@@ -54,7 +56,10 @@ __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ h,
                                                    const typename E::store_t *__restrict__ Bt,
                                                    const typename E::store_t *__restrict__ Ct,
                                                    typename E::store_t *__restrict__ y, int batch, int D,
-                                                   int blocks_per_rows, int64_t ld_xd, int64_t ld_bc) {
+                                                   int blocks_per_rows, int64_t ld_xd, int64_t ld_bc,
+                                                   const typename E::store_t *__restrict__ lam,
+                                                   const typename E::store_t *__restrict__ xp,
+                                                   const typename E::store_t *__restrict__ bp) {
     constexpr int NR = step::kRows;
     const int rg = blockIdx.x / blocks_per_rows;   // group of NR batch rows
     const int lane_in_row = (blockIdx.x - rg * blocks_per_rows) * 256 + threadIdx.x;
@@ -66,8 +71,8 @@ __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ h,
                                : *reinterpret_cast<const float4 *>(A + (int64_t)d * kDState + q * 4);
     const float a0 = scaled_A(av.x), a1 = scaled_A(av.y), a2 = scaled_A(av.z), a3 = scaled_A(av.w);
     const ComplexA ca0 = complex_A(av.x, av.y), ca1 = complex_A(av.z, av.w);
-    float4 hv[NR], bv[NR], cv[NR];
-    float xv[NR], dv[NR];
+    float4 hv[NR], bv[NR], cv[NR], bpv[NR];
+    float xv[NR], dv[NR], lv[NR], xpv[NR];
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
         // a missing last row re-reads the row before it and stores nothing
@@ -77,11 +82,24 @@ __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ h,
         dv[j] = E::load(dl + (int64_t)b * ld_xd + d);
         bv[j] = Quad<E>::load(Bt + (int64_t)b * ld_bc + q * 4);
         cv[j] = Quad<E>::load(Ct + (int64_t)b * ld_bc + q * 4);
+        if constexpr (kTrap) {
+            lv[j] = E::load(lam + (int64_t)b * ld_xd + d);
+            xpv[j] = E::load(xp + (int64_t)b * ld_xd + d);
+            bpv[j] = Quad<E>::load(bp + (int64_t)b * ld_bc + q * 4);
+        }
     }
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
         const int b = rg * NR + j;
-        const float dx = delta_x(dv[j], xv[j]);
+        float dx = delta_x(dv[j], xv[j]);
+        if constexpr (kTrap) {   // left end point in, then the update with q in place of delta * x
+            const float pl = trap_left(dv[j], lv[j], xpv[j]);
+            dx = trap_right(dv[j], lv[j], xv[j]);
+            hv[j].x = trap_left_in(hv[j].x, pl, bpv[j].x);
+            hv[j].y = trap_left_in(hv[j].y, pl, bpv[j].y);
+            hv[j].z = trap_left_in(hv[j].z, pl, bpv[j].z);
+            hv[j].w = trap_left_in(hv[j].w, pl, bpv[j].w);
+        }
         float4 hn;
         if constexpr (kComplexA) {
             hn = hv[j];

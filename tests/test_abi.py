@@ -12,7 +12,7 @@ import mamba_selective_scan_03_amd as jscan
 from mamba_selective_scan_03_amd import _binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OK, ENULL, ESHAPE, EDTYPE, EALIGN, EALIAS, EHIP, EWORKSPACE = range(8)
+OK, ENULL, ESHAPE, EDTYPE, EALIGN, EALIAS, EHIP, EWORKSPACE, EFORM = range(9)
 F32, BF16 = 0, 1
 P = 0x10000000  # a 16-byte aligned address that is never dereferenced
 
@@ -28,17 +28,18 @@ def test_header_symbols_are_exported():
     assert {"jscan_prefill", "jscan_prefill_resume", "jscan_step", "jscan_status_string",
             "jscan_last_hip_error", "jscan_version", "jscan_prefill_chunked",
             "jscan_prefill_chunked_workspace", "jscan_ssm_inputs", "jscan_prefill_fused", "jscan_prefill_scalar_a",
-            "jscan_step_scalar_a", "jscan_prefill_complex", "jscan_step_complex"} <= set(names)
+            "jscan_step_scalar_a", "jscan_prefill_complex", "jscan_step_complex", "jscan_prefill_trapezoid",
+            "jscan_step_trapezoid"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_status_strings_and_version():
     lib = jscan.library()
-    for s in range(8):
+    for s in range(9):
         assert lib.jscan_status_string(s) and lib.jscan_status_string(s) != b"unknown status"
     assert lib.jscan_status_string(99) == b"unknown status"
-    assert lib.jscan_version() == 105
+    assert lib.jscan_version() == 106
     assert lib.jscan_last_hip_error() == 0
 
 
@@ -249,3 +250,54 @@ def test_complex_entry_points_validate_like_the_general_ones():
                                   P + 0x600000, 2, 64, 16, 64, 16, 9, None) == EDTYPE
     assert lib.jscan_step_complex(P, P + 0x100000, P + 0x200000, None, P + 0x400000, P + 0x500000,
                                   P + 0x600000, 2, 64, 16, 64, 16, BF16, None) == ENULL
+
+
+def trap_prefill(x=P, d=P + 0x100000, lam=P + 0x700000, A=P + 0x200000, B=P + 0x300000, C=P + 0x400000, h0=None,
+                 xp=None, bp=None, y=P + 0x500000, h=P + 0x600000, batch=1, L=64, D=64, N=16, form=0, dtype=BF16):
+    return jscan.library().jscan_prefill_trapezoid(x, d, lam, A, B, C, h0, xp, bp, y, h, batch, L, D, N, form, dtype,
+                                                   None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(form=3), EFORM), (dict(form=-1), EFORM), (dict(dtype=5), EDTYPE), (dict(D=60), ESHAPE),
+    (dict(lam=None), ENULL), (dict(xp=P + 0x800000), ENULL), (dict(bp=P + 0x900000), ENULL), (dict(x=None), ENULL),
+    (dict(lam=P + 0x700008), EALIGN), (dict(xp=P + 0x800008, bp=P + 0x900000), EALIGN),
+    (dict(lam=P + 0x500000), EALIAS),                    # y overlaps lam
+    (dict(xp=P + 0x600000, bp=P + 0x900000), EALIAS),    # h_final overlaps x_prev
+    (dict(xp=P + 0x800000, bp=P + 0x500000 + 64), EALIAS),   # y overlaps B_prev
+])
+def test_prefill_trapezoid_validation(kw, code):
+    assert trap_prefill(**kw) == code
+
+
+def test_prefill_trapezoid_a_size_follows_the_form():
+    # A is [D][16] (4 KiB at D = 64) in the diagonal form: h_final 256 bytes past its start overlaps it
+    assert trap_prefill(A=P + 0x200000, h=P + 0x200000 + 256) == EALIAS
+    assert trap_prefill(A=P + 0x200000, h=P + 0x200000 + 256, form=2) == EALIAS
+
+
+def test_prefill_trapezoid_zero_sized_is_a_no_op():
+    assert trap_prefill(batch=0, x=None, lam=None, y=None, h=None, A=None) == OK
+
+
+def trap_step(h=P, xp=P + 0x700000, bp=P + 0x800000, x=P + 0x100000, d=P + 0x200000, lam=P + 0x900000,
+              A=P + 0x300000, B=P + 0x400000, C=P + 0x500000, y=P + 0x600000, batch=2, D=64, N=16, ld_xd=64,
+              ld_bc=16, form=0, dtype=BF16):
+    return jscan.library().jscan_step_trapezoid(h, xp, bp, x, d, lam, A, B, C, y, batch, D, N, ld_xd, ld_bc, form,
+                                                dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(form=7), EFORM), (dict(xp=None), ENULL), (dict(bp=None), ENULL), (dict(lam=None), ENULL),
+    (dict(lam=P + 0x900004), EALIGN), (dict(ld_xd=60), ESHAPE), (dict(y=P + 0x700000), EALIAS),
+    (dict(h=P + 0x900000 - 64), EALIAS), (dict(dtype=3), EDTYPE),
+])
+def test_step_trapezoid_validation(kw, code):
+    assert trap_step(**kw) == code
+
+
+def test_trapezoid_binding_checks_shapes():
+    x = torch.zeros(1, 8, 64)
+    with pytest.raises(ValueError):
+        jscan.prefill_trapezoid(x, x, x, torch.zeros(64, 16), torch.zeros(1, 8, 16), torch.zeros(1, 8, 16),
+                                form="nope")

@@ -24,6 +24,8 @@ Distributions (the same for every workload):
     complex A (pairs 2k, 2k+1 = real, imaginary part of entry k):
             real -(k + 1) * U(0.5, 1.5), imaginary pi * U(-1, 1), one draw per (d, k)
     h0      ~ N(0, 0.1)  (0.1 = standard deviation) decode workload's resident state
+    lam     = sigmoid(z),  z ~ N(0, 1)             evaluated in fp64: the exponential-trapezoidal
+                                                    rule's per-(token, channel) weight in (0, 1)
 bf16 workloads round every drawn value to bf16 by round-to-nearest-even (torch ``.to``).
 
 Seeding: every tensor is drawn block by block from
@@ -47,6 +49,7 @@ T_X, T_Z, T_B, T_C, T_A, T_H0 = 0, 1, 2, 3, 4, 5
 T_WX, T_GAIN, T_WDT, T_BDT = 6, 7, 8, 9     # producer-side weights
 T_ASC = 10                                  # scaled-identity A
 T_ACX = 11                                  # complex A
+T_LAM = 12                                  # trapezoidal-rule weights
 
 
 @dataclasses.dataclass(frozen=True)
@@ -117,6 +120,9 @@ def _draw_rows(wl: Workload, seed: int, tensor: int, row: int, t0: int, t1: int,
         if tensor == T_Z:
             z = rng.standard_normal((BLOCK, width), dtype=np.float64)
             vals = _softplus64(z - 2.0).astype(np.float32)
+        elif tensor == T_LAM:
+            z = rng.standard_normal((BLOCK, width), dtype=np.float64)
+            vals = (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
         else:
             vals = rng.standard_normal((BLOCK, width), dtype=np.float32)
         lo, hi = max(t0, b0), min(t1, b0 + BLOCK)
@@ -201,6 +207,16 @@ def prefill_inputs(name_or_wl, seed: int = 0, t0: int = 0, t1: int | None = None
     }
 
 
+def lam_inputs(name_or_wl, seed: int = 0, t0: int = 0, t1: int | None = None, threads: int | None = None):
+    """The exponential-trapezoidal rule's weights lam ``[batch, T, D]`` (workload dtype) for
+    tokens [t0, t1), drawn like the other inputs of :func:`prefill_inputs`."""
+    wl = get(name_or_wl)
+    t1 = wl.L if t1 is None else t1
+    if not 0 <= t0 < t1 <= wl.L + wl.extra_tokens:
+        raise ValueError("token range outside the workload")
+    return _draw_seq(wl, seed, T_LAM, wl.D, t0, t1, threads or min(16, os.cpu_count() or 1))
+
+
 def decode_layer_inputs(name_or_wl, layer: int, seed: int = 0, token: int = 0):
     """One layer of the batched-decode workload at one token step.
 
@@ -217,6 +233,8 @@ def decode_layer_inputs(name_or_wl, layer: int, seed: int = 0, token: int = 0):
         rng = _rng(seed, wl.wid, tensor, row, 0)
         if tensor == T_Z:
             v = _softplus64(rng.standard_normal((wl.batch, width), dtype=np.float64) - 2.0).astype(np.float32)
+        elif tensor == T_LAM:
+            v = (1.0 / (1.0 + np.exp(-rng.standard_normal((wl.batch, width), dtype=np.float64)))).astype(np.float32)
         else:
             v = rng.standard_normal((wl.batch, width), dtype=np.float32)
         return _to_dtype(v, wl)
@@ -230,6 +248,7 @@ def decode_layer_inputs(name_or_wl, layer: int, seed: int = 0, token: int = 0):
         "A": draw_A(wl, seed, layer),
         "B": mat(T_B, wl.N),
         "C": mat(T_C, wl.N),
+        "lam": mat(T_LAM, wl.D),   # used by the exponential-trapezoidal rule only
     }
 
 
