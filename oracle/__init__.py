@@ -20,7 +20,8 @@ A ``[D, N]``; B, C ``[batch, L, N]``; states ``[batch, D, N]``.
 (one value per channel, the Mamba-2 form); ``prefill_complex`` / ``step_complex`` run it with a
 complex-valued state (the Mamba-3 change); ``prefill_trapezoid`` / ``step_trapezoid`` replace the
 Euler rule by the exponential-trapezoidal one (the other Mamba-3 change), for any of the three
-forms of A.  ``oracle.producer`` is the fp64 (numpy) oracle
+forms of A; ``prefill_mimo`` / ``step_mimo`` give each channel R inputs and R outputs (MIMO, the third
+Mamba-3 change).  ``oracle.producer`` is the fp64 (numpy) oracle
 of the producer side that computes delta, B and C from x.
 """
 from __future__ import annotations
@@ -64,9 +65,11 @@ def _load():
     ci = ctypes.c_int
     lib.oracle_prefill_trapezoid_f64.argtypes = [dp] * 11 + [i64, i64, i64, i64, ci, ci]
     lib.oracle_step_trapezoid_f64.argtypes = [dp] * 10 + [i64, i64, i64, ci]
+    lib.oracle_prefill_mimo_f64.argtypes = [dp] * 8 + [i64, i64, i64, i64, i64, ci, ci]
+    lib.oracle_step_mimo_f64.argtypes = [dp] * 7 + [i64, i64, i64, i64, ci]
     for f in (lib.oracle_prefill_f64, lib.oracle_prefill_chunked_f64, lib.oracle_step_f64,
               lib.oracle_prefill_complex_f64, lib.oracle_step_complex_f64, lib.oracle_prefill_trapezoid_f64,
-              lib.oracle_step_trapezoid_f64):
+              lib.oracle_step_trapezoid_f64, lib.oracle_prefill_mimo_f64, lib.oracle_step_mimo_f64):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -288,4 +291,57 @@ def step_trapezoid(h, x_prev, B_prev, x_t, delta_t, lam_t, A, B_t, C_t, form: st
                                        _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(y), batch, D, N, int(cplx))
     if rc != 0:
         raise RuntimeError(f"oracle_step_trapezoid_f64 failed ({rc})")
+    return y, h
+
+
+# ---- multi-input, multi-output (MIMO, the third Mamba-3 change) ----------------------------
+# The lesson page ("Jamba - Hybrid SSM-Transformer", section "Mamba-3", item 3) replaces the
+# per-channel scalar projections by matrix-valued ones.  Each channel takes R inputs and gives
+# R outputs; B_t and C_t are N x R (jscan_oracle.c, scan_chain_mimo):
+#     h_t[d, n] = Abar_t[d, n] h_{t-1}[d, n] + Delta_t[d] sum_r B_t[n, r] x_t[d, r]
+#     y_t[d, r] = sum_n C_t[n, r] h_t[d, n]
+# Shapes: x, y [batch, L, D, R]; delta [batch, L, D]; B, C [batch, L, N, R].
+
+
+def prefill_mimo(x, delta, A, B, C, h0=None, form: str = "diagonal", nthreads: int = 0):
+    """Sequential fp64 MIMO scan.  Returns ``(y [batch, L, D, R], h_final [batch, D, N])``."""
+    lib = _load()
+    x, delta, B, C = (_f64(v) for v in (x, delta, B, C))
+    if x.ndim != 4 or B.ndim != 4:
+        raise ValueError("x must be [batch, L, D, R] and B, C [batch, L, N, R]")
+    batch, L, D, R = x.shape
+    N = B.shape[2]
+    A = _form_A(A, form, N)
+    h0 = None if h0 is None else _f64(h0)
+    if delta.shape != (batch, L, D) or B.shape != (batch, L, N, R) or C.shape != B.shape or A.shape != (D, N):
+        raise ValueError("prefill_mimo: inconsistent shapes")
+    if h0 is not None and h0.shape != (batch, D, N):
+        raise ValueError("h0 must be [batch, D, N]")
+    cplx = form == "complex"
+    y = np.empty((batch, L, D, R), np.float64)
+    h = np.empty((batch, D, N), np.float64)
+    rc = lib.oracle_prefill_mimo_f64(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(h0), _ptr(y), _ptr(h),
+                                     batch, L, D, N, R, int(cplx), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_prefill_mimo_f64 failed ({rc})")
+    return y, h
+
+
+def step_mimo(h, x_t, delta_t, A, B_t, C_t, form: str = "diagonal"):
+    """One MIMO decode step.  Returns ``(y_t [batch, D, R], h_new)``; the input h is not modified."""
+    lib = _load()
+    h = _f64(h).copy()
+    x_t, delta_t, B_t, C_t = (_f64(v) for v in (x_t, delta_t, B_t, C_t))
+    batch, D, N = h.shape
+    A = _form_A(A, form, N)
+    if x_t.ndim != 3 or x_t.shape[:2] != (batch, D):
+        raise ValueError("step_mimo: x_t must be [batch, D, R]")
+    R = x_t.shape[2]
+    if delta_t.shape != (batch, D) or B_t.shape != (batch, N, R) or C_t.shape != (batch, N, R) or A.shape != (D, N):
+        raise ValueError("step_mimo: inconsistent shapes")
+    y = np.empty((batch, D, R), np.float64)
+    rc = lib.oracle_step_mimo_f64(_ptr(h), _ptr(x_t), _ptr(delta_t), _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(y),
+                                  batch, D, N, R, int(form == "complex"))
+    if rc != 0:
+        raise RuntimeError(f"oracle_step_mimo_f64 failed ({rc})")
     return y, h

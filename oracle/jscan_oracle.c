@@ -44,6 +44,7 @@ typedef struct {
     int trap;                     /* exponential-trapezoidal rule (see scan_chain_trapezoid) */
     const double *lam;            /* trapezoid weights [batch][L][D] */
     const double *x_prev, *B_prev; /* token before the first: [batch][D], [batch][N]; NULL = none */
+    int64_t R;                    /* MIMO rank (see scan_chain_mimo); 0 = single input and output */
     int64_t item_begin, item_end; /* items are (b, d) pairs, item = b * D + d */
 } scan_job;
 
@@ -255,12 +256,96 @@ static void scan_chain_trapezoid_complex(const scan_job *j, int64_t b, int64_t d
     free(u_prev);
 }
 
+/*
+ * Multi-input, multi-output (MIMO) scan: the third Mamba-3 change named on the lesson page
+ * ("Jamba - Hybrid SSM-Transformer", section "Mamba-3", item 3), where the per-channel scalar
+ * input and output projections become matrix-valued.  Each channel d takes R inputs
+ * x_t[d][r] and gives R outputs y_t[d][r]; B_t and C_t are N x R matrices shared by all
+ * channels.  The state keeps its size; its input is a rank-R sum instead of one product:
+ *
+ *     h_t[d][n] = Abar_t[d][n] h_{t-1}[d][n] + Delta_t[d] * sum_r B_t[n][r] x_t[d][r]
+ *     y_t[d][r] = sum_n C_t[n][r] h_t[d][n]
+ *
+ * R = 1 is the single-input scan.  Layouts: x, y [batch][L][D][R]; B, C [batch][L][N][R].
+ * With cplx set the state is complex as in scan_chain_complex: pairs (2k, 2k+1) of states,
+ * of A's entries and of B's and C's rows (for each r) are complex numbers, and
+ * y_t[d][r] = sum_k Re(conj(c_k,r) h_t[k]).
+ */
+static void scan_chain_mimo(const scan_job *j, int64_t b, int64_t d)
+{
+    const int64_t L = j->L, D = j->D, N = j->N, R = j->R;
+    double *h = (double *)malloc((size_t)N * sizeof(double));
+    for (int64_t n = 0; n < N; ++n)
+        h[n] = j->h0 ? j->h0[(b * D + d) * N + n] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+        const double delta_t = j->delta[(b * L + t) * D + d];
+        const double *x_t = j->x + ((b * L + t) * D + d) * R;
+        const double *B_t = j->B + (b * L + t) * N * R;
+        const double *C_t = j->C + (b * L + t) * N * R;
+        double *y_t = j->y + ((b * L + t) * D + d) * R;
+        for (int64_t n = 0; n < N; ++n) {
+            double u = 0.0;
+            for (int64_t r = 0; r < R; ++r)
+                u += B_t[n * R + r] * x_t[r];
+            h[n] = exp(delta_t * j->A[d * N + n]) * h[n] + delta_t * u;
+        }
+        for (int64_t r = 0; r < R; ++r) {
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n)
+                acc += C_t[n * R + r] * h[n];
+            y_t[r] = acc;
+        }
+    }
+    if (j->h_final)
+        for (int64_t n = 0; n < N; ++n)
+            j->h_final[(b * D + d) * N + n] = h[n];
+    free(h);
+}
+
+static void scan_chain_mimo_complex(const scan_job *j, int64_t b, int64_t d)
+{
+    const int64_t L = j->L, D = j->D, N = j->N, R = j->R, K = N / 2;
+    double complex *h = (double complex *)malloc((size_t)K * sizeof(double complex));
+    for (int64_t k = 0; k < K; ++k)
+        h[k] = j->h0 ? j->h0[(b * D + d) * N + 2 * k] + I * j->h0[(b * D + d) * N + 2 * k + 1] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+        const double delta_t = j->delta[(b * L + t) * D + d];
+        const double *x_t = j->x + ((b * L + t) * D + d) * R;
+        const double *B_t = j->B + (b * L + t) * N * R;
+        const double *C_t = j->C + (b * L + t) * N * R;
+        double *y_t = j->y + ((b * L + t) * D + d) * R;
+        for (int64_t k = 0; k < K; ++k) {
+            const double complex a = j->A[d * N + 2 * k] + I * j->A[d * N + 2 * k + 1];
+            double complex u = 0.0;
+            for (int64_t r = 0; r < R; ++r)
+                u += (B_t[2 * k * R + r] + I * B_t[(2 * k + 1) * R + r]) * x_t[r];
+            h[k] = cexp(delta_t * a) * h[k] + delta_t * u;
+        }
+        for (int64_t r = 0; r < R; ++r) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += creal(conj(C_t[2 * k * R + r] + I * C_t[(2 * k + 1) * R + r]) * h[k]);
+            y_t[r] = acc;
+        }
+    }
+    if (j->h_final)
+        for (int64_t k = 0; k < K; ++k) {
+            j->h_final[(b * D + d) * N + 2 * k] = creal(h[k]);
+            j->h_final[(b * D + d) * N + 2 * k + 1] = cimag(h[k]);
+        }
+    free(h);
+}
+
 static void *scan_worker(void *arg)
 {
     const scan_job *j = (const scan_job *)arg;
     for (int64_t item = j->item_begin; item < j->item_end; ++item) {
         const int64_t b = item / j->D, d = item % j->D;
-        if (j->trap && j->cplx)
+        if (j->R > 0 && j->cplx)
+            scan_chain_mimo_complex(j, b, d);
+        else if (j->R > 0)
+            scan_chain_mimo(j, b, d);
+        else if (j->trap && j->cplx)
             scan_chain_trapezoid_complex(j, b, d);
         else if (j->trap)
             scan_chain_trapezoid(j, b, d);
@@ -465,4 +550,41 @@ int oracle_step_trapezoid_f64(double *h, const double *x_prev, const double *B_p
         }
     }
     return 0;
+}
+
+/*
+ * MIMO prefill (scan_chain_mimo, or its complex form when cplx is set): x, y [batch][L][D][R],
+ * delta [batch][L][D], B, C [batch][L][N][R], R >= 1.
+ */
+int oracle_prefill_mimo_f64(const double *x, const double *delta, const double *A, const double *B, const double *C,
+                            const double *h0, double *y, double *h_final, int64_t batch, int64_t L, int64_t D,
+                            int64_t N, int64_t R, int cplx, int nthreads)
+{
+    if (R < 1 || (cplx && N % 2 != 0))
+        return -1;
+    scan_job j;
+    memset(&j, 0, sizeof j);
+    j.x = x; j.delta = delta; j.A = A; j.B = B; j.C = C; j.h0 = h0;
+    j.y = y; j.h_final = h_final;
+    j.batch = batch; j.L = L; j.D = D; j.N = N; j.R = R; j.cplx = cplx;
+    return run_scan(j, nthreads);
+}
+
+/* One MIMO decode step: h [batch][D][N] in place; x_t, y_t [batch][D][R]; B_t, C_t [batch][N][R]. */
+int oracle_step_mimo_f64(double *h, const double *x_t, const double *delta_t, const double *A, const double *B_t,
+                         const double *C_t, double *y_t, int64_t batch, int64_t D, int64_t N, int64_t R, int cplx)
+{
+    /* one token of the prefill is exactly one step: run the chain over L = 1 from h */
+    if (R < 1 || (cplx && N % 2 != 0))
+        return -1;
+    double *hout = (double *)malloc((size_t)(batch * D * N) * sizeof(double));
+    scan_job j;
+    memset(&j, 0, sizeof j);
+    j.x = x_t; j.delta = delta_t; j.A = A; j.B = B_t; j.C = C_t; j.h0 = h;
+    j.y = y_t; j.h_final = hout;
+    j.batch = batch; j.L = 1; j.D = D; j.N = N; j.R = R; j.cplx = cplx;
+    const int rc = run_scan(j, 1);
+    memcpy(h, hout, (size_t)(batch * D * N) * sizeof(double));
+    free(hout);
+    return rc;
 }
