@@ -27,7 +27,12 @@ slots and 21 flops per token (decay, rotation by a hardware sine and cosine, com
 output): 9.5 slots and 10.5 flops per element, a bound of 43.4 TFLOP/s.  --trapezoid (the
 exponential-trapezoidal rule of Mamba-3, with any of the three forms of A) adds one fused
 multiply-add per element, the previous token's input taken in before the decay: one slot and
-two flops more than the form's own count, and lam [B, L, D] to the bytes read.
+two flops more than the form's own count, and lam [B, L, D] to the bytes read.  --mimo R (R
+inputs and outputs per channel, B and C N x R: the MIMO scan of Mamba-3) makes the input term a
+rank-R sum (one product and R - 1 fused multiply-adds) and the output R fused multiply-adds per
+element: 2R + 4 slots and 4R + 3 flops for the diagonal A (12 and 19 at R = 4), 2R + 1 + 3/16
+and 4R + 1 + 2/16 for the scaled identity, (15 + 4R) / 2 and (8R + 13) / 2 for the complex state;
+x and y grow R-fold in bytes.
 """
 from __future__ import annotations
 
@@ -57,6 +62,15 @@ SCALAR_A_FLOPS = 5 + 2 / 16
 COMPLEX_A_SLOTS = 19 / 2
 COMPLEX_A_FLOPS = 21 / 2
 TRAP_SLOTS, TRAP_FLOPS = 1, 2                 # the left end point's fma, on top of the form's count
+
+
+def mimo_cost(form: str, R: int):
+    """(issue slots, flops) per state element of the rank-R scan; R = 1 gives the single-input counts."""
+    if form == "scalar":
+        return 2 * R + 1 + 3 / 16, 4 * R + 1 + 2 / 16
+    if form == "complex":
+        return (15 + 4 * R) / 2, (8 * R + 13) / 2
+    return 2 * R + 4, 4 * R + 3
 KERNEL_SOURCES = {
     "prefill": ["scan_update.h", "mfma_common.h", "prefill_rows_kernel.h"],
     "step": ["scan_update.h", "step_kernel.h"],
@@ -73,10 +87,19 @@ def kernel_source_hash(kind: str) -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(wl, trapezoid: bool = False) -> int:
+def algorithmic_bytes(wl, trapezoid: bool = False, mimo: int = 0) -> int:
     """Bytes a step must move at least.  The trapezoidal rule also reads lam (like delta) and,
-    in decode, the previous token's x and B rows."""
+    in decode, the previous token's x and B rows.  A rank-R MIMO scan has R values per channel
+    in x and y and N x R in B and C."""
     es = 4 if wl.dtype == "f32" else 2
+    if mimo:
+        R = mimo
+        if wl.layers > 1:
+            per_layer = (2 * wl.batch * wl.D * wl.N * 4 + (2 * R + 1) * wl.batch * wl.D * es
+                         + 2 * wl.batch * wl.N * R * es + wl.D * wl.N * 4)
+            return per_layer * wl.layers
+        return ((2 * R + 1) * wl.batch * wl.L * wl.D * es + 2 * wl.batch * wl.L * wl.N * R * es
+                + wl.D * wl.N * 4 + wl.batch * wl.D * wl.N * 4)
     if wl.layers > 1:  # decode: state read + write, token rows in and out, A, per layer
         per_layer = 2 * wl.batch * wl.D * wl.N * 4 + 3 * wl.batch * wl.D * es + 2 * wl.batch * wl.N * es + wl.D * wl.N * 4
         if trapezoid:
@@ -106,7 +129,7 @@ def read_traffic(workload: str, launches_per_step: int):
         return None
 
 
-def cpu_baseline(wl, inp, channels: int, scalar_a=None, complex_a=False, lam=None):
+def cpu_baseline(wl, inp, channels: int, scalar_a=None, complex_a=False, lam=None, mimo=0):
     """The fp64 oracle, as it stands, on a bounded sample: all tokens of `channels` channels
     (with `scalar_a`, the scaled-identity oracle on that A; with `complex_a`, the complex-state
     oracle on inp["A"]; with `lam`, the exponential-trapezoidal oracle)."""
@@ -121,8 +144,10 @@ def cpu_baseline(wl, inp, channels: int, scalar_a=None, complex_a=False, lam=Non
     args = [np.ascontiguousarray(t.float().numpy(), dtype=np.float64) for t in (x, dl, A, inp["B"], inp["C"])]
     fn = oracle.prefill_complex if complex_a else oracle.prefill if scalar_a is None else oracle.prefill_scalar_a
     t0 = time.perf_counter()
-    if lam is not None:
-        form = "complex" if complex_a else "diagonal" if scalar_a is None else "scalar"
+    form = "complex" if complex_a else "diagonal" if scalar_a is None else "scalar"
+    if mimo:
+        oracle.prefill_mimo(*args, form=form, nthreads=threads)
+    elif lam is not None:
         lm = np.ascontiguousarray(lam[:, :, :channels].float().numpy(), dtype=np.float64)
         oracle.prefill_trapezoid(args[0], args[1], lm, *args[2:], form=form, nthreads=threads)
     else:
@@ -159,6 +184,9 @@ def main():
     ap.add_argument("--trapezoid", action="store_true",
                     help="the exponential-trapezoidal rule (the Mamba-3 discretisation), with the diagonal A or "
                          "with --scalar-a / --complex-a: jscan_prefill_trapezoid / jscan_step_trapezoid")
+    ap.add_argument("--mimo", type=int, default=0, metavar="R", choices=[0, 1, 2, 4, 8],
+                    help="the MIMO scan with R inputs and outputs per channel (B and C N x R), with the diagonal A "
+                         "or with --scalar-a / --complex-a: jscan_prefill_mimo / jscan_step_mimo")
     ap.add_argument("--cpu-channels", type=int, default=8192,
                     help="oracle sample: all tokens of the first CPU_CHANNELS channels (default: every channel "
                          "of the 64K workload, a few seconds on 16 cores; 0 = skip)")
@@ -199,9 +227,12 @@ def main():
                           "ms_per_launch": ms, "GBps": 2 * n * 4 / ms / 1e6}), flush=True)
         return
     wl = workloads.get(args.workload)
-    if (args.scalar_a or args.complex_a or args.trapezoid) and (args.producer or args.chunked):
-        print("bench.py: --scalar-a, --complex-a and --trapezoid run the plain prefill or decode step only",
+    if (args.scalar_a or args.complex_a or args.trapezoid or args.mimo) and (args.producer or args.chunked):
+        print("bench.py: --scalar-a, --complex-a, --trapezoid and --mimo run the plain prefill or decode step only",
               file=sys.stderr)
+        sys.exit(2)
+    if args.trapezoid and args.mimo:
+        print("bench.py: the library does not combine --trapezoid with --mimo", file=sys.stderr)
         sys.exit(2)
     if args.scalar_a and args.complex_a:
         print("bench.py: choose one of --scalar-a and --complex-a", file=sys.stderr)
@@ -215,7 +246,11 @@ def main():
         layers = []
         for layer in range(wl.layers):
             # the trapezoidal rule's step is token 1, with token 0 as its previous token
-            inp = workloads.decode_layer_inputs(wl, layer, token=1 if args.trapezoid else 0)
+            if args.mimo:
+                inp = workloads.decode_layer_mimo_inputs(wl, layer, args.mimo)
+                inp["lam"] = None
+            else:
+                inp = workloads.decode_layer_inputs(wl, layer, token=1 if args.trapezoid else 0)
             if args.trapezoid:
                 prev = workloads.decode_layer_inputs(wl, layer, token=0)
                 inp["x_prev"], inp["B_prev"] = prev["x"], prev["B"]
@@ -225,7 +260,7 @@ def main():
                 inp["A"] = workloads.draw_scalar_a(wl, layer=layer)
             if args.complex_a:
                 inp["A"] = workloads.draw_complex_a(wl, layer=layer)
-            layers.append({k: v.to(dev) for k, v in inp.items()})
+            layers.append({k: v.to(dev) for k, v in inp.items() if v is not None})
             layers[-1]["h"] = layers[-1].pop("h0")
 
         for L_ in layers:
@@ -234,7 +269,9 @@ def main():
 
         def token_step():
             for L_ in layers:
-                if args.trapezoid:
+                if args.mimo:
+                    jscan.step_mimo(L_["h"], L_["x"], L_["delta"], L_["A"], L_["B"], L_["C"], form=form, y_t=L_["y"])
+                elif args.trapezoid:
                     jscan.step_trapezoid(L_["h"], L_["x_prev"], L_["B_prev"], L_["x"], L_["delta"], L_["lam"],
                                          L_["A"], L_["B"], L_["C"], form=form, y_t=L_["y"])
                 else:
@@ -256,7 +293,7 @@ def main():
         launches = wl.layers
         host_inp = None
     else:
-        host_inp = workloads.prefill_inputs(wl)
+        host_inp = workloads.mimo_inputs(wl, args.mimo) if args.mimo else workloads.prefill_inputs(wl)
         d = {k: v.to(dev) for k, v in host_inp.items()}
         y = torch.empty_like(d["x"])
         h = torch.empty((wl.batch, wl.D, wl.N), dtype=torch.float32, device=dev)
@@ -298,6 +335,17 @@ def main():
             def one_step():
                 jscan.prefill_chunked(d["x"], d["delta"], d["A"], d["B"], d["C"], y=y, h_final=h, workspace=ws)
             launches = 3 if ws_bytes > 0 else 1
+        elif args.mimo:
+            if args.scalar_a:
+                host_a = workloads.draw_scalar_a(wl)
+                d["A"] = host_a.to(dev)
+            elif args.complex_a:
+                host_inp["A"] = workloads.draw_complex_a(wl)
+                d["A"] = host_inp["A"].to(dev)
+
+            def one_step():
+                jscan.prefill_mimo(d["x"], d["delta"], d["A"], d["B"], d["C"], form=form, y=y, h_final=h)
+            launches = 1
         elif args.trapezoid:
             host_inp["lam"] = workloads.lam_inputs(wl)
             d["lam"] = host_inp["lam"].to(dev)
@@ -351,7 +399,7 @@ def main():
 
     elems = wl.elems
     value = elems / (ms_step * 1e-3)
-    alg_bytes = algorithmic_bytes(wl, args.trapezoid)
+    alg_bytes = algorithmic_bytes(wl, args.trapezoid, args.mimo)
     if args.scalar_a:   # A is [D] instead of [D, N]
         alg_bytes -= (wl.D * wl.N - wl.D) * 4 * max(wl.layers, 1)
     gbps = alg_bytes / (ms_step * 1e-3) / 1e9
@@ -399,13 +447,15 @@ def main():
                         (SLOTS_PER_STATE_ELEM, FLOPS_PER_STATE_ELEM))
         if args.trapezoid:
             slots, flops = slots + TRAP_SLOTS, flops + TRAP_FLOPS
+        if args.mimo:
+            slots, flops = mimo_cost(form, args.mimo)
         achieved_tf = state_elems * flops / (per_launch_ms * 1e-3) / 1e12
         peak_tf = VALU_SLOTS_PER_S / slots * flops / 1e12
         roofline = {"bound": "alu", "achieved": round(achieved_tf, 2), "peak": round(peak_tf, 2), "unit": "TFLOP/s",
                     "frac": round(achieved_tf / peak_tf, 4)}
     roofline["traffic"] = None if (args.chunked or args.producer) else read_traffic(
         wl.name + ("_scalar_a" if args.scalar_a else "_complex_a" if args.complex_a else "")
-        + ("_trapezoid" if args.trapezoid else ""), launches)
+        + ("_trapezoid" if args.trapezoid else "") + (f"_mimo{args.mimo}" if args.mimo else ""), launches)
 
     out = {
         "metric": METRIC,
@@ -424,6 +474,7 @@ def main():
                    "layers": wl.layers, "io_dtype": wl.dtype, "state_dtype": "f32",
                    "A": "scaled_identity" if args.scalar_a else "complex_pairs" if args.complex_a else "diagonal",
                    "discretisation": "exponential-trapezoidal" if args.trapezoid else "euler",
+                   "mimo_rank": args.mimo or 1,
                    "path": ("producer+fused-scan" if args.fused else "producer+scan") if args.producer
                    else ("time-parallel" if args.chunked else "sequential")},
         "hbm_GBps": round(gbps, 1),
@@ -436,7 +487,7 @@ def main():
     if host_inp is not None and args.cpu_channels > 0 and wl.layers == 1:
         out["cpu_baseline"] = cpu_baseline(wl, host_inp, min(args.cpu_channels, wl.D),
                                            host_a if args.scalar_a else None, complex_a=args.complex_a,
-                                           lam=host_inp.get("lam") if args.trapezoid else None)
+                                           lam=host_inp.get("lam") if args.trapezoid else None, mimo=args.mimo)
         log(f"oracle sample: {out['cpu_baseline']['sample']}")
     print(json.dumps(out), flush=True)
 

@@ -309,6 +309,40 @@ jscan_status jscan_step_trapezoid(float *h, const void *x_prev, const void *B_pr
                                   int64_t ld_xd, int64_t ld_bc, jscan_a_form a_form, jscan_dtype dtype,
                                   void *stream);
 
+/*
+ * Multi-input, multi-output (MIMO) scan, the Mamba-3 replacement of the per-channel scalar
+ * projections by matrix-valued ones (lesson page "Jamba - Hybrid SSM-Transformer", section
+ * "Mamba-3", item 3).  Each channel takes R inputs and gives R outputs; B_t and C_t are N x R
+ * matrices shared by the channels; the state keeps its [batch][D][N] size:
+ *
+ *     h_t[d][n] = exp(delta_t[d] a) h_{t-1}[d][n] + sum_r (delta_t[d] * x_t[d][r]) * B_t[n][r]
+ *     y_t[d][r] = sum_n C_t[n][r] * h_t[d][n]
+ *
+ * with the sum over r accumulated in increasing r (first product, then fmaf), and the decay a
+ * of any form of A (jscan_a_form; with JSCAN_A_COMPLEX the state pairs, and B's and C's row
+ * pairs for each r, are complex numbers).  R = 1 is the single-input scan of the form's
+ * entry point, bit for bit in the state.  R must be 1, 2, 4 or 8 (else JSCAN_ERR_SHAPE).
+ *
+ * Prefill from h0 (NULL: zero state).  Layouts:
+ *     x, y : [batch][L][D][R]     delta : [batch][L][D]     B, C : [batch][L][N][R]
+ * Other arguments, ownership, errors (plus JSCAN_ERR_FORM) and the bit-identity of h_final
+ * with the jscan_step_mimo chain are as for jscan_prefill_resume.
+ */
+jscan_status jscan_prefill_mimo(const void *x, const void *delta, const float *A, const void *B,
+                                const void *C, const float *h0, void *y, float *h_final,
+                                int64_t batch, int64_t L, int64_t D, int64_t N, int64_t R,
+                                jscan_a_form a_form, jscan_dtype dtype, void *stream);
+
+/*
+ * One MIMO decode token for a batch, h [batch][D][N] in place.  x_t and y_t are rows of D * R
+ * with row stride ld_x; delta_t rows of D with stride ld_d; B_t and C_t rows of N * R with
+ * stride ld_bc (strides in elements, multiples of 8, at least the row length).
+ */
+jscan_status jscan_step_mimo(float *h, const void *x_t, const void *delta_t, const float *A,
+                             const void *B_t, const void *C_t, void *y_t, int64_t batch, int64_t D,
+                             int64_t N, int64_t R, int64_t ld_x, int64_t ld_d, int64_t ld_bc,
+                             jscan_a_form a_form, jscan_dtype dtype, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *jscan_status_string(jscan_status s);
 
@@ -317,7 +351,7 @@ int jscan_last_hip_error(void);
 
 /* Library ABI version: 100 * major + minor (101 adds the time-parallel prefill, 102 the
  * producer side, 103 the fused prefill, 104 the scaled-identity A entry points, 105 the
- * complex-valued state, 106 the exponential-trapezoidal rule). */
+ * complex-valued state, 106 the exponential-trapezoidal rule, 107 the MIMO scan). */
 int jscan_version(void);
 
 #ifdef __cplusplus

@@ -55,10 +55,12 @@ def library():
     lib.jscan_step_complex.argtypes = [fp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
     lib.jscan_prefill_trapezoid.argtypes = [vp, vp, vp, fp, vp, vp, fp, vp, vp, vp, fp, i64, i64, i64, i64, i32, i32, vp]
     lib.jscan_step_trapezoid.argtypes = [fp, vp, vp, vp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp]
+    lib.jscan_prefill_mimo.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, i64, i32, i32, vp]
+    lib.jscan_step_mimo.argtypes = [fp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32, i32, vp]
     lib.jscan_prefill_chunked_workspace.restype = i64
     for f in (lib.jscan_prefill, lib.jscan_prefill_resume, lib.jscan_step, lib.jscan_prefill_chunked,
               lib.jscan_prefill_scalar_a, lib.jscan_step_scalar_a, lib.jscan_prefill_complex, lib.jscan_step_complex,
-              lib.jscan_prefill_trapezoid, lib.jscan_step_trapezoid):
+              lib.jscan_prefill_trapezoid, lib.jscan_step_trapezoid, lib.jscan_prefill_mimo, lib.jscan_step_mimo):
         f.restype = i32
     lib.jscan_status_string.argtypes = [i32]
     lib.jscan_status_string.restype = ctypes.c_char_p
@@ -382,5 +384,73 @@ def step_trapezoid(h, x_prev, B_prev, x_t, delta_t, lam_t, A, B_t, C_t, form="di
         st = lib.jscan_step_trapezoid(_ptr(h), _ptr(x_prev), _ptr(B_prev), _ptr(x_t), _ptr(delta_t), _ptr(lam_t),
                                       _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(y_t), batch, D, D_STATE, ld_xd, ld_bc,
                                       A_FORMS[form], _DTYPES[x_t.dtype], _stream(h.device))
+    _check(st)
+    return y_t
+
+
+# ---- multi-input, multi-output (MIMO) --------------------------------------------------------
+
+def prefill_mimo(x, delta, A, B, C, h0=None, form="diagonal", y=None, h_final=None):
+    """MIMO prefill (``jscan_prefill_mimo``): each channel takes R inputs and gives R outputs.
+    x ``[batch, L, D, R]``, delta ``[batch, L, D]``, B, C ``[batch, L, 16, R]`` (one dtype),
+    A as for ``form`` ("diagonal" ``[D, 16]``, "scalar" ``[D]``, "complex" ``[D, 16]``), optional
+    h0 ``[batch, D, 16]``; R is 1, 2, 4 or 8.  Returns ``(y [batch, L, D, R], h_final)``."""
+    _require(form in A_FORMS, f"form must be one of {tuple(A_FORMS)}")
+    _require(x.is_cuda and x.dtype in _DTYPES and x.dim() == 4 and x.is_contiguous(),
+             "x must be a contiguous [batch, L, D, R] CUDA tensor (bfloat16 or float32)")
+    batch, L, D, R = x.shape
+    a_shape = (D,) if form == "scalar" else (D, D_STATE)
+    for name, t, shape, dt in (("delta", delta, (batch, L, D), x.dtype), ("A", A, a_shape, torch.float32),
+                               ("B", B, (batch, L, D_STATE, R), x.dtype), ("C", C, (batch, L, D_STATE, R), x.dtype)):
+        _require(tuple(t.shape) == shape, f"{name} must have shape {shape}, got {tuple(t.shape)}")
+        _require(t.dtype == dt and t.is_contiguous() and t.device == x.device, f"{name} must be a contiguous {dt} "
+                 "tensor on x's device")
+    if h0 is not None:
+        _require(tuple(h0.shape) == (batch, D, D_STATE) and h0.dtype == torch.float32 and h0.is_contiguous()
+                 and h0.device == x.device, "h0 must be a contiguous fp32 [batch, D, 16] tensor on x's device")
+    if y is None:
+        y = torch.empty_like(x)
+    if h_final is None:
+        h_final = torch.empty((batch, D, D_STATE), dtype=torch.float32, device=x.device)
+    lib = library()
+    with torch.cuda.device(x.device):
+        st = lib.jscan_prefill_mimo(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(h0), _ptr(y), _ptr(h_final),
+                                    batch, L, D, D_STATE, R, A_FORMS[form], _DTYPES[x.dtype], _stream(x.device))
+    _check(st)
+    return y, h_final
+
+
+def step_mimo(h, x_t, delta_t, A, B_t, C_t, form="diagonal", y_t=None):
+    """One MIMO decode token (``jscan_step_mimo``): h ``[batch, D, 16]`` fp32 in place; x_t
+    ``[batch, D, R]``, delta_t ``[batch, D]``, B_t, C_t ``[batch, 16, R]`` (each row contiguous;
+    rows may be strided views of prefill tensors, e.g. ``x[:, t]``).  Returns y_t ``[batch, D, R]``."""
+    _require(form in A_FORMS, f"form must be one of {tuple(A_FORMS)}")
+    _require(h.is_cuda and h.dtype == torch.float32 and h.dim() == 3 and h.shape[2] == D_STATE and h.is_contiguous(),
+             "h must be a contiguous fp32 [batch, D, 16] CUDA tensor")
+    batch, D, _ = h.shape
+    _require(x_t.dim() == 3 and x_t.shape[:2] == (batch, D) and x_t.dtype in _DTYPES, "x_t must be [batch, D, R]")
+    R = x_t.shape[2]
+    _require(x_t.stride(2) == 1 and x_t.stride(1) == R, "x_t rows must be contiguous")
+    _require(tuple(delta_t.shape) == (batch, D) and delta_t.stride(1) == 1 and delta_t.dtype == x_t.dtype,
+             "delta_t must be [batch, D] with contiguous rows, x_t's dtype")
+    for name, t in (("B_t", B_t), ("C_t", C_t)):
+        _require(tuple(t.shape) == (batch, D_STATE, R) and t.dtype == x_t.dtype and t.stride(2) == 1
+                 and t.stride(1) == R, f"{name} must be [batch, 16, R] with contiguous rows, x_t's dtype")
+    a_shape = (D,) if form == "scalar" else (D, D_STATE)
+    _require(A.dtype == torch.float32 and tuple(A.shape) == a_shape and A.is_contiguous(),
+             f"A must be a contiguous fp32 tensor of shape {a_shape}")
+    ld_x = x_t.stride(0) if batch > 1 else D * R
+    ld_d = delta_t.stride(0) if batch > 1 else D
+    ld_bc = B_t.stride(0) if batch > 1 else D_STATE * R
+    _require(batch <= 1 or C_t.stride(0) == ld_bc, "B_t and C_t must share a row stride")
+    if y_t is None:
+        y_t = torch.empty((batch, ld_x), dtype=x_t.dtype, device=h.device)[:, :D * R].view(batch, D, R)
+    _require(tuple(y_t.shape) == (batch, D, R) and y_t.dtype == x_t.dtype and y_t.stride(2) == 1
+             and y_t.stride(1) == R and (batch <= 1 or y_t.stride(0) == ld_x), "y_t must be [batch, D, R] with x_t's "
+             "row stride")
+    lib = library()
+    with torch.cuda.device(h.device):
+        st = lib.jscan_step_mimo(_ptr(h), _ptr(x_t), _ptr(delta_t), _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(y_t), batch, D,
+                                 D_STATE, R, ld_x, ld_d, ld_bc, A_FORMS[form], _DTYPES[x_t.dtype], _stream(h.device))
     _check(st)
     return y_t

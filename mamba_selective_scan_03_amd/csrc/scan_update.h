@@ -37,9 +37,23 @@ __device__ __forceinline__ float decay(float delta, float a2) {
 // The fp32 product delta * x, shared by the 16 states of one channel.
 __device__ __forceinline__ float delta_x(float delta, float x) { return delta * x; }
 
-// One state element advanced by one token, given its decay:  h <- Abar * h + (delta * x) * B.
+// One state element advanced by one token, given its decay and its input term u:  h <- Abar * h + u.
+__device__ __forceinline__ float advance_input(float h, float abar, float u) { return __builtin_fmaf(abar, h, u); }
+
+// The same with the single-input term u = (delta * x) * B.
 __device__ __forceinline__ float advance_decayed(float h, float abar, float dx, float b) {
-    return __builtin_fmaf(abar, h, dx * b);
+    return advance_input(h, abar, dx * b);
+}
+
+// Multi-input (MIMO) term of one state element: u = sum_r (delta * x_r) * B[r], accumulated in
+// increasing r (the first product rounded, then one fused multiply-add per rank).  With R = 1
+// it is the single-input term (delta * x) * B.
+template <int R>
+__device__ __forceinline__ float mimo_input(const float (&dx)[R], const float *b) {
+    float u = dx[0] * b[0];
+#pragma unroll
+    for (int r = 1; r < R; ++r) u = __builtin_fmaf(dx[r], b[r], u);
+    return u;
 }
 
 // The same with the decay evaluated here, from delta and A2.
@@ -69,15 +83,21 @@ __device__ __forceinline__ ComplexA complex_A(float re, float im) { return Compl
 // exp(delta a) = 2^(delta A2) (cos phi + i sin phi), phi = delta im in turns, reduced to [0, 1)
 // first so that the hardware sine and cosine see a small argument.  The real-part update is
 // fma(r cos, h_re, fma(-r sin, h_im, (delta x) b_re)), the imaginary one mirrors it.
-__device__ __forceinline__ void advance_complex(float &h_re, float &h_im, float delta, ComplexA a, float dx,
-                                                float b_re, float b_im) {
+// The same given the complex input term u = (u_re, u_im), which is (delta x) b above and the
+// rank-R sum of such terms in a MIMO scan.
+__device__ __forceinline__ void advance_complex_input(float &h_re, float &h_im, float delta, ComplexA a, float u_re,
+                                                      float u_im) {
     const float r = decay(delta, a.a2);
     const float phi = __builtin_amdgcn_fractf(delta * a.turns);
     const float rc = r * __builtin_amdgcn_cosf(phi), rs = r * __builtin_amdgcn_sinf(phi);
-    const float re = __builtin_fmaf(rc, h_re, __builtin_fmaf(-rs, h_im, dx * b_re));
-    const float im = __builtin_fmaf(rc, h_im, __builtin_fmaf(rs, h_re, dx * b_im));
+    const float re = __builtin_fmaf(rc, h_re, __builtin_fmaf(-rs, h_im, u_re));
+    const float im = __builtin_fmaf(rc, h_im, __builtin_fmaf(rs, h_re, u_im));
     h_re = re;
     h_im = im;
+}
+__device__ __forceinline__ void advance_complex(float &h_re, float &h_im, float delta, ComplexA a, float dx,
+                                                float b_re, float b_im) {
+    advance_complex_input(h_re, h_im, delta, a, dx * b_re, dx * b_im);
 }
 
 // ---- exponential-trapezoidal rule (the Mamba-3 discretisation) ------------------------------

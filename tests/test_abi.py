@@ -29,7 +29,7 @@ def test_header_symbols_are_exported():
             "jscan_last_hip_error", "jscan_version", "jscan_prefill_chunked",
             "jscan_prefill_chunked_workspace", "jscan_ssm_inputs", "jscan_prefill_fused", "jscan_prefill_scalar_a",
             "jscan_step_scalar_a", "jscan_prefill_complex", "jscan_step_complex", "jscan_prefill_trapezoid",
-            "jscan_step_trapezoid"} <= set(names)
+            "jscan_step_trapezoid", "jscan_prefill_mimo", "jscan_step_mimo"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -39,7 +39,7 @@ def test_status_strings_and_version():
     for s in range(9):
         assert lib.jscan_status_string(s) and lib.jscan_status_string(s) != b"unknown status"
     assert lib.jscan_status_string(99) == b"unknown status"
-    assert lib.jscan_version() == 106
+    assert lib.jscan_version() == 107
     assert lib.jscan_last_hip_error() == 0
 
 
@@ -301,3 +301,38 @@ def test_trapezoid_binding_checks_shapes():
     with pytest.raises(ValueError):
         jscan.prefill_trapezoid(x, x, x, torch.zeros(64, 16), torch.zeros(1, 8, 16), torch.zeros(1, 8, 16),
                                 form="nope")
+
+
+def mimo_prefill(x=P, d=P + 0x100000, A=P + 0x200000, B=P + 0x300000, C=P + 0x400000, h0=None, y=P + 0x500000,
+                 h=P + 0x600000, batch=1, L=64, D=64, N=16, R=4, form=0, dtype=BF16):
+    return jscan.library().jscan_prefill_mimo(x, d, A, B, C, h0, y, h, batch, L, D, N, R, form, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(R=3), ESHAPE), (dict(R=16), ESHAPE), (dict(R=0), ESHAPE), (dict(form=5), EFORM), (dict(dtype=2), EDTYPE),
+    (dict(D=12), ESHAPE), (dict(x=None), ENULL), (dict(h=None), ENULL), (dict(B=P + 0x300008), EALIGN),
+    (dict(y=P + 0x100000), EALIAS),                               # y overlaps delta
+    (dict(h=P + 0x500000 + 64 * 64 * 4 * 2 - 16), EALIAS),        # h_final overlaps the end of y (R = 4)
+])
+def test_prefill_mimo_validation(kw, code):
+    assert mimo_prefill(**kw) == code
+
+
+def test_prefill_mimo_sizes_follow_the_rank():
+    # y is batch * L * D * R elements: at R = 1 the same h_final offset no longer overlaps it,
+    # so validation passes (and would launch); at R = 8 it overlaps
+    assert mimo_prefill(R=8, h=P + 0x500000 + 64 * 64 * 4 * 2) == EALIAS
+    assert mimo_prefill(batch=0, x=None, y=None, h=None, A=None) == OK
+
+
+def mimo_step(h=P, x=P + 0x100000, d=P + 0x200000, A=P + 0x300000, B=P + 0x400000, C=P + 0x500000, y=P + 0x600000,
+              batch=2, D=64, N=16, R=4, ld_x=256, ld_d=64, ld_bc=64, form=0, dtype=BF16):
+    return jscan.library().jscan_step_mimo(h, x, d, A, B, C, y, batch, D, N, R, ld_x, ld_d, ld_bc, form, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(R=5), ESHAPE), (dict(ld_x=128), ESHAPE), (dict(ld_bc=32), ESHAPE), (dict(ld_d=60), ESHAPE),
+    (dict(form=9), EFORM), (dict(C=None), ENULL), (dict(y=P + 0x600004), EALIGN), (dict(y=P + 0x100000), EALIAS),
+])
+def test_step_mimo_validation(kw, code):
+    assert mimo_step(**kw) == code

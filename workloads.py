@@ -26,6 +26,8 @@ Distributions (the same for every workload):
     h0      ~ N(0, 0.1)  (0.1 = standard deviation) decode workload's resident state
     lam     = sigmoid(z),  z ~ N(0, 1)             evaluated in fp64: the exponential-trapezoidal
                                                     rule's per-(token, channel) weight in (0, 1)
+    MIMO (rank R): x [.., D, R], B, C [.., N, R] ~ N(0, 1) per element, from their own streams;
+                   delta, A, h0 as above
 bf16 workloads round every drawn value to bf16 by round-to-nearest-even (torch ``.to``).
 
 Seeding: every tensor is drawn block by block from
@@ -50,6 +52,7 @@ T_WX, T_GAIN, T_WDT, T_BDT = 6, 7, 8, 9     # producer-side weights
 T_ASC = 10                                  # scaled-identity A
 T_ACX = 11                                  # complex A
 T_LAM = 12                                  # trapezoidal-rule weights
+T_XR, T_BR, T_CR = 13, 14, 15               # MIMO inputs and projections
 
 
 @dataclasses.dataclass(frozen=True)
@@ -217,6 +220,24 @@ def lam_inputs(name_or_wl, seed: int = 0, t0: int = 0, t1: int | None = None, th
     return _draw_seq(wl, seed, T_LAM, wl.D, t0, t1, threads or min(16, os.cpu_count() or 1))
 
 
+def mimo_inputs(name_or_wl, R: int, seed: int = 0, t0: int = 0, t1: int | None = None, threads: int | None = None):
+    """Inputs of a MIMO prefill of rank R for tokens [t0, t1): x ``[batch, T, D, R]``, B, C
+    ``[batch, T, N, R]`` in the workload dtype, and the workload's delta ``[batch, T, D]`` and A."""
+    wl = get(name_or_wl)
+    t1 = wl.L if t1 is None else t1
+    if not 0 <= t0 < t1 <= wl.L + wl.extra_tokens:
+        raise ValueError("token range outside the workload")
+    threads = threads or min(16, os.cpu_count() or 1)
+    T = t1 - t0
+    return {
+        "x": _draw_seq(wl, seed, T_XR, wl.D * R, t0, t1, threads).view(wl.batch, T, wl.D, R),
+        "delta": _draw_seq(wl, seed, T_Z, wl.D, t0, t1, threads),
+        "A": draw_A(wl, seed),
+        "B": _draw_seq(wl, seed, T_BR, wl.N * R, t0, t1, threads).view(wl.batch, T, wl.N, R),
+        "C": _draw_seq(wl, seed, T_CR, wl.N * R, t0, t1, threads).view(wl.batch, T, wl.N, R),
+    }
+
+
 def decode_layer_inputs(name_or_wl, layer: int, seed: int = 0, token: int = 0):
     """One layer of the batched-decode workload at one token step.
 
@@ -250,6 +271,22 @@ def decode_layer_inputs(name_or_wl, layer: int, seed: int = 0, token: int = 0):
         "C": mat(T_C, wl.N),
         "lam": mat(T_LAM, wl.D),   # used by the exponential-trapezoidal rule only
     }
+
+
+def decode_layer_mimo_inputs(name_or_wl, layer: int, R: int, seed: int = 0, token: int = 0):
+    """One layer of the batched-decode workload at one token step, MIMO of rank R: the state h0,
+    delta_t and A of :func:`decode_layer_inputs`, with x_t ``[batch, D, R]`` and B_t, C_t
+    ``[batch, N, R]`` from their own streams."""
+    wl = get(name_or_wl)
+    base = decode_layer_inputs(wl, layer, seed, token)
+    row = layer * 1_000_003 + token
+
+    def mat(tensor, shape):
+        v = _rng(seed, wl.wid, tensor, row, 0).standard_normal((wl.batch,) + shape, dtype=np.float32)
+        return _to_dtype(v, wl)
+
+    return {"h0": base["h0"], "delta": base["delta"], "A": base["A"], "x": mat(T_XR, (wl.D, R)),
+            "B": mat(T_BR, (wl.N, R)), "C": mat(T_CR, (wl.N, R))}
 
 
 def producer_weights(D: int, R: int = 256, N: int = 16, seed: int = 0, wid: int = 50):
