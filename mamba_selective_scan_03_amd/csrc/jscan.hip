@@ -11,6 +11,7 @@
 #include "project_kernels.h"
 #include "step_kernel.h"
 #include "mimo_kernels.h"
+#include "prefill_mimo_rows_kernel.h"
 
 namespace {
 
@@ -179,15 +180,26 @@ bool form_of(jscan_a_form f, jscan::AForm *af) {
 
 bool mimo_rank_ok(int64_t R) { return R == 1 || R == 2 || R == 4 || R == 8; }
 
+// Rank 1 is the single-input scan (same layouts), rank 2-8 the row-mapped MIMO kernel when D is
+// a multiple of 32, else one lane per channel.
 template <typename E, jscan::AForm AF, int R>
 void launch_prefill_mimo_r(const void *x, const void *delta, const float *A, const void *B, const void *C,
                            const float *h0, void *y, float *h_final, int64_t batch, int64_t L, int64_t D,
                            hipStream_t s) {
     using T = typename E::store_t;
-    const int blocks_per_row = (int)((D + 63) / 64);
-    hipLaunchKernelGGL((jscan::prefill_mimo_lane_kernel<E, AF, R>), dim3((unsigned)(batch * blocks_per_row)), dim3(64),
-                       0, s, static_cast<const T *>(x), static_cast<const T *>(delta), A, static_cast<const T *>(B),
-                       static_cast<const T *>(C), h0, static_cast<T *>(y), h_final, L, (int)D, blocks_per_row);
+    if constexpr (R == 1) {
+        launch_prefill<E, AF>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s);
+    } else if (jscan::mimo_rows_kernel_applies(D, R)) {
+        jscan::launch_prefill_mimo_rows<E, AF, R>(static_cast<const T *>(x), static_cast<const T *>(delta), A,
+                                                  static_cast<const T *>(B), static_cast<const T *>(C), h0,
+                                                  static_cast<T *>(y), h_final, batch, L, (int)D, s);
+    } else {
+        const int blocks_per_row = (int)((D + 63) / 64);
+        hipLaunchKernelGGL((jscan::prefill_mimo_lane_kernel<E, AF, R>), dim3((unsigned)(batch * blocks_per_row)),
+                           dim3(64), 0, s, static_cast<const T *>(x), static_cast<const T *>(delta), A,
+                           static_cast<const T *>(B), static_cast<const T *>(C), h0, static_cast<T *>(y), h_final, L,
+                           (int)D, blocks_per_row);
+    }
 }
 template <typename E, jscan::AForm AF>
 void launch_prefill_mimo_af(const void *x, const void *delta, const float *A, const void *B, const void *C,

@@ -13,6 +13,7 @@
 #pragma once
 
 #include "scan_update.h"
+#include "step_kernel.h"
 
 namespace jscan {
 
@@ -222,42 +223,50 @@ __global__ __launch_bounds__(256) void step_mimo_kernel(float *__restrict__ h, c
     const float a2v[4] = {scaled_A(av.x), scaled_A(av.y), scaled_A(av.z), scaled_A(av.w)};
     const ComplexA ca0 = complex_A(av.x, av.y), ca1 = complex_A(av.z, av.w);
     using S = typename E::store_t;
+    // every row's loads first (the state with non-temporal accesses, as in the single-input step),
+    // then the arithmetic, so that all of a lane's HBM requests are in flight together
+    float4 h4[NR];
+    float xv[NR][R], dv[NR], bq[NR][4 * R], cq[NR][4 * R];
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
         // a missing last row re-reads the row before it and stores nothing
         const int b = min(rg * NR + j, batch - 1);
-        float *hp = h + ((int64_t)b * D + d) * kDState + q * 4;
-        const float4 h4 = *reinterpret_cast<const float4 *>(hp);
-        float hv[4] = {h4.x, h4.y, h4.z, h4.w};
-        float xv[R], dx[R], bq[4 * R], cq[4 * R];
-        RowLoad<E, R>::load(x + (int64_t)b * ld_x + (int64_t)d * R, xv);
-        const float dv = E::load(dl + (int64_t)b * ld_d + d);
-        RowLoad<E, 4 * R>::load(Bt + (int64_t)b * ld_bc + q * 4 * R, bq);
-        RowLoad<E, 4 * R>::load(Ct + (int64_t)b * ld_bc + q * 4 * R, cq);
+        h4[j] = load_state(h + ((int64_t)b * D + d) * kDState + q * 4);
+        RowLoad<E, R>::load(x + (int64_t)b * ld_x + (int64_t)d * R, xv[j]);
+        dv[j] = E::load(dl + (int64_t)b * ld_d + d);
+        RowLoad<E, 4 * R>::load(Bt + (int64_t)b * ld_bc + q * 4 * R, bq[j]);
+        RowLoad<E, 4 * R>::load(Ct + (int64_t)b * ld_bc + q * 4 * R, cq[j]);
+    }
 #pragma unroll
-        for (int r = 0; r < R; ++r) dx[r] = delta_x(dv, xv[r]);
+    for (int j = 0; j < NR; ++j) {
+        const int b = rg * NR + j;
+        float hv[4] = {h4[j].x, h4[j].y, h4[j].z, h4[j].w};
+        float dx[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) dx[r] = delta_x(dv[j], xv[j][r]);
         if constexpr (kComplexA) {
-            advance_complex_input(hv[0], hv[1], dv, ca0, mimo_input<R>(dx, bq), mimo_input<R>(dx, bq + R));
-            advance_complex_input(hv[2], hv[3], dv, ca1, mimo_input<R>(dx, bq + 2 * R), mimo_input<R>(dx, bq + 3 * R));
+            advance_complex_input(hv[0], hv[1], dv[j], ca0, mimo_input<R>(dx, bq[j]), mimo_input<R>(dx, bq[j] + R));
+            advance_complex_input(hv[2], hv[3], dv[j], ca1, mimo_input<R>(dx, bq[j] + 2 * R),
+                                  mimo_input<R>(dx, bq[j] + 3 * R));
         } else {
-            const float abar = decay(dv, a2v[0]);
+            const float abar = decay(dv[j], a2v[0]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                hv[i] = advance_input(hv[i], kScalarA ? abar : decay(dv, a2v[i]), mimo_input<R>(dx, bq + i * R));
+                hv[i] = advance_input(hv[i], kScalarA ? abar : decay(dv[j], a2v[i]), mimo_input<R>(dx, bq[j] + i * R));
         }
         float p[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            float s = cq[r] * hv[0];
+            float s = cq[j][r] * hv[0];
 #pragma unroll
-            for (int i = 1; i < 4; ++i) s = __builtin_fmaf(cq[i * R + r], hv[i], s);
+            for (int i = 1; i < 4; ++i) s = __builtin_fmaf(cq[j][i * R + r], hv[i], s);
             // quad_perm [1,0,3,2] then [2,3,0,1]: every lane of the quad ends with the quad's sum
             s = s + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, true));
             s = s + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x4E, 0xF, 0xF, true));
             p[r] = s;
         }
-        if (rg * NR + j < batch) {
-            *reinterpret_cast<float4 *>(hp) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+        if (b < batch) {
+            store_state(h + ((int64_t)b * D + d) * kDState + q * 4, make_float4(hv[0], hv[1], hv[2], hv[3]));
             S *yp = y + (int64_t)b * ld_x + (int64_t)d * R;
 #pragma unroll
             for (int r = 0; r < R; ++r)

@@ -1,0 +1,402 @@
+// prefill_mimo_rows_kernel.h - the MIMO prefill (R = 2, 4 or 8 inputs and outputs per channel)
+// for long sequences at small batch, on the row-mapped design of prefill_rows_kernel.h.
+//
+// Mapping.  As in the single-input kernel, a lane carries two states (n0, n0 + 1) of one
+// channel: a wave is 4 rows x 16 lanes, lane c of a row owns channel c of a 16-channel group,
+// row r owns states 8 sh + 2 r + {0, 1}, and two waves (sh = 0, 1) cover a group's 16 states.
+// A 512-thread work-group runs 4 such scan waves (32 channels) and 4 helper waves.
+//   * B_t[n][r] and C_t[n][r] are the same for a whole row: a register holds 16 tokens' values
+//     of one (state, rank) (lane c = token c) and the DPP row broadcast hands token k's value to
+//     the row inside the multiply, as for the single-input B and C.
+//   * delta_t * x_t[d][r] (R values) and delta_t (or, with a scaled-identity A, the decay) are
+//     per channel; the helper waves stage them in LDS in fp32, and the rows read them as
+//     broadcasts.
+//   * The R outputs of a token are summed over the wave's 4 rows R at a time (reduce_rows4 on
+//     four (token, rank) partials, so each row ends with one of them), then over the two waves
+//     by the helper waves, which round to the output dtype and store.
+// Tiles are kT = 32 tokens for R <= 4 and 16 for R = 8, so that the R-fold LDS areas stay
+// within the work-group's share.  One barrier per tile; the helper waves stage tile k + 1,
+// request tile k + 3 and store the outputs of tile k - 1 while the scan waves scan tile k.
+// Tokens past L are identity tokens (delta = 0, x = -0, B = C = 0), which leave every state
+// bit-identical.
+#pragma once
+
+#include "mimo_kernels.h"
+#include "prefill_rows_kernel.h"
+
+namespace jscan {
+
+namespace mrows {
+template <int R> struct Cfg {
+    static_assert(R == 2 || R == 4 || R == 8, "rank 2, 4 or 8");
+    static constexpr int kT = R <= 4 ? 32 : 16;    // tokens per tile
+    static constexpr int kCh = 32;                 // channels per work-group
+    static constexpr int kThreads = 512;
+    static constexpr int kHalf = 256;
+    // helper threads: x and delta, one token and CPT channels per thread
+    static constexpr int kTPT = kHalf / kT;         // threads per token
+    static constexpr int kCPT = kCh / kTPT;         // channels per thread (4 or 2)
+    static constexpr int kXV = kCPT * R;            // x values per thread
+    // B (threads 0-127) and C (128-255): one token and SPT states per thread
+    static constexpr int kTPB = 128 / kT;
+    static constexpr int kSPT = kDState / kTPB;
+    static constexpr int kBV = kSPT * R;
+    // LDS (floats): dx [kT][kCh][R]; delta [kT/4][kCh][4]; B and C [16][R][kBS];
+    // y partials [2 halves][kT][kYS]
+    static constexpr int kDxSize = kT * kCh * R;
+    static constexpr int kDlSize = kT * kCh;
+    // B/C rows of 16 tokens read by the 4 rows of a wave (states 2 apart) land 16 banks apart
+    static constexpr int kBS = R == 2 ? kT + 4 : R == 4 ? kT + 2 : kT + 1;
+    static constexpr int kBcSize = kDState * R * kBS;
+    static constexpr int kYS = kCh * R + (R == 2 ? 32 : 0);
+    static constexpr int kYSize = 2 * kT * kYS;
+};
+}  // namespace mrows
+
+// K raw elements of a row (bf16: 16-bit patterns, K = 2, 4 or a multiple of 8; f32: K = 2 or a
+// multiple of 4), kept packed until they are staged.
+template <typename E, int K> struct RawRow;
+template <int K> struct RawRow<BF16, K> {
+    static constexpr int kW = K == 2 ? 1 : K == 4 ? 2 : K / 2;   // 32-bit words
+    uint32_t w[kW];
+    __device__ __forceinline__ void load(const uint16_t *p) {
+        if constexpr (K == 2) {
+            w[0] = *reinterpret_cast<const uint32_t *>(p);
+        } else if constexpr (K == 4) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(p);
+            w[0] = v.x;
+            w[1] = v.y;
+        } else {
+#pragma unroll
+            for (int i = 0; i < K / 8; ++i) {
+                const uint4 v = reinterpret_cast<const uint4 *>(p)[i];
+                w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+            }
+        }
+    }
+    __device__ __forceinline__ float get(int i) const { return (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]); }
+};
+template <int K> struct RawRow<F32, K> {
+    float v[K];
+    __device__ __forceinline__ void load(const float *p) {
+        if constexpr (K == 2) {
+            const float2 a = *reinterpret_cast<const float2 *>(p);
+            v[0] = a.x;
+            v[1] = a.y;
+        } else {
+#pragma unroll
+            for (int i = 0; i < K / 4; ++i) {
+                const float4 a = reinterpret_cast<const float4 *>(p)[i];
+                v[4 * i] = a.x; v[4 * i + 1] = a.y; v[4 * i + 2] = a.z; v[4 * i + 3] = a.w;
+            }
+        }
+    }
+    __device__ __forceinline__ float get(int i) const { return v[i]; }
+};
+
+template <typename E, int R> struct MimoTileRegs {
+    using C = mrows::Cfg<R>;
+    RawRow<E, C::kXV> x;     // token tid / kTPT, channels kCPT (tid % kTPT) .. + kCPT, all ranks
+    RawRow<E, C::kCPT> dl;   // the same token and channels
+    RawRow<E, C::kBV> bc;    // B or C: token, states kSPT (tid % kTPB) .. + kSPT, all ranks
+};
+
+// Requests one tile's raw inputs (tokens past L re-read token L - 1; staging replaces them).
+template <typename E, int R>
+__device__ __forceinline__ void mimo_load_tile(MimoTileRegs<E, R> &Rg, const typename E::store_t *xb,
+                                               const typename E::store_t *db, const typename E::store_t *bcb,
+                                               int64_t t0, int64_t L, int D, int tid) {
+    using C = mrows::Cfg<R>;
+    const int t = tid / C::kTPT, c0 = (tid % C::kTPT) * C::kCPT;
+    const int64_t tt = min(t0 + t, L - 1);
+    Rg.x.load(xb + (tt * D + c0) * R);
+    Rg.dl.load(db + tt * D + c0);
+    const int tb = (tid & 127) / C::kTPB, s0 = (tid % C::kTPB) * C::kSPT;
+    const int64_t tq = min(t0 + tb, L - 1);
+    Rg.bc.load(bcb + (tq * kDState + s0) * R);
+}
+
+// Converts one tile into LDS: dx = delta * x per (token, channel, rank), delta (or the decay
+// 2^(delta a2) with a scaled-identity A) per (token, channel), and the B and C tiles.
+template <typename E, int R, AForm AF>
+__device__ __forceinline__ void mimo_stage_tile(const MimoTileRegs<E, R> &Rg, float *dx_s, float *dl_s, float *bc_s,
+                                                int64_t t0, int64_t L, int tid, const float (&a2c)[mrows::Cfg<R>::kCPT]) {
+    using C = mrows::Cfg<R>;
+    const int t = tid / C::kTPT, c0 = (tid % C::kTPT) * C::kCPT;
+    const bool live = t0 + t < L;
+    float dx[C::kXV];
+#pragma unroll
+    for (int ci = 0; ci < C::kCPT; ++ci) {
+        const float dv = live ? Rg.dl.get(ci) : 0.0f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) dx[ci * R + r] = delta_x(dv, live ? Rg.x.get(ci * R + r) : -0.0f);
+        dl_s[((t >> 2) * C::kCh + c0 + ci) * 4 + (t & 3)] = AF == AForm::ScaledIdentity ? decay(dv, a2c[ci]) : dv;
+    }
+    float *dst = dx_s + (t * C::kCh + c0) * R;
+#pragma unroll
+    for (int i = 0; i < C::kXV / 4; ++i)
+        reinterpret_cast<float4 *>(dst)[i] = make_float4(dx[4 * i], dx[4 * i + 1], dx[4 * i + 2], dx[4 * i + 3]);
+    if constexpr (C::kXV % 4 == 2)
+        *reinterpret_cast<float2 *>(dst + C::kXV - 2) = make_float2(dx[C::kXV - 2], dx[C::kXV - 1]);
+    const int tb = (tid & 127) / C::kTPB, s0 = (tid % C::kTPB) * C::kSPT;
+    const bool live_bc = t0 + tb < L;
+    float *tile = bc_s + (tid >= 128 ? C::kBcSize : 0);
+#pragma unroll
+    for (int i = 0; i < C::kBV; ++i)   // i = (n - s0) * R + r
+        tile[(s0 * R + i) * C::kBS + tb] = live_bc ? Rg.bc.get(i) : 0.0f;
+}
+
+// The outputs of one tile: this thread's token and channels, the two state halves' partial sums
+// added, rounded and stored as one contiguous run of kCPT * R values.
+template <typename E, int R>
+__device__ __forceinline__ void mimo_write_final(const float *y_tile, typename E::store_t *yb, int64_t t0, int64_t L,
+                                                 int D, int tid) {
+    using C = mrows::Cfg<R>;
+    const int t = tid / C::kTPT, c0 = (tid % C::kTPT) * C::kCPT;
+    if (t0 + t >= L) return;
+    const float *p0 = y_tile + t * C::kYS + c0 * R;
+    const float *p1 = p0 + C::kT * C::kYS;
+    float o[C::kXV];
+#pragma unroll
+    for (int i = 0; i < C::kXV / 4; ++i) {
+        const float4 u = reinterpret_cast<const float4 *>(p0)[i], w = reinterpret_cast<const float4 *>(p1)[i];
+        o[4 * i] = u.x + w.x; o[4 * i + 1] = u.y + w.y; o[4 * i + 2] = u.z + w.z; o[4 * i + 3] = u.w + w.w;
+    }
+    if constexpr (C::kXV % 4 == 2) {
+        const float2 u = *reinterpret_cast<const float2 *>(p0 + C::kXV - 2);
+        const float2 w = *reinterpret_cast<const float2 *>(p1 + C::kXV - 2);
+        o[C::kXV - 2] = u.x + w.x;
+        o[C::kXV - 1] = u.y + w.y;
+    }
+    RowStore<E, C::kXV>::store(yb + ((t0 + t) * D + c0) * R, o);
+}
+
+// The scan lane's LDS operands for 4 tokens: dx (R per token) and delta of its channel.
+template <int R> struct QuarterRegs {
+    float dx[4][R];
+    float4 dl;
+};
+template <int R>
+__device__ __forceinline__ void mimo_load_quarter(QuarterRegs<R> &q, const float *dx_s, const float *dl_s, int t4,
+                                                  int ch) {
+    using C = mrows::Cfg<R>;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float *p = dx_s + ((t4 + k) * C::kCh + ch) * R;
+        if constexpr (R == 2) {
+            const float2 v = *reinterpret_cast<const float2 *>(p);
+            q.dx[k][0] = v.x;
+            q.dx[k][1] = v.y;
+        } else {
+#pragma unroll
+            for (int i = 0; i < R / 4; ++i) {
+                const float4 v = reinterpret_cast<const float4 *>(p)[i];
+                q.dx[k][4 * i] = v.x; q.dx[k][4 * i + 1] = v.y; q.dx[k][4 * i + 2] = v.z; q.dx[k][4 * i + 3] = v.w;
+            }
+        }
+    }
+    q.dl = *reinterpret_cast<const float4 *>(dl_s + ((t4 >> 2) * C::kCh + ch) * 4);
+}
+
+// The lane's B and C registers for one 16-token group: (state n0 + i, rank r) at [i][r]; lane c
+// holds token tg + c.
+template <int R> struct BcRegs {
+    float b[2][R], c[2][R];
+};
+template <int R>
+__device__ __forceinline__ void mimo_load_bc(BcRegs<R> &g, const float *bc_s, int tg, int n0, int c) {
+    using C = mrows::Cfg<R>;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            g.b[i][r] = bc_s[((n0 + i) * R + r) * C::kBS + tg + c];
+            g.c[i][r] = bc_s[C::kBcSize + ((n0 + i) * R + r) * C::kBS + tg + c];
+        }
+}
+
+// v_mul_f32 with the DPP row broadcast of lane k of `tile` as its first operand.
+template <int k> __device__ __forceinline__ float mul_bcast(float tile, float v) {
+    float out;
+    if constexpr (k == 0)
+        asm("s_nop 1\n\tv_mul_f32_dpp %0, %1, %2 row_newbcast:0 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+            : "=v"(out) : "v"(tile), "v"(v));
+    else
+        asm("v_mul_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+            : "=v"(out) : "v"(tile), "v"(v), "i"(k));
+    return out;
+}
+
+// One token (TAU within its 16-token group): advance the lane's two states and leave the R
+// partial outputs (C h summed over the two states) in P.  The rank-R input of state n is
+// dx_0 B[n][0] then + dx_r B[n][r] in increasing r, with B broadcast from lane TAU; this is
+// mimo_input(), bit for bit.
+template <int TAU, int R, AForm AF>
+__device__ __forceinline__ void mimo_token(const BcRegs<R> &g, const float (&dx)[R], float dv, float &h_0, float &h_1,
+                                           float a2_0, float a2_1, float (&P)[R]) {
+    float u0 = mul_bcast<TAU>(g.b[0][0], dx[0]);
+    float u1 = mul_bcast<TAU>(g.b[1][0], dx[0]);
+#pragma unroll
+    for (int r = 1; r < R; ++r) {
+        u0 = fmac_bcast<TAU>(u0, g.b[0][r], dx[r]);
+        u1 = fmac_bcast<TAU>(u1, g.b[1][r], dx[r]);
+    }
+    if constexpr (AF == AForm::ComplexPairs) {
+        advance_complex_input(h_0, h_1, dv, ComplexA{a2_0, a2_1}, u0, u1);
+    } else if constexpr (AF == AForm::ScaledIdentity) {
+        h_0 = advance_input(h_0, dv, u0);
+        h_1 = advance_input(h_1, dv, u1);
+    } else {
+        h_0 = advance_input(h_0, decay(dv, a2_0), u0);
+        h_1 = advance_input(h_1, decay(dv, a2_1), u1);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) P[r] = fmac_bcast<TAU>(mul_bcast<TAU>(g.c[0][r], h_0), g.c[1][r], h_1);
+}
+
+// Four tokens TQ .. TQ + 3 of a group, then their 4R partials summed over the wave's rows four
+// at a time (partial index i = token * R + rank; after reduce_rows4 row j holds i0 + {0,2,1,3}[j])
+// and written to this wave's half of the y exchange.
+template <int TQ, int R, AForm AF>
+__device__ __forceinline__ void mimo_quarter(const BcRegs<R> &g, const QuarterRegs<R> &q, float &h_0, float &h_1,
+                                             float a2_0, float a2_1, float *ys, int tq0, int rt, int ch) {
+    using C = mrows::Cfg<R>;
+    float P[4][R];
+    mimo_token<TQ + 0, R, AF>(g, q.dx[0], q.dl.x, h_0, h_1, a2_0, a2_1, P[0]);
+    mimo_token<TQ + 1, R, AF>(g, q.dx[1], q.dl.y, h_0, h_1, a2_0, a2_1, P[1]);
+    mimo_token<TQ + 2, R, AF>(g, q.dx[2], q.dl.z, h_0, h_1, a2_0, a2_1, P[2]);
+    mimo_token<TQ + 3, R, AF>(g, q.dx[3], q.dl.w, h_0, h_1, a2_0, a2_1, P[3]);
+#pragma unroll
+    for (int m = 0; m < R; ++m) {
+        const int i0 = 4 * m;
+        const float s = reduce_rows4(P[(i0) / R][(i0) % R], P[(i0 + 1) / R][(i0 + 1) % R],
+                                     P[(i0 + 2) / R][(i0 + 2) % R], P[(i0 + 3) / R][(i0 + 3) % R]);
+        const int i = i0 + rt;
+        ys[(tq0 + i / R) * C::kYS + ch * R + (i % R)] = s;
+    }
+}
+
+template <typename E, AForm AF, int R>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mimo_rows_kernel(
+    const typename E::store_t *__restrict__ x, const typename E::store_t *__restrict__ dl,
+    const float *__restrict__ A, const typename E::store_t *__restrict__ B, const typename E::store_t *__restrict__ C,
+    const float *__restrict__ h0, typename E::store_t *__restrict__ y, float *__restrict__ h_final, int64_t L, int D,
+    int blocks_per_row, int xcd_stride) {
+    using Cf = mrows::Cfg<R>;
+    constexpr int kT = Cf::kT;
+    __shared__ __attribute__((aligned(16))) float dx_s[2][Cf::kDxSize];
+    __shared__ __attribute__((aligned(16))) float dl_s[2][Cf::kDlSize];
+    __shared__ __attribute__((aligned(16))) float bc_s[2][2 * Cf::kBcSize];
+    __shared__ __attribute__((aligned(16))) float y_s[2][Cf::kYSize];
+
+    int wg = blockIdx.x;
+    if (xcd_stride > 0) wg = (wg & 7) * xcd_stride + (wg >> 3);
+    const int b = wg / blocks_per_row;
+    const int d0 = (wg - b * blocks_per_row) * Cf::kCh;
+    const int ntiles = (int)((L + kT - 1) / kT);
+    using S = typename E::store_t;
+
+    if (threadIdx.x >= Cf::kHalf) {
+        // ---------------- helper waves ----------------
+        const int tid = threadIdx.x - Cf::kHalf;
+        const S *xb = x + (int64_t)b * L * D * R + (int64_t)d0 * R;
+        const S *db = dl + (int64_t)b * L * D + d0;
+        const S *bcb = (tid < 128 ? B : C) + (int64_t)b * L * kDState * R;
+        S *yb = y + (int64_t)b * L * D * R + (int64_t)d0 * R;
+        float a2c[Cf::kCPT];
+#pragma unroll
+        for (int ci = 0; ci < Cf::kCPT; ++ci)
+            a2c[ci] = AF == AForm::ScaledIdentity ? scaled_A(A[d0 + (tid % Cf::kTPT) * Cf::kCPT + ci]) : 0.0f;
+        MimoTileRegs<E, R> Rg[2];
+        mimo_load_tile<E, R>(Rg[0], xb, db, bcb, 0, L, D, tid);
+        mimo_stage_tile<E, R, AF>(Rg[0], dx_s[0], dl_s[0], bc_s[0], 0, L, tid, a2c);
+        mimo_load_tile<E, R>(Rg[1], xb, db, bcb, kT, L, D, tid);
+        mimo_load_tile<E, R>(Rg[0], xb, db, bcb, 2 * kT, L, D, tid);
+        __syncthreads();
+        auto tile = [&](auto cur_c, int k) {
+            constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
+            if (k + 1 < ntiles) {
+                mimo_stage_tile<E, R, AF>(Rg[nxt], dx_s[nxt], dl_s[nxt], bc_s[nxt], (int64_t)(k + 1) * kT, L, tid, a2c);
+                if (k + 3 < ntiles) mimo_load_tile<E, R>(Rg[nxt], xb, db, bcb, (int64_t)(k + 3) * kT, L, D, tid);
+            }
+            if (k > 0) mimo_write_final<E, R>(y_s[nxt], yb, (int64_t)(k - 1) * kT, L, D, tid);
+            __syncthreads();
+        };
+        for (int k = 0; k < ntiles; k += 2) {
+            tile(IntConst<0>{}, k);
+            if (k + 1 < ntiles) tile(IntConst<1>{}, k + 1);
+        }
+        mimo_write_final<E, R>(y_s[(ntiles - 1) & 1], yb, (int64_t)(ntiles - 1) * kT, L, D, tid);
+        return;
+    }
+
+    // ---------------- scan waves ----------------
+    __builtin_amdgcn_s_setprio(3);
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int r = lane >> 4, c = lane & 15;
+    const int cg = wave >> 1, sh = wave & 1;
+    const int ch = 16 * cg + c;
+    const int d = d0 + ch;
+    const int n0 = 8 * sh + 2 * r;
+    float a2_0 = 0.0f, a2_1 = 0.0f;
+    if constexpr (AF == AForm::Diagonal) {
+        a2_0 = scaled_A(A[(int64_t)d * kDState + n0]);
+        a2_1 = scaled_A(A[(int64_t)d * kDState + n0 + 1]);
+    } else if constexpr (AF == AForm::ComplexPairs) {
+        const ComplexA ca = complex_A(A[(int64_t)d * kDState + n0], A[(int64_t)d * kDState + n0 + 1]);
+        a2_0 = ca.a2;
+        a2_1 = ca.turns;
+    }
+    float h_0 = 0.0f, h_1 = 0.0f;
+    if (h0) {
+        const float2 hv = *reinterpret_cast<const float2 *>(h0 + ((int64_t)b * D + d) * kDState + n0);
+        h_0 = hv.x;
+        h_1 = hv.y;
+    }
+    const int rt = (r == 1) ? 2 : (r == 2) ? 1 : r;   // partial slot of this row after reduce_rows4
+    __syncthreads();   // tile 0 staged
+    auto tile = [&](auto cur_c, int k) {
+        constexpr int cur = decltype(cur_c)::value;
+        float *ys = y_s[cur] + sh * kT * Cf::kYS;
+        const float *dxc = dx_s[cur], *dlc = dl_s[cur], *bcc = bc_s[cur];
+        BcRegs<R> g;
+        QuarterRegs<R> qa, qb;
+#pragma unroll
+        for (int tg = 0; tg < kT; tg += 16) {
+            mimo_load_bc<R>(g, bcc, tg, n0, c);
+            mimo_load_quarter<R>(qa, dxc, dlc, tg, ch);
+            mimo_load_quarter<R>(qb, dxc, dlc, tg + 4, ch);
+            mimo_quarter<0, R, AF>(g, qa, h_0, h_1, a2_0, a2_1, ys, tg, rt, ch);
+            mimo_load_quarter<R>(qa, dxc, dlc, tg + 8, ch);
+            mimo_quarter<4, R, AF>(g, qb, h_0, h_1, a2_0, a2_1, ys, tg + 4, rt, ch);
+            mimo_load_quarter<R>(qb, dxc, dlc, tg + 12, ch);
+            mimo_quarter<8, R, AF>(g, qa, h_0, h_1, a2_0, a2_1, ys, tg + 8, rt, ch);
+            mimo_quarter<12, R, AF>(g, qb, h_0, h_1, a2_0, a2_1, ys, tg + 12, rt, ch);
+        }
+        __syncthreads();
+        (void)k;
+    };
+    for (int k = 0; k < ntiles; k += 2) {
+        tile(IntConst<0>{}, k);
+        if (k + 1 < ntiles) tile(IntConst<1>{}, k + 1);
+    }
+    *reinterpret_cast<float2 *>(h_final + ((int64_t)b * D + d) * kDState + n0) = make_float2(h_0, h_1);
+}
+
+// The row-mapped MIMO kernel needs whole 32-channel blocks.
+inline bool mimo_rows_kernel_applies(int64_t D, int64_t R) { return D % 32 == 0 && (R == 2 || R == 4 || R == 8); }
+
+template <typename E, AForm AF, int R>
+void launch_prefill_mimo_rows(const typename E::store_t *x, const typename E::store_t *dl, const float *A,
+                              const typename E::store_t *B, const typename E::store_t *C, const float *h0,
+                              typename E::store_t *y, float *h_final, int64_t batch, int64_t L, int D,
+                              hipStream_t stream) {
+    const int blocks_per_row = D / mrows::Cfg<R>::kCh;
+    const int64_t blocks = batch * blocks_per_row;
+    const int xcd_stride = (blocks % 8 == 0) ? (int)(blocks / 8) : 0;
+    hipLaunchKernelGGL((prefill_mimo_rows_kernel<E, AF, R>), dim3((unsigned)blocks), dim3(mrows::Cfg<R>::kThreads), 0,
+                       stream, x, dl, A, B, C, h0, y, h_final, L, D, blocks_per_row, xcd_stride);
+}
+
+}  // namespace jscan
