@@ -195,10 +195,12 @@ __global__ __launch_bounds__(64) void prefill_mimo_lane_kernel(
 
 // ---- decode step: one lane per (channel, quad of states) and two batch rows ----------------
 // The mapping of the single-input step (step_kernel.h): the quad's four lanes hold states
-// 4q..4q+3 of a channel, so the state is read and written once with 16-byte accesses.  A lane
-// reads its quad's R columns of B and C (4R contiguous values), forms the four input terms, and
-// its four C h products per output; two DPP quad exchanges sum each output over the quad, and
-// lane q stores outputs q and q + 4, so the quad writes its R outputs as one contiguous run.
+// 4q..4q+3 of a channel, so the state is read and written once with 16-byte accesses.  A
+// work-group's lanes all serve the same two batch rows, so their B and C rows (N x R each) are
+// converted to fp32 once per work-group into LDS, one value per thread, and each lane reads its
+// quad's R columns from there.  A lane forms its four input terms and its four C h products per
+// output; two DPP quad exchanges sum each output over the quad, and lane q stores outputs q and
+// q + 4, so the quad writes its R outputs as one contiguous run.
 namespace mimo_step {
 constexpr int kRows = 2;   // batch rows per lane
 }
@@ -212,54 +214,71 @@ __global__ __launch_bounds__(256) void step_mimo_kernel(float *__restrict__ h, c
                                                         int blocks_per_rows, int64_t ld_x, int64_t ld_d,
                                                         int64_t ld_bc) {
     constexpr int NR = mimo_step::kRows;
+    constexpr int kBC = kDState * R;                 // values of one B or C row
+    __shared__ __attribute__((aligned(16))) float bc_s[NR][2][kBC];
     const int rg = blockIdx.x / blocks_per_rows;
     const int lane_in_row = (blockIdx.x - rg * blocks_per_rows) * 256 + threadIdx.x;
-    if (lane_in_row >= D * 4) return;   // whole quads leave together
-    const int d = lane_in_row >> 2, q = lane_in_row & 3;
+    const bool active = lane_in_row < D * 4;         // whole quads are active or not
+    const int d = active ? lane_in_row >> 2 : 0, q = lane_in_row & 3;
+    using S = typename E::store_t;
+
+    // every row's state, x and delta requested first (the state with non-temporal accesses, as in
+    // the single-input step), so that they are in flight while B and C are staged
+    float4 h4[NR];
+    float xv[NR][R], dv[NR];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        // a missing last row re-reads the row before it and stores nothing
+        const int b = min(rg * NR + j, batch - 1);
+        if (active) {
+            h4[j] = load_state(h + ((int64_t)b * D + d) * kDState + q * 4);
+            RowLoad<E, R>::load(x + (int64_t)b * ld_x + (int64_t)d * R, xv[j]);
+            dv[j] = E::load(dl + (int64_t)b * ld_d + d);
+        }
+    }
+    for (int i = threadIdx.x; i < NR * 2 * kBC; i += 256) {
+        const int j = i / (2 * kBC), w = (i / kBC) & 1, k = i % kBC;
+        const int b = min(rg * NR + j, batch - 1);
+        bc_s[j][w][k] = E::load((w ? Ct : Bt) + (int64_t)b * ld_bc + k);
+    }
+    __syncthreads();
+    if (!active) return;
 
     constexpr bool kScalarA = AF == AForm::ScaledIdentity, kComplexA = AF == AForm::ComplexPairs;
     const float4 av = kScalarA ? make_float4(A[d], A[d], A[d], A[d])
                                : *reinterpret_cast<const float4 *>(A + (int64_t)d * kDState + q * 4);
     const float a2v[4] = {scaled_A(av.x), scaled_A(av.y), scaled_A(av.z), scaled_A(av.w)};
     const ComplexA ca0 = complex_A(av.x, av.y), ca1 = complex_A(av.z, av.w);
-    using S = typename E::store_t;
-    // every row's loads first (the state with non-temporal accesses, as in the single-input step),
-    // then the arithmetic, so that all of a lane's HBM requests are in flight together
-    float4 h4[NR];
-    float xv[NR][R], dv[NR], bq[NR][4 * R], cq[NR][4 * R];
-#pragma unroll
-    for (int j = 0; j < NR; ++j) {
-        // a missing last row re-reads the row before it and stores nothing
-        const int b = min(rg * NR + j, batch - 1);
-        h4[j] = load_state(h + ((int64_t)b * D + d) * kDState + q * 4);
-        RowLoad<E, R>::load(x + (int64_t)b * ld_x + (int64_t)d * R, xv[j]);
-        dv[j] = E::load(dl + (int64_t)b * ld_d + d);
-        RowLoad<E, 4 * R>::load(Bt + (int64_t)b * ld_bc + q * 4 * R, bq[j]);
-        RowLoad<E, 4 * R>::load(Ct + (int64_t)b * ld_bc + q * 4 * R, cq[j]);
-    }
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
         const int b = rg * NR + j;
+        float bq[4 * R], cq[4 * R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {   // the quad's rows 4q..4q+3 of B and C: 4R consecutive values
+            const float4 vb = reinterpret_cast<const float4 *>(&bc_s[j][0][q * 4 * R])[i];
+            const float4 vc = reinterpret_cast<const float4 *>(&bc_s[j][1][q * 4 * R])[i];
+            bq[4 * i] = vb.x; bq[4 * i + 1] = vb.y; bq[4 * i + 2] = vb.z; bq[4 * i + 3] = vb.w;
+            cq[4 * i] = vc.x; cq[4 * i + 1] = vc.y; cq[4 * i + 2] = vc.z; cq[4 * i + 3] = vc.w;
+        }
         float hv[4] = {h4[j].x, h4[j].y, h4[j].z, h4[j].w};
         float dx[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) dx[r] = delta_x(dv[j], xv[j][r]);
         if constexpr (kComplexA) {
-            advance_complex_input(hv[0], hv[1], dv[j], ca0, mimo_input<R>(dx, bq[j]), mimo_input<R>(dx, bq[j] + R));
-            advance_complex_input(hv[2], hv[3], dv[j], ca1, mimo_input<R>(dx, bq[j] + 2 * R),
-                                  mimo_input<R>(dx, bq[j] + 3 * R));
+            advance_complex_input(hv[0], hv[1], dv[j], ca0, mimo_input<R>(dx, bq), mimo_input<R>(dx, bq + R));
+            advance_complex_input(hv[2], hv[3], dv[j], ca1, mimo_input<R>(dx, bq + 2 * R), mimo_input<R>(dx, bq + 3 * R));
         } else {
             const float abar = decay(dv[j], a2v[0]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                hv[i] = advance_input(hv[i], kScalarA ? abar : decay(dv[j], a2v[i]), mimo_input<R>(dx, bq[j] + i * R));
+                hv[i] = advance_input(hv[i], kScalarA ? abar : decay(dv[j], a2v[i]), mimo_input<R>(dx, bq + i * R));
         }
         float p[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            float s = cq[j][r] * hv[0];
+            float s = cq[r] * hv[0];
 #pragma unroll
-            for (int i = 1; i < 4; ++i) s = __builtin_fmaf(cq[j][i * R + r], hv[i], s);
+            for (int i = 1; i < 4; ++i) s = __builtin_fmaf(cq[i * R + r], hv[i], s);
             // quad_perm [1,0,3,2] then [2,3,0,1]: every lane of the quad ends with the quad's sum
             s = s + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, true));
             s = s + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x4E, 0xF, 0xF, true));
@@ -269,8 +288,14 @@ __global__ __launch_bounds__(256) void step_mimo_kernel(float *__restrict__ h, c
             store_state(h + ((int64_t)b * D + d) * kDState + q * 4, make_float4(hv[0], hv[1], hv[2], hv[3]));
             S *yp = y + (int64_t)b * ld_x + (int64_t)d * R;
 #pragma unroll
-            for (int r = 0; r < R; ++r)
-                if ((r & 3) == q) E::store(yp + r, p[r]);
+            for (int r0 = 0; r0 < R; r0 += 4) {   // lane q stores output r0 + q
+                if (r0 + q < R) {
+                    float v = p[r0];
+#pragma unroll
+                    for (int k = 1; k < 4 && r0 + k < R; ++k) v = (q == k) ? p[r0 + k] : v;
+                    E::store(yp + r0 + q, v);
+                }
+            }
         }
     }
 }
