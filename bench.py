@@ -74,11 +74,14 @@ def mimo_cost(form: str, R: int):
 KERNEL_SOURCES = {
     "prefill": ["scan_update.h", "mfma_common.h", "prefill_rows_kernel.h"],
     "step": ["scan_update.h", "step_kernel.h"],
+    "prefill_mimo": ["scan_update.h", "mfma_common.h", "prefill_rows_kernel.h", "step_kernel.h", "mimo_kernels.h",
+                     "prefill_mimo_rows_kernel.h"],
+    "step_mimo": ["scan_update.h", "step_kernel.h", "mimo_kernels.h"],
 }
 
 
 def kernel_source_hash(kind: str) -> str:
-    """Hash of the sources of one kernel ("prefill" or "step"); a profile summary records it,
+    """Hash of the sources of one kernel (a key of KERNEL_SOURCES); a profile summary records it,
     and its counters count only while the sources are unchanged."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kind]:
@@ -120,7 +123,7 @@ def read_traffic(workload: str, launches_per_step: int):
         m = re.match(r"\s*(\w+)\s*=\s*([0-9.eE+-]+|[0-9a-f]+)\s*$", line)
         if m:
             vals[m.group(1)] = m.group(2)
-    kind = "step" if workload.startswith("decode") else "prefill"
+    kind = ("step" if workload.startswith("decode") else "prefill") + ("_mimo" if "_mimo" in workload else "")
     if vals.get("kernel_source_hash") != kernel_source_hash(kind):
         return None
     try:
