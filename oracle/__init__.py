@@ -67,9 +67,11 @@ def _load():
     lib.oracle_step_trapezoid_f64.argtypes = [dp] * 10 + [i64, i64, i64, ci]
     lib.oracle_prefill_mimo_f64.argtypes = [dp] * 8 + [i64, i64, i64, i64, i64, ci, ci]
     lib.oracle_step_mimo_f64.argtypes = [dp] * 7 + [i64, i64, i64, i64, ci]
+    lib.oracle_prefill_mimo_trapezoid_f64.argtypes = [dp] * 11 + [i64, i64, i64, i64, i64, ci, ci]
     for f in (lib.oracle_prefill_f64, lib.oracle_prefill_chunked_f64, lib.oracle_step_f64,
               lib.oracle_prefill_complex_f64, lib.oracle_step_complex_f64, lib.oracle_prefill_trapezoid_f64,
-              lib.oracle_step_trapezoid_f64, lib.oracle_prefill_mimo_f64, lib.oracle_step_mimo_f64):
+              lib.oracle_step_trapezoid_f64, lib.oracle_prefill_mimo_f64, lib.oracle_step_mimo_f64,
+              lib.oracle_prefill_mimo_trapezoid_f64):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -345,3 +347,48 @@ def step_mimo(h, x_t, delta_t, A, B_t, C_t, form: str = "diagonal"):
     if rc != 0:
         raise RuntimeError(f"oracle_step_mimo_f64 failed ({rc})")
     return y, h
+
+
+# ---- MIMO with the exponential-trapezoidal rule ---------------------------------------------
+# Both Mamba-3 changes together (jscan_oracle.c, scan_chain_mimo with the trapezoidal flag): the
+# trapezoidal rule's input term with the rank-R input u_t[n] = sum_r B_t[n, r] x_t[d, r] in place
+# of B_t x_t.  The previous token is (x_prev [batch, D, R], B_prev [batch, N, R]) or none.
+
+
+def prefill_mimo_trapezoid(x, delta, lam, A, B, C, h0=None, x_prev=None, B_prev=None, form: str = "diagonal",
+                           nthreads: int = 0):
+    """Sequential fp64 MIMO scan with the exponential-trapezoidal rule.  Returns ``(y, h_final)``."""
+    lib = _load()
+    x, delta, lam, B, C = (_f64(v) for v in (x, delta, lam, B, C))
+    if x.ndim != 4 or B.ndim != 4:
+        raise ValueError("x must be [batch, L, D, R] and B, C [batch, L, N, R]")
+    batch, L, D, R = x.shape
+    N = B.shape[2]
+    A = _form_A(A, form, N)
+    h0 = None if h0 is None else _f64(h0)
+    if (delta.shape != (batch, L, D) or lam.shape != (batch, L, D) or B.shape != (batch, L, N, R)
+            or C.shape != B.shape or A.shape != (D, N)):
+        raise ValueError("prefill_mimo_trapezoid: inconsistent shapes")
+    if (x_prev is None) != (B_prev is None):
+        raise ValueError("x_prev and B_prev go together")
+    if x_prev is not None:
+        x_prev, B_prev = _f64(x_prev), _f64(B_prev)
+        if x_prev.shape != (batch, D, R) or B_prev.shape != (batch, N, R):
+            raise ValueError("x_prev must be [batch, D, R] and B_prev [batch, N, R]")
+    y = np.empty((batch, L, D, R), np.float64)
+    h = np.empty((batch, D, N), np.float64)
+    rc = lib.oracle_prefill_mimo_trapezoid_f64(_ptr(x), _ptr(delta), _ptr(lam), _ptr(A), _ptr(B), _ptr(C), _ptr(h0),
+                                               _ptr(x_prev), _ptr(B_prev), _ptr(y), _ptr(h), batch, L, D, N, R,
+                                               int(form == "complex"), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_prefill_mimo_trapezoid_f64 failed ({rc})")
+    return y, h
+
+
+def step_mimo_trapezoid(h, x_prev, B_prev, x_t, delta_t, lam_t, A, B_t, C_t, form: str = "diagonal"):
+    """One MIMO decode step with the exponential-trapezoidal rule: the one-token prefill from h with
+    (x_prev, B_prev) as the previous token.  Returns ``(y_t [batch, D, R], h_new)``."""
+    y, hn = prefill_mimo_trapezoid(np.asarray(_f64(x_t))[:, None], _f64(delta_t)[:, None], _f64(lam_t)[:, None], A,
+                                   _f64(B_t)[:, None], _f64(C_t)[:, None], h0=h, x_prev=x_prev, B_prev=B_prev,
+                                   form=form, nthreads=1)
+    return y[:, 0], hn

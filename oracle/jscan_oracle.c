@@ -271,23 +271,45 @@ static void scan_chain_trapezoid_complex(const scan_job *j, int64_t b, int64_t d
  * of A's entries and of B's and C's rows (for each r) are complex numbers, and
  * y_t[d][r] = sum_k Re(conj(c_k,r) h_t[k]).
  */
+/* The rank-R input of state n: sum_r B[n][r] x[r]. */
+static double mimo_u(const double *B, const double *x, int64_t n, int64_t R)
+{
+    double u = 0.0;
+    for (int64_t r = 0; r < R; ++r)
+        u += B[n * R + r] * x[r];
+    return u;
+}
+
+/*
+ * With the exponential-trapezoidal rule as well (j->trap), the input term of scan_chain_trapezoid
+ * with the rank-R input u in place of B x:
+ *     h_t = Abar_t h_{t-1} + (1 - lambda_t) Delta_t Abar_t u_{t-1} + lambda_t Delta_t u_t
+ * the token before the first being (x_prev [batch][D][R], B_prev [batch][N][R]) or none.
+ */
 static void scan_chain_mimo(const scan_job *j, int64_t b, int64_t d)
 {
     const int64_t L = j->L, D = j->D, N = j->N, R = j->R;
     double *h = (double *)malloc((size_t)N * sizeof(double));
-    for (int64_t n = 0; n < N; ++n)
+    double *u_prev = (double *)malloc((size_t)N * sizeof(double));
+    for (int64_t n = 0; n < N; ++n) {
         h[n] = j->h0 ? j->h0[(b * D + d) * N + n] : 0.0;
+        u_prev[n] = (j->trap && j->x_prev) ? mimo_u(j->B_prev + b * N * R, j->x_prev + (b * D + d) * R, n, R) : 0.0;
+    }
     for (int64_t t = 0; t < L; ++t) {
         const double delta_t = j->delta[(b * L + t) * D + d];
+        const double lam_t = j->trap ? j->lam[(b * L + t) * D + d] : 1.0;
         const double *x_t = j->x + ((b * L + t) * D + d) * R;
         const double *B_t = j->B + (b * L + t) * N * R;
         const double *C_t = j->C + (b * L + t) * N * R;
         double *y_t = j->y + ((b * L + t) * D + d) * R;
         for (int64_t n = 0; n < N; ++n) {
-            double u = 0.0;
-            for (int64_t r = 0; r < R; ++r)
-                u += B_t[n * R + r] * x_t[r];
-            h[n] = exp(delta_t * j->A[d * N + n]) * h[n] + delta_t * u;
+            const double Abar = exp(delta_t * j->A[d * N + n]);
+            const double u = mimo_u(B_t, x_t, n, R);
+            if (j->trap)
+                h[n] = Abar * h[n] + (1.0 - lam_t) * delta_t * Abar * u_prev[n] + lam_t * delta_t * u;
+            else
+                h[n] = Abar * h[n] + delta_t * u;
+            u_prev[n] = u;
         }
         for (int64_t r = 0; r < R; ++r) {
             double acc = 0.0;
@@ -300,26 +322,45 @@ static void scan_chain_mimo(const scan_job *j, int64_t b, int64_t d)
         for (int64_t n = 0; n < N; ++n)
             j->h_final[(b * D + d) * N + n] = h[n];
     free(h);
+    free(u_prev);
+}
+
+/* The rank-R complex input of complex state k: sum_r (B[2k][r] + i B[2k+1][r]) x[r]. */
+static double complex mimo_u_complex(const double *B, const double *x, int64_t k, int64_t R)
+{
+    double complex u = 0.0;
+    for (int64_t r = 0; r < R; ++r)
+        u += (B[2 * k * R + r] + I * B[(2 * k + 1) * R + r]) * x[r];
+    return u;
 }
 
 static void scan_chain_mimo_complex(const scan_job *j, int64_t b, int64_t d)
 {
     const int64_t L = j->L, D = j->D, N = j->N, R = j->R, K = N / 2;
     double complex *h = (double complex *)malloc((size_t)K * sizeof(double complex));
-    for (int64_t k = 0; k < K; ++k)
+    double complex *u_prev = (double complex *)malloc((size_t)K * sizeof(double complex));
+    for (int64_t k = 0; k < K; ++k) {
         h[k] = j->h0 ? j->h0[(b * D + d) * N + 2 * k] + I * j->h0[(b * D + d) * N + 2 * k + 1] : 0.0;
+        u_prev[k] = (j->trap && j->x_prev)
+                        ? mimo_u_complex(j->B_prev + b * N * R, j->x_prev + (b * D + d) * R, k, R)
+                        : 0.0;
+    }
     for (int64_t t = 0; t < L; ++t) {
         const double delta_t = j->delta[(b * L + t) * D + d];
+        const double lam_t = j->trap ? j->lam[(b * L + t) * D + d] : 1.0;
         const double *x_t = j->x + ((b * L + t) * D + d) * R;
         const double *B_t = j->B + (b * L + t) * N * R;
         const double *C_t = j->C + (b * L + t) * N * R;
         double *y_t = j->y + ((b * L + t) * D + d) * R;
         for (int64_t k = 0; k < K; ++k) {
             const double complex a = j->A[d * N + 2 * k] + I * j->A[d * N + 2 * k + 1];
-            double complex u = 0.0;
-            for (int64_t r = 0; r < R; ++r)
-                u += (B_t[2 * k * R + r] + I * B_t[(2 * k + 1) * R + r]) * x_t[r];
-            h[k] = cexp(delta_t * a) * h[k] + delta_t * u;
+            const double complex Abar = cexp(delta_t * a);
+            const double complex u = mimo_u_complex(B_t, x_t, k, R);
+            if (j->trap)
+                h[k] = Abar * h[k] + (1.0 - lam_t) * delta_t * Abar * u_prev[k] + lam_t * delta_t * u;
+            else
+                h[k] = Abar * h[k] + delta_t * u;
+            u_prev[k] = u;
         }
         for (int64_t r = 0; r < R; ++r) {
             double acc = 0.0;
@@ -334,6 +375,7 @@ static void scan_chain_mimo_complex(const scan_job *j, int64_t b, int64_t d)
             j->h_final[(b * D + d) * N + 2 * k + 1] = cimag(h[k]);
         }
     free(h);
+    free(u_prev);
 }
 
 static void *scan_worker(void *arg)
@@ -587,4 +629,25 @@ int oracle_step_mimo_f64(double *h, const double *x_t, const double *delta_t, co
     memcpy(h, hout, (size_t)(batch * D * N) * sizeof(double));
     free(hout);
     return rc;
+}
+
+/*
+ * MIMO prefill with the exponential-trapezoidal rule (scan_chain_mimo with j->trap, or its
+ * complex form): lam [batch][L][D]; x_prev [batch][D][R] and B_prev [batch][N][R], both NULL
+ * when there is no previous token.
+ */
+int oracle_prefill_mimo_trapezoid_f64(const double *x, const double *delta, const double *lam, const double *A,
+                                      const double *B, const double *C, const double *h0, const double *x_prev,
+                                      const double *B_prev, double *y, double *h_final, int64_t batch, int64_t L,
+                                      int64_t D, int64_t N, int64_t R, int cplx, int nthreads)
+{
+    if (R < 1 || (cplx && N % 2 != 0) || ((x_prev == NULL) != (B_prev == NULL)))
+        return -1;
+    scan_job j;
+    memset(&j, 0, sizeof j);
+    j.x = x; j.delta = delta; j.A = A; j.B = B; j.C = C; j.h0 = h0;
+    j.y = y; j.h_final = h_final;
+    j.batch = batch; j.L = L; j.D = D; j.N = N; j.R = R; j.cplx = cplx;
+    j.trap = 1; j.lam = lam; j.x_prev = x_prev; j.B_prev = B_prev;
+    return run_scan(j, nthreads);
 }
