@@ -32,7 +32,8 @@ inputs and outputs per channel, B and C N x R: the MIMO scan of Mamba-3) makes t
 rank-R sum (one product and R - 1 fused multiply-adds) and the output R fused multiply-adds per
 element: 2R + 4 slots and 4R + 3 flops for the diagonal A (12 and 19 at R = 4), 2R + 1 + 3/16
 and 4R + 1 + 2/16 for the scaled identity, (15 + 4R) / 2 and (8R + 13) / 2 for the complex state;
-x and y grow R-fold in bytes.
+x and y grow R-fold in bytes.  --mimo R --trapezoid (both Mamba-3 changes) adds the left end
+point's R fused multiply-adds per element (R slots, 2R flops) and lam to the bytes.
 """
 from __future__ import annotations
 
@@ -100,9 +101,11 @@ def algorithmic_bytes(wl, trapezoid: bool = False, mimo: int = 0) -> int:
         if wl.layers > 1:
             per_layer = (2 * wl.batch * wl.D * wl.N * 4 + (2 * R + 1) * wl.batch * wl.D * es
                          + 2 * wl.batch * wl.N * R * es + wl.D * wl.N * 4)
+            if trapezoid:   # lam, and the previous token's x and B rows
+                per_layer += (R + 1) * wl.batch * wl.D * es + wl.batch * wl.N * R * es
             return per_layer * wl.layers
-        return ((2 * R + 1) * wl.batch * wl.L * wl.D * es + 2 * wl.batch * wl.L * wl.N * R * es
-                + wl.D * wl.N * 4 + wl.batch * wl.D * wl.N * 4)
+        return ((2 * R + 1 + (1 if trapezoid else 0)) * wl.batch * wl.L * wl.D * es
+                + 2 * wl.batch * wl.L * wl.N * R * es + wl.D * wl.N * 4 + wl.batch * wl.D * wl.N * 4)
     if wl.layers > 1:  # decode: state read + write, token rows in and out, A, per layer
         per_layer = 2 * wl.batch * wl.D * wl.N * 4 + 3 * wl.batch * wl.D * es + 2 * wl.batch * wl.N * es + wl.D * wl.N * 4
         if trapezoid:
@@ -148,7 +151,10 @@ def cpu_baseline(wl, inp, channels: int, scalar_a=None, complex_a=False, lam=Non
     fn = oracle.prefill_complex if complex_a else oracle.prefill if scalar_a is None else oracle.prefill_scalar_a
     t0 = time.perf_counter()
     form = "complex" if complex_a else "diagonal" if scalar_a is None else "scalar"
-    if mimo:
+    if mimo and lam is not None:
+        lm = np.ascontiguousarray(lam[:, :, :channels].float().numpy(), dtype=np.float64)
+        oracle.prefill_mimo_trapezoid(args[0], args[1], lm, *args[2:], form=form, nthreads=threads)
+    elif mimo:
         oracle.prefill_mimo(*args, form=form, nthreads=threads)
     elif lam is not None:
         lm = np.ascontiguousarray(lam[:, :, :channels].float().numpy(), dtype=np.float64)
@@ -234,9 +240,6 @@ def main():
         print("bench.py: --scalar-a, --complex-a, --trapezoid and --mimo run the plain prefill or decode step only",
               file=sys.stderr)
         sys.exit(2)
-    if args.trapezoid and args.mimo:
-        print("bench.py: the library does not combine --trapezoid with --mimo", file=sys.stderr)
-        sys.exit(2)
     if args.scalar_a and args.complex_a:
         print("bench.py: choose one of --scalar-a and --complex-a", file=sys.stderr)
         sys.exit(2)
@@ -249,13 +252,15 @@ def main():
         layers = []
         for layer in range(wl.layers):
             # the trapezoidal rule's step is token 1, with token 0 as its previous token
+            token = 1 if args.trapezoid else 0
             if args.mimo:
-                inp = workloads.decode_layer_mimo_inputs(wl, layer, args.mimo)
-                inp["lam"] = None
+                inp = workloads.decode_layer_mimo_inputs(wl, layer, args.mimo, token=token)
+                prev = workloads.decode_layer_mimo_inputs(wl, layer, args.mimo, token=0) if args.trapezoid else None
+                inp["lam"] = workloads.decode_layer_inputs(wl, layer, token=token)["lam"]
             else:
-                inp = workloads.decode_layer_inputs(wl, layer, token=1 if args.trapezoid else 0)
+                inp = workloads.decode_layer_inputs(wl, layer, token=token)
+                prev = workloads.decode_layer_inputs(wl, layer, token=0) if args.trapezoid else None
             if args.trapezoid:
-                prev = workloads.decode_layer_inputs(wl, layer, token=0)
                 inp["x_prev"], inp["B_prev"] = prev["x"], prev["B"]
             else:
                 inp.pop("lam")
@@ -263,7 +268,7 @@ def main():
                 inp["A"] = workloads.draw_scalar_a(wl, layer=layer)
             if args.complex_a:
                 inp["A"] = workloads.draw_complex_a(wl, layer=layer)
-            layers.append({k: v.to(dev) for k, v in inp.items() if v is not None})
+            layers.append({k: v.to(dev) for k, v in inp.items()})
             layers[-1]["h"] = layers[-1].pop("h0")
 
         for L_ in layers:
@@ -272,7 +277,10 @@ def main():
 
         def token_step():
             for L_ in layers:
-                if args.mimo:
+                if args.mimo and args.trapezoid:
+                    jscan.step_mimo_trapezoid(L_["h"], L_["x_prev"], L_["B_prev"], L_["x"], L_["delta"], L_["lam"],
+                                              L_["A"], L_["B"], L_["C"], form=form, y_t=L_["y"])
+                elif args.mimo:
                     jscan.step_mimo(L_["h"], L_["x"], L_["delta"], L_["A"], L_["B"], L_["C"], form=form, y_t=L_["y"])
                 elif args.trapezoid:
                     jscan.step_trapezoid(L_["h"], L_["x_prev"], L_["B_prev"], L_["x"], L_["delta"], L_["lam"],
@@ -345,9 +353,16 @@ def main():
             elif args.complex_a:
                 host_inp["A"] = workloads.draw_complex_a(wl)
                 d["A"] = host_inp["A"].to(dev)
+            if args.trapezoid:
+                host_inp["lam"] = workloads.lam_inputs(wl)
+                d["lam"] = host_inp["lam"].to(dev)
 
-            def one_step():
-                jscan.prefill_mimo(d["x"], d["delta"], d["A"], d["B"], d["C"], form=form, y=y, h_final=h)
+                def one_step():
+                    jscan.prefill_mimo_trapezoid(d["x"], d["delta"], d["lam"], d["A"], d["B"], d["C"], form=form, y=y,
+                                                 h_final=h)
+            else:
+                def one_step():
+                    jscan.prefill_mimo(d["x"], d["delta"], d["A"], d["B"], d["C"], form=form, y=y, h_final=h)
             launches = 1
         elif args.trapezoid:
             host_inp["lam"] = workloads.lam_inputs(wl)
@@ -452,6 +467,8 @@ def main():
             slots, flops = slots + TRAP_SLOTS, flops + TRAP_FLOPS
         if args.mimo:
             slots, flops = mimo_cost(form, args.mimo)
+            if args.trapezoid:
+                slots, flops = slots + args.mimo, flops + 2 * args.mimo
         achieved_tf = state_elems * flops / (per_launch_ms * 1e-3) / 1e12
         peak_tf = VALU_SLOTS_PER_S / slots * flops / 1e12
         roofline = {"bound": "alu", "achieved": round(achieved_tf, 2), "peak": round(peak_tf, 2), "unit": "TFLOP/s",

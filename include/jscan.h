@@ -343,6 +343,36 @@ jscan_status jscan_step_mimo(float *h, const void *x_t, const void *delta_t, con
                              int64_t N, int64_t R, int64_t ld_x, int64_t ld_d, int64_t ld_bc,
                              jscan_a_form a_form, jscan_dtype dtype, void *stream);
 
+/*
+ * The MIMO scan with the exponential-trapezoidal rule: both Mamba-3 changes together.  The
+ * rank-R input u_t[n] = sum_r x_t[d][r] B_t[n][r] takes the place of x_t B_t at both end
+ * points of the step, in fp32 as
+ *     k = h;  k = fmaf(p_r, B_{t-1}[n][r], k) for r = 0 .. R-1,   p_r = ((1 - lam) * delta) * x_{t-1}[d][r]
+ * then the MIMO update of k with q_r = (lam * delta) * x_t[d][r] in place of delta * x_t[d][r].
+ * lam = 1 is jscan_prefill_mimo bit for bit; R = 1 is jscan_prefill_trapezoid bit for bit.
+ * lam [batch][L][D] (delta's layout); x_prev [batch][D][R] and B_prev [batch][N][R] are the token
+ * before the first (both NULL when there is none).  Other arguments, layouts and errors as for
+ * jscan_prefill_mimo and jscan_prefill_trapezoid.
+ */
+jscan_status jscan_prefill_mimo_trapezoid(const void *x, const void *delta, const void *lam,
+                                          const float *A, const void *B, const void *C,
+                                          const float *h0, const void *x_prev, const void *B_prev,
+                                          void *y, float *h_final, int64_t batch, int64_t L,
+                                          int64_t D, int64_t N, int64_t R, jscan_a_form a_form,
+                                          jscan_dtype dtype, void *stream);
+
+/*
+ * One MIMO decode token with the exponential-trapezoidal rule.  x_prev has x_t's rows (stride
+ * ld_x), B_prev B_t's (ld_bc), lam_t delta_t's (ld_d); all three required (zeros before a
+ * sequence's first token).  Otherwise as jscan_step_mimo.
+ */
+jscan_status jscan_step_mimo_trapezoid(float *h, const void *x_prev, const void *B_prev,
+                                       const void *x_t, const void *delta_t, const void *lam_t,
+                                       const float *A, const void *B_t, const void *C_t, void *y_t,
+                                       int64_t batch, int64_t D, int64_t N, int64_t R, int64_t ld_x,
+                                       int64_t ld_d, int64_t ld_bc, jscan_a_form a_form,
+                                       jscan_dtype dtype, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *jscan_status_string(jscan_status s);
 
@@ -351,7 +381,8 @@ int jscan_last_hip_error(void);
 
 /* Library ABI version: 100 * major + minor (101 adds the time-parallel prefill, 102 the
  * producer side, 103 the fused prefill, 104 the scaled-identity A entry points, 105 the
- * complex-valued state, 106 the exponential-trapezoidal rule, 107 the MIMO scan). */
+ * complex-valued state, 106 the exponential-trapezoidal rule, 107 the MIMO scan, 108 MIMO with the
+ * trapezoidal rule). */
 int jscan_version(void);
 
 #ifdef __cplusplus

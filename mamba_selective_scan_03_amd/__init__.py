@@ -18,6 +18,8 @@ There is no CPU fallback: without the built library every call raises.
     y_t = step_trapezoid(h, x_prev, B_prev, x_t, delta_t, lam_t, A, B_t, C_t)
     y, h_final = prefill_mimo(x, delta, A, B, C)          # R inputs and outputs per channel (MIMO)
     y_t = step_mimo(h, x_t, delta_t, A, B_t, C_t)
+    y, h_final = prefill_mimo_trapezoid(x, delta, lam, A, B, C)   # both Mamba-3 changes together
+    y_t = step_mimo_trapezoid(h, x_prev, B_prev, x_t, delta_t, lam_t, A, B_t, C_t)
 """
 from ._binding import (  # noqa: F401
     A_FORMS,
@@ -31,12 +33,14 @@ from ._binding import (  # noqa: F401
     prefill_complex,
     prefill_fused,
     prefill_mimo,
+    prefill_mimo_trapezoid,
     prefill_scalar_a,
     prefill_trapezoid,
     ssm_inputs,
     step,
     step_complex,
     step_mimo,
+    step_mimo_trapezoid,
     step_raw,
     step_scalar_a,
     step_trapezoid,

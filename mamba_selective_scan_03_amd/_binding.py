@@ -57,10 +57,15 @@ def library():
     lib.jscan_step_trapezoid.argtypes = [fp, vp, vp, vp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp]
     lib.jscan_prefill_mimo.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, i64, i32, i32, vp]
     lib.jscan_step_mimo.argtypes = [fp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32, i32, vp]
+    lib.jscan_prefill_mimo_trapezoid.argtypes = [vp, vp, vp, fp, vp, vp, fp, vp, vp, vp, fp, i64, i64, i64, i64, i64,
+                                                 i32, i32, vp]
+    lib.jscan_step_mimo_trapezoid.argtypes = [fp, vp, vp, vp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                                              i32, i32, vp]
     lib.jscan_prefill_chunked_workspace.restype = i64
     for f in (lib.jscan_prefill, lib.jscan_prefill_resume, lib.jscan_step, lib.jscan_prefill_chunked,
               lib.jscan_prefill_scalar_a, lib.jscan_step_scalar_a, lib.jscan_prefill_complex, lib.jscan_step_complex,
-              lib.jscan_prefill_trapezoid, lib.jscan_step_trapezoid, lib.jscan_prefill_mimo, lib.jscan_step_mimo):
+              lib.jscan_prefill_trapezoid, lib.jscan_step_trapezoid, lib.jscan_prefill_mimo, lib.jscan_step_mimo,
+              lib.jscan_prefill_mimo_trapezoid, lib.jscan_step_mimo_trapezoid):
         f.restype = i32
     lib.jscan_status_string.argtypes = [i32]
     lib.jscan_status_string.restype = ctypes.c_char_p
@@ -395,6 +400,20 @@ def prefill_mimo(x, delta, A, B, C, h0=None, form="diagonal", y=None, h_final=No
     x ``[batch, L, D, R]``, delta ``[batch, L, D]``, B, C ``[batch, L, 16, R]`` (one dtype),
     A as for ``form`` ("diagonal" ``[D, 16]``, "scalar" ``[D]``, "complex" ``[D, 16]``), optional
     h0 ``[batch, D, 16]``; R is 1, 2, 4 or 8.  Returns ``(y [batch, L, D, R], h_final)``."""
+    batch, L, D, R = _check_mimo_args(x, delta, A, B, C, h0, form)
+    if y is None:
+        y = torch.empty_like(x)
+    if h_final is None:
+        h_final = torch.empty((batch, D, D_STATE), dtype=torch.float32, device=x.device)
+    lib = library()
+    with torch.cuda.device(x.device):
+        st = lib.jscan_prefill_mimo(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(h0), _ptr(y), _ptr(h_final),
+                                    batch, L, D, D_STATE, R, A_FORMS[form], _DTYPES[x.dtype], _stream(x.device))
+    _check(st)
+    return y, h_final
+
+
+def _check_mimo_args(x, delta, A, B, C, h0, form):
     _require(form in A_FORMS, f"form must be one of {tuple(A_FORMS)}")
     _require(x.is_cuda and x.dtype in _DTYPES and x.dim() == 4 and x.is_contiguous(),
              "x must be a contiguous [batch, L, D, R] CUDA tensor (bfloat16 or float32)")
@@ -408,19 +427,44 @@ def prefill_mimo(x, delta, A, B, C, h0=None, form="diagonal", y=None, h_final=No
     if h0 is not None:
         _require(tuple(h0.shape) == (batch, D, D_STATE) and h0.dtype == torch.float32 and h0.is_contiguous()
                  and h0.device == x.device, "h0 must be a contiguous fp32 [batch, D, 16] tensor on x's device")
+    return batch, L, D, R
+
+
+def prefill_mimo_trapezoid(x, delta, lam, A, B, C, h0=None, x_prev=None, B_prev=None, form="diagonal", y=None,
+                           h_final=None):
+    """MIMO prefill with the exponential-trapezoidal rule (``jscan_prefill_mimo_trapezoid``): as
+    :func:`prefill_mimo`, plus ``lam`` ``[batch, L, D]`` (the right-end weight, x's dtype) and the
+    token before the first, ``x_prev [batch, D, R]`` and ``B_prev [batch, 16, R]`` (omit both for a
+    fresh sequence)."""
+    batch, L, D, R = _check_mimo_args(x, delta, A, B, C, h0, form)
+    _require(tuple(lam.shape) == (batch, L, D) and lam.dtype == x.dtype and lam.is_contiguous()
+             and lam.device == x.device, "lam must be a contiguous [batch, L, D] tensor like x")
+    _require((x_prev is None) == (B_prev is None), "x_prev and B_prev go together")
+    if x_prev is not None:
+        for name, t, shape in (("x_prev", x_prev, (batch, D, R)), ("B_prev", B_prev, (batch, D_STATE, R))):
+            _require(tuple(t.shape) == shape and t.dtype == x.dtype and t.is_contiguous() and t.device == x.device,
+                     f"{name} must be a contiguous {shape} tensor like x")
     if y is None:
         y = torch.empty_like(x)
     if h_final is None:
         h_final = torch.empty((batch, D, D_STATE), dtype=torch.float32, device=x.device)
     lib = library()
     with torch.cuda.device(x.device):
-        st = lib.jscan_prefill_mimo(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(h0), _ptr(y), _ptr(h_final),
-                                    batch, L, D, D_STATE, R, A_FORMS[form], _DTYPES[x.dtype], _stream(x.device))
+        st = lib.jscan_prefill_mimo_trapezoid(_ptr(x), _ptr(delta), _ptr(lam), _ptr(A), _ptr(B), _ptr(C), _ptr(h0),
+                                              _ptr(x_prev), _ptr(B_prev), _ptr(y), _ptr(h_final), batch, L, D, D_STATE,
+                                              R, A_FORMS[form], _DTYPES[x.dtype], _stream(x.device))
     _check(st)
     return y, h_final
 
 
-def step_mimo(h, x_t, delta_t, A, B_t, C_t, form="diagonal", y_t=None):
+def step_mimo_trapezoid(h, x_prev, B_prev, x_t, delta_t, lam_t, A, B_t, C_t, form="diagonal", y_t=None):
+    """One MIMO decode token with the exponential-trapezoidal rule (``jscan_step_mimo_trapezoid``):
+    as :func:`step_mimo`, plus the previous token's ``x_prev [batch, D, R]`` (x_t's row stride) and
+    ``B_prev [batch, 16, R]`` (B_t's) and this token's ``lam_t [batch, D]`` (delta_t's)."""
+    return step_mimo(h, x_t, delta_t, A, B_t, C_t, form=form, y_t=y_t, _trap=(x_prev, B_prev, lam_t))
+
+
+def step_mimo(h, x_t, delta_t, A, B_t, C_t, form="diagonal", y_t=None, _trap=None):
     """One MIMO decode token (``jscan_step_mimo``): h ``[batch, D, 16]`` fp32 in place; x_t
     ``[batch, D, R]``, delta_t ``[batch, D]``, B_t, C_t ``[batch, 16, R]`` (each row contiguous;
     rows may be strided views of prefill tensors, e.g. ``x[:, t]``).  Returns y_t ``[batch, D, R]``."""
@@ -443,6 +487,13 @@ def step_mimo(h, x_t, delta_t, A, B_t, C_t, form="diagonal", y_t=None):
     ld_d = delta_t.stride(0) if batch > 1 else D
     ld_bc = B_t.stride(0) if batch > 1 else D_STATE * R
     _require(batch <= 1 or C_t.stride(0) == ld_bc, "B_t and C_t must share a row stride")
+    if _trap is not None:
+        x_prev, B_prev, lam_t = _trap
+        for name, t, shape, ld in (("x_prev", x_prev, (batch, D, R), ld_x), ("B_prev", B_prev, (batch, D_STATE, R), ld_bc),
+                                   ("lam_t", lam_t, (batch, D), ld_d)):
+            _require(tuple(t.shape) == shape and t.dtype == x_t.dtype and t.device == h.device
+                     and t.stride(-1) == 1 and (t.dim() == 2 or t.stride(1) == R) and (batch <= 1 or t.stride(0) == ld),
+                     f"{name} must be {shape} with contiguous rows and the row stride of the matching input")
     if y_t is None:
         y_t = torch.empty((batch, ld_x), dtype=x_t.dtype, device=h.device)[:, :D * R].view(batch, D, R)
     _require(tuple(y_t.shape) == (batch, D, R) and y_t.dtype == x_t.dtype and y_t.stride(2) == 1
@@ -450,7 +501,14 @@ def step_mimo(h, x_t, delta_t, A, B_t, C_t, form="diagonal", y_t=None):
              "row stride")
     lib = library()
     with torch.cuda.device(h.device):
-        st = lib.jscan_step_mimo(_ptr(h), _ptr(x_t), _ptr(delta_t), _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(y_t), batch, D,
-                                 D_STATE, R, ld_x, ld_d, ld_bc, A_FORMS[form], _DTYPES[x_t.dtype], _stream(h.device))
+        if _trap is None:
+            st = lib.jscan_step_mimo(_ptr(h), _ptr(x_t), _ptr(delta_t), _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(y_t), batch,
+                                     D, D_STATE, R, ld_x, ld_d, ld_bc, A_FORMS[form], _DTYPES[x_t.dtype],
+                                     _stream(h.device))
+        else:
+            st = lib.jscan_step_mimo_trapezoid(_ptr(h), _ptr(_trap[0]), _ptr(_trap[1]), _ptr(x_t), _ptr(delta_t),
+                                               _ptr(_trap[2]), _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(y_t), batch, D,
+                                               D_STATE, R, ld_x, ld_d, ld_bc, A_FORMS[form], _DTYPES[x_t.dtype],
+                                               _stream(h.device))
     _check(st)
     return y_t

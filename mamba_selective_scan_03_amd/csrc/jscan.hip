@@ -180,84 +180,195 @@ bool form_of(jscan_a_form f, jscan::AForm *af) {
 
 bool mimo_rank_ok(int64_t R) { return R == 1 || R == 2 || R == 4 || R == 8; }
 
-// Rank 1 is the single-input scan (same layouts), rank 2-8 the row-mapped MIMO kernel when D is
-// a multiple of 32, else one lane per channel.
-template <typename E, jscan::AForm AF, int R>
+// Rank 1 is the single-input scan (same layouts), rank 2-8 the row-mapped MIMO kernel when it
+// applies, else one lane per channel.  kTrap: the exponential-trapezoidal rule (inputs tr).
+template <typename E, jscan::AForm AF, int R, bool kTrap>
 void launch_prefill_mimo_r(const void *x, const void *delta, const float *A, const void *B, const void *C,
                            const float *h0, void *y, float *h_final, int64_t batch, int64_t L, int64_t D,
-                           hipStream_t s) {
+                           jscan::Trap tr, hipStream_t s) {
     using T = typename E::store_t;
     if constexpr (R == 1) {
-        launch_prefill<E, AF>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s);
-    } else if (jscan::mimo_rows_kernel_applies(D, R)) {
-        jscan::launch_prefill_mimo_rows<E, AF, R>(static_cast<const T *>(x), static_cast<const T *>(delta), A,
-                                                  static_cast<const T *>(B), static_cast<const T *>(C), h0,
-                                                  static_cast<T *>(y), h_final, batch, L, (int)D, s);
-    } else {
+        launch_prefill<E, AF, kTrap>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s, tr);
+    } else if constexpr (R == 8 && kTrap) {
         const int blocks_per_row = (int)((D + 63) / 64);
-        hipLaunchKernelGGL((jscan::prefill_mimo_lane_kernel<E, AF, R>), dim3((unsigned)(batch * blocks_per_row)),
+        hipLaunchKernelGGL((jscan::prefill_mimo_lane_kernel<E, AF, R, kTrap>), dim3((unsigned)(batch * blocks_per_row)),
                            dim3(64), 0, s, static_cast<const T *>(x), static_cast<const T *>(delta), A,
                            static_cast<const T *>(B), static_cast<const T *>(C), h0, static_cast<T *>(y), h_final, L,
-                           (int)D, blocks_per_row);
+                           (int)D, blocks_per_row, tr);
+    } else {
+        if (jscan::mimo_rows_kernel_applies(D, R, kTrap)) {
+            jscan::launch_prefill_mimo_rows<E, AF, R, kTrap>(static_cast<const T *>(x), static_cast<const T *>(delta),
+                                                             A, static_cast<const T *>(B), static_cast<const T *>(C),
+                                                             h0, static_cast<T *>(y), h_final, batch, L, (int)D, s, tr);
+        } else {
+            const int blocks_per_row = (int)((D + 63) / 64);
+            hipLaunchKernelGGL((jscan::prefill_mimo_lane_kernel<E, AF, R, kTrap>),
+                               dim3((unsigned)(batch * blocks_per_row)), dim3(64), 0, s, static_cast<const T *>(x),
+                               static_cast<const T *>(delta), A, static_cast<const T *>(B), static_cast<const T *>(C),
+                               h0, static_cast<T *>(y), h_final, L, (int)D, blocks_per_row, tr);
+        }
     }
 }
-template <typename E, jscan::AForm AF>
+template <typename E, jscan::AForm AF, bool kTrap>
 void launch_prefill_mimo_af(const void *x, const void *delta, const float *A, const void *B, const void *C,
                             const float *h0, void *y, float *h_final, int64_t batch, int64_t L, int64_t D, int64_t R,
-                            hipStream_t s) {
+                            jscan::Trap tr, hipStream_t s) {
     switch (R) {
-    case 1: launch_prefill_mimo_r<E, AF, 1>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s); break;
-    case 2: launch_prefill_mimo_r<E, AF, 2>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s); break;
-    case 4: launch_prefill_mimo_r<E, AF, 4>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s); break;
-    default: launch_prefill_mimo_r<E, AF, 8>(x, delta, A, B, C, h0, y, h_final, batch, L, D, s); break;
+    case 1: launch_prefill_mimo_r<E, AF, 1, kTrap>(x, delta, A, B, C, h0, y, h_final, batch, L, D, tr, s); break;
+    case 2: launch_prefill_mimo_r<E, AF, 2, kTrap>(x, delta, A, B, C, h0, y, h_final, batch, L, D, tr, s); break;
+    case 4: launch_prefill_mimo_r<E, AF, 4, kTrap>(x, delta, A, B, C, h0, y, h_final, batch, L, D, tr, s); break;
+    default: launch_prefill_mimo_r<E, AF, 8, kTrap>(x, delta, A, B, C, h0, y, h_final, batch, L, D, tr, s); break;
     }
 }
-template <typename E>
+template <typename E, bool kTrap>
 void launch_prefill_mimo(const void *x, const void *delta, const float *A, const void *B, const void *C,
                          const float *h0, void *y, float *h_final, int64_t batch, int64_t L, int64_t D, int64_t R,
-                         jscan::AForm af, hipStream_t s) {
+                         jscan::AForm af, jscan::Trap tr, hipStream_t s) {
     using jscan::AForm;
     if (af == AForm::ScaledIdentity)
-        launch_prefill_mimo_af<E, AForm::ScaledIdentity>(x, delta, A, B, C, h0, y, h_final, batch, L, D, R, s);
+        launch_prefill_mimo_af<E, AForm::ScaledIdentity, kTrap>(x, delta, A, B, C, h0, y, h_final, batch, L, D, R, tr,
+                                                                s);
     else if (af == AForm::ComplexPairs)
-        launch_prefill_mimo_af<E, AForm::ComplexPairs>(x, delta, A, B, C, h0, y, h_final, batch, L, D, R, s);
+        launch_prefill_mimo_af<E, AForm::ComplexPairs, kTrap>(x, delta, A, B, C, h0, y, h_final, batch, L, D, R, tr, s);
     else
-        launch_prefill_mimo_af<E, AForm::Diagonal>(x, delta, A, B, C, h0, y, h_final, batch, L, D, R, s);
+        launch_prefill_mimo_af<E, AForm::Diagonal, kTrap>(x, delta, A, B, C, h0, y, h_final, batch, L, D, R, tr, s);
 }
 
-template <typename E, jscan::AForm AF, int R>
+template <typename E, jscan::AForm AF, int R, bool kTrap>
 void launch_step_mimo_r(float *h, const void *x, const void *delta, const float *A, const void *B, const void *C,
-                        void *y, int64_t batch, int64_t D, int64_t ld_x, int64_t ld_d, int64_t ld_bc, hipStream_t s) {
+                        void *y, int64_t batch, int64_t D, int64_t ld_x, int64_t ld_d, int64_t ld_bc, jscan::Trap tr,
+                        hipStream_t s) {
     using T = typename E::store_t;
     const int blocks_per_rows = (int)((D * 4 + 255) / 256);
     const int64_t row_groups = (batch + jscan::mimo_step::kRows - 1) / jscan::mimo_step::kRows;
-    hipLaunchKernelGGL((jscan::step_mimo_kernel<E, AF, R>), dim3((unsigned)(row_groups * blocks_per_rows)), dim3(256),
-                       0, s, h, static_cast<const T *>(x), static_cast<const T *>(delta), A, static_cast<const T *>(B),
-                       static_cast<const T *>(C), static_cast<T *>(y), (int)batch, (int)D, blocks_per_rows, ld_x, ld_d,
-                       ld_bc);
+    hipLaunchKernelGGL((jscan::step_mimo_kernel<E, AF, R, kTrap>), dim3((unsigned)(row_groups * blocks_per_rows)),
+                       dim3(256), 0, s, h, static_cast<const T *>(x), static_cast<const T *>(delta), A,
+                       static_cast<const T *>(B), static_cast<const T *>(C), static_cast<T *>(y), (int)batch, (int)D,
+                       blocks_per_rows, ld_x, ld_d, ld_bc, static_cast<const T *>(tr.lam),
+                       static_cast<const T *>(tr.x_prev), static_cast<const T *>(tr.B_prev));
 }
-template <typename E, jscan::AForm AF>
+template <typename E, jscan::AForm AF, bool kTrap>
 void launch_step_mimo_af(float *h, const void *x, const void *delta, const float *A, const void *B, const void *C,
                          void *y, int64_t batch, int64_t D, int64_t R, int64_t ld_x, int64_t ld_d, int64_t ld_bc,
-                         hipStream_t s) {
+                         jscan::Trap tr, hipStream_t s) {
     switch (R) {
-    case 1: launch_step_mimo_r<E, AF, 1>(h, x, delta, A, B, C, y, batch, D, ld_x, ld_d, ld_bc, s); break;
-    case 2: launch_step_mimo_r<E, AF, 2>(h, x, delta, A, B, C, y, batch, D, ld_x, ld_d, ld_bc, s); break;
-    case 4: launch_step_mimo_r<E, AF, 4>(h, x, delta, A, B, C, y, batch, D, ld_x, ld_d, ld_bc, s); break;
-    default: launch_step_mimo_r<E, AF, 8>(h, x, delta, A, B, C, y, batch, D, ld_x, ld_d, ld_bc, s); break;
+    case 1: launch_step_mimo_r<E, AF, 1, kTrap>(h, x, delta, A, B, C, y, batch, D, ld_x, ld_d, ld_bc, tr, s); break;
+    case 2: launch_step_mimo_r<E, AF, 2, kTrap>(h, x, delta, A, B, C, y, batch, D, ld_x, ld_d, ld_bc, tr, s); break;
+    case 4: launch_step_mimo_r<E, AF, 4, kTrap>(h, x, delta, A, B, C, y, batch, D, ld_x, ld_d, ld_bc, tr, s); break;
+    default: launch_step_mimo_r<E, AF, 8, kTrap>(h, x, delta, A, B, C, y, batch, D, ld_x, ld_d, ld_bc, tr, s); break;
     }
 }
-template <typename E>
+template <typename E, bool kTrap>
 void launch_step_mimo(float *h, const void *x, const void *delta, const float *A, const void *B, const void *C,
                       void *y, int64_t batch, int64_t D, int64_t R, int64_t ld_x, int64_t ld_d, int64_t ld_bc,
-                      jscan::AForm af, hipStream_t s) {
+                      jscan::AForm af, jscan::Trap tr, hipStream_t s) {
     using jscan::AForm;
     if (af == AForm::ScaledIdentity)
-        launch_step_mimo_af<E, AForm::ScaledIdentity>(h, x, delta, A, B, C, y, batch, D, R, ld_x, ld_d, ld_bc, s);
+        launch_step_mimo_af<E, AForm::ScaledIdentity, kTrap>(h, x, delta, A, B, C, y, batch, D, R, ld_x, ld_d, ld_bc, tr,
+                                                             s);
     else if (af == AForm::ComplexPairs)
-        launch_step_mimo_af<E, AForm::ComplexPairs>(h, x, delta, A, B, C, y, batch, D, R, ld_x, ld_d, ld_bc, s);
+        launch_step_mimo_af<E, AForm::ComplexPairs, kTrap>(h, x, delta, A, B, C, y, batch, D, R, ld_x, ld_d, ld_bc, tr,
+                                                           s);
     else
-        launch_step_mimo_af<E, AForm::Diagonal>(h, x, delta, A, B, C, y, batch, D, R, ld_x, ld_d, ld_bc, s);
+        launch_step_mimo_af<E, AForm::Diagonal, kTrap>(h, x, delta, A, B, C, y, batch, D, R, ld_x, ld_d, ld_bc, tr, s);
+}
+
+// Checks and launch shared by the MIMO prefill entry points; trap: the trapezoidal rule.
+jscan_status prefill_mimo_impl(const void *x, const void *delta, const void *lam, const float *A, const void *B,
+                               const void *C, const float *h0, const void *x_prev, const void *B_prev, void *y,
+                               float *h_final, int64_t batch, int64_t L, int64_t D, int64_t N, int64_t R,
+                               jscan_a_form a_form, jscan_dtype dtype, void *stream, bool trap) {
+    jscan::AForm af;
+    if (!form_of(a_form, &af)) return JSCAN_ERR_FORM;
+    if (dtype != JSCAN_F32 && dtype != JSCAN_BF16) return JSCAN_ERR_DTYPE;
+    if (batch < 0 || L < 0 || D < 0 || N != JSCAN_D_STATE || D % 8 != 0 || !mimo_rank_ok(R)) return JSCAN_ERR_SHAPE;
+    if (D > (1 << 24) || batch > (1 << 20) || batch * ((D + 63) / 64) > kMaxBlocks) return JSCAN_ERR_SHAPE;
+    if (batch * D * JSCAN_D_STATE / 256 > kMaxBlocks) return JSCAN_ERR_SHAPE;
+    if (batch == 0 || D == 0) return JSCAN_OK;
+    if (!A || !h_final) return JSCAN_ERR_NULL;
+    if (L > 0 && (!x || !delta || !B || !C || !y)) return JSCAN_ERR_NULL;
+    if (trap && ((L > 0 && !lam) || ((x_prev == nullptr) != (B_prev == nullptr)))) return JSCAN_ERR_NULL;
+    const void *arrays[] = {x, delta, A, B, C, h0, y, h_final, lam, x_prev, B_prev};
+    for (const void *p : arrays)
+        if (p && !aligned16(p)) return JSCAN_ERR_ALIGN;
+    const int64_t es = elem_bytes(dtype);
+    const int64_t xs = batch * L * D * R * es, ds = batch * L * D * es, bc = batch * L * N * R * es;
+    const int64_t state = batch * D * N * 4, a_bytes = D * (af == jscan::AForm::ScaledIdentity ? 1 : N) * 4;
+    const Span sy = span(y, L > 0 ? xs : 0), sh = span(h_final, state);
+    const Span inputs[] = {span(x, xs), span(delta, ds), span(A, a_bytes), span(B, bc), span(C, bc),
+                           span(trap ? lam : nullptr, L > 0 ? ds : 0), span(trap ? x_prev : nullptr, batch * D * R * es),
+                           span(trap ? B_prev : nullptr, batch * N * R * es)};
+    for (const Span &sp : inputs)
+        if (overlaps(sy, sp) || overlaps(sh, sp)) return JSCAN_ERR_ALIAS;
+    if (overlaps(sy, sh)) return JSCAN_ERR_ALIAS;
+    if (h0) {
+        const Span s0 = span(h0, state);
+        if (overlaps(sy, s0)) return JSCAN_ERR_ALIAS;
+        if (overlaps(sh, s0) && h0 != h_final) return JSCAN_ERR_ALIAS;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (L == 0) {
+        const int64_t count = batch * D * jscan::kDState;
+        hipLaunchKernelGGL(jscan::copy_state_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, h0,
+                           h_final, count);
+        return launch_status();
+    }
+    const jscan::Trap tr{lam, x_prev, B_prev};
+    if (dtype == JSCAN_BF16) {
+        if (trap) launch_prefill_mimo<jscan::BF16, true>(x, delta, A, B, C, h0, y, h_final, batch, L, D, R, af, tr, s);
+        else launch_prefill_mimo<jscan::BF16, false>(x, delta, A, B, C, h0, y, h_final, batch, L, D, R, af, tr, s);
+    } else {
+        if (trap) launch_prefill_mimo<jscan::F32, true>(x, delta, A, B, C, h0, y, h_final, batch, L, D, R, af, tr, s);
+        else launch_prefill_mimo<jscan::F32, false>(x, delta, A, B, C, h0, y, h_final, batch, L, D, R, af, tr, s);
+    }
+    return launch_status();
+}
+
+// Checks and launch shared by the MIMO step entry points; trap: the trapezoidal rule (lam has
+// delta's rows, x_prev x's rows, B_prev B's rows).
+jscan_status step_mimo_impl(float *h, const void *x_prev, const void *B_prev, const void *x_t, const void *delta_t,
+                            const void *lam_t, const float *A, const void *B_t, const void *C_t, void *y_t,
+                            int64_t batch, int64_t D, int64_t N, int64_t R, int64_t ld_x, int64_t ld_d, int64_t ld_bc,
+                            jscan_a_form a_form, jscan_dtype dtype, void *stream, bool trap) {
+    jscan::AForm af;
+    if (!form_of(a_form, &af)) return JSCAN_ERR_FORM;
+    if (dtype != JSCAN_F32 && dtype != JSCAN_BF16) return JSCAN_ERR_DTYPE;
+    if (batch < 0 || D < 0 || N != JSCAN_D_STATE || D % 8 != 0 || !mimo_rank_ok(R)) return JSCAN_ERR_SHAPE;
+    if (D > (1 << 24) || batch > (1 << 20)) return JSCAN_ERR_SHAPE;
+    if ((batch + jscan::mimo_step::kRows - 1) / jscan::mimo_step::kRows * ((D * 4 + 255) / 256) > kMaxBlocks)
+        return JSCAN_ERR_SHAPE;
+    if (batch == 0 || D == 0) return JSCAN_OK;
+    if (ld_x < D * R || ld_d < D || ld_bc < N * R || ld_x % 8 != 0 || ld_d % 8 != 0 || ld_bc % 8 != 0)
+        return JSCAN_ERR_SHAPE;
+    if (!h || !x_t || !delta_t || !A || !B_t || !C_t || !y_t) return JSCAN_ERR_NULL;
+    if (trap && (!x_prev || !B_prev || !lam_t)) return JSCAN_ERR_NULL;
+    const void *arrays[] = {h, x_t, delta_t, A, B_t, C_t, y_t};
+    for (const void *p : arrays)
+        if (!aligned16(p)) return JSCAN_ERR_ALIGN;
+    const void *extra[] = {x_prev, B_prev, lam_t};
+    for (const void *p : extra)
+        if (trap && !aligned16(p)) return JSCAN_ERR_ALIGN;
+    const int64_t es = elem_bytes(dtype);
+    const int64_t rows_x = ((batch - 1) * ld_x + D * R) * es, rows_d = ((batch - 1) * ld_d + D) * es;
+    const int64_t rows_bc = ((batch - 1) * ld_bc + N * R) * es;
+    const Span sh = span(h, batch * D * N * 4), sy = span(y_t, rows_x);
+    const Span inputs[] = {span(x_t, rows_x), span(delta_t, rows_d),
+                           span(A, D * (af == jscan::AForm::ScaledIdentity ? 1 : N) * 4), span(B_t, rows_bc),
+                           span(C_t, rows_bc), span(trap ? x_prev : nullptr, rows_x),
+                           span(trap ? B_prev : nullptr, rows_bc), span(trap ? lam_t : nullptr, rows_d)};
+    for (const Span &sp : inputs)
+        if (overlaps(sy, sp) || overlaps(sh, sp)) return JSCAN_ERR_ALIAS;
+    if (overlaps(sy, sh)) return JSCAN_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const jscan::Trap tr{lam_t, x_prev, B_prev};
+    if (dtype == JSCAN_BF16) {
+        if (trap) launch_step_mimo<jscan::BF16, true>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, R, ld_x, ld_d, ld_bc, af, tr, s);
+        else launch_step_mimo<jscan::BF16, false>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, R, ld_x, ld_d, ld_bc, af, tr, s);
+    } else {
+        if (trap) launch_step_mimo<jscan::F32, true>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, R, ld_x, ld_d, ld_bc, af, tr, s);
+        else launch_step_mimo<jscan::F32, false>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, R, ld_x, ld_d, ld_bc, af, tr, s);
+    }
+    return launch_status();
 }
 
 // ---- time-parallel prefill ---------------------------------------------------------------
@@ -567,78 +678,33 @@ jscan_status jscan_step_trapezoid(float *h, const void *x_prev, const void *B_pr
 jscan_status jscan_prefill_mimo(const void *x, const void *delta, const float *A, const void *B, const void *C,
                                 const float *h0, void *y, float *h_final, int64_t batch, int64_t L, int64_t D,
                                 int64_t N, int64_t R, jscan_a_form a_form, jscan_dtype dtype, void *stream) {
-    jscan::AForm af;
-    if (!form_of(a_form, &af)) return JSCAN_ERR_FORM;
-    if (dtype != JSCAN_F32 && dtype != JSCAN_BF16) return JSCAN_ERR_DTYPE;
-    if (batch < 0 || L < 0 || D < 0 || N != JSCAN_D_STATE || D % 8 != 0 || !mimo_rank_ok(R)) return JSCAN_ERR_SHAPE;
-    if (D > (1 << 24) || batch > (1 << 20) || batch * ((D + 63) / 64) > kMaxBlocks) return JSCAN_ERR_SHAPE;
-    if (batch * D * JSCAN_D_STATE / 256 > kMaxBlocks) return JSCAN_ERR_SHAPE;
-    if (batch == 0 || D == 0) return JSCAN_OK;
-    if (!A || !h_final) return JSCAN_ERR_NULL;
-    if (L > 0 && (!x || !delta || !B || !C || !y)) return JSCAN_ERR_NULL;
-    const void *arrays[] = {x, delta, A, B, C, h0, y, h_final};
-    for (const void *p : arrays)
-        if (p && !aligned16(p)) return JSCAN_ERR_ALIGN;
-    const int64_t es = elem_bytes(dtype);
-    const int64_t xs = batch * L * D * R * es, ds = batch * L * D * es, bc = batch * L * N * R * es;
-    const int64_t state = batch * D * N * 4, a_bytes = D * (af == jscan::AForm::ScaledIdentity ? 1 : N) * 4;
-    const Span sy = span(y, L > 0 ? xs : 0), sh = span(h_final, state);
-    const Span inputs[] = {span(x, xs), span(delta, ds), span(A, a_bytes), span(B, bc), span(C, bc)};
-    for (const Span &sp : inputs)
-        if (overlaps(sy, sp) || overlaps(sh, sp)) return JSCAN_ERR_ALIAS;
-    if (overlaps(sy, sh)) return JSCAN_ERR_ALIAS;
-    if (h0) {
-        const Span s0 = span(h0, state);
-        if (overlaps(sy, s0)) return JSCAN_ERR_ALIAS;
-        if (overlaps(sh, s0) && h0 != h_final) return JSCAN_ERR_ALIAS;
-    }
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (L == 0) {
-        const int64_t count = batch * D * jscan::kDState;
-        hipLaunchKernelGGL(jscan::copy_state_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, h0,
-                           h_final, count);
-        return launch_status();
-    }
-    if (dtype == JSCAN_BF16)
-        launch_prefill_mimo<jscan::BF16>(x, delta, A, B, C, h0, y, h_final, batch, L, D, R, af, s);
-    else
-        launch_prefill_mimo<jscan::F32>(x, delta, A, B, C, h0, y, h_final, batch, L, D, R, af, s);
-    return launch_status();
+    return prefill_mimo_impl(x, delta, nullptr, A, B, C, h0, nullptr, nullptr, y, h_final, batch, L, D, N, R, a_form,
+                             dtype, stream, false);
 }
 
 jscan_status jscan_step_mimo(float *h, const void *x_t, const void *delta_t, const float *A, const void *B_t,
                              const void *C_t, void *y_t, int64_t batch, int64_t D, int64_t N, int64_t R, int64_t ld_x,
                              int64_t ld_d, int64_t ld_bc, jscan_a_form a_form, jscan_dtype dtype, void *stream) {
-    jscan::AForm af;
-    if (!form_of(a_form, &af)) return JSCAN_ERR_FORM;
-    if (dtype != JSCAN_F32 && dtype != JSCAN_BF16) return JSCAN_ERR_DTYPE;
-    if (batch < 0 || D < 0 || N != JSCAN_D_STATE || D % 8 != 0 || !mimo_rank_ok(R)) return JSCAN_ERR_SHAPE;
-    if (D > (1 << 24) || batch > (1 << 20)) return JSCAN_ERR_SHAPE;
-    if ((batch + jscan::mimo_step::kRows - 1) / jscan::mimo_step::kRows * ((D * 4 + 255) / 256) > kMaxBlocks)
-        return JSCAN_ERR_SHAPE;
-    if (batch == 0 || D == 0) return JSCAN_OK;
-    if (ld_x < D * R || ld_d < D || ld_bc < N * R || ld_x % 8 != 0 || ld_d % 8 != 0 || ld_bc % 8 != 0)
-        return JSCAN_ERR_SHAPE;
-    if (!h || !x_t || !delta_t || !A || !B_t || !C_t || !y_t) return JSCAN_ERR_NULL;
-    const void *arrays[] = {h, x_t, delta_t, A, B_t, C_t, y_t};
-    for (const void *p : arrays)
-        if (!aligned16(p)) return JSCAN_ERR_ALIGN;
-    const int64_t es = elem_bytes(dtype);
-    const int64_t rows_x = ((batch - 1) * ld_x + D * R) * es, rows_d = ((batch - 1) * ld_d + D) * es;
-    const int64_t rows_bc = ((batch - 1) * ld_bc + N * R) * es;
-    const Span sh = span(h, batch * D * N * 4), sy = span(y_t, rows_x);
-    const Span inputs[] = {span(x_t, rows_x), span(delta_t, rows_d),
-                           span(A, D * (af == jscan::AForm::ScaledIdentity ? 1 : N) * 4), span(B_t, rows_bc),
-                           span(C_t, rows_bc)};
-    for (const Span &sp : inputs)
-        if (overlaps(sy, sp) || overlaps(sh, sp)) return JSCAN_ERR_ALIAS;
-    if (overlaps(sy, sh)) return JSCAN_ERR_ALIAS;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (dtype == JSCAN_BF16)
-        launch_step_mimo<jscan::BF16>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, R, ld_x, ld_d, ld_bc, af, s);
-    else
-        launch_step_mimo<jscan::F32>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, R, ld_x, ld_d, ld_bc, af, s);
-    return launch_status();
+    return step_mimo_impl(h, nullptr, nullptr, x_t, delta_t, nullptr, A, B_t, C_t, y_t, batch, D, N, R, ld_x, ld_d,
+                          ld_bc, a_form, dtype, stream, false);
+}
+
+jscan_status jscan_prefill_mimo_trapezoid(const void *x, const void *delta, const void *lam, const float *A,
+                                          const void *B, const void *C, const float *h0, const void *x_prev,
+                                          const void *B_prev, void *y, float *h_final, int64_t batch, int64_t L,
+                                          int64_t D, int64_t N, int64_t R, jscan_a_form a_form, jscan_dtype dtype,
+                                          void *stream) {
+    return prefill_mimo_impl(x, delta, lam, A, B, C, h0, x_prev, B_prev, y, h_final, batch, L, D, N, R, a_form, dtype,
+                             stream, true);
+}
+
+jscan_status jscan_step_mimo_trapezoid(float *h, const void *x_prev, const void *B_prev, const void *x_t,
+                                       const void *delta_t, const void *lam_t, const float *A, const void *B_t,
+                                       const void *C_t, void *y_t, int64_t batch, int64_t D, int64_t N, int64_t R,
+                                       int64_t ld_x, int64_t ld_d, int64_t ld_bc, jscan_a_form a_form,
+                                       jscan_dtype dtype, void *stream) {
+    return step_mimo_impl(h, x_prev, B_prev, x_t, delta_t, lam_t, A, B_t, C_t, y_t, batch, D, N, R, ld_x, ld_d, ld_bc,
+                          a_form, dtype, stream, true);
 }
 
 jscan_status jscan_ssm_inputs(const void *x, const void *w_x, const float *g_delta, const float *g_B,
@@ -733,6 +799,6 @@ const char *jscan_status_string(jscan_status s) {
 
 int jscan_last_hip_error(void) { return g_last_hip_error; }
 
-int jscan_version(void) { return 107; }
+int jscan_version(void) { return 108; }
 
 }  // extern "C"

@@ -123,13 +123,16 @@ template <int K> struct UniformRow<F32, K> {
 // A work-group is one wave of 64 consecutive channels of one batch row, so B_t and C_t (N x R)
 // are the same for the whole wave and are read through the scalar cache; the channel's R
 // inputs and R outputs are one vector access each.  One lane carries a channel's whole state,
-// so the R outputs need no exchange between lanes.
-template <typename E, AForm AF, int R>
+// so the R outputs need no exchange between lanes.  With the exponential-trapezoidal rule (kTrap;
+// tr.lam like delta, tr.x_prev [rows][D][R], tr.B_prev [rows][16][R]) the previous token's input
+// enters each step first (mimo_left_in); the lane keeps the previous token's x, and reads its B
+// row again through the scalar cache.
+template <typename E, AForm AF, int R, bool kTrap = false>
 __global__ __launch_bounds__(64) void prefill_mimo_lane_kernel(
     const typename E::store_t *__restrict__ x, const typename E::store_t *__restrict__ dl,
     const float *__restrict__ A, const typename E::store_t *__restrict__ B, const typename E::store_t *__restrict__ C,
     const float *__restrict__ h0, typename E::store_t *__restrict__ y, float *__restrict__ h_final, int64_t L, int D,
-    int blocks_per_row) {
+    int blocks_per_row, Trap tr) {
     const int b = blockIdx.x / blocks_per_row;
     const int d = (blockIdx.x - b * blocks_per_row) * 64 + threadIdx.x;
     if (d >= D) return;   // no cross-lane work, so idle lanes may leave
@@ -152,6 +155,12 @@ __global__ __launch_bounds__(64) void prefill_mimo_lane_kernel(
     S *yr = y + ((int64_t)b * L * D + d) * R;
     const S *Br = B + (int64_t)b * L * kDState * R;
     const S *Cr = C + (int64_t)b * L * kDState * R;
+    const S *lr = kTrap ? static_cast<const S *>(tr.lam) + (int64_t)b * L * D + d : nullptr;
+    const S *Bp0 = (kTrap && tr.B_prev) ? static_cast<const S *>(tr.B_prev) + (int64_t)b * kDState * R : nullptr;
+    float xprev[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) xprev[r] = 0.0f;
+    if (kTrap && tr.x_prev) RowLoad<E, R>::load(static_cast<const S *>(tr.x_prev) + ((int64_t)b * D + d) * R, xprev);
 
     for (int64_t t = 0; t < L; ++t) {
         float xv[R], dx[R];
@@ -162,6 +171,29 @@ __global__ __launch_bounds__(64) void prefill_mimo_lane_kernel(
         // B_t and C_t in pairs of states (2R values), so that at most 4R of them are live at once
         const S *Bt = Br + t * kDState * R;
         const S *Ct = Cr + t * kDState * R;
+        if constexpr (kTrap) {   // the left end point in first; q replaces delta * x below
+            const float lv = E::load(lr + t * D);
+            float pl[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                pl[r] = trap_left(dv, lv, xprev[r]);
+                dx[r] = trap_right(dv, lv, xv[r]);
+                xprev[r] = xv[r];
+            }
+            const S *Bp = t > 0 ? Bt - kDState * R : Bp0;   // the previous token's B row, or none
+#pragma unroll
+            for (int k = 0; k < kDState / 2; ++k) {
+                float bp[2 * R];
+                if (Bp) {
+                    UniformRow<E, 2 * R>::load(Bp + 2 * k * R, bp);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 2 * R; ++i) bp[i] = 0.0f;
+                }
+                h[2 * k] = mimo_left_in<R>(h[2 * k], pl, bp);
+                h[2 * k + 1] = mimo_left_in<R>(h[2 * k + 1], pl, bp + R);
+            }
+        }
         const float abar = kScalarA ? decay(dv, a2[0]) : 0.0f;
 #pragma unroll
         for (int k = 0; k < kDState / 2; ++k) {
@@ -200,11 +232,13 @@ __global__ __launch_bounds__(64) void prefill_mimo_lane_kernel(
 // converted to fp32 once per work-group into LDS, one value per thread, and each lane reads its
 // quad's R columns from there.  A lane forms its four input terms and its four C h products per
 // output; two DPP quad exchanges sum each output over the quad, and lane q stores outputs q and
-// q + 4, so the quad writes its R outputs as one contiguous run.
+// q + 4, so the quad writes its R outputs as one contiguous run.  With the exponential-trapezoidal
+// rule (kTrap) the previous token's x (xp, rows like x) and B (bp, rows like B, staged with B and
+// C) enter first as the left end point (mimo_left_in), weighted by 1 - lam (rows like delta).
 namespace mimo_step {
 constexpr int kRows = 2;   // batch rows per lane
 }
-template <typename E, AForm AF, int R>
+template <typename E, AForm AF, int R, bool kTrap = false>
 __global__ __launch_bounds__(256) void step_mimo_kernel(float *__restrict__ h, const typename E::store_t *__restrict__ x,
                                                         const typename E::store_t *__restrict__ dl,
                                                         const float *__restrict__ A,
@@ -212,10 +246,13 @@ __global__ __launch_bounds__(256) void step_mimo_kernel(float *__restrict__ h, c
                                                         const typename E::store_t *__restrict__ Ct,
                                                         typename E::store_t *__restrict__ y, int batch, int D,
                                                         int blocks_per_rows, int64_t ld_x, int64_t ld_d,
-                                                        int64_t ld_bc) {
+                                                        int64_t ld_bc, const typename E::store_t *__restrict__ lam,
+                                                        const typename E::store_t *__restrict__ xp,
+                                                        const typename E::store_t *__restrict__ bp) {
     constexpr int NR = mimo_step::kRows;
     constexpr int kBC = kDState * R;                 // values of one B or C row
-    __shared__ __attribute__((aligned(16))) float bc_s[NR][2][kBC];
+    constexpr int kW = kTrap ? 3 : 2;                // B, C (and the previous token's B)
+    __shared__ __attribute__((aligned(16))) float bc_s[NR][kW][kBC];
     const int rg = blockIdx.x / blocks_per_rows;
     const int lane_in_row = (blockIdx.x - rg * blocks_per_rows) * 256 + threadIdx.x;
     const bool active = lane_in_row < D * 4;         // whole quads are active or not
@@ -225,7 +262,7 @@ __global__ __launch_bounds__(256) void step_mimo_kernel(float *__restrict__ h, c
     // every row's state, x and delta requested first (the state with non-temporal accesses, as in
     // the single-input step), so that they are in flight while B and C are staged
     float4 h4[NR];
-    float xv[NR][R], dv[NR];
+    float xv[NR][R], dv[NR], xpv[NR][R], lv[NR];
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
         // a missing last row re-reads the row before it and stores nothing
@@ -234,12 +271,16 @@ __global__ __launch_bounds__(256) void step_mimo_kernel(float *__restrict__ h, c
             h4[j] = load_state(h + ((int64_t)b * D + d) * kDState + q * 4);
             RowLoad<E, R>::load(x + (int64_t)b * ld_x + (int64_t)d * R, xv[j]);
             dv[j] = E::load(dl + (int64_t)b * ld_d + d);
+            if constexpr (kTrap) {
+                RowLoad<E, R>::load(xp + (int64_t)b * ld_x + (int64_t)d * R, xpv[j]);
+                lv[j] = E::load(lam + (int64_t)b * ld_d + d);
+            }
         }
     }
-    for (int i = threadIdx.x; i < NR * 2 * kBC; i += 256) {
-        const int j = i / (2 * kBC), w = (i / kBC) & 1, k = i % kBC;
+    for (int i = threadIdx.x; i < NR * kW * kBC; i += 256) {
+        const int j = i / (kW * kBC), w = (i / kBC) % kW, k = i % kBC;
         const int b = min(rg * NR + j, batch - 1);
-        bc_s[j][w][k] = E::load((w ? Ct : Bt) + (int64_t)b * ld_bc + k);
+        bc_s[j][w][k] = E::load((w == 0 ? Bt : w == 1 ? Ct : bp) + (int64_t)b * ld_bc + k);
     }
     __syncthreads();
     if (!active) return;
@@ -252,18 +293,32 @@ __global__ __launch_bounds__(256) void step_mimo_kernel(float *__restrict__ h, c
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
         const int b = rg * NR + j;
-        float bq[4 * R], cq[4 * R];
+        float bq[4 * R], cq[4 * R], pq[4 * R];
 #pragma unroll
         for (int i = 0; i < R; ++i) {   // the quad's rows 4q..4q+3 of B and C: 4R consecutive values
             const float4 vb = reinterpret_cast<const float4 *>(&bc_s[j][0][q * 4 * R])[i];
             const float4 vc = reinterpret_cast<const float4 *>(&bc_s[j][1][q * 4 * R])[i];
             bq[4 * i] = vb.x; bq[4 * i + 1] = vb.y; bq[4 * i + 2] = vb.z; bq[4 * i + 3] = vb.w;
             cq[4 * i] = vc.x; cq[4 * i + 1] = vc.y; cq[4 * i + 2] = vc.z; cq[4 * i + 3] = vc.w;
+            if constexpr (kTrap) {
+                const float4 vp = reinterpret_cast<const float4 *>(&bc_s[j][kW - 1][q * 4 * R])[i];
+                pq[4 * i] = vp.x; pq[4 * i + 1] = vp.y; pq[4 * i + 2] = vp.z; pq[4 * i + 3] = vp.w;
+            }
         }
         float hv[4] = {h4[j].x, h4[j].y, h4[j].z, h4[j].w};
         float dx[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) dx[r] = delta_x(dv[j], xv[j][r]);
+        if constexpr (kTrap) {   // the left end point in first; q replaces delta * x below
+            float pl[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                pl[r] = trap_left(dv[j], lv[j], xpv[j][r]);
+                dx[r] = trap_right(dv[j], lv[j], xv[j][r]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hv[i] = mimo_left_in<R>(hv[i], pl, pq + i * R);
+        }
         if constexpr (kComplexA) {
             advance_complex_input(hv[0], hv[1], dv[j], ca0, mimo_input<R>(dx, bq), mimo_input<R>(dx, bq + R));
             advance_complex_input(hv[2], hv[3], dv[j], ca1, mimo_input<R>(dx, bq + 2 * R), mimo_input<R>(dx, bq + 3 * R));

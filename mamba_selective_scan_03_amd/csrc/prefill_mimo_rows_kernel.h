@@ -17,6 +17,10 @@
 // Tiles are kT = 32 tokens for R <= 4 and 16 for R = 8, so that the R-fold LDS areas stay
 // within the work-group's share.  One barrier per tile; the helper waves stage tile k + 1,
 // request tile k + 3 and store the outputs of tile k - 1 while the scan waves scan tile k.
+// With the exponential-trapezoidal rule (kTrap) the helper waves also stage
+// p_r = ((1 - lam) delta) x_{t-1}[r] like delta x, and the previous token's B as a third B/C
+// tile; the scan lane takes the left end point in first (mimo_left_in, the DPP broadcast folded
+// in).  Tiles are then 16 tokens at R = 4, and R = 8 runs the lane kernel.
 // Tokens past L are identity tokens (delta = 0, x = -0, B = C = 0), which leave every state
 // bit-identical.
 #pragma once
@@ -27,9 +31,9 @@
 namespace jscan {
 
 namespace mrows {
-template <int R> struct Cfg {
-    static_assert(R == 2 || R == 4 || R == 8, "rank 2, 4 or 8");
-    static constexpr int kT = R <= 4 ? 32 : 16;    // tokens per tile
+template <int R, bool kTrap = false> struct Cfg {
+    static_assert(R == 2 || R == 4 || (R == 8 && !kTrap), "rank 2, 4 or 8 (8 without the trapezoidal rule)");
+    static constexpr int kT = (R <= 4 && !(kTrap && R == 4)) ? 32 : 16;   // tokens per tile
     static constexpr int kCh = 32;                 // channels per work-group
     static constexpr int kThreads = 512;
     static constexpr int kHalf = 256;
@@ -48,6 +52,7 @@ template <int R> struct Cfg {
     // B/C rows of 16 tokens read by the 4 rows of a wave (states 2 apart) land 16 banks apart
     static constexpr int kBS = R == 2 ? kT + 4 : R == 4 ? kT + 2 : kT + 1;
     static constexpr int kBcSize = kDState * R * kBS;
+    static constexpr int kBcTiles = kTrap ? 3 : 2;   // B, C (and the previous token's B)
     static constexpr int kYS = kCh * R + (R == 2 ? 32 : 0);
     static constexpr int kYSize = 2 * kT * kYS;
 };
@@ -94,19 +99,32 @@ template <int K> struct RawRow<F32, K> {
     __device__ __forceinline__ float get(int i) const { return v[i]; }
 };
 
-template <typename E, int R> struct MimoTileRegs {
-    using C = mrows::Cfg<R>;
+template <typename E, int R, bool kTrap = false> struct MimoTileRegs {
+    using C = mrows::Cfg<R, kTrap>;
     RawRow<E, C::kXV> x;     // token tid / kTPT, channels kCPT (tid % kTPT) .. + kCPT, all ranks
     RawRow<E, C::kCPT> dl;   // the same token and channels
     RawRow<E, C::kBV> bc;    // B or C: token, states kSPT (tid % kTPB) .. + kSPT, all ranks
+    // trapezoidal rule only: lam of the token and channels; x of the token before; B (or C) of
+    // the token before
+    RawRow<E, C::kCPT> lam;
+    RawRow<E, C::kXV> xp;
+    RawRow<E, C::kBV> bcp;
+};
+
+// Where a trapezoidal helper thread finds the token before its row's first: the caller's
+// x_prev and B_prev (at this thread's channels and states), or stand-ins staged as zero.
+template <typename E> struct MimoPrev {
+    const typename E::store_t *lam, *x, *bc;
+    bool given;
 };
 
 // Requests one tile's raw inputs (tokens past L re-read token L - 1; staging replaces them).
-template <typename E, int R>
-__device__ __forceinline__ void mimo_load_tile(MimoTileRegs<E, R> &Rg, const typename E::store_t *xb,
+template <typename E, int R, bool kTrap = false>
+__device__ __forceinline__ void mimo_load_tile(MimoTileRegs<E, R, kTrap> &Rg, const typename E::store_t *xb,
                                                const typename E::store_t *db, const typename E::store_t *bcb,
-                                               int64_t t0, int64_t L, int D, int tid) {
-    using C = mrows::Cfg<R>;
+                                               int64_t t0, int64_t L, int D, int tid,
+                                               const MimoPrev<E> &pr = MimoPrev<E>{nullptr, nullptr, nullptr, false}) {
+    using C = mrows::Cfg<R, kTrap>;
     const int t = tid / C::kTPT, c0 = (tid % C::kTPT) * C::kCPT;
     const int64_t tt = min(t0 + t, L - 1);
     Rg.x.load(xb + (tt * D + c0) * R);
@@ -114,44 +132,78 @@ __device__ __forceinline__ void mimo_load_tile(MimoTileRegs<E, R> &Rg, const typ
     const int tb = (tid & 127) / C::kTPB, s0 = (tid % C::kTPB) * C::kSPT;
     const int64_t tq = min(t0 + tb, L - 1);
     Rg.bc.load(bcb + (tq * kDState + s0) * R);
+    if constexpr (kTrap) {
+        Rg.lam.load(pr.lam + tt * D + c0);
+        const int64_t tp = min(t0 + t - 1, L - 1), tb1 = min(t0 + tb - 1, L - 1);
+        Rg.xp.load(tp >= 0 ? xb + (tp * D + c0) * R : pr.x);
+        Rg.bcp.load(tb1 >= 0 ? bcb + (tb1 * kDState + s0) * R : pr.bc);
+    }
 }
 
 // Converts one tile into LDS: dx = delta * x per (token, channel, rank), delta (or the decay
 // 2^(delta a2) with a scaled-identity A) per (token, channel), and the B and C tiles.
-template <typename E, int R, AForm AF>
-__device__ __forceinline__ void mimo_stage_tile(const MimoTileRegs<E, R> &Rg, float *dx_s, float *dl_s, float *bc_s,
-                                                int64_t t0, int64_t L, int tid, const float (&a2c)[mrows::Cfg<R>::kCPT]) {
-    using C = mrows::Cfg<R>;
+//
+// With the trapezoidal rule dx holds q = (lam delta) x, p_s the left-end weights p = ((1 - lam)
+// delta) x_{t-1}, and the B threads stage the previous token's B as the third tile (zero for
+// tokens at or past L and, without a caller's previous token, for the row's token 0).  A token
+// at or past L gets p = -0, so its left-end term (-0 times a zero B) leaves the state as it is.
+template <typename E, int R, AForm AF, bool kTrap = false>
+__device__ __forceinline__ void mimo_stage_tile(const MimoTileRegs<E, R, kTrap> &Rg, float *dx_s, float *dl_s,
+                                                float *bc_s, float *p_s, int64_t t0, int64_t L, int tid,
+                                                const float (&a2c)[mrows::Cfg<R, kTrap>::kCPT], bool prev_given) {
+    using C = mrows::Cfg<R, kTrap>;
     const int t = tid / C::kTPT, c0 = (tid % C::kTPT) * C::kCPT;
     const bool live = t0 + t < L;
-    float dx[C::kXV];
+    const bool has_prev = t0 + t > 0 || prev_given;
+    float dx[C::kXV], pv[C::kXV];
 #pragma unroll
     for (int ci = 0; ci < C::kCPT; ++ci) {
         const float dv = live ? Rg.dl.get(ci) : 0.0f;
+        if constexpr (kTrap) {
+            const float lv = live ? Rg.lam.get(ci) : 0.0f;
 #pragma unroll
-        for (int r = 0; r < R; ++r) dx[ci * R + r] = delta_x(dv, live ? Rg.x.get(ci * R + r) : -0.0f);
+            for (int r = 0; r < R; ++r) {
+                dx[ci * R + r] = trap_right(dv, lv, live ? Rg.x.get(ci * R + r) : -0.0f);
+                pv[ci * R + r] = live ? trap_left(dv, lv, has_prev ? Rg.xp.get(ci * R + r) : 0.0f) : -0.0f;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < R; ++r) dx[ci * R + r] = delta_x(dv, live ? Rg.x.get(ci * R + r) : -0.0f);
+        }
         dl_s[((t >> 2) * C::kCh + c0 + ci) * 4 + (t & 3)] = AF == AForm::ScaledIdentity ? decay(dv, a2c[ci]) : dv;
     }
     float *dst = dx_s + (t * C::kCh + c0) * R;
 #pragma unroll
     for (int i = 0; i < C::kXV / 4; ++i)
         reinterpret_cast<float4 *>(dst)[i] = make_float4(dx[4 * i], dx[4 * i + 1], dx[4 * i + 2], dx[4 * i + 3]);
-    if constexpr (C::kXV % 4 == 2)
-        *reinterpret_cast<float2 *>(dst + C::kXV - 2) = make_float2(dx[C::kXV - 2], dx[C::kXV - 1]);
+    if constexpr (kTrap) {
+        float *pd = p_s + (t * C::kCh + c0) * R;
+#pragma unroll
+        for (int i = 0; i < C::kXV / 4; ++i)
+            reinterpret_cast<float4 *>(pd)[i] = make_float4(pv[4 * i], pv[4 * i + 1], pv[4 * i + 2], pv[4 * i + 3]);
+    }
     const int tb = (tid & 127) / C::kTPB, s0 = (tid % C::kTPB) * C::kSPT;
     const bool live_bc = t0 + tb < L;
     float *tile = bc_s + (tid >= 128 ? C::kBcSize : 0);
 #pragma unroll
     for (int i = 0; i < C::kBV; ++i)   // i = (n - s0) * R + r
         tile[(s0 * R + i) * C::kBS + tb] = live_bc ? Rg.bc.get(i) : 0.0f;
+    if constexpr (kTrap) {
+        if (tid < 128) {   // whole waves: the B threads
+            const bool prev_live = live_bc && (t0 + tb > 0 || prev_given);
+            float *bp = bc_s + 2 * C::kBcSize;
+#pragma unroll
+            for (int i = 0; i < C::kBV; ++i) bp[(s0 * R + i) * C::kBS + tb] = prev_live ? Rg.bcp.get(i) : 0.0f;
+        }
+    }
 }
 
 // The outputs of one tile: this thread's token and channels, the two state halves' partial sums
 // added, rounded and stored as one contiguous run of kCPT * R values.
-template <typename E, int R>
+template <typename E, int R, bool kTrap = false>
 __device__ __forceinline__ void mimo_write_final(const float *y_tile, typename E::store_t *yb, int64_t t0, int64_t L,
                                                  int D, int tid) {
-    using C = mrows::Cfg<R>;
+    using C = mrows::Cfg<R, kTrap>;
     const int t = tid / C::kTPT, c0 = (tid % C::kTPT) * C::kCPT;
     if (t0 + t >= L) return;
     const float *p0 = y_tile + t * C::kYS + c0 * R;
@@ -171,47 +223,54 @@ __device__ __forceinline__ void mimo_write_final(const float *y_tile, typename E
     RowStore<E, C::kXV>::store(yb + ((t0 + t) * D + c0) * R, o);
 }
 
-// The scan lane's LDS operands for 4 tokens: dx (R per token) and delta of its channel.
+// The scan lane's LDS operands for 4 tokens: dx (R per token) and delta of its channel (and the
+// left-end weights p with the trapezoidal rule).
 template <int R> struct QuarterRegs {
-    float dx[4][R];
+    float dx[4][R], p[4][R];
     float4 dl;
 };
-template <int R>
-__device__ __forceinline__ void mimo_load_quarter(QuarterRegs<R> &q, const float *dx_s, const float *dl_s, int t4,
-                                                  int ch) {
-    using C = mrows::Cfg<R>;
+template <int R, int kCh>
+__device__ __forceinline__ void mimo_load_ranks(float (&dst)[4][R], const float *src, int t4, int ch) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const float *p = dx_s + ((t4 + k) * C::kCh + ch) * R;
+        const float *p = src + ((t4 + k) * kCh + ch) * R;
         if constexpr (R == 2) {
             const float2 v = *reinterpret_cast<const float2 *>(p);
-            q.dx[k][0] = v.x;
-            q.dx[k][1] = v.y;
+            dst[k][0] = v.x;
+            dst[k][1] = v.y;
         } else {
 #pragma unroll
             for (int i = 0; i < R / 4; ++i) {
                 const float4 v = reinterpret_cast<const float4 *>(p)[i];
-                q.dx[k][4 * i] = v.x; q.dx[k][4 * i + 1] = v.y; q.dx[k][4 * i + 2] = v.z; q.dx[k][4 * i + 3] = v.w;
+                dst[k][4 * i] = v.x; dst[k][4 * i + 1] = v.y; dst[k][4 * i + 2] = v.z; dst[k][4 * i + 3] = v.w;
             }
         }
     }
+}
+template <int R, bool kTrap>
+__device__ __forceinline__ void mimo_load_quarter(QuarterRegs<R> &q, const float *dx_s, const float *dl_s,
+                                                  const float *p_s, int t4, int ch) {
+    using C = mrows::Cfg<R, kTrap>;
+    mimo_load_ranks<R, C::kCh>(q.dx, dx_s, t4, ch);
+    if constexpr (kTrap) mimo_load_ranks<R, C::kCh>(q.p, p_s, t4, ch);
     q.dl = *reinterpret_cast<const float4 *>(dl_s + ((t4 >> 2) * C::kCh + ch) * 4);
 }
 
 // The lane's B and C registers for one 16-token group: (state n0 + i, rank r) at [i][r]; lane c
-// holds token tg + c.
+// holds token tg + c (and the previous token's B with the trapezoidal rule).
 template <int R> struct BcRegs {
-    float b[2][R], c[2][R];
+    float b[2][R], c[2][R], bp[2][R];
 };
-template <int R>
+template <int R, bool kTrap>
 __device__ __forceinline__ void mimo_load_bc(BcRegs<R> &g, const float *bc_s, int tg, int n0, int c) {
-    using C = mrows::Cfg<R>;
+    using C = mrows::Cfg<R, kTrap>;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             g.b[i][r] = bc_s[((n0 + i) * R + r) * C::kBS + tg + c];
             g.c[i][r] = bc_s[C::kBcSize + ((n0 + i) * R + r) * C::kBS + tg + c];
+            if constexpr (kTrap) g.bp[i][r] = bc_s[2 * C::kBcSize + ((n0 + i) * R + r) * C::kBS + tg + c];
         }
 }
 
@@ -231,9 +290,16 @@ template <int k> __device__ __forceinline__ float mul_bcast(float tile, float v)
 // partial outputs (C h summed over the two states) in P.  The rank-R input of state n is
 // dx_0 B[n][0] then + dx_r B[n][r] in increasing r, with B broadcast from lane TAU; this is
 // mimo_input(), bit for bit.
-template <int TAU, int R, AForm AF>
-__device__ __forceinline__ void mimo_token(const BcRegs<R> &g, const float (&dx)[R], float dv, float &h_0, float &h_1,
-                                           float a2_0, float a2_1, float (&P)[R]) {
+template <int TAU, int R, AForm AF, bool kTrap>
+__device__ __forceinline__ void mimo_token(const BcRegs<R> &g, const float (&dx)[R], const float (&pl)[R], float dv,
+                                           float &h_0, float &h_1, float a2_0, float a2_1, float (&P)[R]) {
+    if constexpr (kTrap) {   // the left end point: h + sum_r p_r B_prev[r], as mimo_left_in()
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            h_0 = fmac_bcast<TAU>(h_0, g.bp[0][r], pl[r]);
+            h_1 = fmac_bcast<TAU>(h_1, g.bp[1][r], pl[r]);
+        }
+    }
     float u0 = mul_bcast<TAU>(g.b[0][0], dx[0]);
     float u1 = mul_bcast<TAU>(g.b[1][0], dx[0]);
 #pragma unroll
@@ -257,15 +323,15 @@ __device__ __forceinline__ void mimo_token(const BcRegs<R> &g, const float (&dx)
 // Four tokens TQ .. TQ + 3 of a group, then their 4R partials summed over the wave's rows four
 // at a time (partial index i = token * R + rank; after reduce_rows4 row j holds i0 + {0,2,1,3}[j])
 // and written to this wave's half of the y exchange.
-template <int TQ, int R, AForm AF>
+template <int TQ, int R, AForm AF, bool kTrap>
 __device__ __forceinline__ void mimo_quarter(const BcRegs<R> &g, const QuarterRegs<R> &q, float &h_0, float &h_1,
                                              float a2_0, float a2_1, float *ys, int tq0, int rt, int ch) {
-    using C = mrows::Cfg<R>;
+    using C = mrows::Cfg<R, kTrap>;
     float P[4][R];
-    mimo_token<TQ + 0, R, AF>(g, q.dx[0], q.dl.x, h_0, h_1, a2_0, a2_1, P[0]);
-    mimo_token<TQ + 1, R, AF>(g, q.dx[1], q.dl.y, h_0, h_1, a2_0, a2_1, P[1]);
-    mimo_token<TQ + 2, R, AF>(g, q.dx[2], q.dl.z, h_0, h_1, a2_0, a2_1, P[2]);
-    mimo_token<TQ + 3, R, AF>(g, q.dx[3], q.dl.w, h_0, h_1, a2_0, a2_1, P[3]);
+    mimo_token<TQ + 0, R, AF, kTrap>(g, q.dx[0], q.p[0], q.dl.x, h_0, h_1, a2_0, a2_1, P[0]);
+    mimo_token<TQ + 1, R, AF, kTrap>(g, q.dx[1], q.p[1], q.dl.y, h_0, h_1, a2_0, a2_1, P[1]);
+    mimo_token<TQ + 2, R, AF, kTrap>(g, q.dx[2], q.p[2], q.dl.z, h_0, h_1, a2_0, a2_1, P[2]);
+    mimo_token<TQ + 3, R, AF, kTrap>(g, q.dx[3], q.p[3], q.dl.w, h_0, h_1, a2_0, a2_1, P[3]);
 #pragma unroll
     for (int m = 0; m < R; ++m) {
         const int i0 = 4 * m;
@@ -276,18 +342,19 @@ __device__ __forceinline__ void mimo_quarter(const BcRegs<R> &g, const QuarterRe
     }
 }
 
-template <typename E, AForm AF, int R>
+template <typename E, AForm AF, int R, bool kTrap = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mimo_rows_kernel(
     const typename E::store_t *__restrict__ x, const typename E::store_t *__restrict__ dl,
     const float *__restrict__ A, const typename E::store_t *__restrict__ B, const typename E::store_t *__restrict__ C,
     const float *__restrict__ h0, typename E::store_t *__restrict__ y, float *__restrict__ h_final, int64_t L, int D,
-    int blocks_per_row, int xcd_stride) {
-    using Cf = mrows::Cfg<R>;
+    int blocks_per_row, int xcd_stride, Trap tr) {
+    using Cf = mrows::Cfg<R, kTrap>;
     constexpr int kT = Cf::kT;
     __shared__ __attribute__((aligned(16))) float dx_s[2][Cf::kDxSize];
     __shared__ __attribute__((aligned(16))) float dl_s[2][Cf::kDlSize];
-    __shared__ __attribute__((aligned(16))) float bc_s[2][2 * Cf::kBcSize];
+    __shared__ __attribute__((aligned(16))) float bc_s[2][Cf::kBcTiles * Cf::kBcSize];
     __shared__ __attribute__((aligned(16))) float y_s[2][Cf::kYSize];
+    __shared__ __attribute__((aligned(16))) float p_s[2][kTrap ? Cf::kDxSize : 4];
 
     int wg = blockIdx.x;
     if (xcd_stride > 0) wg = (wg & 7) * xcd_stride + (wg >> 3);
@@ -307,26 +374,37 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int ci = 0; ci < Cf::kCPT; ++ci)
             a2c[ci] = AF == AForm::ScaledIdentity ? scaled_A(A[d0 + (tid % Cf::kTPT) * Cf::kCPT + ci]) : 0.0f;
-        MimoTileRegs<E, R> Rg[2];
-        mimo_load_tile<E, R>(Rg[0], xb, db, bcb, 0, L, D, tid);
-        mimo_stage_tile<E, R, AF>(Rg[0], dx_s[0], dl_s[0], bc_s[0], 0, L, tid, a2c);
-        mimo_load_tile<E, R>(Rg[1], xb, db, bcb, kT, L, D, tid);
-        mimo_load_tile<E, R>(Rg[0], xb, db, bcb, 2 * kT, L, D, tid);
+        // trapezoidal rule: lam, and the caller's previous token (or stand-ins staged as zero)
+        const bool prev_given = kTrap && tr.x_prev != nullptr;
+        MimoPrev<E> pr{nullptr, nullptr, nullptr, prev_given};
+        if constexpr (kTrap) {
+            const int c0 = (tid % Cf::kTPT) * Cf::kCPT, s0 = (tid % Cf::kTPB) * Cf::kSPT;
+            pr.lam = static_cast<const S *>(tr.lam) + (int64_t)b * L * D + d0;
+            pr.x = prev_given ? static_cast<const S *>(tr.x_prev) + ((int64_t)b * D + d0 + c0) * R : xb + c0 * R;
+            pr.bc = prev_given ? static_cast<const S *>(tr.B_prev) + ((int64_t)b * kDState + s0) * R : bcb + s0 * R;
+        }
+        MimoTileRegs<E, R, kTrap> Rg[2];
+        mimo_load_tile<E, R, kTrap>(Rg[0], xb, db, bcb, 0, L, D, tid, pr);
+        mimo_stage_tile<E, R, AF, kTrap>(Rg[0], dx_s[0], dl_s[0], bc_s[0], p_s[0], 0, L, tid, a2c, prev_given);
+        mimo_load_tile<E, R, kTrap>(Rg[1], xb, db, bcb, kT, L, D, tid, pr);
+        mimo_load_tile<E, R, kTrap>(Rg[0], xb, db, bcb, 2 * kT, L, D, tid, pr);
         __syncthreads();
         auto tile = [&](auto cur_c, int k) {
             constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
             if (k + 1 < ntiles) {
-                mimo_stage_tile<E, R, AF>(Rg[nxt], dx_s[nxt], dl_s[nxt], bc_s[nxt], (int64_t)(k + 1) * kT, L, tid, a2c);
-                if (k + 3 < ntiles) mimo_load_tile<E, R>(Rg[nxt], xb, db, bcb, (int64_t)(k + 3) * kT, L, D, tid);
+                mimo_stage_tile<E, R, AF, kTrap>(Rg[nxt], dx_s[nxt], dl_s[nxt], bc_s[nxt], p_s[nxt],
+                                                 (int64_t)(k + 1) * kT, L, tid, a2c, prev_given);
+                if (k + 3 < ntiles)
+                    mimo_load_tile<E, R, kTrap>(Rg[nxt], xb, db, bcb, (int64_t)(k + 3) * kT, L, D, tid, pr);
             }
-            if (k > 0) mimo_write_final<E, R>(y_s[nxt], yb, (int64_t)(k - 1) * kT, L, D, tid);
+            if (k > 0) mimo_write_final<E, R, kTrap>(y_s[nxt], yb, (int64_t)(k - 1) * kT, L, D, tid);
             __syncthreads();
         };
         for (int k = 0; k < ntiles; k += 2) {
             tile(IntConst<0>{}, k);
             if (k + 1 < ntiles) tile(IntConst<1>{}, k + 1);
         }
-        mimo_write_final<E, R>(y_s[(ntiles - 1) & 1], yb, (int64_t)(ntiles - 1) * kT, L, D, tid);
+        mimo_write_final<E, R, kTrap>(y_s[(ntiles - 1) & 1], yb, (int64_t)(ntiles - 1) * kT, L, D, tid);
         return;
     }
 
@@ -359,20 +437,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto tile = [&](auto cur_c, int k) {
         constexpr int cur = decltype(cur_c)::value;
         float *ys = y_s[cur] + sh * kT * Cf::kYS;
-        const float *dxc = dx_s[cur], *dlc = dl_s[cur], *bcc = bc_s[cur];
+        const float *dxc = dx_s[cur], *dlc = dl_s[cur], *bcc = bc_s[cur], *psc = p_s[cur];
         BcRegs<R> g;
         QuarterRegs<R> qa, qb;
 #pragma unroll
         for (int tg = 0; tg < kT; tg += 16) {
-            mimo_load_bc<R>(g, bcc, tg, n0, c);
-            mimo_load_quarter<R>(qa, dxc, dlc, tg, ch);
-            mimo_load_quarter<R>(qb, dxc, dlc, tg + 4, ch);
-            mimo_quarter<0, R, AF>(g, qa, h_0, h_1, a2_0, a2_1, ys, tg, rt, ch);
-            mimo_load_quarter<R>(qa, dxc, dlc, tg + 8, ch);
-            mimo_quarter<4, R, AF>(g, qb, h_0, h_1, a2_0, a2_1, ys, tg + 4, rt, ch);
-            mimo_load_quarter<R>(qb, dxc, dlc, tg + 12, ch);
-            mimo_quarter<8, R, AF>(g, qa, h_0, h_1, a2_0, a2_1, ys, tg + 8, rt, ch);
-            mimo_quarter<12, R, AF>(g, qb, h_0, h_1, a2_0, a2_1, ys, tg + 12, rt, ch);
+            mimo_load_bc<R, kTrap>(g, bcc, tg, n0, c);
+            mimo_load_quarter<R, kTrap>(qa, dxc, dlc, psc, tg, ch);
+            mimo_load_quarter<R, kTrap>(qb, dxc, dlc, psc, tg + 4, ch);
+            mimo_quarter<0, R, AF, kTrap>(g, qa, h_0, h_1, a2_0, a2_1, ys, tg, rt, ch);
+            mimo_load_quarter<R, kTrap>(qa, dxc, dlc, psc, tg + 8, ch);
+            mimo_quarter<4, R, AF, kTrap>(g, qb, h_0, h_1, a2_0, a2_1, ys, tg + 4, rt, ch);
+            mimo_load_quarter<R, kTrap>(qb, dxc, dlc, psc, tg + 12, ch);
+            mimo_quarter<8, R, AF, kTrap>(g, qa, h_0, h_1, a2_0, a2_1, ys, tg + 8, rt, ch);
+            mimo_quarter<12, R, AF, kTrap>(g, qb, h_0, h_1, a2_0, a2_1, ys, tg + 12, rt, ch);
         }
         __syncthreads();
         (void)k;
@@ -384,19 +462,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     *reinterpret_cast<float2 *>(h_final + ((int64_t)b * D + d) * kDState + n0) = make_float2(h_0, h_1);
 }
 
-// The row-mapped MIMO kernel needs whole 32-channel blocks.
-inline bool mimo_rows_kernel_applies(int64_t D, int64_t R) { return D % 32 == 0 && (R == 2 || R == 4 || R == 8); }
+// The row-mapped MIMO kernel needs whole 32-channel blocks (and, with the trapezoidal rule,
+// rank 2 or 4: rank 8 would not fit its LDS areas).
+inline bool mimo_rows_kernel_applies(int64_t D, int64_t R, bool trap = false) {
+    return D % 32 == 0 && (R == 2 || R == 4 || (R == 8 && !trap));
+}
 
-template <typename E, AForm AF, int R>
+template <typename E, AForm AF, int R, bool kTrap = false>
 void launch_prefill_mimo_rows(const typename E::store_t *x, const typename E::store_t *dl, const float *A,
                               const typename E::store_t *B, const typename E::store_t *C, const float *h0,
                               typename E::store_t *y, float *h_final, int64_t batch, int64_t L, int D,
-                              hipStream_t stream) {
-    const int blocks_per_row = D / mrows::Cfg<R>::kCh;
+                              hipStream_t stream, Trap tr = Trap{nullptr, nullptr, nullptr}) {
+    const int blocks_per_row = D / mrows::Cfg<R, kTrap>::kCh;
     const int64_t blocks = batch * blocks_per_row;
     const int xcd_stride = (blocks % 8 == 0) ? (int)(blocks / 8) : 0;
-    hipLaunchKernelGGL((prefill_mimo_rows_kernel<E, AF, R>), dim3((unsigned)blocks), dim3(mrows::Cfg<R>::kThreads), 0,
-                       stream, x, dl, A, B, C, h0, y, h_final, L, D, blocks_per_row, xcd_stride);
+    hipLaunchKernelGGL((prefill_mimo_rows_kernel<E, AF, R, kTrap>), dim3((unsigned)blocks),
+                       dim3(mrows::Cfg<R, kTrap>::kThreads), 0, stream, x, dl, A, B, C, h0, y, h_final, L, D,
+                       blocks_per_row, xcd_stride, tr);
 }
 
 }  // namespace jscan

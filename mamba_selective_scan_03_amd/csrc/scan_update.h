@@ -115,6 +115,16 @@ __device__ __forceinline__ float trap_left(float delta, float lam, float x_prev)
 }
 __device__ __forceinline__ float trap_left_in(float h, float p, float b_prev) { return __builtin_fmaf(p, b_prev, h); }
 
+// The left end point of a MIMO step: k = h + sum_r p_r B_prev[r], taken in onto h in increasing r
+// (one fused multiply-add per rank).  With R = 1 it is trap_left_in().
+template <int R>
+__device__ __forceinline__ float mimo_left_in(float h, const float (&p)[R], const float *b_prev) {
+    float k = h;
+#pragma unroll
+    for (int r = 0; r < R; ++r) k = __builtin_fmaf(p[r], b_prev[r], k);
+    return k;
+}
+
 // The extra inputs of a trapezoidal prefill, in the dtype of x: lam [tokens][D] like delta, and
 // the token before each row's first one, x_prev [rows][D] and B_prev [rows][16] (both null when
 // there is none: its term is then zero).

@@ -29,7 +29,8 @@ def test_header_symbols_are_exported():
             "jscan_last_hip_error", "jscan_version", "jscan_prefill_chunked",
             "jscan_prefill_chunked_workspace", "jscan_ssm_inputs", "jscan_prefill_fused", "jscan_prefill_scalar_a",
             "jscan_step_scalar_a", "jscan_prefill_complex", "jscan_step_complex", "jscan_prefill_trapezoid",
-            "jscan_step_trapezoid", "jscan_prefill_mimo", "jscan_step_mimo"} <= set(names)
+            "jscan_step_trapezoid", "jscan_prefill_mimo", "jscan_step_mimo", "jscan_prefill_mimo_trapezoid",
+            "jscan_step_mimo_trapezoid"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -39,7 +40,7 @@ def test_status_strings_and_version():
     for s in range(9):
         assert lib.jscan_status_string(s) and lib.jscan_status_string(s) != b"unknown status"
     assert lib.jscan_status_string(99) == b"unknown status"
-    assert lib.jscan_version() == 107
+    assert lib.jscan_version() == 108
     assert lib.jscan_last_hip_error() == 0
 
 
@@ -336,3 +337,33 @@ def mimo_step(h=P, x=P + 0x100000, d=P + 0x200000, A=P + 0x300000, B=P + 0x40000
 ])
 def test_step_mimo_validation(kw, code):
     assert mimo_step(**kw) == code
+
+
+def mimo_trap_prefill(x=P, d=P + 0x100000, lam=P + 0x700000, A=P + 0x200000, B=P + 0x300000, C=P + 0x400000, h0=None,
+                      xp=None, bp=None, y=P + 0x500000, h=P + 0x600000, batch=1, L=64, D=64, N=16, R=4, form=0,
+                      dtype=BF16):
+    return jscan.library().jscan_prefill_mimo_trapezoid(x, d, lam, A, B, C, h0, xp, bp, y, h, batch, L, D, N, R, form,
+                                                        dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(R=3), ESHAPE), (dict(form=4), EFORM), (dict(lam=None), ENULL), (dict(xp=P + 0x800000), ENULL),
+    (dict(bp=P + 0x900000), ENULL), (dict(lam=P + 0x700004), EALIGN), (dict(lam=P + 0x500000 + 64), EALIAS),
+    (dict(xp=P + 0x600000, bp=P + 0x900000), EALIAS),   # h_final overlaps x_prev
+])
+def test_prefill_mimo_trapezoid_validation(kw, code):
+    assert mimo_trap_prefill(**kw) == code
+
+
+def test_step_mimo_trapezoid_validation():
+    lib = jscan.library()
+    args = [P, P + 0x700000, P + 0x800000, P + 0x100000, P + 0x200000, P + 0x900000, P + 0x300000, P + 0x400000,
+            P + 0x500000, P + 0x600000, 2, 64, 16, 4, 256, 64, 64, 0, BF16, None]
+    assert lib.jscan_step_mimo_trapezoid(*args[:1], None, *args[2:]) == ENULL          # x_prev
+    assert lib.jscan_step_mimo_trapezoid(*args[:5], None, *args[6:]) == ENULL          # lam_t
+    bad = list(args)
+    bad[9] = P + 0x700000                                                               # y_t on x_prev
+    assert lib.jscan_step_mimo_trapezoid(*bad) == EALIAS
+    bad = list(args)
+    bad[17] = 3
+    assert lib.jscan_step_mimo_trapezoid(*bad) == EFORM
