@@ -17,9 +17,9 @@
 //     instruction is issued.
 //   * delta_t[d] and delta_t[d] * x_t[d] are per lane (per channel).  The workgroup converts
 //     each tile once into fp32 pairs in LDS, and every row reads them as a broadcast.  With a
-//     scaled-identity A (AForm::ScaledIdentity: one a[d] for all states of a channel) the pair carries the
-//     channel's decay 2^(delta * a2[d]) in place of delta, computed once per (token, channel)
-//     while staging, and the scan waves run no exponential at all.
+//     scaled-identity A (AForm::ScaledIdentity: one a[d] for all states of a channel) the pair
+//     carries the channel's decay 2^(delta * a2[d]) in place of delta, computed once per
+//     (token, channel) while staging, and the scan waves run no exponential at all.
 //   * y_t[d] = sum over 16 states = 2 states in-lane, 4 rows in-wave (two permlane swap
 //     stages), then 2 waves through LDS.  The last stage is fused with the bf16 conversion
 //     and a coalesced row store.
@@ -31,6 +31,12 @@
 // HBM requests and the previous tile's y stores are spread into the scan of the first group.
 // A ragged last tile is padded with identity tokens (delta = 0, x = -0, B = C = 0): they
 // leave every state bit-identical (decay 2^0 = 1, input term -0) and their y is not stored.
+//
+// Modes (template parameters): a segment-summary pass for the time-parallel prefill
+// (kSummary), delta computed on the load path from the low-rank projection (kFused), the form
+// of A (AF: diagonal, scaled identity, complex pairs) and the exponential-trapezoidal rule
+// (kTrap: the helper waves also stage the left-end weights and the previous token's B, and the
+// scan lane takes the left end point in first, one more DPP-fused FMA per state element).
 #pragma once
 
 #include "mfma_common.h"

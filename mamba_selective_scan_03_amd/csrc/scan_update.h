@@ -1,8 +1,8 @@
 // scan_update.h - the one definition of how a state element advances by one token.
 //
 // Every kernel of the library (prefill, resume, decode step) advances state elements only
-// through `advance()` below, so they all compute bit-identical fp32 states for the same
-// tokens.  That is what lets a prefill's final state equal, bit for bit, the state after
+// through the functions below (`advance()` for the diagonal A), so they all compute
+// bit-identical fp32 states for the same tokens.  That is what lets a prefill's final state equal, bit for bit, the state after
 // the same tokens fed one at a time through the decode step.
 //
 // With a scaled-identity A (one value a[d] for all 16 states of a channel, the Mamba-2 form)
@@ -10,7 +10,10 @@
 // evaluate it once per (token, channel) with the same `decay()` and hand it to
 // `advance_decayed()`, which is the second half of `advance()`: their states are therefore
 // bit-identical to the general kernels' run on A[d][n] = a[d].  A complex-valued state (the
-// Mamba-3 form) advances through `advance_complex()`, the one definition of that update.
+// Mamba-3 form) advances through `advance_complex()`, the one definition of that update.  The
+// exponential-trapezoidal rule takes the previous token's input in first (`trap_left_in()`,
+// `mimo_left_in()`), and a MIMO scan forms its rank-R input with `mimo_input()` and advances
+// through `advance_input()` / `advance_complex_input()`: each form has one definition here.
 //
 // The recurrence is the S6 equation of the Jamba notes page ("Jamba: A Hybrid
 // Transformer-Mamba Language Model", section "Mamba layer"):
