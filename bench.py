@@ -81,13 +81,20 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments and blank space removed: what the compiler sees."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(kind: str) -> str:
-    """Hash of the sources of one kernel (a key of KERNEL_SOURCES); a profile summary records it,
-    and its counters count only while the sources are unchanged."""
+    """Hash of the code of one kernel's sources (a key of KERNEL_SOURCES, comments left out); a
+    profile summary records it, and its counters count only while that code is unchanged."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, "mamba_selective_scan_03_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "mamba_selective_scan_03_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
