@@ -170,9 +170,15 @@ def cpu_baseline(wl, inp, channels: int, scalar_a=None, complex_a=False, lam=Non
         fn(*args, nthreads=threads)
     dt = time.perf_counter() - t0
     elems = wl.batch * wl.L * channels
+    cpu = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next(line.split(":", 1)[1].strip() for line in fh if line.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": elems / dt, "unit": "elems/s", "cores": threads, "kind": "oracle",
             "sample": f"{wl.name}: batch {wl.batch}, all {wl.L} tokens, first {channels} of {wl.D} channels, "
-                      f"N {wl.N}, fp64 ({dt:.1f} s)"}
+                      f"N {wl.N}, fp64 ({dt:.1f} s on {cpu})"}
 
 
 def main():
@@ -422,6 +428,24 @@ def main():
     ms_step = ms_total / args.steps
     log(f"{args.steps} steps: {ms_total:.3f} ms by HIP events, {wall * 1e3:.3f} ms wall")
 
+    # Per-step times, taken after the timed region: median and minimum.  A workload whose bytes
+    # fit in the 256 MB last-level cache is timed cold, with 512 MiB of scratch written between
+    # steps (outside the events).
+    cold = algorithmic_bytes(wl, args.trapezoid, args.mimo) < (1 << 30)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if cold else None
+    marks = []
+    for _ in range(min(args.steps, 50)):
+        if scratch is not None:
+            scratch.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        one_step()
+        b.record(stream)
+        marks.append((a, b))
+    torch.cuda.synchronize()
+    per_step = sorted(a.elapsed_time(b) for a, b in marks)
+    del scratch
+
     elems = wl.elems
     value = elems / (ms_step * 1e-3)
     alg_bytes = algorithmic_bytes(wl, args.trapezoid, args.mimo)
@@ -504,6 +528,9 @@ def main():
                    "mimo_rank": args.mimo or 1,
                    "path": ("producer+fused-scan" if args.fused else "producer+scan") if args.producer
                    else ("time-parallel" if args.chunked else "sequential")},
+        "step_ms_median": round(per_step[len(per_step) // 2], 4),
+        "step_ms_min": round(per_step[0], 4),
+        "step_timing": "cold: 512 MiB written between steps" if cold else "back to back",
         "hbm_GBps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": alg_bytes,
