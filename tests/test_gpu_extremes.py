@@ -9,7 +9,9 @@ row-mapped kernel (D a multiple of 32, ragged last tile) and the lane kernel (D 
 * large magnitudes: x, B and C of order 1e3, 1e2 and 1e2;
 * mixed scales: delta log-uniform over five decades, token by token.
 
-In every regime the prefill's final state equals the decode step chain bit for bit."""
+In every regime the prefill's final state equals the decode step chain bit for bit.  The
+exponential-trapezoidal rule and the rank-4 MIMO scan (with and without it) run the same
+regimes on the row-mapped kernels."""
 import pytest
 import torch
 
@@ -96,3 +98,60 @@ def test_regime_state_equals_step_chain(form, regime):
         run_step(form, hs, d, t)
     torch.cuda.synchronize()
     assert torch.equal(bits(hs), bits(h)), f"{regime} {form}: step chain state differs from the prefill's"
+
+
+def with_lam(host, seed):
+    """lam in (0, 1), rows like delta."""
+    g = torch.Generator().manual_seed(seed)
+    return torch.rand(host["delta"].shape, generator=g).to(host["delta"].dtype)
+
+
+def to_mimo(host, R, seed):
+    """Rank-R x [b, L, D, R], B and C [b, L, 16, R] at the regime's scales (rank 0 is the
+    single-input draw)."""
+    g = torch.Generator().manual_seed(seed)
+    out = dict(host)
+    for k in ("x", "B", "C"):
+        v = host[k].double()
+        scale = float(v.abs().max()) / 4.0
+        extra = torch.randn(*v.shape, R - 1, generator=g, dtype=torch.float64) * scale
+        out[k] = torch.cat([v[..., None], extra], -1).to(host[k].dtype).contiguous()
+    return out
+
+
+@pytest.mark.parametrize("form", ["diagonal", "complex"])
+@pytest.mark.parametrize("regime", REGIMES)
+def test_regime_trapezoid_matches_oracle(form, regime):
+    L = 2800 if regime == "long_memory" else 700
+    host = draw(regime, form, 1, L, 256, "bf16", seed=300 + REGIMES.index(regime))
+    host["lam"] = with_lam(host, 11)
+    d = {k: v.cuda() for k, v in host.items()}
+    y, h = jscan.prefill_trapezoid(d["x"], d["delta"], d["lam"], d["A"], d["B"], d["C"], form=form)
+    torch.cuda.synchronize()
+    y_ref, h_ref = oracle.prefill_trapezoid(host["x"], host["delta"], host["lam"], host["A"], host["B"], host["C"],
+                                            form=form)
+    what = f"trapezoid {regime} {form}"
+    assert_parity(f64(y), y_ref, torch.bfloat16, f"{what} y")
+    assert_parity(f64(h), h_ref, torch.bfloat16, f"{what} h_final")
+
+
+@pytest.mark.parametrize("form", ["diagonal", "complex"])
+@pytest.mark.parametrize("regime", REGIMES)
+@pytest.mark.parametrize("trap", [False, True])
+def test_regime_mimo_matches_oracle(form, regime, trap):
+    L = 1400 if regime == "long_memory" else 400
+    host = to_mimo(draw(regime, form, 1, L, 256, "bf16", seed=400 + REGIMES.index(regime)), 4, 12)
+    if trap:
+        host["lam"] = with_lam(host, 13)
+    d = {k: v.cuda() for k, v in host.items()}
+    if trap:
+        y, h = jscan.prefill_mimo_trapezoid(d["x"], d["delta"], d["lam"], d["A"], d["B"], d["C"], form=form)
+        y_ref, h_ref = oracle.prefill_mimo_trapezoid(host["x"], host["delta"], host["lam"], host["A"], host["B"],
+                                                     host["C"], form=form)
+    else:
+        y, h = jscan.prefill_mimo(d["x"], d["delta"], d["A"], d["B"], d["C"], form=form)
+        y_ref, h_ref = oracle.prefill_mimo(host["x"], host["delta"], host["A"], host["B"], host["C"], form=form)
+    torch.cuda.synchronize()
+    what = f"mimo R=4 trap={trap} {regime} {form}"
+    assert_parity(f64(y), y_ref, torch.bfloat16, f"{what} y")
+    assert_parity(f64(h), h_ref, torch.bfloat16, f"{what} h_final")
