@@ -45,15 +45,21 @@ template <int R, bool kTrap = false> struct Cfg {
     static constexpr int kTPB = 128 / kT;
     static constexpr int kSPT = kDState / kTPB;
     static constexpr int kBV = kSPT * R;
-    // LDS (floats): dx [kT][kCh][R]; delta [kT/4][kCh][4]; B and C [16][R][kBS];
-    // y partials [2 halves][kT][kYS]
-    static constexpr int kDxSize = kT * kCh * R;
+    // LDS (floats): dx [kT][kXS] (channel-major rows of kCh * R); delta [kT/4][kCh][4]; B and C
+    // [16][R][kBS]; y partials [2 halves][kT][kYS].  At R = 4 and 8 without the trapezoidal rule
+    // the dx and y token rows are padded by 4 floats, so that the helper threads' 16-byte
+    // accesses (8 or 16 threads per token, 16 floats each) spread over all 32 LDS banks instead
+    // of a quarter of them: 2-3% faster there.  The same padding measured 1-2% slower at R = 2 and
+    // with the trapezoidal rule, which keep unpadded rows.
+    static constexpr int kPad = (R == 2 || kTrap) ? 0 : 4;
+    static constexpr int kXS = kCh * R + kPad;
+    static constexpr int kDxSize = kT * kXS;
     static constexpr int kDlSize = kT * kCh;
     // B/C rows of 16 tokens read by the 4 rows of a wave (states 2 apart) land 16 banks apart
     static constexpr int kBS = R == 2 ? kT + 4 : R == 4 ? kT + 2 : kT + 1;
     static constexpr int kBcSize = kDState * R * kBS;
     static constexpr int kBcTiles = kTrap ? 3 : 2;   // B, C (and the previous token's B)
-    static constexpr int kYS = kCh * R + (R == 2 ? 32 : 0);
+    static constexpr int kYS = kCh * R + (R == 2 ? 32 : kPad);
     static constexpr int kYSize = 2 * kT * kYS;
 };
 }  // namespace mrows
@@ -172,12 +178,12 @@ __device__ __forceinline__ void mimo_stage_tile(const MimoTileRegs<E, R, kTrap> 
         }
         dl_s[((t >> 2) * C::kCh + c0 + ci) * 4 + (t & 3)] = AF == AForm::ScaledIdentity ? decay(dv, a2c[ci]) : dv;
     }
-    float *dst = dx_s + (t * C::kCh + c0) * R;
+    float *dst = dx_s + t * C::kXS + c0 * R;
 #pragma unroll
     for (int i = 0; i < C::kXV / 4; ++i)
         reinterpret_cast<float4 *>(dst)[i] = make_float4(dx[4 * i], dx[4 * i + 1], dx[4 * i + 2], dx[4 * i + 3]);
     if constexpr (kTrap) {
-        float *pd = p_s + (t * C::kCh + c0) * R;
+        float *pd = p_s + t * C::kXS + c0 * R;
 #pragma unroll
         for (int i = 0; i < C::kXV / 4; ++i)
             reinterpret_cast<float4 *>(pd)[i] = make_float4(pv[4 * i], pv[4 * i + 1], pv[4 * i + 2], pv[4 * i + 3]);
@@ -229,11 +235,11 @@ template <int R> struct QuarterRegs {
     float dx[4][R], p[4][R];
     float4 dl;
 };
-template <int R, int kCh>
+template <int R, int kXS>
 __device__ __forceinline__ void mimo_load_ranks(float (&dst)[4][R], const float *src, int t4, int ch) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const float *p = src + ((t4 + k) * kCh + ch) * R;
+        const float *p = src + (t4 + k) * kXS + ch * R;
         if constexpr (R == 2) {
             const float2 v = *reinterpret_cast<const float2 *>(p);
             dst[k][0] = v.x;
@@ -251,8 +257,8 @@ template <int R, bool kTrap>
 __device__ __forceinline__ void mimo_load_quarter(QuarterRegs<R> &q, const float *dx_s, const float *dl_s,
                                                   const float *p_s, int t4, int ch) {
     using C = mrows::Cfg<R, kTrap>;
-    mimo_load_ranks<R, C::kCh>(q.dx, dx_s, t4, ch);
-    if constexpr (kTrap) mimo_load_ranks<R, C::kCh>(q.p, p_s, t4, ch);
+    mimo_load_ranks<R, C::kXS>(q.dx, dx_s, t4, ch);
+    if constexpr (kTrap) mimo_load_ranks<R, C::kXS>(q.p, p_s, t4, ch);
     q.dl = *reinterpret_cast<const float4 *>(dl_s + ((t4 >> 2) * C::kCh + ch) * 4);
 }
 

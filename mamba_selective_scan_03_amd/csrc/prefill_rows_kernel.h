@@ -52,8 +52,8 @@ constexpr int kHalf = 256;      // threads per role
 // LDS row lengths, padded so that the accesses of a wave spread over all banks:
 constexpr int kDxStride = (kCh + 1) * 4;   // [token pair][channel][4]: +1 float4 per pair row
 constexpr int kBcStride = kT + 8;          // [state][token] B and C tiles
-constexpr int kYStride = kCh + 16;         // [token][channel] y exchange: the 4 rows of a wave
-                                           // (token offsets 0, 2, 1, 3) land 16 banks apart
+constexpr int kYStride = kCh + 16;         // [token][channel] y exchange (kCh + 8, which puts
+                                           // the 4 rows of a wave in distinct banks, measured slower)
 // LDS (floats): delta*x/delta pairs [kT/2][kDxStride], B and C [16][kBcStride], y [2][kT][kYStride]
 constexpr int kDxSize = kT / 2 * kDxStride;
 constexpr int kBcSize = kDState * kBcStride;
