@@ -280,17 +280,123 @@ __device__ __forceinline__ void mimo_load_bc(BcRegs<R> &g, const float *bc_s, in
         }
 }
 
-// v_mul_f32 with the DPP row broadcast of lane k of `tile` as its first operand.
-template <int k> __device__ __forceinline__ float mul_bcast(float tile, float v) {
-    float out;
-    if constexpr (k == 0)
-        asm("s_nop 1\n\tv_mul_f32_dpp %0, %1, %2 row_newbcast:0 row_mask:0xf bank_mask:0xf bound_ctrl:1"
-            : "=v"(out) : "v"(tile), "v"(v));
-    else
-        asm("v_mul_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
-            : "=v"(out) : "v"(tile), "v"(v), "i"(k));
-    return out;
+// The token's DPP-fused FMAs as few asm statements.  The compiler cannot see into an asm
+// statement, so it treats each one's results as possibly late (a transcendental's) and waits a
+// cycle before the next instruction that reads them; one statement per group of independent
+// chains (the lane's two states, or the R ranks) keeps those waits to one per statement.  The
+// plain products before them are the compiler's own v_mul_f32_dpp (row_bcast() folded into the
+// multiply).  Every B, C and B_prev operand broadcast here is only ever written by LDS reads;
+// the leading s_nop on token 0 is the same margin as in fmac_bcast().
+#define JSCAN_RB " row_newbcast:%[k] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+#define JSCAN_F(d, t, v) "v_fmac_f32_dpp %[" #d "], %[" #t "], %[" #v "]" JSCAN_RB
+#define JSCAN_ASM_K(TAU)                                      \
+    if constexpr ((TAU) == 0) asm("s_nop 1\n\t" BODY : OUTS : INS); \
+    else asm(BODY : OUTS : INS);
+
+// u_s += (B_s[r] of token TAU) * dx[r] for r = 1 .. R-1, for both states s, r increasing.
+template <int TAU, int R>
+__device__ __forceinline__ void mimo_input_tail(const BcRegs<R> &g, const float (&dx)[R], float &u0, float &u1) {
+    if constexpr (R == 2) {
+#define BODY JSCAN_F(u0, b01, x1) JSCAN_F(u1, b11, x1)
+#define OUTS [u0] "+v"(u0), [u1] "+v"(u1)
+#define INS [b01] "v"(g.b[0][1]), [b11] "v"(g.b[1][1]), [x1] "v"(dx[1]), [k] "i"(TAU)
+        JSCAN_ASM_K(TAU)
+#undef BODY
+#undef OUTS
+#undef INS
+    } else if constexpr (R == 4) {
+#define BODY JSCAN_F(u0, b01, x1) JSCAN_F(u1, b11, x1) JSCAN_F(u0, b02, x2) JSCAN_F(u1, b12, x2) \
+             JSCAN_F(u0, b03, x3) JSCAN_F(u1, b13, x3)
+#define OUTS [u0] "+v"(u0), [u1] "+v"(u1)
+#define INS [b01] "v"(g.b[0][1]), [b11] "v"(g.b[1][1]), [x1] "v"(dx[1]), [b02] "v"(g.b[0][2]), \
+            [b12] "v"(g.b[1][2]), [x2] "v"(dx[2]), [b03] "v"(g.b[0][3]), [b13] "v"(g.b[1][3]), [x3] "v"(dx[3]), [k] "i"(TAU)
+        JSCAN_ASM_K(TAU)
+#undef BODY
+#undef OUTS
+#undef INS
+    } else {
+        static_assert(R == 8, "rank 2, 4 or 8");
+#define BODY JSCAN_F(u0, b01, x1) JSCAN_F(u1, b11, x1) JSCAN_F(u0, b02, x2) JSCAN_F(u1, b12, x2) \
+             JSCAN_F(u0, b03, x3) JSCAN_F(u1, b13, x3) JSCAN_F(u0, b04, x4) JSCAN_F(u1, b14, x4) \
+             JSCAN_F(u0, b05, x5) JSCAN_F(u1, b15, x5) JSCAN_F(u0, b06, x6) JSCAN_F(u1, b16, x6) \
+             JSCAN_F(u0, b07, x7) JSCAN_F(u1, b17, x7)
+#define OUTS [u0] "+v"(u0), [u1] "+v"(u1)
+#define INS [b01] "v"(g.b[0][1]), [b11] "v"(g.b[1][1]), [x1] "v"(dx[1]), [b02] "v"(g.b[0][2]), \
+            [b12] "v"(g.b[1][2]), [x2] "v"(dx[2]), [b03] "v"(g.b[0][3]), [b13] "v"(g.b[1][3]), [x3] "v"(dx[3]), \
+            [b04] "v"(g.b[0][4]), [b14] "v"(g.b[1][4]), [x4] "v"(dx[4]), [b05] "v"(g.b[0][5]), \
+            [b15] "v"(g.b[1][5]), [x5] "v"(dx[5]), [b06] "v"(g.b[0][6]), [b16] "v"(g.b[1][6]), [x6] "v"(dx[6]), \
+            [b07] "v"(g.b[0][7]), [b17] "v"(g.b[1][7]), [x7] "v"(dx[7]), [k] "i"(TAU)
+        JSCAN_ASM_K(TAU)
+#undef BODY
+#undef OUTS
+#undef INS
+    }
 }
+
+// P[r] += (C_1[r] of token TAU) * h_1 for every rank r (P[r] already holds C_0[r] * h_0).
+template <int TAU, int R>
+__device__ __forceinline__ void mimo_output_tail(const BcRegs<R> &g, float h_1, float (&P)[R]) {
+    if constexpr (R == 2) {
+#define BODY JSCAN_F(p0, c0, h) JSCAN_F(p1, c1, h)
+#define OUTS [p0] "+v"(P[0]), [p1] "+v"(P[1])
+#define INS [c0] "v"(g.c[1][0]), [c1] "v"(g.c[1][1]), [h] "v"(h_1), [k] "i"(TAU)
+        JSCAN_ASM_K(TAU)
+#undef BODY
+#undef OUTS
+#undef INS
+    } else if constexpr (R == 4) {
+#define BODY JSCAN_F(p0, c0, h) JSCAN_F(p1, c1, h) JSCAN_F(p2, c2, h) JSCAN_F(p3, c3, h)
+#define OUTS [p0] "+v"(P[0]), [p1] "+v"(P[1]), [p2] "+v"(P[2]), [p3] "+v"(P[3])
+#define INS [c0] "v"(g.c[1][0]), [c1] "v"(g.c[1][1]), [c2] "v"(g.c[1][2]), [c3] "v"(g.c[1][3]), [h] "v"(h_1), \
+            [k] "i"(TAU)
+        JSCAN_ASM_K(TAU)
+#undef BODY
+#undef OUTS
+#undef INS
+    } else {
+#define BODY JSCAN_F(p0, c0, h) JSCAN_F(p1, c1, h) JSCAN_F(p2, c2, h) JSCAN_F(p3, c3, h) \
+             JSCAN_F(p4, c4, h) JSCAN_F(p5, c5, h) JSCAN_F(p6, c6, h) JSCAN_F(p7, c7, h)
+#define OUTS [p0] "+v"(P[0]), [p1] "+v"(P[1]), [p2] "+v"(P[2]), [p3] "+v"(P[3]), [p4] "+v"(P[4]), \
+             [p5] "+v"(P[5]), [p6] "+v"(P[6]), [p7] "+v"(P[7])
+#define INS [c0] "v"(g.c[1][0]), [c1] "v"(g.c[1][1]), [c2] "v"(g.c[1][2]), [c3] "v"(g.c[1][3]), \
+            [c4] "v"(g.c[1][4]), [c5] "v"(g.c[1][5]), [c6] "v"(g.c[1][6]), [c7] "v"(g.c[1][7]), [h] "v"(h_1), [k] "i"(TAU)
+        JSCAN_ASM_K(TAU)
+#undef BODY
+#undef OUTS
+#undef INS
+    }
+}
+
+// The trapezoidal left end point: h_s += (B_prev_s[r] of token TAU) * p[r], r increasing, as
+// mimo_left_in().
+template <int TAU, int R>
+__device__ __forceinline__ void mimo_left_tail(const BcRegs<R> &g, const float (&pl)[R], float &h_0, float &h_1) {
+    if constexpr (R == 2) {
+#define BODY JSCAN_F(h0, q00, p0) JSCAN_F(h1, q10, p0) JSCAN_F(h0, q01, p1) JSCAN_F(h1, q11, p1)
+#define OUTS [h0] "+v"(h_0), [h1] "+v"(h_1)
+#define INS [q00] "v"(g.bp[0][0]), [q10] "v"(g.bp[1][0]), [p0] "v"(pl[0]), [q01] "v"(g.bp[0][1]), \
+            [q11] "v"(g.bp[1][1]), [p1] "v"(pl[1]), [k] "i"(TAU)
+        JSCAN_ASM_K(TAU)
+#undef BODY
+#undef OUTS
+#undef INS
+    } else {
+        static_assert(R == 4, "the trapezoidal rule runs rank 2 or 4 here");
+#define BODY JSCAN_F(h0, q00, p0) JSCAN_F(h1, q10, p0) JSCAN_F(h0, q01, p1) JSCAN_F(h1, q11, p1) \
+             JSCAN_F(h0, q02, p2) JSCAN_F(h1, q12, p2) JSCAN_F(h0, q03, p3) JSCAN_F(h1, q13, p3)
+#define OUTS [h0] "+v"(h_0), [h1] "+v"(h_1)
+#define INS [q00] "v"(g.bp[0][0]), [q10] "v"(g.bp[1][0]), [p0] "v"(pl[0]), [q01] "v"(g.bp[0][1]), \
+            [q11] "v"(g.bp[1][1]), [p1] "v"(pl[1]), [q02] "v"(g.bp[0][2]), [q12] "v"(g.bp[1][2]), [p2] "v"(pl[2]), \
+            [q03] "v"(g.bp[0][3]), [q13] "v"(g.bp[1][3]), [p3] "v"(pl[3]), [k] "i"(TAU)
+        JSCAN_ASM_K(TAU)
+#undef BODY
+#undef OUTS
+#undef INS
+    }
+}
+#undef JSCAN_ASM_K
+#undef JSCAN_F
+#undef JSCAN_RB
 
 // One token (TAU within its 16-token group): advance the lane's two states and leave the R
 // partial outputs (C h summed over the two states) in P.  The rank-R input of state n is
@@ -299,20 +405,10 @@ template <int k> __device__ __forceinline__ float mul_bcast(float tile, float v)
 template <int TAU, int R, AForm AF, bool kTrap>
 __device__ __forceinline__ void mimo_token(const BcRegs<R> &g, const float (&dx)[R], const float (&pl)[R], float dv,
                                            float &h_0, float &h_1, float a2_0, float a2_1, float (&P)[R]) {
-    if constexpr (kTrap) {   // the left end point: h + sum_r p_r B_prev[r], as mimo_left_in()
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            h_0 = fmac_bcast<TAU>(h_0, g.bp[0][r], pl[r]);
-            h_1 = fmac_bcast<TAU>(h_1, g.bp[1][r], pl[r]);
-        }
-    }
-    float u0 = mul_bcast<TAU>(g.b[0][0], dx[0]);
-    float u1 = mul_bcast<TAU>(g.b[1][0], dx[0]);
-#pragma unroll
-    for (int r = 1; r < R; ++r) {
-        u0 = fmac_bcast<TAU>(u0, g.b[0][r], dx[r]);
-        u1 = fmac_bcast<TAU>(u1, g.b[1][r], dx[r]);
-    }
+    if constexpr (kTrap) mimo_left_tail<TAU, R>(g, pl, h_0, h_1);   // h + sum_r p_r B_prev[r]
+    float u0 = row_bcast<TAU>(g.b[0][0]) * dx[0];
+    float u1 = row_bcast<TAU>(g.b[1][0]) * dx[0];
+    mimo_input_tail<TAU, R>(g, dx, u0, u1);
     if constexpr (AF == AForm::ComplexPairs) {
         advance_complex_input(h_0, h_1, dv, ComplexA{a2_0, a2_1}, u0, u1);
     } else if constexpr (AF == AForm::ScaledIdentity) {
@@ -323,7 +419,8 @@ __device__ __forceinline__ void mimo_token(const BcRegs<R> &g, const float (&dx)
         h_1 = advance_input(h_1, decay(dv, a2_1), u1);
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) P[r] = fmac_bcast<TAU>(mul_bcast<TAU>(g.c[0][r], h_0), g.c[1][r], h_1);
+    for (int r = 0; r < R; ++r) P[r] = row_bcast<TAU>(g.c[0][r]) * h_0;
+    mimo_output_tail<TAU, R>(g, h_1, P);
 }
 
 // Four tokens TQ .. TQ + 3 of a group, then their 4R partials summed over the wave's rows four
