@@ -139,6 +139,19 @@ template <int k> __device__ __forceinline__ float fmac_bcast(float acc, float c_
     return acc;
 }
 
+// fmac_bcast() for the lane's two states in one asm statement, so that the compiler, which
+// cannot see into it, waits once for both results rather than once for each.
+template <int k> __device__ __forceinline__ void fmac2_bcast(float &a0, float &a1, float t0, float t1, float v) {
+    if constexpr (k == 0)
+        asm("s_nop 1\n\tv_fmac_f32_dpp %0, %2, %4 row_newbcast:0 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %1, %3, %4 row_newbcast:0 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+            : "+v"(a0), "+v"(a1) : "v"(t0), "v"(t1), "v"(v));
+    else
+        asm("v_fmac_f32_dpp %0, %2, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %1, %3, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+            : "+v"(a0), "+v"(a1) : "v"(t0), "v"(t1), "v"(v), "i"(k));
+}
+
 // Sum of four tokens' partials over the 4 rows: returns a register whose row r holds the
 // row-sum of token kRowToken[r] = {0, 2, 1, 3}[r], added as (row0 + row2) + (row1 + row3).
 __device__ __forceinline__ float reduce_rows4(float p0, float p1, float p2, float p3) {
@@ -147,6 +160,19 @@ __device__ __forceinline__ float reduce_rows4(float p0, float p1, float p2, floa
     float u01 = p0 + p1, u23 = p2 + p3;
     swap16(u01, u23);
     return u01 + u23;
+}
+// Two reduce_rows4() interleaved, so that no swap reads an add of the instruction before it.
+__device__ __forceinline__ void reduce_rows4x2(const float (&P)[8], float &ra, float &rb) {
+    float a0 = P[0], a1 = P[1], a2 = P[2], a3 = P[3], b0 = P[4], b1 = P[5], b2 = P[6], b3 = P[7];
+    swap32(a0, a1);
+    swap32(b0, b1);
+    swap32(a2, a3);
+    swap32(b2, b3);
+    float a01 = a0 + a1, b01 = b0 + b1, a23 = a2 + a3, b23 = b2 + b3;
+    swap16(a01, a23);
+    swap16(b01, b23);
+    ra = a01 + a23;
+    rb = b01 + b23;
 }
 
 // Requests one tile's raw inputs.  The loads are unconditional per lane: a load inside a
@@ -371,8 +397,7 @@ __device__ __forceinline__ float token_step(const GroupRegs &g, float &h_0, floa
                                             float &dsum) {
     if constexpr (kTrap) {   // the left end point: h + p * B_prev, the DPP broadcast folded in
         const float pl = component<TAU & 3>(g.pv[TAU >> 2]);
-        h_0 = fmac_bcast<TAU>(h_0, g.bp0, pl);
-        h_1 = fmac_bcast<TAU>(h_1, g.bp1, pl);
+        fmac2_bcast<TAU>(h_0, h_1, g.bp0, g.bp1, pl);
     }
     const float4 v = g.v[TAU >> 1];
     const float dxv = (TAU & 1) ? v.z : v.x;
@@ -413,8 +438,10 @@ __device__ __forceinline__ void scan_half(const GroupRegs &g, float &h_0, float 
         asm volatile("" : "+v"(h_0), "+v"(h_1), "+v"(dsum));
     } else {
         // rows -> one register per 4 tokens; row r holds token 4j + {0,2,1,3}[r]
-        ys[(8 * H + rt) * rows::kYStride + ch] = reduce_rows4(P[0], P[1], P[2], P[3]);
-        ys[(8 * H + 4 + rt) * rows::kYStride + ch] = reduce_rows4(P[4], P[5], P[6], P[7]);
+        float ra, rb;
+        reduce_rows4x2(P, ra, rb);
+        ys[(8 * H + rt) * rows::kYStride + ch] = ra;
+        ys[(8 * H + 4 + rt) * rows::kYStride + ch] = rb;
     }
 }
 // The same half split in two: the tokens' partials (computed in one scheduling region) and their
@@ -432,8 +459,10 @@ __device__ __forceinline__ void half_partials(const GroupRegs &g, float &h_0, fl
 }
 template <int H>
 __device__ __forceinline__ void half_store(const float (&P)[8], float *ys, int rt, int ch) {
-    ys[(8 * H + rt) * rows::kYStride + ch] = reduce_rows4(P[0], P[1], P[2], P[3]);
-    ys[(8 * H + 4 + rt) * rows::kYStride + ch] = reduce_rows4(P[4], P[5], P[6], P[7]);
+    float ra, rb;
+    reduce_rows4x2(P, ra, rb);
+    ys[(8 * H + rt) * rows::kYStride + ch] = ra;
+    ys[(8 * H + 4 + rt) * rows::kYStride + ch] = rb;
 }
 
 // The last step of y for one tile: this thread's token row t = tid / 4 and 8 channels, as the
