@@ -424,7 +424,8 @@ __device__ __forceinline__ void mimo_token(const BcRegs<R> &g, const float (&dx)
 }
 
 // Four tokens TQ .. TQ + 3 of a group, then their 4R partials summed over the wave's rows four
-// at a time (partial index i = token * R + rank; after reduce_rows4 row j holds i0 + {0,2,1,3}[j])
+// at a time, two such groups interleaved (partial index i = token * R + rank; after the reduction
+// row j holds i0 + {0,2,1,3}[j])
 // and written to this wave's half of the y exchange.
 template <int TQ, int R, AForm AF, bool kTrap>
 __device__ __forceinline__ void mimo_quarter(const BcRegs<R> &g, const QuarterRegs<R> &q, float &h_0, float &h_1,
@@ -436,12 +437,16 @@ __device__ __forceinline__ void mimo_quarter(const BcRegs<R> &g, const QuarterRe
     mimo_token<TQ + 2, R, AF, kTrap>(g, q.dx[2], q.p[2], q.dl.z, h_0, h_1, a2_0, a2_1, P[2]);
     mimo_token<TQ + 3, R, AF, kTrap>(g, q.dx[3], q.p[3], q.dl.w, h_0, h_1, a2_0, a2_1, P[3]);
 #pragma unroll
-    for (int m = 0; m < R; ++m) {
+    for (int m = 0; m < R; m += 2) {   // two groups of four partials at a time, interleaved
         const int i0 = 4 * m;
-        const float s = reduce_rows4(P[(i0) / R][(i0) % R], P[(i0 + 1) / R][(i0 + 1) % R],
-                                     P[(i0 + 2) / R][(i0 + 2) % R], P[(i0 + 3) / R][(i0 + 3) % R]);
-        const int i = i0 + rt;
-        ys[(tq0 + i / R) * C::kYS + ch * R + (i % R)] = s;
+        float Q[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) Q[j] = P[(i0 + j) / R][(i0 + j) % R];
+        float sa, sb;
+        reduce_rows4x2(Q, sa, sb);
+        const int ia = i0 + rt, ib = i0 + 4 + rt;
+        ys[(tq0 + ia / R) * C::kYS + ch * R + (ia % R)] = sa;
+        ys[(tq0 + ib / R) * C::kYS + ch * R + (ib % R)] = sb;
     }
 }
 
