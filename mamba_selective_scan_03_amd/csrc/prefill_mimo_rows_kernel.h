@@ -109,7 +109,7 @@ template <typename E, int R, bool kTrap = false> struct MimoTileRegs {
     using C = mrows::Cfg<R, kTrap>;
     RawRow<E, C::kXV> x;     // token tid / kTPT, channels kCPT (tid % kTPT) .. + kCPT, all ranks
     RawRow<E, C::kCPT> dl;   // the same token and channels
-    RawRow<E, C::kBV> bc;    // B or C: token, states kSPT (tid % kTPB) .. + kSPT, all ranks
+    RawRow<E, C::kBV> bc;    // B or C: the token and kSPT states of bc_thread(), all ranks
     // trapezoidal rule only: lam of the token and channels; x of the token before; B (or C) of
     // the token before
     RawRow<E, C::kCPT> lam;
@@ -124,6 +124,16 @@ template <typename E> struct MimoPrev {
     bool given;
 };
 
+// The B or C thread's token (tb) and first state (s0) within a tile.  Consecutive threads take
+// consecutive tokens, so a half-wave's staging writes to the [state][rank][token] tile fall on
+// distinct LDS banks.  Every use (loads, staging, the previous token's row) goes through here.
+template <int R, bool kTrap>
+__device__ __forceinline__ void bc_thread(int tid, int &tb, int &s0) {
+    using C = mrows::Cfg<R, kTrap>;
+    tb = (tid & 127) % C::kT;
+    s0 = (tid & 127) / C::kT * C::kSPT;
+}
+
 // Requests one tile's raw inputs (tokens past L re-read token L - 1; staging replaces them).
 template <typename E, int R, bool kTrap = false>
 __device__ __forceinline__ void mimo_load_tile(MimoTileRegs<E, R, kTrap> &Rg, const typename E::store_t *xb,
@@ -135,7 +145,8 @@ __device__ __forceinline__ void mimo_load_tile(MimoTileRegs<E, R, kTrap> &Rg, co
     const int64_t tt = min(t0 + t, L - 1);
     Rg.x.load(xb + (tt * D + c0) * R);
     Rg.dl.load(db + tt * D + c0);
-    const int tb = (tid & 127) / C::kTPB, s0 = (tid % C::kTPB) * C::kSPT;
+    int tb, s0;
+    bc_thread<R, kTrap>(tid, tb, s0);
     const int64_t tq = min(t0 + tb, L - 1);
     Rg.bc.load(bcb + (tq * kDState + s0) * R);
     if constexpr (kTrap) {
@@ -188,7 +199,8 @@ __device__ __forceinline__ void mimo_stage_tile(const MimoTileRegs<E, R, kTrap> 
         for (int i = 0; i < C::kXV / 4; ++i)
             reinterpret_cast<float4 *>(pd)[i] = make_float4(pv[4 * i], pv[4 * i + 1], pv[4 * i + 2], pv[4 * i + 3]);
     }
-    const int tb = (tid & 127) / C::kTPB, s0 = (tid % C::kTPB) * C::kSPT;
+    int tb, s0;
+    bc_thread<R, kTrap>(tid, tb, s0);
     const bool live_bc = t0 + tb < L;
     float *tile = bc_s + (tid >= 128 ? C::kBcSize : 0);
 #pragma unroll
@@ -486,7 +498,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const bool prev_given = kTrap && tr.x_prev != nullptr;
         MimoPrev<E> pr{nullptr, nullptr, nullptr, prev_given};
         if constexpr (kTrap) {
-            const int c0 = (tid % Cf::kTPT) * Cf::kCPT, s0 = (tid % Cf::kTPB) * Cf::kSPT;
+            const int c0 = (tid % Cf::kTPT) * Cf::kCPT;
+            int tb, s0;
+            bc_thread<R, kTrap>(tid, tb, s0);
+            (void)tb;
             pr.lam = static_cast<const S *>(tr.lam) + (int64_t)b * L * D + d0;
             pr.x = prev_given ? static_cast<const S *>(tr.x_prev) + ((int64_t)b * D + d0 + c0) * R : xb + c0 * R;
             pr.bc = prev_given ? static_cast<const S *>(tr.B_prev) + ((int64_t)b * kDState + s0) * R : bcb + s0 * R;
