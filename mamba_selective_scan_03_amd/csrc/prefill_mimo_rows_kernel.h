@@ -46,7 +46,7 @@ template <int R, bool kTrap = false> struct Cfg {
     static constexpr int kSPT = kDState / kTPB;
     static constexpr int kBV = kSPT * R;
     // LDS (floats): dx [kT][kXS] (channel-major rows of kCh * R); delta [kT/4][kCh][4]; B and C
-    // [16][R][kBS]; y partials [2 halves][kT][kYS].  At R = 4 and 8 without the trapezoidal rule
+    // [kT][kTS] (token rows of [16 states][R ranks]); y partials [2 halves][kT][kYS].  At R = 4 and 8 without the trapezoidal rule
     // the dx and y token rows are padded by 4 floats, so that the helper threads' 16-byte
     // accesses (8 or 16 threads per token, 16 floats each) spread over all 32 LDS banks instead
     // of a quarter of them: 2-3% faster there.  The same padding measured 1-2% slower at R = 2 and
@@ -55,9 +55,11 @@ template <int R, bool kTrap = false> struct Cfg {
     static constexpr int kXS = kCh * R + kPad;
     static constexpr int kDxSize = kT * kXS;
     static constexpr int kDlSize = kT * kCh;
-    // B/C rows of 16 tokens read by the 4 rows of a wave (states 2 apart) land 16 banks apart
-    static constexpr int kBS = R == 2 ? kT + 4 : R == 4 ? kT + 2 : kT + 1;
-    static constexpr int kBcSize = kDState * R * kBS;
+    // A scan lane reads its two states' 2R values of one token as 16-byte reads, 16 lanes on 16
+    // consecutive tokens; the token rows are padded by 4 floats so that those reads spread over
+    // the banks.
+    static constexpr int kTS = kDState * R + 4;
+    static constexpr int kBcSize = kT * kTS;
     static constexpr int kBcTiles = kTrap ? 3 : 2;   // B, C (and the previous token's B)
     static constexpr int kYS = kCh * R + (R == 2 ? 32 : kPad);
     static constexpr int kYSize = 2 * kT * kYS;
@@ -202,16 +204,21 @@ __device__ __forceinline__ void mimo_stage_tile(const MimoTileRegs<E, R, kTrap> 
     int tb, s0;
     bc_thread<R, kTrap>(tid, tb, s0);
     const bool live_bc = t0 + tb < L;
-    float *tile = bc_s + (tid >= 128 ? C::kBcSize : 0);
+    // this thread's kBV values (i = (n - s0) * R + r) are one contiguous run of its token's row
+    float4 *tile = reinterpret_cast<float4 *>(bc_s + (tid >= 128 ? C::kBcSize : 0) + tb * C::kTS + s0 * R);
 #pragma unroll
-    for (int i = 0; i < C::kBV; ++i)   // i = (n - s0) * R + r
-        tile[(s0 * R + i) * C::kBS + tb] = live_bc ? Rg.bc.get(i) : 0.0f;
+    for (int i = 0; i < C::kBV / 4; ++i)
+        tile[i] = live_bc ? make_float4(Rg.bc.get(4 * i), Rg.bc.get(4 * i + 1), Rg.bc.get(4 * i + 2), Rg.bc.get(4 * i + 3))
+                          : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if constexpr (kTrap) {
         if (tid < 128) {   // whole waves: the B threads
             const bool prev_live = live_bc && (t0 + tb > 0 || prev_given);
-            float *bp = bc_s + 2 * C::kBcSize;
+            float4 *bp = reinterpret_cast<float4 *>(bc_s + 2 * C::kBcSize + tb * C::kTS + s0 * R);
 #pragma unroll
-            for (int i = 0; i < C::kBV; ++i) bp[(s0 * R + i) * C::kBS + tb] = prev_live ? Rg.bcp.get(i) : 0.0f;
+            for (int i = 0; i < C::kBV / 4; ++i)
+                bp[i] = prev_live ? make_float4(Rg.bcp.get(4 * i), Rg.bcp.get(4 * i + 1), Rg.bcp.get(4 * i + 2),
+                                                Rg.bcp.get(4 * i + 3))
+                                  : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         }
     }
 }
@@ -279,17 +286,25 @@ __device__ __forceinline__ void mimo_load_quarter(QuarterRegs<R> &q, const float
 template <int R> struct BcRegs {
     float b[2][R], c[2][R], bp[2][R];
 };
+template <int R>
+__device__ __forceinline__ void mimo_read_pair(float (&dst)[2][R], const float *src) {
+    // states n0 and n0 + 1, all ranks: 2R contiguous floats
+#pragma unroll
+    for (int j = 0; j < 2 * R / 4; ++j) {
+        const float4 v = reinterpret_cast<const float4 *>(src)[j];
+        dst[(4 * j) / R][(4 * j) % R] = v.x;
+        dst[(4 * j + 1) / R][(4 * j + 1) % R] = v.y;
+        dst[(4 * j + 2) / R][(4 * j + 2) % R] = v.z;
+        dst[(4 * j + 3) / R][(4 * j + 3) % R] = v.w;
+    }
+}
 template <int R, bool kTrap>
 __device__ __forceinline__ void mimo_load_bc(BcRegs<R> &g, const float *bc_s, int tg, int n0, int c) {
     using C = mrows::Cfg<R, kTrap>;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            g.b[i][r] = bc_s[((n0 + i) * R + r) * C::kBS + tg + c];
-            g.c[i][r] = bc_s[C::kBcSize + ((n0 + i) * R + r) * C::kBS + tg + c];
-            if constexpr (kTrap) g.bp[i][r] = bc_s[2 * C::kBcSize + ((n0 + i) * R + r) * C::kBS + tg + c];
-        }
+    const float *row = bc_s + (tg + c) * C::kTS + n0 * R;
+    mimo_read_pair<R>(g.b, row);
+    mimo_read_pair<R>(g.c, row + C::kBcSize);
+    if constexpr (kTrap) mimo_read_pair<R>(g.bp, row + 2 * C::kBcSize);
 }
 
 // The token's DPP-fused FMAs as few asm statements.  The compiler cannot see into an asm
