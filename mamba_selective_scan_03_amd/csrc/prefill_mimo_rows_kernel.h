@@ -127,8 +127,9 @@ template <typename E> struct MimoPrev {
 };
 
 // The B or C thread's token (tb) and first state (s0) within a tile.  Consecutive threads take
-// consecutive tokens, so a half-wave's staging writes to the [state][rank][token] tile fall on
-// distinct LDS banks.  Every use (loads, staging, the previous token's row) goes through here.
+// consecutive tokens, so a half-wave's 16-byte staging stores land on consecutive padded token
+// rows and spread over the LDS banks.  Every use (loads, staging, the previous token's row) goes
+// through here.
 template <int R, bool kTrap>
 __device__ __forceinline__ void bc_thread(int tid, int &tb, int &s0) {
     using C = mrows::Cfg<R, kTrap>;
