@@ -591,19 +591,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         constexpr int cur = decltype(cur_c)::value;
         float *ys = y_s[cur] + sh * kT * Cf::kYS;
         const float *dxc = dx_s[cur], *dlc = dl_s[cur], *bcc = bc_s[cur], *psc = p_s[cur];
-        BcRegs<R> g;
+        BcRegs<R> g[2];
         QuarterRegs<R> qa, qb;
+        mimo_load_bc<R, kTrap>(g[0], bcc, 0, n0, c);
+        mimo_load_quarter<R, kTrap>(qa, dxc, dlc, psc, 0, ch);
+        mimo_load_quarter<R, kTrap>(qb, dxc, dlc, psc, 4, ch);
 #pragma unroll
         for (int tg = 0; tg < kT; tg += 16) {
-            mimo_load_bc<R, kTrap>(g, bcc, tg, n0, c);
-            mimo_load_quarter<R, kTrap>(qa, dxc, dlc, psc, tg, ch);
-            mimo_load_quarter<R, kTrap>(qb, dxc, dlc, psc, tg + 4, ch);
-            mimo_quarter<0, R, AF, kTrap>(g, qa, h_0, h_1, a2_0, a2_1, ys, tg, rt, ch);
+            const BcRegs<R> &gc = g[(tg >> 4) & 1];
+            mimo_quarter<0, R, AF, kTrap>(gc, qa, h_0, h_1, a2_0, a2_1, ys, tg, rt, ch);
             mimo_load_quarter<R, kTrap>(qa, dxc, dlc, psc, tg + 8, ch);
-            mimo_quarter<4, R, AF, kTrap>(g, qb, h_0, h_1, a2_0, a2_1, ys, tg + 4, rt, ch);
+            if (tg + 16 < kT) mimo_load_bc<R, kTrap>(g[((tg >> 4) + 1) & 1], bcc, tg + 16, n0, c);
+            mimo_quarter<4, R, AF, kTrap>(gc, qb, h_0, h_1, a2_0, a2_1, ys, tg + 4, rt, ch);
             mimo_load_quarter<R, kTrap>(qb, dxc, dlc, psc, tg + 12, ch);
-            mimo_quarter<8, R, AF, kTrap>(g, qa, h_0, h_1, a2_0, a2_1, ys, tg + 8, rt, ch);
-            mimo_quarter<12, R, AF, kTrap>(g, qb, h_0, h_1, a2_0, a2_1, ys, tg + 12, rt, ch);
+            mimo_quarter<8, R, AF, kTrap>(gc, qa, h_0, h_1, a2_0, a2_1, ys, tg + 8, rt, ch);
+            if (tg + 16 < kT) mimo_load_quarter<R, kTrap>(qa, dxc, dlc, psc, tg + 16, ch);
+            mimo_quarter<12, R, AF, kTrap>(gc, qb, h_0, h_1, a2_0, a2_1, ys, tg + 12, rt, ch);
+            if (tg + 16 < kT) mimo_load_quarter<R, kTrap>(qb, dxc, dlc, psc, tg + 20, ch);
         }
         __syncthreads();
         (void)k;
