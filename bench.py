@@ -145,12 +145,13 @@ def read_traffic(workload: str, launches_per_step: int):
 def cpu_baseline(wl, inp, channels: int, scalar_a=None, complex_a=False, lam=None, mimo=0):
     """The fp64 oracle, as it stands, on a bounded sample: all tokens of `channels` channels
     (with `scalar_a`, the scaled-identity oracle on that A; with `complex_a`, the complex-state
-    oracle on inp["A"]; with `lam`, the exponential-trapezoidal oracle)."""
+    oracle on inp["A"]; with `lam`, the exponential-trapezoidal oracle).  Returns the report
+    and the oracle's (y, h_final) on the sample, which the bench compares with its own outputs."""
     import numpy as np
 
     import oracle
 
-    threads = min(16, os.cpu_count() or 1)
+    threads = min(16, len(os.sched_getaffinity(0)))
     x = inp["x"][:, :, :channels]
     dl = inp["delta"][:, :, :channels]
     A = inp["A"][:channels] if scalar_a is None else scalar_a[:channels]
@@ -160,14 +161,14 @@ def cpu_baseline(wl, inp, channels: int, scalar_a=None, complex_a=False, lam=Non
     form = "complex" if complex_a else "diagonal" if scalar_a is None else "scalar"
     if mimo and lam is not None:
         lm = np.ascontiguousarray(lam[:, :, :channels].float().numpy(), dtype=np.float64)
-        oracle.prefill_mimo_trapezoid(args[0], args[1], lm, *args[2:], form=form, nthreads=threads)
+        ref = oracle.prefill_mimo_trapezoid(args[0], args[1], lm, *args[2:], form=form, nthreads=threads)
     elif mimo:
-        oracle.prefill_mimo(*args, form=form, nthreads=threads)
+        ref = oracle.prefill_mimo(*args, form=form, nthreads=threads)
     elif lam is not None:
         lm = np.ascontiguousarray(lam[:, :, :channels].float().numpy(), dtype=np.float64)
-        oracle.prefill_trapezoid(args[0], args[1], lm, *args[2:], form=form, nthreads=threads)
+        ref = oracle.prefill_trapezoid(args[0], args[1], lm, *args[2:], form=form, nthreads=threads)
     else:
-        fn(*args, nthreads=threads)
+        ref = fn(*args, nthreads=threads)
     dt = time.perf_counter() - t0
     elems = wl.batch * wl.L * channels
     cpu = "unknown CPU"
@@ -176,9 +177,125 @@ def cpu_baseline(wl, inp, channels: int, scalar_a=None, complex_a=False, lam=Non
             cpu = next(line.split(":", 1)[1].strip() for line in fh if line.startswith("model name"))
     except (OSError, StopIteration):
         pass
-    return {"value": elems / dt, "unit": "elems/s", "cores": threads, "kind": "oracle",
-            "sample": f"{wl.name}: batch {wl.batch}, all {wl.L} tokens, first {channels} of {wl.D} channels, "
-                      f"N {wl.N}, fp64 ({dt:.1f} s on {cpu})"}
+    out = {"value": elems / dt, "unit": "elems/s", "cores": threads, "kind": "oracle",
+           "sample": f"{wl.name}: batch {wl.batch}, all {wl.L} tokens, first {channels} of {wl.D} channels, "
+                     f"N {wl.N}, fp64 ({dt:.1f} s on {threads} threads)",
+           "host_cpu": cpu, "host_cpus": os.cpu_count(), "cpus_allowed": len(os.sched_getaffinity(0)),
+           "threads": threads}
+    return out, ref
+
+
+def single_thread_rate():
+    """The oracle on one thread over a bounded sample of the 4K workload (all 4096 tokens of
+    its first 256 channels): elems/s of B*L*D."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    wl = workloads.get("prefill_4k")
+    inp = workloads.prefill_inputs(wl)
+    ch = 256
+    args = [np.ascontiguousarray(t.float().numpy(), dtype=np.float64)
+            for t in (inp["x"][:, :, :ch], inp["delta"][:, :, :ch], inp["A"][:ch], inp["B"], inp["C"])]
+    t0 = time.perf_counter()
+    oracle.prefill(*args, nthreads=1)
+    dt = time.perf_counter() - t0
+    return {"value": wl.batch * wl.L * ch / dt, "unit": "elems/s", "threads": 1,
+            "sample": f"prefill_4k: all {wl.L} tokens, first {ch} of {wl.D} channels ({dt:.2f} s)"}
+
+
+def run_micro(log):
+    """The microbenchmarks of libjscan_micro: vector-ALU issue rates (FMA, exponential, their
+    mix, DPP and permlane forms) at 8 waves and at 1 wave per SIMD, matrix cores beside the
+    vector ALU, the matrix core's rounding of a*b + c, LDS read bandwidth and HBM streams.
+    Returns one dict of measured and derived rates."""
+    import torch
+
+    from mamba_selective_scan_03_amd import micro
+
+    cus, simds = 256, 1024
+    out = {"gpu": torch.cuda.get_device_name(0), "rocm": torch.version.hip}
+    # shader clock from the FMA loop: clocks over 100 MHz reference ticks
+    ms, clk, ticks = micro.valu(0, 100000, 2048, 256)
+    ghz = clk / (ticks / 100e6) / 1e9
+    out["shader_clock_GHz"] = round(ghz, 3)
+    hz = ghz * 1e9
+
+    def cycles_per_instr(kind, waves_per_simd, iters, per_trip=16):
+        threads = 256 if waves_per_simd >= 4 else 64
+        blocks = simds * waves_per_simd * 64 // threads
+        ms, _, _ = micro.valu(kind, iters, blocks, threads)
+        instr_per_simd = waves_per_simd * iters * per_trip
+        return ms * 1e-3 * hz / instr_per_simd
+
+    valu = {}
+    for kind, name in micro.VALU_KINDS.items():
+        row = {}
+        for w, iters in ((8, 20000), (1, 160000)):
+            row[f"cycles_per_instr_{w}w"] = round(cycles_per_instr(kind, w, iters), 3)
+        valu[name] = row
+        log(f"micro valu {name}: {row}")
+    out["valu_cycles_per_wave_instruction"] = valu
+    c_fma = valu["fma"]["cycles_per_instr_8w"]
+    c_exp = valu["exp"]["cycles_per_instr_8w"]
+    mix = valu["exp8+fma8"]["cycles_per_instr_8w"] * 16
+    pair = valu["mul+exp pairs"]["cycles_per_instr_8w"] * 16 / 8
+    swap = (valu["permlane32_swap+max"]["cycles_per_instr_8w"] * 16 - 8 * c_fma) / 8
+    out["derived"] = {
+        "fma_lane_ops_per_CU_clock": round(4 * 64 / c_fma, 2),
+        "exp_lane_ops_per_CU_clock": round(4 * 64 / c_exp, 2),
+        "exp_cost_in_fma_slots": round(c_exp / c_fma, 3),
+        "exp8_fma8_trip_cycles": round(mix, 1),
+        "exp8_fma8_if_serial": round(8 * c_exp + 8 * c_fma, 1),
+        "exp8_fma8_if_overlapped": round(max(8 * c_exp, 8 * c_fma), 1),
+        "mul_exp_pair_cost_in_fma_slots": round(pair / c_fma, 3),
+        "permlane32_swap_cost_in_fma_slots": round(swap / c_fma, 3),
+        "mul_dpp_cost_in_fma_slots": round(valu["mul_dpp_bcast"]["cycles_per_instr_8w"] / c_fma, 3),
+        "valu_lane_slots_per_s": round(cus * 4 * 64 * hz / c_fma, -9),
+    }
+
+    # matrix cores beside the vector ALU: 4 waves per SIMD
+    mf_iters = 16000
+    t = [micro.mfma_valu(m, mf_iters, 1024, 256) for m in (0, 1, 2)]
+    out["mfma_beside_valu"] = {"mfma_only_ms": round(t[0], 3), "valu_only_ms": round(t[1], 3),
+                               "both_ms": round(t[2], 3),
+                               "overlap": round((t[0] + t[1] - t[2]) / min(t[0], t[1]), 3),
+                               "mfma_16x16x4_f32_cycles": round(t[0] * 1e-3 * hz / (4 * mf_iters * 4), 2)}
+    log(f"micro mfma beside valu: {out['mfma_beside_valu']}")
+
+    g = torch.Generator().manual_seed(0)
+    a = torch.randn(64, generator=g).cuda()
+    b = torch.randn(64, generator=g).cuda()
+    c = (torch.randn(256, generator=g) * 4).cuda()
+    d1, d2 = micro.mfma_rounding(a, b, c)
+    diff = int((d1.view(torch.int32) != d2.view(torch.int32)).sum())
+    near = float(((d1 - d2).abs() / d2.abs().clamp_min(1e-30)).max())
+    out["mfma_4x4x1_f32_vs_fmaf"] = {"values": 256, "bitwise_differences": diff, "max_rel_diff": near}
+    log(f"micro mfma rounding: {out['mfma_4x4x1_f32_vs_fmaf']}")
+
+    iters = 20000
+    ms = micro.lds(iters, 2048, 256)
+    out["lds_read_bytes_per_CU_clock"] = round(2048 * 256 * iters * 128 / (ms * 1e-3 * hz) / cus, 1)
+    log(f"micro lds: {out['lds_read_bytes_per_CU_clock']} B/clk/CU")
+
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    hbm = {}
+    for kind, name in ((0, "read"), (1, "write"), (2, "copy")):
+        for nt in (False, True):
+            best = None
+            for blocks in (1024, 2048, 4096, 8192):
+                ms = micro.hbm(kind, nt, src, dst, nbytes, blocks, 10) / 10
+                moved = nbytes * (2 if kind == 2 else 1)
+                gbps = moved / (ms * 1e-3) / 1e9
+                if best is None or gbps > best[0]:
+                    best = (gbps, blocks)
+            hbm[f"{name}{'_nt' if nt else ''}"] = {"GBps": round(best[0], 1), "blocks": best[1]}
+    out["hbm_1GiB_streams"] = hbm
+    log(f"micro hbm: {hbm}")
+    return out
 
 
 def main():
@@ -212,6 +329,11 @@ def main():
     ap.add_argument("--cpu-channels", type=int, default=8192,
                     help="oracle sample: all tokens of the first CPU_CHANNELS channels (default: every channel "
                          "of the 64K workload, a few seconds on 16 cores; 0 = skip)")
+    ap.add_argument("--micro", action="store_true",
+                    help="instead of the scan, run the microbenchmarks (vector ALU, matrix cores, LDS, HBM) and print "
+                         "their rates as one JSON line")
+    ap.add_argument("--cpu-single-thread", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time the oracle on one thread over a sample of the 4K workload")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the scan, time a plain device-to-device copy of MIB mebibytes (the reference "
                          "kernel for scaling the profiler's FETCH_SIZE / WRITE_SIZE counters)")
@@ -231,6 +353,11 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.micro:
+        torch.cuda.set_device(dev)
+        print(json.dumps({"micro": run_micro(lambda *a: print("[bench]", *a, file=sys.stderr, flush=True))}),
+              flush=True)
+        return
     if args.calibrate_copy:
         n = args.calibrate_copy * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -485,11 +612,19 @@ def main():
         # three launches per step (segment summaries, carry, rescan): the line reports the
         # whole pass against the one-pass ALU bound
         per_launch_ms = ms_step
-    if wl.layers > 1:
-        roofline = {"bound": "hbm", "achieved": round(alg_bytes / launches / (per_launch_ms * 1e-3) / 1e9, 1),
-                    "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
-        roofline["frac"] = round(roofline["achieved"] / HBM_PEAK_GBPS, 4)
-    else:
+    # The metric's roofline is HBM: algorithmic bytes of one launch of the dominant kernel over
+    # its average launch time (HIP events on the stream the kernels run on).  For the prefill the
+    # binding resource is the vector ALU, so its issue-bound fraction is reported beside it.
+    hbm_achieved = alg_bytes / launches / (per_launch_ms * 1e-3) / 1e9
+    if args.producer or args.chunked:
+        hbm_achieved = alg_bytes / (per_launch_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(hbm_achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(hbm_achieved / HBM_PEAK_GBPS, 4)}
+    roofline["traffic"] = None if (args.chunked or args.producer) else read_traffic(
+        wl.name + ("_scalar_a" if args.scalar_a else "_complex_a" if args.complex_a else "")
+        + ("_trapezoid" if args.trapezoid else "") + (f"_mimo{args.mimo}" if args.mimo else ""), launches)
+    roofline_alu = None
+    if wl.layers == 1:
         state_elems = elems * wl.N
         slots, flops = ((SCALAR_A_SLOTS, SCALAR_A_FLOPS) if args.scalar_a else
                         (COMPLEX_A_SLOTS, COMPLEX_A_FLOPS) if args.complex_a else
@@ -502,11 +637,10 @@ def main():
                 slots, flops = slots + args.mimo, flops + 2 * args.mimo
         achieved_tf = state_elems * flops / (per_launch_ms * 1e-3) / 1e12
         peak_tf = VALU_SLOTS_PER_S / slots * flops / 1e12
-        roofline = {"bound": "alu", "achieved": round(achieved_tf, 2), "peak": round(peak_tf, 2), "unit": "TFLOP/s",
-                    "frac": round(achieved_tf / peak_tf, 4)}
-    roofline["traffic"] = None if (args.chunked or args.producer) else read_traffic(
-        wl.name + ("_scalar_a" if args.scalar_a else "_complex_a" if args.complex_a else "")
-        + ("_trapezoid" if args.trapezoid else "") + (f"_mimo{args.mimo}" if args.mimo else ""), launches)
+        roofline_alu = {"bound": "alu", "achieved": round(achieved_tf, 2), "peak": round(peak_tf, 2),
+                        "unit": "TFLOP/s", "frac": round(achieved_tf / peak_tf, 4), "slots_per_state_elem": slots,
+                        "hbm_frac_at_this_bound": round(alg_bytes * VALU_SLOTS_PER_S / slots / state_elems
+                                                        / 1e9 / HBM_PEAK_GBPS, 4)}
 
     out = {
         "metric": METRIC,
@@ -535,15 +669,65 @@ def main():
         "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": alg_bytes,
         "roofline": roofline,
+        "roofline_alu": roofline_alu,
     }
     if producer_info is not None:
         out["producer"] = producer_info
+    out.update(run_info(torch))
     if host_inp is not None and args.cpu_channels > 0 and wl.layers == 1:
-        out["cpu_baseline"] = cpu_baseline(wl, host_inp, min(args.cpu_channels, wl.D),
-                                           host_a if args.scalar_a else None, complex_a=args.complex_a,
-                                           lam=host_inp.get("lam") if args.trapezoid else None, mimo=args.mimo)
+        ch = min(args.cpu_channels, wl.D)
+        out["cpu_baseline"], ref = cpu_baseline(wl, host_inp, ch, host_a if args.scalar_a else None,
+                                                complex_a=args.complex_a,
+                                                lam=host_inp.get("lam") if args.trapezoid else None, mimo=args.mimo)
         log(f"oracle sample: {out['cpu_baseline']['sample']}")
+        if args.cpu_single_thread:
+            out["cpu_baseline"]["single_thread"] = single_thread_rate()
+        if not args.producer:
+            # the timed run's own outputs (last step) against the oracle on the sampled channels
+            import numpy as np
+
+            y_ref, h_ref = ref
+            y_got = y[..., :ch, :] if args.mimo else y[..., :ch]
+            err_y = float(np.max(np.abs(y_got.double().cpu().numpy() - y_ref))) / float(np.max(np.abs(y_ref)))
+            err_h = float(np.max(np.abs(h[:, :ch].double().cpu().numpy() - h_ref))) / float(np.max(np.abs(h_ref)))
+            out["parity_max_rel"] = {"y": float(f"{err_y:.3e}"), "h_final": float(f"{err_h:.3e}"),
+                                     "tol": 1e-4 if wl.dtype == "f32" else 2e-2,
+                                     "channels": f"first {ch} of {wl.D}, all tokens"}
+    if wl.layers == 1 and not (args.producer or args.chunked or args.mimo or args.trapezoid or args.scalar_a
+                               or args.complex_a):
+        out["bitexact_ok"] = bitexact_check(jscan, d, wl)
     print(json.dumps(out), flush=True)
+
+
+def run_info(torch):
+    """GPU, ROCm and source identification for the report line."""
+    info = {"gpu": torch.cuda.get_device_name(0), "rocm": torch.version.hip, "torch": torch.__version__}
+    sha = None
+    try:
+        import subprocess
+
+        sha = subprocess.run(["git", "rev-parse", "--short=12", "HEAD"], cwd=ROOT, capture_output=True, text=True,
+                             timeout=10).stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        pass
+    info["git_sha"] = sha
+    info["kernel_source_hash"] = kernel_source_hash("prefill")
+    return info
+
+
+def bitexact_check(jscan, d, wl, tokens: int = 256):
+    """The first `tokens` tokens of the workload through jscan_prefill and through as many
+    jscan_step calls from the zero state: the two final states must be equal bit for bit."""
+    import torch
+
+    x, dl, B, C = (d[k][:, :tokens].contiguous() for k in ("x", "delta", "B", "C"))
+    _, h_pre = jscan.prefill(x, dl, d["A"], B, C)
+    h = torch.zeros_like(h_pre)
+    y_t = torch.empty((wl.batch, wl.D), dtype=x.dtype, device=x.device)
+    for t in range(tokens):
+        jscan.step(h, x[:, t], dl[:, t], d["A"], B[:, t], C[:, t], y_t=y_t if wl.batch == 1 else None)
+    torch.cuda.synchronize()
+    return bool(torch.equal(h.view(torch.int32), h_pre.view(torch.int32)))
 
 
 if __name__ == "__main__":

@@ -39,19 +39,28 @@ def softplus(z) -> np.ndarray:
     return np.logaddexp(0.0, np.asarray(z, np.float64))
 
 
-def ssm_inputs(x, w_x, g_d, g_b, g_c, w_dt, b_dt, eps: float, R: int, N: int = 16):
-    """Producer side for M tokens: x [M, D] -> (d_low [M, R], B [M, N], C [M, N], delta [M, D]),
-    each rounded once to bf16 (returned as float64 arrays of bf16 values)."""
+def ssm_inputs_low(x, w_x, g_d, g_b, g_c, eps: float, R: int, N: int = 16):
+    """Steps 1 and 2 for M tokens: x [M, D] -> (d_low [M, R], B [M, N], C [M, N]), each rounded
+    once to bf16 (returned as float64 arrays of bf16 values)."""
     x = np.asarray(x, np.float64)
     w_x = np.asarray(w_x, np.float64)
-    w_dt = np.asarray(w_dt, np.float64)
-    if w_x.shape != (R + 2 * N, x.shape[1]) or w_dt.shape != (x.shape[1], R):
-        raise ValueError("w_x must be [R + 2N, D] and w_dt [D, R]")
+    if w_x.shape != (R + 2 * N, x.shape[1]):
+        raise ValueError("w_x must be [R + 2N, D]")
     proj = x @ w_x.T                                             # step 1
     d_low = round_bf16(rms_norm(proj[:, :R], g_d, eps))          # step 2
     B = round_bf16(rms_norm(proj[:, R:R + N], g_b, eps))
     C = round_bf16(rms_norm(proj[:, R + N:], g_c, eps))
-    delta = round_bf16(softplus(d_low @ w_dt.T + np.asarray(b_dt, np.float64)))   # step 3
+    return d_low, B, C
+
+
+def ssm_inputs(x, w_x, g_d, g_b, g_c, w_dt, b_dt, eps: float, R: int, N: int = 16):
+    """Producer side for M tokens: x [M, D] -> (d_low [M, R], B [M, N], C [M, N], delta [M, D]),
+    each rounded once to bf16 (returned as float64 arrays of bf16 values)."""
+    w_dt = np.asarray(w_dt, np.float64)
+    if w_dt.shape != (np.shape(x)[1], R):
+        raise ValueError("w_dt must be [D, R]")
+    d_low, B, C = ssm_inputs_low(x, w_x, g_d, g_b, g_c, eps, R, N)
+    delta = delta_from_low(d_low, w_dt, b_dt)                    # step 3
     return d_low, B, C, delta
 
 

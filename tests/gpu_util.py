@@ -35,3 +35,29 @@ def assert_parity(got, ref, dtype, what):
 
 def bits(t):
     return t.detach().contiguous().view(torch.int32 if t.dtype == torch.float32 else torch.int16).cpu()
+
+
+class GlobalRel:
+    """max|got - ref| / max|ref| accumulated over blocks of one output, so that a whole tensor
+    can be compared without holding its fp64 reference at once."""
+
+    def __init__(self, what):
+        self.what, self.err, self.ref, self.finite = what, 0.0, 0.0, True
+
+    def add(self, got, ref):
+        got = np.asarray(got, np.float64)
+        ref = np.asarray(ref, np.float64)
+        self.finite = self.finite and bool(np.all(np.isfinite(got)))
+        self.err = max(self.err, float(np.max(np.abs(got - ref))))
+        self.ref = max(self.ref, float(np.max(np.abs(ref))))
+
+    def check(self, dtype):
+        rel = self.err / max(self.ref, 1e-30)
+        say(f"{self.what}: max|err|/max|ref| = {rel:.3e} over every element (tol {TOL[dtype]:g})")
+        assert self.finite, f"{self.what}: non-finite output"
+        assert rel <= TOL[dtype], f"{self.what}: {rel:.3e} > {TOL[dtype]:g}"
+        return rel
+
+
+def channel_blocks(D, block):
+    return [(c0, min(c0 + block, D)) for c0 in range(0, D, block)]

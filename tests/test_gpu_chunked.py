@@ -100,10 +100,11 @@ def test_chunked_agrees_with_sequential_gpu_scan_on_zero_A():
     assert float(h1[0, 0, 0]) == L
 
 
-def test_prefill_64k_tp8_chunked_sampled_parity():
+@pytest.mark.timeout(600)
+def test_prefill_64k_tp8_chunked_every_channel():
     """The channel-sharded 64K prompt (D = 1024 per GPU) through the automatic time-parallel
-    path, in the launch configuration the benchmark times, against the oracle on sampled
-    channels over all 65536 tokens."""
+    path, in the launch configuration the benchmark times, against the oracle on every
+    channel over all 65536 tokens."""
     wl = workloads.get("prefill_64k_tp8")
     say("generating prefill_64k_tp8 inputs")
     inp = workloads.prefill_inputs(wl)
@@ -111,14 +112,9 @@ def test_prefill_64k_tp8_chunked_sampled_parity():
     y, h = jscan.prefill_chunked(d["x"], d["delta"], d["A"], d["B"], d["C"])
     y_seq, h_seq = jscan.prefill(d["x"], d["delta"], d["A"], d["B"], d["C"])
     torch.cuda.synchronize()
-    rng = np.random.default_rng(11)
-    chans = sorted(set([0, 1, 31, 32, 511, 512, 1022, 1023] + rng.choice(wl.D, 16, replace=False).tolist()))
-    say(f"oracle on {len(chans)} channels x {wl.L} tokens")
-    y_ref, h_ref = oracle.prefill(inp["x"][:, :, chans], inp["delta"][:, :, chans], inp["A"][chans],
-                                  inp["B"], inp["C"])
-    idx = torch.tensor(chans, device="cuda")
-    assert_parity(f64(y.index_select(2, idx)), y_ref, torch.bfloat16, "prefill_64k_tp8 chunked y (sampled)")
-    assert_parity(f64(h.index_select(1, idx)), h_ref, torch.bfloat16, "prefill_64k_tp8 chunked h_final (sampled)")
-    # against the GPU's own sequential scan on every channel: the same tolerance form
-    assert_parity(f64(y), f64(y_seq), torch.bfloat16, "prefill_64k_tp8 chunked vs sequential y")
-    assert_parity(f64(h), f64(h_seq), torch.bfloat16, "prefill_64k_tp8 chunked vs sequential h_final")
+    say(f"oracle on all {wl.D} channels x {wl.L} tokens")
+    y_ref, h_ref = oracle.prefill(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], nthreads=16)
+    assert_parity(f64(y), y_ref, torch.bfloat16, "prefill_64k_tp8 chunked y")
+    assert_parity(f64(h), h_ref, torch.bfloat16, "prefill_64k_tp8 chunked h_final")
+    assert_parity(f64(y_seq), y_ref, torch.bfloat16, "prefill_64k_tp8 sequential y")
+    assert_parity(f64(h_seq), h_ref, torch.bfloat16, "prefill_64k_tp8 sequential h_final")

@@ -1,10 +1,10 @@
 """Full-size long-context workloads on the GPU, in the launch configuration the bench times.
 
-The oracle cannot redo a whole 64K x 8192 or 256K x 8192 scan in seconds, but channels are
-independent, so it recomputes a sample of channels over the whole sequence: channels at
-the edges of the 16-channel lane groups, the 32-channel workgroups and the XCD channel
-ranges, plus random ones.  The tolerance is the workload's own, taken against the sampled
-max|y_ref| (which can only make the check stricter than against the global maximum).
+Every channel of the 64K x 8192 and 256K x 8192 scans is compared with the fp64 oracle.
+Channels are independent, so the oracle runs one block of channels at a time over the whole
+sequence and the comparison is streamed block by block: the fp64 reference of a whole 256K
+output (16 GiB) is never held at once.  The tolerance is the workload's own,
+max|y - y_ref| <= tol * max|y_ref| with both maxima taken over every element of the output.
 """
 import numpy as np
 import pytest
@@ -13,11 +13,11 @@ import torch
 import mamba_selective_scan_03_amd as jscan
 import oracle
 import workloads
-from gpu_util import assert_parity, bits, f64, say
+from gpu_util import GlobalRel, bits, channel_blocks, f64, say
 
 pytestmark = pytest.mark.gpu
 
-
+ORACLE_THREADS = 16
 _INPUTS = {}
 
 
@@ -30,17 +30,11 @@ def inputs_256k():
     return _INPUTS["256k"]
 
 
-def sample_channels(D, seed=0):
-    edges = [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 1023, 1024, D // 2 - 1, D // 2, D - 33, D - 32, D - 2, D - 1]
-    rnd = np.random.default_rng(seed).choice(D, 14, replace=False).tolist()
-    return sorted(set(e for e in edges + rnd if 0 <= e < D))
-
-
-def oracle_on_channels(inp, chans, t1=None):
+def oracle_block(inp, c0, c1, t0=0, t1=None, h0=None):
+    """The oracle over channels [c0, c1) and tokens [t0, t1), from h0 (zero when None)."""
     t1 = inp["x"].shape[1] if t1 is None else t1
-    x = inp["x"][:, :t1, chans]
-    dl = inp["delta"][:, :t1, chans]
-    return oracle.prefill(x, dl, inp["A"][chans], inp["B"][:, :t1], inp["C"][:, :t1])
+    return oracle.prefill(inp["x"][:, t0:t1, c0:c1], inp["delta"][:, t0:t1, c0:c1], inp["A"][c0:c1],
+                          inp["B"][:, t0:t1], inp["C"][:, t0:t1], h0=h0, nthreads=ORACLE_THREADS)
 
 
 def step_chain(d, h, t0, t1):
@@ -50,20 +44,23 @@ def step_chain(d, h, t0, t1):
     return ys
 
 
-def test_prefill_64k_sampled_parity_and_bit_exact_steps():
+@pytest.mark.timeout(900)
+def test_prefill_64k_every_channel_and_bit_exact_steps():
     wl = workloads.get("prefill_64k")
     say("generating prefill_64k inputs")
     inp = workloads.prefill_inputs(wl)
     d = {k: v.cuda() for k, v in inp.items()}
     y, h = jscan.prefill(d["x"], d["delta"], d["A"], d["B"], d["C"])
     torch.cuda.synchronize()
-    chans = sample_channels(wl.D)
-    say(f"oracle on {len(chans)} channels x {wl.L} tokens")
-    y_ref, h_ref = oracle_on_channels(inp, chans)
-    idx = torch.tensor(chans, device="cuda")
-    assert_parity(f64(y.index_select(2, idx)), y_ref, torch.bfloat16, "prefill_64k y (sampled)")
-    assert_parity(f64(h.index_select(1, idx)), h_ref, torch.bfloat16, "prefill_64k h_final (sampled)")
-    assert torch.isfinite(y.float()).all()
+    y_host, h_host = y.cpu(), h.cpu()
+    gy, gh = GlobalRel("prefill_64k y"), GlobalRel("prefill_64k h_final")
+    for c0, c1 in channel_blocks(wl.D, 1024):
+        y_ref, h_ref = oracle_block(inp, c0, c1)
+        gy.add(f64(y_host[:, :, c0:c1]), y_ref)
+        gh.add(f64(h_host[:, c0:c1]), h_ref)
+        say(f"  channels {c0}..{c1 - 1} compared")
+    gy.check(torch.bfloat16)
+    gh.check(torch.bfloat16)
     say("65536 decode steps from the zero state")
     hs = torch.zeros_like(h)
     step_chain(d, hs, 0, wl.L)
@@ -71,28 +68,36 @@ def test_prefill_64k_sampled_parity_and_bit_exact_steps():
     assert torch.equal(bits(hs), bits(h)), "step chain final state differs from prefill (64K)"
 
 
-def test_prefill_256k_sampled_parity_and_step_continuation():
+@pytest.mark.timeout(900)
+def test_prefill_256k_every_channel_and_step_continuation():
     """256K tokens through prefill, then 64 more tokens through jscan_step from the GPU's own
-    final state; the oracle continues its fp64 state over the same 64 tokens."""
+    final state; the oracle continues its own fp64 state over the same 64 tokens.  Every
+    channel of y, of the state after the prefill, of the 64 step outputs and of the final
+    state is compared."""
     wl = workloads.get("prefill_256k")
     inp = inputs_256k()
     d = {k: v.cuda() for k, v in inp.items()}
     L = wl.L
     pre = {k: (v if k == "A" else v[:, :L]) for k, v in d.items()}
     y, h = jscan.prefill(pre["x"], pre["delta"], pre["A"], pre["B"], pre["C"])
+    h_L = h.clone()
+    y_steps = torch.stack(step_chain(d, h, L, L + wl.extra_tokens), 1)
     torch.cuda.synchronize()
-    chans = sample_channels(wl.D, seed=1)
-    say(f"oracle on {len(chans)} channels x {L + wl.extra_tokens} tokens")
-    y_ref_all, h_ref_all = oracle_on_channels(inp, chans)          # all L + 64 tokens
-    _, h_ref_L = oracle_on_channels(inp, chans, t1=L)
-    idx = torch.tensor(chans, device="cuda")
-    assert_parity(f64(y.index_select(2, idx)), y_ref_all[:, :L], torch.bfloat16, "prefill_256k y (sampled)")
-    assert_parity(f64(h.index_select(1, idx)), h_ref_L, torch.bfloat16, "prefill_256k h_final (sampled)")
-    ys = step_chain(d, h, L, L + wl.extra_tokens)
-    y_steps = torch.stack(ys, 1)
-    torch.cuda.synchronize()
-    assert_parity(f64(y_steps.index_select(2, idx)), y_ref_all[:, L:], torch.bfloat16, "256k + 64 step outputs")
-    assert_parity(f64(h.index_select(1, idx)), h_ref_all, torch.bfloat16, "state after 256k + 64 tokens")
+    y_host, hL_host, ys_host, hE_host = y.cpu(), h_L.cpu(), y_steps.cpu(), h.cpu()
+    del y, pre, d
+    gy, gh = GlobalRel("prefill_256k y"), GlobalRel("prefill_256k h_final")
+    gys, ghe = GlobalRel("256k + 64 step outputs"), GlobalRel("state after 256k + 64 tokens")
+    for c0, c1 in channel_blocks(wl.D, 512):
+        y_ref, h_ref = oracle_block(inp, c0, c1, 0, L)
+        gy.add(f64(y_host[:, :, c0:c1]), y_ref)
+        gh.add(f64(hL_host[:, c0:c1]), h_ref)
+        del y_ref
+        ys_ref, hE_ref = oracle_block(inp, c0, c1, L, L + wl.extra_tokens, h0=h_ref)
+        gys.add(f64(ys_host[:, :, c0:c1]), ys_ref)
+        ghe.add(f64(hE_host[:, c0:c1]), hE_ref)
+        say(f"  channels {c0}..{c1 - 1} compared")
+    for g in (gy, gh, gys, ghe):
+        g.check(torch.bfloat16)
 
 
 def test_prefill_256k_matches_resume_split():

@@ -36,6 +36,25 @@ def one_step_close(got, ref, what):
     assert differ <= max(8, ref.size // 200), f"{what}: too many rounding differences ({differ})"
 
 
+def delta_end_to_end_close(delta, d_low, d_low_ref, wts, what):
+    """The GPU's delta against the oracle's own end-to-end delta (computed from the oracle's
+    d_low, not the GPU's).  Where the two d_low differ by a bf16 step, delta's pre-activation
+    W_dt d_low + b_dt moves by at most sum_k |W_dt[d, k]| |d_low[k] - d_low_ref[k]|, and
+    softplus moves by no more than its argument (its slope is below 1).  On top of that each
+    side rounds delta once to bf16 (together at most one bf16 step) and accumulates in fp32
+    (the 2^-16 slack of one_step_close)."""
+    delta = np.asarray(delta, np.float64)
+    w = np.abs(wts["w_dt"].double().numpy())
+    ref = P.delta_from_low(d_low_ref, wts["w_dt"].double().numpy(), wts["b_dt"].numpy())
+    moved = np.abs(np.asarray(d_low, np.float64) - d_low_ref) @ w.T
+    bound = 2.0 ** -7 * np.maximum(np.abs(ref), np.abs(delta)) + moved + 2.0 ** -16 * np.max(np.abs(ref))
+    bad = np.abs(delta - ref) > bound
+    say(f"{what} (end to end): {np.count_nonzero(delta != ref)} of {ref.size} elements differ, "
+        f"{np.count_nonzero(bad)} beyond the bound")
+    assert not bad.any(), f"{what}: {np.count_nonzero(bad)} elements beyond the end-to-end bound"
+    assert np.all(delta > 0) and np.all(np.isfinite(delta))
+
+
 def run(M, D, R, seed=0, rows=None):
     g = torch.Generator().manual_seed(seed)
     x = torch.randn(M, D, generator=g).to(torch.bfloat16)
@@ -53,8 +72,9 @@ def run(M, D, R, seed=0, rows=None):
     one_step_close(f64(d_low)[sel], d_ref, f"{tag} d_low")
     one_step_close(f64(B)[sel], B_ref, f"{tag} B")
     one_step_close(f64(C)[sel], C_ref, f"{tag} C")
+    delta_end_to_end_close(f64(delta)[sel], f64(d_low)[sel], d_ref, wts, f"{tag} delta")
     delta_ref = P.delta_from_low(f64(d_low)[sel], wts["w_dt"].double().numpy(), wts["b_dt"].numpy())
-    one_step_close(f64(delta)[sel], delta_ref, f"{tag} delta (from the GPU's d_low)")
+    one_step_close(f64(delta)[sel], delta_ref, f"{tag} delta (staged: from the GPU's d_low)")
     return x, wts, (delta, B, C, d_low)
 
 
@@ -121,8 +141,9 @@ def test_ssm_inputs_full_size_sampled_rows():
     one_step_close(dl, d_ref, "64K d_low (sampled rows)")
     one_step_close(f64(B.cpu()[idx]), B_ref, "64K B (sampled rows)")
     one_step_close(f64(C.cpu()[idx]), C_ref, "64K C (sampled rows)")
+    delta_end_to_end_close(f64(delta.cpu()[idx]), dl, d_ref, wts, "64K delta (sampled rows)")
     one_step_close(f64(delta.cpu()[idx]), P.delta_from_low(dl, wts["w_dt"].double().numpy(), wts["b_dt"].numpy()),
-                   "64K delta (sampled rows)")
+                   "64K delta (sampled rows, staged: from the GPU's d_low)")
     assert torch.isfinite(delta.float()).all() and float(delta.float().min()) > 0
 
 
@@ -167,3 +188,70 @@ def test_fused_prefill_64k_full_size():
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "fused 64K y differs"
     assert torch.equal(h1.view(torch.int32), h2.view(torch.int32)), "fused 64K h_final differs"
+
+
+def oracle_producer_then_scan(x, wts, A, h0=None, R=256):
+    """The oracle's x -> (delta, B, C) (oracle.producer) -> scan (oracle.prefill), fed nothing
+    the GPU computed.  x [batch, L, D] bf16."""
+    batch, L, D = x.shape
+    ds, Bs, Cs = [], [], []
+    for b in range(batch):
+        _, B_ref, C_ref, delta_ref = P.ssm_inputs(x[b].double().numpy(), wts["w_x"].double().numpy(),
+                                                  wts["g_d"].numpy(), wts["g_b"].numpy(), wts["g_c"].numpy(),
+                                                  wts["w_dt"].double().numpy(), wts["b_dt"].numpy(), EPS, R)
+        ds.append(delta_ref)
+        Bs.append(B_ref)
+        Cs.append(C_ref)
+    return oracle.prefill(x.double().numpy(), np.stack(ds), A.double().numpy(), np.stack(Bs), np.stack(Cs),
+                          h0=None if h0 is None else h0.double().numpy(), nthreads=16)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("batch,L,D,with_h0", [(1, 4096, 8192, False), (2, 300, 1024, True), (1, 63, 128, True)])
+def test_fused_prefill_against_oracle(batch, L, D, with_h0):
+    """x -> jscan_ssm_inputs (x projection only) -> jscan_prefill_fused (delta's projection,
+    bias and softplus inside the scan) against the oracle's producer followed by the oracle's
+    scan on the same x, at the bf16 tolerance."""
+    inp = workloads.small_prefill(batch, L, D, "bf16", seed=L + 3 * D)
+    wts = workloads.producer_weights(D, 256, seed=D + 1)
+    dev = {k: v.cuda() for k, v in wts.items()}
+    x, A = inp["x"].cuda(), inp["A"].cuda()
+    h0 = (torch.randn(batch, D, 16, generator=torch.Generator().manual_seed(2)) * 0.1) if with_h0 else None
+    _, B, C, d_low = jscan.ssm_inputs(x, dev["w_x"], dev["g_d"], dev["g_b"], dev["g_c"], dev["w_dt"], dev["b_dt"],
+                                      eps=EPS, skip_delta=True)
+    y, h = jscan.prefill_fused(x, d_low, dev["w_dt"], dev["b_dt"], A, B, C, h0=None if h0 is None else h0.cuda())
+    torch.cuda.synchronize()
+    say(f"fused {batch}x{L}x{D} h0={with_h0} against the oracle's producer + scan")
+    y_ref, h_ref = oracle_producer_then_scan(inp["x"], wts, inp["A"], h0)
+    assert_parity(f64(y), y_ref, torch.bfloat16, f"fused {batch}x{L}x{D} y")
+    assert_parity(f64(h), h_ref, torch.bfloat16, f"fused {batch}x{L}x{D} h_final")
+
+
+@pytest.mark.timeout(900)
+def test_fused_prefill_64k_against_oracle_sampled_channels():
+    """The 64K x 8192 workload's x through the x projection and the fused scan, in the launch
+    configuration the benchmark times (bench.py --producer --fused), against the oracle's
+    producer and scan: the oracle projects every token (B and C are shared by all channels)
+    and scans sampled channels over all 65536 tokens."""
+    wl = workloads.get("prefill_64k")
+    say("generating prefill_64k x, A")
+    inp = workloads.prefill_inputs(wl)
+    wts = workloads.producer_weights(wl.D, 256)
+    dev = {k: v.cuda() for k, v in wts.items()}
+    x, A = inp["x"].cuda(), inp["A"].cuda()
+    _, B, C, d_low = jscan.ssm_inputs(x, dev["w_x"], dev["g_d"], dev["g_b"], dev["g_c"], dev["w_dt"], dev["b_dt"],
+                                      eps=EPS, skip_delta=True)
+    y, h = jscan.prefill_fused(x, d_low, dev["w_dt"], dev["b_dt"], A, B, C)
+    torch.cuda.synchronize()
+    chans = sorted(set([0, 1, 15, 16, 31, 32, 4095, 4096, 8190, 8191] +
+                       np.random.default_rng(4).choice(wl.D, 14, replace=False).tolist()))
+    say("oracle producer over 65536 tokens")
+    dl_ref, B_ref, C_ref = P.ssm_inputs_low(inp["x"][0].double().numpy(), wts["w_x"].double().numpy(),
+                                            wts["g_d"].numpy(), wts["g_b"].numpy(), wts["g_c"].numpy(), EPS, 256)
+    delta_ref = P.delta_from_low(dl_ref, wts["w_dt"][chans].double().numpy(), wts["b_dt"][chans].numpy())
+    say(f"oracle scan on {len(chans)} channels x {wl.L} tokens")
+    y_ref, h_ref = oracle.prefill(inp["x"][:, :, chans], delta_ref[None], inp["A"][chans], B_ref[None], C_ref[None],
+                                  nthreads=16)
+    idx = torch.tensor(chans, device="cuda")
+    assert_parity(f64(y.index_select(2, idx)), y_ref, torch.bfloat16, "fused 64K y (sampled channels)")
+    assert_parity(f64(h.index_select(1, idx)), h_ref, torch.bfloat16, "fused 64K h_final (sampled channels)")
