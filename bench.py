@@ -223,20 +223,34 @@ def run_micro(log):
     hz = ghz * 1e9
 
     def cycles_per_instr(kind, waves_per_simd, iters, per_trip=16):
-        threads = 256 if waves_per_simd >= 4 else 64
-        blocks = simds * waves_per_simd * 64 // threads
-        ms, _, _ = micro.valu(kind, iters, blocks, threads)
+        # work-groups of 4 waves, one per SIMD of a CU; waves_per_simd work-groups per CU
+        blocks = cus * waves_per_simd
+        ms, _, _ = micro.valu(kind, iters, blocks, 256)
         instr_per_simd = waves_per_simd * iters * per_trip
         return ms * 1e-3 * hz / instr_per_simd
 
+    # where the waves of a 256-work-group launch land: at most this many share a SIMD
+    out["max_waves_per_simd_1w"] = micro.valu(0, 1000, cus, 256, placement=True)[3]
+    out["max_waves_per_simd_2w"] = micro.valu(0, 1000, 2 * cus, 256, placement=True)[3]
     valu = {}
     for kind, name in micro.VALU_KINDS.items():
         row = {}
-        for w, iters in ((8, 20000), (1, 160000)):
+        for w, iters in ((8, 20000), (4, 40000), (2, 80000), (1, 80000)):
+            if w in (2, 4) and kind not in (0, 1, 10):
+                continue
             row[f"cycles_per_instr_{w}w"] = round(cycles_per_instr(kind, w, iters), 3)
         valu[name] = row
         log(f"micro valu {name}: {row}")
     out["valu_cycles_per_wave_instruction"] = valu
+    # the scan's token body for a lane of two states: cycles per token per wave
+    body = {}
+    for kind, name in ((8, "sgpr_bc"), (9, "dpp_bc")):
+        row = {}
+        for w in (1, 2, 4, 8):
+            row[f"cycles_per_token_{w}w"] = round(cycles_per_instr(kind, w, 160000 // w, per_trip=4), 2)
+        body[name] = row
+        log(f"micro scan body {name}: {row}")
+    out["scan_token_body_cycles"] = body
     c_fma = valu["fma"]["cycles_per_instr_8w"]
     c_exp = valu["exp"]["cycles_per_instr_8w"]
     mix = valu["exp8+fma8"]["cycles_per_instr_8w"] * 16
@@ -255,29 +269,47 @@ def run_micro(log):
         "valu_lane_slots_per_s": round(cus * 4 * 64 * hz / c_fma, -9),
     }
 
-    # matrix cores beside the vector ALU: 4 waves per SIMD
-    mf_iters = 16000
-    t = [micro.mfma_valu(m, mf_iters, 1024, 256) for m in (0, 1, 2)]
-    out["mfma_beside_valu"] = {"mfma_only_ms": round(t[0], 3), "valu_only_ms": round(t[1], 3),
-                               "both_ms": round(t[2], 3),
-                               "overlap": round((t[0] + t[1] - t[2]) / min(t[0], t[1]), 3),
-                               "mfma_16x16x4_f32_cycles": round(t[0] * 1e-3 * hz / (4 * mf_iters * 4), 2)}
-    log(f"micro mfma beside valu: {out['mfma_beside_valu']}")
+    # matrix cores beside the vector ALU: 4 waves per SIMD, then one wave per SIMD
+    mf = {}
+    for label, blocks, threads, iters in (("4w", 1024, 256, 16000), ("1w", 256, 256, 64000)):
+        waves = blocks * threads // 64 / simds
+        t = [micro.mfma_valu(m, iters, blocks, threads) for m in (0, 1, 2, 3, 4)]
+        mf[label] = {"mfma_only_ms": round(t[0], 3), "valu_only_ms": round(t[1], 3), "both_ms": round(t[2], 3),
+                     "overlap": round((t[0] + t[1] - t[2]) / min(t[0], t[1]), 3),
+                     "mfma_16x16x4_f32_cycles": round(t[0] * 1e-3 * hz / (waves * iters * 4), 2),
+                     "fma_cycles": round(t[1] * 1e-3 * hz / (waves * iters * 32), 2),
+                     "bf16_mfma_only_ms": round(t[3], 3), "bf16_both_ms": round(t[4], 3),
+                     "bf16_overlap": round((t[3] + t[1] - t[4]) / min(t[3], t[1]), 3),
+                     "mfma_16x16x32_bf16_cycles": round(t[3] * 1e-3 * hz / (waves * iters * 4), 2)}
+    out["mfma_beside_valu"] = mf
+    log(f"micro mfma beside valu: {mf}")
 
     g = torch.Generator().manual_seed(0)
-    a = torch.randn(64, generator=g).cuda()
-    b = torch.randn(64, generator=g).cuda()
-    c = (torch.randn(256, generator=g) * 4).cuda()
-    d1, d2 = micro.mfma_rounding(a, b, c)
-    diff = int((d1.view(torch.int32) != d2.view(torch.int32)).sum())
-    near = float(((d1 - d2).abs() / d2.abs().clamp_min(1e-30)).max())
-    out["mfma_4x4x1_f32_vs_fmaf"] = {"values": 256, "bitwise_differences": diff, "max_rel_diff": near}
-    log(f"micro mfma rounding: {out['mfma_4x4x1_f32_vs_fmaf']}")
+    rnd = {}
+    for variant, name in ((0, "4x4x1_16b"), (1, "16x16x4_onehot")):
+        a = torch.randn(64, generator=g)
+        b = torch.randn(64, generator=g)
+        c = torch.randn(256, generator=g) * 4
+        if variant == 1:
+            # A[i][k] (lane i + 16 k) nonzero only for k = i % 4: one product per output
+            lane = torch.arange(64)
+            a = torch.where(lane // 16 == (lane % 16) % 4, a, torch.zeros(()))
+        d1, d2 = micro.mfma_rounding(variant, a.cuda(), b.cuda(), c.cuda())
+        diff = int((d1.view(torch.int32) != d2.view(torch.int32)).sum())
+        rel = float(((d1 - d2).abs() / d2.abs().clamp_min(1e-30)).max())
+        rnd[name] = {"values": 256, "bitwise_differences": diff, "max_rel_diff": rel}
+    out["mfma_f32_vs_fmaf"] = rnd
+    log(f"micro mfma rounding: {rnd}")
 
     iters = 20000
-    ms = micro.lds(iters, 2048, 256)
-    out["lds_read_bytes_per_CU_clock"] = round(2048 * 256 * iters * 128 / (ms * 1e-3 * hz) / cus, 1)
-    log(f"micro lds: {out['lds_read_bytes_per_CU_clock']} B/clk/CU")
+    lds = {}
+    for unique in (64, 32, 16):
+        ms = micro.lds(iters, 2048, 256, unique)
+        # bytes the lanes asked for, and wave instructions per CU clock
+        lds[f"unique{unique}"] = {"requested_bytes_per_CU_clock": round(2048 * 256 * iters * 128 / (ms * 1e-3 * hz) / cus, 1),
+                                  "b128_reads_per_CU_clock": round(2048 * 4 * iters * 8 / (ms * 1e-3 * hz) / cus, 3)}
+    out["lds_read"] = lds
+    log(f"micro lds: {lds}")
 
     nbytes = 1 << 30
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")

@@ -11,6 +11,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csrc", "jscan.hip")
 LIB = os.path.join(HERE, "libjscan.so")
+# the microbenchmarks of the chip's ALU, matrix-core, LDS and HBM rates (measurement only)
+MICRO_SRC = os.path.join(HERE, "csrc", "micro.hip")
+MICRO_LIB = os.path.join(HERE, "libjscan_micro.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -25,10 +28,9 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library (always recompiles) and return its path."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-o", tmp, SRC]
+def _compile(src: str, lib: str, verbose: bool) -> str:
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-o", tmp, src]
     res = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the device-only target feature; that note is harmless
     noise = "is not a recognized feature for this target"
@@ -37,8 +39,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library and the microbenchmark library (always recompiles); returns the
+    library's path."""
+    _compile(MICRO_SRC, MICRO_LIB, verbose)
+    return _compile(SRC, LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -35,6 +35,29 @@ def test_header_symbols_are_exported():
         assert hasattr(lib, n), n
 
 
+def test_micro_header_symbols_are_exported():
+    """include/jscan_micro.h (the microbenchmarks) against libjscan_micro.so, and their argument
+    checks, which return -1 before any launch."""
+    from mamba_selective_scan_03_amd import micro
+
+    text = open(os.path.join(ROOT, "include", "jscan_micro.h")).read()
+    names = sorted(set(re.findall(r"^\s*int\s+(jscan_micro_\w+)\s*\(", text, re.M)))
+    assert names == ["jscan_micro_hbm", "jscan_micro_lds", "jscan_micro_mfma_rounding", "jscan_micro_mfma_valu",
+                     "jscan_micro_valu"]
+    lib = micro.library()
+    for n in names:
+        assert hasattr(lib, n), n
+    ms = ctypes.c_float()
+    assert lib.jscan_micro_valu(99, 10, 1, 64, P, None, ctypes.byref(ms)) == -1
+    assert lib.jscan_micro_valu(0, 10, 1, 96, P, None, ctypes.byref(ms)) == -1
+    assert lib.jscan_micro_mfma_valu(0, 10, 1, 1024, P, None, ctypes.byref(ms)) == -1
+    assert lib.jscan_micro_mfma_rounding(2, P, P, P, P, P, None) == -1
+    assert lib.jscan_micro_lds(10, 8, 1, 64, P, None, ctypes.byref(ms)) == -1
+    assert lib.jscan_micro_hbm(0, 0, P, P, 1000, 1, 1, P, None, ctypes.byref(ms)) == -1
+    assert lib.jscan_micro_hbm(1, 0, P, P + 4, 16384, 1, 1, P, None, ctypes.byref(ms)) == -1
+
+
+
 def test_status_strings_and_version():
     lib = jscan.library()
     for s in range(9):
