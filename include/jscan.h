@@ -373,6 +373,30 @@ jscan_status jscan_step_mimo_trapezoid(float *h, const void *x_prev, const void 
                                        int64_t ld_d, int64_t ld_bc, jscan_a_form a_form,
                                        jscan_dtype dtype, void *stream);
 
+/*
+ * jscan_prefill_chunked without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  It runs the same three passes on the same kernels, with the segment states and
+ * delta sums in a library-owned scratch array of JSCAN_NOALLOC_SCRATCH_BYTES in each GPU's
+ * memory (a static device array, held until the process ends).  The call itself allocates
+ * nothing; the first call on a device looks up that device's copy of the array once.
+ *   - A shape and chunk whose jscan_prefill_chunked_workspace(...) exceeds
+ *     JSCAN_NOALLOC_SCRATCH_BYTES returns JSCAN_ERR_WORKSPACE and launches nothing (8 MiB
+ *     holds every automatic plan of the row-mapped kernel, about 560 KiB, and of the lane
+ *     kernel, about 4.4 MiB; explicit chunks of batch * n_seg * D * 68 bytes up to 8 MiB).
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap in time on one GPU
+ *     (from different streams or threads, or an unordered graph) race and give wrong results.
+ *     Order them on one stream.  The array's contents on entry do not matter (every element
+ *     the passes read was written earlier in the same call).
+ * The other arguments, the results and the errors are those of jscan_prefill_chunked; a
+ * failure to look up the array returns JSCAN_ERR_HIP.
+ */
+#define JSCAN_NOALLOC_SCRATCH_BYTES (8 * 1024 * 1024)
+jscan_status jscan_prefill_chunked_noalloc(const void *x, const void *delta, const float *A,
+                                           const void *B, const void *C, const float *h0, void *y,
+                                           float *h_final, int64_t batch, int64_t L, int64_t D,
+                                           int64_t N, int64_t chunk, jscan_dtype dtype, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *jscan_status_string(jscan_status s);
 

@@ -30,6 +30,7 @@ from ._binding import (  # noqa: F401
     library_path,
     prefill,
     prefill_chunked,
+    prefill_chunked_noalloc,
     prefill_complex,
     prefill_fused,
     prefill_mimo,

@@ -44,6 +44,8 @@ def library():
     lib.jscan_step.argtypes = [fp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
     lib.jscan_prefill_chunked.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, i64, vp, i64, i32, vp]
     lib.jscan_prefill_chunked_workspace.argtypes = [i64, i64, i64, i64, i64]
+    lib.jscan_prefill_chunked_noalloc.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, i64, i32, vp]
+    lib.jscan_prefill_chunked_noalloc.restype = i32
     lib.jscan_ssm_inputs.argtypes = [vp, vp, fp, fp, fp, vp, fp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, i32,
                                      vp]
     lib.jscan_ssm_inputs.restype = i32
@@ -196,6 +198,27 @@ def prefill_chunked(x, delta, A, B, C, h0=None, y=None, h_final=None, chunk=0, w
         st = lib.jscan_prefill_chunked(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(h0), _ptr(y),
                                        _ptr(h_final), batch, L, D, D_STATE, chunk, _ptr(workspace), ws_bytes,
                                        _DTYPES[x.dtype], _stream(x.device))
+    _check(st)
+    return y, h_final
+
+
+NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024   # JSCAN_NOALLOC_SCRATCH_BYTES
+
+
+def prefill_chunked_noalloc(x, delta, A, B, C, h0=None, y=None, h_final=None, chunk=0):
+    """:func:`prefill_chunked` through ``jscan_prefill_chunked_noalloc``: the library's own
+    scratch array instead of a workspace (calls on one GPU must not overlap in time).  Pass
+    ``y`` and ``h_final`` to allocate nothing here either."""
+    batch, L, D = _check_prefill_args(x, delta, A, B, C, h0)
+    if y is None:
+        y = torch.empty_like(x)
+    if h_final is None:
+        h_final = torch.empty((batch, D, D_STATE), dtype=torch.float32, device=x.device)
+    lib = library()
+    with torch.cuda.device(x.device):
+        st = lib.jscan_prefill_chunked_noalloc(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(h0), _ptr(y),
+                                               _ptr(h_final), batch, L, D, D_STATE, chunk, _DTYPES[x.dtype],
+                                               _stream(x.device))
     _check(st)
     return y, h_final
 

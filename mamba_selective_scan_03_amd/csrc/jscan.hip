@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/jscan.h"
 #include "prefill_lane_kernel.h"
 #include "prefill_rows_kernel.h"
@@ -430,6 +432,49 @@ jscan_status launch_chunked(const void *x, const void *delta, const float *A, co
     return launch_status();
 }
 
+// ---- the time-parallel prefill's library-owned scratch -----------------------------------
+// One array per GPU for jscan_prefill_chunked_noalloc.  Host code never passes `scratch`
+// itself to a kernel (on the host the name only stands for the symbol); it looks up each
+// device's address once with hipGetSymbolAddress and uses that.
+static __device__ __align__(256) unsigned char scratch[JSCAN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the device that owns `stream` (the current device for NULL).
+jscan_status scratch_on_stream_device(hipStream_t stream, void **out) {
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        g_last_hip_error = static_cast<int>(e);
+        return JSCAN_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        g_last_hip_error = static_cast<int>(hipErrorInvalidDevice);
+        return JSCAN_ERR_HIP;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        e = hipGetDevice(&cur);
+        if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+        void *p = nullptr;
+        if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        if (e != hipSuccess || !p) {
+            g_last_hip_error = static_cast<int>(e != hipSuccess ? e : hipErrorInvalidSymbol);
+            return JSCAN_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return JSCAN_OK;
+}
+
 // ---- producer side: delta, B and C from x ---------------------------------------------
 
 template <int R>
@@ -600,6 +645,28 @@ jscan_status jscan_prefill_chunked(const void *x, const void *delta, const float
     if (dtype == JSCAN_BF16)
         return launch_chunked<jscan::BF16>(x, delta, A, B, C, h0, y, h_final, batch, L, D, p, workspace, s);
     return launch_chunked<jscan::F32>(x, delta, A, B, C, h0, y, h_final, batch, L, D, p, workspace, s);
+}
+
+jscan_status jscan_prefill_chunked_noalloc(const void *x, const void *delta, const float *A, const void *B,
+                                           const void *C, const float *h0, void *y, float *h_final, int64_t batch,
+                                           int64_t L, int64_t D, int64_t N, int64_t chunk, jscan_dtype dtype,
+                                           void *stream) {
+    bool empty = false;
+    jscan_status st = check_prefill(x, delta, A, B, C, h0, false, y, h_final, batch, L, D, N, dtype, &empty);
+    if (st != JSCAN_OK) return st;
+    if (chunk < 0) return JSCAN_ERR_SHAPE;
+    if (empty) return JSCAN_OK;
+    const ChunkPlan p = plan_chunks(batch, L, D, chunk);
+    if (p.n_seg <= 1) return prefill_impl(x, delta, A, B, C, h0, false, y, h_final, batch, L, D, N, dtype, stream);
+    if (batch * p.n_seg > (1 << 24) || batch * p.n_seg * ((D + 63) / 64) > kMaxBlocks) return JSCAN_ERR_SHAPE;
+    if (chunk_workspace_bytes(p, batch, D) > JSCAN_NOALLOC_SCRATCH_BYTES) return JSCAN_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void *ws = nullptr;
+    st = scratch_on_stream_device(s, &ws);
+    if (st != JSCAN_OK) return st;
+    if (dtype == JSCAN_BF16)
+        return launch_chunked<jscan::BF16>(x, delta, A, B, C, h0, y, h_final, batch, L, D, p, ws, s);
+    return launch_chunked<jscan::F32>(x, delta, A, B, C, h0, y, h_final, batch, L, D, p, ws, s);
 }
 
 jscan_status jscan_step(float *h, const void *x_t, const void *delta_t, const float *A,

@@ -30,7 +30,7 @@ def test_header_symbols_are_exported():
             "jscan_prefill_chunked_workspace", "jscan_ssm_inputs", "jscan_prefill_fused", "jscan_prefill_scalar_a",
             "jscan_step_scalar_a", "jscan_prefill_complex", "jscan_step_complex", "jscan_prefill_trapezoid",
             "jscan_step_trapezoid", "jscan_prefill_mimo", "jscan_step_mimo", "jscan_prefill_mimo_trapezoid",
-            "jscan_step_mimo_trapezoid"} <= set(names)
+            "jscan_step_mimo_trapezoid", "jscan_prefill_chunked_noalloc"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -56,6 +56,26 @@ def test_micro_header_symbols_are_exported():
     assert lib.jscan_micro_hbm(0, 0, P, P, 1000, 1, 1, P, None, ctypes.byref(ms)) == -1
     assert lib.jscan_micro_hbm(1, 0, P, P + 4, 16384, 1, 1, P, None, ctypes.byref(ms)) == -1
 
+
+def noalloc(**kw):
+    a = dict(x=P, d=P + 0x100000, A=P + 0x200000, B=P + 0x300000, C=P + 0x400000, h0=None, y=P + 0x500000,
+             h=P + 0x600000, batch=1, L=4096, D=64, N=16, chunk=256, dtype=BF16)
+    a.update(kw)
+    return jscan.library().jscan_prefill_chunked_noalloc(a["x"], a["d"], a["A"], a["B"], a["C"], a["h0"], a["y"],
+                                                         a["h"], a["batch"], a["L"], a["D"], a["N"], a["chunk"],
+                                                         a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), EDTYPE), (dict(N=8), ESHAPE), (dict(D=20), ESHAPE), (dict(chunk=-1), ESHAPE),
+    (dict(x=None), ENULL), (dict(y=P + 0x100000), EALIAS), (dict(h=P + 0x200000), EALIAS),
+    # 16 segments x 8192 channels x 68 bytes exceed the 8 MiB scratch: refused before any launch
+    (dict(L=8192, D=8192, chunk=512, x=P, d=P + 0x8000000, A=P + 0x10000000, B=P + 0x10100000,
+          C=P + 0x10200000, y=P + 0x10300000, h=P + 0x18300000), EWORKSPACE),
+    (dict(batch=0), OK),
+])
+def test_chunked_noalloc_validation(kw, code):
+    assert noalloc(**kw) == code
 
 
 def test_status_strings_and_version():
