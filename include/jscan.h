@@ -122,7 +122,9 @@ jscan_status jscan_prefill_resume(const void *x, const void *delta, const float 
  * segments start from composed states whose rounding differs from the token-by-token walk,
  * so their y and h_final agree with it to within fp32 rounding of the composition, not bit
  * for bit.  Results are deterministic (no atomics; fixed summation orders).
- *   chunk      tokens per segment; 0 picks a length that fills the GPU.  When it yields a
+ *   chunk      tokens per segment; 0 picks enough segments for four waves per SIMD (262144
+ *              segment-channel lanes, segments of at least 256 tokens), or one segment when
+ *              batch * D already fills the GPU (at least 8192 channels, D a multiple of 32).  When it yields a
  *              single segment the call is exactly jscan_prefill_resume (and needs no
  *              workspace).
  *   workspace  device memory of at least jscan_prefill_chunked_workspace(...) bytes,
@@ -381,9 +383,9 @@ jscan_status jscan_step_mimo_trapezoid(float *h, const void *x_prev, const void 
  * memory (a static device array, held until the process ends).  The call itself allocates
  * nothing; the first call on a device looks up that device's copy of the array once.
  *   - A shape and chunk whose jscan_prefill_chunked_workspace(...) exceeds
- *     JSCAN_NOALLOC_SCRATCH_BYTES returns JSCAN_ERR_WORKSPACE and launches nothing (8 MiB
- *     holds every automatic plan of the row-mapped kernel, about 560 KiB, and of the lane
- *     kernel, about 4.4 MiB; explicit chunks of batch * n_seg * D * 68 bytes up to 8 MiB).
+ *     JSCAN_NOALLOC_SCRATCH_BYTES returns JSCAN_ERR_WORKSPACE and launches nothing (24 MiB
+ *     holds every automatic plan, which needs at most 262144 * 68 bytes = 17 MiB; explicit
+ *     chunks need batch * n_seg * D * 68 bytes).
  *   - Every call on one GPU uses that GPU's one array: calls that overlap in time on one GPU
  *     (from different streams or threads, or an unordered graph) race and give wrong results.
  *     Order them on one stream.  The array's contents on entry do not matter (every element
@@ -391,7 +393,7 @@ jscan_status jscan_step_mimo_trapezoid(float *h, const void *x_prev, const void 
  * The other arguments, the results and the errors are those of jscan_prefill_chunked; a
  * failure to look up the array returns JSCAN_ERR_HIP.
  */
-#define JSCAN_NOALLOC_SCRATCH_BYTES (8 * 1024 * 1024)
+#define JSCAN_NOALLOC_SCRATCH_BYTES (24 * 1024 * 1024)
 jscan_status jscan_prefill_chunked_noalloc(const void *x, const void *delta, const float *A,
                                            const void *B, const void *C, const float *h0, void *y,
                                            float *h_final, int64_t batch, int64_t L, int64_t D,

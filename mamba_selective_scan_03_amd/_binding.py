@@ -202,7 +202,7 @@ def prefill_chunked(x, delta, A, B, C, h0=None, y=None, h_final=None, chunk=0, w
     return y, h_final
 
 
-NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024   # JSCAN_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 24 * 1024 * 1024   # JSCAN_NOALLOC_SCRATCH_BYTES
 
 
 def prefill_chunked_noalloc(x, delta, A, B, C, h0=None, y=None, h_final=None, chunk=0):

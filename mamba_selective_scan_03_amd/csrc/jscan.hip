@@ -10,6 +10,7 @@
 #include "prefill_lane_kernel.h"
 #include "prefill_rows_kernel.h"
 #include "chunk_carry_kernel.h"
+#include "prefill_seg_lane_kernel.h"
 #include "project_kernels.h"
 #include "step_kernel.h"
 #include "mimo_kernels.h"
@@ -380,10 +381,12 @@ struct ChunkPlan {
     int64_t n_seg = 1;
 };
 
-// Segments of `chunk` tokens, or (chunk == 0) as many segments as it takes for the rows of
-// all segments to fill the GPU once: 8192 channels for the row-mapped kernel (256
-// work-groups of 32 channels, one per CU), 65536 for the lane kernel (one wave per SIMD).
-// Automatic segments are at least 256 tokens long and a multiple of the 64-token tile.
+// Segments of `chunk` tokens, or (chunk == 0) as many as it takes to give the segment-lane
+// kernel kSegLanes (segment, channel) lanes, four waves on each of the 1024 SIMDs, when the
+// sequences' channels are too few for the token-by-token kernel to fill the GPU (fewer than
+// 8192 channels, or D not a multiple of 32).  Automatic segments are at least 256 tokens long
+// and a multiple of 64.
+constexpr int64_t kSegLanes = (int64_t)1024 * jscan::seglane::kWavesPerSimd * 64;
 ChunkPlan plan_chunks(int64_t batch, int64_t L, int64_t D, int64_t chunk) {
     ChunkPlan p;
     p.seg_len = L;
@@ -392,16 +395,23 @@ ChunkPlan plan_chunks(int64_t batch, int64_t L, int64_t D, int64_t chunk) {
         p.seg_len = chunk < L ? chunk : L;
     } else {
         const int64_t channels = batch * D;
-        const int64_t target = (D % jscan::rows::kCh == 0) ? 8192 : 65536;
-        int64_t n = channels >= target ? 1 : target / channels;
+        const bool filled = channels >= 8192 && D % jscan::rows::kCh == 0;
+        int64_t n = (filled || channels >= kSegLanes) ? 1 : kSegLanes / channels;
         const int64_t by_length = L / 256 > 1 ? L / 256 : 1;
         if (n > by_length) n = by_length;
         p.seg_len = (L + n - 1) / n;
-        p.seg_len = (p.seg_len + jscan::rows::kT - 1) / jscan::rows::kT * jscan::rows::kT;
+        p.seg_len = (p.seg_len + 63) / 64 * 64;
         if (p.seg_len > L) p.seg_len = L;
     }
     p.n_seg = (L + p.seg_len - 1) / p.seg_len;
     return p;
+}
+
+// Whether the plan's grids fit the launchers: segment rows and scan work-groups, the carry
+// pass's work-groups of carry::kPairs (channel, state) pairs, and 32-bit token indexes.
+bool chunk_grids_fit(int64_t batch, int64_t D, const ChunkPlan &p) {
+    return batch * p.n_seg <= (1 << 24) && batch * p.n_seg * ((D + 63) / 64) <= kMaxBlocks &&
+           batch * D * JSCAN_D_STATE / jscan::carry::kPairs <= kMaxBlocks && p.seg_len < ((int64_t)1 << 31);
 }
 
 // Workspace bytes of a plan: h_loc / h_in [batch * n_seg][D][N] and delta sums [batch * n_seg][D].
@@ -417,18 +427,27 @@ jscan_status launch_chunked(const void *x, const void *delta, const float *A, co
     float *hbuf = static_cast<float *>(workspace);
     float *dsum = hbuf + batch * p.n_seg * D * jscan::kDState;
     const int64_t nrows = batch * p.n_seg;
+    using T = typename E::store_t;
+    const T *xt = static_cast<const T *>(x), *dt = static_cast<const T *>(delta);
+    const T *bt = static_cast<const T *>(B), *ct = static_cast<const T *>(C);
     // 1. every segment from zero: end states into hbuf, delta sums into dsum (no y)
     const jscan::Segments each{L, p.seg_len, (int)p.n_seg, 0};
-    launch_rows<E, true>(x, delta, A, B, C, nullptr, y, hbuf, dsum, each, nrows, D, stream);
+    jscan::launch_prefill_seg_lane<E, true, true>(xt, dt, A, bt, ct, nullptr, nullptr, hbuf, dsum, each, nrows,
+                                                  (int)D, stream);
     if (launch_status() != JSCAN_OK) return JSCAN_ERR_HIP;
     // 2. starting state of every segment, in place in hbuf
     const int64_t count = batch * D * jscan::kDState;
-    hipLaunchKernelGGL(jscan::chunk_carry_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream, hbuf,
-                       dsum, A, h0, count, (int)D, (int)p.n_seg);
+    jscan::launch_chunk_carry(hbuf, dsum, A, h0, count, (int)D, (int)p.n_seg, stream);
     if (launch_status() != JSCAN_OK) return JSCAN_ERR_HIP;
     // 3. every segment again from its starting state: y, and h_final from the last segments
     const jscan::Segments again{L, p.seg_len, (int)p.n_seg, 1};
-    launch_rows<E, false>(x, delta, A, B, C, hbuf, y, h_final, nullptr, again, nrows, D, stream);
+    // y summed in the order the sequential prefill uses for this D, so segment 0 matches it
+    if (jscan::rows_kernel_applies(batch, D))
+        jscan::launch_prefill_seg_lane<E, false, true>(xt, dt, A, bt, ct, hbuf, static_cast<T *>(y), h_final,
+                                                       nullptr, again, nrows, (int)D, stream);
+    else
+        jscan::launch_prefill_seg_lane<E, false, false>(xt, dt, A, bt, ct, hbuf, static_cast<T *>(y), h_final,
+                                                        nullptr, again, nrows, (int)D, stream);
     return launch_status();
 }
 
@@ -614,7 +633,7 @@ int64_t jscan_prefill_chunked_workspace(int64_t batch, int64_t L, int64_t D, int
     if (batch < 0 || L < 0 || D < 0 || N != JSCAN_D_STATE || D % 8 != 0 || chunk < 0) return -1;
     if (D > (1 << 24) || batch > (1 << 20)) return -1;
     const ChunkPlan p = plan_chunks(batch, L, D, chunk);
-    if (batch * p.n_seg > (1 << 24) || batch * p.n_seg * ((D + 63) / 64) > kMaxBlocks) return -1;
+    if (!chunk_grids_fit(batch, D, p)) return -1;
     return chunk_workspace_bytes(p, batch, D);
 }
 
@@ -629,7 +648,7 @@ jscan_status jscan_prefill_chunked(const void *x, const void *delta, const float
     if (empty) return JSCAN_OK;
     const ChunkPlan p = plan_chunks(batch, L, D, chunk);
     if (p.n_seg <= 1) return prefill_impl(x, delta, A, B, C, h0, false, y, h_final, batch, L, D, N, dtype, stream);
-    if (batch * p.n_seg > (1 << 24) || batch * p.n_seg * ((D + 63) / 64) > kMaxBlocks) return JSCAN_ERR_SHAPE;
+    if (!chunk_grids_fit(batch, D, p)) return JSCAN_ERR_SHAPE;
     const int64_t need = chunk_workspace_bytes(p, batch, D);
     if (!workspace) return JSCAN_ERR_NULL;
     if (workspace_bytes < need) return JSCAN_ERR_WORKSPACE;
@@ -658,7 +677,7 @@ jscan_status jscan_prefill_chunked_noalloc(const void *x, const void *delta, con
     if (empty) return JSCAN_OK;
     const ChunkPlan p = plan_chunks(batch, L, D, chunk);
     if (p.n_seg <= 1) return prefill_impl(x, delta, A, B, C, h0, false, y, h_final, batch, L, D, N, dtype, stream);
-    if (batch * p.n_seg > (1 << 24) || batch * p.n_seg * ((D + 63) / 64) > kMaxBlocks) return JSCAN_ERR_SHAPE;
+    if (!chunk_grids_fit(batch, D, p)) return JSCAN_ERR_SHAPE;
     if (chunk_workspace_bytes(p, batch, D) > JSCAN_NOALLOC_SCRATCH_BYTES) return JSCAN_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     void *ws = nullptr;

@@ -69,9 +69,9 @@ def noalloc(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=5), EDTYPE), (dict(N=8), ESHAPE), (dict(D=20), ESHAPE), (dict(chunk=-1), ESHAPE),
     (dict(x=None), ENULL), (dict(y=P + 0x100000), EALIAS), (dict(h=P + 0x200000), EALIAS),
-    # 16 segments x 8192 channels x 68 bytes exceed the 8 MiB scratch: refused before any launch
-    (dict(L=8192, D=8192, chunk=512, x=P, d=P + 0x8000000, A=P + 0x10000000, B=P + 0x10100000,
-          C=P + 0x10200000, y=P + 0x10300000, h=P + 0x18300000), EWORKSPACE),
+    # 64 segments x 8192 channels x 68 bytes exceed the 24 MiB scratch: refused before any launch
+    (dict(L=16384, D=8192, chunk=256, x=P, d=P + 0x10000000, A=P + 0x20000000, B=P + 0x20100000,
+          C=P + 0x20200000, y=P + 0x20300000, h=P + 0x30300000), EWORKSPACE),
     (dict(batch=0), OK),
 ])
 def test_chunked_noalloc_validation(kw, code):
@@ -185,11 +185,13 @@ def chunked(x=P, d=P + 0x100000, A=P + 0x200000, B=P + 0x300000, C=P + 0x400000,
 
 def test_chunked_workspace_sizes():
     ws = jscan.library().jscan_prefill_chunked_workspace
-    # automatic chunking of one sequence of 1024 channels: 8 segments fill 256 work-groups
-    assert ws(1, 65536, 1024, 16, 0) == 8 * 1024 * 17 * 4
+    # automatic chunking of one sequence of 1024 channels: 256 segments of 256 tokens give
+    # 262144 segment-channel lanes, four waves per SIMD
+    assert ws(1, 65536, 1024, 16, 0) == 256 * 1024 * 17 * 4
     assert ws(1, 4096, 64, 16, 256) == 16 * 64 * 17 * 4          # explicit 256-token segments
     assert ws(2, 4000, 64, 16, 1000) == 2 * 4 * 64 * 17 * 4       # 4 segments per sequence
     assert ws(1, 65536, 8192, 16, 0) == 0                         # enough channels: one segment
+    assert ws(1, 65536, 8200, 16, 0) == 31 * 8200 * 17 * 4        # D not a multiple of 32: segments
     assert ws(1, 100, 64, 16, 0) == 0                             # too short to split
     assert ws(1, 4096, 64, 16, 4096) == 0 and ws(1, 4096, 64, 16, 10 ** 6) == 0
     assert ws(1, 0, 64, 16, 0) == 0

@@ -63,9 +63,9 @@ def test_noalloc_matches_the_workspace_path_twice(first, second):
 
 
 def test_noalloc_rejects_plans_beyond_the_scratch():
-    """A plan needing more than 8 MiB of segment states returns JSCAN_ERR_WORKSPACE before any
+    """A plan needing more than 16 MiB of segment states returns JSCAN_ERR_WORKSPACE before any
     launch; the outputs stay untouched."""
-    batch, L, D, chunk = 1, 8192, 8192, 512         # 16 segments x 8192 channels x 68 B = 8.5 MiB
+    batch, L, D, chunk = 1, 16384, 8192, 256        # 64 segments x 8192 channels x 68 B = 34 MiB
     assert jscan.chunked_workspace_bytes(batch, L, D, chunk) > jscan._binding.NOALLOC_SCRATCH_BYTES
     inp = workloads.small_prefill(batch, L, D, "bf16", seed=3)
     d = to_dev(inp)
