@@ -9,31 +9,21 @@ Inputs are generated once, moved to HBM, and stay resident; the timed region hol
 the library's kernels, bracketed by stream synchronisation and timed with HIP events on
 the stream the kernels run on.  Prints exactly one JSON line.
 
-The roofline of the prefill kernel is its VALU issue rate, not HBM: each state element
-needs 5 fp32 instructions (the exponent product, the base-2 exponential, the input
-product and two fused multiply-adds), and the exponential issues at half rate, so
-6 issue slots per element is the floor.  The chip issues 256 CUs x 4 SIMDs x 16 lanes x
-2.4 GHz = 3.93e13 lane-slots/s, hence at most 6.55e12 state elements/s.  In flops the
-five instructions are 7 operations (each FMA counts 2), so the same bound reads
-45.9 TFLOP/s.  HBM traffic (about 6 bytes per B*L*D element in bf16) is reported beside
-it as GB/s and as a fraction of 8 TB/s.
-
-With --scalar-a (A a scaled identity, one value per channel: the Mamba-2 form) the decay is
-shared by a channel's 16 states, so a state element needs only the input product and two
-fused multiply-adds (3 slots) plus a sixteenth of the decay's product and exponential
-(3/16): 3.1875 slots and 5.125 flops per element, a bound of 63.2 TFLOP/s.  With --complex-a
-(the complex-valued state of the Mamba-3 form) one complex state, two elements, takes 19
-slots and 21 flops per token (decay, rotation by a hardware sine and cosine, complex update,
-output): 9.5 slots and 10.5 flops per element, a bound of 43.4 TFLOP/s.  --trapezoid (the
-exponential-trapezoidal rule of Mamba-3, with any of the three forms of A) adds one fused
-multiply-add per element, the previous token's input taken in before the decay: one slot and
-two flops more than the form's own count, and lam [B, L, D] to the bytes read.  --mimo R (R
-inputs and outputs per channel, B and C N x R: the MIMO scan of Mamba-3) makes the input term a
-rank-R sum (one product and R - 1 fused multiply-adds) and the output R fused multiply-adds per
-element: 2R + 4 slots and 4R + 3 flops for the diagonal A (12 and 19 at R = 4), 2R + 1 + 3/16
-and 4R + 1 + 2/16 for the scaled identity, (15 + 4R) / 2 and (8R + 13) / 2 for the complex state;
-x and y grow R-fold in bytes.  --mimo R --trapezoid (both Mamba-3 changes) adds the left end
-point's R fused multiply-adds per element (R slots, 2R flops) and lam to the bytes.
+The line's `roofline` is the metric's: HBM, algorithmic bytes of a launch of the dominant
+kernel over its average launch time (HIP events), against 8 TB/s.  `roofline_alu` puts the
+same launch against the vector-ALU bound that actually binds the prefill.  That bound comes
+from the committed microbenchmarks (profiles/micro_gfx950.txt, `bench.py --micro`): a SIMD
+retires a 64-lane fp32 FMA-class instruction every FMA_CYCLES and an exponential every
+EXP_CYCLES (about 3 FMA slots) when enough waves feed it.  A state element of the S6 scan
+needs an exponent product, the exponential, the input product and two fused multiply-adds,
+4 + EXP_SLOTS slots, 7 flops; at the 2.4 GHz peak engine clock over 256 CUs x 4 SIMDs that is
+about 8.6e12 state elements/s (1.0 ms for the 64K x 8192 scan, 40% of the HBM peak).  The
+other forms count their own instructions the same way: a scaled-identity A evaluates the decay
+once per 16 states; a complex state adds the rotation (a sine and a cosine, each costed like
+the exponential); the exponential-trapezoidal rule adds one FMA per element and reads lam; a
+rank-R MIMO scan makes the input term a rank-R sum and the output R FMAs per element.  None of
+these counts includes the instructions that deliver operands between lanes (DPP broadcasts,
+permlane swaps), which the kernels also need.
 """
 from __future__ import annotations
 
@@ -52,15 +42,40 @@ METRIC = "selective-scan elems/s (B·L·D) + HBM GB/s % of peak, L=64K D=8192 N=
 HBM_PEAK_GBPS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0                # dense bf16 matrix-core peak of MI355X
 PRODUCER_RANK = 256                           # rank of delta's projection (d_model 4096 / 16)
-VALU_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9      # fp32 lane-instructions per second (no packed math)
-SLOTS_PER_STATE_ELEM = 6                      # mul, exp (2 slots), mul, fma, fma
+
+
+def _micro_rates():
+    """Cycles per wave instruction of a SIMD running 8 waves, for the fused multiply-add and the
+    base-2 exponential, from the committed microbenchmark summary (bench.py --micro); the
+    values measured on the MI355X when it is absent."""
+    fma, exp = 2.59, 7.91
+    path = os.path.join(ROOT, "profiles", "micro_gfx950.txt")
+    if os.path.exists(path):
+        for line in open(path):
+            if line.startswith("valu_cycles_per_wave_instruction.fma.cycles_per_instr_8w ="):
+                fma = float(line.split("=")[1])
+            elif line.startswith("valu_cycles_per_wave_instruction.exp.cycles_per_instr_8w ="):
+                exp = float(line.split("=")[1])
+    return fma, exp
+
+
+# The vector-ALU bound of the scans.  A SIMD retires one wave-wide (64-lane) FMA-class instruction
+# per FMA_CYCLES and one exponential (or sine, cosine) per EXP_CYCLES when enough waves feed it,
+# measured by the microbenchmarks; at MI355X's 2.4 GHz peak engine clock that is
+# VALU_SLOTS_PER_S FMA-class lane-instructions per second over 256 CUs x 4 SIMDs, and a
+# transcendental costs EXP_SLOTS of them.  The counts below are the instructions the
+# arithmetic needs per state element, with no operand-delivery (DPP, permlane) overhead.
+FMA_CYCLES, EXP_CYCLES = _micro_rates()
+VALU_SLOTS_PER_S = 256 * 4 * 64 * 2.4e9 / FMA_CYCLES
+EXP_SLOTS = EXP_CYCLES / FMA_CYCLES
+SLOTS_PER_STATE_ELEM = 4 + EXP_SLOTS          # mul, exp, mul, fma, fma
 FLOPS_PER_STATE_ELEM = 7                      # mul 1 + exp 1 + mul 1 + fma 2 + fma 2
 PEAK_STATE_ELEMS = VALU_SLOTS_PER_S / SLOTS_PER_STATE_ELEM
-SCALAR_A_SLOTS = 3 + 3 / 16                   # mul, fma, fma; decay (mul + exp) once per 16 states
+SCALAR_A_SLOTS = 3 + (1 + EXP_SLOTS) / 16     # mul, fma, fma; decay (mul + exp) once per 16 states
 SCALAR_A_FLOPS = 5 + 2 / 16
-# complex state, per real component (half a complex state): decay mul + exp (3), angle mul +
-# fract (2), cos and sin (4), r cos and r sin (2), two input products (2), four fma (4), y (2)
-COMPLEX_A_SLOTS = 19 / 2
+# complex state, per real component (half a complex state): decay mul + exp, angle mul + fract,
+# cos and sin, r cos and r sin, two input products, four fma, y (2)
+COMPLEX_A_SLOTS = (1 + EXP_SLOTS + 2 + 2 * EXP_SLOTS + 2 + 2 + 4 + 2) / 2
 COMPLEX_A_FLOPS = 21 / 2
 TRAP_SLOTS, TRAP_FLOPS = 1, 2                 # the left end point's fma, on top of the form's count
 
@@ -68,10 +83,12 @@ TRAP_SLOTS, TRAP_FLOPS = 1, 2                 # the left end point's fma, on top
 def mimo_cost(form: str, R: int):
     """(issue slots, flops) per state element of the rank-R scan; R = 1 gives the single-input counts."""
     if form == "scalar":
-        return 2 * R + 1 + 3 / 16, 4 * R + 1 + 2 / 16
+        return 2 * R + 1 + (1 + EXP_SLOTS) / 16, 4 * R + 1 + 2 / 16
     if form == "complex":
-        return (15 + 4 * R) / 2, (8 * R + 13) / 2
-    return 2 * R + 4, 4 * R + 3
+        return (11 + 3 * EXP_SLOTS + 4 * R) / 2, (8 * R + 13) / 2
+    return 2 * R + 3 + EXP_SLOTS, 4 * R + 3
+
+
 KERNEL_SOURCES = {
     "prefill": ["scan_update.h", "mfma_common.h", "prefill_rows_kernel.h"],
     "step": ["scan_update.h", "step_kernel.h"],
@@ -330,11 +347,36 @@ def run_micro(log):
     return out
 
 
+def trace_summary(directory: str, warmup: int) -> str:
+    """Per-kernel durations from rocprofv3 --kernel-trace CSV files, in launch order, leaving out
+    each kernel's first `warmup` launches; one line per kernel (microseconds)."""
+    import csv
+    import glob
+    import statistics
+    rows = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True)):
+        with open(path, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    by_kernel = {}
+    for r in rows:
+        by_kernel.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = []
+    for name, us in by_kernel.items():
+        kept = us[warmup:] if len(us) > warmup else us
+        out.append(f"{name}\n    launches {len(us)}, after the first {len(us) - len(kept)}: median "
+                   f"{statistics.median(kept):.1f} us, mean {statistics.fmean(kept):.1f}, min {min(kept):.1f}, "
+                   f"max {max(kept):.1f}")
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default: at least 5, and as many more as fill one "
+                         "second: short steps run slower until the GPU has been busy for about that long)")
     ap.add_argument("--workload", default="prefill_64k",
                     choices=["prefill_64k", "prefill_4k", "prefill_256k", "decode_256x28", "tiny_fp32",
                              "prefill_64k_tp8", "prefill_16x4k"])
@@ -369,7 +411,14 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the scan, time a plain device-to-device copy of MIB mebibytes (the reference "
                          "kernel for scaling the profiler's FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="instead of the scan, summarise the rocprofv3 kernel trace(s) in DIR (*kernel_trace.csv): "
+                         "per kernel, the launches after the first WARMUP, their median, mean, min and max")
     args = ap.parse_args()
+
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary, args.warmup or 0))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: the benchmark runs on one GPU; sharding the scan over several GPUs is described in the "
@@ -394,7 +443,7 @@ def main():
         n = args.calibrate_copy * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        for _ in range(args.warmup):
+        for _ in range(args.warmup or 5):
             dst.copy_(src)
         torch.cuda.synchronize()
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -571,9 +620,20 @@ def main():
     torch.cuda.synchronize()
     log(f"inputs for {wl.name} resident in HBM ({time.perf_counter() - t0:.1f} s)")
 
-    for _ in range(args.warmup):
+    warmup = args.warmup if args.warmup is not None else 5
+    for _ in range(warmup):
         one_step()
     torch.cuda.synchronize()
+    if args.warmup is None:
+        # Short steps measured right after start run up to 10% slower than after a second of
+        # work (prefill_64k_tp8 through the time-parallel path: 0.362 ms after 10 warm-up steps,
+        # 0.328 ms after 3000); the default warm-up therefore lasts at least one second.
+        w0 = time.perf_counter()
+        while time.perf_counter() - w0 < 1.0:
+            for _ in range(10):
+                one_step()
+            warmup += 10
+            torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     w0 = time.perf_counter()
@@ -680,7 +740,7 @@ def main():
         "unit": "elems/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
