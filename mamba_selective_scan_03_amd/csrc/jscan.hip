@@ -507,7 +507,7 @@ void launch_ssm_inputs(const uint16_t *x, const uint16_t *w_x, const float *g_d,
     if (!delta) return;   // x projection only: delta is computed inside jscan_prefill_fused
     // one work-group per CU (the LDS tiles allow one): 256 groups of (channel slice, token tiles)
     const int ch_tiles = D / jscan::proj::kTileDt;
-    const int64_t tok_tiles = (M + jscan::proj::kTileDt - 1) / jscan::proj::kTileDt;
+    const int64_t tok_tiles = (M + jscan::proj::kDtTok - 1) / jscan::proj::kDtTok;
     int64_t groups = ch_tiles >= 256 ? 1 : 256 / ch_tiles;
     if (groups > tok_tiles) groups = tok_tiles;
     hipLaunchKernelGGL((jscan::dtproj_kernel<R>), dim3((unsigned)(groups * ch_tiles)), dim3(512), 0, stream, d_low,

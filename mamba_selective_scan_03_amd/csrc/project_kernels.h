@@ -20,7 +20,7 @@ namespace jscan {
 
 namespace proj {
 constexpr int kRowsX = 128;   // x-projection rows (tokens) per work-group: 4 waves x 32
-constexpr int kTileDt = 128;  // delta-projection tile: 128 channels x 128 tokens, 4 waves of 64 x 64
+constexpr int kTileDt = 128;  // delta-projection channel slice of a work-group: two waves of 64 channels
 }
 
 // Sum over the 16 lanes of a DPP row (lanes 16q .. 16q+15); every lane gets the total.
@@ -33,84 +33,60 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
+// 16 bytes per lane from src straight into LDS at lds + 16 * lane (global_load_lds_dwordx4; lds
+// is wave-uniform).  Written as a statement the compiler does not look into: given the
+// builtin, it cannot tell which LDS array the load writes and waits for every such load in
+// flight before later LDS writes, which undoes the prefetch.  Its caller orders the load with
+// an explicit s_waitcnt and a barrier before any wave reads the data.  The address registers
+// are read when the instruction issues; the instruction writes no register.  M0 (the LDS
+// base of the load) is set here; nothing else in the library's kernels keeps a value in M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// vmcnt for an s_waitcnt that leaves `n` vector-memory operations outstanding (gfx9 encoding:
+// low four bits and bits 14-15; expcnt and lgkmcnt at their maxima, so they do not wait).
+template <int n> constexpr int vmcnt_only() { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 // x projection: one work-group = 128 rows (tokens) x all R + 2N output columns, eight waves in
 // a 4 x 2 grid: wave (wr, wc) owns rows 32 wr .. 32 wr + 31 (two 16-row tiles) and the half
 // wc of the CT = R / 16 + 2 column tiles (d_low's R / 16 tiles, then one each of B and C).
-// K (= D) goes in stages of 64: each stage's x tile [128][64] and W_x tile [16 CT][64] are
-// loaded by all 512 threads into registers two stages ahead, then written to LDS (double-
-// buffered) for the waves' MFMA operand reads.  LDS rows are padded to 72 bf16 (144 bytes),
-// so the 16 rows one operand read touches fall on distinct banks.  Two waves per SIMD, and a
-// register budget that keeps the accumulators in place, let one wave's operand reads and
-// MFMAs overlap the other's.
+// K (= D) goes in stages of 64.  Each stage's x tile [128][64] and W_x tile [16 CT][64] go
+// from memory straight into LDS (global_load_lds_dwordx4, 1 KB per wave instruction), three
+// stages deep, so a stage's loads are issued two stages before its MFMAs and take no
+// registers.  A tile row (64 bf16, 128 bytes) holds its eight 16-byte chunks XOR-swizzled with
+// (row / 2) % 8, so the 16 rows one operand read touches fall on distinct banks.  Two waves per
+// SIMD, and a register budget that keeps the accumulators in place, let one wave's operand
+// reads and MFMAs overlap the other's.
 namespace proj {
 constexpr int kStageK = 64;          // K per stage
-constexpr int kLdsRow = 72;          // bf16 per LDS row (64 + 8 padding)
 constexpr int kXThreads = 512;       // threads of an x-projection work-group
+constexpr int kXBufs = 3;            // stages in LDS: the one being read and two in flight
 }
 
-// (ext_vector_type, not HIP's uint4 struct: copies of the struct type become memcpys that
-// keep the whole set in scratch memory)
-template <int CT> struct XprojRegs {
-    static constexpr int kW = (16 * CT * 8 + proj::kXThreads - 1) / proj::kXThreads;
-    u32x4_t xr[2];          // x: 128 rows x 8 chunks of 16 bytes = 1024 chunks, 2 per thread
-    u32x4_t wr[kW];         // W_x: 16 CT rows x 8 chunks; the last one only in some waves
-};
-
-// Whether W_x chunk tid + 512 j exists.  16 CT * 8 chunks is a multiple of 64, so the answer is
-// the same for a whole wave; it is taken from the wave's first lane to make that visible.
-template <int CT>
-__device__ __forceinline__ bool xproj_w_chunk(int j, int tid) {
-    return __builtin_amdgcn_readfirstlane(tid) + proj::kXThreads * j < 16 * CT * 8;
-}
-
-template <int CT>
-__device__ __forceinline__ void xproj_load(XprojRegs<CT> &g, const uint16_t *x, const uint16_t *w, int64_t row_base,
-                                           int64_t M, int D, int k0, int tid) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int i = tid + proj::kXThreads * j, r = i >> 3, part = i & 7;
-        g.xr[j] = *reinterpret_cast<const u32x4_t *>(x + min(row_base + r, M - 1) * D + k0 + 8 * part);
-    }
-    // every lane loads (a missing chunk re-reads the last one): a load under a branch would be
-    // waited for where the branch ends
-#pragma unroll
-    for (int j = 0; j < XprojRegs<CT>::kW; ++j) {
-        const int i = min(tid + proj::kXThreads * j, 16 * CT * 8 - 1), r = i >> 3, part = i & 7;
-        g.wr[j] = *reinterpret_cast<const u32x4_t *>(w + (int64_t)r * D + k0 + 8 * part);
-    }
-}
-
-template <int CT>
-__device__ __forceinline__ void xproj_store(const XprojRegs<CT> &g, uint16_t *xs, uint16_t *ws, int tid) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int i = tid + proj::kXThreads * j, r = i >> 3, part = i & 7;
-        *reinterpret_cast<u32x4_t *>(xs + r * proj::kLdsRow + 8 * part) = g.xr[j];
-    }
-#pragma unroll
-    for (int j = 0; j < XprojRegs<CT>::kW; ++j) {
-        if (!xproj_w_chunk<CT>(j, tid)) continue;
-        const int i = tid + proj::kXThreads * j, r = i >> 3, part = i & 7;
-        *reinterpret_cast<u32x4_t *>(ws + r * proj::kLdsRow + 8 * part) = g.wr[j];
-    }
-}
+// LDS position (in 16-byte chunks) of chunk c of row r of a swizzled 64-wide tile.
+__device__ __forceinline__ int swz64(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
 // One stage's MFMAs of one wave: its 32 rows (two 16-row tiles) against its CH column tiles
 // (from tile c0), two 32-wide k steps, operands read from LDS.  All of the stage's operands
 // are requested before the first MFMA, so their LDS latency overlaps the matrix work.
 template <int CH>
 __device__ __forceinline__ void xproj_mfma(f32x4_t (&acc)[2][CH], const uint16_t *xs, const uint16_t *ws, int wr,
-                                           int c0, int r16, int kq) {
-    const uint16_t *xw = xs + (wr * 32 + r16) * proj::kLdsRow + kq;
-    const uint16_t *wb = ws + (16 * c0 + r16) * proj::kLdsRow + kq;
+                                           int c0, int r16, int g4) {
     bf16x8_t a[2][2], b[2][CH];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-        a[k][0] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(xw + 32 * k));
-        a[k][1] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(xw + 16 * proj::kLdsRow + 32 * k));
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            a[k][t] = __builtin_bit_cast(
+                bf16x8_t, *reinterpret_cast<const u32x4_t *>(xs + 8 * swz64(wr * 32 + 16 * t + r16, 4 * k + g4)));
 #pragma unroll
         for (int c = 0; c < CH; ++c)
-            b[k][c] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(wb + 16 * c * proj::kLdsRow + 32 * k));
+            b[k][c] = __builtin_bit_cast(
+                bf16x8_t, *reinterpret_cast<const u32x4_t *>(ws + 8 * swz64(16 * (c0 + c) + r16, 4 * k + g4)));
     }
     __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the MFMAs
 #pragma unroll
@@ -130,14 +106,19 @@ __global__ __launch_bounds__(proj::kXThreads) __attribute__((amdgpu_waves_per_eu
     constexpr int CT = RT + 2;   // column tiles
     constexpr int CH = CT / 2;   // column tiles per wave
     static_assert(CT % 2 == 0 && CH <= RT, "each wave half must hold d_low tiles only or d_low then B and C");
-    constexpr int kXs = proj::kRowsX * proj::kLdsRow, kWs = 16 * CT * proj::kLdsRow;
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][kXs];
-    __shared__ __attribute__((aligned(16))) uint16_t ws[2][kWs];
+    constexpr int kXs = proj::kRowsX * proj::kStageK, kWs = 16 * CT * proj::kStageK;   // bf16 per stage
+    constexpr int kXInst = kXs / 512 / 8;                  // x DMA instructions per wave per stage
+    constexpr int kWInstAll = kWs / 512;                   // W DMA instructions per stage
+    constexpr int kWInst = (kWInstAll + 7) / 8;            // per wave (the last few repeat one)
+    constexpr int kDmaPerWave = kXInst + kWInst;
+    static_assert(kXs % (512 * 8) == 0, "the x tile is whole wave instructions per wave");
+    __shared__ __attribute__((aligned(16))) uint16_t xs[proj::kXBufs][kXs];
+    __shared__ __attribute__((aligned(16))) uint16_t ws[proj::kXBufs][kWs];
     __shared__ float ssq[2][proj::kRowsX];   // d_low sums of squares of each column half, per row
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
     const int wr = wave & 3, wc = wave >> 2, c0 = CH * wc;
     const int64_t row_base = (int64_t)blockIdx.x * proj::kRowsX;
-    const int r16 = l & 15, kq = 8 * (l >> 4);
+    const int r16 = l & 15, g4 = l >> 4;
     const int stages = D / proj::kStageK;
 
     f32x4_t acc[2][CH];
@@ -146,31 +127,39 @@ __global__ __launch_bounds__(proj::kXThreads) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int c = 0; c < CH; ++c) acc[t][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Two named register sets (not an array) so that nothing is indexed at run time.
-    XprojRegs<CT> Ga, Gb;
-    xproj_load<CT>(Ga, x, w, row_base, M, D, 0, tid);
-    if (stages > 1) xproj_load<CT>(Gb, x, w, row_base, M, D, proj::kStageK, tid);
-    xproj_store<CT>(Ga, xs[0], ws[0], tid);
-    if (stages > 2) xproj_load<CT>(Ga, x, w, row_base, M, D, 2 * proj::kStageK, tid);
-    __syncthreads();
-
-    // Stage s: MFMAs from LDS buffer s & 1; stage s+1 (in registers since stage s-2) goes to the
-    // other buffer, and stage s+3 is requested into the registers it leaves.
-    for (int s = 0; s < stages; s += 2) {
-        xproj_mfma<CH>(acc, xs[0], ws[0], wr, c0, r16, kq);
-        if (s + 1 < stages) {
-            xproj_store<CT>(Gb, xs[1], ws[1], tid);
-            if (s + 3 < stages) xproj_load<CT>(Gb, x, w, row_base, M, D, (s + 3) * proj::kStageK, tid);
+    // This wave's loads of stage st into buffer b.  Wave instruction q of a tile fills its
+    // chunk positions 64 q .. 64 q + 63; position P holds row P / 8's chunk (P % 8) ^ swizzle.
+    // Every wave issues kDmaPerWave instructions a stage: the W instructions past the tile's
+    // last repeat that one (the same bytes to the same place), so the counts stay uniform.
+    auto dma = [&](int st, int b) {
+        const int k0 = st * proj::kStageK;
+#pragma unroll
+        for (int j = 0; j < kXInst; ++j) {
+            const int q = wave * kXInst + j, P = q * 64 + l, r = P >> 3;
+            const int c = (P & 7) ^ ((r >> 1) & 7);
+            lds_dma16(x + min(row_base + r, M - 1) * D + k0 + 8 * c,
+                      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)(xs[b] + q * 512));
         }
-        __syncthreads();
-        if (s + 1 < stages) {
-            xproj_mfma<CH>(acc, xs[1], ws[1], wr, c0, r16, kq);
-            if (s + 2 < stages) {
-                xproj_store<CT>(Ga, xs[0], ws[0], tid);
-                if (s + 4 < stages) xproj_load<CT>(Ga, x, w, row_base, M, D, (s + 4) * proj::kStageK, tid);
-            }
-            __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kWInst; ++j) {
+            const int q = min(wave * kWInst + j, kWInstAll - 1), P = q * 64 + l, r = P >> 3;
+            const int c = (P & 7) ^ ((r >> 1) & 7);
+            lds_dma16(w + (int64_t)r * D + k0 + 8 * c,
+                      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)(ws[b] + q * 512));
         }
+    };
+    dma(0, 0);
+    if (stages > 1) dma(1, 1);
+    for (int s = 0; s < stages; ++s) {
+        // this wave's loads of stage s have landed once at most stage s + 1's are outstanding
+        if (s + 1 < stages)
+            __builtin_amdgcn_s_waitcnt(vmcnt_only<kDmaPerWave>());
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
+        __syncthreads();   // every wave's part of stage s is in; every wave is done with s - 1
+        if (s + 2 < stages) dma(s + 2, (s + 2) % proj::kXBufs);
+        const int b = s % proj::kXBufs;
+        xproj_mfma<CH>(acc, xs[b], ws[b], wr, c0, r16, g4);
     }
 
     // Epilogue.  Lane l holds rows 4 * (l / 16) + i of each 16-row tile, column 16 c + l % 16.
@@ -228,28 +217,45 @@ __global__ __launch_bounds__(proj::kXThreads) __attribute__((amdgpu_waves_per_eu
 }
 
 // Delta projection.  A work-group owns one 128-channel slice of W_dt and walks the token
-// tiles t = g, g + G, g + 2G, ... (G groups per channel slice).  Each wave keeps its 64
-// channels of W_dt as MFMA A operands in registers for the whole kernel; each 128-token tile
-// of d_low is loaded by all 512 threads into registers one tile ahead and stored to LDS
-// (double-buffered, rows padded to R + 8 bf16), from where the waves read their B operands
-// (wave w of 8: channels 64 (w & 1) .. +63, tokens 32 (w >> 1) .. +31 of the tile).  Two waves
-// per SIMD let one wave's softplus epilogue overlap the other's matrix work.  A = W_dt and
-// B = d_low^T, so each lane's result is 4 consecutive channels of one token: the epilogue adds
-// the bias, applies softplus and writes 8 bytes.
+// tiles t = g, g + G, g + 2G, ... (G groups per channel slice, kDtTok tokens a tile).  Each
+// wave keeps its 64 channels of W_dt as MFMA A operands in registers for the whole kernel.
+// A = W_dt and B = d_low^T, so each lane's result is 4 consecutive channels of one token.
+//
+// d_low tiles go from memory straight into LDS (global_load_lds_dwordx4: each wave
+// instruction fills 1 KB of LDS, lane by lane), kDtBufs tiles deep, so a tile's loads are
+// issued two tiles before it is used and take no registers.  (The three tile buffers are
+// separate arrays so that each step of the loop, unrolled by three, names its own.)  Inside a tile row (one token's R
+// values) the 16-byte chunks are stored XOR-swizzled with the row index, so the 16 rows one
+// B-operand read touches fall on distinct banks.  Each wave's result (64 channels x 16
+// tokens) passes through a small LDS area of its own, which turns the MFMA layout (4
+// channels per lane) into whole 128-byte rows of delta: each lane then writes 16 bytes.
+namespace proj {
+constexpr int kDtTok = 64;    // tokens per d_low tile
+constexpr int kDtBufs = 3;    // d_low tiles in LDS: the one being read and two in flight
+constexpr int kDtOutRow = 72; // bf16 per row of a wave's output area (64 channels + 8 padding)
+}
+
 template <int R>
 __global__ __launch_bounds__(512) void dtproj_kernel(const uint16_t *__restrict__ d_low, const uint16_t *__restrict__ w,
                                                      const float *__restrict__ bias, uint16_t *__restrict__ delta,
                                                      int64_t M, int D, int ch_tiles, int groups) {
-    constexpr int KS = R / 32;                 // MFMA k steps
-    constexpr int kRow = R + 8;                // LDS row (bf16), padded
-    constexpr int kChunks = proj::kTileDt * R / 8 / 512;   // 16-byte chunks of a d_low tile per thread
-    __shared__ __attribute__((aligned(16))) uint16_t ds[2][proj::kTileDt * kRow];
-    const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+    constexpr int KS = R / 32;                                  // MFMA k steps
+    constexpr int kRowChunks = R / 8;                           // 16-byte chunks per d_low row
+    constexpr int kSwz = kRowChunks >= 16 ? 15 : kRowChunks - 1;
+    constexpr int kDma = proj::kDtTok * kRowChunks / (64 * 8);  // DMA instructions per wave per tile
+    constexpr int kSt = 2;                                      // global stores per wave per tile
+    static_assert(kDma >= 1 && proj::kDtTok * kRowChunks % (64 * 8) == 0, "a tile is whole wave instructions");
+    __shared__ __attribute__((aligned(16))) uint16_t tiles0[proj::kDtTok * R];
+    __shared__ __attribute__((aligned(16))) uint16_t tiles1[proj::kDtTok * R];
+    __shared__ __attribute__((aligned(16))) uint16_t tiles2[proj::kDtTok * R];
+    __shared__ __attribute__((aligned(16))) uint16_t outs[8][16 * proj::kDtOutRow];
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
     const int ct = blockIdx.x % ch_tiles, grp = blockIdx.x / ch_tiles;
     const int ch0 = ct * proj::kTileDt + 64 * (wave & 1);
-    const int tw = 32 * (wave >> 1);           // this wave's token offset inside a tile
-    const int r16 = l & 15, kq = 8 * (l >> 4);
-    const int64_t tok_tiles = (M + proj::kTileDt - 1) / proj::kTileDt;
+    const int tw = 16 * (wave >> 1);           // this wave's tokens inside a tile
+    const int r16 = l & 15, g4 = l >> 4, kq = 8 * g4;
+    const int64_t tok_tiles = (M + proj::kDtTok - 1) / proj::kDtTok;
+    const int count = grp < tok_tiles ? (int)((tok_tiles - grp + groups - 1) / groups) : 0;
 
     bf16x8_t a[4][KS];
 #pragma unroll
@@ -258,69 +264,73 @@ __global__ __launch_bounds__(512) void dtproj_kernel(const uint16_t *__restrict_
         for (int ks = 0; ks < KS; ++ks) a[u][ks] = load_frag(w + (int64_t)(ch0 + 16 * u + r16) * R + 32 * ks + kq);
     float4 bs[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) bs[u] = *reinterpret_cast<const float4 *>(bias + ch0 + 16 * u + 4 * (l >> 4));
+    for (int u = 0; u < 4; ++u) bs[u] = *reinterpret_cast<const float4 *>(bias + ch0 + 16 * u + 4 * g4);
 
-    u32x4_t pre[kChunks];
-    auto load_tile = [&](int64_t t) {
+    // This wave's share of tile i's loads into buf: LDS chunk position P of the tile holds
+    // row P / kRowChunks, chunk (P % kRowChunks) ^ (row & kSwz) of that row.
+    auto dma = [&](int i, uint16_t *buf) {
+        const int64_t t = grp + (int64_t)i * groups;
 #pragma unroll
-        for (int j = 0; j < kChunks; ++j) {
-            const int i = tid + 512 * j, r = i / (R / 8), part = i % (R / 8);
-            pre[j] = *reinterpret_cast<const u32x4_t *>(d_low + min(t * proj::kTileDt + r, M - 1) * R + 8 * part);
+        for (int q = 0; q < kDma; ++q) {
+            const int inst = wave * kDma + q, P = inst * 64 + l;
+            const int row = P / kRowChunks, c = (P % kRowChunks) ^ (row & kSwz);
+            const int64_t tok = min(t * proj::kDtTok + row, M - 1);
+            lds_dma16(d_low + tok * R + 8 * c,
+                      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)(buf + inst * 64 * 8));
         }
     };
-    auto store_tile = [&](uint16_t *dst) {
+    uint16_t *ow = outs[wave];
+    // Tile i, read from rbuf; tile i + 2's loads go into dbuf (the buffer of tile i - 1).
+    auto step = [&](int i, const uint16_t *rbuf, uint16_t *dbuf) {
+        // This wave's loads of tile i have landed when at most the vector-memory operations
+        // issued after them are outstanding: tile i + 1's loads and the stores of tiles i - 1
+        // and i - 2 (each of which issues all of its instructions: only a sequence's last tile
+        // can be partial, and it is its group's last).
+        if (i + 1 >= count)
+            __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
+        else if (i == 0)
+            __builtin_amdgcn_s_waitcnt(vmcnt_only<kDma>());
+        else if (i == 1)
+            __builtin_amdgcn_s_waitcnt(vmcnt_only<kDma + kSt>());
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_only<kDma + 2 * kSt>());
+        __syncthreads();   // every wave's part of tile i is in; every wave is done with tile i - 1
+        if (i + 2 < count) dma(i + 2, dbuf);
+        const int64_t t = grp + (int64_t)i * groups;
+        const int row = tw + r16;
+        f32x4_t acc[4];
 #pragma unroll
-        for (int j = 0; j < kChunks; ++j) {
-            const int i = tid + 512 * j, r = i / (R / 8), part = i % (R / 8);
-            *reinterpret_cast<u32x4_t *>(dst + r * kRow + 8 * part) = pre[j];
-        }
-    };
-
-    int buf = 0;
-    if (grp < tok_tiles) {
-        load_tile(grp);
-        store_tile(ds[0]);
-    }
-    __syncthreads();
-    for (int64_t t = grp; t < tok_tiles; t += groups) {
-        const int64_t tn = t + groups;
-        if (tn < tok_tiles) load_tile(tn);      // in flight during this tile's MFMAs
-        const uint16_t *bt = ds[buf] + (tw + r16) * kRow + kq;
-        f32x4_t acc[4][2];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int v = 0; v < 2; ++v) acc[u][v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < 4; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            bf16x8_t b[2];
+            const int c = (4 * ks + g4) ^ (row & kSwz);
+            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(rbuf + row * R + 8 * c));
 #pragma unroll
-            for (int v = 0; v < 2; ++v)
-                b[v] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(bt + 16 * v * kRow + 32 * ks));
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int v = 0; v < 2; ++v) acc[u][v] = mfma16(a[u][ks], b[v], acc[u][v]);
+            for (int u = 0; u < 4; ++u) acc[u] = mfma16(a[u][ks], b, acc[u]);
         }
-        // the next tile goes to LDS before this tile's stores are issued: waiting for its loads
-        // then does not also wait for fresh stores (one counter covers both)
-        if (tn < tok_tiles) store_tile(ds[buf ^ 1]);
+        // bias, softplus, bf16: token tw + r16, channels 16 u + 4 g4 .. + 3 of the wave's 64
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int c = ch0 + 16 * u + 4 * (l >> 4);
-#pragma unroll
-            for (int v = 0; v < 2; ++v) {
-                const int64_t tok = t * proj::kTileDt + tw + 16 * v + r16;
-                if (tok < M) {
-                    uint2 pk;
-                    pk.x = pack_bf16x2(softplus_f32(acc[u][v][0] + bs[u].x), softplus_f32(acc[u][v][1] + bs[u].y));
-                    pk.y = pack_bf16x2(softplus_f32(acc[u][v][2] + bs[u].z), softplus_f32(acc[u][v][3] + bs[u].w));
-                    *reinterpret_cast<uint2 *>(delta + tok * D + c) = pk;
-                }
-            }
+            uint2 pk;
+            pk.x = pack_bf16x2(softplus_f32(acc[u][0] + bs[u].x), softplus_f32(acc[u][1] + bs[u].y));
+            pk.y = pack_bf16x2(softplus_f32(acc[u][2] + bs[u].z), softplus_f32(acc[u][3] + bs[u].w));
+            *reinterpret_cast<uint2 *>(ow + r16 * proj::kDtOutRow + 16 * u + 4 * g4) = pk;
         }
-        buf ^= 1;
-        __syncthreads();
+        // whole rows out: lane l writes 16 bytes (8 channels) of token row l / 8 + 8 k
+#pragma unroll
+        for (int k = 0; k < kSt; ++k) {
+            const int orow = (l >> 3) + 8 * k, oc = l & 7;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(ow + orow * proj::kDtOutRow + 8 * oc);
+            const int64_t tok = t * proj::kDtTok + tw + orow;
+            if (tok < M) *reinterpret_cast<u32x4_t *>(delta + tok * D + ch0 + 8 * oc) = v;
+        }
+    };
+    if (count > 0) dma(0, tiles0);
+    if (count > 1) dma(1, tiles1);
+    for (int i = 0; i < count; i += proj::kDtBufs) {
+        step(i, tiles0, tiles2);
+        if (i + 1 < count) step(i + 1, tiles1, tiles0);
+        if (i + 2 < count) step(i + 2, tiles2, tiles1);
     }
 }
 
