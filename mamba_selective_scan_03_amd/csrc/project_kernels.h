@@ -250,7 +250,15 @@ __global__ __launch_bounds__(512) void dtproj_kernel(const uint16_t *__restrict_
     __shared__ __attribute__((aligned(16))) uint16_t tiles2[proj::kDtTok * R];
     __shared__ __attribute__((aligned(16))) uint16_t outs[8][16 * proj::kDtOutRow];
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
-    const int ct = blockIdx.x % ch_tiles, grp = blockIdx.x / ch_tiles;
+    // Work-groups go to the 8 XCDs in turn (work-group b to XCD b % 8).  The groups that walk
+    // the same token tiles are kept on the same XCDs, so each XCD's L2 fetches only its share of
+    // d_low (when the group count divides 8; otherwise groups are spread over all XCDs).
+    int ct = blockIdx.x % ch_tiles, grp = blockIdx.x / ch_tiles;
+    if (8 % groups == 0 && ch_tiles % (8 / groups) == 0 && (int)gridDim.x == groups * ch_tiles) {
+        const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+        grp = xcd % groups;
+        ct = (xcd / groups) * (ch_tiles / (8 / groups)) + local;
+    }
     const int ch0 = ct * proj::kTileDt + 64 * (wave & 1);
     const int tw = 16 * (wave >> 1);           // this wave's tokens inside a tile
     const int r16 = l & 15, g4 = l >> 4, kq = 8 * g4;
