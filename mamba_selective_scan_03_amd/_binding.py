@@ -315,7 +315,11 @@ def step_complex(h, x_t, delta_t, A, B_t, C_t, y_t=None):
 def step(h, x_t, delta_t, A, B_t, C_t, y_t=None, _scalar_a=False, _complex_a=False):
     """One decode token for a batch: h ``[batch, D, 16]`` fp32 is updated in place; x_t, delta_t
     ``[batch, D]`` and B_t, C_t ``[batch, 16]`` (rows may be strided views of prefill tensors,
-    e.g. ``x[:, t]``).  Returns y_t ``[batch, D]``."""
+    e.g. ``x[:, t]``).  Returns y_t ``[batch, D]``.
+
+    In the ABI y_t's rows share x_t's row stride.  Without ``y_t`` this allocates one with that
+    stride: for ``x[:, t]`` of a ``[batch, L, D]`` tensor that is about batch * L * D elements
+    per call.  Pass ``y_t`` (for example ``y[:, t]`` of a ``[batch, L, D]`` output) to avoid it."""
     _require(h.is_cuda and h.dtype == torch.float32 and h.dim() == 3 and h.shape[2] == D_STATE and h.is_contiguous(),
              "h must be a contiguous fp32 [batch, D, 16] CUDA tensor")
     batch, D, _ = h.shape

@@ -55,23 +55,22 @@ constexpr int64_t kMaxBlocks = (int64_t)1 << 30;
 
 // Scans `nrows` rows (see Segments) with the row-mapped kernel when it applies, otherwise
 // with one lane per (row, channel).  AF: the form of A; kTrap: the trapezoidal rule (inputs tr).
-template <typename E, bool kSummary, jscan::AForm AF = jscan::AForm::Diagonal, bool kTrap = false>
+template <typename E, jscan::AForm AF = jscan::AForm::Diagonal, bool kTrap = false>
 void launch_rows(const void *x, const void *delta, const float *A, const void *B, const void *C, const float *h0,
-                 void *y, float *h_final, float *dsum, const jscan::Segments &sg, int64_t nrows, int64_t D,
-                 hipStream_t stream, jscan::Trap tr = jscan::Trap{nullptr, nullptr, nullptr}) {
+                 void *y, float *h_final, const jscan::Segments &sg, int64_t nrows, int64_t D, hipStream_t stream,
+                 jscan::Trap tr = jscan::Trap{nullptr, nullptr, nullptr}) {
     using T = typename E::store_t;
     const T *xt = static_cast<const T *>(x), *dt = static_cast<const T *>(delta);
     const T *bt = static_cast<const T *>(B), *ct = static_cast<const T *>(C);
     T *yt = static_cast<T *>(y);
     if (jscan::rows_kernel_applies(nrows, D)) {
-        jscan::launch_prefill_rows<E, kSummary, false, AF, kTrap>(xt, dt, A, bt, ct, h0, yt, h_final, dsum, sg,
-                                                                  nrows, (int)D, stream,
-                                                                  jscan::DeltaProj{nullptr, nullptr, nullptr}, tr);
+        jscan::launch_prefill_rows<E, false, AF, kTrap>(xt, dt, A, bt, ct, h0, yt, h_final, sg, nrows, (int)D, stream,
+                                                        jscan::DeltaProj{nullptr, nullptr, nullptr}, tr);
         return;
     }
     const int blocks_per_row = (int)((D + 63) / 64);
-    hipLaunchKernelGGL((jscan::prefill_lane_kernel<E, kSummary, AF, kTrap>), dim3((unsigned)(nrows * blocks_per_row)),
-                       dim3(64), 0, stream, xt, dt, A, bt, ct, h0, yt, h_final, dsum, sg, (int)D, blocks_per_row, tr);
+    hipLaunchKernelGGL((jscan::prefill_lane_kernel<E, AF, kTrap>), dim3((unsigned)(nrows * blocks_per_row)), dim3(64),
+                       0, stream, xt, dt, A, bt, ct, h0, yt, h_final, sg, (int)D, blocks_per_row, tr);
 }
 
 // Token-by-token prefill of whole sequences (one row per sequence).
@@ -86,7 +85,7 @@ jscan_status launch_prefill(const void *x, const void *delta, const float *A, co
         return launch_status();
     }
     const jscan::Segments sg{L, L, 1, 0};
-    launch_rows<E, false, AF, kTrap>(x, delta, A, B, C, h0, y, h_final, nullptr, sg, batch, D, stream, tr);
+    launch_rows<E, AF, kTrap>(x, delta, A, B, C, h0, y, h_final, sg, batch, D, stream, tr);
     return launch_status();
 }
 
@@ -861,10 +860,9 @@ jscan_status jscan_prefill_fused(const void *x, const void *delta_low, const voi
     using U = uint16_t;
     const jscan::Segments sg{L, L, 1, 0};
     const jscan::DeltaProj dp{static_cast<const U *>(delta_low), static_cast<const U *>(w_dt), b_dt};
-    jscan::launch_prefill_rows<jscan::BF16, false, true>(static_cast<const U *>(x), nullptr, A,
-                                                         static_cast<const U *>(B), static_cast<const U *>(C), h0,
-                                                         static_cast<U *>(y), h_final, nullptr, sg, batch, (int)D, s,
-                                                         dp);
+    jscan::launch_prefill_rows<jscan::BF16, true>(static_cast<const U *>(x), nullptr, A, static_cast<const U *>(B),
+                                                  static_cast<const U *>(C), h0, static_cast<U *>(y), h_final, sg,
+                                                  batch, (int)D, s, dp);
     return launch_status();
 }
 

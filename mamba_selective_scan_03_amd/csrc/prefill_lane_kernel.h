@@ -13,25 +13,23 @@
 namespace jscan {
 
 // One lane scans one channel of one row (see Segments) from the row's initial state (zero
-// when h0 is null).  A segment-summary launch (kSummary) writes no y; it writes the row's
-// final state and the sum of the row's delta values to dsum[row][D].  With a scaled-identity
+// when h0 is null), writing y and the row's final state.  With a scaled-identity
 // A (AF), A is a[D] and the channel's one decay per token serves all 16 states; with a complex
 // state, states 2k and 2k+1 form one complex state advanced by advance_complex().  With the
 // exponential-trapezoidal rule (Trap, see trap_left_in) each token also takes in the previous
 // token's input; the token before the row's first is (xp[row][D], bp[row][16]), or none.
-template <typename E, bool kSummary, AForm AF = AForm::Diagonal, bool kTrap = false>
+template <typename E, AForm AF = AForm::Diagonal, bool kTrap = false>
 __global__ __launch_bounds__(64) void prefill_lane_kernel(
     const typename E::store_t *__restrict__ x, const typename E::store_t *__restrict__ dl,
     const float *__restrict__ A, const typename E::store_t *__restrict__ B,
     const typename E::store_t *__restrict__ C, const float *__restrict__ h0,
-    typename E::store_t *__restrict__ y, float *__restrict__ h_final, float *__restrict__ dsum, Segments sg, int D,
-    int blocks_per_row, Trap tr) {
+    typename E::store_t *__restrict__ y, float *__restrict__ h_final, Segments sg, int D, int blocks_per_row,
+    Trap tr) {
     const int vrow = blockIdx.x / blocks_per_row;
     const int d = (blockIdx.x - vrow * blocks_per_row) * 64 + threadIdx.x;
     if (d >= D) return;  // no cross-lane work below, so idle lanes may leave
     const RowSpan span = row_span(sg, vrow);
 
-    static_assert((AF == AForm::Diagonal && !kTrap) || !kSummary, "the other forms run the plain prefill");
     constexpr bool kScalarA = AF == AForm::ScaledIdentity, kComplexA = AF == AForm::ComplexPairs;
     float a2[kDState], h[kDState];
 #pragma unroll
@@ -62,7 +60,6 @@ __global__ __launch_bounds__(64) void prefill_lane_kernel(
         for (int n = 0; n < kDState; ++n) bprev[n] = E::load(static_cast<const S *>(tr.B_prev) + vrow * kDState + n);
     }
 
-    float dacc = 0.0f;
     for (int64_t t = 0; t < span.len; ++t) {
         const float xv = E::load(xr + t * D), dv = E::load(dr + t * D);
         float dx = delta_x(dv, xv);
@@ -92,19 +89,15 @@ __global__ __launch_bounds__(64) void prefill_lane_kernel(
             for (int n = 0; n < kDState; ++n) {
                 const float b = E::load(Br + t * kDState + n);
                 h[n] = kScalarA ? advance_decayed(h[n], abar, dx, b) : advance(h[n], dv, a2[n], dx, b);
-                if constexpr (!kSummary) acc = __builtin_fmaf(E::load(Cr + t * kDState + n), h[n], acc);
+                acc = __builtin_fmaf(E::load(Cr + t * kDState + n), h[n], acc);
             }
         }
-        if constexpr (kSummary)
-            dacc += dv;
-        else
-            E::store(yr + t * D, acc);
+        E::store(yr + t * D, acc);
     }
     if (span.state >= 0) {
 #pragma unroll
         for (int n = 0; n < kDState; ++n) h_final[((int64_t)span.state * D + d) * kDState + n] = h[n];
     }
-    if constexpr (kSummary) dsum[(int64_t)vrow * D + d] = dacc;
 }
 
 // Fills the final state when there are no tokens: copies h0, or writes zeros.

@@ -32,9 +32,9 @@
 // A ragged last tile is padded with identity tokens (delta = 0, x = -0, B = C = 0): they
 // leave every state bit-identical (decay 2^0 = 1, input term -0) and their y is not stored.
 //
-// Modes (template parameters): a segment-summary pass for the time-parallel prefill
-// (kSummary), delta computed on the load path from the low-rank projection (kFused), the form
-// of A (AF: diagonal, scaled identity, complex pairs) and the exponential-trapezoidal rule
+// Modes (template parameters): delta computed on the load path from the low-rank projection
+// (kFused), the form of A (AF: diagonal, scaled identity, complex pairs) and the
+// exponential-trapezoidal rule
 // (kTrap: the helper waves also stage the left-end weights and the previous token's B, and the
 // scan lane takes the left end point in first, one more DPP-fused FMA per state element).
 #pragma once
@@ -388,13 +388,11 @@ template <int i> __device__ __forceinline__ float component(const float4 &v) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// One token: advance this lane's two states and return C*h summed over them (a summary
-// scan adds the token's delta to `dsum` instead and returns nothing useful).  With a
+// One token: advance this lane's two states and return C*h summed over them.  With a
 // scaled-identity A the pair's second member is already the decay; with a complex state the
 // lane's two states are one complex state and (a2_0, a2_1) its prepared ComplexA.
-template <int TAU, bool kSummary, AForm AF, bool kTrap = false>
-__device__ __forceinline__ float token_step(const GroupRegs &g, float &h_0, float &h_1, float a2_0, float a2_1,
-                                            float &dsum) {
+template <int TAU, AForm AF, bool kTrap = false>
+__device__ __forceinline__ float token_step(const GroupRegs &g, float &h_0, float &h_1, float a2_0, float a2_1) {
     if constexpr (kTrap) {   // the left end point: h + p * B_prev, the DPP broadcast folded in
         const float pl = component<TAU & 3>(g.pv[TAU >> 2]);
         fmac2_bcast<TAU>(h_0, h_1, g.bp0, g.bp1, pl);
@@ -411,38 +409,24 @@ __device__ __forceinline__ float token_step(const GroupRegs &g, float &h_0, floa
         h_0 = advance(h_0, dv, a2_0, dxv, row_bcast<TAU>(g.b0));
         h_1 = advance(h_1, dv, a2_1, dxv, row_bcast<TAU>(g.b1));
     }
-    if constexpr (kSummary) {
-        dsum += dv;
-        return 0.0f;
-    } else {
-        return fmac_bcast<TAU>(row_bcast<TAU>(g.c0) * h_0, g.c1, h_1);
-    }
+    return fmac_bcast<TAU>(row_bcast<TAU>(g.c0) * h_0, g.c1, h_1);
 }
 
 // Advance this lane's two states over tokens 8H..8H+7 of a 16-token group and leave their y
 // partials (summed over the wave's 4 rows) in the y exchange rows `ys` (row = token in group).
-// A segment-summary scan (kSummary) produces no y; it adds the tokens' delta to `dsum` in
-// token order instead, and the y arithmetic is left out of the code altogether.
-template <int H, bool kSummary, AForm AF, bool kTrap = false>
+template <int H, AForm AF, bool kTrap = false>
 __device__ __forceinline__ void scan_half(const GroupRegs &g, float &h_0, float &h_1, float a2_0, float a2_1, float *ys,
-                                          int rt, int ch, float &dsum) {
+                                          int rt, int ch) {
     float P[8];
-#define JSCAN_STEP(i) P[i] = token_step<8 * H + (i), kSummary, AF, kTrap>(g, h_0, h_1, a2_0, a2_1, dsum);
+#define JSCAN_STEP(i) P[i] = token_step<8 * H + (i), AF, kTrap>(g, h_0, h_1, a2_0, a2_1);
     JSCAN_STEP(0) JSCAN_STEP(1) JSCAN_STEP(2) JSCAN_STEP(3)
     JSCAN_STEP(4) JSCAN_STEP(5) JSCAN_STEP(6) JSCAN_STEP(7)
 #undef JSCAN_STEP
-    if constexpr (kSummary) {
-        // Nothing stores from this half, so without an anchor the compiler may sink the whole
-        // state chain past the scheduling barriers to the end of the tile, keeping every
-        // broadcast operand alive until then.  The empty asm pins the states here.
-        asm volatile("" : "+v"(h_0), "+v"(h_1), "+v"(dsum));
-    } else {
-        // rows -> one register per 4 tokens; row r holds token 4j + {0,2,1,3}[r]
-        float ra, rb;
-        reduce_rows4x2(P, ra, rb);
-        ys[(8 * H + rt) * rows::kYStride + ch] = ra;
-        ys[(8 * H + 4 + rt) * rows::kYStride + ch] = rb;
-    }
+    // rows -> one register per 4 tokens; row r holds token 4j + {0,2,1,3}[r]
+    float ra, rb;
+    reduce_rows4x2(P, ra, rb);
+    ys[(8 * H + rt) * rows::kYStride + ch] = ra;
+    ys[(8 * H + 4 + rt) * rows::kYStride + ch] = rb;
 }
 // The same half split in two: the tokens' partials (computed in one scheduling region) and their
 // reduction over rows and store (done in the next region, beside the next half's tokens).  The
@@ -451,8 +435,7 @@ __device__ __forceinline__ void scan_half(const GroupRegs &g, float &h_0, float 
 template <int H, AForm AF, bool kTrap = false>
 __device__ __forceinline__ void half_partials(const GroupRegs &g, float &h_0, float &h_1, float a2_0, float a2_1,
                                               float (&P)[8]) {
-    float dsum = 0.0f;
-#define JSCAN_STEP(i) P[i] = token_step<8 * H + (i), false, AF, kTrap>(g, h_0, h_1, a2_0, a2_1, dsum);
+#define JSCAN_STEP(i) P[i] = token_step<8 * H + (i), AF, kTrap>(g, h_0, h_1, a2_0, a2_1);
     JSCAN_STEP(0) JSCAN_STEP(1) JSCAN_STEP(2) JSCAN_STEP(3)
     JSCAN_STEP(4) JSCAN_STEP(5) JSCAN_STEP(6) JSCAN_STEP(7)
 #undef JSCAN_STEP
@@ -508,21 +491,19 @@ __device__ __forceinline__ void write_final(const FinalRegs &F, typename E::stor
 }
 
 // One work-group scans 32 channels of one row (see Segments) from the row's initial state
-// (zero when h0 is null).  A segment-summary launch (kSummary) writes no y; it writes the
-// row's final state and, per channel, the sum of the row's delta values to dsum[row][D].
-// With kFused, delta is not read: the helper waves compute it from dp (bf16 only).  With
+// (zero when h0 is null).  With kFused, delta is not read: the helper waves compute it from dp (bf16 only).  With
 // a scaled-identity A (AF), A is a[D] (one value per channel) instead of A[D][16]; with a
 // complex state, A[D][16] holds 8 complex entries per channel as (real, imaginary) pairs.  With
 // kTrap the exponential-trapezoidal rule replaces the Euler rule (extra inputs in tr).
-template <typename E, bool kSummary, bool kFused = false, AForm AF = AForm::Diagonal, bool kTrap = false>
+template <typename E, bool kFused = false, AForm AF = AForm::Diagonal, bool kTrap = false>
 __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_rows_kernel(
     const typename E::store_t *__restrict__ x, const typename E::store_t *__restrict__ dl,
     const float *__restrict__ A, const typename E::store_t *__restrict__ B,
     const typename E::store_t *__restrict__ C, const float *__restrict__ h0,
-    typename E::store_t *__restrict__ y, float *__restrict__ h_final, float *__restrict__ dsum, Segments sg, int D,
-    int blocks_per_row, int xcd_stride, DeltaProj dp, Trap tr) {
-    static_assert(!kFused || (sizeof(typename E::store_t) == 2 && !kSummary), "the fused delta path is bf16 only");
-    static_assert((AF == AForm::Diagonal && !kTrap) || (!kSummary && !kFused),
+    typename E::store_t *__restrict__ y, float *__restrict__ h_final, Segments sg, int D, int blocks_per_row,
+    int xcd_stride, DeltaProj dp, Trap tr) {
+    static_assert(!kFused || sizeof(typename E::store_t) == 2, "the fused delta path is bf16 only");
+    static_assert((AF == AForm::Diagonal && !kTrap) || !kFused,
                   "the other forms of A and the trapezoidal rule run the plain prefill");
     constexpr bool kScalarA = AF == AForm::ScaledIdentity;
     using S = typename E::store_t;
@@ -611,7 +592,7 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
                     if constexpr (kFused) load_dlow(dfr[nxt], dp.d_low, row, (int64_t)(k + 3) * rows::kT, L, hw, l);
                 }
             }
-            if (!kSummary && k > 0) {
+            if (k > 0) {
                 read_final(F, y_s[nxt], tid);
                 write_final<E>(F, yb, (int64_t)(k - 1) * rows::kT, L, D, tid);
             }
@@ -621,10 +602,8 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
             tile(IntConst<0>{}, k);
             if (k + 1 < ntiles) tile(IntConst<1>{}, k + 1);
         }
-        if constexpr (!kSummary) {
-            read_final(F, y_s[(ntiles - 1) & 1], tid);
-            write_final<E>(F, yb, (int64_t)(ntiles - 1) * rows::kT, L, D, tid);
-        }
+        read_final(F, y_s[(ntiles - 1) & 1], tid);
+        write_final<E>(F, yb, (int64_t)(ntiles - 1) * rows::kT, L, D, tid);
         return;
     }
 
@@ -659,7 +638,6 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
     const int rt = (r == 1) ? 2 : (r == 2) ? 1 : r;   // token slot of this row after reduce_rows4
     __syncthreads();   // tile 0 staged by the helper waves
     GroupRegs G[2];
-    float dacc = 0.0f;
     load_half<0, kTrap>(G[0], dx_s[0], bc_s[0], p_s[0], 0, ch, n0, c);
     load_half<1, kTrap>(G[0], dx_s[0], bc_s[0], p_s[0], 0, ch, n0, c);
 
@@ -675,31 +653,31 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
         if constexpr (AF != AForm::ScaledIdentity) {
             load_half<0, kTrap>(G[1], dxc, bcc, psc, 16, ch, n0, c);
             JSCAN_SB;
-            scan_half<0, kSummary, AF, kTrap>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch, dacc);
+            scan_half<0, AF, kTrap>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch);
             JSCAN_SB;
             load_half<1, kTrap>(G[1], dxc, bcc, psc, 16, ch, n0, c);
             JSCAN_SB;
-            scan_half<1, kSummary, AF, kTrap>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch, dacc);
+            scan_half<1, AF, kTrap>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch);
             JSCAN_SB;
             load_half<0, kTrap>(G[0], dxc, bcc, psc, 32, ch, n0, c);
             JSCAN_SB;
-            scan_half<0, kSummary, AF, kTrap>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch, dacc);
+            scan_half<0, AF, kTrap>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch);
             JSCAN_SB;
             load_half<1, kTrap>(G[0], dxc, bcc, psc, 32, ch, n0, c);
             JSCAN_SB;
-            scan_half<1, kSummary, AF, kTrap>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch, dacc);
+            scan_half<1, AF, kTrap>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch);
             JSCAN_SB;
             load_half<0, kTrap>(G[1], dxc, bcc, psc, 48, ch, n0, c);
             JSCAN_SB;
-            scan_half<0, kSummary, AF, kTrap>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch, dacc);
+            scan_half<0, AF, kTrap>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch);
             JSCAN_SB;
             load_half<1, kTrap>(G[1], dxc, bcc, psc, 48, ch, n0, c);
             JSCAN_SB;
-            scan_half<1, kSummary, AF, kTrap>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch, dacc);
+            scan_half<1, AF, kTrap>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch);
             JSCAN_SB;
-            scan_half<0, kSummary, AF, kTrap>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch, dacc);
+            scan_half<0, AF, kTrap>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch);
             JSCAN_SB;
-            scan_half<1, kSummary, AF, kTrap>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch, dacc);
+            scan_half<1, AF, kTrap>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch);
         } else {
             float Pa[8], Pb[8];
             load_half<0, kTrap>(G[1], dxc, bcc, psc, 16, ch, n0, c);
@@ -752,9 +730,6 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
     }
     if (span.state >= 0)
         *reinterpret_cast<float2 *>(h_final + ((int64_t)span.state * D + d) * kDState + n0) = make_float2(h_0, h_1);
-    if constexpr (kSummary) {
-        if (n0 == 0) dsum[(int64_t)vrow * D + d] = dacc;
-    }
 }
 
 // The row-mapped kernel needs whole 32-channel blocks.  It serves every batch: even where one
@@ -763,17 +738,17 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
 inline bool rows_kernel_applies(int64_t /*batch*/, int64_t D) { return D % rows::kCh == 0; }
 
 // Launches one work-group per 32 channels of each of the `nrows` rows described by sg.
-template <typename E, bool kSummary, bool kFused = false, AForm AF = AForm::Diagonal, bool kTrap = false>
+template <typename E, bool kFused = false, AForm AF = AForm::Diagonal, bool kTrap = false>
 void launch_prefill_rows(const typename E::store_t *x, const typename E::store_t *dl, const float *A,
                          const typename E::store_t *B, const typename E::store_t *C, const float *h0,
-                         typename E::store_t *y, float *h_final, float *dsum, const Segments &sg, int64_t nrows,
+                         typename E::store_t *y, float *h_final, const Segments &sg, int64_t nrows,
                          int D, hipStream_t stream, DeltaProj dp = DeltaProj{nullptr, nullptr, nullptr},
                          Trap tr = Trap{nullptr, nullptr, nullptr}) {
     const int blocks_per_row = D / rows::kCh;
     const int64_t blocks = nrows * blocks_per_row;
     const int xcd_stride = (blocks % 8 == 0) ? (int)(blocks / 8) : 0;
-    hipLaunchKernelGGL((prefill_rows_kernel<E, kSummary, kFused, AF, kTrap>), dim3((unsigned)blocks),
-                       dim3(rows::kThreads), 0, stream, x, dl, A, B, C, h0, y, h_final, dsum, sg, D, blocks_per_row,
+    hipLaunchKernelGGL((prefill_rows_kernel<E, kFused, AF, kTrap>), dim3((unsigned)blocks),
+                       dim3(rows::kThreads), 0, stream, x, dl, A, B, C, h0, y, h_final, sg, D, blocks_per_row,
                        xcd_stride, dp, tr);
 }
 
