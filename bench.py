@@ -364,10 +364,80 @@ def trace_summary(directory: str, warmup: int) -> str:
     out = []
     for name, us in by_kernel.items():
         kept = us[warmup:] if len(us) > warmup else us
-        out.append(f"{name}\n    launches {len(us)}, after the first {len(us) - len(kept)}: median "
+        # the bench also makes short launches of its own (checks on a few tokens): leave out
+        # those under a quarter of the median
+        med = statistics.median(kept)
+        short = [u for u in kept if u < med / 4]
+        kept = [u for u in kept if u >= med / 4]
+        out.append(f"{name}\n    launches {len(us)}, after the first {len(us) - len(kept) - len(short)}"
+                   f"{f' (and {len(short)} short ones)' if short else ''}: median "
                    f"{statistics.median(kept):.1f} us, mean {statistics.fmean(kept):.1f}, min {min(kept):.1f}, "
                    f"max {max(kept):.1f}")
     return "\n".join(out)
+
+
+def counter_summary(args, fetch_dir: str, write_dir: str) -> str:
+    """HBM traffic of the dominant kernel of a workload and mode from two rocprofv3 --pmc runs
+    (FETCH_SIZE in fetch_dir, WRITE_SIZE in write_dir), per launch (every dispatch of the kernel
+    is counted: mean, and the spread over dispatches), scaled by what the counters read for a
+    plain device-to-device copy of 1 GiB (profiles/counters_copy_calibration.txt)."""
+    import csv
+    import glob
+    import statistics
+    import workloads
+    wl = workloads.get(args.workload)
+    decode = wl.layers > 1
+    name = ("jscan::step_mimo_kernel<" if args.mimo else "jscan::step_kernel<") if decode else \
+        ("jscan::prefill_mimo_rows_kernel<" if args.mimo else "jscan::prefill_rows_kernel<")
+    cal = {}
+    for line in open(os.path.join(ROOT, "profiles", "counters_copy_calibration.txt")):
+        m = re.match(r"\s*(\w+)\s*=\s*([0-9.eE+-]+)\s*$", line)
+        if m:
+            cal[m.group(1)] = float(m.group(2))
+    fetch_scale = (1 << 20) / cal["copy_fetch_KiB_per_GiB"]
+    write_scale = (1 << 20) / cal["copy_write_KiB_per_GiB"]
+
+    def per_dispatch(directory, counter):
+        # the workload's launches are the kernel's long ones (the bench also makes short
+        # launches of its own, e.g. the bit-exactness check on a few tokens)
+        vals, dur = {}, {}
+        for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+            with open(path, newline="") as fh:
+                for r in csv.DictReader(fh):
+                    if r["Counter_Name"] == counter and r["Kernel_Name"].startswith("void " + name):
+                        key = (path, r["Dispatch_Id"])
+                        vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+                        dur[key] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        top = max(dur.values(), default=0)
+        return [v for k, v in vals.items() if dur[k] >= top / 2]
+    fetch, write = per_dispatch(fetch_dir, "FETCH_SIZE"), per_dispatch(write_dir, "WRITE_SIZE")
+    if not fetch or not write:
+        return f"no dispatches of {name} in {fetch_dir} / {write_dir}"
+    alg = algorithmic_bytes(wl, args.trapezoid, args.mimo)
+    if args.scalar_a:
+        alg -= (wl.D * wl.N - wl.D) * 4 * max(wl.layers, 1)
+    launches = wl.layers if decode else 1
+    rd = statistics.fmean(fetch) * 1024 * fetch_scale
+    wr = statistics.fmean(write) * 1024 * write_scale
+    kind = ("step" if decode else "prefill") + ("_mimo" if args.mimo else "")
+    lines = [
+        f"kernel = {name}...>",
+        f"fetch_scale = {fetch_scale:.4f}",
+        f"write_scale = {write_scale:.4f}",
+        f"dispatches_fetch = {len(fetch)}",
+        f"dispatches_write = {len(write)}",
+        f"FETCH_SIZE_KiB_per_launch = {statistics.fmean(fetch):.6g}",
+        f"FETCH_SIZE_KiB_per_launch_min_median_max = {min(fetch):.6g} {statistics.median(fetch):.6g} {max(fetch):.6g}",
+        f"WRITE_SIZE_KiB_per_launch = {statistics.fmean(write):.6g}",
+        f"WRITE_SIZE_KiB_per_launch_min_median_max = {min(write):.6g} {statistics.median(write):.6g} {max(write):.6g}",
+        f"hbm_read_bytes_per_launch = {rd:.6g}",
+        f"hbm_write_bytes_per_launch = {wr:.6g}",
+        f"hbm_bytes_per_launch = {rd + wr:.6g}",
+        f"algorithmic_bytes_per_launch = {alg // launches}",
+        f"traffic_over_algorithmic = {(rd + wr) / (alg / launches):.4f}",
+        f"kernel_source_hash = {kernel_source_hash(kind)}",
+    ]
+    return "\n".join(lines)
 
 
 def main():
@@ -411,6 +481,10 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the scan, time a plain device-to-device copy of MIB mebibytes (the reference "
                          "kernel for scaling the profiler's FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--counter-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="instead of the scan, summarise two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of "
+                         "this workload and mode: the dominant kernel's HBM bytes per launch, scaled by the copy "
+                         "calibration in profiles/counters_copy_calibration.txt, against its algorithmic bytes")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="instead of the scan, summarise the rocprofv3 kernel trace(s) in DIR (*kernel_trace.csv): "
                          "per kernel, the launches after the first WARMUP, their median, mean, min and max")
@@ -418,6 +492,9 @@ def main():
 
     if args.trace_summary:
         print(trace_summary(args.trace_summary, args.warmup or 0))
+        return
+    if args.counter_summary:
+        print(counter_summary(args, *args.counter_summary))
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

@@ -15,13 +15,12 @@ pytestmark = pytest.mark.gpu
 def step_chain(d, h, t0=0, t1=None):
     """Feed tokens [t0, t1) one by one through jscan_step using strided token views."""
     t1 = d["x"].shape[1] if t1 is None else t1
-    # y rows go into one preallocated [batch, tokens, D] tensor: without y_t, step() would
-    # allocate each y_t with x_t's row stride (L * D here)
-    y = torch.empty((d["x"].shape[0], t1 - t0, d["x"].shape[2]), dtype=d["x"].dtype, device=d["x"].device)
+    # y rows go into one preallocated tensor shaped like x (y_t shares x_t's row stride in the
+    # ABI): without y_t, step() would allocate a batch x L x D tensor for every token
+    y = torch.empty_like(d["x"])
     ys = []
     for t in range(t0, t1):
-        ys.append(jscan.step(h, d["x"][:, t], d["delta"][:, t], d["A"], d["B"][:, t], d["C"][:, t],
-                             y_t=y[:, t - t0]))
+        ys.append(jscan.step(h, d["x"][:, t], d["delta"][:, t], d["A"], d["B"][:, t], d["C"][:, t], y_t=y[:, t]))
     return ys
 
 
