@@ -500,7 +500,8 @@ void launch_ssm_inputs(const uint16_t *x, const uint16_t *w_x, const float *g_d,
                        const uint16_t *w_dt, const float *b_dt, uint16_t *d_low, uint16_t *delta, uint16_t *B,
                        uint16_t *C, int64_t M, int D, float eps, hipStream_t stream) {
     const int64_t row_tiles = (M + jscan::proj::kRowsX - 1) / jscan::proj::kRowsX;
-    hipLaunchKernelGGL((jscan::xproj_kernel<R / 16>), dim3((unsigned)row_tiles), dim3(jscan::proj::kXThreads), 0, stream,
+    hipLaunchKernelGGL((jscan::xproj_kernel<R / 16, jscan::proj::kXRowTiles>), dim3((unsigned)row_tiles),
+                       dim3(jscan::proj::xproj_threads(jscan::proj::kXRowTiles)), 0, stream,
                        x, w_x, g_d,
                        g_b, g_c, d_low, B, C, M, D, eps);
     if (!delta) return;   // x projection only: delta is computed inside jscan_prefill_fused

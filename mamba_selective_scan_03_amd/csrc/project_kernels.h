@@ -51,38 +51,40 @@ __device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds) {
 // low four bits and bits 14-15; expcnt and lgkmcnt at their maxima, so they do not wait).
 template <int n> constexpr int vmcnt_only() { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-// x projection: one work-group = 128 rows (tokens) x all R + 2N output columns, eight waves in
-// a 4 x 2 grid: wave (wr, wc) owns rows 32 wr .. 32 wr + 31 (two 16-row tiles) and the half
-// wc of the CT = R / 16 + 2 column tiles (d_low's R / 16 tiles, then one each of B and C).
+// x projection: one work-group = 128 rows (tokens) x all R + 2N output columns.  Its waves form
+// a (128 / 16 kRT) x 2 grid: wave (wr, wc) owns kRT 16-row tiles (rows 16 kRT wr ..) and the
+// half wc of the CT = R / 16 + 2 column tiles (d_low's R / 16 tiles, then one each of B and
+// C).  The launcher uses kRT = 2: eight waves, two per SIMD, each with 32 rows x 144 columns.
+// (kRT = 4, four waves of 64 rows, reads a third less from LDS per stage, but with one wave
+// per SIMD nothing hides the operand reads' latency: 0.378 against 0.358 ms on 64K x 8192.)
 // K (= D) goes in stages of 64.  Each stage's x tile [128][64] and W_x tile [16 CT][64] go
 // from memory straight into LDS (global_load_lds_dwordx4, 1 KB per wave instruction), three
 // stages deep, so a stage's loads are issued two stages before its MFMAs and take no
 // registers.  A tile row (64 bf16, 128 bytes) holds its eight 16-byte chunks XOR-swizzled with
-// (row / 2) % 8, so the 16 rows one operand read touches fall on distinct banks.  Two waves per
-// SIMD, and a register budget that keeps the accumulators in place, let one wave's operand
-// reads and MFMAs overlap the other's.
+// (row / 2) % 8, so the 16 rows one operand read touches fall on distinct banks.
 namespace proj {
 constexpr int kStageK = 64;          // K per stage
-constexpr int kXThreads = 512;       // threads of an x-projection work-group
 constexpr int kXBufs = 3;            // stages in LDS: the one being read and two in flight
+constexpr int kXRowTiles = 2;        // 16-row tiles per wave (the launcher's layout)
+constexpr int xproj_threads(int kRT) { return 2 * (kRowsX / (16 * kRT)) * 64; }
 }
 
 // LDS position (in 16-byte chunks) of chunk c of row r of a swizzled 64-wide tile.
 __device__ __forceinline__ int swz64(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
-// One stage's MFMAs of one wave: its 32 rows (two 16-row tiles) against its CH column tiles
+// One stage's MFMAs of one wave: its kRT row tiles (from row r0) against its CH column tiles
 // (from tile c0), two 32-wide k steps, operands read from LDS.  All of the stage's operands
 // are requested before the first MFMA, so their LDS latency overlaps the matrix work.
-template <int CH>
-__device__ __forceinline__ void xproj_mfma(f32x4_t (&acc)[2][CH], const uint16_t *xs, const uint16_t *ws, int wr,
+template <int kRT, int CH>
+__device__ __forceinline__ void xproj_mfma(f32x4_t (&acc)[kRT][CH], const uint16_t *xs, const uint16_t *ws, int r0,
                                            int c0, int r16, int g4) {
-    bf16x8_t a[2][2], b[2][CH];
+    bf16x8_t a[2][kRT], b[2][CH];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < kRT; ++t)
             a[k][t] = __builtin_bit_cast(
-                bf16x8_t, *reinterpret_cast<const u32x4_t *>(xs + 8 * swz64(wr * 32 + 16 * t + r16, 4 * k + g4)));
+                bf16x8_t, *reinterpret_cast<const u32x4_t *>(xs + 8 * swz64(r0 + 16 * t + r16, 4 * k + g4)));
 #pragma unroll
         for (int c = 0; c < CH; ++c)
             b[k][c] = __builtin_bit_cast(
@@ -92,45 +94,46 @@ __device__ __forceinline__ void xproj_mfma(f32x4_t (&acc)[2][CH], const uint16_t
 #pragma unroll
     for (int k = 0; k < 2; ++k)
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            acc[0][c] = mfma16(a[k][0], b[k][c], acc[0][c]);
-            acc[1][c] = mfma16(a[k][1], b[k][c], acc[1][c]);
-        }
+        for (int c = 0; c < CH; ++c)
+#pragma unroll
+            for (int t = 0; t < kRT; ++t) acc[t][c] = mfma16(a[k][t], b[k][c], acc[t][c]);
 }
 
-template <int RT>
-__global__ __launch_bounds__(proj::kXThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void xproj_kernel(
+template <int RT, int kRT>
+__global__ __launch_bounds__(proj::xproj_threads(kRT))
+__attribute__((amdgpu_waves_per_eu(proj::xproj_threads(kRT) / 256, proj::xproj_threads(kRT) / 256))) void xproj_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ g_d,
     const float *__restrict__ g_b, const float *__restrict__ g_c, uint16_t *__restrict__ d_low,
     uint16_t *__restrict__ Bo, uint16_t *__restrict__ Co, int64_t M, int D, float eps) {
     constexpr int CT = RT + 2;   // column tiles
     constexpr int CH = CT / 2;   // column tiles per wave
     static_assert(CT % 2 == 0 && CH <= RT, "each wave half must hold d_low tiles only or d_low then B and C");
+    constexpr int kThreads = proj::xproj_threads(kRT), kWaves = kThreads / 64, kRowsW = 16 * kRT;
     constexpr int kXs = proj::kRowsX * proj::kStageK, kWs = 16 * CT * proj::kStageK;   // bf16 per stage
-    constexpr int kXInst = kXs / 512 / 8;                  // x DMA instructions per wave per stage
+    constexpr int kXInst = kXs / 512 / kWaves;             // x DMA instructions per wave per stage
     constexpr int kWInstAll = kWs / 512;                   // W DMA instructions per stage
-    constexpr int kWInst = (kWInstAll + 7) / 8;            // per wave (the last few repeat one)
+    constexpr int kWInst = (kWInstAll + kWaves - 1) / kWaves;   // per wave (the last few repeat one)
     constexpr int kDmaPerWave = kXInst + kWInst;
-    static_assert(kXs % (512 * 8) == 0, "the x tile is whole wave instructions per wave");
+    static_assert(kXs % (512 * kWaves) == 0, "the x tile is whole wave instructions per wave");
     __shared__ __attribute__((aligned(16))) uint16_t xs[proj::kXBufs][kXs];
     __shared__ __attribute__((aligned(16))) uint16_t ws[proj::kXBufs][kWs];
     __shared__ float ssq[2][proj::kRowsX];   // d_low sums of squares of each column half, per row
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
-    const int wr = wave & 3, wc = wave >> 2, c0 = CH * wc;
+    const int wr = wave >> 1, wc = wave & 1, c0 = CH * wc, r0 = kRowsW * wr;
     const int64_t row_base = (int64_t)blockIdx.x * proj::kRowsX;
     const int r16 = l & 15, g4 = l >> 4;
     const int stages = D / proj::kStageK;
 
-    f32x4_t acc[2][CH];
+    f32x4_t acc[kRT][CH];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < kRT; ++t)
 #pragma unroll
         for (int c = 0; c < CH; ++c) acc[t][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // This wave's loads of stage st into buffer b.  Wave instruction q of a tile fills its
     // chunk positions 64 q .. 64 q + 63; position P holds row P / 8's chunk (P % 8) ^ swizzle.
-    // Every wave issues kDmaPerWave instructions a stage: the W instructions past the tile's
-    // last repeat that one (the same bytes to the same place), so the counts stay uniform.
+    // Every wave issues kDmaPerWave instructions a stage: W instructions past the tile's last
+    // repeat that one (the same bytes to the same place), so the counts stay uniform.
     auto dma = [&](int st, int b) {
         const int k0 = st * proj::kStageK;
 #pragma unroll
@@ -159,7 +162,7 @@ __global__ __launch_bounds__(proj::kXThreads) __attribute__((amdgpu_waves_per_eu
         __syncthreads();   // every wave's part of stage s is in; every wave is done with s - 1
         if (s + 2 < stages) dma(s + 2, (s + 2) % proj::kXBufs);
         const int b = s % proj::kXBufs;
-        xproj_mfma<CH>(acc, xs[b], ws[b], wr, c0, r16, g4);
+        xproj_mfma<kRT, CH>(acc, xs[b], ws[b], r0, c0, r16, g4);
     }
 
     // Epilogue.  Lane l holds rows 4 * (l / 16) + i of each 16-row tile, column 16 c + l % 16.
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(proj::kXThreads) __attribute__((amdgpu_waves_per_eu
     // (half 0 + half 1, the same order in both waves).  B and C lie in half 1.
     constexpr int kDl1 = RT - CH;   // d_low tiles in half 1
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < kRT; ++t) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float sd = 0.f;
@@ -180,15 +183,15 @@ __global__ __launch_bounds__(proj::kXThreads) __attribute__((amdgpu_waves_per_eu
                 for (int c = 0; c < kDl1; ++c) sd = __builtin_fmaf(acc[t][c][i], acc[t][c][i], sd);
             }
             sd = row16_sum(sd);
-            if (r16 == 0) ssq[wc][wr * 32 + 16 * t + 4 * (l >> 4) + i] = sd;
+            if (r16 == 0) ssq[wc][r0 + 16 * t + 4 * (l >> 4) + i] = sd;
         }
     }
     __syncthreads();
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < kRT; ++t) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int rr = wr * 32 + 16 * t + 4 * (l >> 4) + i;
+            const int rr = r0 + 16 * t + 4 * (l >> 4) + i;
             const int64_t row = row_base + rr;
             const float sd = ssq[0][rr] + ssq[1][rr];
             const float nd = __builtin_amdgcn_rsqf(sd * (1.0f / (16 * RT)) + eps);
