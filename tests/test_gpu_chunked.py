@@ -23,13 +23,14 @@ def h0_for(batch, D, seed):
 
 
 @pytest.mark.parametrize("batch,L,D,dtype,chunk", [
-    (1, 1000, 64, "f32", 0),       # row-mapped kernel, automatic segments, ragged last tile
-    (1, 1000, 64, "bf16", 64),     # one tile per segment
-    (2, 777, 40, "f32", 100),      # D not a multiple of 32: lane kernel, ragged segments
+    (1, 1000, 64, "f32", 0),       # automatic plan: 3 segments of 384 tokens, ragged last one
+    (1, 1000, 64, "bf16", 64),     # 64-token segments
+    (2, 777, 40, "f32", 100),      # D not a multiple of 32 (state-order sums), ragged segments
     (2, 777, 40, "bf16", 0),
-    (3, 513, 96, "f32", 7),        # many short segments, shorter than a tile
-    (1, 300, 32, "f32", 1),        # one token per segment
-    (1, 4096, 1024, "bf16", 0),    # eight 512-token segments
+    (3, 513, 96, "f32", 7),        # segments shorter than the kernel's 16-token main loop
+    (1, 300, 32, "f32", 1),        # one token per segment; the carry's groups hold 19 segments
+    (1, 4096, 1024, "bf16", 0),    # automatic plan: 16 segments of 256 tokens
+    (2, 3000, 1000, "bf16", 0),    # 10 segments of 320 tokens a sequence; a partly filled work-group
 ])
 @pytest.mark.parametrize("with_h0", [False, True])
 def test_chunked_matches_oracle(batch, L, D, dtype, chunk, with_h0):
