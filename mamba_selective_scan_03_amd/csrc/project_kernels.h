@@ -19,7 +19,7 @@
 namespace jscan {
 
 namespace proj {
-constexpr int kRowsX = 128;   // x-projection rows (tokens) per work-group: 4 waves x 32
+constexpr int kRowsX = 256;   // x-projection rows (tokens) per work-group: 4 row groups x 64
 constexpr int kTileDt = 128;  // delta-projection channel slice of a work-group: two waves of 64 channels
 }
 
@@ -45,27 +45,36 @@ __device__ __forceinline__ float row16_sum(float v) {
 __device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
+// The same with the non-temporal hint, for data read once (it is not kept in the caches).
+__device__ __forceinline__ void lds_dma16_nt(const void *src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(lds)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // vmcnt for an s_waitcnt that leaves `n` vector-memory operations outstanding (gfx9 encoding:
 // low four bits and bits 14-15; expcnt and lgkmcnt at their maxima, so they do not wait).
 template <int n> constexpr int vmcnt_only() { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-// x projection: one work-group = 128 rows (tokens) x all R + 2N output columns.  Its waves form
-// a (128 / 16 kRT) x 2 grid: wave (wr, wc) owns kRT 16-row tiles (rows 16 kRT wr ..) and the
+// x projection: one work-group = 256 rows (tokens) x all R + 2N output columns.  Its waves form
+// a (256 / 16 kRT) x 2 grid: wave (wr, wc) owns kRT 16-row tiles (rows 16 kRT wr ..) and the
 // half wc of the CT = R / 16 + 2 column tiles (d_low's R / 16 tiles, then one each of B and
-// C).  The launcher uses kRT = 2: eight waves, two per SIMD, each with 32 rows x 144 columns.
-// (kRT = 4, four waves of 64 rows, reads a third less from LDS per stage, but with one wave
-// per SIMD nothing hides the operand reads' latency: 0.378 against 0.358 ms on 64K x 8192.)
-// K (= D) goes in stages of 64.  Each stage's x tile [128][64] and W_x tile [16 CT][64] go
-// from memory straight into LDS (global_load_lds_dwordx4, 1 KB per wave instruction), three
-// stages deep, so a stage's loads are issued two stages before its MFMAs and take no
-// registers.  A tile row (64 bf16, 128 bytes) holds its eight 16-byte chunks XOR-swizzled with
-// (row / 2) % 8, so the 16 rows one operand read touches fall on distinct banks.
+// C).  The launcher uses kRT = 4: eight waves, two per SIMD, each with 64 rows x 144 columns.
+// Every work-group reads all of W_x, so the rows per work-group set how much W_x traffic the
+// L2 serves per row of x: 256 rows halve it against 128, and the kernel went from 0.34 to
+// 0.27 ms on 64K x 8192.
+// K (= D) goes in stages of 64.  Each stage's x tile [256][64] and W_x tile [16 CT][64] go
+// from memory straight into LDS (global_load_lds_dwordx4, 1 KB per wave instruction) and take
+// no registers.  Two such stages fill the LDS, so a stage's loads are issued one stage before
+// its MFMAs.  (Stages of 32 with three or four buffers, x still read in whole 128-byte lines,
+// were slower, 0.31 ms: twice the barriers, each of which idles the matrix cores while a
+// stage's first operands come from LDS.)  x is read once and loaded non-temporal.  A tile row
+// (64 bf16, 128 bytes) holds its eight 16-byte chunks XOR-swizzled with (row / 2) % 8, so the
+// 16 rows one operand read touches fall on distinct banks.
 namespace proj {
 constexpr int kStageK = 64;          // K per stage
-constexpr int kXBufs = 3;            // stages in LDS: the one being read and two in flight
-constexpr int kXRowTiles = 2;        // 16-row tiles per wave (the launcher's layout)
+constexpr int kXBufs = 2;            // stages in LDS: the one being read and the next in flight
+constexpr int kXRowTiles = 4;        // 16-row tiles per wave (the launcher's layout)
 constexpr int xproj_threads(int kRT) { return 2 * (kRowsX / (16 * kRT)) * 64; }
 }
 
@@ -73,30 +82,30 @@ constexpr int xproj_threads(int kRT) { return 2 * (kRowsX / (16 * kRT)) * 64; }
 __device__ __forceinline__ int swz64(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
 // One stage's MFMAs of one wave: its kRT row tiles (from row r0) against its CH column tiles
-// (from tile c0), two 32-wide k steps, operands read from LDS.  All of the stage's operands
-// are requested before the first MFMA, so their LDS latency overlaps the matrix work.
+// (from tile c0), two 32-wide k steps, operands read from LDS.  Each k step's operands are
+// requested before its first MFMA, so their LDS latency overlaps the matrix work (the other
+// wave of the SIMD covers the rest); one k step at a time keeps the operands of 64 rows in
+// the register budget of two waves per SIMD.
 template <int kRT, int CH>
 __device__ __forceinline__ void xproj_mfma(f32x4_t (&acc)[kRT][CH], const uint16_t *xs, const uint16_t *ws, int r0,
                                            int c0, int r16, int g4) {
-    bf16x8_t a[2][kRT], b[2][CH];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
+        bf16x8_t a[kRT], b[CH];
 #pragma unroll
         for (int t = 0; t < kRT; ++t)
-            a[k][t] = __builtin_bit_cast(
+            a[t] = __builtin_bit_cast(
                 bf16x8_t, *reinterpret_cast<const u32x4_t *>(xs + 8 * swz64(r0 + 16 * t + r16, 4 * k + g4)));
 #pragma unroll
         for (int c = 0; c < CH; ++c)
-            b[k][c] = __builtin_bit_cast(
+            b[c] = __builtin_bit_cast(
                 bf16x8_t, *reinterpret_cast<const u32x4_t *>(ws + 8 * swz64(16 * (c0 + c) + r16, 4 * k + g4)));
-    }
-    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the MFMAs
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
+        __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the MFMAs
 #pragma unroll
         for (int c = 0; c < CH; ++c)
 #pragma unroll
-            for (int t = 0; t < kRT; ++t) acc[t][c] = mfma16(a[k][t], b[k][c], acc[t][c]);
+            for (int t = 0; t < kRT; ++t) acc[t][c] = mfma16(a[t], b[c], acc[t][c]);
+    }
 }
 
 template <int RT, int kRT>
@@ -110,11 +119,10 @@ __attribute__((amdgpu_waves_per_eu(proj::xproj_threads(kRT) / 256, proj::xproj_t
     static_assert(CT % 2 == 0 && CH <= RT, "each wave half must hold d_low tiles only or d_low then B and C");
     constexpr int kThreads = proj::xproj_threads(kRT), kWaves = kThreads / 64, kRowsW = 16 * kRT;
     constexpr int kXs = proj::kRowsX * proj::kStageK, kWs = 16 * CT * proj::kStageK;   // bf16 per stage
-    constexpr int kXInst = kXs / 512 / kWaves;             // x DMA instructions per wave per stage
-    constexpr int kWInstAll = kWs / 512;                   // W DMA instructions per stage
-    constexpr int kWInst = (kWInstAll + kWaves - 1) / kWaves;   // per wave (the last few repeat one)
-    constexpr int kDmaPerWave = kXInst + kWInst;
-    static_assert(kXs % (512 * kWaves) == 0, "the x tile is whole wave instructions per wave");
+    constexpr int kXInst = kXs / 512 / kWaves;   // x DMA instructions per wave per stage
+    constexpr int kWInstAll = kWs / 512;         // W DMA instructions per stage, dealt out to the
+    constexpr int kWJ = (kWInstAll + kWaves - 1) / kWaves;   // waves in turn (at most kWJ each)
+    static_assert(kXs % (512 * kWaves) == 0 && kWs % 512 == 0, "the tiles are whole wave instructions");
     __shared__ __attribute__((aligned(16))) uint16_t xs[proj::kXBufs][kXs];
     __shared__ __attribute__((aligned(16))) uint16_t ws[proj::kXBufs][kWs];
     __shared__ float ssq[2][proj::kRowsX];   // d_low sums of squares of each column half, per row
@@ -132,37 +140,35 @@ __attribute__((amdgpu_waves_per_eu(proj::xproj_threads(kRT) / 256, proj::xproj_t
 
     // This wave's loads of stage st into buffer b.  Wave instruction q of a tile fills its
     // chunk positions 64 q .. 64 q + 63; position P holds row P / 8's chunk (P % 8) ^ swizzle.
-    // Every wave issues kDmaPerWave instructions a stage: W instructions past the tile's last
-    // repeat that one (the same bytes to the same place), so the counts stay uniform.
+    // The x tile's instructions are split evenly over the waves; W instruction q goes to wave
+    // q % kWaves.
     auto dma = [&](int st, int b) {
         const int k0 = st * proj::kStageK;
 #pragma unroll
         for (int j = 0; j < kXInst; ++j) {
             const int q = wave * kXInst + j, P = q * 64 + l, r = P >> 3;
             const int c = (P & 7) ^ ((r >> 1) & 7);
-            lds_dma16(x + min(row_base + r, M - 1) * D + k0 + 8 * c,
+            lds_dma16_nt(x + min(row_base + r, M - 1) * D + k0 + 8 * c,
                       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)(xs[b] + q * 512));
         }
 #pragma unroll
-        for (int j = 0; j < kWInst; ++j) {
-            const int q = min(wave * kWInst + j, kWInstAll - 1), P = q * 64 + l, r = P >> 3;
-            const int c = (P & 7) ^ ((r >> 1) & 7);
-            lds_dma16(w + (int64_t)r * D + k0 + 8 * c,
-                      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)(ws[b] + q * 512));
+        for (int j = 0; j < kWJ; ++j) {
+            const int q = wave + kWaves * j;
+            if (q < kWInstAll) {
+                const int P = q * 64 + l, r = P >> 3;
+                const int c = (P & 7) ^ ((r >> 1) & 7);
+                lds_dma16(w + (int64_t)r * D + k0 + 8 * c,
+                          (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)(ws[b] + q * 512));
+            }
         }
     };
+    static_assert(proj::kXBufs == 2, "the loop below runs one stage ahead");
     dma(0, 0);
-    if (stages > 1) dma(1, 1);
     for (int s = 0; s < stages; ++s) {
-        // this wave's loads of stage s have landed once at most stage s + 1's are outstanding
-        if (s + 1 < stages)
-            __builtin_amdgcn_s_waitcnt(vmcnt_only<kDmaPerWave>());
-        else
-            __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
+        __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());   // this wave's loads of stage s have landed
         __syncthreads();   // every wave's part of stage s is in; every wave is done with s - 1
-        if (s + 2 < stages) dma(s + 2, (s + 2) % proj::kXBufs);
-        const int b = s % proj::kXBufs;
-        xproj_mfma<kRT, CH>(acc, xs[b], ws[b], r0, c0, r16, g4);
+        if (s + 1 < stages) dma(s + 1, (s + 1) & 1);
+        xproj_mfma<kRT, CH>(acc, xs[s & 1], ws[s & 1], r0, c0, r16, g4);
     }
 
     // Epilogue.  Lane l holds rows 4 * (l / 16) + i of each 16-row tile, column 16 c + l % 16.
