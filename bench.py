@@ -95,6 +95,7 @@ KERNEL_SOURCES = {
     "prefill_mimo": ["scan_update.h", "mfma_common.h", "prefill_rows_kernel.h", "step_kernel.h", "mimo_kernels.h",
                      "prefill_mimo_rows_kernel.h"],
     "step_mimo": ["scan_update.h", "step_kernel.h", "mimo_kernels.h"],
+    "producer": ["scan_update.h", "mfma_common.h", "project_kernels.h"],
 }
 
 
