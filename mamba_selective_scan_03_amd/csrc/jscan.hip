@@ -505,8 +505,8 @@ void launch_ssm_inputs(const uint16_t *x, const uint16_t *w_x, const float *g_d,
                        x, w_x, g_d,
                        g_b, g_c, d_low, B, C, M, D, eps);
     if (!delta) return;   // x projection only: delta is computed inside jscan_prefill_fused
-    // one work-group per CU (the LDS tiles allow one): 256 groups of (channel slice, token tiles)
-    const int ch_tiles = D / jscan::proj::kTileDt;
+    // one work-group per CU (the registers allow one): 256 groups of (channel slice, token tiles)
+    const int ch_tiles = (D + jscan::proj::kDtCh - 1) / jscan::proj::kDtCh;
     const int64_t tok_tiles = (M + jscan::proj::kDtTok - 1) / jscan::proj::kDtTok;
     int64_t groups = ch_tiles >= 256 ? 1 : 256 / ch_tiles;
     if (groups > tok_tiles) groups = tok_tiles;
@@ -800,10 +800,9 @@ jscan_status jscan_ssm_inputs(const void *x, const void *w_x, const float *g_del
     if (dtype != JSCAN_F32 && dtype != JSCAN_BF16) return JSCAN_ERR_DTYPE;
     if (dtype != JSCAN_BF16) return JSCAN_ERR_DTYPE;   // the matrix-core path is bf16 in, fp32 accumulate
     if (M < 0 || D <= 0 || N != JSCAN_D_STATE || (R != 64 && R != 128 && R != 256)) return JSCAN_ERR_SHAPE;
-    if (D % jscan::proj::kTileDt != 0 || D > (1 << 24)) return JSCAN_ERR_SHAPE;
+    if (D % 128 != 0 || D > (1 << 24)) return JSCAN_ERR_SHAPE;   // channels go in pairs of 64-channel waves
     if (!(eps >= 0.0f) || eps > 1.0f) return JSCAN_ERR_SHAPE;
-    const int64_t tok_tiles = (M + jscan::proj::kTileDt - 1) / jscan::proj::kTileDt;
-    if (tok_tiles * (D / jscan::proj::kTileDt) > kMaxBlocks) return JSCAN_ERR_SHAPE;
+    if ((M + jscan::proj::kRowsX - 1) / jscan::proj::kRowsX > kMaxBlocks) return JSCAN_ERR_SHAPE;
     if (M == 0) return JSCAN_OK;
     // delta == NULL: the x projection alone (w_dt and b_dt are then not used and may be NULL)
     const void *arrays[] = {x, w_x, g_delta, g_B, g_C, delta_low, B, C};

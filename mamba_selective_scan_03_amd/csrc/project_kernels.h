@@ -20,7 +20,6 @@ namespace jscan {
 
 namespace proj {
 constexpr int kRowsX = 256;   // x-projection rows (tokens) per work-group: 4 row groups x 64
-constexpr int kTileDt = 128;  // delta-projection channel slice of a work-group: two waves of 64 channels
 }
 
 // Sum over the 16 lanes of a DPP row (lanes 16q .. 16q+15); every lane gets the total.
@@ -225,21 +224,28 @@ __attribute__((amdgpu_waves_per_eu(proj::xproj_threads(kRT) / 256, proj::xproj_t
     }
 }
 
-// Delta projection.  A work-group owns one 128-channel slice of W_dt and walks the token
-// tiles t = g, g + G, g + 2G, ... (G groups per channel slice, kDtTok tokens a tile).  Each
-// wave keeps its 64 channels of W_dt as MFMA A operands in registers for the whole kernel.
-// A = W_dt and B = d_low^T, so each lane's result is 4 consecutive channels of one token.
+// Delta projection.  A work-group owns a 512-channel slice of W_dt: eight waves of 64 channels,
+// each holding its channels of W_dt as MFMA A operands in registers for the whole kernel.  It
+// walks the token tiles t = g, g + G, g + 2G, ... (G groups per channel slice, kDtTok tokens a
+// tile), and every wave computes its 64 channels for all of a tile's tokens.  A = W_dt and
+// B = d_low^T, so each lane's result is 4 consecutive channels of one token.  Every work-group
+// reads the d_low tiles of its group from the L2, so the channels per work-group set that
+// traffic (512 channels: 16 reads of d_low at D = 8192), and each token row of delta is written
+// in runs of 1 KB.
 //
 // d_low tiles go from memory straight into LDS (global_load_lds_dwordx4: each wave
 // instruction fills 1 KB of LDS, lane by lane), kDtBufs tiles deep, so a tile's loads are
 // issued two tiles before it is used and take no registers.  (The three tile buffers are
-// separate arrays so that each step of the loop, unrolled by three, names its own.)  Inside a tile row (one token's R
-// values) the 16-byte chunks are stored XOR-swizzled with the row index, so the 16 rows one
-// B-operand read touches fall on distinct banks.  Each wave's result (64 channels x 16
-// tokens) passes through a small LDS area of its own, which turns the MFMA layout (4
-// channels per lane) into whole 128-byte rows of delta: each lane then writes 16 bytes.
+// separate arrays so that each step of the loop, unrolled by three, names its own.)  Inside a
+// tile row (one token's R values) the 16-byte chunks are stored XOR-swizzled with the row
+// index, so the 16 rows one B-operand read touches fall on distinct banks.  Each wave's result
+// (64 channels x 16 tokens) passes through a small LDS area of its own, which turns the MFMA
+// layout (4 channels per lane) into whole 128-byte rows of delta: each lane then writes 16
+// bytes.  Waves whose channels lie past D (D a multiple of 128, not of 512) load and wait like
+// the others but compute and store nothing.
 namespace proj {
-constexpr int kDtTok = 64;    // tokens per d_low tile
+constexpr int kDtCh = 512;    // channels per work-group: eight waves of 64
+constexpr int kDtTok = 16;    // tokens per d_low tile
 constexpr int kDtBufs = 3;    // d_low tiles in LDS: the one being read and two in flight
 constexpr int kDtOutRow = 72; // bf16 per row of a wave's output area (64 channels + 8 padding)
 }
@@ -251,25 +257,28 @@ __global__ __launch_bounds__(512) void dtproj_kernel(const uint16_t *__restrict_
     constexpr int KS = R / 32;                                  // MFMA k steps
     constexpr int kRowChunks = R / 8;                           // 16-byte chunks per d_low row
     constexpr int kSwz = kRowChunks >= 16 ? 15 : kRowChunks - 1;
-    constexpr int kDma = proj::kDtTok * kRowChunks / (64 * 8);  // DMA instructions per wave per tile
+    constexpr int kDmaAll = proj::kDtTok * kRowChunks / 64;     // DMA wave instructions per tile
     constexpr int kSt = 2;                                      // global stores per wave per tile
-    static_assert(kDma >= 1 && proj::kDtTok * kRowChunks % (64 * 8) == 0, "a tile is whole wave instructions");
+    static_assert(proj::kDtTok * kRowChunks % 64 == 0 && kDmaAll >= 1 && kDmaAll <= 8,
+                  "a tile is whole wave instructions, at most one per wave");
     __shared__ __attribute__((aligned(16))) uint16_t tiles0[proj::kDtTok * R];
     __shared__ __attribute__((aligned(16))) uint16_t tiles1[proj::kDtTok * R];
     __shared__ __attribute__((aligned(16))) uint16_t tiles2[proj::kDtTok * R];
     __shared__ __attribute__((aligned(16))) uint16_t outs[8][16 * proj::kDtOutRow];
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
-    // Work-groups go to the 8 XCDs in turn (work-group b to XCD b % 8).  The groups that walk
-    // the same token tiles are kept on the same XCDs, so each XCD's L2 fetches only its share of
-    // d_low (when the group count divides 8; otherwise groups are spread over all XCDs).
+    // Work-groups go to the 8 XCDs in turn (work-group b to XCD b % 8).  The channel slices of a
+    // token group are kept on one XCD, so each XCD's L2 fetches only its groups' d_low tiles
+    // (when the group count is a multiple of 8; otherwise groups are spread over all XCDs).
     int ct = blockIdx.x % ch_tiles, grp = blockIdx.x / ch_tiles;
-    if (8 % groups == 0 && ch_tiles % (8 / groups) == 0 && (int)gridDim.x == groups * ch_tiles) {
+    if (groups % 8 == 0 && (int)gridDim.x == groups * ch_tiles) {
         const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
-        grp = xcd % groups;
-        ct = (xcd / groups) * (ch_tiles / (8 / groups)) + local;
+        grp = xcd * (groups / 8) + local / ch_tiles;
+        ct = local % ch_tiles;
     }
-    const int ch0 = ct * proj::kTileDt + 64 * (wave & 1);
-    const int tw = 16 * (wave >> 1);           // this wave's tokens inside a tile
+    const int ch0 = ct * proj::kDtCh + 64 * wave;
+    const bool active = ch0 < D;              // D is a multiple of 64: a wave is all in or all out
+    const int chw = active ? ch0 : D - 64;    // an idle wave's (unused) operands: any valid rows
+    const bool dma_wave = wave < kDmaAll;     // this wave issues one DMA instruction per tile
     const int r16 = l & 15, g4 = l >> 4, kq = 8 * g4;
     const int64_t tok_tiles = (M + proj::kDtTok - 1) / proj::kDtTok;
     const int count = grp < tok_tiles ? (int)((tok_tiles - grp + groups - 1) / groups) : 0;
@@ -278,54 +287,64 @@ __global__ __launch_bounds__(512) void dtproj_kernel(const uint16_t *__restrict_
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) a[u][ks] = load_frag(w + (int64_t)(ch0 + 16 * u + r16) * R + 32 * ks + kq);
+        for (int ks = 0; ks < KS; ++ks) a[u][ks] = load_frag(w + (int64_t)(chw + 16 * u + r16) * R + 32 * ks + kq);
     float4 bs[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) bs[u] = *reinterpret_cast<const float4 *>(bias + ch0 + 16 * u + 4 * g4);
+    for (int u = 0; u < 4; ++u) bs[u] = *reinterpret_cast<const float4 *>(bias + chw + 16 * u + 4 * g4);
 
-    // This wave's share of tile i's loads into buf: LDS chunk position P of the tile holds
-    // row P / kRowChunks, chunk (P % kRowChunks) ^ (row & kSwz) of that row.
+    // This wave's share of tile i's loads into buf (instruction `wave` of the tile): LDS chunk
+    // position P of the tile holds row P / kRowChunks, chunk (P % kRowChunks) ^ (row & kSwz).
     auto dma = [&](int i, uint16_t *buf) {
-        const int64_t t = grp + (int64_t)i * groups;
-#pragma unroll
-        for (int q = 0; q < kDma; ++q) {
-            const int inst = wave * kDma + q, P = inst * 64 + l;
+        if (dma_wave) {
+            const int64_t t = grp + (int64_t)i * groups;
+            const int P = wave * 64 + l;
             const int row = P / kRowChunks, c = (P % kRowChunks) ^ (row & kSwz);
             const int64_t tok = min(t * proj::kDtTok + row, M - 1);
             lds_dma16(d_low + tok * R + 8 * c,
-                      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)(buf + inst * 64 * 8));
+                      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)(buf + wave * 64 * 8));
+        }
+    };
+    // Wait for this wave's loads of tile i.  In issue order this wave's vector-memory operations
+    // are tiles 0 and 1's loads, then per tile j: tile j + 2's loads and tile j's stores.  After
+    // tile i's loads come tile i - 2's stores, tile i + 1's loads and tile i - 1's stores, so
+    // waiting until at most those are outstanding waits for tile i.  (Every store issues all its
+    // instructions but those of a partial tile, which is the last of its group; the last tile
+    // waits for everything.)
+    auto wait_tile = [&](int i) {
+        if (i + 1 >= count) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
+        } else if (!active) {   // no stores
+            if (dma_wave) __builtin_amdgcn_s_waitcnt(vmcnt_only<1>());
+            else __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
+        } else if (dma_wave) {
+            if (i == 0) __builtin_amdgcn_s_waitcnt(vmcnt_only<1>());
+            else if (i == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only<1 + kSt>());
+            else __builtin_amdgcn_s_waitcnt(vmcnt_only<1 + 2 * kSt>());
+        } else {
+            if (i == 0) __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
+            else if (i == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only<kSt>());
+            else __builtin_amdgcn_s_waitcnt(vmcnt_only<2 * kSt>());
         }
     };
     uint16_t *ow = outs[wave];
     // Tile i, read from rbuf; tile i + 2's loads go into dbuf (the buffer of tile i - 1).
     auto step = [&](int i, const uint16_t *rbuf, uint16_t *dbuf) {
-        // This wave's loads of tile i have landed when at most the vector-memory operations
-        // issued after them are outstanding: tile i + 1's loads and the stores of tiles i - 1
-        // and i - 2 (each of which issues all of its instructions: only a sequence's last tile
-        // can be partial, and it is its group's last).
-        if (i + 1 >= count)
-            __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
-        else if (i == 0)
-            __builtin_amdgcn_s_waitcnt(vmcnt_only<kDma>());
-        else if (i == 1)
-            __builtin_amdgcn_s_waitcnt(vmcnt_only<kDma + kSt>());
-        else
-            __builtin_amdgcn_s_waitcnt(vmcnt_only<kDma + 2 * kSt>());
+        wait_tile(i);
         __syncthreads();   // every wave's part of tile i is in; every wave is done with tile i - 1
         if (i + 2 < count) dma(i + 2, dbuf);
+        if (!active) return;
         const int64_t t = grp + (int64_t)i * groups;
-        const int row = tw + r16;
         f32x4_t acc[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const int c = (4 * ks + g4) ^ (row & kSwz);
-            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(rbuf + row * R + 8 * c));
+            const int c = (4 * ks + g4) ^ (r16 & kSwz);
+            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(rbuf + r16 * R + 8 * c));
 #pragma unroll
             for (int u = 0; u < 4; ++u) acc[u] = mfma16(a[u][ks], b, acc[u]);
         }
-        // bias, softplus, bf16: token tw + r16, channels 16 u + 4 g4 .. + 3 of the wave's 64
+        // bias, softplus, bf16: token r16 of the tile, channels 16 u + 4 g4 .. + 3 of the wave's 64
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             uint2 pk;
@@ -333,13 +352,14 @@ __global__ __launch_bounds__(512) void dtproj_kernel(const uint16_t *__restrict_
             pk.y = pack_bf16x2(softplus_f32(acc[u][2] + bs[u].z), softplus_f32(acc[u][3] + bs[u].w));
             *reinterpret_cast<uint2 *>(ow + r16 * proj::kDtOutRow + 16 * u + 4 * g4) = pk;
         }
-        // whole rows out: lane l writes 16 bytes (8 channels) of token row l / 8 + 8 k
+        // whole rows out: lane l writes 16 bytes (8 channels) of token row l / 8 + 8 k, with the
+        // non-temporal hint (delta is not read again here)
 #pragma unroll
         for (int k = 0; k < kSt; ++k) {
             const int orow = (l >> 3) + 8 * k, oc = l & 7;
             const u32x4_t v = *reinterpret_cast<const u32x4_t *>(ow + orow * proj::kDtOutRow + 8 * oc);
-            const int64_t tok = t * proj::kDtTok + tw + orow;
-            if (tok < M) *reinterpret_cast<u32x4_t *>(delta + tok * D + ch0 + 8 * oc) = v;
+            const int64_t tok = t * proj::kDtTok + orow;
+            if (tok < M) __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(delta + tok * D + ch0 + 8 * oc));
         }
     };
     if (count > 0) dma(0, tiles0);
