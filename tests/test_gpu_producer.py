@@ -79,10 +79,12 @@ def run(M, D, R, seed=0, rows=None):
 
 
 @pytest.mark.parametrize("M,D,R", [
-    (256, 256, 64),      # whole tiles
+    (256, 256, 64),      # one whole x-projection row tile; half of one delta channel slice
     (1000, 512, 128),    # ragged last row tile
     (777, 1024, 256),    # the full rank, ragged
     (1, 128, 256),       # a single token (decode-sized)
+    (300, 640, 256),     # a partial last delta channel slice (128 of 512 channels) and ragged tokens
+    (20007, 384, 64),    # about five token tiles per group, six of eight channel waves busy, ragged
 ])
 def test_ssm_inputs_match_oracle(M, D, R):
     run(M, D, R, seed=M + D)
