@@ -164,7 +164,7 @@ int64_t jscan_prefill_chunked_workspace(int64_t batch, int64_t L, int64_t D, int
  *   b_dt       [D]         fp32
  *   delta_low  [M][R]      out, bf16, the normalised d_low (also the input of the second product)
  *   delta      [M][D]      out, bf16;   B, C [M][N] out, bf16
- * R must be 64, 128 or 256; N = 16; D a multiple of 128; eps in [0, 1].  dtype must be
+ * R must be 64, 128 or 256; N = 16; D a multiple of 128; 0 <= M <= 2^31; eps in [0, 1].  dtype must be
  * JSCAN_BF16 (JSCAN_ERR_DTYPE otherwise).  Outputs must not overlap inputs or each other.
  * Two kernels are launched on `stream`, in order.  With delta == NULL only the first
  * product runs (delta_low, B and C; w_dt and b_dt may then be NULL): the input of

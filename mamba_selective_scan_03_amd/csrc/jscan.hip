@@ -802,7 +802,7 @@ jscan_status jscan_ssm_inputs(const void *x, const void *w_x, const float *g_del
     if (M < 0 || D <= 0 || N != JSCAN_D_STATE || (R != 64 && R != 128 && R != 256)) return JSCAN_ERR_SHAPE;
     if (D % 128 != 0 || D > (1 << 24)) return JSCAN_ERR_SHAPE;   // channels go in pairs of 64-channel waves
     if (!(eps >= 0.0f) || eps > 1.0f) return JSCAN_ERR_SHAPE;
-    if ((M + jscan::proj::kRowsX - 1) / jscan::proj::kRowsX > kMaxBlocks) return JSCAN_ERR_SHAPE;
+    if (M > ((int64_t)1 << 31)) return JSCAN_ERR_SHAPE;   // keeps the kernels' per-group tile counts in int
     if (M == 0) return JSCAN_OK;
     // delta == NULL: the x projection alone (w_dt and b_dt are then not used and may be NULL)
     const void *arrays[] = {x, w_x, g_delta, g_B, g_C, delta_low, B, C};

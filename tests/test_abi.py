@@ -217,7 +217,8 @@ def ssm_inputs(x=P, wx=P + 0x100000, gd=P + 0x200000, gb=P + 0x210000, gc=P + 0x
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=F32), EDTYPE), (dict(dtype=9), EDTYPE), (dict(R=96), ESHAPE), (dict(N=8), ESHAPE),
-    (dict(D=192), ESHAPE), (dict(M=-1), ESHAPE), (dict(eps=-1.0), ESHAPE), (dict(eps=float("nan")), ESHAPE),
+    (dict(D=192), ESHAPE), (dict(M=-1), ESHAPE), (dict(M=(1 << 31) + 1), ESHAPE), (dict(eps=-1.0), ESHAPE),
+    (dict(eps=float("nan")), ESHAPE),
     (dict(x=None), ENULL), (dict(C=None), ENULL), (dict(gb=P + 0x210004), EALIGN),
     (dict(delta=P + 0x100000), EALIAS), (dict(B=P + 0x500000 + 256 * 64 * 2 - 16), EALIAS),
     (dict(C=P + 0x700000 + 16), EALIAS),
