@@ -871,7 +871,9 @@ def main():
 
 def run_info(torch):
     """GPU, ROCm and source identification for the report line."""
-    info = {"gpu": torch.cuda.get_device_name(0), "rocm": torch.version.hip, "torch": torch.__version__}
+    props = torch.cuda.get_device_properties(0)
+    info = {"gpu": torch.cuda.get_device_name(0), "gpu_arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "rocm": torch.version.hip, "torch": torch.__version__}
     sha = None
     try:
         import subprocess
@@ -880,7 +882,7 @@ def run_info(torch):
                              timeout=10).stdout.strip() or None
     except (OSError, subprocess.SubprocessError):
         pass
-    info["git_sha"] = sha
+    info["git_sha"] = sha   # None where the tree was copied without its history
     info["kernel_source_hash"] = kernel_source_hash("prefill")
     return info
 
