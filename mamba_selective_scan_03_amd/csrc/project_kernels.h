@@ -60,8 +60,8 @@ template <int n> constexpr int vmcnt_only() { return (n & 15) | ((n >> 4) << 14)
 // half wc of the CT = R / 16 + 2 column tiles (d_low's R / 16 tiles, then one each of B and
 // C).  The launcher uses kRT = 4: eight waves, two per SIMD, each with 64 rows x 144 columns.
 // Every work-group reads all of W_x, so the rows per work-group set how much W_x traffic the
-// L2 serves per row of x: 256 rows halve it against 128, and the kernel went from 0.34 to
-// 0.27 ms on 64K x 8192.
+// L2 serves per row of x: 256 rows halve it against 128 (with the loads below, 0.34 -> 0.25 ms
+// on 64K x 8192, rank 256).
 // K (= D) goes in stages of 64.  Each stage's x tile [256][64] and W_x tile [16 CT][64] go
 // from memory straight into LDS (global_load_lds_dwordx4, 1 KB per wave instruction) and take
 // no registers.  Two such stages fill the LDS, so a stage's loads are issued one stage before
