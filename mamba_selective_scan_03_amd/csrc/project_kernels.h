@@ -18,6 +18,14 @@
 
 namespace jscan {
 
+// Two fp32 values rounded to bf16 and packed into one word, lo in the low half: one
+// v_cvt_pk_bf16_f32, the same round-to-nearest-even as pack_bf16x2(), so the bits are equal.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
+
 namespace proj {
 constexpr int kRowsX = 256;   // x-projection rows (tokens) per work-group: 4 row groups x 64
 }
@@ -304,37 +312,26 @@ __global__ __launch_bounds__(512) void dtproj_kernel(const uint16_t *__restrict_
                       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)(buf + wave * 64 * 8));
         }
     };
-    // Wait for this wave's loads of tile i.  In issue order this wave's vector-memory operations
-    // are tiles 0 and 1's loads, then per tile j: tile j + 2's loads and tile j's stores.  After
-    // tile i's loads come tile i - 2's stores, tile i + 1's loads and tile i - 1's stores, so
-    // waiting until at most those are outstanding waits for tile i.  (Every store issues all its
-    // instructions but those of a partial tile, which is the last of its group; the last tile
-    // waits for everything.)
-    auto wait_tile = [&](int i) {
-        if (i + 1 >= count) {
-            __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
-        } else if (!active) {   // no stores
-            if (dma_wave) __builtin_amdgcn_s_waitcnt(vmcnt_only<1>());
-            else __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
-        } else if (dma_wave) {
-            if (i == 0) __builtin_amdgcn_s_waitcnt(vmcnt_only<1>());
-            else if (i == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only<1 + kSt>());
-            else __builtin_amdgcn_s_waitcnt(vmcnt_only<1 + 2 * kSt>());
-        } else {
-            if (i == 0) __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
-            else if (i == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only<kSt>());
-            else __builtin_amdgcn_s_waitcnt(vmcnt_only<2 * kSt>());
-        }
+    // Wait for this wave's loads of tile j.  In issue order this wave's vector-memory operations
+    // are tiles 0, 1 and 2's loads, then per step i: tile i + 3's loads and tile i's stores.
+    // Tile j's loads (j >= 3) are issued in step j - 3, so before step j - 1 waits for them,
+    // tile j - 3's stores, tile j + 1's loads and tile j - 2's stores come after them; tiles 1
+    // and 2 have fewer operations behind them.  The last tile waits for everything (which also
+    // covers groups of fewer than four tiles, and a partial tile's shorter store list, which is
+    // only ever the last tile's).  Waves without loads wait for nothing: the loading waves wait
+    // before the barrier that follows.
+    auto wait_tile = [&](int j) {
+        if (!dma_wave) return;
+        if (j + 1 >= count) __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
+        else if (j == 0 && count == 2) __builtin_amdgcn_s_waitcnt(vmcnt_only<1>());
+        else if (j == 0) __builtin_amdgcn_s_waitcnt(vmcnt_only<2>());
+        else if (!active) __builtin_amdgcn_s_waitcnt(vmcnt_only<1>());   // no stores
+        else if (j == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only<1>());
+        else if (j == 2) __builtin_amdgcn_s_waitcnt(vmcnt_only<1 + kSt>());
+        else __builtin_amdgcn_s_waitcnt(vmcnt_only<1 + 2 * kSt>());
     };
-    uint16_t *ow = outs[wave];
-    // Tile i, read from rbuf; tile i + 2's loads go into dbuf (the buffer of tile i - 1).
-    auto step = [&](int i, const uint16_t *rbuf, uint16_t *dbuf) {
-        wait_tile(i);
-        __syncthreads();   // every wave's part of tile i is in; every wave is done with tile i - 1
-        if (i + 2 < count) dma(i + 2, dbuf);
-        if (!active) return;
-        const int64_t t = grp + (int64_t)i * groups;
-        f32x4_t acc[4];
+    // Tile i's products from rbuf: token r16 of the tile, channels 16 u + 4 g4 .. + 3.
+    auto products = [&](const uint16_t *rbuf, f32x4_t (&acc)[4]) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -344,16 +341,12 @@ __global__ __launch_bounds__(512) void dtproj_kernel(const uint16_t *__restrict_
 #pragma unroll
             for (int u = 0; u < 4; ++u) acc[u] = mfma16(a[u][ks], b, acc[u]);
         }
-        // bias, softplus, bf16: token r16 of the tile, channels 16 u + 4 g4 .. + 3 of the wave's 64
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            uint2 pk;
-            pk.x = pack_bf16x2(softplus_f32(acc[u][0] + bs[u].x), softplus_f32(acc[u][1] + bs[u].y));
-            pk.y = pack_bf16x2(softplus_f32(acc[u][2] + bs[u].z), softplus_f32(acc[u][3] + bs[u].w));
-            *reinterpret_cast<uint2 *>(ow + r16 * proj::kDtOutRow + 16 * u + 4 * g4) = pk;
-        }
-        // whole rows out: lane l writes 16 bytes (8 channels) of token row l / 8 + 8 k, with the
-        // non-temporal hint (delta is not read again here)
+    };
+    uint16_t *ow = outs[wave];
+    // Tile i's rows out of this wave's output area: lane l writes 16 bytes (8 channels) of token
+    // row l / 8 + 8 k, with the non-temporal hint (delta is not read again here).
+    auto store = [&](int i) {
+        const int64_t t = grp + (int64_t)i * groups;
 #pragma unroll
         for (int k = 0; k < kSt; ++k) {
             const int orow = (l >> 3) + 8 * k, oc = l & 7;
@@ -362,12 +355,72 @@ __global__ __launch_bounds__(512) void dtproj_kernel(const uint16_t *__restrict_
             if (tok < M) __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(delta + tok * D + ch0 + 8 * oc));
         }
     };
+    // Tile i + 1's products (from nbuf, into nxt) beside tile i's bias, softplus and bf16
+    // rounding (from cur, into the output area), in KS slices: each slice issues one k step's
+    // four MFMAs, then the vector work on 16 / KS of tile i's values while they run; the
+    // scheduling barrier keeps the compiler from gathering the MFMAs back together.  The next k
+    // step's operand read is issued a slice ahead.
+    auto overlap = [&](const uint16_t *nbuf, f32x4_t (&nxt)[4], const f32x4_t (&cur)[4]) {
+        constexpr int kPer = 16 / KS;   // values of tile i per slice (2, 4 or 8)
+        uint32_t pw[8];                 // tile i's values packed in pairs, pair j = values 2j, 2j+1
+        bf16x8_t b[2];
+        auto read_b = [&](int ks) {
+            const int c = (4 * ks + g4) ^ (r16 & kSwz);
+            return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(nbuf + r16 * R + 8 * c));
+        };
+        auto value = [&](int j) {
+            const int u = j >> 2, e = j & 3;
+            const float bias = e == 0 ? bs[u].x : e == 1 ? bs[u].y : e == 2 ? bs[u].z : bs[u].w;
+            return softplus_f32(cur[u][e] + bias);
+        };
+#pragma unroll
+        for (int u = 0; u < 4; ++u) nxt[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        b[0] = read_b(0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) b[(ks + 1) & 1] = read_b(ks + 1);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) nxt[u] = mfma16(a[u][ks], b[ks & 1], nxt[u]);
+#pragma unroll
+            for (int j = kPer * ks; j < kPer * (ks + 1); j += 2) {
+                const float v0 = value(j), v1 = value(j + 1);
+                pw[j >> 1] = pack2_bf16(v0, v1);
+                if ((j & 3) == 2)   // channel group u = j / 4 complete: 4 channels of token r16
+                    *reinterpret_cast<uint2 *>(ow + r16 * proj::kDtOutRow + 16 * (j >> 2) + 4 * g4) =
+                        make_uint2(pw[(j >> 1) - 1], pw[j >> 1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // Step i: tile i + 1's products beside tile i's epilogue; tile i + 3's loads go into dbuf
+    // (tile i's buffer, whose products every wave finished in the step before the barrier).  The
+    // last step's products read a buffer no load writes any more, and are not used.
+    f32x4_t acc[2][4];
+    auto step = [&](int i, const uint16_t *nbuf, uint16_t *dbuf, f32x4_t (&cur)[4], f32x4_t (&nxt)[4]) {
+        if (i + 1 < count) {
+            wait_tile(i + 1);
+            __syncthreads();   // every wave's part of tile i + 1 is in; every wave is done with tile i's buffer
+            if (i + 3 < count) dma(i + 3, dbuf);
+        }
+        if (!active) return;
+        overlap(nbuf, nxt, cur);
+        store(i);
+    };
     if (count > 0) dma(0, tiles0);
     if (count > 1) dma(1, tiles1);
-    for (int i = 0; i < count; i += proj::kDtBufs) {
-        step(i, tiles0, tiles2);
-        if (i + 1 < count) step(i + 1, tiles1, tiles0);
-        if (i + 2 < count) step(i + 2, tiles2, tiles1);
+    if (count > 2) dma(2, tiles2);
+    if (count > 0) {
+        wait_tile(0);
+        __syncthreads();
+        if (active) products(tiles0, acc[0]);
+    }
+    for (int i = 0; i < count; i += 2 * proj::kDtBufs) {
+        step(i, tiles1, tiles0, acc[0], acc[1]);
+        if (i + 1 < count) step(i + 1, tiles2, tiles1, acc[1], acc[0]);
+        if (i + 2 < count) step(i + 2, tiles0, tiles2, acc[0], acc[1]);
+        if (i + 3 < count) step(i + 3, tiles1, tiles0, acc[1], acc[0]);
+        if (i + 4 < count) step(i + 4, tiles2, tiles1, acc[0], acc[1]);
+        if (i + 5 < count) step(i + 5, tiles0, tiles2, acc[1], acc[0]);
     }
 }
 

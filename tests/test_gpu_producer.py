@@ -85,6 +85,8 @@ def run(M, D, R, seed=0, rows=None):
     (1, 128, 256),       # a single token (decode-sized)
     (300, 640, 256),     # a partial last delta channel slice (128 of 512 channels) and ragged tokens
     (20007, 384, 64),    # about five token tiles per group, six of eight channel waves busy, ragged
+    (700, 8192, 256),    # two or three token tiles per group (the pipeline's short-group waits), ragged
+    (1500, 8192, 64),    # five or six token tiles per group at the smallest rank, ragged
 ])
 def test_ssm_inputs_match_oracle(M, D, R):
     run(M, D, R, seed=M + D)
