@@ -63,6 +63,8 @@ constexpr int kPStride = kCh * 4 + 4;
 constexpr int kPSize = kT / 4 * kPStride;
 }  // namespace rows
 
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
+
 // Four consecutive elements from global memory as fp32 (bf16: one 8-byte load).
 template <typename E> struct Vec4;
 template <> struct Vec4<BF16> {
@@ -414,19 +416,53 @@ __device__ __forceinline__ float token_step(const GroupRegs &g, float &h_0, floa
 
 // Advance this lane's two states over tokens 8H..8H+7 of a 16-token group and leave their y
 // partials (summed over the wave's 4 rows) in the y exchange rows `ys` (row = token in group).
-template <int H, AForm AF, bool kTrap = false>
+// With kRowMma the partials are only rounded to bf16 into `pa`, the A operand of the row sum on
+// the matrix cores (row_sum_mma()).
+template <int H, AForm AF, bool kTrap = false, bool kRowMma = false>
 __device__ __forceinline__ void scan_half(const GroupRegs &g, float &h_0, float &h_1, float a2_0, float a2_1, float *ys,
-                                          int rt, int ch) {
+                                          int rt, int ch, bf16x8_t &pa) {
     float P[8];
 #define JSCAN_STEP(i) P[i] = token_step<8 * H + (i), AF, kTrap>(g, h_0, h_1, a2_0, a2_1);
     JSCAN_STEP(0) JSCAN_STEP(1) JSCAN_STEP(2) JSCAN_STEP(3)
     JSCAN_STEP(4) JSCAN_STEP(5) JSCAN_STEP(6) JSCAN_STEP(7)
 #undef JSCAN_STEP
-    // rows -> one register per 4 tokens; row r holds token 4j + {0,2,1,3}[r]
-    float ra, rb;
-    reduce_rows4x2(P, ra, rb);
-    ys[(8 * H + rt) * rows::kYStride + ch] = ra;
-    ys[(8 * H + 4 + rt) * rows::kYStride + ch] = rb;
+    if constexpr (kRowMma) {
+        pa = __builtin_convertvector((f32x8_t{P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7]}), bf16x8_t);
+    } else {
+        // rows -> one register per 4 tokens; row r holds token 4j + {0,2,1,3}[r]
+        float ra, rb;
+        reduce_rows4x2(P, ra, rb);
+        ys[(8 * H + rt) * rows::kYStride + ch] = ra;
+        ys[(8 * H + 4 + rt) * rows::kYStride + ch] = rb;
+    }
+}
+
+// The sum over the wave's 4 rows of a 16-token group on the matrix cores, for bf16 output.  Lane
+// (r, c) holds its partials of tokens 0-7 (pa0) and 8-15 (pa1) of the group as bf16, so pa0 is
+// the A operand A[c][8r + j] = partial of row r, token j; the constant B operand sel[0] is the
+// one-hot B[8r + j][col] = (j == col) for col < 8, and sel[1] the same for col = 8 + j.  Two
+// MFMAs then give D[c][tok] = sum over r of the token's partials, and lane l holds channels
+// 4 (l / 16) .. + 3 of token l % 16: one 16-byte write into the y exchange rows.  The partials
+// are rounded to bf16 once (2^-9 relative), below the bf16 rounding of y itself.
+struct RowSel {
+    bf16x8_t sel[2];
+};
+__device__ __forceinline__ RowSel row_sum_operands(int lane) {
+    const int col = lane & 15;
+    RowSel s;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        s.sel[0][j] = (__bf16)(col == j ? 1.0f : 0.0f);
+        s.sel[1][j] = (__bf16)(col == 8 + j ? 1.0f : 0.0f);
+    }
+    return s;
+}
+__device__ __forceinline__ f32x4_t row_sum_mma(const bf16x8_t &pa0, const bf16x8_t &pa1, const RowSel &s) {
+    f32x4_t d = mfma16(pa0, s.sel[0], f32x4_t{0.f, 0.f, 0.f, 0.f});
+    return mfma16(pa1, s.sel[1], d);
+}
+__device__ __forceinline__ void row_sum_store(const f32x4_t &d, float *ys, int cg, int lane) {
+    *reinterpret_cast<f32x4_t *>(ys + (lane & 15) * rows::kYStride + 16 * cg + 4 * (lane >> 4)) = d;
 }
 // The same half split in two: the tokens' partials (computed in one scheduling region) and their
 // reduction over rows and store (done in the next region, beside the next half's tokens).  The
@@ -654,6 +690,10 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
         h_1 = hv.y;
     }
     const int rt = (r == 1) ? 2 : (r == 2) ? 1 : r;   // token slot of this row after reduce_rows4
+    // bf16 output: the sum over the wave's rows on the matrix cores (row_sum_mma()); fp32 output
+    // keeps the exact fp32 sum through permlane swaps.
+    constexpr bool kRowMma = sizeof(S) == 2;
+    const RowSel rsel = row_sum_operands(lane);
     __syncthreads();   // tile 0 staged by the helper waves
     GroupRegs G[2];
     load_half<0, kTrap>(G[0], dx_s[0], bc_s[0], p_s[0], 0, ch, n0, c);
@@ -668,34 +708,47 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
         constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
         float *ys = y_s[cur] + sh * rows::kT * rows::kYStride;
         const float *dxc = dx_s[cur], *bcc = bc_s[cur], *psc = p_s[cur];
-        if constexpr (AF != AForm::ScaledIdentity) {
+        if constexpr (AF != AForm::ScaledIdentity || kRowMma) {
+            // With the row sums on the matrix cores, a group's sums are stored in the next
+            // scheduling region, when its MFMAs have had a half group's tokens to finish.
+            bf16x8_t pa[2];
+            f32x4_t dsum;
+#define JSCAN_H0(GR, off)                                                                              \
+    scan_half<0, AF, kTrap, kRowMma>(GR, h_0, h_1, a2_0, a2_1, ys + (off) * rows::kYStride, rt, ch, pa[0]); \
+    if constexpr (kRowMma && (off) > 0) row_sum_store(dsum, ys + ((off) - 16) * rows::kYStride, cg, lane);
+#define JSCAN_H1(GR, off)                                                                              \
+    scan_half<1, AF, kTrap, kRowMma>(GR, h_0, h_1, a2_0, a2_1, ys + (off) * rows::kYStride, rt, ch, pa[1]); \
+    if constexpr (kRowMma) dsum = row_sum_mma(pa[0], pa[1], rsel);
             load_half<0, kTrap>(G[1], dxc, bcc, psc, 16, ch, n0, c);
             JSCAN_SB;
-            scan_half<0, AF, kTrap>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch);
+            JSCAN_H0(G[0], 0)
             JSCAN_SB;
             load_half<1, kTrap>(G[1], dxc, bcc, psc, 16, ch, n0, c);
             JSCAN_SB;
-            scan_half<1, AF, kTrap>(G[0], h_0, h_1, a2_0, a2_1, ys, rt, ch);
+            JSCAN_H1(G[0], 0)
             JSCAN_SB;
             load_half<0, kTrap>(G[0], dxc, bcc, psc, 32, ch, n0, c);
             JSCAN_SB;
-            scan_half<0, AF, kTrap>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch);
+            JSCAN_H0(G[1], 16)
             JSCAN_SB;
             load_half<1, kTrap>(G[0], dxc, bcc, psc, 32, ch, n0, c);
             JSCAN_SB;
-            scan_half<1, AF, kTrap>(G[1], h_0, h_1, a2_0, a2_1, ys + 16 * rows::kYStride, rt, ch);
+            JSCAN_H1(G[1], 16)
             JSCAN_SB;
             load_half<0, kTrap>(G[1], dxc, bcc, psc, 48, ch, n0, c);
             JSCAN_SB;
-            scan_half<0, AF, kTrap>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch);
+            JSCAN_H0(G[0], 32)
             JSCAN_SB;
             load_half<1, kTrap>(G[1], dxc, bcc, psc, 48, ch, n0, c);
             JSCAN_SB;
-            scan_half<1, AF, kTrap>(G[0], h_0, h_1, a2_0, a2_1, ys + 32 * rows::kYStride, rt, ch);
+            JSCAN_H1(G[0], 32)
             JSCAN_SB;
-            scan_half<0, AF, kTrap>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch);
+            JSCAN_H0(G[1], 48)
             JSCAN_SB;
-            scan_half<1, AF, kTrap>(G[1], h_0, h_1, a2_0, a2_1, ys + 48 * rows::kYStride, rt, ch);
+            JSCAN_H1(G[1], 48)
+            if constexpr (kRowMma) row_sum_store(dsum, ys + 48 * rows::kYStride, cg, lane);
+#undef JSCAN_H0
+#undef JSCAN_H1
         } else {
             float Pa[8], Pb[8];
             load_half<0, kTrap>(G[1], dxc, bcc, psc, 16, ch, n0, c);

@@ -50,13 +50,21 @@ def test_chunked_matches_oracle(batch, L, D, dtype, chunk, with_h0):
 
 @pytest.mark.parametrize("batch,L,D,dtype,chunk", [(1, 1000, 64, "bf16", 192), (2, 777, 40, "f32", 100)])
 def test_first_segment_is_the_sequential_scan(batch, L, D, dtype, chunk):
-    """Segment 0 starts from h0 itself, so its y is bit-identical to the sequential prefill."""
+    """Segment 0 starts from h0 itself, so its states are the sequential prefill's.  With fp32
+    output its y is bit-identical too (the same sums in the same order); with bf16 output the
+    sequential prefill sums over states on the matrix cores from bf16-rounded partials, so y
+    agrees to that rounding."""
     inp = to_dev(workloads.small_prefill(batch, L, D, dtype, seed=4))
     h0 = h0_for(batch, D, 6).cuda()
     y_seq, _ = jscan.prefill(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], h0=h0)
     y_chk, _ = jscan.prefill_chunked(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], h0=h0, chunk=chunk)
     torch.cuda.synchronize()
-    assert torch.equal(bits(y_chk[:, :chunk]), bits(y_seq[:, :chunk]))
+    a, b = y_chk[:, :chunk], y_seq[:, :chunk]
+    if dtype == "f32":
+        assert torch.equal(bits(a), bits(b))
+    else:
+        err = (a.double() - b.double()).abs().max().item()
+        assert err <= 2 ** -7 * b.double().abs().max().item(), err
 
 
 @pytest.mark.parametrize("chunk", [0, 4096, 100000])
