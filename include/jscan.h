@@ -22,7 +22,12 @@
  * and exp2 is the hardware v_exp_f32.  Tokens are visited in increasing t, one after the
  * other.  So the state that jscan_prefill returns is bit-identical to the state after L
  * calls of jscan_step on the same tokens, starting from +0.0.  y accumulates in fp32 and is
- * rounded to nearest even to the output dtype.
+ * rounded to nearest even to the output dtype.  With bf16 output the prefill's sum over the
+ * states runs on the matrix cores: its terms are rounded to bf16 once (2^-9 relative) and
+ * summed in fp32 (the products C_t[n] h_t[d,n] with h rounded, or, in jscan_prefill_fused, the
+ * lanes' fp32 partial sums over two states).  A NaN in a channel's state then also reaches
+ * that channel's outputs earlier in the same 16-token group (a NaN term times a zero weight of
+ * the summing matrix), never another channel.
  *
  * Layouts.  All arrays are row-major with the last index contiguous:
  *     x, delta, y : [batch][L][D]      B, C : [batch][L][N]
@@ -118,7 +123,8 @@ jscan_status jscan_prefill_resume(const void *x, const void *delta, const float 
  * h -> exp(delta A) h + delta B x composes to h -> exp(A * sum delta) h + h_loc, where h_loc
  * is the run's end state from zero (S6 equation, notes page "Jamba: A Hybrid
  * Transformer-Mamba Language Model", section "Mamba layer").
- * Rounding: the first segment's y is bit-identical to jscan_prefill_resume's; later
+ * Rounding: with fp32 output the first segment's y is bit-identical to jscan_prefill_resume's
+ * (with bf16 output it agrees to the rounding of the prefill's sum over states); later
  * segments start from composed states whose rounding differs from the token-by-token walk,
  * so their y and h_final agree with it to within fp32 rounding of the composition, not bit
  * for bit.  Results are deterministic (no atomics; fixed summation orders).
@@ -179,8 +185,10 @@ jscan_status jscan_ssm_inputs(const void *x, const void *w_x, const float *g_del
  * Prefill with the second product of jscan_ssm_inputs folded into the scan's load path: delta
  * is never stored.  The kernel computes, tile by tile, delta = softplus(W_dt delta_low + b_dt)
  * with the same matrix-core sequence, bias add, softplus and bf16 rounding as
- * jscan_ssm_inputs, so y and h_final are bit-identical to jscan_ssm_inputs followed by
- * jscan_prefill_resume (jscan_prefill when h0 is NULL).
+ * jscan_ssm_inputs, so h_final is bit-identical to jscan_ssm_inputs followed by
+ * jscan_prefill_resume (jscan_prefill when h0 is NULL).  y agrees with it to the rounding of the
+ * sum over states: this kernel's matrix cores also compute delta, so it sums the lanes' partials
+ * there (half the MFMAs) rather than contracting the states with C.
  *   x          [batch][L][D] bf16      delta_low [batch][L][R] bf16 (from jscan_ssm_inputs)
  *   w_dt       [D][R] bf16             b_dt [D] fp32
  *   A, B, C, h0 (may be NULL), y, h_final as for jscan_prefill_resume

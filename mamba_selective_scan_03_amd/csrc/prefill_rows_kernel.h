@@ -61,9 +61,17 @@ constexpr int kYSize = 2 * kT * kYStride;
 // Trapezoidal rule: the left-end weights p [kT/4][kPStride] (4 tokens of a channel per float4)
 constexpr int kPStride = kCh * 4 + 4;
 constexpr int kPSize = kT / 4 * kPStride;
+// bf16 output: the C operands of the output MFMAs, [group][state half][table, zeros][lane][4 dwords]
+// per tile buffer (see c_operands())
+constexpr int kSelLane = 4;                    // dwords per lane entry
+constexpr int kSelHalf = 2 * 64 * kSelLane;    // table and zero block of one state half
+constexpr int kSelGroup = 2 * kSelHalf;        // both state halves of a 16-token group
+constexpr int kSelSize = (kT / 16) * kSelGroup;
 }  // namespace rows
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Four consecutive elements from global memory as fp32 (bf16: one 8-byte load).
 template <typename E> struct Vec4;
@@ -287,9 +295,9 @@ __device__ __forceinline__ void fused_delta(const u32x4_t (&f)[fused::kKS], cons
 // B of the previous token into the third B/C tile (zero for tokens at or past L, and for token
 // 0 of a row without a previous token).  A token at or past L gets p = -0, so with its zero
 // previous B the left-end term is -0 and the state stays bit-identical.
-template <typename E, int part, AForm AF, bool kTrap>
-__device__ __forceinline__ void stage_part(const TileRegs<E> &R, float *dx_s, float *bc_s, float *p_s, int64_t t0,
-                                           int64_t L, int tid, const float4 &a2q, bool prev_given) {
+template <typename E, int part, AForm AF, bool kTrap, bool kCOps>
+__device__ __forceinline__ void stage_part(const TileRegs<E> &R, float *dx_s, float *bc_s, float *p_s, uint32_t *cs_s,
+                                           int64_t t0, int64_t L, int tid, const float4 &a2q, bool prev_given) {
     constexpr bool kScalarA = AF == AForm::ScaledIdentity;
     const float a2 = part == 0 ? a2q.x : part == 1 ? a2q.y : part == 2 ? a2q.z : a2q.w;
     const int p = tid >> 3, q = tid & 7;
@@ -326,14 +334,30 @@ __device__ __forceinline__ void stage_part(const TileRegs<E> &R, float *dx_s, fl
     *reinterpret_cast<float4 *>(dx_s + p * rows::kDxStride + (4 * q + part) * 4) = v;
     const int tb = (tid & 127) >> 1, nb = (tid & 1) * 8;
     const bool live = t0 + tb < L;
-    float *dst = bc_s + (tid >= 128 ? rows::kBcSize : 0);
-    float f[4];
-    Vec4<E>::widen(live ? R.bc[part >> 1] : Vec4<E>::zero(), f);
-    dst[(nb + 2 * part) * rows::kBcStride + tb] = f[(2 * part) & 3];
-    dst[(nb + 2 * part + 1) * rows::kBcStride + tb] = f[(2 * part + 1) & 3];
+    if constexpr (kCOps) {
+        if (tid >= 128) {   // whole waves: the C threads write their pair of states nb + 2 part, + 1 as
+                            // the raw bf16 pair, into the table entry of lane (row part, column tb % 16)
+            const typename Vec4<E>::raw r = live ? R.bc[part >> 1] : Vec4<E>::zero();
+            const uint32_t pair = (part & 1) ? r.y : r.x;
+            cs_s[(tb >> 4) * rows::kSelGroup + (nb >> 3) * rows::kSelHalf + (16 * part + (tb & 15)) * rows::kSelLane +
+                 (tb & 3)] = pair;
+        } else {
+            float f[4];
+            Vec4<E>::widen(live ? R.bc[part >> 1] : Vec4<E>::zero(), f);
+            bc_s[(nb + 2 * part) * rows::kBcStride + tb] = f[(2 * part) & 3];
+            bc_s[(nb + 2 * part + 1) * rows::kBcStride + tb] = f[(2 * part + 1) & 3];
+        }
+    } else {
+        float *dst = bc_s + (tid >= 128 ? rows::kBcSize : 0);
+        float f[4];
+        Vec4<E>::widen(live ? R.bc[part >> 1] : Vec4<E>::zero(), f);
+        dst[(nb + 2 * part) * rows::kBcStride + tb] = f[(2 * part) & 3];
+        dst[(nb + 2 * part + 1) * rows::kBcStride + tb] = f[(2 * part + 1) & 3];
+    }
     if constexpr (kTrap) {
         if (tid < 128) {   // whole waves: the B threads
             const bool prev_live = live && (t0 + tb > 0 || prev_given);
+            float f[4];
             Vec4<E>::widen(prev_live ? R.bcp[part >> 1] : Vec4<E>::zero(), f);
             float *bp = bc_s + 2 * rows::kBcSize;
             bp[(nb + 2 * part) * rows::kBcStride + tb] = f[(2 * part) & 3];
@@ -341,13 +365,13 @@ __device__ __forceinline__ void stage_part(const TileRegs<E> &R, float *dx_s, fl
         }
     }
 }
-template <typename E, AForm AF, bool kTrap = false>
-__device__ __forceinline__ void stage_tile(const TileRegs<E> &R, float *dx_s, float *bc_s, float *p_s, int64_t t0,
-                                           int64_t L, int tid, const float4 &a2q, bool prev_given = false) {
-    stage_part<E, 0, AF, kTrap>(R, dx_s, bc_s, p_s, t0, L, tid, a2q, prev_given);
-    stage_part<E, 1, AF, kTrap>(R, dx_s, bc_s, p_s, t0, L, tid, a2q, prev_given);
-    stage_part<E, 2, AF, kTrap>(R, dx_s, bc_s, p_s, t0, L, tid, a2q, prev_given);
-    stage_part<E, 3, AF, kTrap>(R, dx_s, bc_s, p_s, t0, L, tid, a2q, prev_given);
+template <typename E, AForm AF, bool kTrap = false, bool kCOps = false>
+__device__ __forceinline__ void stage_tile(const TileRegs<E> &R, float *dx_s, float *bc_s, float *p_s, uint32_t *cs_s,
+                                           int64_t t0, int64_t L, int tid, const float4 &a2q, bool prev_given = false) {
+    stage_part<E, 0, AF, kTrap, kCOps>(R, dx_s, bc_s, p_s, cs_s, t0, L, tid, a2q, prev_given);
+    stage_part<E, 1, AF, kTrap, kCOps>(R, dx_s, bc_s, p_s, cs_s, t0, L, tid, a2q, prev_given);
+    stage_part<E, 2, AF, kTrap, kCOps>(R, dx_s, bc_s, p_s, cs_s, t0, L, tid, a2q, prev_given);
+    stage_part<E, 3, AF, kTrap, kCOps>(R, dx_s, bc_s, p_s, cs_s, t0, L, tid, a2q, prev_given);
 }
 
 // One 16-token group's LDS operands for one lane: (delta*x, delta) of its channel for the 16
@@ -357,15 +381,18 @@ __device__ __forceinline__ void stage_tile(const TileRegs<E> &R, float *dx_s, fl
 // bursts stall issue until the oldest complete.
 // A trapezoidal scan also reads the 16 tokens' left-end weights p (pv) and the previous token's
 // B of its two states (bp0, bp1; broadcast per token like B).
+// With bf16 output the lane reads, instead of C, the B operands of the group's four output
+// MFMAs (cs; see c_operands()).
 struct GroupRegs {
     float4 v[8];
     float b0, b1, c0, c1;
     float4 pv[4];
     float bp0, bp1;
+    u32x4_t cs[4];
 };
-template <int H, bool kTrap = false>
+template <int H, bool kTrap = false, bool kCOps = false>
 __device__ __forceinline__ void load_half(GroupRegs &g, const float *dxs, const float *bcs, const float *ps, int tg,
-                                          int ch, int n0, int c) {
+                                          int ch, int n0, int c, const uint32_t *const *selp = nullptr, int selo = 0) {
 #pragma unroll
     for (int i = 4 * H; i < 4 * H + 4; ++i)
         g.v[i] = *reinterpret_cast<const float4 *>(dxs + ((tg >> 1) + i) * rows::kDxStride + ch * 4);
@@ -377,8 +404,14 @@ __device__ __forceinline__ void load_half(GroupRegs &g, const float *dxs, const 
     if constexpr (H == 0) {
         g.b0 = bcs[n0 * rows::kBcStride + tg + c];
         g.b1 = bcs[(n0 + 1) * rows::kBcStride + tg + c];
-        g.c0 = bcs[rows::kBcSize + n0 * rows::kBcStride + tg + c];
-        g.c1 = bcs[rows::kBcSize + (n0 + 1) * rows::kBcStride + tg + c];
+        if constexpr (kCOps) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                g.cs[m] = *reinterpret_cast<const u32x4_t *>(selp[m] + selo + (tg >> 4) * rows::kSelGroup);
+        } else {
+            g.c0 = bcs[rows::kBcSize + n0 * rows::kBcStride + tg + c];
+            g.c1 = bcs[rows::kBcSize + (n0 + 1) * rows::kBcStride + tg + c];
+        }
         if constexpr (kTrap) {
             g.bp0 = bcs[2 * rows::kBcSize + n0 * rows::kBcStride + tg + c];
             g.bp1 = bcs[2 * rows::kBcSize + (n0 + 1) * rows::kBcStride + tg + c];
@@ -393,7 +426,7 @@ template <int i> __device__ __forceinline__ float component(const float4 &v) {
 // One token: advance this lane's two states and return C*h summed over them.  With a
 // scaled-identity A the pair's second member is already the decay; with a complex state the
 // lane's two states are one complex state and (a2_0, a2_1) its prepared ComplexA.
-template <int TAU, AForm AF, bool kTrap = false>
+template <int TAU, AForm AF, bool kTrap = false, bool kNoPartial = false>
 __device__ __forceinline__ float token_step(const GroupRegs &g, float &h_0, float &h_1, float a2_0, float a2_1) {
     if constexpr (kTrap) {   // the left end point: h + p * B_prev, the DPP broadcast folded in
         const float pl = component<TAU & 3>(g.pv[TAU >> 2]);
@@ -411,59 +444,98 @@ __device__ __forceinline__ float token_step(const GroupRegs &g, float &h_0, floa
         h_0 = advance(h_0, dv, a2_0, dxv, row_bcast<TAU>(g.b0));
         h_1 = advance(h_1, dv, a2_1, dxv, row_bcast<TAU>(g.b1));
     }
-    return fmac_bcast<TAU>(row_bcast<TAU>(g.c0) * h_0, g.c1, h_1);
+    if constexpr (kNoPartial) return 0.0f;
+    else return fmac_bcast<TAU>(row_bcast<TAU>(g.c0) * h_0, g.c1, h_1);
 }
+
+// How a wave sums y over its 8 states (OutSum):
+//   Permlane: in-lane over the lane's two states, then over the 4 rows by permlane swaps (fp32);
+//   RowMma:   in-lane, then the 4-row sum on the matrix cores (row_sum_operands());
+//   CMma:     the whole contraction with C on the matrix cores (c_operand_bases()).
+enum class OutSum : int { Permlane, RowMma, CMma };
 
 // Advance this lane's two states over tokens 8H..8H+7 of a 16-token group and leave their y
 // partials (summed over the wave's 4 rows) in the y exchange rows `ys` (row = token in group).
-// With kRowMma the partials are only rounded to bf16 into `pa`, the A operand of the row sum on
-// the matrix cores (row_sum_mma()).
-template <int H, AForm AF, bool kTrap = false, bool kRowMma = false>
+// With RowMma or CMma (bf16 output) the sum runs on the matrix cores instead: two MFMAs per half
+// accumulate into d (zeroed by the first half), which the caller stores.
+template <int H, AForm AF, bool kTrap = false, OutSum OS = OutSum::Permlane>
 __device__ __forceinline__ void scan_half(const GroupRegs &g, float &h_0, float &h_1, float a2_0, float a2_1, float *ys,
-                                          int rt, int ch, bf16x8_t &pa) {
-    float P[8];
-#define JSCAN_STEP(i) P[i] = token_step<8 * H + (i), AF, kTrap>(g, h_0, h_1, a2_0, a2_1);
-    JSCAN_STEP(0) JSCAN_STEP(1) JSCAN_STEP(2) JSCAN_STEP(3)
-    JSCAN_STEP(4) JSCAN_STEP(5) JSCAN_STEP(6) JSCAN_STEP(7)
+                                          int rt, int ch, f32x4_t &d, const bf16x8_t *sel) {
+    if constexpr (OS == OutSum::CMma) {
+        uint32_t hp[8];
+#define JSCAN_STEP(i)                                                           \
+    token_step<8 * H + (i), AF, kTrap, true>(g, h_0, h_1, a2_0, a2_1);           \
+    hp[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{h_0, h_1}), bf16x2_t));
+        JSCAN_STEP(0) JSCAN_STEP(1) JSCAN_STEP(2) JSCAN_STEP(3)
+        JSCAN_STEP(4) JSCAN_STEP(5) JSCAN_STEP(6) JSCAN_STEP(7)
 #undef JSCAN_STEP
-    if constexpr (kRowMma) {
-        pa = __builtin_convertvector((f32x8_t{P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7]}), bf16x8_t);
+        const f32x4_t d0 = H == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : d;
+        d = mfma16(__builtin_bit_cast(bf16x8_t, (u32x4_t{hp[0], hp[1], hp[2], hp[3]})),
+                   __builtin_bit_cast(bf16x8_t, g.cs[2 * H]), d0);
+        d = mfma16(__builtin_bit_cast(bf16x8_t, (u32x4_t{hp[4], hp[5], hp[6], hp[7]})),
+                   __builtin_bit_cast(bf16x8_t, g.cs[2 * H + 1]), d);
     } else {
-        // rows -> one register per 4 tokens; row r holds token 4j + {0,2,1,3}[r]
-        float ra, rb;
-        reduce_rows4x2(P, ra, rb);
-        ys[(8 * H + rt) * rows::kYStride + ch] = ra;
-        ys[(8 * H + 4 + rt) * rows::kYStride + ch] = rb;
+        float P[8];
+#define JSCAN_STEP(i) P[i] = token_step<8 * H + (i), AF, kTrap>(g, h_0, h_1, a2_0, a2_1);
+        JSCAN_STEP(0) JSCAN_STEP(1) JSCAN_STEP(2) JSCAN_STEP(3)
+        JSCAN_STEP(4) JSCAN_STEP(5) JSCAN_STEP(6) JSCAN_STEP(7)
+#undef JSCAN_STEP
+        if constexpr (OS == OutSum::RowMma) {
+            const bf16x8_t pa = __builtin_convertvector((f32x8_t{P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7]}), bf16x8_t);
+            d = mfma16(pa, sel[H], H == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : d);
+        } else {
+            // rows -> one register per 4 tokens; row r holds token 4j + {0,2,1,3}[r]
+            float ra, rb;
+            reduce_rows4x2(P, ra, rb);
+            ys[(8 * H + rt) * rows::kYStride + ch] = ra;
+            ys[(8 * H + 4 + rt) * rows::kYStride + ch] = rb;
+        }
     }
 }
 
-// The sum over the wave's 4 rows of a 16-token group on the matrix cores, for bf16 output.  Lane
-// (r, c) holds its partials of tokens 0-7 (pa0) and 8-15 (pa1) of the group as bf16, so pa0 is
-// the A operand A[c][8r + j] = partial of row r, token j; the constant B operand sel[0] is the
-// one-hot B[8r + j][col] = (j == col) for col < 8, and sel[1] the same for col = 8 + j.  Two
-// MFMAs then give D[c][tok] = sum over r of the token's partials, and lane l holds channels
-// 4 (l / 16) .. + 3 of token l % 16: one 16-byte write into the y exchange rows.  The partials
-// are rounded to bf16 once (2^-9 relative), below the bf16 rounding of y itself.
-struct RowSel {
-    bf16x8_t sel[2];
-};
-__device__ __forceinline__ RowSel row_sum_operands(int lane) {
+// The 4-row sum of a 16-token group on the matrix cores, from the lanes' partials.  Lane (r, c)
+// holds its partials of tokens 0-7 (first half) and 8-15 (second half) of the group as bf16, so
+// a half's partials are the A operand A[c][8r + j] = partial of row r, token j; the constant B
+// operand sel[0] is the one-hot B[8r + j][col] = (j == col) for col < 8, and sel[1] the same for
+// col = 8 + j.  The two MFMAs give D[c][tok] = sum over r of the token's partials, in the layout
+// of the contraction below.  The partials are rounded to bf16 once (2^-9 relative).
+__device__ __forceinline__ void row_sum_operands(bf16x8_t (&sel)[2], int lane) {
     const int col = lane & 15;
-    RowSel s;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        s.sel[0][j] = (__bf16)(col == j ? 1.0f : 0.0f);
-        s.sel[1][j] = (__bf16)(col == 8 + j ? 1.0f : 0.0f);
+        sel[0][j] = (__bf16)(col == j ? 1.0f : 0.0f);
+        sel[1][j] = (__bf16)(col == 8 + j ? 1.0f : 0.0f);
     }
-    return s;
 }
-__device__ __forceinline__ f32x4_t row_sum_mma(const bf16x8_t &pa0, const bf16x8_t &pa1, const RowSel &s) {
-    f32x4_t d = mfma16(pa0, s.sel[0], f32x4_t{0.f, 0.f, 0.f, 0.f});
-    return mfma16(pa1, s.sel[1], d);
+
+// The output contraction of bf16 output on the matrix cores.  For a 16-token group, a wave's
+// share of y is y[c][t] = sum over its 8 states n of C_t[n] h_t[c][n], for its 16 channels c.
+// MFMA m (m = 0..3) covers tokens 4m .. 4m + 3 with k = 8 r + 2 t' + s (row r, token 4m + t',
+// state n0(r) + s):
+//   A[c][k] = h of lane (r, c) after token 4m + t', state s, rounded to bf16: the lane's own
+//             states, four tokens in four registers;
+//   B[k][col] = C_col[n0(r) + s] where col = 4m + t', else 0: lane (r, col) holds, for the m
+//             with col / 4 = m, the bf16 pair C_col[n0], C_col[n0 + 1] in register col % 4 and
+//             zeros elsewhere, and zeros for the other three m.
+// The four MFMAs accumulate D[c][col] = y share of channel c, token col, four channels of one
+// token per lane, written to the exchange rows with one 16-byte write.  The helper waves stage
+// the B operands: a table per (group, state half) in which each lane's entry holds the raw bf16
+// pair in its register col % 4 (the other registers are zeroed once), and a zero block; lane
+// (r, col) reads the table for its m and the zero block for the other three, at the same
+// offsets, so the reads need no per-lane selection.  Products of bf16 values are exact and the
+// MFMA sums in fp32, so y differs from the fp32 contraction by the rounding of h to bf16
+// (2^-9 relative per term), below y's own rounding to bf16.
+__device__ __forceinline__ void c_operand_bases(const uint32_t *(&selp)[4], const uint32_t *cs_s, int sh, int lane) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int z = (m == ((lane & 15) >> 2)) ? 0 : 1;
+        selp[m] = cs_s + sh * rows::kSelHalf + (z * 64 + lane) * rows::kSelLane;
+    }
 }
 __device__ __forceinline__ void row_sum_store(const f32x4_t &d, float *ys, int cg, int lane) {
     *reinterpret_cast<f32x4_t *>(ys + (lane & 15) * rows::kYStride + 16 * cg + 4 * (lane >> 4)) = d;
 }
+
 // The same half split in two: the tokens' partials (computed in one scheduling region) and their
 // reduction over rows and store (done in the next region, beside the next half's tokens).  The
 // scaled-identity form, whose tokens are short, runs its halves this way: 2% faster there, 2%
@@ -543,11 +615,19 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
                   "the other forms of A and the trapezoidal rule run the plain prefill");
     constexpr bool kScalarA = AF == AForm::ScaledIdentity;
     using S = typename E::store_t;
+    // bf16 output: the output contraction on the matrix cores, with C as an MFMA operand
+    // (c_operand_bases()), or, with delta computed here, whose helper waves keep the matrix cores
+    // busy with delta's MFMAs, only the 4-row sum of the lanes' partials (row_sum_operands(): half
+    // the MFMAs).  fp32 output keeps the fp32 contraction, in-lane and by permlane swaps.
+    constexpr OutSum OS = sizeof(S) != 2 ? OutSum::Permlane : kFused ? OutSum::RowMma : OutSum::CMma;
+    constexpr bool kRowMma = OS != OutSum::Permlane;   // the row sums on the matrix cores
+    constexpr bool kCOps = OS == OutSum::CMma;         // C operand tables in LDS
     __shared__ __attribute__((aligned(16))) float dx_s[2][rows::kDxSize];
     __shared__ __attribute__((aligned(16))) float bc_s[2][(kTrap ? 3 : 2) * rows::kBcSize];
     __shared__ __attribute__((aligned(16))) float p_s[2][kTrap ? rows::kPSize : 4];
     __shared__ __attribute__((aligned(16))) float y_s[2][rows::kYSize];
     __shared__ __attribute__((aligned(16))) uint16_t xch_s[kFused ? 4 * fused::kXchWave : 8];
+    __shared__ __attribute__((aligned(16))) uint32_t cs_s[2][kCOps ? rows::kSelSize : 4];
 
     // Consecutive channel blocks go to the same XCD (work-groups are dealt round-robin over
     // the 8 XCDs), so the two blocks sharing a 128-byte row segment share one L2.
@@ -604,11 +684,18 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
             }
         }
         load_tile<E, !kFused, kTrap>(R[0], xb, db, bcb, 0, L, D, tid, pr);
+        if constexpr (kCOps) {
+            // the C operand tables start as zeros; staging only ever writes each entry's live register
+            u32x4_t *z = reinterpret_cast<u32x4_t *>(&cs_s[0][0]);
+#pragma unroll
+            for (int i = 0; i < 2 * rows::kSelSize / 4 / rows::kHalf; ++i) z[tid + rows::kHalf * i] = u32x4_t{0, 0, 0, 0};
+            __syncthreads();
+        }
         if constexpr (kFused) {
             load_dlow(dfr[0], dp.d_low, row, 0, L, hw, l);
             fused_delta(dfr[0], wf, bias, xch, R[0], l);
         }
-        stage_tile<E, AF, kTrap>(R[0], dx_s[0], bc_s[0], p_s[0], 0, L, tid, a2q, prev_given);
+        stage_tile<E, AF, kTrap, kCOps>(R[0], dx_s[0], bc_s[0], p_s[0], cs_s[0], 0, L, tid, a2q, prev_given);
         // tiles 1 and 2, in the order the loop issues its loads
         load_tile<E, !kFused, kTrap>(R[1], xb, db, bcb, rows::kT, L, D, tid, pr);
         if constexpr (kFused) load_dlow(dfr[1], dp.d_low, row, rows::kT, L, hw, l);
@@ -628,8 +715,8 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
             constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
             if (k + 1 < ntiles) {
                 if constexpr (kFused) fused_delta(dfr[nxt], wf, bias, xch, R[nxt], l);
-                stage_tile<E, AF, kTrap>(R[nxt], dx_s[nxt], bc_s[nxt], p_s[nxt], (int64_t)(k + 1) * rows::kT, L, tid,
-                                         a2q, prev_given);
+                stage_tile<E, AF, kTrap, kCOps>(R[nxt], dx_s[nxt], bc_s[nxt], p_s[nxt], cs_s[nxt],
+                                                  (int64_t)(k + 1) * rows::kT, L, tid, a2q, prev_given);
                 if (!kFused && k + 3 < ntiles)
                     load_tile<E, !kFused, kTrap>(R[nxt], xb, db, bcb, (int64_t)(k + 3) * rows::kT, L, D, tid, pr);
             }
@@ -690,14 +777,18 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
         h_1 = hv.y;
     }
     const int rt = (r == 1) ? 2 : (r == 2) ? 1 : r;   // token slot of this row after reduce_rows4
-    // bf16 output: the sum over the wave's rows on the matrix cores (row_sum_mma()); fp32 output
-    // keeps the exact fp32 sum through permlane swaps.
-    constexpr bool kRowMma = sizeof(S) == 2;
-    const RowSel rsel = row_sum_operands(lane);
+    const uint32_t *selp[4] = {nullptr, nullptr, nullptr, nullptr};
+    bf16x8_t sel[2];
+    if constexpr (kCOps) {
+        c_operand_bases(selp, &cs_s[0][0], sh, lane);
+        __syncthreads();   // the C operand tables zeroed by the helper waves
+    } else if constexpr (kRowMma) {
+        row_sum_operands(sel, lane);
+    }
     __syncthreads();   // tile 0 staged by the helper waves
     GroupRegs G[2];
-    load_half<0, kTrap>(G[0], dx_s[0], bc_s[0], p_s[0], 0, ch, n0, c);
-    load_half<1, kTrap>(G[0], dx_s[0], bc_s[0], p_s[0], 0, ch, n0, c);
+    load_half<0, kTrap, kCOps>(G[0], dx_s[0], bc_s[0], p_s[0], 0, ch, n0, c, selp, 0);
+    load_half<1, kTrap, kCOps>(G[0], dx_s[0], bc_s[0], p_s[0], 0, ch, n0, c, selp, 0);
 
     // Per tile: four 16-token groups, each group's LDS operands read (in two halves) while the
     // previous group is scanned.  One barrier per tile, shared with the helper waves, orders
@@ -711,35 +802,35 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
         if constexpr (AF != AForm::ScaledIdentity || kRowMma) {
             // With the row sums on the matrix cores, a group's sums are stored in the next
             // scheduling region, when its MFMAs have had a half group's tokens to finish.
-            bf16x8_t pa[2];
-            f32x4_t dsum;
+            f32x4_t dn, dsum;
 #define JSCAN_H0(GR, off)                                                                              \
-    scan_half<0, AF, kTrap, kRowMma>(GR, h_0, h_1, a2_0, a2_1, ys + (off) * rows::kYStride, rt, ch, pa[0]); \
+    scan_half<0, AF, kTrap, OS>(GR, h_0, h_1, a2_0, a2_1, ys + (off) * rows::kYStride, rt, ch, dn, sel); \
     if constexpr (kRowMma && (off) > 0) row_sum_store(dsum, ys + ((off) - 16) * rows::kYStride, cg, lane);
 #define JSCAN_H1(GR, off)                                                                              \
-    scan_half<1, AF, kTrap, kRowMma>(GR, h_0, h_1, a2_0, a2_1, ys + (off) * rows::kYStride, rt, ch, pa[1]); \
-    if constexpr (kRowMma) dsum = row_sum_mma(pa[0], pa[1], rsel);
-            load_half<0, kTrap>(G[1], dxc, bcc, psc, 16, ch, n0, c);
+    scan_half<1, AF, kTrap, OS>(GR, h_0, h_1, a2_0, a2_1, ys + (off) * rows::kYStride, rt, ch, dn, sel); \
+    if constexpr (kRowMma) dsum = dn;
+            constexpr int so = cur * rows::kSelSize;
+            load_half<0, kTrap, kCOps>(G[1], dxc, bcc, psc, 16, ch, n0, c, selp, so);
             JSCAN_SB;
             JSCAN_H0(G[0], 0)
             JSCAN_SB;
-            load_half<1, kTrap>(G[1], dxc, bcc, psc, 16, ch, n0, c);
+            load_half<1, kTrap, kCOps>(G[1], dxc, bcc, psc, 16, ch, n0, c, selp, so);
             JSCAN_SB;
             JSCAN_H1(G[0], 0)
             JSCAN_SB;
-            load_half<0, kTrap>(G[0], dxc, bcc, psc, 32, ch, n0, c);
+            load_half<0, kTrap, kCOps>(G[0], dxc, bcc, psc, 32, ch, n0, c, selp, so);
             JSCAN_SB;
             JSCAN_H0(G[1], 16)
             JSCAN_SB;
-            load_half<1, kTrap>(G[0], dxc, bcc, psc, 32, ch, n0, c);
+            load_half<1, kTrap, kCOps>(G[0], dxc, bcc, psc, 32, ch, n0, c, selp, so);
             JSCAN_SB;
             JSCAN_H1(G[1], 16)
             JSCAN_SB;
-            load_half<0, kTrap>(G[1], dxc, bcc, psc, 48, ch, n0, c);
+            load_half<0, kTrap, kCOps>(G[1], dxc, bcc, psc, 48, ch, n0, c, selp, so);
             JSCAN_SB;
             JSCAN_H0(G[0], 32)
             JSCAN_SB;
-            load_half<1, kTrap>(G[1], dxc, bcc, psc, 48, ch, n0, c);
+            load_half<1, kTrap, kCOps>(G[1], dxc, bcc, psc, 48, ch, n0, c, selp, so);
             JSCAN_SB;
             JSCAN_H1(G[0], 32)
             JSCAN_SB;
@@ -790,8 +881,8 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
         }
         __syncthreads();
         if (k + 1 < ntiles) {
-            load_half<0, kTrap>(G[0], dx_s[nxt], bc_s[nxt], p_s[nxt], 0, ch, n0, c);
-            load_half<1, kTrap>(G[0], dx_s[nxt], bc_s[nxt], p_s[nxt], 0, ch, n0, c);
+            load_half<0, kTrap, kCOps>(G[0], dx_s[nxt], bc_s[nxt], p_s[nxt], 0, ch, n0, c, selp, nxt * rows::kSelSize);
+            load_half<1, kTrap, kCOps>(G[0], dx_s[nxt], bc_s[nxt], p_s[nxt], 0, ch, n0, c, selp, nxt * rows::kSelSize);
         }
     };
 #undef JSCAN_SB

@@ -61,3 +61,17 @@ class GlobalRel:
 
 def channel_blocks(D, block):
     return [(c0, min(c0 + block, D)) for c0 in range(0, D, block)]
+
+
+def assert_bf16_sums_close(y1, y2, what):
+    """Two bf16 outputs of the same fp32 states whose sums over states were formed in two ways
+    (terms rounded to bf16 once, 2^-9 relative, then summed in fp32; or summed in fp32): each
+    element is then rounded to bf16, so the two may differ by up to two units in the last
+    place (2^-6 relative) plus what the terms' rounding leaves after cancellation: up to 2^-9
+    of the sum of the terms' magnitudes each way, taken as 2^-6 of the largest output (below
+    the 2e-2 of it that both are held to against the oracle)."""
+    a, b = y1.double(), y2.double()
+    tol = 2 ** -6 * torch.maximum(a.abs(), b.abs()) + 2 ** -6 * b.abs().max()
+    bad = (a - b).abs() > tol
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements, max |diff| {(a - b).abs().max().item():.3g}"
+

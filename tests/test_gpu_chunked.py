@@ -12,7 +12,7 @@ import torch
 import mamba_selective_scan_03_amd as jscan
 import oracle
 import workloads
-from gpu_util import assert_parity, bits, f64, say, to_dev
+from gpu_util import assert_bf16_sums_close, assert_parity, bits, f64, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -63,8 +63,7 @@ def test_first_segment_is_the_sequential_scan(batch, L, D, dtype, chunk):
     if dtype == "f32":
         assert torch.equal(bits(a), bits(b))
     else:
-        err = (a.double() - b.double()).abs().max().item()
-        assert err <= 2 ** -7 * b.double().abs().max().item(), err
+        assert_bf16_sums_close(a, b, "first segment y")
 
 
 @pytest.mark.parametrize("chunk", [0, 4096, 100000])

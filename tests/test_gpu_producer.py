@@ -17,7 +17,7 @@ import torch
 import mamba_selective_scan_03_amd as jscan
 import oracle
 import workloads
-from gpu_util import assert_parity, bits, f64, say
+from gpu_util import assert_bf16_sums_close, assert_parity, bits, f64, say
 from oracle import producer as P
 
 pytestmark = pytest.mark.gpu
@@ -155,7 +155,10 @@ def test_ssm_inputs_full_size_sampled_rows():
                                                 (1, 63, 128, True), (1, 1, 128, False)])
 def test_fused_prefill_is_bit_identical_to_producer_then_scan(batch, L, D, with_h0):
     """Delta computed inside the scan (jscan_prefill_fused) equals the producer's delta bit for
-    bit, so y and h_final match jscan_ssm_inputs followed by jscan_prefill(_resume) exactly."""
+    bit, so h_final matches jscan_ssm_inputs followed by jscan_prefill(_resume) exactly.  y sums
+    over the states differently on the matrix cores (the fused scan sums the lanes' partials,
+    rounded to bf16; the plain scan contracts the states, rounded to bf16, with C), so y agrees to
+    those roundings."""
     inp = workloads.small_prefill(batch, L, D, "bf16", seed=L + D)
     wts = workloads.producer_weights(D, 256, seed=D)
     dev = {k: v.cuda() for k, v in wts.items()}
@@ -170,14 +173,15 @@ def test_fused_prefill_is_bit_identical_to_producer_then_scan(batch, L, D, with_
     torch.cuda.synchronize()
     say(f"fused {batch}x{L}x{D} h0={with_h0}")
     assert torch.equal(bits(d_low), bits(d_low2)) and torch.equal(bits(B), bits(B2))
-    assert torch.equal(bits(y1), bits(y2)), "fused y differs"
     assert torch.equal(bits(h1), bits(h2)), "fused h_final differs"
+    assert_bf16_sums_close(y1, y2, "fused y")
 
 
 def test_fused_prefill_64k_full_size():
     """The 64K x 8192 workload through the producer in the launch configurations the
     benchmark times: the fused scan (delta computed on the load path) equals the producer's
-    stored delta followed by jscan_prefill on every output bit."""
+    stored delta followed by jscan_prefill on every state bit, and on y to the roundings of
+    the two sums over states."""
     wl = workloads.get("prefill_64k")
     say("generating prefill_64k x, A")
     inp = workloads.prefill_inputs(wl)
@@ -190,8 +194,9 @@ def test_fused_prefill_64k_full_size():
     del delta
     y2, h2 = jscan.prefill_fused(x, d_low, dev["w_dt"], dev["b_dt"], A, B, C)
     torch.cuda.synchronize()
-    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "fused 64K y differs"
     assert torch.equal(h1.view(torch.int32), h2.view(torch.int32)), "fused 64K h_final differs"
+    for i in range(0, wl.L, 8192):   # in token blocks, to bound the fp64 copies
+        assert_bf16_sums_close(y1[:, i:i + 8192], y2[:, i:i + 8192], f"fused 64K y, tokens {i}..")
 
 
 def oracle_producer_then_scan(x, wts, A, h0=None, R=256):
