@@ -54,6 +54,11 @@ constexpr int kDxStride = (kCh + 1) * 4;   // [token pair][channel][4]: +1 float
 constexpr int kBcStride = kT + 8;          // [state][token] B and C tiles
 constexpr int kYStride = kCh + 16;         // [token][channel] y exchange (kCh + 8, which puts
                                            // the 4 rows of a wave in distinct banks, measured slower)
+// The same with the contraction on the matrix cores with C as an operand, whose 16-byte stores
+// put token t of a group at t * kYStrideC: an odd number of 16-byte units, so the 16 tokens'
+// stores fall on distinct banks (the 64K scan 1.83 -> 1.77 ms; the fused scan, which keeps the
+// row sums of partials, was slower with it and keeps kYStride)
+constexpr int kYStrideC = kCh + 12;
 // LDS (floats): delta*x/delta pairs [kT/2][kDxStride], B and C [16][kBcStride], y [2][kT][kYStride]
 constexpr int kDxSize = kT / 2 * kDxStride;
 constexpr int kBcSize = kDState * kBcStride;
@@ -532,8 +537,8 @@ __device__ __forceinline__ void c_operand_bases(const uint32_t *(&selp)[4], cons
         selp[m] = cs_s + sh * rows::kSelHalf + (z * 64 + lane) * rows::kSelLane;
     }
 }
-__device__ __forceinline__ void row_sum_store(const f32x4_t &d, float *ys, int cg, int lane) {
-    *reinterpret_cast<f32x4_t *>(ys + (lane & 15) * rows::kYStride + 16 * cg + 4 * (lane >> 4)) = d;
+__device__ __forceinline__ void row_sum_store(const f32x4_t &d, float *ys, int cg, int lane, int yst) {
+    *reinterpret_cast<f32x4_t *>(ys + (lane & 15) * yst + 16 * cg + 4 * (lane >> 4)) = d;
 }
 
 // The same half split in two: the tokens' partials (computed in one scheduling region) and their
@@ -561,10 +566,10 @@ __device__ __forceinline__ void half_store(const float (&P)[8], float *ys, int r
 struct FinalRegs {
     float4 u[2], w[2];
 };
-__device__ __forceinline__ void read_final(FinalRegs &F, const float *y_tile, int tid) {
+__device__ __forceinline__ void read_final(FinalRegs &F, const float *y_tile, int tid, int yst) {
     const int t = tid >> 2, c8 = (tid & 3) * 8;
-    const float *y0 = y_tile + t * rows::kYStride + c8;
-    const float *y1 = y0 + rows::kT * rows::kYStride;
+    const float *y0 = y_tile + t * yst + c8;
+    const float *y1 = y0 + rows::kT * yst;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         F.u[j] = *reinterpret_cast<const float4 *>(y0 + 4 * j);
@@ -625,7 +630,8 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
     __shared__ __attribute__((aligned(16))) float dx_s[2][rows::kDxSize];
     __shared__ __attribute__((aligned(16))) float bc_s[2][(kTrap ? 3 : 2) * rows::kBcSize];
     __shared__ __attribute__((aligned(16))) float p_s[2][kTrap ? rows::kPSize : 4];
-    __shared__ __attribute__((aligned(16))) float y_s[2][rows::kYSize];
+    constexpr int kYS = kCOps ? rows::kYStrideC : rows::kYStride;   // y exchange row stride
+    __shared__ __attribute__((aligned(16))) float y_s[2][2 * rows::kT * kYS];
     __shared__ __attribute__((aligned(16))) uint16_t xch_s[kFused ? 4 * fused::kXchWave : 8];
     __shared__ __attribute__((aligned(16))) uint32_t cs_s[2][kCOps ? rows::kSelSize : 4];
 
@@ -725,7 +731,7 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
                 load_dlow(dfr[nxt], dp.d_low, row, (int64_t)(k + 3) * rows::kT, L, hw, l);
             }
             if (k > 0) {
-                read_final(F, y_s[nxt], tid);
+                read_final(F, y_s[nxt], tid, kYS);
                 write_final<E>(F, yb, (int64_t)(k - 1) * rows::kT, L, D, tid);
             }
             __syncthreads();
@@ -743,7 +749,7 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
                 if (k + 1 < ntiles) tile(IntConst<1>{}, k + 1);
             }
         }
-        read_final(F, y_s[(ntiles - 1) & 1], tid);
+        read_final(F, y_s[(ntiles - 1) & 1], tid, kYS);
         write_final<E>(F, yb, (int64_t)(ntiles - 1) * rows::kT, L, D, tid);
         return;
     }
@@ -797,17 +803,17 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
 #define JSCAN_SB __builtin_amdgcn_sched_barrier(0)
     auto tile = [&](auto cur_c, int k) {
         constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
-        float *ys = y_s[cur] + sh * rows::kT * rows::kYStride;
+        float *ys = y_s[cur] + sh * rows::kT * kYS;
         const float *dxc = dx_s[cur], *bcc = bc_s[cur], *psc = p_s[cur];
         if constexpr (AF != AForm::ScaledIdentity || kRowMma) {
             // With the row sums on the matrix cores, a group's sums are stored in the next
             // scheduling region, when its MFMAs have had a half group's tokens to finish.
             f32x4_t dn, dsum;
 #define JSCAN_H0(GR, off)                                                                              \
-    scan_half<0, AF, kTrap, OS>(GR, h_0, h_1, a2_0, a2_1, ys + (off) * rows::kYStride, rt, ch, dn, sel); \
-    if constexpr (kRowMma && (off) > 0) row_sum_store(dsum, ys + ((off) - 16) * rows::kYStride, cg, lane);
+    scan_half<0, AF, kTrap, OS>(GR, h_0, h_1, a2_0, a2_1, ys + (off) * kYS, rt, ch, dn, sel); \
+    if constexpr (kRowMma && (off) > 0) row_sum_store(dsum, ys + ((off) - 16) * kYS, cg, lane, kYS);
 #define JSCAN_H1(GR, off)                                                                              \
-    scan_half<1, AF, kTrap, OS>(GR, h_0, h_1, a2_0, a2_1, ys + (off) * rows::kYStride, rt, ch, dn, sel); \
+    scan_half<1, AF, kTrap, OS>(GR, h_0, h_1, a2_0, a2_1, ys + (off) * kYS, rt, ch, dn, sel); \
     if constexpr (kRowMma) dsum = dn;
             constexpr int so = cur * rows::kSelSize;
             load_half<0, kTrap, kCOps>(G[1], dxc, bcc, psc, 16, ch, n0, c, selp, so);
@@ -837,7 +843,7 @@ __global__ __launch_bounds__(rows::kThreads) __attribute__((amdgpu_waves_per_eu(
             JSCAN_H0(G[1], 48)
             JSCAN_SB;
             JSCAN_H1(G[1], 48)
-            if constexpr (kRowMma) row_sum_store(dsum, ys + 48 * rows::kYStride, cg, lane);
+            if constexpr (kRowMma) row_sum_store(dsum, ys + 48 * kYS, cg, lane, kYS);
 #undef JSCAN_H0
 #undef JSCAN_H1
         } else {
