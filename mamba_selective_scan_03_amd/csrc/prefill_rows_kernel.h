@@ -11,18 +11,21 @@
 // group; row r owns the state pair n = 8*sh + 2*r + {0,1}, where sh picks one half of the
 // states.  Two waves (sh = 0, 1) cover all 16 states of one 16-channel group, and a
 // 256-thread workgroup covers 32 channels (two groups).
-//   * B_t[n] and C_t[n] are the same for all 16 lanes of a row.  A register holds 16
-//     consecutive tokens' values of one state (lane c = token c), and the DPP row broadcast
-//     (row_newbcast:k) hands token k's value to the whole row inside the multiply.  No extra
-//     instruction is issued.
+//   * B_t[n] (and, with fp32 output, C_t[n]) is the same for all 16 lanes of a row.  A
+//     register holds 16 consecutive tokens' values of one state (lane c = token c), and the
+//     DPP row broadcast (row_newbcast:k) hands token k's value to the whole row inside the
+//     multiply.  No extra instruction is issued.
 //   * delta_t[d] and delta_t[d] * x_t[d] are per lane (per channel).  The workgroup converts
 //     each tile once into fp32 pairs in LDS, and every row reads them as a broadcast.  With a
 //     scaled-identity A (AForm::ScaledIdentity: one a[d] for all states of a channel) the pair
 //     carries the channel's decay 2^(delta * a2[d]) in place of delta, computed once per
 //     (token, channel) while staging, and the scan waves run no exponential at all.
-//   * y_t[d] = sum over 16 states = 2 states in-lane, 4 rows in-wave (two permlane swap
-//     stages), then 2 waves through LDS.  The last stage is fused with the bf16 conversion
-//     and a coalesced row store.
+//   * y_t[d] = sum over 16 states: each wave's 8 states, then its 2 waves through LDS (the
+//     last stage fused with the bf16 conversion and a coalesced row store).  With bf16 output
+//     a wave's share is a small product on the matrix cores, its states (rounded to bf16)
+//     against C as an MFMA operand (c_operand_bases()); with delta computed on the load path
+//     the lanes' 2-state partials are summed over the 4 rows there instead (row_sum_operands());
+//     with fp32 output the 2-state partials are summed over the rows by permlane swaps.
 //
 // Pipeline.  Tokens go in tiles of 64.  While tile k is scanned, tile k+1 is converted from
 // registers into LDS and tiles k+2 and k+3 are in flight from HBM into two register sets,
