@@ -223,6 +223,43 @@ def single_thread_rate():
             "sample": f"prefill_4k: all {wl.L} tokens, first {ch} of {wl.D} channels ({dt:.2f} s)"}
 
 
+def run_micro_scan(log):
+    """The wavefront-level associative scan of (a, b) pairs over the 64 lanes of a wave, by DPP
+    (libjscan_micro kind 11: 6 levels of a DPP-fed FMA and multiply on 8 independent chains),
+    beside the FMA and the DPP-broadcast multiply it is built from, at 8 waves and 1 wave per
+    SIMD.  Reports cycles per wave instruction and the combine's cost per (a, b) element in FMA
+    slots, to set against the sequential scan's 7.05 slots for a whole state element."""
+    import torch
+
+    from mamba_selective_scan_03_amd import micro
+
+    cus = 256
+    out = {"gpu": torch.cuda.get_device_name(0), "rocm": torch.version.hip}
+    ms, clk, ticks = micro.valu(0, 100000, 2048, 256)
+    hz = clk / (ticks / 100e6)
+    out["shader_clock_GHz"] = round(hz / 1e9, 3)
+
+    def cycles_per_instr(kind, waves_per_simd, iters, per_trip):
+        ms, _, _ = micro.valu(kind, iters, cus * waves_per_simd, 256)
+        return ms * 1e-3 * hz / (waves_per_simd * iters * per_trip)
+
+    rows = {}
+    for kind, name, per_trip in ((0, "fma", 16), (4, "mul_dpp_bcast", 16), (11, "wave_scan_level_dpp", 96)):
+        rows[name] = {f"cycles_per_instr_{w}w": round(cycles_per_instr(kind, w, iters // per_trip * 16, per_trip), 3)
+                      for w, iters in ((8, 20000), (1, 80000))}
+        log(f"micro {name}: {rows[name]}")
+    out["valu_cycles_per_wave_instruction"] = rows
+    c_fma = rows["fma"]["cycles_per_instr_8w"]
+    c_lvl = rows["wave_scan_level_dpp"]["cycles_per_instr_8w"]
+    out["derived"] = {
+        "scan_levels": 6,
+        "instructions_per_element": 12,
+        "combine_cost_in_fma_slots_per_element": round(12 * c_lvl / c_fma, 2),
+        "sequential_state_element_fma_slots": 7.05,
+    }
+    return out
+
+
 def run_micro(log):
     """The microbenchmarks of libjscan_micro: vector-ALU issue rates (FMA, exponential, their
     mix, DPP and permlane forms) at 8 waves and at 1 wave per SIMD, matrix cores beside the
@@ -474,6 +511,8 @@ def main():
     ap.add_argument("--cpu-channels", type=int, default=8192,
                     help="oracle sample: all tokens of the first CPU_CHANNELS channels (default: every channel "
                          "of the 64K workload, a few seconds on 16 cores; 0 = skip)")
+    ap.add_argument("--micro-scan", action="store_true",
+                    help="time the wavefront-level (a, b) scan combine by DPP against the FMA (no bench line)")
     ap.add_argument("--micro", action="store_true",
                     help="instead of the scan, run the microbenchmarks (vector ALU, matrix cores, LDS, HBM) and print "
                          "their rates as one JSON line")
@@ -512,6 +551,11 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.micro_scan:
+        torch.cuda.set_device(dev)
+        print(json.dumps({"micro_scan": run_micro_scan(lambda *a: print("[bench]", *a, file=sys.stderr, flush=True))}),
+              flush=True)
+        return
     if args.micro:
         torch.cuda.set_device(dev)
         print(json.dumps({"micro": run_micro(lambda *a: print("[bench]", *a, file=sys.stderr, flush=True))}),

@@ -44,6 +44,9 @@ extern "C" {
  *      2-term output partial (10 instructions), plus 2 register moves (12 per token counted)
  *   9  the same with B and C broadcast by DPP (row_newbcast) inside the multiplies
  *  10  v_fmac_f32 x16, independent, with three distinct source registers each
+ *  11  an inclusive scan of 8 independent (a, b) chains over the wave's 64 lanes: 6 levels
+ *      (row_shr 1, 2, 4, 8, then row_bcast 15 and 31), each a v_fmac_f32_dpp (b) and a
+ *      v_mul_f32_dpp (a) per chain: 96 instructions per trip
  * sink: blocks * threads floats, then 4 more: (shader clocks, 100 MHz real-time ticks) of
  * block 0's first wave over its loop, as two pairs of floats (low, high 32 bits); kinds 0-7
  * and 10 then store each wave's HW_ID and XCC_ID registers (2 floats per wave, as raw bits),

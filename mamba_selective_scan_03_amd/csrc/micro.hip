@@ -100,6 +100,29 @@ __device__ __forceinline__ void valu_trip(float (&r)[16], float a, float b) {
             "v_fmac_f32 %8, %13, %3\n\tv_fmac_f32 %9, %14, %4\n\tv_fmac_f32 %10, %15, %5\n\tv_fmac_f32 %11, %0, %6\n\t"
             "v_fmac_f32 %12, %1, %7\n\tv_fmac_f32 %13, %2, %8\n\tv_fmac_f32 %14, %3, %9\n\tv_fmac_f32 %15, %4, %10"
             : R16);
+    } else if constexpr (KIND == 11) {
+        // one inclusive scan of 8 independent (a, b) chains over the 64 lanes, by DPP: the
+        // composition (a, b) of lanes i-k and i is (a_{i-k} a_i, a_i b_{i-k} + b_i), k = 1, 2, 4, 8
+        // inside each 16-lane row (row_shr; lanes with no source lane keep their pair), then across
+        // rows (row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3).  r[j] holds a of
+        // chain j, r[8 + j] its b; b is updated before a so that it uses the old a.
+#define JSCAN_LVL(ctl)                                                                                    \
+    "v_fmac_f32_dpp %8, %8, %0 " ctl "\n\tv_fmac_f32_dpp %9, %9, %1 " ctl "\n\t"                          \
+    "v_fmac_f32_dpp %10, %10, %2 " ctl "\n\tv_fmac_f32_dpp %11, %11, %3 " ctl "\n\t"                       \
+    "v_fmac_f32_dpp %12, %12, %4 " ctl "\n\tv_fmac_f32_dpp %13, %13, %5 " ctl "\n\t"                       \
+    "v_fmac_f32_dpp %14, %14, %6 " ctl "\n\tv_fmac_f32_dpp %15, %15, %7 " ctl "\n\t"                       \
+    "v_mul_f32_dpp %0, %0, %0 " ctl "\n\tv_mul_f32_dpp %1, %1, %1 " ctl "\n\t"                             \
+    "v_mul_f32_dpp %2, %2, %2 " ctl "\n\tv_mul_f32_dpp %3, %3, %3 " ctl "\n\t"                             \
+    "v_mul_f32_dpp %4, %4, %4 " ctl "\n\tv_mul_f32_dpp %5, %5, %5 " ctl "\n\t"                             \
+    "v_mul_f32_dpp %6, %6, %6 " ctl "\n\tv_mul_f32_dpp %7, %7, %7 " ctl "\n\t"
+        asm volatile(JSCAN_LVL("row_shr:1 row_mask:0xf bank_mask:0xf")
+                     JSCAN_LVL("row_shr:2 row_mask:0xf bank_mask:0xf")
+                     JSCAN_LVL("row_shr:4 row_mask:0xf bank_mask:0xf")
+                     JSCAN_LVL("row_shr:8 row_mask:0xf bank_mask:0xf")
+                     JSCAN_LVL("row_bcast:15 row_mask:0xa bank_mask:0xf")
+                     JSCAN_LVL("row_bcast:31 row_mask:0xc bank_mask:0xf")
+                     : R16);
+#undef JSCAN_LVL
     } else if constexpr (KIND == 7) {
         // 8 (product, exponential) pairs: the decay 2^(delta * A2) of 8 state elements;
         // r[8 + i] holds the product, r[i] the exponential
@@ -363,7 +386,7 @@ int timed(hipStream_t stream, int reps, float *ms_out, F launch) {
 extern "C" {
 
 int jscan_micro_valu(int kind, int64_t iters, int blocks, int threads, float *sink, void *stream, float *ms_out) {
-    if (kind < 0 || kind > 10 || iters < 1 || iters > (1 << 24) || blocks < 1 || blocks > 65536 ||
+    if (kind < 0 || kind > 11 || iters < 1 || iters > (1 << 24) || blocks < 1 || blocks > 65536 ||
         !threads_ok(threads, 1024) || !sink || !ms_out)
         return -1;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -389,6 +412,7 @@ int jscan_micro_valu(int kind, int64_t iters, int blocks, int threads, float *si
     case 5: return go(std::integral_constant<int, 5>{});
     case 6: return go(std::integral_constant<int, 6>{});
     case 7: return go(std::integral_constant<int, 7>{});
+    case 11: return go(std::integral_constant<int, 11>{});
     default: return go(std::integral_constant<int, 10>{});
     }
 }
