@@ -887,7 +887,7 @@ def main():
     }
     if producer_info is not None:
         out["producer"] = producer_info
-    out.update(run_info(torch))
+    out.update(run_info(torch, ("step" if wl.layers > 1 else "prefill") + ("_mimo" if args.mimo else "")))
     if host_inp is not None and args.cpu_channels > 0 and wl.layers == 1:
         ch = min(args.cpu_channels, wl.D)
         out["cpu_baseline"], ref = cpu_baseline(wl, host_inp, ch, host_a if args.scalar_a else None,
@@ -913,8 +913,9 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def run_info(torch):
-    """GPU, ROCm and source identification for the report line."""
+def run_info(torch, kind: str):
+    """GPU, ROCm and source identification for the report line; `kind` names the timed
+    kernel's sources (a key of KERNEL_SOURCES)."""
     props = torch.cuda.get_device_properties(0)
     info = {"gpu": torch.cuda.get_device_name(0), "gpu_arch": getattr(props, "gcnArchName", None),
             "compute_units": props.multi_processor_count, "rocm": torch.version.hip, "torch": torch.__version__}
@@ -927,7 +928,7 @@ def run_info(torch):
     except (OSError, subprocess.SubprocessError):
         pass
     info["git_sha"] = sha   # None where the tree was copied without its history
-    info["kernel_source_hash"] = kernel_source_hash("prefill")
+    info["kernel_source_hash"] = kernel_source_hash(kind)
     return info
 
 
@@ -941,7 +942,7 @@ def bitexact_check(jscan, d, wl, tokens: int = 256):
     h = torch.zeros_like(h_pre)
     y_t = torch.empty((wl.batch, wl.D), dtype=x.dtype, device=x.device)
     for t in range(tokens):
-        jscan.step(h, x[:, t], dl[:, t], d["A"], B[:, t], C[:, t], y_t=y_t if wl.batch == 1 else None)
+        jscan.step(h, x[:, t], dl[:, t], d["A"], B[:, t], C[:, t], y_t=y_t)
     torch.cuda.synchronize()
     return bool(torch.equal(h.view(torch.int32), h_pre.view(torch.int32)))
 

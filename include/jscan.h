@@ -207,14 +207,15 @@ jscan_status jscan_prefill_fused(const void *x, const void *delta_low, const voi
  *   x_t, delta_t: batch rows of D values; row b starts at element b * ld_xd
  *   A        [D][N] fp32
  *   B_t, C_t: batch rows of N values; row b starts at element b * ld_bc
- *   y_t      batch rows of D values, row stride ld_xd, same dtype as x_t
+ *   y_t      batch rows of D values; row b starts at element b * ld_y; same dtype as x_t
  * The strides let a caller pass token t of prefill-layout tensors without a copy
- * (x + t*D with ld_xd = L*D, B + t*N with ld_bc = L*N).  ld_xd >= D, ld_bc >= N, and
- * both must be multiples of 8.
+ * (x + t*D with ld_xd = L*D, B + t*N with ld_bc = L*N), and write y_t either into a
+ * prefill-layout output (y + t*D with ld_y = L*D) or into a contiguous [batch][D] (ld_y = D).
+ * ld_xd >= D, ld_bc >= N, ld_y >= D, and all three must be multiples of 8.
  */
 jscan_status jscan_step(float *h, const void *x_t, const void *delta_t, const float *A,
                         const void *B_t, const void *C_t, void *y_t, int64_t batch, int64_t D,
-                        int64_t N, int64_t ld_xd, int64_t ld_bc, jscan_dtype dtype,
+                        int64_t N, int64_t ld_xd, int64_t ld_bc, int64_t ld_y, jscan_dtype dtype,
                         void *stream);
 
 /*
@@ -241,7 +242,7 @@ jscan_status jscan_prefill_scalar_a(const void *x, const void *delta, const floa
 jscan_status jscan_step_scalar_a(float *h, const void *x_t, const void *delta_t, const float *a,
                                  const void *B_t, const void *C_t, void *y_t, int64_t batch,
                                  int64_t D, int64_t N, int64_t ld_xd, int64_t ld_bc,
-                                 jscan_dtype dtype, void *stream);
+                                 int64_t ld_y, jscan_dtype dtype, void *stream);
 
 /*
  * Complex-valued state (the Mamba-3 form).  The lesson page ("Jamba - Hybrid SSM-Transformer",
@@ -270,7 +271,7 @@ jscan_status jscan_prefill_complex(const void *x, const void *delta, const float
 jscan_status jscan_step_complex(float *h, const void *x_t, const void *delta_t, const float *A,
                                 const void *B_t, const void *C_t, void *y_t, int64_t batch,
                                 int64_t D, int64_t N, int64_t ld_xd, int64_t ld_bc,
-                                jscan_dtype dtype, void *stream);
+                                int64_t ld_y, jscan_dtype dtype, void *stream);
 
 /*
  * Exponential-trapezoidal discretisation, the Mamba-3 replacement of the Euler rule (lesson
@@ -316,8 +317,8 @@ jscan_status jscan_prefill_trapezoid(const void *x, const void *delta, const voi
 jscan_status jscan_step_trapezoid(float *h, const void *x_prev, const void *B_prev, const void *x_t,
                                   const void *delta_t, const void *lam_t, const float *A, const void *B_t,
                                   const void *C_t, void *y_t, int64_t batch, int64_t D, int64_t N,
-                                  int64_t ld_xd, int64_t ld_bc, jscan_a_form a_form, jscan_dtype dtype,
-                                  void *stream);
+                                  int64_t ld_xd, int64_t ld_bc, int64_t ld_y, jscan_a_form a_form,
+                                  jscan_dtype dtype, void *stream);
 
 /*
  * Multi-input, multi-output (MIMO) scan, the Mamba-3 replacement of the per-channel scalar
@@ -344,14 +345,15 @@ jscan_status jscan_prefill_mimo(const void *x, const void *delta, const float *A
                                 jscan_a_form a_form, jscan_dtype dtype, void *stream);
 
 /*
- * One MIMO decode token for a batch, h [batch][D][N] in place.  x_t and y_t are rows of D * R
- * with row stride ld_x; delta_t rows of D with stride ld_d; B_t and C_t rows of N * R with
- * stride ld_bc (strides in elements, multiples of 8, at least the row length).
+ * One MIMO decode token for a batch, h [batch][D][N] in place.  x_t is rows of D * R with
+ * row stride ld_x; delta_t rows of D with stride ld_d; B_t and C_t rows of N * R with stride
+ * ld_bc; y_t rows of D * R with stride ld_y (strides in elements, multiples of 8, at least the
+ * row length).
  */
 jscan_status jscan_step_mimo(float *h, const void *x_t, const void *delta_t, const float *A,
                              const void *B_t, const void *C_t, void *y_t, int64_t batch, int64_t D,
                              int64_t N, int64_t R, int64_t ld_x, int64_t ld_d, int64_t ld_bc,
-                             jscan_a_form a_form, jscan_dtype dtype, void *stream);
+                             int64_t ld_y, jscan_a_form a_form, jscan_dtype dtype, void *stream);
 
 /*
  * The MIMO scan with the exponential-trapezoidal rule: both Mamba-3 changes together.  The
@@ -380,8 +382,8 @@ jscan_status jscan_step_mimo_trapezoid(float *h, const void *x_prev, const void 
                                        const void *x_t, const void *delta_t, const void *lam_t,
                                        const float *A, const void *B_t, const void *C_t, void *y_t,
                                        int64_t batch, int64_t D, int64_t N, int64_t R, int64_t ld_x,
-                                       int64_t ld_d, int64_t ld_bc, jscan_a_form a_form,
-                                       jscan_dtype dtype, void *stream);
+                                       int64_t ld_d, int64_t ld_bc, int64_t ld_y,
+                                       jscan_a_form a_form, jscan_dtype dtype, void *stream);
 
 /*
  * jscan_prefill_chunked without a workspace argument, for callers that cannot allocate device
@@ -416,7 +418,7 @@ int jscan_last_hip_error(void);
 /* Library ABI version: 100 * major + minor (101 adds the time-parallel prefill, 102 the
  * producer side, 103 the fused prefill, 104 the scaled-identity A entry points, 105 the
  * complex-valued state, 106 the exponential-trapezoidal rule, 107 the MIMO scan, 108 MIMO with the
- * trapezoidal rule). */
+ * trapezoidal rule, 109 the output row stride ld_y of the decode steps). */
 int jscan_version(void);
 
 #ifdef __cplusplus

@@ -41,7 +41,7 @@ def library():
     vp, fp, i64, i32 = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.jscan_prefill.argtypes = [vp, vp, fp, vp, vp, vp, fp, i64, i64, i64, i64, i32, vp]
     lib.jscan_prefill_resume.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, i32, vp]
-    lib.jscan_step.argtypes = [fp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+    lib.jscan_step.argtypes = [fp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, vp]
     lib.jscan_prefill_chunked.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, i64, vp, i64, i32, vp]
     lib.jscan_prefill_chunked_workspace.argtypes = [i64, i64, i64, i64, i64]
     lib.jscan_prefill_chunked_noalloc.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, i64, i32, vp]
@@ -52,17 +52,18 @@ def library():
     lib.jscan_prefill_fused.argtypes = [vp, vp, vp, fp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, i64, i32, vp]
     lib.jscan_prefill_fused.restype = i32
     lib.jscan_prefill_scalar_a.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, i32, vp]
-    lib.jscan_step_scalar_a.argtypes = [fp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+    lib.jscan_step_scalar_a.argtypes = [fp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, vp]
     lib.jscan_prefill_complex.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, i32, vp]
-    lib.jscan_step_complex.argtypes = [fp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+    lib.jscan_step_complex.argtypes = [fp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, vp]
     lib.jscan_prefill_trapezoid.argtypes = [vp, vp, vp, fp, vp, vp, fp, vp, vp, vp, fp, i64, i64, i64, i64, i32, i32, vp]
-    lib.jscan_step_trapezoid.argtypes = [fp, vp, vp, vp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp]
+    lib.jscan_step_trapezoid.argtypes = [fp, vp, vp, vp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32,
+                                         vp]
     lib.jscan_prefill_mimo.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, i64, i32, i32, vp]
-    lib.jscan_step_mimo.argtypes = [fp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32, i32, vp]
+    lib.jscan_step_mimo.argtypes = [fp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i32, i32, vp]
     lib.jscan_prefill_mimo_trapezoid.argtypes = [vp, vp, vp, fp, vp, vp, fp, vp, vp, vp, fp, i64, i64, i64, i64, i64,
                                                  i32, i32, vp]
     lib.jscan_step_mimo_trapezoid.argtypes = [fp, vp, vp, vp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
-                                              i32, i32, vp]
+                                              i64, i32, i32, vp]
     lib.jscan_prefill_chunked_workspace.restype = i64
     for f in (lib.jscan_prefill, lib.jscan_prefill_resume, lib.jscan_step, lib.jscan_prefill_chunked,
               lib.jscan_prefill_scalar_a, lib.jscan_step_scalar_a, lib.jscan_prefill_complex, lib.jscan_step_complex,
@@ -285,11 +286,27 @@ def prefill_fused(x, delta_low, w_dt, b_dt, A, B, C, h0=None, y=None, h_final=No
     return y, h_final
 
 
-def step_raw(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, dtype, scalar_a=False, complex_a=False):
+def _step_output(y_t, shape, dtype, device):
+    """The output of a decode step and its row stride in elements: a new contiguous tensor, or
+    the caller's ``y_t`` of that shape and dtype whose rows are contiguous (the row stride of a
+    strided view, e.g. ``y[:, t]``, is passed to the library, which checks it)."""
+    if y_t is None:
+        y_t = torch.empty(shape, dtype=dtype, device=device)
+    _require(tuple(y_t.shape) == tuple(shape) and y_t.dtype == dtype and y_t.device == device,
+             f"y_t must be {tuple(shape)} of dtype {dtype} on {device}")
+    row = 1
+    for k in range(len(shape) - 1, 0, -1):
+        _require(y_t.stride(k) == row, "y_t rows must be contiguous")
+        row *= shape[k]
+    return y_t, (y_t.stride(0) if shape[0] > 1 else row)
+
+
+def step_raw(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, dtype, scalar_a=False, complex_a=False,
+             ld_y=None):
     """Direct call of ``jscan_step`` (``jscan_step_scalar_a`` with ``scalar_a``,
     ``jscan_step_complex`` with ``complex_a``) on raw tensors/pointers with explicit row strides
-    (no checks beyond the library's own).  ``x_t`` etc. may be tensors or integer device
-    addresses."""
+    (no checks beyond the library's own; ``ld_y`` defaults to ``ld_xd``).  ``x_t`` etc. may be
+    tensors or integer device addresses."""
     lib = library()
 
     def p(v):
@@ -297,8 +314,8 @@ def step_raw(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, dtype, s
 
     dev = h.device if hasattr(h, "device") else torch.device("cuda")
     fn = lib.jscan_step_scalar_a if scalar_a else lib.jscan_step_complex if complex_a else lib.jscan_step
-    st = fn(p(h), p(x_t), p(delta_t), p(A), p(B_t), p(C_t), p(y_t), batch, D, D_STATE, ld_xd, ld_bc, _DTYPES[dtype],
-            _stream(dev))
+    st = fn(p(h), p(x_t), p(delta_t), p(A), p(B_t), p(C_t), p(y_t), batch, D, D_STATE, ld_xd, ld_bc,
+            ld_xd if ld_y is None else ld_y, _DTYPES[dtype], _stream(dev))
     _check(st)
 
 
@@ -315,11 +332,8 @@ def step_complex(h, x_t, delta_t, A, B_t, C_t, y_t=None):
 def step(h, x_t, delta_t, A, B_t, C_t, y_t=None, _scalar_a=False, _complex_a=False):
     """One decode token for a batch: h ``[batch, D, 16]`` fp32 is updated in place; x_t, delta_t
     ``[batch, D]`` and B_t, C_t ``[batch, 16]`` (rows may be strided views of prefill tensors,
-    e.g. ``x[:, t]``).  Returns y_t ``[batch, D]``.
-
-    In the ABI y_t's rows share x_t's row stride.  Without ``y_t`` this allocates one with that
-    stride: for ``x[:, t]`` of a ``[batch, L, D]`` tensor that is about batch * L * D elements
-    per call.  Pass ``y_t`` (for example ``y[:, t]`` of a ``[batch, L, D]`` output) to avoid it."""
+    e.g. ``x[:, t]``).  Returns y_t ``[batch, D]``: a new contiguous tensor, or the given ``y_t``,
+    whose rows may be strided too (for example ``y[:, t]`` of a ``[batch, L, D]`` output)."""
     _require(h.is_cuda and h.dtype == torch.float32 and h.dim() == 3 and h.shape[2] == D_STATE and h.is_contiguous(),
              "h must be a contiguous fp32 [batch, D, 16] CUDA tensor")
     batch, D, _ = h.shape
@@ -337,14 +351,10 @@ def step(h, x_t, delta_t, A, B_t, C_t, y_t=None, _scalar_a=False, _complex_a=Fal
     _require(batch <= 1 or delta_t.stride(0) == ld_xd, "x_t and delta_t must share a row stride")
     ld_bc = B_t.stride(0) if batch > 1 else D_STATE
     _require(batch <= 1 or C_t.stride(0) == ld_bc, "B_t and C_t must share a row stride")
-    if y_t is None:
-        # y_t rows share x_t's row stride in the ABI
-        y_t = torch.empty((batch, ld_xd), dtype=x_t.dtype, device=h.device)[:, :D]
-    _require(tuple(y_t.shape) == (batch, D) and y_t.dtype == x_t.dtype and y_t.stride(1) == 1
-             and (batch <= 1 or y_t.stride(0) == ld_xd), "y_t must be [batch, D] with x_t's row stride")
+    y_t, ld_y = _step_output(y_t, (batch, D), x_t.dtype, h.device)
     with torch.cuda.device(h.device):
         step_raw(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, x_t.dtype, scalar_a=_scalar_a,
-                 complex_a=_complex_a)
+                 complex_a=_complex_a, ld_y=ld_y)
     return y_t
 
 
@@ -407,15 +417,12 @@ def step_trapezoid(h, x_prev, B_prev, x_t, delta_t, lam_t, A, B_t, C_t, form="di
     a_shape = (D,) if form == "scalar" else (D, D_STATE)
     _require(A.dtype == torch.float32 and tuple(A.shape) == a_shape and A.is_contiguous(),
              f"A must be a contiguous fp32 tensor of shape {a_shape}")
-    if y_t is None:
-        y_t = torch.empty((batch, ld_xd), dtype=x_t.dtype, device=h.device)[:, :D]
-    _require(tuple(y_t.shape) == (batch, D) and y_t.dtype == x_t.dtype and y_t.stride(1) == 1
-             and (batch <= 1 or y_t.stride(0) == ld_xd), "y_t must be [batch, D] with x_t's row stride")
+    y_t, ld_y = _step_output(y_t, (batch, D), x_t.dtype, h.device)
     lib = library()
     with torch.cuda.device(h.device):
         st = lib.jscan_step_trapezoid(_ptr(h), _ptr(x_prev), _ptr(B_prev), _ptr(x_t), _ptr(delta_t), _ptr(lam_t),
                                       _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(y_t), batch, D, D_STATE, ld_xd, ld_bc,
-                                      A_FORMS[form], _DTYPES[x_t.dtype], _stream(h.device))
+                                      ld_y, A_FORMS[form], _DTYPES[x_t.dtype], _stream(h.device))
     _check(st)
     return y_t
 
@@ -521,21 +528,17 @@ def step_mimo(h, x_t, delta_t, A, B_t, C_t, form="diagonal", y_t=None, _trap=Non
             _require(tuple(t.shape) == shape and t.dtype == x_t.dtype and t.device == h.device
                      and t.stride(-1) == 1 and (t.dim() == 2 or t.stride(1) == R) and (batch <= 1 or t.stride(0) == ld),
                      f"{name} must be {shape} with contiguous rows and the row stride of the matching input")
-    if y_t is None:
-        y_t = torch.empty((batch, ld_x), dtype=x_t.dtype, device=h.device)[:, :D * R].view(batch, D, R)
-    _require(tuple(y_t.shape) == (batch, D, R) and y_t.dtype == x_t.dtype and y_t.stride(2) == 1
-             and y_t.stride(1) == R and (batch <= 1 or y_t.stride(0) == ld_x), "y_t must be [batch, D, R] with x_t's "
-             "row stride")
+    y_t, ld_y = _step_output(y_t, (batch, D, R), x_t.dtype, h.device)
     lib = library()
     with torch.cuda.device(h.device):
         if _trap is None:
             st = lib.jscan_step_mimo(_ptr(h), _ptr(x_t), _ptr(delta_t), _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(y_t), batch,
-                                     D, D_STATE, R, ld_x, ld_d, ld_bc, A_FORMS[form], _DTYPES[x_t.dtype],
+                                     D, D_STATE, R, ld_x, ld_d, ld_bc, ld_y, A_FORMS[form], _DTYPES[x_t.dtype],
                                      _stream(h.device))
         else:
             st = lib.jscan_step_mimo_trapezoid(_ptr(h), _ptr(_trap[0]), _ptr(_trap[1]), _ptr(x_t), _ptr(delta_t),
                                                _ptr(_trap[2]), _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(y_t), batch, D,
-                                               D_STATE, R, ld_x, ld_d, ld_bc, A_FORMS[form], _DTYPES[x_t.dtype],
-                                               _stream(h.device))
+                                               D_STATE, R, ld_x, ld_d, ld_bc, ld_y, A_FORMS[form],
+                                               _DTYPES[x_t.dtype], _stream(h.device))
     _check(st)
     return y_t

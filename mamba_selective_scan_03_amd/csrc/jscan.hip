@@ -238,41 +238,42 @@ void launch_prefill_mimo(const void *x, const void *delta, const float *A, const
 
 template <typename E, jscan::AForm AF, int R, bool kTrap>
 void launch_step_mimo_r(float *h, const void *x, const void *delta, const float *A, const void *B, const void *C,
-                        void *y, int64_t batch, int64_t D, int64_t ld_x, int64_t ld_d, int64_t ld_bc, jscan::Trap tr,
-                        hipStream_t s) {
+                        void *y, int64_t batch, int64_t D, int64_t ld_x, int64_t ld_d, int64_t ld_bc, int64_t ld_y,
+                        jscan::Trap tr, hipStream_t s) {
     using T = typename E::store_t;
     const int blocks_per_rows = (int)((D * 4 + 255) / 256);
     const int64_t row_groups = (batch + jscan::mimo_step::kRows - 1) / jscan::mimo_step::kRows;
     hipLaunchKernelGGL((jscan::step_mimo_kernel<E, AF, R, kTrap>), dim3((unsigned)(row_groups * blocks_per_rows)),
                        dim3(256), 0, s, h, static_cast<const T *>(x), static_cast<const T *>(delta), A,
                        static_cast<const T *>(B), static_cast<const T *>(C), static_cast<T *>(y), (int)batch, (int)D,
-                       blocks_per_rows, ld_x, ld_d, ld_bc, static_cast<const T *>(tr.lam),
+                       blocks_per_rows, ld_x, ld_d, ld_bc, ld_y, static_cast<const T *>(tr.lam),
                        static_cast<const T *>(tr.x_prev), static_cast<const T *>(tr.B_prev));
 }
 template <typename E, jscan::AForm AF, bool kTrap>
 void launch_step_mimo_af(float *h, const void *x, const void *delta, const float *A, const void *B, const void *C,
                          void *y, int64_t batch, int64_t D, int64_t R, int64_t ld_x, int64_t ld_d, int64_t ld_bc,
-                         jscan::Trap tr, hipStream_t s) {
+                         int64_t ld_y, jscan::Trap tr, hipStream_t s) {
     switch (R) {
-    case 1: launch_step_mimo_r<E, AF, 1, kTrap>(h, x, delta, A, B, C, y, batch, D, ld_x, ld_d, ld_bc, tr, s); break;
-    case 2: launch_step_mimo_r<E, AF, 2, kTrap>(h, x, delta, A, B, C, y, batch, D, ld_x, ld_d, ld_bc, tr, s); break;
-    case 4: launch_step_mimo_r<E, AF, 4, kTrap>(h, x, delta, A, B, C, y, batch, D, ld_x, ld_d, ld_bc, tr, s); break;
-    default: launch_step_mimo_r<E, AF, 8, kTrap>(h, x, delta, A, B, C, y, batch, D, ld_x, ld_d, ld_bc, tr, s); break;
+    case 1: launch_step_mimo_r<E, AF, 1, kTrap>(h, x, delta, A, B, C, y, batch, D, ld_x, ld_d, ld_bc, ld_y, tr, s); break;
+    case 2: launch_step_mimo_r<E, AF, 2, kTrap>(h, x, delta, A, B, C, y, batch, D, ld_x, ld_d, ld_bc, ld_y, tr, s); break;
+    case 4: launch_step_mimo_r<E, AF, 4, kTrap>(h, x, delta, A, B, C, y, batch, D, ld_x, ld_d, ld_bc, ld_y, tr, s); break;
+    default: launch_step_mimo_r<E, AF, 8, kTrap>(h, x, delta, A, B, C, y, batch, D, ld_x, ld_d, ld_bc, ld_y, tr, s); break;
     }
 }
 template <typename E, bool kTrap>
 void launch_step_mimo(float *h, const void *x, const void *delta, const float *A, const void *B, const void *C,
                       void *y, int64_t batch, int64_t D, int64_t R, int64_t ld_x, int64_t ld_d, int64_t ld_bc,
-                      jscan::AForm af, jscan::Trap tr, hipStream_t s) {
+                      int64_t ld_y, jscan::AForm af, jscan::Trap tr, hipStream_t s) {
     using jscan::AForm;
     if (af == AForm::ScaledIdentity)
-        launch_step_mimo_af<E, AForm::ScaledIdentity, kTrap>(h, x, delta, A, B, C, y, batch, D, R, ld_x, ld_d, ld_bc, tr,
-                                                             s);
+        launch_step_mimo_af<E, AForm::ScaledIdentity, kTrap>(h, x, delta, A, B, C, y, batch, D, R, ld_x, ld_d, ld_bc,
+                                                             ld_y, tr, s);
     else if (af == AForm::ComplexPairs)
-        launch_step_mimo_af<E, AForm::ComplexPairs, kTrap>(h, x, delta, A, B, C, y, batch, D, R, ld_x, ld_d, ld_bc, tr,
-                                                           s);
+        launch_step_mimo_af<E, AForm::ComplexPairs, kTrap>(h, x, delta, A, B, C, y, batch, D, R, ld_x, ld_d, ld_bc,
+                                                           ld_y, tr, s);
     else
-        launch_step_mimo_af<E, AForm::Diagonal, kTrap>(h, x, delta, A, B, C, y, batch, D, R, ld_x, ld_d, ld_bc, tr, s);
+        launch_step_mimo_af<E, AForm::Diagonal, kTrap>(h, x, delta, A, B, C, y, batch, D, R, ld_x, ld_d, ld_bc, ld_y,
+                                                       tr, s);
 }
 
 // Checks and launch shared by the MIMO prefill entry points; trap: the trapezoidal rule.
@@ -331,7 +332,7 @@ jscan_status prefill_mimo_impl(const void *x, const void *delta, const void *lam
 jscan_status step_mimo_impl(float *h, const void *x_prev, const void *B_prev, const void *x_t, const void *delta_t,
                             const void *lam_t, const float *A, const void *B_t, const void *C_t, void *y_t,
                             int64_t batch, int64_t D, int64_t N, int64_t R, int64_t ld_x, int64_t ld_d, int64_t ld_bc,
-                            jscan_a_form a_form, jscan_dtype dtype, void *stream, bool trap) {
+                            int64_t ld_y, jscan_a_form a_form, jscan_dtype dtype, void *stream, bool trap) {
     jscan::AForm af;
     if (!form_of(a_form, &af)) return JSCAN_ERR_FORM;
     if (dtype != JSCAN_F32 && dtype != JSCAN_BF16) return JSCAN_ERR_DTYPE;
@@ -340,7 +341,8 @@ jscan_status step_mimo_impl(float *h, const void *x_prev, const void *B_prev, co
     if ((batch + jscan::mimo_step::kRows - 1) / jscan::mimo_step::kRows * ((D * 4 + 255) / 256) > kMaxBlocks)
         return JSCAN_ERR_SHAPE;
     if (batch == 0 || D == 0) return JSCAN_OK;
-    if (ld_x < D * R || ld_d < D || ld_bc < N * R || ld_x % 8 != 0 || ld_d % 8 != 0 || ld_bc % 8 != 0)
+    if (ld_x < D * R || ld_d < D || ld_bc < N * R || ld_y < D * R || ld_x % 8 != 0 || ld_d % 8 != 0 ||
+        ld_bc % 8 != 0 || ld_y % 8 != 0)
         return JSCAN_ERR_SHAPE;
     if (!h || !x_t || !delta_t || !A || !B_t || !C_t || !y_t) return JSCAN_ERR_NULL;
     if (trap && (!x_prev || !B_prev || !lam_t)) return JSCAN_ERR_NULL;
@@ -353,7 +355,7 @@ jscan_status step_mimo_impl(float *h, const void *x_prev, const void *B_prev, co
     const int64_t es = elem_bytes(dtype);
     const int64_t rows_x = ((batch - 1) * ld_x + D * R) * es, rows_d = ((batch - 1) * ld_d + D) * es;
     const int64_t rows_bc = ((batch - 1) * ld_bc + N * R) * es;
-    const Span sh = span(h, batch * D * N * 4), sy = span(y_t, rows_x);
+    const Span sh = span(h, batch * D * N * 4), sy = span(y_t, ((batch - 1) * ld_y + D * R) * es);
     const Span inputs[] = {span(x_t, rows_x), span(delta_t, rows_d),
                            span(A, D * (af == jscan::AForm::ScaledIdentity ? 1 : N) * 4), span(B_t, rows_bc),
                            span(C_t, rows_bc), span(trap ? x_prev : nullptr, rows_x),
@@ -364,11 +366,15 @@ jscan_status step_mimo_impl(float *h, const void *x_prev, const void *B_prev, co
     hipStream_t s = static_cast<hipStream_t>(stream);
     const jscan::Trap tr{lam_t, x_prev, B_prev};
     if (dtype == JSCAN_BF16) {
-        if (trap) launch_step_mimo<jscan::BF16, true>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, R, ld_x, ld_d, ld_bc, af, tr, s);
-        else launch_step_mimo<jscan::BF16, false>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, R, ld_x, ld_d, ld_bc, af, tr, s);
+        if (trap) launch_step_mimo<jscan::BF16, true>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, R, ld_x, ld_d,
+                                                      ld_bc, ld_y, af, tr, s);
+        else launch_step_mimo<jscan::BF16, false>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, R, ld_x, ld_d, ld_bc,
+                                                  ld_y, af, tr, s);
     } else {
-        if (trap) launch_step_mimo<jscan::F32, true>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, R, ld_x, ld_d, ld_bc, af, tr, s);
-        else launch_step_mimo<jscan::F32, false>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, R, ld_x, ld_d, ld_bc, af, tr, s);
+        if (trap) launch_step_mimo<jscan::F32, true>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, R, ld_x, ld_d,
+                                                     ld_bc, ld_y, af, tr, s);
+        else launch_step_mimo<jscan::F32, false>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, R, ld_x, ld_d, ld_bc,
+                                                 ld_y, af, tr, s);
     }
     return launch_status();
 }
@@ -520,7 +526,7 @@ void launch_ssm_inputs(const uint16_t *x, const uint16_t *w_x, const float *g_d,
 template <typename E, jscan::AForm AF, bool kTrap = false>
 jscan_status launch_step(float *h, const void *x_t, const void *delta_t, const float *A,
                          const void *B_t, const void *C_t, void *y_t, int64_t batch, int64_t D,
-                         int64_t ld_xd, int64_t ld_bc, hipStream_t stream,
+                         int64_t ld_xd, int64_t ld_bc, int64_t ld_y, hipStream_t stream,
                          jscan::Trap tr = jscan::Trap{nullptr, nullptr, nullptr}) {
     using T = typename E::store_t;
     const int blocks_per_rows = (int)((D * 4 + 255) / 256);
@@ -528,7 +534,7 @@ jscan_status launch_step(float *h, const void *x_t, const void *delta_t, const f
     hipLaunchKernelGGL((jscan::step_kernel<E, AF, kTrap>), dim3((unsigned)(row_groups * blocks_per_rows)), dim3(256), 0,
                        stream, h, static_cast<const T *>(x_t), static_cast<const T *>(delta_t), A,
                        static_cast<const T *>(B_t), static_cast<const T *>(C_t), static_cast<T *>(y_t), (int)batch,
-                       (int)D, blocks_per_rows, ld_xd, ld_bc, static_cast<const T *>(tr.lam),
+                       (int)D, blocks_per_rows, ld_xd, ld_bc, ld_y, static_cast<const T *>(tr.lam),
                        static_cast<const T *>(tr.x_prev), static_cast<const T *>(tr.B_prev));
     return launch_status();
 }
@@ -536,29 +542,31 @@ jscan_status launch_step(float *h, const void *x_t, const void *delta_t, const f
 template <typename E>
 jscan_status dispatch_step_trap_e(float *h, const void *x_t, const void *delta_t, const float *A, const void *B_t,
                                   const void *C_t, void *y_t, int64_t batch, int64_t D, int64_t ld_xd, int64_t ld_bc,
-                                  hipStream_t s, jscan::AForm af, jscan::Trap tr) {
+                                  int64_t ld_y, hipStream_t s, jscan::AForm af, jscan::Trap tr) {
     using jscan::AForm;
     if (af == AForm::ScaledIdentity)
         return launch_step<E, AForm::ScaledIdentity, true>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc,
-                                                           s, tr);
+                                                           ld_y, s, tr);
     if (af == AForm::ComplexPairs)
-        return launch_step<E, AForm::ComplexPairs, true>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s,
-                                                         tr);
-    return launch_step<E, AForm::Diagonal, true>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s, tr);
+        return launch_step<E, AForm::ComplexPairs, true>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc,
+                                                         ld_y, s, tr);
+    return launch_step<E, AForm::Diagonal, true>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, ld_y, s,
+                                                 tr);
 }
 jscan_status dispatch_step_trap(float *h, const void *x_t, const void *delta_t, const float *A, const void *B_t,
                                 const void *C_t, void *y_t, int64_t batch, int64_t D, int64_t ld_xd, int64_t ld_bc,
-                                jscan_dtype dtype, hipStream_t s, jscan::AForm af, jscan::Trap tr) {
+                                int64_t ld_y, jscan_dtype dtype, hipStream_t s, jscan::AForm af, jscan::Trap tr) {
     if (dtype == JSCAN_BF16)
-        return dispatch_step_trap_e<jscan::BF16>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s, af, tr);
-    return dispatch_step_trap_e<jscan::F32>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s, af, tr);
+        return dispatch_step_trap_e<jscan::BF16>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, ld_y, s,
+                                                 af, tr);
+    return dispatch_step_trap_e<jscan::F32>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, ld_y, s, af, tr);
 }
 
 // Checks and launch shared by the decode-step entry points.  af: the form of A.
 // With tr.lam set, the trapezoidal rule: lam_t and x_prev have the rows of x_t, B_prev those of B_t.
 jscan_status step_impl(float *h, const void *x_t, const void *delta_t, const float *A, const void *B_t, const void *C_t,
-                       void *y_t, int64_t batch, int64_t D, int64_t N, int64_t ld_xd, int64_t ld_bc, jscan_dtype dtype,
-                       void *stream, jscan::AForm af, jscan::Trap tr = jscan::Trap{nullptr, nullptr, nullptr},
+                       void *y_t, int64_t batch, int64_t D, int64_t N, int64_t ld_xd, int64_t ld_bc, int64_t ld_y,
+                       jscan_dtype dtype, void *stream, jscan::AForm af, jscan::Trap tr = jscan::Trap{nullptr, nullptr, nullptr},
                        bool trap = false) {
     using jscan::AForm;
     if (dtype != JSCAN_F32 && dtype != JSCAN_BF16) return JSCAN_ERR_DTYPE;
@@ -567,7 +575,8 @@ jscan_status step_impl(float *h, const void *x_t, const void *delta_t, const flo
     if ((batch + jscan::step::kRows - 1) / jscan::step::kRows * ((D * 4 + 255) / 256) > kMaxBlocks)
         return JSCAN_ERR_SHAPE;
     if (batch == 0 || D == 0) return JSCAN_OK;
-    if (ld_xd < D || ld_bc < N || ld_xd % 8 != 0 || ld_bc % 8 != 0) return JSCAN_ERR_SHAPE;
+    if (ld_xd < D || ld_bc < N || ld_y < D || ld_xd % 8 != 0 || ld_bc % 8 != 0 || ld_y % 8 != 0)
+        return JSCAN_ERR_SHAPE;
     if (!h || !x_t || !delta_t || !A || !B_t || !C_t || !y_t) return JSCAN_ERR_NULL;
     if (trap && (!tr.lam || !tr.x_prev || !tr.B_prev)) return JSCAN_ERR_NULL;
     const void *arrays[] = {h, x_t, delta_t, A, B_t, C_t, y_t};
@@ -579,7 +588,7 @@ jscan_status step_impl(float *h, const void *x_t, const void *delta_t, const flo
 
     const int64_t es = elem_bytes(dtype);
     const int64_t rows_xd = ((batch - 1) * ld_xd + D) * es, rows_bc = ((batch - 1) * ld_bc + N) * es;
-    const Span sh = span(h, batch * D * N * 4), sy = span(y_t, rows_xd);
+    const Span sh = span(h, batch * D * N * 4), sy = span(y_t, ((batch - 1) * ld_y + D) * es);
     const Span inputs[] = {span(x_t, rows_xd), span(delta_t, rows_xd), span(A, D * (af == AForm::ScaledIdentity ? 1 : N) * 4), span(B_t, rows_bc),
                            span(C_t, rows_bc)};
     for (const Span &s : inputs)
@@ -592,24 +601,26 @@ jscan_status step_impl(float *h, const void *x_t, const void *delta_t, const flo
     }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (trap) return dispatch_step_trap(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, dtype, s, af, tr);
+    if (trap)
+        return dispatch_step_trap(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, ld_y, dtype, s, af, tr);
     if (af == AForm::ScaledIdentity) {
         if (dtype == JSCAN_BF16)
             return launch_step<jscan::BF16, AForm::ScaledIdentity>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd,
-                                                                    ld_bc, s);
-        return launch_step<jscan::F32, AForm::ScaledIdentity>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc,
-                                                               s);
+                                                                    ld_bc, ld_y, s);
+        return launch_step<jscan::F32, AForm::ScaledIdentity>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd,
+                                                              ld_bc, ld_y, s);
     }
     if (af == AForm::ComplexPairs) {
         if (dtype == JSCAN_BF16)
             return launch_step<jscan::BF16, AForm::ComplexPairs>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd,
-                                                                  ld_bc, s);
+                                                                  ld_bc, ld_y, s);
         return launch_step<jscan::F32, AForm::ComplexPairs>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc,
-                                                             s);
+                                                            ld_y, s);
     }
     if (dtype == JSCAN_BF16)
-        return launch_step<jscan::BF16, AForm::Diagonal>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s);
-    return launch_step<jscan::F32, AForm::Diagonal>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, s);
+        return launch_step<jscan::BF16, AForm::Diagonal>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc,
+                                                         ld_y, s);
+    return launch_step<jscan::F32, AForm::Diagonal>(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, ld_xd, ld_bc, ld_y, s);
 }
 
 }  // namespace
@@ -690,9 +701,9 @@ jscan_status jscan_prefill_chunked_noalloc(const void *x, const void *delta, con
 
 jscan_status jscan_step(float *h, const void *x_t, const void *delta_t, const float *A,
                         const void *B_t, const void *C_t, void *y_t, int64_t batch, int64_t D,
-                        int64_t N, int64_t ld_xd, int64_t ld_bc, jscan_dtype dtype,
+                        int64_t N, int64_t ld_xd, int64_t ld_bc, int64_t ld_y, jscan_dtype dtype,
                         void *stream) {
-    return step_impl(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, N, ld_xd, ld_bc, dtype, stream,
+    return step_impl(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, N, ld_xd, ld_bc, ld_y, dtype, stream,
                      jscan::AForm::Diagonal);
 }
 
@@ -705,8 +716,8 @@ jscan_status jscan_prefill_scalar_a(const void *x, const void *delta, const floa
 
 jscan_status jscan_step_scalar_a(float *h, const void *x_t, const void *delta_t, const float *a, const void *B_t,
                                  const void *C_t, void *y_t, int64_t batch, int64_t D, int64_t N, int64_t ld_xd,
-                                 int64_t ld_bc, jscan_dtype dtype, void *stream) {
-    return step_impl(h, x_t, delta_t, a, B_t, C_t, y_t, batch, D, N, ld_xd, ld_bc, dtype, stream,
+                                 int64_t ld_bc, int64_t ld_y, jscan_dtype dtype, void *stream) {
+    return step_impl(h, x_t, delta_t, a, B_t, C_t, y_t, batch, D, N, ld_xd, ld_bc, ld_y, dtype, stream,
                      jscan::AForm::ScaledIdentity);
 }
 
@@ -719,8 +730,8 @@ jscan_status jscan_prefill_complex(const void *x, const void *delta, const float
 
 jscan_status jscan_step_complex(float *h, const void *x_t, const void *delta_t, const float *A, const void *B_t,
                                 const void *C_t, void *y_t, int64_t batch, int64_t D, int64_t N, int64_t ld_xd,
-                                int64_t ld_bc, jscan_dtype dtype, void *stream) {
-    return step_impl(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, N, ld_xd, ld_bc, dtype, stream,
+                                int64_t ld_bc, int64_t ld_y, jscan_dtype dtype, void *stream) {
+    return step_impl(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, N, ld_xd, ld_bc, ld_y, dtype, stream,
                      jscan::AForm::ComplexPairs);
 }
 
@@ -754,10 +765,10 @@ jscan_status jscan_prefill_trapezoid(const void *x, const void *delta, const voi
 jscan_status jscan_step_trapezoid(float *h, const void *x_prev, const void *B_prev, const void *x_t,
                                   const void *delta_t, const void *lam_t, const float *A, const void *B_t,
                                   const void *C_t, void *y_t, int64_t batch, int64_t D, int64_t N, int64_t ld_xd,
-                                  int64_t ld_bc, jscan_a_form a_form, jscan_dtype dtype, void *stream) {
+                                  int64_t ld_bc, int64_t ld_y, jscan_a_form a_form, jscan_dtype dtype, void *stream) {
     jscan::AForm af;
     if (!form_of(a_form, &af)) return JSCAN_ERR_FORM;
-    return step_impl(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, N, ld_xd, ld_bc, dtype, stream, af,
+    return step_impl(h, x_t, delta_t, A, B_t, C_t, y_t, batch, D, N, ld_xd, ld_bc, ld_y, dtype, stream, af,
                      jscan::Trap{lam_t, x_prev, B_prev}, true);
 }
 
@@ -770,9 +781,10 @@ jscan_status jscan_prefill_mimo(const void *x, const void *delta, const float *A
 
 jscan_status jscan_step_mimo(float *h, const void *x_t, const void *delta_t, const float *A, const void *B_t,
                              const void *C_t, void *y_t, int64_t batch, int64_t D, int64_t N, int64_t R, int64_t ld_x,
-                             int64_t ld_d, int64_t ld_bc, jscan_a_form a_form, jscan_dtype dtype, void *stream) {
+                             int64_t ld_d, int64_t ld_bc, int64_t ld_y, jscan_a_form a_form, jscan_dtype dtype,
+                             void *stream) {
     return step_mimo_impl(h, nullptr, nullptr, x_t, delta_t, nullptr, A, B_t, C_t, y_t, batch, D, N, R, ld_x, ld_d,
-                          ld_bc, a_form, dtype, stream, false);
+                          ld_bc, ld_y, a_form, dtype, stream, false);
 }
 
 jscan_status jscan_prefill_mimo_trapezoid(const void *x, const void *delta, const void *lam, const float *A,
@@ -787,10 +799,10 @@ jscan_status jscan_prefill_mimo_trapezoid(const void *x, const void *delta, cons
 jscan_status jscan_step_mimo_trapezoid(float *h, const void *x_prev, const void *B_prev, const void *x_t,
                                        const void *delta_t, const void *lam_t, const float *A, const void *B_t,
                                        const void *C_t, void *y_t, int64_t batch, int64_t D, int64_t N, int64_t R,
-                                       int64_t ld_x, int64_t ld_d, int64_t ld_bc, jscan_a_form a_form,
+                                       int64_t ld_x, int64_t ld_d, int64_t ld_bc, int64_t ld_y, jscan_a_form a_form,
                                        jscan_dtype dtype, void *stream) {
     return step_mimo_impl(h, x_prev, B_prev, x_t, delta_t, lam_t, A, B_t, C_t, y_t, batch, D, N, R, ld_x, ld_d, ld_bc,
-                          a_form, dtype, stream, true);
+                          ld_y, a_form, dtype, stream, true);
 }
 
 jscan_status jscan_ssm_inputs(const void *x, const void *w_x, const float *g_delta, const float *g_B,
@@ -883,6 +895,6 @@ const char *jscan_status_string(jscan_status s) {
 
 int jscan_last_hip_error(void) { return g_last_hip_error; }
 
-int jscan_version(void) { return 108; }
+int jscan_version(void) { return 109; }
 
 }  // extern "C"

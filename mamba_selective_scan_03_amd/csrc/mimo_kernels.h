@@ -246,7 +246,8 @@ __global__ __launch_bounds__(256) void step_mimo_kernel(float *__restrict__ h, c
                                                         const typename E::store_t *__restrict__ Ct,
                                                         typename E::store_t *__restrict__ y, int batch, int D,
                                                         int blocks_per_rows, int64_t ld_x, int64_t ld_d,
-                                                        int64_t ld_bc, const typename E::store_t *__restrict__ lam,
+                                                        int64_t ld_bc, int64_t ld_y,
+                                                        const typename E::store_t *__restrict__ lam,
                                                         const typename E::store_t *__restrict__ xp,
                                                         const typename E::store_t *__restrict__ bp) {
     constexpr int NR = mimo_step::kRows;
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(256) void step_mimo_kernel(float *__restrict__ h, c
         }
         if (b < batch) {
             store_state(h + ((int64_t)b * D + d) * kDState + q * 4, make_float4(hv[0], hv[1], hv[2], hv[3]));
-            S *yp = y + (int64_t)b * ld_x + (int64_t)d * R;
+            S *yp = y + (int64_t)b * ld_y + (int64_t)d * R;
 #pragma unroll
             for (int r0 = 0; r0 < R; r0 += 4) {   // lane q stores output r0 + q
                 if (r0 + q < R) {

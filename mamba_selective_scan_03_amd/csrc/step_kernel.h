@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ h,
                                                    const typename E::store_t *__restrict__ Bt,
                                                    const typename E::store_t *__restrict__ Ct,
                                                    typename E::store_t *__restrict__ y, int batch, int D,
-                                                   int blocks_per_rows, int64_t ld_xd, int64_t ld_bc,
+                                                   int blocks_per_rows, int64_t ld_xd, int64_t ld_bc, int64_t ld_y,
                                                    const typename E::store_t *__restrict__ lam,
                                                    const typename E::store_t *__restrict__ xp,
                                                    const typename E::store_t *__restrict__ bp) {
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void step_kernel(float *__restrict__ h,
         p = p + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, p), 0x4E, 0xF, 0xF, true));
         if (b < batch) {
             store_state(h + ((int64_t)b * D + d) * kDState + q * 4, hn);
-            if (q == 0) E::store(y + (int64_t)b * ld_xd + d, p);
+            if (q == 0) E::store(y + (int64_t)b * ld_y + d, p);
         }
     }
 }

@@ -83,7 +83,7 @@ def test_status_strings_and_version():
     for s in range(9):
         assert lib.jscan_status_string(s) and lib.jscan_status_string(s) != b"unknown status"
     assert lib.jscan_status_string(99) == b"unknown status"
-    assert lib.jscan_version() == 108
+    assert lib.jscan_version() == 109
     assert lib.jscan_last_hip_error() == 0
 
 
@@ -100,8 +100,8 @@ def resume(h0, h=P + 0x600000, **kw):
 
 
 def step(h=P, x=P + 0x100000, d=P + 0x200000, A=P + 0x300000, B=P + 0x400000, C=P + 0x500000,
-         y=P + 0x600000, batch=2, D=64, N=16, ld_xd=64, ld_bc=16, dtype=BF16):
-    return jscan.library().jscan_step(h, x, d, A, B, C, y, batch, D, N, ld_xd, ld_bc, dtype, None)
+         y=P + 0x600000, batch=2, D=64, N=16, ld_xd=64, ld_bc=16, ld_y=64, dtype=BF16):
+    return jscan.library().jscan_step(h, x, d, A, B, C, y, batch, D, N, ld_xd, ld_bc, ld_y, dtype, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -135,7 +135,8 @@ def test_resume_aliasing_rules():
     (dict(dtype=3), EDTYPE), (dict(N=17), ESHAPE), (dict(D=12), ESHAPE), (dict(ld_xd=32), ESHAPE),
     (dict(ld_bc=8), ESHAPE), (dict(ld_xd=68), ESHAPE), (dict(h=None), ENULL), (dict(B=None), ENULL),
     (dict(x=P + 0x100004), EALIGN), (dict(y=P + 0x100000), EALIAS), (dict(y=P + 64 * 16 * 4), EALIAS),
-    (dict(h=P + 0x300000 - 64), EALIAS),
+    (dict(h=P + 0x300000 - 64), EALIAS), (dict(ld_y=32), ESHAPE), (dict(ld_y=68), ESHAPE),
+    (dict(y=P + 0x100000 - 8192, ld_y=4096), EALIAS),   # y's second row, 4096 elements on, is x
 ])
 def test_step_validation(kw, code):
     assert step(**kw) == code
@@ -161,8 +162,8 @@ def test_prefill_scalar_a_zero_sized_is_a_no_op():
 
 
 def step_sa(h=P, x=P + 0x100000, d=P + 0x200000, a=P + 0x300000, B=P + 0x400000, C=P + 0x500000,
-            y=P + 0x600000, batch=2, D=64, N=16, ld_xd=64, ld_bc=16, dtype=BF16):
-    return jscan.library().jscan_step_scalar_a(h, x, d, a, B, C, y, batch, D, N, ld_xd, ld_bc, dtype, None)
+            y=P + 0x600000, batch=2, D=64, N=16, ld_xd=64, ld_bc=16, ld_y=64, dtype=BF16):
+    return jscan.library().jscan_step_scalar_a(h, x, d, a, B, C, y, batch, D, N, ld_xd, ld_bc, ld_y, dtype, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -294,9 +295,9 @@ def test_complex_entry_points_validate_like_the_general_ones():
     assert lib.jscan_prefill_complex(P, P + 0x100000, P + 0x200000, P + 0x300000, P + 0x400000, None,
                                      P + 0x500000, P + 0x600000, 1, 64, 60, 16, BF16, None) == ESHAPE
     assert lib.jscan_step_complex(P, P + 0x100000, P + 0x200000, P + 0x300000, P + 0x400000, P + 0x500000,
-                                  P + 0x600000, 2, 64, 16, 64, 16, 9, None) == EDTYPE
+                                  P + 0x600000, 2, 64, 16, 64, 16, 64, 9, None) == EDTYPE
     assert lib.jscan_step_complex(P, P + 0x100000, P + 0x200000, None, P + 0x400000, P + 0x500000,
-                                  P + 0x600000, 2, 64, 16, 64, 16, BF16, None) == ENULL
+                                  P + 0x600000, 2, 64, 16, 64, 16, 64, BF16, None) == ENULL
 
 
 def trap_prefill(x=P, d=P + 0x100000, lam=P + 0x700000, A=P + 0x200000, B=P + 0x300000, C=P + 0x400000, h0=None,
@@ -329,15 +330,15 @@ def test_prefill_trapezoid_zero_sized_is_a_no_op():
 
 def trap_step(h=P, xp=P + 0x700000, bp=P + 0x800000, x=P + 0x100000, d=P + 0x200000, lam=P + 0x900000,
               A=P + 0x300000, B=P + 0x400000, C=P + 0x500000, y=P + 0x600000, batch=2, D=64, N=16, ld_xd=64,
-              ld_bc=16, form=0, dtype=BF16):
-    return jscan.library().jscan_step_trapezoid(h, xp, bp, x, d, lam, A, B, C, y, batch, D, N, ld_xd, ld_bc, form,
-                                                dtype, None)
+              ld_bc=16, ld_y=64, form=0, dtype=BF16):
+    return jscan.library().jscan_step_trapezoid(h, xp, bp, x, d, lam, A, B, C, y, batch, D, N, ld_xd, ld_bc, ld_y,
+                                                form, dtype, None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(form=7), EFORM), (dict(xp=None), ENULL), (dict(bp=None), ENULL), (dict(lam=None), ENULL),
     (dict(lam=P + 0x900004), EALIGN), (dict(ld_xd=60), ESHAPE), (dict(y=P + 0x700000), EALIAS),
-    (dict(h=P + 0x900000 - 64), EALIAS), (dict(dtype=3), EDTYPE),
+    (dict(h=P + 0x900000 - 64), EALIAS), (dict(dtype=3), EDTYPE), (dict(ld_y=60), ESHAPE),
 ])
 def test_step_trapezoid_validation(kw, code):
     assert trap_step(**kw) == code
@@ -373,13 +374,15 @@ def test_prefill_mimo_sizes_follow_the_rank():
 
 
 def mimo_step(h=P, x=P + 0x100000, d=P + 0x200000, A=P + 0x300000, B=P + 0x400000, C=P + 0x500000, y=P + 0x600000,
-              batch=2, D=64, N=16, R=4, ld_x=256, ld_d=64, ld_bc=64, form=0, dtype=BF16):
-    return jscan.library().jscan_step_mimo(h, x, d, A, B, C, y, batch, D, N, R, ld_x, ld_d, ld_bc, form, dtype, None)
+              batch=2, D=64, N=16, R=4, ld_x=256, ld_d=64, ld_bc=64, ld_y=256, form=0, dtype=BF16):
+    return jscan.library().jscan_step_mimo(h, x, d, A, B, C, y, batch, D, N, R, ld_x, ld_d, ld_bc, ld_y, form, dtype,
+                                           None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(R=5), ESHAPE), (dict(ld_x=128), ESHAPE), (dict(ld_bc=32), ESHAPE), (dict(ld_d=60), ESHAPE),
     (dict(form=9), EFORM), (dict(C=None), ENULL), (dict(y=P + 0x600004), EALIGN), (dict(y=P + 0x100000), EALIAS),
+    (dict(ld_y=128), ESHAPE), (dict(ld_y=260), ESHAPE),
 ])
 def test_step_mimo_validation(kw, code):
     assert mimo_step(**kw) == code
@@ -404,12 +407,15 @@ def test_prefill_mimo_trapezoid_validation(kw, code):
 def test_step_mimo_trapezoid_validation():
     lib = jscan.library()
     args = [P, P + 0x700000, P + 0x800000, P + 0x100000, P + 0x200000, P + 0x900000, P + 0x300000, P + 0x400000,
-            P + 0x500000, P + 0x600000, 2, 64, 16, 4, 256, 64, 64, 0, BF16, None]
+            P + 0x500000, P + 0x600000, 2, 64, 16, 4, 256, 64, 64, 256, 0, BF16, None]
     assert lib.jscan_step_mimo_trapezoid(*args[:1], None, *args[2:]) == ENULL          # x_prev
     assert lib.jscan_step_mimo_trapezoid(*args[:5], None, *args[6:]) == ENULL          # lam_t
     bad = list(args)
     bad[9] = P + 0x700000                                                               # y_t on x_prev
     assert lib.jscan_step_mimo_trapezoid(*bad) == EALIAS
     bad = list(args)
-    bad[17] = 3
+    bad[18] = 3
     assert lib.jscan_step_mimo_trapezoid(*bad) == EFORM
+    bad = list(args)
+    bad[17] = 200                                                                       # ld_y below D * R
+    assert lib.jscan_step_mimo_trapezoid(*bad) == ESHAPE

@@ -15,8 +15,7 @@ pytestmark = pytest.mark.gpu
 def step_chain(d, h, t0=0, t1=None):
     """Feed tokens [t0, t1) one by one through jscan_step using strided token views."""
     t1 = d["x"].shape[1] if t1 is None else t1
-    # y rows go into one preallocated tensor shaped like x (y_t shares x_t's row stride in the
-    # ABI): without y_t, step() would allocate a batch x L x D tensor for every token
+    # y rows go into one preallocated tensor shaped like x, through strided views like x's
     y = torch.empty_like(d["x"])
     ys = []
     for t in range(t0, t1):
@@ -117,3 +116,49 @@ def test_step_odd_batches(batch):
     y_ref, h_ref = oracle.step(inp["h0"], inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"])
     assert_parity(f64(y), y_ref, torch.bfloat16, f"odd batch {batch} y")
     assert_parity(f64(h), h_ref, torch.bfloat16, f"odd batch {batch} h")
+
+
+def test_step_output_row_stride_is_its_own():
+    """y_t's row stride (ld_y) is independent of x_t's: strided token views of x written to a
+    new contiguous [batch, D], to token views of a [batch, L, D] output, and to the first D
+    columns of a wider NaN-filled buffer give the same bits, and nothing past the D columns is
+    written.  Checked for the single-input step, the trapezoidal step and the MIMO step."""
+    batch, L, D, R = 3, 6, 256, 4
+    d = to_dev(workloads.small_prefill(batch, L, D, "bf16", seed=5))
+    A = d["A"]
+    h_runs = [torch.randn(batch, D, 16, generator=torch.Generator().manual_seed(2)).cuda() for _ in range(3)]
+    y_tok = torch.empty_like(d["x"])
+    wide = torch.full((batch, D + 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    for t in range(L):
+        args = (d["x"][:, t], d["delta"][:, t], A, d["B"][:, t], d["C"][:, t])
+        y_new = jscan.step(h_runs[0], *args)
+        jscan.step(h_runs[1], *args, y_t=y_tok[:, t])
+        jscan.step(h_runs[2], *args, y_t=wide[:, :D])
+        assert y_new.is_contiguous() and y_new.shape == (batch, D)
+        assert torch.equal(bits(y_new), bits(y_tok[:, t])) and torch.equal(bits(y_new), bits(wide[:, :D]))
+        assert torch.isnan(wide[:, D:].float()).all(), "step wrote past y_t's rows"
+    assert torch.equal(bits(h_runs[0]), bits(h_runs[1])) and torch.equal(bits(h_runs[0]), bits(h_runs[2]))
+
+    # the trapezoidal step shares the launch: token views in, contiguous and wide out
+    lam = torch.rand(batch, L, D, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16).cuda()
+    hs = [torch.zeros(batch, D, 16, device="cuda") for _ in range(2)]
+    for t in range(1, L):
+        targs = (d["x"][:, t - 1], d["B"][:, t - 1], d["x"][:, t], d["delta"][:, t], lam[:, t], A, d["B"][:, t],
+                 d["C"][:, t])
+        y_new = jscan.step_trapezoid(hs[0], *targs)
+        jscan.step_trapezoid(hs[1], *targs, y_t=wide[:, :D])
+        assert torch.equal(bits(y_new), bits(wide[:, :D])) and torch.isnan(wide[:, D:].float()).all()
+    assert torch.equal(bits(hs[0]), bits(hs[1]))
+
+    # MIMO: x_t rows of D * R, y_t rows of D * R with a stride of their own
+    xm = torch.randn(batch, L, D, R, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16).cuda()
+    Bm = torch.randn(batch, L, 16, R, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).cuda()
+    wide_m = torch.full((batch, D * R + 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    hm = [torch.zeros(batch, D, 16, device="cuda") for _ in range(2)]
+    for t in range(L):
+        margs = (xm[:, t], d["delta"][:, t], A, Bm[:, t], Bm[:, t])
+        y_new = jscan.step_mimo(hm[0], *margs)
+        y_w = jscan.step_mimo(hm[1], *margs, y_t=wide_m[:, :D * R].view(batch, D, R))
+        assert y_new.is_contiguous() and torch.equal(bits(y_new), bits(y_w))
+        assert torch.isnan(wide_m[:, D * R:].float()).all(), "MIMO step wrote past y_t's rows"
+    assert torch.equal(bits(hm[0]), bits(hm[1]))
