@@ -38,8 +38,7 @@ def oracle_block(inp, c0, c1, t0=0, t1=None, h0=None):
 
 
 def step_chain(d, h, t0, t1):
-    # y rows go into one preallocated tensor shaped like x (y_t shares x_t's row stride in the
-    # ABI): without y_t, step() would allocate a batch x L x D tensor for every token
+    # y rows go into one preallocated tensor shaped like x, through strided views like x's
     y = torch.empty_like(d["x"])
     ys = []
     for t in range(t0, t1):
