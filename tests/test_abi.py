@@ -419,3 +419,29 @@ def test_step_mimo_trapezoid_validation():
     bad = list(args)
     bad[17] = 200                                                                       # ld_y below D * R
     assert lib.jscan_step_mimo_trapezoid(*bad) == ESHAPE
+
+
+def test_step_output_and_its_row_stride():
+    """The decode steps' y_t: a new contiguous tensor (row stride D, or D * R for MIMO), or the
+    caller's tensor with contiguous rows and a row stride of its own (passed on as ld_y)."""
+    cpu = torch.device("cpu")
+    y, ld = _binding._step_output(None, (3, 64), torch.bfloat16, cpu)
+    assert y.shape == (3, 64) and y.is_contiguous() and ld == 64
+    y, ld = _binding._step_output(None, (2, 64, 4), torch.float32, cpu)
+    assert y.shape == (2, 64, 4) and y.is_contiguous() and ld == 256
+    buf = torch.empty(3, 10, 64, dtype=torch.bfloat16)
+    y, ld = _binding._step_output(buf[:, 7], (3, 64), torch.bfloat16, cpu)   # token view of [batch, L, D]
+    assert ld == 640 and y.data_ptr() == buf[:, 7].data_ptr()
+    wide = torch.empty(2, 64 * 4 + 64)
+    _, ld = _binding._step_output(wide[:, :256].view(2, 64, 4), (2, 64, 4), torch.float32, cpu)
+    assert ld == 320
+    _, ld = _binding._step_output(buf[:1, 3], (1, 64), torch.bfloat16, cpu)    # one row: its length
+    assert ld == 64
+    with pytest.raises(ValueError):
+        _binding._step_output(buf[:, :, 0], (3, 10), torch.bfloat16, cpu)       # strided row elements
+    with pytest.raises(ValueError):
+        _binding._step_output(torch.empty(3, 64), (3, 64), torch.bfloat16, cpu)  # wrong dtype
+    with pytest.raises(ValueError):
+        _binding._step_output(torch.empty(3, 32, dtype=torch.bfloat16), (3, 64), torch.bfloat16, cpu)
+    with pytest.raises(ValueError):   # MIMO rows must be [D][R] with R contiguous
+        _binding._step_output(torch.empty(2, 4, 64).transpose(1, 2), (2, 64, 4), torch.float32, cpu)
