@@ -44,7 +44,8 @@
  * launched and no output is touched.
  *     JSCAN_ERR_NULL   a required pointer is NULL
  *     JSCAN_ERR_SHAPE  negative sizes, N != 16, D not a multiple of 8, a row stride
- *                      shorter than its row or not a multiple of 8
+ *                      shorter than its row or not a multiple of 8, D above 2^24 or batch
+ *                      above 2^20 (the kernels index channels and rows in 32 bits)
  *     JSCAN_ERR_DTYPE  unknown dtype
  *     JSCAN_ERR_ALIGN  an array pointer not 16-byte aligned
  *     JSCAN_ERR_ALIAS  an output overlaps an input or another output (the exceptions are

@@ -445,3 +445,15 @@ def test_step_output_and_its_row_stride():
         _binding._step_output(torch.empty(3, 32, dtype=torch.bfloat16), (3, 64), torch.bfloat16, cpu)
     with pytest.raises(ValueError):   # MIMO rows must be [D][R] with R contiguous
         _binding._step_output(torch.empty(2, 4, 64).transpose(1, 2), (2, 64, 4), torch.float32, cpu)
+
+
+@pytest.mark.parametrize("fn", ["prefill", "step"])
+def test_size_limits_are_where_the_header_puts_them(fn):
+    """D up to 2^24 and batch up to 2^20 pass the shape checks (the call then stops at the
+    missing x, before any launch); one step past either limit is a shape error."""
+    call = prefill if fn == "prefill" else step
+    extra = {} if fn == "prefill" else dict(ld_xd=1 << 24, ld_y=1 << 24)
+    assert call(D=1 << 24, batch=1, x=None, **extra) == ENULL
+    assert call(D=(1 << 24) + 8, batch=1, x=None, **{k: v + 8 for k, v in extra.items()}) == ESHAPE
+    assert call(D=64, batch=1 << 20, x=None) == ENULL
+    assert call(D=64, batch=(1 << 20) + 1, x=None) == ESHAPE
