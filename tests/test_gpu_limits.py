@@ -91,3 +91,28 @@ def test_prefill_and_step_at_the_batch_limit():
     torch.cuda.synchronize()
     assert yb.shape == (MAX_BATCH, 32)
     assert tiled_equal(yb, ys, 0) and tiled_equal(hb, hs, 0)
+
+
+def test_mimo_at_the_channel_limit():
+    """The rank-8 MIMO prefill and step at D = 2^24 (rows of D * R = 2^27 values)."""
+    R = 8
+    wl = workloads.Workload("adhoc_mimo_limit", 611, 1, 66, 256, 16, "bf16", True)
+    inp = workloads.mimo_inputs(wl, R, seed=3, threads=1)
+    d = to_dev(inp)
+    y_s, h_s = jscan.prefill_mimo(d["x"], d["delta"], d["A"], d["B"], d["C"])
+    y_ref, h_ref = oracle.prefill_mimo(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"])
+    assert_parity(f64(y_s), y_ref, torch.bfloat16, "mimo 1x66x256 R8 y")
+    reps = MAX_D // 256
+    say(f"prefill_mimo 1x66x{MAX_D} R{R} bf16: 256 channels tiled {reps} times")
+    x, dl, A = d["x"].repeat(1, 1, reps, 1), d["delta"].repeat(1, 1, reps), d["A"].repeat(reps, 1)
+    y_b, h_b = jscan.prefill_mimo(x, dl, A, d["B"], d["C"])
+    torch.cuda.synchronize()
+    assert tiled_equal(y_b, y_s, 2) and tiled_equal(h_b, h_s, 1)
+    del y_b
+    # one more token through the MIMO step from the final states, token views of the same inputs
+    hs, hb = h_s.clone(), h_b
+    ys = jscan.step_mimo(hs, d["x"][:, 1], d["delta"][:, 1], d["A"], d["B"][:, 1], d["C"][:, 1])
+    say(f"step_mimo 1x{MAX_D} R{R} bf16")
+    yb = jscan.step_mimo(hb, x[:, 1], dl[:, 1], A, d["B"][:, 1], d["C"][:, 1])
+    torch.cuda.synchronize()
+    assert tiled_equal(yb, ys, 1) and tiled_equal(hb, hs, 1)
